@@ -1,0 +1,262 @@
+/*
+ * FP64 CPU oracle for the deterministic, batch-invariant H3 full attention node with its per-head
+ * q/k RMSNorm.
+ *
+ * TEST INFRASTRUCTURE ONLY.  Nothing in the product path links, loads or calls this file; only the
+ * test suite, the smoke check and the benchmark's CPU-baseline leg do.  It shares no code, header,
+ * table or constant with the HIP library: it is written from the pages' description of the node,
+ * not from the kernels.
+ *
+ * What it follows (the RL-Kernel pull-request pages on MiniMax-H3):
+ *  - "ws1_one_h3_block + full-model qualification", Bindings table: the block runs
+ *    q_norm/k_norm -> rope -> attention(causal=False); q_norm/k_norm is an RMSNorm over each
+ *    128-wide head that is bitwise equal to nn.RMSNorm, and its output (the node's output) is bf16.
+ *  - same page, Results: the q-norm weight is a 128-element tensor shared by all heads.
+ *  - same page, Summary: several sequences are packed on one token axis (packed layouts); each
+ *    token attends only to the tokens of its own sequence, non-causally.
+ *  - "33B forward/backward and rollout-vs-train control", Scope: FP32 accumulation with one final
+ *    rounding.  The oracle is the exact (FP64) value that such a kernel approximates.
+ *
+ * Readings where the pages are silent (each is listed with its reason in the design notes):
+ *  - segments: int32 ids per token, non-decreasing; a segment is a maximal run of equal ids;
+ *  - norm: y = x * (mean(x^2) + eps)^(-1/2) * w over the 128 channels of one (token, head), computed
+ *    in FP64 and rounded ONCE, round-to-nearest-even, directly from FP64 to bf16 (the q_norm node's
+ *    output dtype); with no weights the inputs are taken as already normalised (no norm at all);
+ *  - attention: exact two-pass softmax in FP64 over the keys of the query's own segment,
+ *    s_ij = scale * <qhat_i, khat_j>,  O_i = sum_j exp(s_ij - m_i) v_j / sum_j exp(s_ij - m_i),
+ *    LSE_i = m_i + ln(sum_j exp(s_ij - m_i)); O is returned in FP64, NOT rounded.
+ *
+ * Layouts: q, k, v, out are [T, H, 128] (token-major, then head, then channel); lse is [T, H].
+ * bf16 values are passed as their uint16 bit patterns.
+ */
+#include <math.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+#ifdef _OPENMP
+#include <omp.h>
+#endif
+
+#define HD 128
+
+enum { ORACLE_OK = 0, ORACLE_ERR_ARGS = 1, ORACLE_ERR_SEGMENTS = 2, ORACLE_ERR_NOMEM = 3 };
+
+int oracle_num_threads(void) {
+#ifdef _OPENMP
+  return omp_get_max_threads();
+#else
+  return 1;
+#endif
+}
+
+void oracle_set_num_threads(int n) {
+#ifdef _OPENMP
+  if (n > 0) omp_set_num_threads(n);
+#else
+  (void)n;
+#endif
+}
+
+/* ---------------------------------------------------------------- bf16 <-> FP64 */
+
+double oracle_bf16_to_f64(uint16_t b) {
+  uint32_t bits = (uint32_t)b << 16;
+  float f;
+  memcpy(&f, &bits, 4);
+  return (double)f;
+}
+
+/* Round an FP64 value to bf16 in ONE step, round-to-nearest, ties to even.  bf16 keeps 8
+ * significant bits and float's exponent range (normals down to 2^-126, subnormals in steps of
+ * 2^-133).  x / ulp is exact (ulp is a power of two), nearbyint rounds half to even in the default
+ * rounding mode, and the rounded value has at most 8 significant bits, so converting it to float is
+ * exact and its top 16 bits are the bf16 pattern. */
+uint16_t oracle_f64_to_bf16(double x) {
+  uint16_t sign = signbit(x) ? 0x8000u : 0u;
+  if (isnan(x)) return (uint16_t)(sign | 0x7FC0u);
+  double a = fabs(x);
+  if (isinf(a)) return (uint16_t)(sign | 0x7F80u);
+  if (a == 0.0) return sign;
+  int e;
+  frexp(a, &e);          /* a in [2^(e-1), 2^e) */
+  int E = e - 1;         /* unbiased exponent */
+  if (E < -126) E = -126; /* subnormal range shares the smallest normal's ulp */
+  double ulp = ldexp(1.0, E - 7);
+  double r = nearbyint(a / ulp) * ulp;
+  if (r >= ldexp(1.0, 128)) return (uint16_t)(sign | 0x7F80u); /* overflow to infinity */
+  float f = (float)r;
+  uint32_t bits;
+  memcpy(&bits, &f, 4);
+  return (uint16_t)(sign | (uint16_t)(bits >> 16));
+}
+
+/* Element-wise array form of oracle_f64_to_bf16. */
+void oracle_f64_to_bf16_array(const double* x, uint16_t* y, int64_t n) {
+  for (int64_t i = 0; i < n; i++) y[i] = oracle_f64_to_bf16(x[i]);
+}
+
+/* ---------------------------------------------------------------- segments */
+
+/* Maximal runs of equal ids.  Ids must be non-decreasing; a decrease is an error.
+ * starts/lens have room for T entries.  Returns ORACLE_OK or ORACLE_ERR_SEGMENTS. */
+int oracle_segments(const int32_t* seg, int64_t T, int64_t* starts, int64_t* lens, int64_t* nseg) {
+  int64_t n = 0;
+  for (int64_t t = 0; t < T; t++) {
+    if (t > 0 && seg[t] < seg[t - 1]) { *nseg = 0; return ORACLE_ERR_SEGMENTS; }
+    if (t == 0 || seg[t] != seg[t - 1]) { starts[n] = t; n++; }
+  }
+  for (int64_t s = 0; s < n; s++) lens[s] = (s + 1 < n ? starts[s + 1] : T) - starts[s];
+  *nseg = n;
+  return ORACLE_OK;
+}
+
+/* ---------------------------------------------------------------- RMSNorm */
+
+/* One (token, head) row, unrounded: y_d = x_d * (mean(x^2) + eps)^(-1/2) * w_d. */
+static void norm_row_f64(const uint16_t* x, const uint16_t* w, double eps, double* y) {
+  double ss = 0.0;
+  double xv[HD];
+  for (int d = 0; d < HD; d++) {
+    xv[d] = oracle_bf16_to_f64(x[d]);
+    ss += xv[d] * xv[d];
+  }
+  double ms = ss / HD;
+  double r = 1.0 / sqrt(ms + eps);
+  for (int d = 0; d < HD; d++) y[d] = xv[d] * r * oracle_bf16_to_f64(w[d]);
+}
+
+/* Unrounded FP64 norm of every row of x [T, H, 128]; w is [128]. */
+int oracle_rmsnorm_f64(const uint16_t* x, const uint16_t* w, double* y, int64_t T, int32_t H, double eps) {
+  if (T < 0 || H < 1 || (T > 0 && (!x || !w || !y))) return ORACLE_ERR_ARGS;
+  int64_t rows = T * (int64_t)H;
+#pragma omp parallel for schedule(static)
+  for (int64_t r = 0; r < rows; r++) norm_row_f64(x + r * HD, w, eps, y + r * HD);
+  return ORACLE_OK;
+}
+
+/* The q_norm / k_norm node: the FP64 norm rounded once to bf16.  y may alias x. */
+int oracle_qknorm(const uint16_t* x, const uint16_t* w, uint16_t* y, int64_t T, int32_t H, double eps) {
+  if (T < 0 || H < 1 || (T > 0 && (!x || !w || !y))) return ORACLE_ERR_ARGS;
+  int64_t rows = T * (int64_t)H;
+#pragma omp parallel for schedule(static)
+  for (int64_t r = 0; r < rows; r++) {
+    double yr[HD];
+    norm_row_f64(x + r * HD, w, eps, yr);
+    for (int d = 0; d < HD; d++) y[r * HD + d] = oracle_f64_to_bf16(yr[d]);
+  }
+  return ORACLE_OK;
+}
+
+/* ---------------------------------------------------------------- attention */
+
+/* The bf16 operands entering Q.K^T: the norm node's output, or the inputs themselves when no
+ * weights are given.  Returned as FP64 [T*H*128] (bf16 values are exact in FP64). */
+static double* normed_operand(const uint16_t* x, const uint16_t* w, int64_t T, int32_t H, double eps) {
+  int64_t n = T * (int64_t)H * HD;
+  double* out = (double*)malloc((size_t)(n > 0 ? n : 1) * sizeof(double));
+  if (!out) return NULL;
+  int64_t rows = T * (int64_t)H;
+#pragma omp parallel for schedule(static)
+  for (int64_t r = 0; r < rows; r++) {
+    if (w) {
+      double yr[HD];
+      norm_row_f64(x + r * HD, w, eps, yr);
+      for (int d = 0; d < HD; d++) out[r * HD + d] = oracle_bf16_to_f64(oracle_f64_to_bf16(yr[d]));
+    } else {
+      for (int d = 0; d < HD; d++) out[r * HD + d] = oracle_bf16_to_f64(x[r * HD + d]);
+    }
+  }
+  return out;
+}
+
+/* Exact softmax attention of query token i (head h) over its segment [s0, s0+L).
+ * qh, kh: normed operands (FP64 [T,H,128]); v: bf16 [T,H,128]. */
+static void attend_one(const double* qh, const double* kh, const uint16_t* v, int32_t H, int h, int64_t i,
+                       int64_t s0, int64_t L, double scale, double* scores, double* o, double* lse) {
+  const double* qi = qh + (i * H + h) * HD;
+  double m = -INFINITY;
+  for (int64_t j = 0; j < L; j++) {
+    const double* kj = kh + ((s0 + j) * H + h) * HD;
+    double dot = 0.0;
+    for (int d = 0; d < HD; d++) dot += qi[d] * kj[d];
+    scores[j] = scale * dot;
+    if (scores[j] > m) m = scores[j];
+  }
+  double l = 0.0;
+  double acc[HD];
+  for (int d = 0; d < HD; d++) acc[d] = 0.0;
+  for (int64_t j = 0; j < L; j++) {
+    double e = exp(scores[j] - m);
+    l += e;
+    const uint16_t* vj = v + ((s0 + j) * H + h) * HD;
+    for (int d = 0; d < HD; d++) acc[d] += e * oracle_bf16_to_f64(vj[d]);
+  }
+  for (int d = 0; d < HD; d++) o[d] = acc[d] / l;
+  *lse = m + log(l);
+}
+
+/* Shared driver.  rows == NULL: every token; else only the listed query tokens (n_rows of them),
+ * with out/lse laid out [n_rows, H, 128] / [n_rows, H]. */
+static int fwd_impl(const uint16_t* q, const uint16_t* k, const uint16_t* v, const int32_t* seg, const uint16_t* wq,
+                    const uint16_t* wk, int64_t T, int32_t H, double eps, double scale, const int64_t* rows,
+                    int64_t n_rows, double* out, double* lse) {
+  if (T < 0 || H < 1) return ORACLE_ERR_ARGS;
+  if ((wq == NULL) != (wk == NULL)) return ORACLE_ERR_ARGS;
+  if (T == 0) return ORACLE_OK;
+  if (!q || !k || !v || !seg || !out) return ORACLE_ERR_ARGS;
+  int64_t* starts = (int64_t*)malloc((size_t)T * sizeof(int64_t));
+  int64_t* lens = (int64_t*)malloc((size_t)T * sizeof(int64_t));
+  int64_t* seg_of = (int64_t*)malloc((size_t)T * sizeof(int64_t));
+  if (!starts || !lens || !seg_of) { free(starts); free(lens); free(seg_of); return ORACLE_ERR_NOMEM; }
+  int64_t nseg = 0;
+  int rc = oracle_segments(seg, T, starts, lens, &nseg);
+  if (rc != ORACLE_OK) { free(starts); free(lens); free(seg_of); return rc; }
+  for (int64_t s = 0; s < nseg; s++)
+    for (int64_t t = starts[s]; t < starts[s] + lens[s]; t++) seg_of[t] = s;
+  int64_t maxlen = 0;
+  for (int64_t s = 0; s < nseg; s++) if (lens[s] > maxlen) maxlen = lens[s];
+
+  double* qh = normed_operand(q, wq, T, H, eps);
+  double* kh = normed_operand(k, wk, T, H, eps);
+  if (!qh || !kh) { free(qh); free(kh); free(starts); free(lens); free(seg_of); return ORACLE_ERR_NOMEM; }
+
+  int64_t nq = rows ? n_rows : T;
+  for (int64_t r = 0; r < nq; r++)
+    if (rows && (rows[r] < 0 || rows[r] >= T)) { rc = ORACLE_ERR_ARGS; break; }
+  if (rc == ORACLE_OK) {
+    int64_t units = nq * (int64_t)H;
+#pragma omp parallel
+    {
+      double* scores = (double*)malloc((size_t)(maxlen > 0 ? maxlen : 1) * sizeof(double));
+#pragma omp for schedule(dynamic, 16)
+      for (int64_t u = 0; u < units; u++) {
+        int64_t r = u / H;
+        int h = (int)(u % H);
+        int64_t i = rows ? rows[r] : r;
+        int64_t s = seg_of[i];
+        double lse_val;
+        attend_one(qh, kh, v, H, h, i, starts[s], lens[s], scale, scores, out + (r * H + h) * HD, &lse_val);
+        if (lse) lse[r * H + h] = lse_val;
+      }
+      free(scores);
+    }
+  }
+  free(qh); free(kh); free(starts); free(lens); free(seg_of);
+  return rc;
+}
+
+/* Forward of the whole node: out [T,H,128] FP64, lse [T,H] FP64 (may be NULL).
+ * wq and wk both NULL means q and k are already normalised; exactly one NULL is an error. */
+int oracle_fwd(const uint16_t* q, const uint16_t* k, const uint16_t* v, const int32_t* seg, const uint16_t* wq,
+               const uint16_t* wk, int64_t T, int32_t H, double eps, double scale, double* out, double* lse) {
+  return fwd_impl(q, k, v, seg, wq, wk, T, H, eps, scale, NULL, 0, out, lse);
+}
+
+/* Forward for selected query tokens only (for sampling full-size workloads). */
+int oracle_fwd_rows(const uint16_t* q, const uint16_t* k, const uint16_t* v, const int32_t* seg, const uint16_t* wq,
+                    const uint16_t* wk, int64_t T, int32_t H, double eps, double scale, const int64_t* rows,
+                    int64_t n_rows, double* out, double* lse) {
+  if (n_rows < 0 || (n_rows > 0 && !rows)) return ORACLE_ERR_ARGS;
+  if (n_rows == 0) return ORACLE_OK;
+  return fwd_impl(q, k, v, seg, wq, wk, T, H, eps, scale, rows, n_rows, out, lse);
+}
