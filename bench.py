@@ -1,0 +1,158 @@
+"""Throughput of the H3 attention forward on one MI355X.
+
+One step = one h3attn_fwd call (segment plan, K norm + fp16 V staging, attention with the fused Q
+norm) over the full workload, inputs resident in HBM.  Prints ONE JSON line:
+  value     whole-step attention TFLOP/s (nominal 4 * sum(L^2) * H * 128 FLOPs per step)
+  roofline  the attention kernel alone (h3attn_attend), timed per launch with HIP events on the
+            launch stream, against the bf16/fp16 dense MFMA peak (2516.6 TFLOP/s)
+  cpu_baseline  the FP64 CPU oracle on a bounded sample of query rows of the same workload
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload long] [--no-cpu-baseline]
+"""
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "attention fwd TFLOP/s + % bf16 MFMA peak @8349 tok; bitwise batch-invariant"
+PEAK_MFMA_TFLOPS = 2516.6  # MI355X dense bf16/fp16 MFMA: 256 CU x 2.4 GHz x 4096 FLOP/clk
+PEAK_HBM_GBS = 8000.0
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="long")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=12.0, help="target oracle time of the CPU sample")
+    args = ap.parse_args()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print(f"bench.py measures one GPU only (asked for --gpus {args.gpus}, WORLD_SIZE {world}); "
+              "the attention node shards by head or packed row with no exchange, see the design notes",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import deterministic_invariant_attention_amd as h3
+    import workloads
+
+    wl = workloads.WORKLOADS[args.workload]
+    dev = torch.device("cuda:0")
+    x = workloads.make_inputs(wl)
+    g = {n: (t.to(dev) if t is not None else None) for n, t in x.items()}
+    T, H = wl.tokens, wl.heads
+    flops = wl.flops()
+    out = torch.empty_like(g["q"])
+    ws = h3.workspace(T, H, dev)
+    stream = torch.cuda.current_stream(dev)
+    log(f"workload {wl.name}: {wl.description}; nominal {flops:.4e} FLOP/step")
+
+    def step():
+        h3.h3attn_fwd(g["q"], g["k"], g["v"], g["seg"], g["wq"], g["wk"], eps=wl.eps, scale=wl.scale, out=out,
+                      workspace_buf=ws, stream=stream)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    ref_bits = out.view(torch.int16).clone()
+
+    # ---- timed region: K whole steps
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    e0.record(stream)
+    for _ in range(args.steps):
+        step()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    wall_ms = (time.perf_counter() - t0) * 1e3 / args.steps
+    ms_per_step = e0.elapsed_time(e1) / args.steps
+    repeat_bitwise = bool(torch.equal(out.view(torch.int16), ref_bits))
+    status = h3.h3attn_status_read(ws, stream)
+    value = flops / (ms_per_step * 1e-3) / 1e12
+    log(f"step: {ms_per_step:.4f} ms (wall {wall_ms:.4f} ms) -> {value:.1f} TFLOP/s; repeat bitwise {repeat_bitwise}; "
+        f"status {status}")
+
+    # ---- the dominant kernel alone: attention launches, one event pair each, on the launch stream
+    h3.h3attn_plan(g["seg"], H, ws, stream=stream)
+    h3.h3attn_prep_kv(g["k"], g["v"], g["wk"], ws, eps=wl.eps, stream=stream)
+    for _ in range(2):
+        h3.h3attn_attend(g["q"], g["wq"], ws, out, eps=wl.eps, scale=wl.scale, stream=stream)
+    torch.cuda.synchronize()
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
+    for a, b in evs:
+        a.record(stream)
+        h3.h3attn_attend(g["q"], g["wq"], ws, out, eps=wl.eps, scale=wl.scale, stream=stream)
+        b.record(stream)
+    torch.cuda.synchronize()
+    kms = [a.elapsed_time(b) for a, b in evs]
+    attn_ms = float(np.mean(kms))
+    attn_tflops = flops / (attn_ms * 1e-3) / 1e12
+    log(f"attention kernel: mean {attn_ms:.4f} ms, median {np.median(kms):.4f} ms -> {attn_tflops:.1f} TFLOP/s "
+        f"({100 * attn_tflops / PEAK_MFMA_TFLOPS:.1f}% of bf16 MFMA peak)")
+
+    # ---- CPU baseline: the FP64 oracle on a bounded sample of query rows (rank 0, N = 1)
+    cpu = None
+    if not args.no_cpu_baseline:
+        import oracle
+        seg_np = x["seg"].numpy()
+        rng = np.random.default_rng(0)
+        L = max(wl.seg_lens)
+
+        def run_rows(n):
+            rows = np.sort(rng.choice(T, size=n, replace=False))
+            t1 = time.perf_counter()
+            oracle.fwd_rows(x["q"], x["k"], x["v"], seg_np, rows, x["wq"], x["wk"], wl.eps, wl.scale)
+            return rows, time.perf_counter() - t1
+
+        rows, dt = run_rows(min(32, T))
+        n = int(min(T, max(32, len(rows) * args.cpu_seconds / max(dt, 1e-3))))
+        rows, dt = run_rows(n)
+        starts, lens = oracle.segments(seg_np)
+        seg_len = np.repeat(lens, lens)
+        sample_flops = float(4.0 * np.sum(seg_len[rows]) * H * 128)
+        cpu = {"value": round(sample_flops / dt / 1e12, 6), "unit": "TFLOP/s", "cores": oracle.num_threads(),
+               "kind": "oracle",
+               "sample": f"{len(rows)} of {T} query rows x {H} heads of the {wl.name} workload "
+                         f"(segment length {L}); {dt:.1f} s FP64"}
+        log(f"cpu baseline: {cpu}")
+
+    line = {
+        "metric": METRIC,
+        "value": round(value, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": wl.name, "tokens": T, "heads": H, "head_dim": 128, "segments": list(wl.seg_lens),
+                   "qk_draw_scale": wl.qk_scale, "pv_operands": "fp16", "accumulate": "fp32",
+                   "pct_bf16_mfma_peak": round(100 * value / PEAK_MFMA_TFLOPS, 2),
+                   "repeat_bitwise": repeat_bitwise, "device_status": status},
+        "roofline": {"bound": "mfma", "achieved": round(attn_tflops, 2), "peak": PEAK_MFMA_TFLOPS,
+                     "unit": "TFLOP/s", "frac": round(attn_tflops / PEAK_MFMA_TFLOPS, 4), "traffic": None,
+                     "kernel": "k_attn_fwd", "kernel_ms": round(attn_ms, 4)},
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,172 @@
+"""Deterministic, batch-invariant H3 full attention for MI355X (gfx950).
+
+A thin ctypes binding of ``libh3attn.so`` (C ABI in ``include/h3attn.h``).  The functions keep the
+C names and only marshal arguments: torch provides device memory and the stream, every step of the
+computation runs in the library's HIP kernels.  There is no other code path: if the library is not
+built, or the tensors are not on a gfx950 device, the calls raise.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "lib", "libh3attn.so")
+HEAD_DIM = 128
+
+H3ATTN_OK = 0
+H3ATTN_ERR_NULL = 1
+H3ATTN_ERR_SHAPE = 2
+H3ATTN_ERR_ALIGN = 3
+H3ATTN_ERR_ALIAS = 4
+H3ATTN_ERR_WORKSPACE = 5
+H3ATTN_ERR_DEVICE = 6
+H3ATTN_ERR_LAUNCH = 7
+H3ATTN_ERR_SEGMENTS = 8
+H3ATTN_ERR_RANGE = 9
+
+# every symbol the header declares
+EXPORTS = ("h3attn_version", "h3attn_strerror", "h3attn_workspace_bytes", "h3attn_qknorm", "h3attn_fwd",
+           "h3attn_plan", "h3attn_prep_kv", "h3attn_attend", "h3attn_status_read")
+
+
+class H3AttnError(RuntimeError):
+    def __init__(self, code: int, where: str):
+        self.code = code
+        super().__init__(f"{where}: {h3attn_strerror(code)} (status {code})")
+
+
+_lib = None
+
+
+def load():
+    """Load libh3attn.so (built in-tree by __graft_entry__.build()); raises if it is missing."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise RuntimeError(f"{LIB_PATH} is not built; run `python -c 'import __graft_entry__ as g; g.build()'`")
+    lib = ctypes.CDLL(LIB_PATH)
+    P, I64, I32, F, SZ = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32, ctypes.c_float, ctypes.c_size_t
+    lib.h3attn_version.restype = ctypes.c_int
+    lib.h3attn_strerror.argtypes = [ctypes.c_int]
+    lib.h3attn_strerror.restype = ctypes.c_char_p
+    lib.h3attn_workspace_bytes.argtypes = [I64, I32]
+    lib.h3attn_workspace_bytes.restype = SZ
+    lib.h3attn_qknorm.argtypes = [P, P, P, I64, I32, I32, F, P]
+    lib.h3attn_fwd.argtypes = [P, P, P, P, P, P, I64, I32, I32, F, F, P, P, P, SZ, P]
+    lib.h3attn_plan.argtypes = [P, I64, I32, P, SZ, P]
+    lib.h3attn_prep_kv.argtypes = [P, P, P, I64, I32, I32, F, P, SZ, P]
+    lib.h3attn_attend.argtypes = [P, P, I64, I32, I32, F, F, P, P, P, SZ, P]
+    lib.h3attn_status_read.argtypes = [P, ctypes.POINTER(ctypes.c_int32), P]
+    for name in ("h3attn_qknorm", "h3attn_fwd", "h3attn_plan", "h3attn_prep_kv", "h3attn_attend",
+                 "h3attn_status_read"):
+        getattr(lib, name).restype = ctypes.c_int
+    _lib = lib
+    return lib
+
+
+def _ptr(t):
+    return None if t is None else t.data_ptr()
+
+
+def _stream(stream, device):
+    if stream is None:
+        stream = torch.cuda.current_stream(device)
+    return stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream)
+
+
+def _check(rc: int, where: str):
+    if rc != H3ATTN_OK:
+        raise H3AttnError(rc, where)
+
+
+def _shape(q):
+    if q.dim() != 3:
+        raise H3AttnError(H3ATTN_ERR_SHAPE, "expected [tokens, heads, head_dim]")
+    return q.shape[0], q.shape[1], q.shape[2]
+
+
+def _bf16(t, name):
+    if t is not None and (t.dtype != torch.bfloat16 or not t.is_contiguous()):
+        raise TypeError(f"{name} must be a contiguous bfloat16 tensor")
+    return t
+
+
+def h3attn_version() -> int:
+    return load().h3attn_version()
+
+
+def h3attn_strerror(code: int) -> str:
+    return load().h3attn_strerror(int(code)).decode()
+
+
+def h3attn_workspace_bytes(tokens: int, heads: int) -> int:
+    return load().h3attn_workspace_bytes(int(tokens), int(heads))
+
+
+def workspace(tokens: int, heads: int, device) -> torch.Tensor:
+    """A device buffer of h3attn_workspace_bytes(tokens, heads) bytes (torch's allocator is 256-B aligned)."""
+    n = h3attn_workspace_bytes(tokens, heads)
+    return torch.empty(max(n, 256), dtype=torch.uint8, device=device)
+
+
+def h3attn_qknorm(x, w, eps: float = 1e-6, out=None, stream=None):
+    """RMSNorm of every 128-wide (token, head) row of x [T, H, 128] with weight w [128]; returns y."""
+    _bf16(x, "x"), _bf16(w, "w")
+    T, H, D = _shape(x)
+    y = torch.empty_like(x) if out is None else _bf16(out, "out")
+    rc = load().h3attn_qknorm(_ptr(x), _ptr(w), _ptr(y), T, H, D, float(eps), _stream(stream, x.device))
+    _check(rc, "h3attn_qknorm")
+    return y
+
+
+def h3attn_fwd(q, k, v, seg_ids, wq=None, wk=None, eps: float = 1e-6, scale: float | None = None, out=None,
+               lse=None, workspace_buf=None, stream=None, want_lse: bool = False):
+    """Forward of the attention node with its fused q/k norm.  Returns (out, lse) (lse None unless asked)."""
+    for t, n in ((q, "q"), (k, "k"), (v, "v"), (wq, "wq"), (wk, "wk")):
+        _bf16(t, n)
+    if seg_ids.dtype != torch.int32 or not seg_ids.is_contiguous():
+        raise TypeError("seg_ids must be a contiguous int32 tensor")
+    T, H, D = _shape(q)
+    scale = D ** -0.5 if scale is None else scale
+    out = torch.empty_like(q) if out is None else _bf16(out, "out")
+    if lse is None and want_lse:
+        lse = torch.empty((T, H), dtype=torch.float32, device=q.device)
+    ws = workspace(T, H, q.device) if workspace_buf is None else workspace_buf
+    rc = load().h3attn_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(seg_ids), _ptr(wq), _ptr(wk), T, H, D, float(eps),
+                           float(scale), _ptr(out), _ptr(lse), _ptr(ws), ws.numel(), _stream(stream, q.device))
+    _check(rc, "h3attn_fwd")
+    return out, lse
+
+
+def h3attn_plan(seg_ids, heads: int, workspace_buf, stream=None):
+    T = seg_ids.shape[0]
+    rc = load().h3attn_plan(_ptr(seg_ids), T, int(heads), _ptr(workspace_buf), workspace_buf.numel(),
+                            _stream(stream, seg_ids.device))
+    _check(rc, "h3attn_plan")
+
+
+def h3attn_prep_kv(k, v, wk, workspace_buf, eps: float = 1e-6, stream=None):
+    T, H, D = _shape(k)
+    rc = load().h3attn_prep_kv(_ptr(k), _ptr(v), _ptr(wk), T, H, D, float(eps), _ptr(workspace_buf),
+                               workspace_buf.numel(), _stream(stream, k.device))
+    _check(rc, "h3attn_prep_kv")
+
+
+def h3attn_attend(q, wq, workspace_buf, out, lse=None, eps: float = 1e-6, scale: float | None = None, stream=None):
+    T, H, D = _shape(q)
+    scale = D ** -0.5 if scale is None else scale
+    rc = load().h3attn_attend(_ptr(q), _ptr(wq), T, H, D, float(eps), float(scale), _ptr(out), _ptr(lse),
+                              _ptr(workspace_buf), workspace_buf.numel(), _stream(stream, q.device))
+    _check(rc, "h3attn_attend")
+    return out
+
+
+def h3attn_status_read(workspace_buf, stream=None) -> int:
+    st = ctypes.c_int32(-1)
+    rc = load().h3attn_status_read(_ptr(workspace_buf), ctypes.byref(st), _stream(stream, workspace_buf.device))
+    _check(rc, "h3attn_status_read")
+    return st.value

@@ -1,0 +1,240 @@
+// C ABI of libh3attn (declared and documented in include/h3attn.h): argument checks, workspace
+// carve-up and kernel launches.  Strict mode of the H3 pages ("33B forward/backward" page, Scope):
+// unsupported shapes, dtypes and devices raise instead of falling back -- every check below returns
+// an error before anything is enqueued, and there is no other code path.
+#include <hip/hip_runtime.h>
+
+#include <atomic>
+#include <cmath>
+#include <cstring>
+#include <mutex>
+
+#include "h3_common.h"
+#include "h3_launch.h"
+#include "h3attn.h"
+
+namespace {
+
+using namespace h3;
+
+constexpr int kMaxDevices = 64;
+
+struct DeviceInfo {
+  bool ok = false;
+  int cus = 0;
+};
+
+std::once_flag g_once[kMaxDevices];
+DeviceInfo g_info[kMaxDevices];
+
+// Current device must be gfx950.  The properties are read once per device and cached.
+int device_info(DeviceInfo* out) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) {
+    (void)hipGetLastError();
+    return H3ATTN_ERR_DEVICE;
+  }
+  std::call_once(g_once[dev], [dev] {
+    hipDeviceProp_t prop;
+    if (hipGetDeviceProperties(&prop, dev) != hipSuccess) {
+      (void)hipGetLastError();
+      return;
+    }
+    g_info[dev].ok = std::strncmp(prop.gcnArchName, "gfx950", 6) == 0;
+    g_info[dev].cus = prop.multiProcessorCount;
+  });
+  if (!g_info[dev].ok) return H3ATTN_ERR_DEVICE;
+  *out = g_info[dev];
+  return H3ATTN_OK;
+}
+
+bool aligned(const void* p, size_t a) { return ((uintptr_t)p % a) == 0; }
+
+bool overlap(const void* a, size_t na, const void* b, size_t nb) {
+  if (!a || !b || na == 0 || nb == 0) return false;
+  const uintptr_t x = (uintptr_t)a, y = (uintptr_t)b;
+  return x < y + nb && y < x + na;
+}
+
+// Shape checks shared by every entry point; also bounds the index arithmetic of the kernels.
+int check_shape(int64_t T, int32_t H, int32_t D) {
+  if (T < 0 || H < 1 || D != HD) return H3ATTN_ERR_SHAPE;
+  if (T > ((int64_t)1 << 28)) return H3ATTN_ERR_SHAPE;  // keeps every int32 index product of the kernels in range
+  const int64_t max_items = T + (T + BQ - 1) / BQ;
+  if (max_items * (int64_t)H > (int64_t)INT32_MAX) return H3ATTN_ERR_SHAPE;
+  if ((T * H * 16 + 255) / 256 > (int64_t)INT32_MAX) return H3ATTN_ERR_SHAPE;
+  return H3ATTN_OK;
+}
+
+int launch_status(hipError_t e) {
+  if (e != hipSuccess) {
+    (void)hipGetLastError();
+    return H3ATTN_ERR_LAUNCH;
+  }
+  return H3ATTN_OK;
+}
+
+size_t tensor_bytes(int64_t T, int32_t H) { return (size_t)T * (size_t)H * HD * 2; }
+
+}  // namespace
+
+extern "C" {
+
+int h3attn_version(void) { return H3ATTN_VERSION; }
+
+const char* h3attn_strerror(int status) {
+  switch (status) {
+    case H3ATTN_OK: return "ok";
+    case H3ATTN_ERR_NULL: return "a required pointer is NULL (or exactly one of wq/wk is NULL)";
+    case H3ATTN_ERR_SHAPE: return "unsupported shape (tokens < 0, heads < 1, head_dim != 128, or too large)";
+    case H3ATTN_ERR_ALIGN: return "misaligned buffer (tensors 16 B, seg_ids/lse 4 B, workspace 256 B)";
+    case H3ATTN_ERR_ALIAS: return "an output overlaps an input or the workspace";
+    case H3ATTN_ERR_WORKSPACE: return "workspace too small";
+    case H3ATTN_ERR_DEVICE: return "no current device or it is not gfx950 (MI355X)";
+    case H3ATTN_ERR_LAUNCH: return "the HIP runtime rejected a launch or copy";
+    case H3ATTN_ERR_SEGMENTS: return "segment ids decrease (device status)";
+    case H3ATTN_ERR_RANGE: return "a finite |v| > 65504 cannot enter the fp16 P.V product (device status)";
+    default: return "unknown status";
+  }
+}
+
+size_t h3attn_workspace_bytes(int64_t tokens, int32_t heads) {
+  if (check_shape(tokens, heads, HD) != H3ATTN_OK) return 0;
+  return ws_layout(tokens, heads).total;
+}
+
+int h3attn_qknorm(const void* x, const void* w, void* y, int64_t tokens, int32_t heads, int32_t head_dim, float eps,
+                  void* stream) {
+  int rc = check_shape(tokens, heads, head_dim);
+  if (rc) return rc;
+  if (!(eps > 0.0f) || !std::isfinite(eps)) return H3ATTN_ERR_SHAPE;
+  if (tokens == 0) return H3ATTN_OK;
+  if (!x || !w || !y) return H3ATTN_ERR_NULL;
+  if (!aligned(x, 16) || !aligned(w, 16) || !aligned(y, 16)) return H3ATTN_ERR_ALIGN;
+  const size_t n = tensor_bytes(tokens, heads);
+  if (x != y && overlap(x, n, y, n)) return H3ATTN_ERR_ALIAS;
+  if (overlap(w, HD * 2, y, n)) return H3ATTN_ERR_ALIAS;
+  DeviceInfo di;
+  if ((rc = device_info(&di))) return rc;
+  return launch_status(launch_qknorm(x, w, y, tokens, heads, eps, (hipStream_t)stream));
+}
+
+// ---- argument checks of the three stages (no device access; nothing is enqueued)
+
+static int check_plan(const int32_t* seg_ids, int64_t tokens, int32_t heads, void* workspace, size_t workspace_bytes) {
+  if (!seg_ids || !workspace) return H3ATTN_ERR_NULL;
+  if (!aligned(seg_ids, 4) || !aligned(workspace, 256)) return H3ATTN_ERR_ALIGN;
+  if (overlap(seg_ids, (size_t)tokens * 4, workspace, workspace_bytes)) return H3ATTN_ERR_ALIAS;
+  if (workspace_bytes < ws_layout(tokens, heads).total) return H3ATTN_ERR_WORKSPACE;
+  return H3ATTN_OK;
+}
+
+static int check_prep(const void* k, const void* v, const void* wk, int64_t tokens, int32_t heads, float eps,
+                      void* workspace, size_t workspace_bytes) {
+  if (wk && (!(eps > 0.0f) || !std::isfinite(eps))) return H3ATTN_ERR_SHAPE;
+  if (!k || !v || !workspace) return H3ATTN_ERR_NULL;
+  if (!aligned(k, 16) || !aligned(v, 16) || (wk && !aligned(wk, 16)) || !aligned(workspace, 256))
+    return H3ATTN_ERR_ALIGN;
+  const size_t n = tensor_bytes(tokens, heads);
+  if (overlap(k, n, workspace, workspace_bytes) || overlap(v, n, workspace, workspace_bytes) ||
+      overlap(wk, HD * 2, workspace, workspace_bytes))
+    return H3ATTN_ERR_ALIAS;
+  if (workspace_bytes < ws_layout(tokens, heads).total) return H3ATTN_ERR_WORKSPACE;
+  return H3ATTN_OK;
+}
+
+static int check_attend(const void* q, const void* wq, int64_t tokens, int32_t heads, float eps, float scale,
+                        void* out, float* lse, void* workspace, size_t workspace_bytes) {
+  if (wq && (!(eps > 0.0f) || !std::isfinite(eps))) return H3ATTN_ERR_SHAPE;
+  if (!(scale > 0.0f) || !std::isfinite(scale)) return H3ATTN_ERR_SHAPE;
+  if (!q || !out || !workspace) return H3ATTN_ERR_NULL;
+  if (!aligned(q, 16) || (wq && !aligned(wq, 16)) || !aligned(out, 16) || (lse && !aligned(lse, 4)) ||
+      !aligned(workspace, 256))
+    return H3ATTN_ERR_ALIGN;
+  const size_t n = tensor_bytes(tokens, heads);
+  const size_t nl = (size_t)tokens * heads * 4;
+  if (overlap(out, n, q, n) || overlap(out, n, wq, HD * 2) || overlap(out, n, workspace, workspace_bytes) ||
+      overlap(out, n, lse, nl) || overlap(lse, nl, q, n) || overlap(lse, nl, wq, HD * 2) ||
+      overlap(lse, nl, workspace, workspace_bytes))
+    return H3ATTN_ERR_ALIAS;
+  if (workspace_bytes < ws_layout(tokens, heads).total) return H3ATTN_ERR_WORKSPACE;
+  return H3ATTN_OK;
+}
+
+int h3attn_plan(const int32_t* seg_ids, int64_t tokens, int32_t heads, void* workspace, size_t workspace_bytes,
+                void* stream) {
+  int rc = check_shape(tokens, heads, HD);
+  if (rc) return rc;
+  if (tokens == 0) return H3ATTN_OK;
+  if ((rc = check_plan(seg_ids, tokens, heads, workspace, workspace_bytes))) return rc;
+  DeviceInfo di;
+  if ((rc = device_info(&di))) return rc;
+  return launch_status(launch_plan(seg_ids, tokens, workspace, heads, (hipStream_t)stream));
+}
+
+int h3attn_prep_kv(const void* k, const void* v, const void* wk, int64_t tokens, int32_t heads, int32_t head_dim,
+                   float eps, void* workspace, size_t workspace_bytes, void* stream) {
+  int rc = check_shape(tokens, heads, head_dim);
+  if (rc) return rc;
+  if (tokens == 0) return H3ATTN_OK;
+  if ((rc = check_prep(k, v, wk, tokens, heads, eps, workspace, workspace_bytes))) return rc;
+  DeviceInfo di;
+  if ((rc = device_info(&di))) return rc;
+  return launch_status(launch_prep_kv(k, v, wk, tokens, heads, eps, workspace, (hipStream_t)stream));
+}
+
+int h3attn_attend(const void* q, const void* wq, int64_t tokens, int32_t heads, int32_t head_dim, float eps,
+                  float scale, void* out, float* lse, void* workspace, size_t workspace_bytes, void* stream) {
+  int rc = check_shape(tokens, heads, head_dim);
+  if (rc) return rc;
+  if (tokens == 0) return (!(scale > 0.0f) || !std::isfinite(scale)) ? H3ATTN_ERR_SHAPE : H3ATTN_OK;
+  if ((rc = check_attend(q, wq, tokens, heads, eps, scale, out, lse, workspace, workspace_bytes))) return rc;
+  DeviceInfo di;
+  if ((rc = device_info(&di))) return rc;
+  return launch_status(
+      launch_attend(q, wq, tokens, heads, eps, scale, out, lse, workspace, 2 * di.cus, (hipStream_t)stream));
+}
+
+int h3attn_fwd(const void* q, const void* k, const void* v, const int32_t* seg_ids, const void* wq, const void* wk,
+               int64_t tokens, int32_t heads, int32_t head_dim, float eps, float scale, void* out, float* lse,
+               void* workspace, size_t workspace_bytes, void* stream) {
+  int rc = check_shape(tokens, heads, head_dim);
+  if (rc) return rc;
+  if ((wq == nullptr) != (wk == nullptr)) return H3ATTN_ERR_NULL;
+  if (wq && (!(eps > 0.0f) || !std::isfinite(eps))) return H3ATTN_ERR_SHAPE;
+  if (!(scale > 0.0f) || !std::isfinite(scale)) return H3ATTN_ERR_SHAPE;
+  if (tokens == 0) return H3ATTN_OK;
+  if (!q || !k || !v || !seg_ids || !out || !workspace) return H3ATTN_ERR_NULL;
+  if ((rc = check_plan(seg_ids, tokens, heads, workspace, workspace_bytes))) return rc;
+  if ((rc = check_prep(k, v, wk, tokens, heads, eps, workspace, workspace_bytes))) return rc;
+  if ((rc = check_attend(q, wq, tokens, heads, eps, scale, out, lse, workspace, workspace_bytes))) return rc;
+  const size_t n = tensor_bytes(tokens, heads);
+  const size_t nl = (size_t)tokens * heads * 4;
+  const size_t ns = (size_t)tokens * 4;
+  if (overlap(out, n, k, n) || overlap(out, n, v, n) || overlap(out, n, seg_ids, ns) ||
+      overlap(out, n, wk, HD * 2) || overlap(lse, nl, k, n) || overlap(lse, nl, v, n) ||
+      overlap(lse, nl, seg_ids, ns) || overlap(lse, nl, wk, HD * 2))
+    return H3ATTN_ERR_ALIAS;
+  DeviceInfo di;
+  if ((rc = device_info(&di))) return rc;
+  hipStream_t st = (hipStream_t)stream;
+  if ((rc = launch_status(launch_plan(seg_ids, tokens, workspace, heads, st)))) return rc;
+  if ((rc = launch_status(launch_prep_kv(k, v, wk, tokens, heads, eps, workspace, st)))) return rc;
+  return launch_status(launch_attend(q, wq, tokens, heads, eps, scale, out, lse, workspace, 2 * di.cus, st));
+}
+
+int h3attn_status_read(const void* workspace, int32_t* device_status, void* stream) {
+  if (!workspace || !device_status) return H3ATTN_ERR_NULL;
+  if (!aligned(workspace, 256)) return H3ATTN_ERR_ALIGN;
+  int32_t bits = 0;
+  hipStream_t st = (hipStream_t)stream;
+  if (hipMemcpyAsync(&bits, workspace, sizeof(bits), hipMemcpyDeviceToHost, st) != hipSuccess ||
+      hipStreamSynchronize(st) != hipSuccess) {
+    (void)hipGetLastError();
+    return H3ATTN_ERR_LAUNCH;
+  }
+  *device_status = (bits & STATUS_SEG_BIT) ? H3ATTN_ERR_SEGMENTS : (bits & STATUS_RANGE_BIT) ? H3ATTN_ERR_RANGE : H3ATTN_OK;
+  return H3ATTN_OK;
+}
+
+}  // extern "C"

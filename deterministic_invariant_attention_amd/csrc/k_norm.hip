@@ -1,0 +1,101 @@
+// The q_norm / k_norm node (RMSNorm over each 128-wide head, one 128-element weight shared by all
+// heads: "ws1_one_h3_block" page, Bindings table and Results) as a standalone kernel, and the K/V
+// staging kernel of the attention: K normed with the same arithmetic, V converted to fp16.
+//
+// Mapping: 16 lanes per (token, head) row, lane c holds channels 8c..8c+7 (one 16-byte chunk), so
+// each wave moves 4 rows with fully coalesced 16-byte accesses.  The sum of squares follows the
+// fixed tree of h3_common.h, so these kernels and the attention's fused Q prologue (2 lanes per
+// row) give identical bits.
+#include "h3_common.h"
+#include "h3_launch.h"
+
+namespace h3 {
+
+__device__ __forceinline__ u32x4 ld16(const uint16_t* p) { return *(const u32x4*)p; }
+__device__ __forceinline__ void st16(uint16_t* p, const u32x4& v) { *(u32x4*)p = v; }
+
+// Norm one row chunk held by this lane (16-lane mapping); every lane of the group must call it.
+__device__ __forceinline__ u32x4 norm_16lane(const u32x4& xv, const uint16_t* w, int c, float eps) {
+  float x[8], wf[8];
+  unpack8_bf16(xv, x);
+  const double total = row_total_16lanes(chunk_sumsq(x));
+  const double r = norm_rscale(total, eps);
+  unpack8_bf16(ld16(w + c * 8), wf);
+  return norm_chunk(x, wf, r);
+}
+
+__global__ __launch_bounds__(256) void k_qknorm(const uint16_t* x, const uint16_t* __restrict__ w, uint16_t* y,
+                                               int64_t rows, float eps) {
+  const int64_t g = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  const int64_t row = g >> 4;
+  const int c = threadIdx.x & 15;
+  const bool valid = row < rows;  // uniform over each 16-lane group
+  u32x4 xv = {0, 0, 0, 0};
+  if (valid) xv = ld16(x + row * HD + c * 8);
+  const u32x4 o = norm_16lane(xv, w, c, eps);
+  if (valid) st16(y + row * HD + c * 8, o);
+}
+
+// rows are visited token-major (r = t*H + h) so the reads are contiguous; each row is written to
+// its head-major slot (h*T + t).
+__global__ __launch_bounds__(256) void k_prep_kv(const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
+                                                const uint16_t* __restrict__ wk, uint16_t* __restrict__ khat,
+                                                uint16_t* __restrict__ v16, int64_t T, int32_t H, float eps,
+                                                WsHeader* hdr) {
+  const int64_t g = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  const int64_t row = g >> 4;
+  const int c = threadIdx.x & 15;
+  const int64_t rows = T * H;
+  const bool valid = row < rows;
+  const int64_t t = valid ? row / H : 0;
+  const int64_t h = valid ? row - t * H : 0;
+  const int64_t dst = (h * T + t) * HD + c * 8;
+
+  u32x4 kv = {0, 0, 0, 0}, vv = {0, 0, 0, 0};
+  if (valid) {
+    kv = ld16(k + row * HD + c * 8);
+    vv = ld16(v + row * HD + c * 8);
+  }
+  const u32x4 ko = wk ? norm_16lane(kv, wk, c, eps) : kv;
+
+  // V: bf16 -> fp16, exact for normal fp16 magnitudes; a finite |v| > 65504 would overflow.
+  u32x4 vo;
+  bool over = false;
+#pragma unroll
+  for (int i = 0; i < 4; i++) {
+    const float a = bf16_lo(vv[i]), b = bf16_hi(vv[i]);
+    over |= (__builtin_fabsf(a) > 65504.0f && __builtin_fabsf(a) != __builtin_inff());
+    over |= (__builtin_fabsf(b) > 65504.0f && __builtin_fabsf(b) != __builtin_inff());
+    vo[i] = pack_f16(a, b);
+  }
+  if (valid) {
+    st16(khat + dst, ko);
+    st16(v16 + dst, vo);
+  }
+  const uint64_t any_over = __ballot(valid && over);
+  if (any_over && (threadIdx.x & 63) == __builtin_ctzll(any_over)) atomicOr(&hdr->status, STATUS_RANGE_BIT);
+}
+
+static inline unsigned grid_for_rows(int64_t rows) { return (unsigned)((rows * 16 + 255) / 256); }
+
+hipError_t launch_qknorm(const void* x, const void* w, void* y, int64_t T, int32_t H, float eps, hipStream_t stream) {
+  const int64_t rows = T * H;
+  if (rows == 0) return hipSuccess;
+  hipLaunchKernelGGL(k_qknorm, dim3(grid_for_rows(rows)), dim3(256), 0, stream, (const uint16_t*)x,
+                     (const uint16_t*)w, (uint16_t*)y, rows, eps);
+  return hipGetLastError();
+}
+
+hipError_t launch_prep_kv(const void* k, const void* v, const void* wk, int64_t T, int32_t H, float eps, void* ws,
+                          hipStream_t stream) {
+  const int64_t rows = T * H;
+  if (rows == 0) return hipSuccess;
+  const WsLayout L = ws_layout(T, H);
+  char* base = (char*)ws;
+  hipLaunchKernelGGL(k_prep_kv, dim3(grid_for_rows(rows)), dim3(256), 0, stream, (const uint16_t*)k,
+                     (const uint16_t*)v, (const uint16_t*)wk, (uint16_t*)(base + L.khat), (uint16_t*)(base + L.v16),
+                     T, H, eps, (WsHeader*)base);
+  return hipGetLastError();
+}
+
+}  // namespace h3

@@ -1,0 +1,106 @@
+// Segment decode: per-token int32 segment ids -> segment table (start, length) and the list of
+// (segment, q-tile) attention work items, plus the status word.
+//
+// Packed layouts ("ws1_one_h3_block" page, Summary: several sequences share one token axis) are
+// described to the library by one id per token; a segment is a maximal run of equal ids, and ids
+// must not decrease.  The decode runs in one 1024-thread workgroup: three passes of block-wide
+// exclusive scans over tokens, then segments.  Its cost is T/1024 scan steps, negligible next to
+// the attention for the workloads served here.
+#include "h3_common.h"
+#include "h3_launch.h"
+
+namespace h3 {
+
+// Exclusive scan of one int per thread over a 1024-thread block; also returns the block total.
+__device__ __forceinline__ int block_excl_scan(int v, int* lds_wave, int& total) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  int x = v;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const int y = __shfl_up(x, o, 64);
+    if (lane >= o) x += y;
+  }
+  if (lane == 63) lds_wave[wave] = x;
+  __syncthreads();
+  int before = 0, all = 0;
+#pragma unroll
+  for (int w = 0; w < 16; w++) {
+    const int s = lds_wave[w];
+    before += (w < wave) ? s : 0;
+    all += s;
+  }
+  __syncthreads();
+  total = all;
+  return before + x - v;
+}
+
+__global__ __launch_bounds__(1024) void k_plan(const int32_t* __restrict__ seg, int64_t T, WsHeader* hdr,
+                                              int32_t* __restrict__ segtab, int32_t* __restrict__ items) {
+  __shared__ int lds_wave[16];
+  __shared__ int s_bad;
+  const int tid = threadIdx.x;
+  if (tid == 0) s_bad = 0;
+  __syncthreads();
+
+  // pass 1: segment starts at every token whose id differs from its predecessor's
+  int nseg = 0, bad = 0;
+  for (int64_t base = 0; base < T; base += 1024) {
+    const int64_t t = base + tid;
+    int flag = 0;
+    if (t < T) {
+      const int32_t cur = seg[t];
+      if (t == 0) {
+        flag = 1;
+      } else {
+        const int32_t prev = seg[t - 1];
+        flag = cur != prev;
+        bad |= cur < prev;
+      }
+    }
+    int total;
+    const int pos = block_excl_scan(flag, lds_wave, total);
+    if (flag) segtab[2 * (nseg + pos)] = (int32_t)t;
+    nseg += total;
+  }
+  if (bad) atomicOr(&s_bad, 1);
+  __syncthreads();
+
+  // pass 2: lengths
+  for (int s = tid; s < nseg; s += 1024) {
+    const int32_t st = segtab[2 * s];
+    const int32_t en = (s + 1 < nseg) ? segtab[2 * (s + 1)] : (int32_t)T;
+    segtab[2 * s + 1] = en - st;
+  }
+  __syncthreads();
+
+  // pass 3: work items, ceil(L / BQ) q-tiles per segment, in segment order
+  int nitems = 0;
+  for (int base = 0; base < nseg; base += 1024) {
+    const int s = base + tid;
+    const int nt = (s < nseg) ? (segtab[2 * s + 1] + BQ - 1) / BQ : 0;
+    int total;
+    const int off = block_excl_scan(nt, lds_wave, total);
+    for (int j = 0; j < nt; j++) {
+      items[2 * (nitems + off + j)] = s;
+      items[2 * (nitems + off + j) + 1] = j;
+    }
+    nitems += total;
+  }
+
+  if (tid == 0) {
+    const int b = s_bad;
+    hdr->nseg = b ? 0 : nseg;
+    hdr->nitems = b ? 0 : nitems;
+    hdr->status = b ? STATUS_SEG_BIT : 0;
+  }
+}
+
+hipError_t launch_plan(const int32_t* seg, int64_t T, void* ws, int32_t H, hipStream_t stream) {
+  const WsLayout L = ws_layout(T, H);
+  char* base = (char*)ws;
+  hipLaunchKernelGGL(k_plan, dim3(1), dim3(1024), 0, stream, seg, T, (WsHeader*)base, (int32_t*)(base + L.segtab),
+                     (int32_t*)(base + L.items));
+  return hipGetLastError();
+}
+
+}  // namespace h3

@@ -1,0 +1,120 @@
+/*
+ * h3attn -- deterministic, batch-invariant full attention of the MiniMax-H3 block with its fused
+ * per-head q/k RMSNorm, for AMD Instinct MI355X (gfx950).  C ABI of libh3attn.so.
+ *
+ * The operation (RL-Kernel MiniMax-H3 pull-request pages):
+ *   - "ws1_one_h3_block + full-model qualification", Bindings table: q_norm/k_norm is an RMSNorm over
+ *     each 128-wide head (bitwise nn.RMSNorm semantics), then attention with causal=False;
+ *     Results: the norm weight is one 128-element tensor shared by all heads; Summary: sequences are
+ *     packed on one token axis, and a token attends only to its own sequence.
+ *   - "33B forward/backward and rollout-vs-train control", Scope (strict mode): no fast-math, no
+ *     split-K, FP32 accumulation with one final rounding; unsupported shapes, dtypes and devices
+ *     raise instead of falling back.
+ *   - same page, dual-trajectory results: a row must give the same bits whether it runs alone
+ *     (rollout) or inside a batch (training).
+ *
+ * Definitions used by every entry point below:
+ *   T = tokens >= 0, H = heads >= 1, head_dim must be 128.
+ *   q, k, v, out: bf16 [T, H, 128], contiguous, token-major (element (t, h, d) at (t*H + h)*128 + d).
+ *   seg_ids: int32 [T], non-decreasing; a segment is a maximal run of equal ids.  Every token attends
+ *     to all tokens of its own segment (non-causal) and to nothing else.  A batch of packed rows is
+ *     the concatenation of the rows with distinct ids at row boundaries.
+ *   wq, wk: bf16 [128] RMSNorm weights.  Norm of one (token, head) row x, evaluated in FP64 because
+ *     its bf16 output is a rounding decision: ms = (sum_d x_d^2) / 128 summed in a fixed tree,
+ *     r = 1 / sqrt(ms + eps) (correctly rounded sqrt and division), y_d = (x_d * r) * w_d, then ONE
+ *     round-to-nearest-even from FP64 to bf16.  The normed q and k enter Q.K^T as bf16.
+ *   Attention: S = scale * Qn.Kn^T in FP32 (bf16 MFMA, FP32 accumulate); an online softmax over the
+ *     segment's keys in fixed 64-key tiles, walked in ascending order from the segment's first key;
+ *     O = (sum_j p_ij v_j) / l_i, rounded once to bf16.  P.V runs on fp16 MFMA with V converted
+ *     exactly to fp16 (bf16 P would miss the accuracy bound; see the design notes).
+ *   lse (optional, may be NULL): fp32 [T, H], natural-log log-sum-exp of each row's scaled scores.
+ *   Determinism: every output row is a function of its own segment's bytes, the weights, eps and
+ *     scale only -- not of the batch, the segment's offset in the batch, neighbouring segments,
+ *     the grid size or occupancy.  Repeated calls give identical bits.
+ *
+ * Ownership and threading: the caller allocates every buffer (device memory unless stated) and keeps
+ * it alive until the enqueued work completes.  The library never allocates or frees device memory,
+ * never synchronises except in h3attn_status_read, and keeps no mutable global state beyond a
+ * per-device cache of device properties.  All work is enqueued on `stream` (a hipStream_t; NULL =
+ * the default stream) of the current device.  Entry points are thread-safe.
+ *
+ * Errors are fail-closed, never a fallback.  Argument errors are returned synchronously before any
+ * work is enqueued.  Data errors that only the device can see (decreasing segment ids, a V value
+ * outside fp16 range) are recorded in the workspace's status word; the attention output is then
+ * filled with NaN so it cannot be mistaken for a valid result, and h3attn_status_read reports it.
+ */
+#ifndef H3ATTN_H
+#define H3ATTN_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define H3ATTN_VERSION 1
+
+enum {
+  H3ATTN_OK = 0,
+  H3ATTN_ERR_NULL = 1,      /* a required pointer is NULL, or exactly one of wq/wk is NULL */
+  H3ATTN_ERR_SHAPE = 2,     /* tokens < 0, heads < 1, head_dim != 128, or sizes overflow */
+  H3ATTN_ERR_ALIGN = 3,     /* a tensor is not 16-byte aligned (seg_ids/lse: 4; workspace: 256) */
+  H3ATTN_ERR_ALIAS = 4,     /* an output overlaps an input or the workspace */
+  H3ATTN_ERR_WORKSPACE = 5, /* workspace_bytes < h3attn_workspace_bytes(tokens, heads) */
+  H3ATTN_ERR_DEVICE = 6,    /* no current device, or it is not gfx950 */
+  H3ATTN_ERR_LAUNCH = 7,    /* the HIP runtime rejected a launch */
+  H3ATTN_ERR_SEGMENTS = 8,  /* device status: segment ids decrease somewhere */
+  H3ATTN_ERR_RANGE = 9      /* device status: a finite |v| > 65504 cannot enter the fp16 P.V product */
+};
+
+/* H3ATTN_VERSION of the loaded library. */
+int h3attn_version(void);
+
+/* Static, NUL-terminated description of a status code (never NULL). */
+const char* h3attn_strerror(int status);
+
+/* Bytes of device workspace that h3attn_fwd (and the staged calls) need for `tokens` x `heads`:
+ * a 256-byte header (status word, counts), the segment table and work list (O(tokens) int32), and
+ * the normed K and fp16 V in head-major layout (2 * tokens * heads * 256 bytes).  Returns 0 for
+ * invalid sizes. */
+size_t h3attn_workspace_bytes(int64_t tokens, int32_t heads);
+
+/* The q_norm / k_norm node on its own: y = RMSNorm(x) * w per (token, head) row, as defined above,
+ * bitwise identical to the norm fused into h3attn_fwd.  x, y: bf16 [T, H, 128]; w: bf16 [128].
+ * y may equal x (in place); any other overlap is H3ATTN_ERR_ALIAS.  eps > 0 (the H3 node uses 1e-6). */
+int h3attn_qknorm(const void* x, const void* w, void* y, int64_t tokens, int32_t heads, int32_t head_dim,
+                  float eps, void* stream);
+
+/* Full forward of the attention node with its fused q/k norm:
+ *   plan (segment decode) -> K norm + fp16 V staging -> attention with the Q norm in the load prologue.
+ * wq and wk both NULL means q and k are already normalised (no norm is applied); exactly one NULL
+ * is H3ATTN_ERR_NULL.  scale is the softmax scale (the H3 node uses 1/sqrt(128)); it must be finite
+ * and > 0.  out must not overlap q, k, v, seg_ids, lse or the workspace.  workspace: device memory
+ * of at least h3attn_workspace_bytes(tokens, heads), 256-byte aligned, used as scratch and for the
+ * status word; its prior contents do not matter.  tokens == 0 is a no-op returning H3ATTN_OK. */
+int h3attn_fwd(const void* q, const void* k, const void* v, const int32_t* seg_ids, const void* wq,
+               const void* wk, int64_t tokens, int32_t heads, int32_t head_dim, float eps, float scale, void* out,
+               float* lse, void* workspace, size_t workspace_bytes, void* stream);
+
+/* The three stages of h3attn_fwd, for callers that reuse one segment plan across layers (the 50
+ * blocks of the model share the packed layout) or time the stages.  They must be enqueued in this
+ * order on one stream with one workspace: h3attn_plan (resets the status word), h3attn_prep_kv,
+ * h3attn_attend.  h3attn_fwd is exactly these three calls. */
+int h3attn_plan(const int32_t* seg_ids, int64_t tokens, int32_t heads, void* workspace, size_t workspace_bytes,
+                void* stream);
+int h3attn_prep_kv(const void* k, const void* v, const void* wk, int64_t tokens, int32_t heads, int32_t head_dim,
+                   float eps, void* workspace, size_t workspace_bytes, void* stream);
+int h3attn_attend(const void* q, const void* wq, int64_t tokens, int32_t heads, int32_t head_dim, float eps,
+                  float scale, void* out, float* lse, void* workspace, size_t workspace_bytes, void* stream);
+
+/* Wait for `stream`, then copy the workspace's device status word to *device_status (host memory):
+ * H3ATTN_OK, H3ATTN_ERR_SEGMENTS or H3ATTN_ERR_RANGE (segments first if both).  Returns the HIP
+ * copy's status (H3ATTN_OK or H3ATTN_ERR_LAUNCH). */
+int h3attn_status_read(const void* workspace, int32_t* device_status, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* H3ATTN_H */

@@ -150,7 +150,8 @@ int oracle_qknorm(const uint16_t* x, const uint16_t* w, uint16_t* y, int64_t T, 
 /* ---------------------------------------------------------------- attention */
 
 /* The bf16 operands entering Q.K^T: the norm node's output, or the inputs themselves when no
- * weights are given.  Returned as FP64 [T*H*128] (bf16 values are exact in FP64). */
+ * weights are given.  Returned as FP64 in head-major order [H][T][128] (bf16 values are exact in
+ * FP64), so one head's rows are contiguous. */
 static double* normed_operand(const uint16_t* x, const uint16_t* w, int64_t T, int32_t H, double eps) {
   int64_t n = T * (int64_t)H * HD;
   double* out = (double*)malloc((size_t)(n > 0 ? n : 1) * sizeof(double));
@@ -158,27 +159,32 @@ static double* normed_operand(const uint16_t* x, const uint16_t* w, int64_t T, i
   int64_t rows = T * (int64_t)H;
 #pragma omp parallel for schedule(static)
   for (int64_t r = 0; r < rows; r++) {
+    const int64_t t = r / H, h = r % H;
+    double* o = out + (h * T + t) * HD;
     if (w) {
       double yr[HD];
       norm_row_f64(x + r * HD, w, eps, yr);
-      for (int d = 0; d < HD; d++) out[r * HD + d] = oracle_bf16_to_f64(oracle_f64_to_bf16(yr[d]));
+      for (int d = 0; d < HD; d++) o[d] = oracle_bf16_to_f64(oracle_f64_to_bf16(yr[d]));
     } else {
-      for (int d = 0; d < HD; d++) out[r * HD + d] = oracle_bf16_to_f64(x[r * HD + d]);
+      for (int d = 0; d < HD; d++) o[d] = oracle_bf16_to_f64(x[r * HD + d]);
     }
   }
   return out;
 }
 
 /* Exact softmax attention of query token i (head h) over its segment [s0, s0+L).
- * qh, kh: normed operands (FP64 [T,H,128]); v: bf16 [T,H,128]. */
-static void attend_one(const double* qh, const double* kh, const uint16_t* v, int32_t H, int h, int64_t i,
+ * qh, kh: normed operands, vd: v; all FP64 head-major [H][T][128]. */
+static void attend_one(const double* qh, const double* kh, const double* vd, int64_t T, int h, int64_t i,
                        int64_t s0, int64_t L, double scale, double* scores, double* o, double* lse) {
-  const double* qi = qh + (i * H + h) * HD;
+  const double* qi = qh + (h * T + i) * HD;
   double m = -INFINITY;
   for (int64_t j = 0; j < L; j++) {
-    const double* kj = kh + ((s0 + j) * H + h) * HD;
-    double dot = 0.0;
-    for (int d = 0; d < HD; d++) dot += qi[d] * kj[d];
+    const double* kj = kh + (h * T + s0 + j) * HD;
+    /* four interleaved partial sums (channels d = 4i + r), added in a fixed order */
+    double part[4] = {0.0, 0.0, 0.0, 0.0};
+    for (int d = 0; d < HD; d += 4)
+      for (int r = 0; r < 4; r++) part[r] += qi[d + r] * kj[d + r];
+    const double dot = (part[0] + part[1]) + (part[2] + part[3]);
     scores[j] = scale * dot;
     if (scores[j] > m) m = scores[j];
   }
@@ -188,8 +194,8 @@ static void attend_one(const double* qh, const double* kh, const uint16_t* v, in
   for (int64_t j = 0; j < L; j++) {
     double e = exp(scores[j] - m);
     l += e;
-    const uint16_t* vj = v + ((s0 + j) * H + h) * HD;
-    for (int d = 0; d < HD; d++) acc[d] += e * oracle_bf16_to_f64(vj[d]);
+    const double* vj = vd + (h * T + s0 + j) * HD;
+    for (int d = 0; d < HD; d++) acc[d] += e * vj[d];
   }
   for (int d = 0; d < HD; d++) o[d] = acc[d] / l;
   *lse = m + log(l);
@@ -218,7 +224,11 @@ static int fwd_impl(const uint16_t* q, const uint16_t* k, const uint16_t* v, con
 
   double* qh = normed_operand(q, wq, T, H, eps);
   double* kh = normed_operand(k, wk, T, H, eps);
-  if (!qh || !kh) { free(qh); free(kh); free(starts); free(lens); free(seg_of); return ORACLE_ERR_NOMEM; }
+  double* vd = normed_operand(v, NULL, T, H, eps); /* no weights: the exact values of v */
+  if (!qh || !kh || !vd) {
+    free(qh); free(kh); free(vd); free(starts); free(lens); free(seg_of);
+    return ORACLE_ERR_NOMEM;
+  }
 
   int64_t nq = rows ? n_rows : T;
   for (int64_t r = 0; r < nq; r++)
@@ -229,19 +239,19 @@ static int fwd_impl(const uint16_t* q, const uint16_t* k, const uint16_t* v, con
     {
       double* scores = (double*)malloc((size_t)(maxlen > 0 ? maxlen : 1) * sizeof(double));
 #pragma omp for schedule(dynamic, 16)
-      for (int64_t u = 0; u < units; u++) {
-        int64_t r = u / H;
-        int h = (int)(u % H);
+      for (int64_t u = 0; u < units; u++) { /* head-major: neighbouring units share one head's rows */
+        int h = (int)(u / nq);
+        int64_t r = u % nq;
         int64_t i = rows ? rows[r] : r;
         int64_t s = seg_of[i];
         double lse_val;
-        attend_one(qh, kh, v, H, h, i, starts[s], lens[s], scale, scores, out + (r * H + h) * HD, &lse_val);
+        attend_one(qh, kh, vd, T, h, i, starts[s], lens[s], scale, scores, out + (r * H + h) * HD, &lse_val);
         if (lse) lse[r * H + h] = lse_val;
       }
       free(scores);
     }
   }
-  free(qh); free(kh); free(starts); free(lens); free(seg_of);
+  free(qh); free(kh); free(vd); free(starts); free(lens); free(seg_of);
   return rc;
 }
 

@@ -1,0 +1,107 @@
+"""The C ABI library on a machine without a GPU: it loads, exports every declared symbol, and
+rejects bad arguments synchronously before touching the device (strict mode: "unsupported shapes,
+dtypes and devices raise instead of falling back", "33B forward/backward" page, Scope)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import deterministic_invariant_attention_amd as h3
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "h3attn.h")
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(h3attn_[a-z_]+)\s*\(", text)))
+
+
+def test_every_declared_symbol_is_exported():
+    lib = h3.load()
+    names = declared_functions()
+    assert len(names) == 9
+    for n in names:
+        assert hasattr(lib, n), f"{n} missing from libh3attn.so"
+    assert sorted(h3.EXPORTS) == names
+
+
+def test_version_and_strerror():
+    assert h3.h3attn_version() == 1
+    for code in range(10):
+        assert h3.h3attn_strerror(code)
+    assert h3.h3attn_strerror(999) == "unknown status"
+
+
+def test_workspace_bytes():
+    assert h3.h3attn_workspace_bytes(0, 1) > 0
+    n = h3.h3attn_workspace_bytes(8349, 40)
+    assert n >= 2 * 8349 * 40 * 256
+    assert n % 256 == 0
+    assert h3.h3attn_workspace_bytes(-1, 4) == 0
+    assert h3.h3attn_workspace_bytes(10, 0) == 0
+
+
+# fake, suitably aligned addresses: every call below fails its checks before any pointer is used
+A = 0x7F0000000000
+P = ctypes.c_void_p
+
+
+def fwd(lib, q=A, k=A + 0x1000000, v=A + 0x2000000, seg=A + 0x3000000, wq=A + 0x4000000, wk=A + 0x4001000, T=16,
+        H=2, D=128, eps=1e-6, scale=0.088, out=A + 0x5000000, lse=None, ws=A + 0x6000000, wsb=None):
+    if wsb is None:
+        wsb = h3.h3attn_workspace_bytes(T, H) if T >= 0 and H >= 1 else 0
+    return lib.h3attn_fwd(q, k, v, seg, wq, wk, T, H, D, eps, scale, out, lse, ws, wsb, None)
+
+
+def test_fwd_argument_errors():
+    lib = h3.load()
+    assert fwd(lib, T=0) == h3.H3ATTN_OK                       # empty input is a no-op
+    assert fwd(lib, T=-1) == h3.H3ATTN_ERR_SHAPE
+    assert fwd(lib, H=0) == h3.H3ATTN_ERR_SHAPE
+    assert fwd(lib, D=64) == h3.H3ATTN_ERR_SHAPE
+    assert fwd(lib, scale=0.0) == h3.H3ATTN_ERR_SHAPE
+    assert fwd(lib, scale=float("nan")) == h3.H3ATTN_ERR_SHAPE
+    assert fwd(lib, eps=0.0) == h3.H3ATTN_ERR_SHAPE
+    assert fwd(lib, T=2 ** 31) == h3.H3ATTN_ERR_SHAPE
+    assert fwd(lib, q=None) == h3.H3ATTN_ERR_NULL
+    assert fwd(lib, out=None) == h3.H3ATTN_ERR_NULL
+    assert fwd(lib, seg=None) == h3.H3ATTN_ERR_NULL
+    assert fwd(lib, wq=None) == h3.H3ATTN_ERR_NULL             # exactly one weight missing
+    assert fwd(lib, wk=None) == h3.H3ATTN_ERR_NULL
+    assert fwd(lib, q=A + 8) == h3.H3ATTN_ERR_ALIGN
+    assert fwd(lib, out=A + 0x5000002) == h3.H3ATTN_ERR_ALIGN
+    assert fwd(lib, ws=A + 0x6000010) == h3.H3ATTN_ERR_ALIGN
+    assert fwd(lib, seg=A + 0x3000002) == h3.H3ATTN_ERR_ALIGN
+    assert fwd(lib, out=A) == h3.H3ATTN_ERR_ALIAS              # out == q
+    assert fwd(lib, out=A + 0x6000000 + 4096) == h3.H3ATTN_ERR_ALIAS   # out inside the workspace
+    assert fwd(lib, wsb=1024) == h3.H3ATTN_ERR_WORKSPACE
+
+
+def test_no_device_is_refused_not_faked():
+    """With valid arguments and no GPU the library reports ERR_DEVICE (never a CPU fallback)."""
+    import torch
+    if torch.cuda.is_available():
+        pytest.skip("a GPU is present; this checks the no-device path")
+    lib = h3.load()
+    assert fwd(lib) == h3.H3ATTN_ERR_DEVICE
+    assert fwd(lib, wq=None, wk=None) == h3.H3ATTN_ERR_DEVICE
+    n = 16 * 2 * 128 * 2
+    assert lib.h3attn_qknorm(A, A + 0x100000, A + 0x200000, 16, 2, 128, 1e-6, None) == h3.H3ATTN_ERR_DEVICE
+    assert lib.h3attn_qknorm(A, A + 0x100000, A + n // 2, 16, 2, 128, 1e-6, None) == h3.H3ATTN_ERR_ALIAS
+    assert lib.h3attn_qknorm(A, A + 0x100000, A, 16, 2, 128, 1e-6, None) == h3.H3ATTN_ERR_DEVICE  # in place is fine
+
+
+def test_staged_calls_check_arguments():
+    lib = h3.load()
+    wsb = h3.h3attn_workspace_bytes(16, 2)
+    assert lib.h3attn_plan(None, 16, 2, A, wsb, None) == h3.H3ATTN_ERR_NULL
+    assert lib.h3attn_plan(A, 16, 2, A + 0x1000000, 8, None) == h3.H3ATTN_ERR_WORKSPACE
+    assert lib.h3attn_prep_kv(A, None, None, 16, 2, 128, 1e-6, A + 0x1000000, wsb, None) == h3.H3ATTN_ERR_NULL
+    assert lib.h3attn_attend(A, None, 16, 2, 128, 1e-6, -1.0, A + 0x100000, None, A + 0x1000000, wsb,
+                             None) == h3.H3ATTN_ERR_SHAPE
+    st = ctypes.c_int32(0)
+    assert lib.h3attn_status_read(None, ctypes.byref(st), None) == h3.H3ATTN_ERR_NULL
+    assert lib.h3attn_status_read(A + 4, ctypes.byref(st), None) == h3.H3ATTN_ERR_ALIGN

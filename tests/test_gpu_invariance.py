@@ -1,0 +1,131 @@
+"""Bitwise properties of the HIP path: repeatability, single-vs-batched (rollout vs train:
+"33B forward/backward" page, dual trajectory), invariance to a segment's offset and neighbours,
+head permutation, exact power-of-two scaling of V, and closed forms."""
+import numpy as np
+import pytest
+import torch
+
+import workloads
+from gpu_util import bitwise_equal, digest, f64, run_fwd, say, to_dev
+
+pytestmark = pytest.mark.gpu
+
+
+def test_repeat_bitwise_short3_x10():
+    g = to_dev(workloads.make_inputs(workloads.WORKLOADS["short3"]))
+    say("[bitwise] short3 repeat x10")
+    ref, lse = run_fwd(g, want_lse=True)
+    d0, l0 = digest(ref), digest(lse)
+    for _ in range(9):
+        o, l = run_fwd(g, want_lse=True)
+        assert digest(o) == d0 and digest(l) == l0
+
+
+def test_repeat_bitwise_long_x3():
+    g = to_dev(workloads.make_inputs(workloads.WORKLOADS["long"]))
+    say("[bitwise] long repeat x3")
+    d0 = digest(run_fwd(g)[0])
+    for _ in range(2):
+        assert digest(run_fwd(g)[0]) == d0
+
+
+def test_batch2_alone_equals_batched():
+    """Row 0 (one 4253-token segment) and row 1 (2000+2000+253) alone vs in the batch, both orders."""
+    wl = workloads.WORKLOADS["batch2"]
+    x = workloads.make_inputs(wl)
+    g = to_dev(x)
+    say("[bitwise] batch2 alone vs batched")
+    batched, blse = run_fwd(g, want_lse=True)
+    (a0, a1), (b0, b1) = workloads.row_slices(wl)
+    for (t0, t1) in ((a0, a1), (b0, b1)):
+        alone = {n: (g[n][t0:t1].contiguous() if n in ("q", "k", "v", "seg") else g[n]) for n in g}
+        o, l = run_fwd(alone, want_lse=True)
+        assert bitwise_equal(o, batched[t0:t1]), f"row [{t0},{t1}) alone differs from batched"
+        assert bitwise_equal(l, blse[t0:t1])
+    # reversed row order (row 1 first): ids must stay non-decreasing, so re-number
+    rev = {n: (torch.cat([g[n][b0:b1], g[n][a0:a1]]) if n in ("q", "k", "v") else g[n]) for n in g}
+    rev["seg"] = torch.cat([g["seg"][b0:b1] - 1, torch.full((a1 - a0,), 100, dtype=torch.int32, device=g["seg"].device)])
+    o, _ = run_fwd(rev)
+    n1 = b1 - b0
+    assert bitwise_equal(o[:n1], batched[b0:b1]) and bitwise_equal(o[n1:], batched[a0:a1])
+
+
+@pytest.mark.parametrize("pad", [1, 63, 64, 65, 127])
+def test_leading_segment_offset_invariance(pad):
+    """A dummy leading segment shifts every other segment's offset; outputs must not change."""
+    x = workloads.random_inputs([300, 129, 64], 3, seed=17)
+    g = to_dev(x)
+    say(f"[bitwise] offset shift by a {pad}-token leading segment")
+    base, blse = run_fwd(g, want_lse=True)
+    d = workloads.random_inputs([pad], 3, seed=99)
+    sh = {n: torch.cat([d[n].to(g[n].device), g[n]]) for n in ("q", "k", "v")}
+    sh["seg"] = torch.cat([torch.full((pad,), -1, dtype=torch.int32), x["seg"]]).to(g["seg"].device)
+    sh["wq"], sh["wk"] = g["wq"], g["wk"]
+    o, l = run_fwd(sh, want_lse=True)
+    assert bitwise_equal(o[pad:], base) and bitwise_equal(l[pad:], blse)
+
+
+def test_nan_neighbours_do_not_leak():
+    x = workloads.random_inputs([70, 131, 45], 2, seed=23)
+    g = to_dev(x)
+    say("[bitwise] NaN-filled neighbour segments")
+    base, _ = run_fwd(g)
+    p = {n: g[n].clone() for n in ("q", "k", "v")}
+    for n in p:
+        p[n][:70] = float("nan")
+        p[n][201:] = float("inf")
+    p.update(seg=g["seg"], wq=g["wq"], wk=g["wk"])
+    o, _ = run_fwd(p)
+    assert bitwise_equal(o[70:201], base[70:201])
+
+
+def test_head_permutation_permutes_output():
+    x = workloads.random_inputs([180, 40], 5, seed=29)
+    g = to_dev(x)
+    say("[bitwise] head permutation")
+    base, _ = run_fwd(g)
+    perm = torch.tensor([3, 0, 4, 1, 2], device=g["q"].device)
+    p = {n: g[n][:, perm].contiguous() for n in ("q", "k", "v")}
+    p.update(seg=g["seg"], wq=g["wq"], wk=g["wk"])
+    o, _ = run_fwd(p)
+    assert bitwise_equal(o, base[:, perm].contiguous())
+
+
+def test_v_power_of_two_scaling_is_exact():
+    x = workloads.random_inputs([150, 66], 3, seed=31)
+    v = x["v"].float()
+    v[v.abs() < 2.0 ** -10] = 0.0    # keep V out of fp16's subnormal range before and after scaling
+    x["v"] = v.to(torch.bfloat16)
+    g = to_dev(x)
+    say("[bitwise] V * 4 -> O * 4")
+    base, _ = run_fwd(g)
+    g4 = dict(g)
+    g4["v"] = g["v"] * 4
+    o4, _ = run_fwd(g4)
+    assert bitwise_equal(o4, base * 4)
+
+
+def test_closed_forms():
+    say("[closed form] single key, identical keys, V = 1")
+    x = workloads.random_inputs([1, 5, 1, 77, 1], 3, seed=37)
+    g = to_dev(x)
+    o, _ = run_fwd(g)
+    for t in (0, 6, 84):                       # single-token segments return their own v exactly
+        assert bitwise_equal(o[t], g["v"][t])
+    # identical keys within a segment: uniform softmax, the mean of V (only fp32 summation error)
+    k = g["k"].clone()
+    k[7:84] = k[7]
+    o2, _ = run_fwd(dict(g, k=k))
+    mean_v = f64(g["v"][7:84]).mean(0)
+    assert np.max(np.abs(f64(o2[7:84]) - mean_v[None])) <= 2 ** -8 * np.max(np.abs(mean_v)) + 1e-6
+    # V = 1 everywhere: every output within one bf16 ulp of 1
+    ones = torch.ones_like(g["v"])
+    o3, _ = run_fwd(dict(g, v=ones))
+    assert np.max(np.abs(f64(o3) - 1.0)) <= 2 ** -7
+
+
+def test_empty_input_is_a_noop():
+    e = torch.zeros(0, 2, 128, dtype=torch.bfloat16, device="cuda:0")
+    w = torch.ones(128, dtype=torch.bfloat16, device="cuda:0")
+    out, _ = run_fwd(dict(q=e, k=e, v=e, seg=torch.zeros(0, dtype=torch.int32, device="cuda:0"), wq=w, wk=w))
+    assert out.shape == (0, 2, 128)

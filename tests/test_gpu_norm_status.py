@@ -1,0 +1,103 @@
+"""The standalone q/k norm against the oracle, the fused prologue against the standalone norm
+(bitwise), and the device status word for data errors."""
+import numpy as np
+import pytest
+import torch
+
+import deterministic_invariant_attention_amd as h3
+import oracle
+import workloads
+from gpu_util import bitwise_equal, f64, run_fwd, say, to_dev
+
+pytestmark = pytest.mark.gpu
+
+
+def _ulp_distance(a_bits, b_bits):
+    """Distance in bf16 steps between two arrays of bf16 patterns (same-sign values)."""
+    a = a_bits.astype(np.int32)
+    b = b_bits.astype(np.int32)
+    ka = np.where(a & 0x8000, -(a & 0x7FFF), a & 0x7FFF)
+    kb = np.where(b & 0x8000, -(b & 0x7FFF), b & 0x7FFF)
+    return np.abs(ka - kb)
+
+
+@pytest.mark.parametrize("name", ["short3", "long_w25"])
+def test_qknorm_matches_oracle_bitwise(name):
+    """Both sides round the FP64 norm once to bf16: the codes are identical.  (The FP64 sums of
+    squares are exact for bf16 inputs of any ordinary range, so the summation order cannot move a
+    value across a rounding midpoint.)"""
+    wl = workloads.WORKLOADS[name]
+    x = workloads.make_inputs(wl)
+    say(f"[qknorm] {name}")
+    for n, w in (("q", "wq"), ("k", "wk")):
+        y = h3.h3attn_qknorm(x[n].cuda(), x[w].cuda(), eps=wl.eps)
+        torch.cuda.synchronize()
+        got = y.cpu().view(torch.int16).numpy().view(np.uint16)
+        ref = oracle.qknorm(x[n], x[w], wl.eps)
+        dist = _ulp_distance(got, ref)
+        frac = float(np.mean(dist > 0))
+        say(f"[qknorm] {name}.{n}: max ulp {dist.max()}, flipped fraction {frac:.2e}")
+        assert dist.max() == 0
+
+
+def test_qknorm_in_place_equals_out_of_place():
+    x = workloads.random_inputs([333], 7, seed=41)
+    a = x["q"].cuda()
+    y = h3.h3attn_qknorm(a, x["wq"].cuda())
+    b = a.clone()
+    h3.h3attn_qknorm(b, x["wq"].cuda(), out=b)
+    torch.cuda.synchronize()
+    assert bitwise_equal(y, b)
+
+
+def test_fused_prologue_equals_standalone_norm():
+    """fwd with weights == fwd on h3attn_qknorm outputs without weights, bit for bit."""
+    x = workloads.random_inputs([255, 513, 70], 6, seed=43)
+    g = to_dev(x)
+    say("[qknorm] fused prologue vs standalone")
+    fused, flse = run_fwd(g, want_lse=True)
+    qn = h3.h3attn_qknorm(g["q"], g["wq"])
+    kn = h3.h3attn_qknorm(g["k"], g["wk"])
+    pre, plse = run_fwd(dict(g, q=qn, k=kn), want_lse=True, weights=False)
+    assert bitwise_equal(fused, pre) and bitwise_equal(flse, plse)
+
+
+def test_decreasing_segment_ids_set_status_and_nan_fill():
+    x = workloads.random_inputs([40, 40], 2, seed=47)
+    g = to_dev(x)
+    g["seg"] = torch.tensor([0] * 30 + [1] * 20 + [0] * 30, dtype=torch.int32, device="cuda:0")
+    say("[status] decreasing segment ids")
+    ws = h3.workspace(80, 2, "cuda:0")
+    out, lse = run_fwd(g, want_lse=True, ws=ws)
+    assert h3.h3attn_status_read(ws) == h3.H3ATTN_ERR_SEGMENTS
+    assert torch.isnan(out.float()).all() and torch.isnan(lse).all()
+    # the next valid call on the same workspace resets the status and computes normally
+    g["seg"] = x["seg"].cuda()
+    out2, _ = run_fwd(g, ws=ws)
+    assert h3.h3attn_status_read(ws) == h3.H3ATTN_OK
+    assert torch.isfinite(out2.float()).all()
+
+
+def test_v_out_of_fp16_range_sets_status():
+    x = workloads.random_inputs([40, 40], 2, seed=53)
+    x["v"][10, 1, 5] = 1.0e5
+    g = to_dev(x)
+    say("[status] |v| > 65504")
+    ws = h3.workspace(80, 2, "cuda:0")
+    out, _ = run_fwd(g, ws=ws)
+    assert h3.h3attn_status_read(ws) == h3.H3ATTN_ERR_RANGE
+    assert torch.isnan(out.float()).all()
+    # infinities are not a range error: they propagate as IEEE values (only in their own segment)
+    x["v"][10, 1, 5] = float("inf")
+    g = to_dev(x)
+    out, _ = run_fwd(g, ws=ws)
+    assert h3.h3attn_status_read(ws) == h3.H3ATTN_OK
+    assert torch.isfinite(out[40:].float()).all()
+
+
+def test_wrong_arguments_raise():
+    x = to_dev(workloads.random_inputs([8], 2, seed=1))
+    with pytest.raises(h3.H3AttnError):
+        h3.h3attn_fwd(x["q"], x["k"], x["v"], x["seg"], x["wq"], None)
+    with pytest.raises(h3.H3AttnError):
+        h3.h3attn_fwd(x["q"], x["k"], x["v"], x["seg"], scale=-1.0)

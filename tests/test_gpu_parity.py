@@ -1,0 +1,93 @@
+"""Parity of the HIP path with the FP64 oracle, element by element on the same seeded inputs.
+
+Bound (whole output tensor, bf16 output upcast exactly): relative L2 <= 2e-3 and max abs <= 2e-2;
+LSE within 1e-5 * max(1, |LSE|) (FP32 logits; the normed q/k are bit-identical to the oracle's).  Full-size workloads the oracle cannot finish in seconds are checked on sampled
+query rows (every head), which the oracle computes one by one.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import workloads
+from gpu_util import EPS, LSE_REL_BOUND, MAX_ABS_BOUND, REL_L2_BOUND, f64, lse_error, metrics, run_fwd, say, to_dev
+
+pytestmark = pytest.mark.gpu
+
+
+def _check_full(name, x, eps=EPS, scale=128 ** -0.5):
+    g = to_dev(x)
+    say(f"[parity] {name}: T={x['q'].shape[0]} H={x['q'].shape[1]} via h3attn_fwd")
+    out, lse = run_fwd(g, eps=eps, scale=scale, want_lse=True, weights=x["wq"] is not None)
+    ref, ref_lse = oracle.fwd(x["q"], x["k"], x["v"], x["seg"].numpy(), x["wq"], x["wk"], eps, scale)
+    rel, mx = metrics(out, ref)
+    lse_err = lse_error(lse, ref_lse)
+    say(f"[parity] {name}: rel_l2={rel:.3e} max_abs={mx:.3e} lse_rel_err={lse_err:.2e}")
+    assert np.all(np.isfinite(f64(out)))
+    assert rel <= REL_L2_BOUND and mx <= MAX_ABS_BOUND and lse_err <= LSE_REL_BOUND
+    return out
+
+
+@pytest.mark.parametrize("name", ["tiny", "short3"])
+def test_parity_small_workloads(name):
+    _check_full(name, workloads.make_inputs(workloads.WORKLOADS[name]))
+
+
+def test_parity_batch2_full():
+    """2 packed rows x 4253 tokens (4253 | 2000 + 2000 + 253), 40 heads, the whole output."""
+    _check_full("batch2", workloads.make_inputs(workloads.WORKLOADS["batch2"]))
+
+
+def test_parity_ragged_tiles():
+    """Segment lengths around the 64-key and 128-query tile edges, plus single-token segments."""
+    lens = [1, 2, 63, 64, 65, 127, 128, 129, 300, 3, 1, 257]
+    _check_full("ragged", workloads.random_inputs(lens, 3, seed=21))
+
+
+def test_parity_without_weights():
+    """wq = wk = NULL: q and k enter Q.K^T as given (already-normalised inputs)."""
+    x = workloads.random_inputs([200, 77], 4, seed=5, normed=False)
+    _check_full("no-norm", x)
+
+
+def test_parity_other_scale_and_eps():
+    x = workloads.random_inputs([150, 90], 2, seed=9)
+    _check_full("scale0.2-eps1e-3", x, eps=float(np.float32(1e-3)), scale=0.2)
+
+
+def _sample_rows(L, n, seed):
+    rng = np.random.default_rng(seed)
+    fixed = [0, 1, 63, 64, 127, 128, L // 2, L - 129, L - 65, L - 2, L - 1]
+    return np.unique(np.concatenate([fixed, rng.integers(0, L, n)]))
+
+
+@pytest.mark.parametrize("name", ["long", "long_w3", "long_w8", "long_w25", "long_raw"])
+def test_parity_long_sampled(name):
+    """8349 tokens in one segment, 40 heads, at full size; sampled rows against the oracle.
+    "long" is the throughput workload; the others sharpen the softmax (max logit up to ~3400)."""
+    wl = workloads.WORKLOADS[name]
+    x = workloads.make_inputs(wl)
+    g = to_dev(x)
+    say(f"[parity] {name}: T={wl.tokens} H={wl.heads} sampled rows via h3attn_fwd")
+    out, lse = run_fwd(g, eps=wl.eps, scale=wl.scale, want_lse=True, weights=wl.normed)
+    rows = _sample_rows(wl.tokens, 48, seed=3)
+    ref, ref_lse = oracle.fwd_rows(x["q"], x["k"], x["v"], x["seg"].numpy(), rows, x["wq"], x["wk"], wl.eps, wl.scale)
+    got = f64(out)[rows]
+    rel, mx = metrics(got, ref)
+    lse_err = lse_error(f64(lse)[rows], ref_lse)
+    say(f"[parity] {name}: rows={len(rows)} rel_l2={rel:.3e} max_abs={mx:.3e} lse_rel_err={lse_err:.2e}")
+    assert np.all(np.isfinite(f64(out)))
+    assert rel <= REL_L2_BOUND and mx <= MAX_ABS_BOUND and lse_err <= LSE_REL_BOUND
+
+
+def test_parity_long_segment_many_tiles():
+    """A 20000-token segment (313 KV tiles) on 2 heads, sampled rows."""
+    x = workloads.random_inputs([20000], 2, seed=13, qk_scale=2.0)
+    g = to_dev(x)
+    say("[parity] 20000-token segment, H=2")
+    out, _ = run_fwd(g)
+    rows = _sample_rows(20000, 24, seed=4)
+    ref, _ = oracle.fwd_rows(x["q"], x["k"], x["v"], x["seg"].numpy(), rows, x["wq"], x["wk"], EPS)
+    rel, mx = metrics(f64(out)[rows], ref)
+    say(f"[parity] 20000-token: rel_l2={rel:.3e} max_abs={mx:.3e}")
+    assert rel <= REL_L2_BOUND and mx <= MAX_ABS_BOUND

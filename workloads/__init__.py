@@ -20,6 +20,9 @@ import hashlib
 import torch
 
 HEAD_DIM = 128
+# The norm's eps (1e-6) as the float32 value the C ABI receives, so that the oracle and the library
+# are handed the same number.
+EPS = 9.999999974752427e-07
 
 
 @dataclasses.dataclass(frozen=True)
@@ -30,7 +33,7 @@ class Workload:
     qk_scale: float = 1.0  # multiplier on the q and k draws before the bf16 cast
     w_scale: float = 1.0   # multiplier on the norm weights (sharp-softmax companions)
     normed: bool = True    # False: no norm weights (q/k are taken as already normalised)
-    eps: float = 1e-6
+    eps: float = EPS
     seed: int = 0
     description: str = ""
 
