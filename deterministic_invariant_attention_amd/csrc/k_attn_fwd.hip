@@ -4,18 +4,31 @@
 // output ("33B forward/backward" page, Scope: strict mode).
 //
 // Work item = (segment, 128-query tile, head); a persistent grid walks the items.  Each wave owns 32
-// queries.  The product is computed transposed so that one lane owns one query:
+// queries.  The products are computed transposed so that one lane pair owns one query:
 //   S^T[key][query] = Khat . Qhat^T   (A = 32 keys x 16 dims from LDS, B = the wave's normed Q held
 //                                      in registers; v_mfma_f32_32x32x16_bf16)
 //   O^T[dim][query] += V^T . P^T      (A = 32 dims x 16 keys, read from the row-major V tile with
 //                                      ds_read_b64_tr_b16; B = P in fp16; v_mfma_f32_32x32x16_f16)
 // With that layout the softmax row max and row sum are lane-local over 32 scores plus one exchange
-// with lane ^ 32 (the other half of the query's keys).
+// with lane ^ 32 (the other half of the query's keys), done with v_permlane32_swap.
+//
+// Pipeline.  K and V tiles (64 keys, 16 KB each) are copied from the workspace straight into LDS
+// with global_load_lds_dwordx4 (no register staging), double-buffered: at the top of iteration j
+// the loads of K(j+2) and V(j+1) are issued, and they have the whole iteration to land.  Within a
+// wave, iteration j overlaps the S MFMAs of tile j+1 with the softmax of tile j, then the P.V MFMAs
+// of tile j with the row maximum of tile j+1.  One barrier per iteration.
+//
+// LDS layouts are XOR-swizzled by 16-byte chunk (the copy picks, per lane, which global chunk
+// lands in its LDS slot), so that both read patterns are free of bank conflicts:
+//   K: row r, chunk c at slot c ^ (r & 15)        (ds_read_b128 of 32 rows x 16 B)
+//   V: row r, chunk c at slot c ^ 4 * (r & 3)     (ds_read_b64_tr_b16 of 8 rows x 64 B)
 //
 // Determinism and batch invariance: tiles are anchored at the segment's first key and walked in
-// ascending order; keys past the segment end are zero in LDS and masked to -inf; every reduction
-// tree is fixed; the code path depends only on the segment length.  So each output row is a
-// function of its own segment's bytes, never of the batch, the offset, neighbours or the grid.
+// ascending order; keys past the segment end are masked to -inf by a select (their K rows are
+// in-segment duplicates, their V rows likewise and they meet p = 0); every sum is a fixed tree; the
+// code path depends only on the segment length.  So each output row is a function of its own
+// segment's bytes, never of the batch, the offset, neighbours or the grid.  (Maxima are exact, so
+// their evaluation order cannot change a bit.)
 //
 // Online softmax with a lazy maximum: the running maximum m (log2 units) moves only when a tile's
 // maximum exceeds it by more than 8, so p = exp2(s*c - m) <= 2^8 stays well inside fp16, and the
@@ -25,10 +38,9 @@
 
 namespace h3 {
 
-constexpr int KPITCH = 136;  // 16-bit elements per K row in LDS (272 B: 16-byte rows shift 4 banks)
-constexpr int VPITCH = 160;  // 16-bit elements per V row in LDS (320 B: transposed reads stay conflict-free)
 constexpr float LN2 = 0.69314718055994530942f;
 constexpr float RESCALE_THRESHOLD = 8.0f;  // log2 units
+constexpr int TILE_ELEMS = BK * HD;        // 16-bit elements in one K or V tile (16 KB)
 
 struct AttnParams {
   const uint16_t* q;
@@ -44,9 +56,40 @@ struct AttnParams {
   int32_t H;
   float eps;
   float c;  // scale * log2(e)
+  int32_t xcd_slots;  // workgroups per XCD (grid / 8), for the XCD-aware item order
 };
 
 typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
+typedef __attribute__((address_space(3))) void lds_void;
+typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+
+// Element offsets of a 16-bit value (row r, column d) inside a swizzled tile.
+__device__ __forceinline__ int k_off(int r, int d) { return r * HD + ((((d >> 3) ^ (r & 15))) << 3) + (d & 7); }
+__device__ __forceinline__ int v_off(int r, int d) { return r * HD + ((((d >> 3) ^ ((r & 3) << 2))) << 3) + (d & 7); }
+
+// Copy one 64-row tile of a head-major [rows][128] 16-bit array into a swizzled LDS tile with
+// buffer_load_dwordx4 ... lds.  The buffer resource covers only the tile's rows inside the segment
+// (`valid` rows), so the rows past the segment end read as zeros: nothing outside the segment can
+// reach the products.  256 threads, 4 x 1 KB per wave; each lane's 16 bytes land at LDS base +
+// lane * 16, so the lane fetches the global chunk that belongs in that slot.  The slot pattern
+// repeats every 16 rows, so one lane offset serves all four blocks.
+__device__ __forceinline__ int tile_lane_offset(bool is_v, int wv, int lane) {
+  const int r = 4 * wv + (lane >> 4);  // tile row of the lane's slot in block wv (rows 4wv..4wv+3)
+  const int slot = lane & 15;
+  const int c = is_v ? (slot ^ ((r & 3) << 2)) : (slot ^ (r & 15));
+  return r * 256 + c * 16;  // bytes
+}
+
+__device__ __forceinline__ void tile_to_lds(const uint16_t* gtile, int valid, uint16_t* lds_tile, int wv,
+                                            int lane_off) {
+  const __amdgpu_buffer_rsrc_t rs =
+      __builtin_amdgcn_make_buffer_rsrc((void*)gtile, (short)0, (valid < BK ? valid : BK) * 256, 0x00020000);
+#pragma unroll
+  for (int i = 0; i < 4; i++)  // block 4i + wv = rows 16i + 4wv .. +3
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void*)(lds_tile + (4 * i + wv) * 4 * HD), 16,
+                                             lane_off + i * 4096, 0, 0, 0);
+}
 
 // Transposed LDS read (gfx950): within each 16-lane group, lane s supplies the address of 4
 // consecutive 16-bit elements C_s; lane s receives {C_{s/4}[s%4], C_{4+s/4}[s%4], C_{8+s/4}[s%4],
@@ -56,7 +99,15 @@ __device__ __forceinline__ i16x4 tr_read(const uint16_t* lds_ptr) {
   return __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(uint16_t*)lds_ptr);
 }
 
-__device__ __forceinline__ float max3(float a, float b, float c) { return __builtin_fmaxf(__builtin_fmaxf(a, b), c); }
+// The value of lane ^ 32 (the other half of this query's keys), exchanged without LDS.
+__device__ __forceinline__ void swap_halves(float x, float& lo_half, float& hi_half) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__builtin_bit_cast(uint32_t, x), __builtin_bit_cast(uint32_t, x),
+                                                  false, false);
+  // r[0]: lanes 0-31 keep x, lanes 32-63 receive x of lanes 0-31; r[1]: the other way round.  So
+  // every lane holds (x of lane l%32, x of lane l%32 + 32), in that order, in both halves.
+  lo_half = __builtin_bit_cast(float, (uint32_t)r[0]);
+  hi_half = __builtin_bit_cast(float, (uint32_t)r[1]);
+}
 
 template <int N>
 __device__ __forceinline__ float tree_sum(const float* x) {
@@ -67,13 +118,64 @@ __device__ __forceinline__ float tree_sum(const float* x) {
   }
 }
 
+// S^T for the 64 keys of one LDS tile: S[kb] holds keys 32kb + 8(i/4) + 4hh + (i%4) of the lane's
+// query.  The k-slices are accumulated in ascending dimension order.
+__device__ __forceinline__ void tile_scores(const uint16_t* Ks, const bf16x8* qf, int l32, int hh, f32x16* S) {
+#pragma unroll
+  for (int kb = 0; kb < 2; kb++) {
+#pragma unroll
+    for (int i = 0; i < 16; i++) S[kb][i] = 0.0f;
+#pragma unroll
+    for (int m = 0; m < 8; m++) {
+      const bf16x8 a = *(const bf16x8*)(Ks + k_off(32 * kb + l32, 16 * m + 8 * hh));
+      S[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[m], S[kb], 0, 0, 0);
+    }
+  }
+}
+
+// Keys at or past `rem` (the valid keys of the segment's last tile) get -inf.
+__device__ __forceinline__ void mask_tail(f32x16* S, int rem, int hh) {
+#pragma unroll
+  for (int kb = 0; kb < 2; kb++)
+#pragma unroll
+    for (int i = 0; i < 16; i++)
+      if (32 * kb + 8 * (i >> 2) + 4 * hh + (i & 3) >= rem) S[kb][i] = -__builtin_inff();
+}
+
+// Maximum over the query's 64 keys of one tile (exact, so any evaluation order gives these bits).
+__device__ __forceinline__ float tile_max(const f32x16* S) {
+  float a = __builtin_fmaxf(__builtin_fmaxf(S[0][0], S[0][1]), S[0][2]);
+  float b = __builtin_fmaxf(__builtin_fmaxf(S[1][0], S[1][1]), S[1][2]);
+#pragma unroll
+  for (int i = 3; i < 15; i += 2) {
+    a = __builtin_fmaxf(__builtin_fmaxf(a, S[0][i]), S[0][i + 1]);
+    b = __builtin_fmaxf(__builtin_fmaxf(b, S[1][i]), S[1][i + 1]);
+  }
+  a = __builtin_fmaxf(a, S[0][15]);
+  b = __builtin_fmaxf(b, S[1][15]);
+  float lo, hi;
+  swap_halves(__builtin_fmaxf(a, b), lo, hi);
+  return __builtin_fmaxf(lo, hi);
+}
+
+template <int N>
+struct Par {
+  static constexpr int value = N;
+};
+
+// Modes of one KV iteration j (tile j's softmax and P.V, tile j+1's scores):
+//   FULL  j + 2 < ntiles: tile j+1 is a full tile, K(j+2) and V(j+1) are prefetched
+//   MASK  j + 2 == ntiles: tile j+1 is the segment's last tile (masked past `rem`), V(j+1) prefetched
+//   LAST  j + 1 == ntiles: no next tile
+enum Mode { FULL = 0, MASK = 1, LAST = 2 };
+
 __global__ __launch_bounds__(256, 2) void k_attn_fwd(AttnParams p) {
-  __shared__ __attribute__((aligned(16))) uint16_t Ks[BK * KPITCH];
-  __shared__ __attribute__((aligned(16))) uint16_t Vs[BK * VPITCH];
+  // K tiles in buffers 0, 1 and V tiles in buffers 2, 3 (16 KB each)
+  __shared__ __attribute__((aligned(1024))) uint16_t lds[4 * TILE_ELEMS];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int wv = tid >> 6;
+  const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform
   const int hh = lane >> 5;    // which half of the 16-wide MFMA k-slice this lane feeds
   const int l32 = lane & 31;   // query (B / D column) index within the wave
   const int64_t T = p.T;
@@ -95,20 +197,43 @@ __global__ __launch_bounds__(256, 2) void k_attn_fwd(AttnParams p) {
   // cannot send a work item outside the tensors.
   const int64_t max_items = T + (T + BQ - 1) / BQ;
   const int nseg = (int)min((int64_t)max(p.hdr->nseg, 0), T);
-  const int nwork = (int)min((int64_t)max(p.hdr->nitems, 0), max_items) * H;
-  // staging map: thread covers 16-byte chunk (tid & 15) of rows (tid >> 4) + 16*i, i = 0..3
-  const int st_c = tid & 15;
-  const int st_r = tid >> 4;
+  const int nitems = (int)min((int64_t)max(p.hdr->nitems, 0), max_items);
+  const int nwork = nitems * H;
 
-  for (int w = blockIdx.x; w < nwork; w += gridDim.x) {
-    const int item = w / H;
-    const int head = w - item * H;
+  // XCD-aware order: workgroup b runs on XCD b % 8; the workgroups of one XCD take consecutive
+  // positions of the head-major work order, so they share the K/V tiles of one head in that XCD's L2.
+  const int xcd = blockIdx.x & 7;
+  const int slot = blockIdx.x >> 3;
+  const int nslots = p.xcd_slots;
+
+  const int k_lane_off = tile_lane_offset(false, wv, lane);
+  const int v_lane_off = tile_lane_offset(true, wv, lane);
+  const int tr_row = 4 * hh + ((lane & 15) >> 2);
+  const int tr_col = 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
+  const float c = p.c;
+
+  for (int round = 0;; round++) {
+    const int64_t v = ((int64_t)round * 8 + xcd) * nslots + slot;
+    if (v >= nwork) break;
+    const int head = (int)(v / nitems);
+    const int item = (int)(v - (int64_t)head * nitems);
     const int seg = p.items[2 * item];
     const int qt = p.items[2 * item + 1];
     if ((unsigned)seg >= (unsigned)nseg) continue;
     const int s0 = p.segtab[2 * seg];
     const int L = p.segtab[2 * seg + 1];
     if (s0 < 0 || L <= 0 || (int64_t)s0 + L > T || qt < 0 || qt * BQ >= L) continue;
+
+    const int ntiles = (L + BK - 1) / BK;
+    const int rem = L - (ntiles - 1) * BK;  // valid keys of the last tile, 1..64
+    const uint16_t* kbase = p.khat + ((int64_t)head * T + s0) * HD;
+    const uint16_t* vbase = p.v16 + ((int64_t)head * T + s0) * HD;
+
+    // Every wave has finished reading LDS for the previous item before it is overwritten.
+    __syncthreads();
+    tile_to_lds(kbase, L, lds, wv, k_lane_off);
+    tile_to_lds(vbase, L, lds + 2 * TILE_ELEMS, wv, v_lane_off);
+    if (ntiles > 1) tile_to_lds(kbase + BK * HD, L - BK, lds + TILE_ELEMS, wv, k_lane_off);
 
     // ---------------- Q prologue: load, RMSNorm (2 lanes per row), round to bf16 B-operands
     const int qrow = qt * BQ + wv * 32 + l32;
@@ -119,9 +244,9 @@ __global__ __launch_bounds__(256, 2) void k_attn_fwd(AttnParams p) {
       const uint16_t* qp = p.q + ((int64_t)(s0 + (qvalid ? qrow : 0)) * H + head) * HD;
 #pragma unroll
       for (int m = 0; m < 8; m++) {
-        u32x4 v = {0, 0, 0, 0};
-        if (qvalid) v = *(const u32x4*)(qp + 16 * m + 8 * hh);
-        unpack8_bf16(v, x[m]);
+        u32x4 w4 = {0, 0, 0, 0};
+        if (qvalid) w4 = *(const u32x4*)(qp + 16 * m + 8 * hh);
+        unpack8_bf16(w4, x[m]);
       }
       if (p.wq) {
         double part[8];
@@ -150,124 +275,113 @@ __global__ __launch_bounds__(256, 2) void k_attn_fwd(AttnParams p) {
       }
     }
 
-    // ---------------- KV walk
-    const int ntiles = (L + BK - 1) / BK;
-    const uint16_t* kbase = p.khat + ((int64_t)head * T + s0) * HD;
-    const uint16_t* vbase = p.v16 + ((int64_t)head * T + s0) * HD;
-    u32x4 kreg[4], vreg[4];
-    auto prefetch = [&](int j) {
-#pragma unroll
-      for (int i = 0; i < 4; i++) {
-        const int key = j * BK + st_r + 16 * i;
-        kreg[i] = u32x4{0, 0, 0, 0};
-        vreg[i] = u32x4{0, 0, 0, 0};
-        if (key < L) {
-          kreg[i] = *(const u32x4*)(kbase + (int64_t)key * HD + st_c * 8);
-          vreg[i] = *(const u32x4*)(vbase + (int64_t)key * HD + st_c * 8);
-        }
-      }
-    };
+    // ---------------- scores of tile 0
+    __builtin_amdgcn_s_waitcnt(0xF70);  // vmcnt(0): this wave's tile copies have landed
+    __syncthreads();                    // ... and every other wave's
+    f32x16 S[2];
+    tile_scores(lds, qf, l32, hh, S);
+    if (ntiles == 1 && rem < BK) mask_tail(S, rem, hh);
 
     f32x16 O[4];
 #pragma unroll
     for (int d = 0; d < 4; d++)
 #pragma unroll
       for (int i = 0; i < 16; i++) O[d][i] = 0.0f;
-    float m_run = -__builtin_inff();
     float lsum = 0.0f;
+    float m_run = tile_max(S) * c;  // first tile: m is the tile maximum (log2 units)
 
-    prefetch(0);
-    for (int j = 0; j < ntiles; j++) {
-      __syncthreads();  // every wave is done reading the previous tile
-#pragma unroll
-      for (int i = 0; i < 4; i++) {
-        *(u32x4*)(Ks + (st_r + 16 * i) * KPITCH + st_c * 8) = kreg[i];
-        *(u32x4*)(Vs + (st_r + 16 * i) * VPITCH + st_c * 8) = vreg[i];
-      }
+    // One KV iteration; PAR = j & 1 selects the buffers: K(j) and V(j) live in buffers PAR and 2+PAR.
+    auto iteration = [&](auto par, auto mode, int j) {
+      constexpr int PAR = decltype(par)::value;
+      constexpr int MODE = decltype(mode)::value;
+      uint16_t* const Kcur = lds + PAR * TILE_ELEMS;         // K(j): free once the iteration starts
+      const uint16_t* const Knext = lds + (1 - PAR) * TILE_ELEMS;  // K(j+1)
+      const uint16_t* const Vcur = lds + (2 + PAR) * TILE_ELEMS;   // V(j)
+      uint16_t* const Vnext = lds + (3 - PAR) * TILE_ELEMS;        // V(j+1): its buffer held V(j-1)
+      __builtin_amdgcn_s_waitcnt(0xF70);
       __syncthreads();
-      if (j + 1 < ntiles) prefetch(j + 1);
+      if constexpr (MODE == FULL) tile_to_lds(kbase + (int64_t)(j + 2) * BK * HD, L - (j + 2) * BK, Kcur, wv, k_lane_off);
+      if constexpr (MODE != LAST) tile_to_lds(vbase + (int64_t)(j + 1) * BK * HD, L - (j + 1) * BK, Vnext, wv, v_lane_off);
 
-      // S^T for keys [32kb, 32kb+32) of the tile
-      f32x16 S[2];
-#pragma unroll
-      for (int kb = 0; kb < 2; kb++) {
-#pragma unroll
-        for (int i = 0; i < 16; i++) S[kb][i] = 0.0f;
-#pragma unroll
-        for (int m = 0; m < 8; m++) {
-          const bf16x8 a = *(const bf16x8*)(Ks + (32 * kb + l32) * KPITCH + 16 * m + 8 * hh);
-          S[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[m], S[kb], 0, 0, 0);
-        }
-      }
-      // lane holds keys 32kb + 8(i/4) + 4hh + (i%4) of its query
-      if (j == ntiles - 1) {
-        const int rem = L - j * BK;
-        if (rem < BK) {
-#pragma unroll
-          for (int kb = 0; kb < 2; kb++)
-#pragma unroll
-            for (int i = 0; i < 16; i++)
-              if (32 * kb + 8 * (i >> 2) + 4 * hh + (i & 3) >= rem) S[kb][i] = -__builtin_inff();
-        }
-      }
+      // scores of tile j+1 (MFMA) alongside the softmax of tile j (VALU)
+      f32x16 Sn[2];
+      if constexpr (MODE != LAST) tile_scores(Knext, qf, l32, hh, Sn);
 
-      // ---- online softmax (one query per lane pair)
-      float mx[8];
-#pragma unroll
-      for (int g = 0; g < 8; g++) {
-        const int kb = g >> 2, i0 = (g & 3) * 4;
-        mx[g] = __builtin_fmaxf(max3(S[kb][i0], S[kb][i0 + 1], S[kb][i0 + 2]), S[kb][i0 + 3]);
-      }
-      float tmax = __builtin_fmaxf(max3(mx[0], mx[1], mx[2]), max3(mx[3], mx[4], mx[5]));
-      tmax = max3(tmax, mx[6], mx[7]);
-      tmax = __builtin_fmaxf(tmax, __shfl_xor(tmax, 32, 64));
-      const float mt = tmax * p.c;
-      const bool need = mt > m_run + RESCALE_THRESHOLD;
-      if (__ballot(need)) {
-        const float m_new = need ? mt : m_run;
-        const float alpha = need ? __builtin_amdgcn_exp2f(m_run - m_new) : 1.0f;
-        lsum *= alpha;
-#pragma unroll
-        for (int d = 0; d < 4; d++)
-#pragma unroll
-          for (int i = 0; i < 16; i++) O[d][i] *= alpha;
-        m_run = m_new;
-      }
       float pr[32];
 #pragma unroll
       for (int kb = 0; kb < 2; kb++)
 #pragma unroll
-        for (int i = 0; i < 16; i++) pr[16 * kb + i] = __builtin_amdgcn_exp2f(__builtin_fmaf(S[kb][i], p.c, -m_run));
+        for (int i = 0; i < 16; i++) pr[16 * kb + i] = __builtin_amdgcn_exp2f(__builtin_fmaf(S[kb][i], c, -m_run));
       lsum += tree_sum<32>(pr);
-
       f16x8 pf[4];
 #pragma unroll
       for (int ks = 0; ks < 4; ks++) {
         u32x4 w4;
 #pragma unroll
-        for (int i = 0; i < 4; i++) w4[i] = pack_f16(pr[8 * ks + 2 * i], pr[8 * ks + 2 * i + 1]);
+        for (int i = 0; i < 4; i++) {
+          const f32x2 two = {pr[8 * ks + 2 * i], pr[8 * ks + 2 * i + 1]};
+          w4[i] = __builtin_bit_cast(uint32_t, __builtin_convertvector(two, f16x2));  // RNE
+        }
         pf[ks] = __builtin_bit_cast(f16x8, w4);
       }
 
-      // ---- O^T += V^T P^T ; A rows = dims 32db + l32, A k-slots = keys 16ks + {4hh..4hh+3, 8+4hh..8+4hh+3}
-      const int tr_row = 4 * hh + ((lane & 15) >> 2);
-      const int tr_col = 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
+      // O^T += V^T P^T ; A rows = dims 32db + l32, A k-slots = keys 16ks + {4hh..4hh+3, 8+4hh..8+4hh+3}
 #pragma unroll
       for (int ks = 0; ks < 4; ks++) {
 #pragma unroll
         for (int db = 0; db < 4; db++) {
-          const uint16_t* base = Vs + (16 * ks + tr_row) * VPITCH + 32 * db + tr_col;
-          const i16x4 lo = tr_read(base);
-          const i16x4 hi = tr_read(base + 8 * VPITCH);
+          const i16x4 lo = tr_read(Vcur + v_off(16 * ks + tr_row, 32 * db + tr_col));
+          const i16x4 hi = tr_read(Vcur + v_off(16 * ks + 8 + tr_row, 32 * db + tr_col));
           const f16x4 flo = __builtin_bit_cast(f16x4, lo), fhi = __builtin_bit_cast(f16x4, hi);
           const f16x8 a = {flo[0], flo[1], flo[2], flo[3], fhi[0], fhi[1], fhi[2], fhi[3]};
           O[db] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a, pf[ks], O[db], 0, 0, 0);
         }
       }
+
+      if constexpr (MODE != LAST) {
+        if constexpr (MODE == MASK) {
+          if (rem < BK) mask_tail(Sn, rem, hh);
+        }
+        const float mt = tile_max(Sn) * c;
+        const bool need = mt > m_run + RESCALE_THRESHOLD;
+        if (__builtin_expect(__ballot(need) != 0, 0)) {  // rare: keep it a branch, not a select
+          const float m_new = need ? mt : m_run;
+          const float alpha = need ? __builtin_amdgcn_exp2f(m_run - m_new) : 1.0f;
+          lsum *= alpha;
+#pragma unroll
+          for (int d = 0; d < 4; d++)
+#pragma unroll
+            for (int i = 0; i < 16; i++) O[d][i] *= alpha;
+          m_run = m_new;
+        }
+        S[0] = Sn[0];
+        S[1] = Sn[1];
+      }
+    };
+
+    // j = 0 .. ntiles-3 in FULL mode (unrolled by two so the buffers are fixed), then MASK, LAST
+    int j = 0;
+    for (; j + 3 < ntiles; j += 2) {
+      iteration(Par<0>{}, Par<FULL>{}, j);
+      iteration(Par<1>{}, Par<FULL>{}, j + 1);
     }
+    if (j + 2 < ntiles) {
+      iteration(Par<0>{}, Par<FULL>{}, j);
+      j++;
+    }
+    // now j == ntiles - 2 (or ntiles == 1 and j == 0)
+    if (j + 2 == ntiles) {
+      if (j & 1) iteration(Par<1>{}, Par<MASK>{}, j);
+      else iteration(Par<0>{}, Par<MASK>{}, j);
+      j++;
+    }
+    if (j & 1) iteration(Par<1>{}, Par<LAST>{}, j);
+    else iteration(Par<0>{}, Par<LAST>{}, j);
 
     // ---------------- epilogue: one division per row, one bf16 rounding per element
-    const float l = lsum + __shfl_xor(lsum, 32, 64);
+    float l_lo, l_hi;
+    swap_halves(lsum, l_lo, l_hi);
+    const float l = l_lo + l_hi;
     const float inv = __fdiv_rn(1.0f, l);
     if (qvalid) {
       uint16_t* op = p.out + ((int64_t)(s0 + qrow) * H + head) * HD;
@@ -304,9 +418,12 @@ hipError_t launch_attend(const void* q, const void* wq, int64_t T, int32_t H, fl
   p.H = H;
   p.eps = eps;
   p.c = (float)((double)scale * 1.4426950408889634074);
+  // a multiple of 8 workgroups (one slot per XCD each), at most grid_cap and no more than the work
   const int64_t max_work = Lw.max_items * H;
-  const int grid = (int)(max_work < grid_cap ? max_work : grid_cap);
-  hipLaunchKernelGGL(k_attn_fwd, dim3(grid), dim3(256), 0, stream, p);
+  int64_t grid = grid_cap < max_work ? grid_cap : max_work;
+  grid = (grid + 7) & ~(int64_t)7;
+  p.xcd_slots = (int32_t)(grid / 8);
+  hipLaunchKernelGGL(k_attn_fwd, dim3((unsigned)grid), dim3(256), 0, stream, p);
   return hipGetLastError();
 }
 
