@@ -192,7 +192,7 @@ int h3attn_attend(const void* q, const void* wq, int64_t tokens, int32_t heads, 
   DeviceInfo di;
   if ((rc = device_info(&di))) return rc;
   return launch_status(
-      launch_attend(q, wq, tokens, heads, eps, scale, out, lse, workspace, 2 * di.cus, (hipStream_t)stream));
+      launch_attend(q, wq, tokens, heads, eps, scale, out, lse, workspace, di.cus, (hipStream_t)stream));
 }
 
 int h3attn_fwd(const void* q, const void* k, const void* v, const int32_t* seg_ids, const void* wq, const void* wk,
@@ -220,7 +220,7 @@ int h3attn_fwd(const void* q, const void* k, const void* v, const int32_t* seg_i
   hipStream_t st = (hipStream_t)stream;
   if ((rc = launch_status(launch_plan(seg_ids, tokens, workspace, heads, st)))) return rc;
   if ((rc = launch_status(launch_prep_kv(k, v, wk, tokens, heads, eps, workspace, st)))) return rc;
-  return launch_status(launch_attend(q, wq, tokens, heads, eps, scale, out, lse, workspace, 2 * di.cus, st));
+  return launch_status(launch_attend(q, wq, tokens, heads, eps, scale, out, lse, workspace, di.cus, st));
 }
 
 int h3attn_status_read(const void* workspace, int32_t* device_status, void* stream) {

@@ -3,20 +3,26 @@
 // the q RMSNorm fused into the Q load prologue, FP32 accumulation and one bf16 rounding of the
 // output ("33B forward/backward" page, Scope: strict mode).
 //
-// Work item = (segment, 128-query tile, head); a persistent grid walks the items.  Each wave owns 32
-// queries.  The products are computed transposed so that one lane pair owns one query:
+// Work item = (segment, 256-query tile, head); a persistent grid of one workgroup per CU walks the
+// items.  The workgroup has 8 waves of 32 queries; waves w and w + 4 share a SIMD.  The products
+// are computed transposed so that one lane pair owns one query:
 //   S^T[key][query] = Khat . Qhat^T   (A = 32 keys x 16 dims from LDS, B = the wave's normed Q held
 //                                      in registers; v_mfma_f32_32x32x16_bf16)
 //   O^T[dim][query] += V^T . P^T      (A = 32 dims x 16 keys, read from the row-major V tile with
 //                                      ds_read_b64_tr_b16; B = P in fp16; v_mfma_f32_32x32x16_f16)
-// With that layout the softmax row max and row sum are lane-local over 32 scores plus one exchange
-// with lane ^ 32 (the other half of the query's keys), done with v_permlane32_swap.
+// The softmax row max and row sum are lane-local over 32 scores plus one exchange with lane ^ 32
+// (the other half of the query's keys), done with v_permlane32_swap.
 //
-// Pipeline.  K and V tiles (64 keys, 16 KB each) are copied from the workspace straight into LDS
-// with global_load_lds_dwordx4 (no register staging), double-buffered: at the top of iteration j
-// the loads of K(j+2) and V(j+1) are issued, and they have the whole iteration to land.  Within a
-// wave, iteration j overlaps the S MFMAs of tile j+1 with the softmax of tile j, then the P.V MFMAs
-// of tile j with the row maximum of tile j+1.  One barrier per iteration.
+// Ping-pong.  The KV walk of a wave alternates two kinds of phase: a matrix phase G(k) (the 16
+// score MFMAs of tile k+1 and the 16 P.V MFMAs of tile k, operands read from LDS a few MFMAs
+// ahead) and a vector phase V(k) (the softmax of tile k+1: maximum, lazy rescale, exp, sum, fp16
+// packing).  Waves 4..7 run one phase behind waves 0..3, and every phase ends at a workgroup
+// barrier, so on each SIMD one wave issues MFMAs back to back while its partner does the vector
+// work: the matrix cores stay busy and the softmax is hidden behind them.
+//
+// K and V tiles (64 keys, 16 KB each) are copied from the workspace straight into LDS with
+// buffer_load_dwordx4 ... lds (no register staging), double-buffered; the copies of K(m+1) and
+// V(m) are issued at the start of phase slot 2m and have two slots to land.
 //
 // LDS layouts are XOR-swizzled by 16-byte chunk (the copy picks, per lane, which global chunk
 // lands in its LDS slot), so that both read patterns are free of bank conflicts:
@@ -24,11 +30,10 @@
 //   V: row r, chunk c at slot c ^ 4 * (r & 3)     (ds_read_b64_tr_b16 of 8 rows x 64 B)
 //
 // Determinism and batch invariance: tiles are anchored at the segment's first key and walked in
-// ascending order; keys past the segment end are masked to -inf by a select (their K rows are
-// in-segment duplicates, their V rows likewise and they meet p = 0); every sum is a fixed tree; the
-// code path depends only on the segment length.  So each output row is a function of its own
-// segment's bytes, never of the batch, the offset, neighbours or the grid.  (Maxima are exact, so
-// their evaluation order cannot change a bit.)
+// ascending order; rows past the segment end are zero in LDS and their scores are replaced by -inf;
+// every sum is a fixed tree; the code path depends only on the segment length.  So each output row
+// is a function of its own segment's bytes, never of the batch, the offset, neighbours or the grid.
+// (Maxima are exact, so their evaluation order cannot change a bit.)
 //
 // Online softmax with a lazy maximum: the running maximum m (log2 units) moves only when a tile's
 // maximum exceeds it by more than 8, so p = exp2(s*c - m) <= 2^8 stays well inside fp16, and the
@@ -41,6 +46,9 @@ namespace h3 {
 constexpr float LN2 = 0.69314718055994530942f;
 constexpr float RESCALE_THRESHOLD = 8.0f;  // log2 units
 constexpr int TILE_ELEMS = BK * HD;        // 16-bit elements in one K or V tile (16 KB)
+constexpr int NWAVES = 8;                 // waves per workgroup (two per SIMD)
+static_assert(BK == 64, "two 32-key blocks per tile");
+static_assert(BQ == 32 * NWAVES, "one 32-query block per wave");
 
 struct AttnParams {
   const uint16_t* q;
@@ -55,7 +63,7 @@ struct AttnParams {
   int64_t T;
   int32_t H;
   float eps;
-  float c;  // scale * log2(e)
+  float c;            // scale * log2(e)
   int32_t xcd_slots;  // workgroups per XCD (grid / 8), for the XCD-aware item order
 };
 
@@ -71,9 +79,9 @@ __device__ __forceinline__ int v_off(int r, int d) { return r * HD + ((((d >> 3)
 // Copy one 64-row tile of a head-major [rows][128] 16-bit array into a swizzled LDS tile with
 // buffer_load_dwordx4 ... lds.  The buffer resource covers only the tile's rows inside the segment
 // (`valid` rows), so the rows past the segment end read as zeros: nothing outside the segment can
-// reach the products.  256 threads, 4 x 1 KB per wave; each lane's 16 bytes land at LDS base +
-// lane * 16, so the lane fetches the global chunk that belongs in that slot.  The slot pattern
-// repeats every 16 rows, so one lane offset serves all four blocks.
+// reach the products.  8 waves, 2 x 1 KB each; each lane's 16 bytes land at LDS base + lane * 16,
+// so the lane fetches the global chunk that belongs in that slot.  The slot pattern repeats every
+// 16 rows, so one lane offset serves both blocks.
 __device__ __forceinline__ int tile_lane_offset(bool is_v, int wv, int lane) {
   const int r = 4 * wv + (lane >> 4);  // tile row of the lane's slot in block wv (rows 4wv..4wv+3)
   const int slot = lane & 15;
@@ -86,27 +94,24 @@ __device__ __forceinline__ void tile_to_lds(const uint16_t* gtile, int valid, ui
   const __amdgpu_buffer_rsrc_t rs =
       __builtin_amdgcn_make_buffer_rsrc((void*)gtile, (short)0, (valid < BK ? valid : BK) * 256, 0x00020000);
 #pragma unroll
-  for (int i = 0; i < 4; i++)  // block 4i + wv = rows 16i + 4wv .. +3
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void*)(lds_tile + (4 * i + wv) * 4 * HD), 16,
-                                             lane_off + i * 4096, 0, 0, 0);
+  for (int i = 0; i < BK / (4 * NWAVES); i++)  // block NWAVES*i + wv = rows 4*NWAVES*i + 4wv .. +3
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void*)(lds_tile + (NWAVES * i + wv) * 4 * HD), 16,
+                                             lane_off + i * NWAVES * 1024, 0, 0, 0);
 }
 
-// Transposed LDS read (gfx950): within each 16-lane group, lane s supplies the address of 4
-// consecutive 16-bit elements C_s; lane s receives {C_{s/4}[s%4], C_{4+s/4}[s%4], C_{8+s/4}[s%4],
-// C_{12+s/4}[s%4]}.  With C_s = V[key0 + s/4][dim0 + 4(s%4) .. +3] lane s gets V[key0 + i][dim0 + s],
-// i = 0..3: four consecutive keys of one dim, the A-operand layout of a P.V MFMA.
-__device__ __forceinline__ i16x4 tr_read(const uint16_t* lds_ptr) {
-  return __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(uint16_t*)lds_ptr);
-}
+// Transposed LDS read (ds_read_b64_tr_b16, gfx950): within each 16-lane group, lane s supplies the
+// address of 4 consecutive 16-bit elements C_s; lane s receives {C_{s/4}[s%4], C_{4+s/4}[s%4],
+// C_{8+s/4}[s%4], C_{12+s/4}[s%4]}.  With C_s = V[key0 + s/4][dim0 + 4(s%4) .. +3] lane s gets
+// V[key0 + i][dim0 + s], i = 0..3: four consecutive keys of one dim, the A-operand layout of a P.V
+// MFMA.  (Issued as inline assembly below: tr_read_asm.)
 
-// The value of lane ^ 32 (the other half of this query's keys), exchanged without LDS.
-__device__ __forceinline__ void swap_halves(float x, float& lo_half, float& hi_half) {
+// Every lane receives (x of lane l % 32, x of lane l % 32 + 32) in some fixed order; callers only
+// combine the pair with commutative operations (max, +), which give the same bits either way.
+__device__ __forceinline__ void swap_halves(float x, float& a, float& b) {
   const auto r = __builtin_amdgcn_permlane32_swap(__builtin_bit_cast(uint32_t, x), __builtin_bit_cast(uint32_t, x),
                                                   false, false);
-  // r[0]: lanes 0-31 keep x, lanes 32-63 receive x of lanes 0-31; r[1]: the other way round.  So
-  // every lane holds (x of lane l%32, x of lane l%32 + 32), in that order, in both halves.
-  lo_half = __builtin_bit_cast(float, (uint32_t)r[0]);
-  hi_half = __builtin_bit_cast(float, (uint32_t)r[1]);
+  a = __builtin_bit_cast(float, (uint32_t)r[0]);
+  b = __builtin_bit_cast(float, (uint32_t)r[1]);
 }
 
 template <int N>
@@ -118,22 +123,8 @@ __device__ __forceinline__ float tree_sum(const float* x) {
   }
 }
 
-// S^T for the 64 keys of one LDS tile: S[kb] holds keys 32kb + 8(i/4) + 4hh + (i%4) of the lane's
-// query.  The k-slices are accumulated in ascending dimension order.
-__device__ __forceinline__ void tile_scores(const uint16_t* Ks, const bf16x8* qf, int l32, int hh, f32x16* S) {
-#pragma unroll
-  for (int kb = 0; kb < 2; kb++) {
-#pragma unroll
-    for (int i = 0; i < 16; i++) S[kb][i] = 0.0f;
-#pragma unroll
-    for (int m = 0; m < 8; m++) {
-      const bf16x8 a = *(const bf16x8*)(Ks + k_off(32 * kb + l32, 16 * m + 8 * hh));
-      S[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[m], S[kb], 0, 0, 0);
-    }
-  }
-}
-
-// Keys at or past `rem` (the valid keys of the segment's last tile) get -inf.
+// Keys at or past `rem` (the valid keys of the segment's last tile) get -inf.  S[kb] holds keys
+// 32kb + 8(i/4) + 4hh + (i%4) of the lane's query.
 __device__ __forceinline__ void mask_tail(f32x16* S, int rem, int hh) {
 #pragma unroll
   for (int kb = 0; kb < 2; kb++)
@@ -142,20 +133,64 @@ __device__ __forceinline__ void mask_tail(f32x16* S, int rem, int hh) {
       if (32 * kb + 8 * (i >> 2) + 4 * hh + (i & 3) >= rem) S[kb][i] = -__builtin_inff();
 }
 
-// Maximum over the query's 64 keys of one tile (exact, so any evaluation order gives these bits).
+// Maximum over the query's 64 keys of one tile (exact: any evaluation order gives these bits).
 __device__ __forceinline__ float tile_max(const f32x16* S) {
-  float a = __builtin_fmaxf(__builtin_fmaxf(S[0][0], S[0][1]), S[0][2]);
-  float b = __builtin_fmaxf(__builtin_fmaxf(S[1][0], S[1][1]), S[1][2]);
+  float a = -__builtin_inff();
 #pragma unroll
-  for (int i = 3; i < 15; i += 2) {
-    a = __builtin_fmaxf(__builtin_fmaxf(a, S[0][i]), S[0][i + 1]);
-    b = __builtin_fmaxf(__builtin_fmaxf(b, S[1][i]), S[1][i + 1]);
+  for (int kb = 0; kb < 2; kb++)
+#pragma unroll
+    for (int i = 0; i < 16; i += 2) a = __builtin_fmaxf(__builtin_fmaxf(a, S[kb][i]), S[kb][i + 1]);
+  float x, y;
+  swap_halves(a, x, y);
+  return __builtin_fmaxf(x, y);
+}
+
+// p -> packed fp16 B operand (8 keys), round to nearest even.
+__device__ __forceinline__ f16x8 pack_p(const float* p) {
+  u32x4 w4;
+#pragma unroll
+  for (int i = 0; i < 4; i++) {
+    const f32x2 two = {p[2 * i], p[2 * i + 1]};
+    w4[i] = __builtin_bit_cast(uint32_t, __builtin_convertvector(two, f16x2));
   }
-  a = __builtin_fmaxf(a, S[0][15]);
-  b = __builtin_fmaxf(b, S[1][15]);
-  float lo, hi;
-  swap_halves(__builtin_fmaxf(a, b), lo, hi);
-  return __builtin_fmaxf(lo, hi);
+  return __builtin_bit_cast(f16x8, w4);
+}
+
+// Q prologue for one 32-query block: load, RMSNorm (2 lanes per row), round to bf16 B-operands.
+__device__ __forceinline__ void load_q(const AttnParams& p, int s0, int qrow, bool qvalid, int head, int hh,
+                                       bf16x8* qf) {
+  float x[8][8];
+  const uint16_t* qp = p.q + ((int64_t)(s0 + (qvalid ? qrow : 0)) * p.H + head) * HD;
+#pragma unroll
+  for (int m = 0; m < 8; m++) {
+    u32x4 w4 = {0, 0, 0, 0};
+    if (qvalid) w4 = *(const u32x4*)(qp + 16 * m + 8 * hh);
+    unpack8_bf16(w4, x[m]);
+  }
+  if (p.wq) {
+    double part[8];
+#pragma unroll
+    for (int m = 0; m < 8; m++) part[m] = chunk_sumsq(x[m]);
+    const double r = norm_rscale(row_total_2lanes(part), p.eps);
+#pragma unroll
+    for (int m = 0; m < 8; m++) {
+      float wf[8];
+      unpack8_bf16(*(const u32x4*)(p.wq + 16 * m + 8 * hh), wf);
+      qf[m] = __builtin_bit_cast(bf16x8, norm_chunk(x[m], wf, r));
+    }
+  } else {
+#pragma unroll
+    for (int m = 0; m < 8; m++) {
+      u32x4 o;
+#pragma unroll
+      for (int i = 0; i < 4; i++) o[i] = pack_bf16(x[m][2 * i], x[m][2 * i + 1]);
+      qf[m] = __builtin_bit_cast(bf16x8, o);
+    }
+  }
+  if (!qvalid) {
+#pragma unroll
+    for (int m = 0; m < 8; m++) qf[m] = __builtin_bit_cast(bf16x8, u32x4{0, 0, 0, 0});
+  }
 }
 
 template <int N>
@@ -163,19 +198,92 @@ struct Par {
   static constexpr int value = N;
 };
 
-// Modes of one KV iteration j (tile j's softmax and P.V, tile j+1's scores):
-//   FULL  j + 2 < ntiles: tile j+1 is a full tile, K(j+2) and V(j+1) are prefetched
-//   MASK  j + 2 == ntiles: tile j+1 is the segment's last tile (masked past `rem`), V(j+1) prefetched
-//   LAST  j + 1 == ntiles: no next tile
-enum Mode { FULL = 0, MASK = 1, LAST = 2 };
+// Scores of one 64-key tile: S[kb] holds keys 32kb + 8(i/4) + 4hh + (i%4) of the lane's query.
+// Each accumulator sums its k-slices m = 0..7 in order.
+template <int NPRE>
+__device__ __forceinline__ void gemm_scores(const uint16_t* Kb, const bf16x8* qf, int l32, int hh, f32x16* S) {
+  bf16x8 ka[16];
+  auto kread = [&](int s) { ka[s] = *(const bf16x8*)(Kb + k_off(32 * (s & 1) + l32, 16 * (s >> 1) + 8 * hh)); };
+#pragma unroll
+  for (int kb = 0; kb < 2; kb++)
+#pragma unroll
+    for (int i = 0; i < 16; i++) S[kb][i] = 0.0f;
+#pragma unroll
+  for (int s = 0; s < NPRE; s++) kread(s);
+#pragma unroll
+  for (int s = 0; s < 16; s++) {  // step s = 2m + kb
+    if (s + NPRE < 16) kread(s + NPRE);
+    S[s & 1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka[s], qf[s >> 1], S[s & 1], 0, 0, 0);
+    __builtin_amdgcn_sched_barrier(0);
+  }
+}
 
-__global__ __launch_bounds__(256, 2) void k_attn_fwd(AttnParams p) {
+// ds_read_b64_tr_b16 as inline assembly.  The builtin carries no memory operand, so the compiler's
+// wait insertion assumes it may read what an outstanding global-to-LDS copy writes and waits for
+// every copy before it, which serialises the copies with the matrix phase.  The assembly form is
+// invisible to that analysis, so the caller waits for the results itself (LGKM_WAIT_TIED).  base is
+// an LDS byte address, OFF a constant byte offset (the instruction's 16-bit offset field).
+template <int OFF>
+__device__ __forceinline__ u32x2 tr_read_asm(uint32_t base) {
+  static_assert(OFF >= 0 && OFF < 65536, "ds offset field");
+  u32x2 r;
+  asm volatile("ds_read_b64_tr_b16 %0, %1 offset:%2" : "=v"(r) : "v"(base), "i"(OFF));
+  return r;
+}
+
+// Wait until at most N LDS operations are outstanding; x and y are tied to the wait, so nothing
+// that reads them can be scheduled before it.
+#define LGKM_WAIT_TIED(N, x, y) asm volatile("s_waitcnt lgkmcnt(" #N ")" : "+v"(x), "+v"(y))
+
+// V operand of P.V step T = 4ks + db from V buffer VBUF: rows 16ks + {0..7} and 16ks + 8 + {0..7}
+// of the tile.  vb[db] is the lane's LDS byte address of (row tr_row, column 32db + tr_col) in
+// buffer 0; the swizzle of a row depends on row & 3 only, so the other rows are constant offsets.
+template <int VBUF, int T>
+__device__ __forceinline__ void pv_read(const uint32_t* vb, u32x2 (&va)[16][2]) {
+  constexpr int ks = T >> 2, db = T & 3;
+  constexpr int off = (2 + VBUF) * TILE_ELEMS * 2 + 16 * ks * HD * 2;
+  va[T][0] = tr_read_asm<off>(vb[db]);
+  va[T][1] = tr_read_asm<off + 8 * HD * 2>(vb[db]);
+}
+
+// O^T += V^T P^T for one 64-key tile, step T = 4ks + db, so every O[db] sums its key slices in
+// order.  V operands are read 4 steps ahead; before step T's MFMA the reads of the steps after it
+// (two each, at most 4 steps) may still be in flight, and no other LDS operation is (the score
+// MFMAs before this have consumed their K reads).
+template <int VBUF, int T>
+__device__ __forceinline__ void pv_step(const uint32_t* vb, const f16x8* pf, f32x16* O, u32x2 (&va)[16][2]) {
+  if constexpr (T + 4 < 16) pv_read<VBUF, T + 4>(vb, va);
+  constexpr int ahead = (T + 4 < 16 ? T + 4 : 15) - T;  // later steps already issued
+  if constexpr (ahead == 4) LGKM_WAIT_TIED(8, va[T][0], va[T][1]);
+  else if constexpr (ahead == 3) LGKM_WAIT_TIED(6, va[T][0], va[T][1]);
+  else if constexpr (ahead == 2) LGKM_WAIT_TIED(4, va[T][0], va[T][1]);
+  else if constexpr (ahead == 1) LGKM_WAIT_TIED(2, va[T][0], va[T][1]);
+  else LGKM_WAIT_TIED(0, va[T][0], va[T][1]);
+  const f16x4 lo = __builtin_bit_cast(f16x4, va[T][0]), hi = __builtin_bit_cast(f16x4, va[T][1]);
+  const f16x8 a = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+  O[T & 3] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a, pf[T >> 2], O[T & 3], 0, 0, 0);
+  __builtin_amdgcn_sched_barrier(0);
+  if constexpr (T + 1 < 16) pv_step<VBUF, T + 1>(vb, pf, O, va);
+}
+
+template <int VBUF>
+__device__ __forceinline__ void gemm_pv(const uint32_t* vb, const f16x8* pf, f32x16* O) {
+  u32x2 va[16][2];
+  pv_read<VBUF, 0>(vb, va);
+  pv_read<VBUF, 1>(vb, va);
+  pv_read<VBUF, 2>(vb, va);
+  pv_read<VBUF, 3>(vb, va);
+  pv_step<VBUF, 0>(vb, pf, O, va);
+}
+
+__global__ __launch_bounds__(64 * NWAVES, 1) void k_attn_fwd(AttnParams p) {
   // K tiles in buffers 0, 1 and V tiles in buffers 2, 3 (16 KB each)
   __shared__ __attribute__((aligned(1024))) uint16_t lds[4 * TILE_ELEMS];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform
+  const int grp = wv >> 2;     // 0: leading waves, 1: waves one phase behind (same SIMDs)
   const int hh = lane >> 5;    // which half of the 16-wide MFMA k-slice this lane feeds
   const int l32 = lane & 31;   // query (B / D column) index within the wave
   const int64_t T = p.T;
@@ -184,12 +292,11 @@ __global__ __launch_bounds__(256, 2) void k_attn_fwd(AttnParams p) {
   if (p.hdr->status != 0) {
     // A data error was recorded: make the result unmistakably invalid.
     const int64_t n16 = T * H * HD / 8;
+    const int64_t stride = (int64_t)gridDim.x * blockDim.x;
     const u32x4 nan4 = {0x7FC07FC0u, 0x7FC07FC0u, 0x7FC07FC0u, 0x7FC07FC0u};
-    for (int64_t e = (int64_t)blockIdx.x * 256 + tid; e < n16; e += (int64_t)gridDim.x * 256)
-      *(u32x4*)(p.out + e * 8) = nan4;
+    for (int64_t e = (int64_t)blockIdx.x * blockDim.x + tid; e < n16; e += stride) *(u32x4*)(p.out + e * 8) = nan4;
     if (p.lse)
-      for (int64_t e = (int64_t)blockIdx.x * 256 + tid; e < T * H; e += (int64_t)gridDim.x * 256)
-        p.lse[e] = __builtin_nanf("");
+      for (int64_t e = (int64_t)blockIdx.x * blockDim.x + tid; e < T * H; e += stride) p.lse[e] = __builtin_nanf("");
     return;
   }
 
@@ -211,6 +318,10 @@ __global__ __launch_bounds__(256, 2) void k_attn_fwd(AttnParams p) {
   const int tr_row = 4 * hh + ((lane & 15) >> 2);
   const int tr_col = 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
   const float c = p.c;
+  uint32_t vb[4];  // LDS byte addresses of the lane's V operand rows (buffer 0, rows tr_row), by db
+#pragma unroll
+  for (int db = 0; db < 4; db++)
+    vb[db] = (uint32_t)(size_t)(const __attribute__((address_space(3))) uint16_t*)(lds + v_off(tr_row, 32 * db + tr_col));
 
   for (int round = 0;; round++) {
     const int64_t v = ((int64_t)round * 8 + xcd) * nslots + slot;
@@ -231,157 +342,111 @@ __global__ __launch_bounds__(256, 2) void k_attn_fwd(AttnParams p) {
 
     // Every wave has finished reading LDS for the previous item before it is overwritten.
     __syncthreads();
-    tile_to_lds(kbase, L, lds, wv, k_lane_off);
-    tile_to_lds(vbase, L, lds + 2 * TILE_ELEMS, wv, v_lane_off);
-    if (ntiles > 1) tile_to_lds(kbase + BK * HD, L - BK, lds + TILE_ELEMS, wv, k_lane_off);
+    tile_to_lds(kbase, L, lds, wv, k_lane_off);  // K(0)
 
-    // ---------------- Q prologue: load, RMSNorm (2 lanes per row), round to bf16 B-operands
     const int qrow = qt * BQ + wv * 32 + l32;
     const bool qvalid = qrow < L;
     bf16x8 qf[8];
-    {
-      float x[8][8];
-      const uint16_t* qp = p.q + ((int64_t)(s0 + (qvalid ? qrow : 0)) * H + head) * HD;
-#pragma unroll
-      for (int m = 0; m < 8; m++) {
-        u32x4 w4 = {0, 0, 0, 0};
-        if (qvalid) w4 = *(const u32x4*)(qp + 16 * m + 8 * hh);
-        unpack8_bf16(w4, x[m]);
-      }
-      if (p.wq) {
-        double part[8];
-#pragma unroll
-        for (int m = 0; m < 8; m++) part[m] = chunk_sumsq(x[m]);
-        const double r = norm_rscale(row_total_2lanes(part), p.eps);
-#pragma unroll
-        for (int m = 0; m < 8; m++) {
-          float wf[8];
-          unpack8_bf16(*(const u32x4*)(p.wq + 16 * m + 8 * hh), wf);
-          const u32x4 o = norm_chunk(x[m], wf, r);
-          qf[m] = __builtin_bit_cast(bf16x8, o);
-        }
-      } else {
-#pragma unroll
-        for (int m = 0; m < 8; m++) {
-          u32x4 o;
-#pragma unroll
-          for (int i = 0; i < 4; i++) o[i] = pack_bf16(x[m][2 * i], x[m][2 * i + 1]);
-          qf[m] = __builtin_bit_cast(bf16x8, o);
-        }
-      }
-      if (!qvalid) {
-#pragma unroll
-        for (int m = 0; m < 8; m++) qf[m] = __builtin_bit_cast(bf16x8, u32x4{0, 0, 0, 0});
-      }
-    }
+    load_q(p, s0, qrow, qvalid, head, hh, qf);
 
-    // ---------------- scores of tile 0
-    __builtin_amdgcn_s_waitcnt(0xF70);  // vmcnt(0): this wave's tile copies have landed
-    __syncthreads();                    // ... and every other wave's
-    f32x16 S[2];
-    tile_scores(lds, qf, l32, hh, S);
-    if (ntiles == 1 && rem < BK) mask_tail(S, rem, hh);
-
+    f32x16 S[2];   // scores of the tile whose softmax is next
+    f16x8 pf[4];   // P of the tile whose P.V is next
     f32x16 O[4];
 #pragma unroll
     for (int d = 0; d < 4; d++)
 #pragma unroll
       for (int i = 0; i < 16; i++) O[d][i] = 0.0f;
     float lsum = 0.0f;
-    float m_run = tile_max(S) * c;  // first tile: m is the tile maximum (log2 units)
+    float m_run = 0.0f;
 
-    // One KV iteration; PAR = j & 1 selects the buffers: K(j) and V(j) live in buffers PAR and 2+PAR.
-    auto iteration = [&](auto par, auto mode, int j) {
-      constexpr int PAR = decltype(par)::value;
-      constexpr int MODE = decltype(mode)::value;
-      uint16_t* const Kcur = lds + PAR * TILE_ELEMS;         // K(j): free once the iteration starts
-      const uint16_t* const Knext = lds + (1 - PAR) * TILE_ELEMS;  // K(j+1)
-      const uint16_t* const Vcur = lds + (2 + PAR) * TILE_ELEMS;   // V(j)
-      uint16_t* const Vnext = lds + (3 - PAR) * TILE_ELEMS;        // V(j+1): its buffer held V(j-1)
-      __builtin_amdgcn_s_waitcnt(0xF70);
+    // Copies issued at phase slot 2m: K(m+1) and V(m), into the buffers of K(m-1) and V(m-2),
+    // which were last read in slot 2m-1.
+    // The buffer parity MP = m & 1 is a compile-time constant at every call, so the compiler can
+    // see that a copy never writes the buffers being read and needs no wait for it.
+    auto issue_copies = [&](int t, auto mp) {
+      constexpr int MP = decltype(mp)::value;
+      const int m = t >> 1;
+      if (m + 1 < ntiles)
+        tile_to_lds(kbase + (int64_t)(m + 1) * BK * HD, L - (m + 1) * BK, lds + (1 - MP) * TILE_ELEMS, wv,
+                    k_lane_off);
+      if (m < ntiles)
+        tile_to_lds(vbase + (int64_t)m * BK * HD, L - m * BK, lds + (2 + MP) * TILE_ELEMS, wv, v_lane_off);
+    };
+
+    // Phase tau of this wave runs in slot t = tau + grp.  Even tau: G(k), k = tau/2 - 1 (scores of
+    // tile k+1 from K buffer (k+1)&1, P.V of tile k from V buffer k&1).  Odd tau: V(k),
+    // k = (tau-1)/2 - 1 (softmax of tile k+1).  TM = tau % 4 fixes the buffers at compile time.
+    auto phase = [&](int tau, auto tm) {
+      constexpr int TM = decltype(tm)::value;
+      const int t = tau + grp;
+      if (t & 1) __builtin_amdgcn_s_waitcnt(0xF70);  // vmcnt(0): slot t-1's copies land before slot t+1
       __syncthreads();
-      if constexpr (MODE == FULL) tile_to_lds(kbase + (int64_t)(j + 2) * BK * HD, L - (j + 2) * BK, Kcur, wv, k_lane_off);
-      if constexpr (MODE != LAST) tile_to_lds(vbase + (int64_t)(j + 1) * BK * HD, L - (j + 1) * BK, Vnext, wv, v_lane_off);
-
-      // scores of tile j+1 (MFMA) alongside the softmax of tile j (VALU)
-      f32x16 Sn[2];
-      if constexpr (MODE != LAST) tile_scores(Knext, qf, l32, hh, Sn);
-
-      float pr[32];
-#pragma unroll
-      for (int kb = 0; kb < 2; kb++)
-#pragma unroll
-        for (int i = 0; i < 16; i++) pr[16 * kb + i] = __builtin_amdgcn_exp2f(__builtin_fmaf(S[kb][i], c, -m_run));
-      lsum += tree_sum<32>(pr);
-      f16x8 pf[4];
-#pragma unroll
-      for (int ks = 0; ks < 4; ks++) {
-        u32x4 w4;
-#pragma unroll
-        for (int i = 0; i < 4; i++) {
-          const f32x2 two = {pr[8 * ks + 2 * i], pr[8 * ks + 2 * i + 1]};
-          w4[i] = __builtin_bit_cast(uint32_t, __builtin_convertvector(two, f16x2));  // RNE
-        }
-        pf[ks] = __builtin_bit_cast(f16x8, w4);
+      // slot t = tau + grp is even (a copy slot) for tau % 2 == grp; m = t / 2 has the parity below
+      if constexpr ((TM & 1) == 0) {
+        if (grp == 0) issue_copies(t, Par<(TM >> 1)>{});  // t = tau = 4n + TM: m = 2n + TM/2
+      } else {
+        if (grp == 1) issue_copies(t, Par<(TM == 1 ? 1 : 0)>{});  // t = 4n + TM + 1: m = 2n + 1 or 2n + 2
       }
-
-      // O^T += V^T P^T ; A rows = dims 32db + l32, A k-slots = keys 16ks + {4hh..4hh+3, 8+4hh..8+4hh+3}
+      if constexpr ((TM & 1) == 0) {
+        const int k = tau / 2 - 1;
+        constexpr int KBUF = TM == 0 ? 0 : 1;  // K(k+1): k = 2n-1 -> K(2n); k = 2n -> K(2n+1)
+        constexpr int VBUF = TM == 0 ? 1 : 0;  // V(k)
+        if (k + 1 < ntiles) gemm_scores<4>(lds + KBUF * TILE_ELEMS, qf, l32, hh, S);
+        if (k >= 0) gemm_pv<VBUF>(vb, pf, O);
+      } else {
+        const int k = (tau - 1) / 2 - 1;
+        if (k + 1 < ntiles) {
+          if (k + 1 == ntiles - 1 && rem < BK) mask_tail(S, rem, hh);
+          const float mt = tile_max(S) * c;
+          if (k + 1 == 0) {
+            m_run = mt;  // first tile: m is the tile maximum (log2 units)
+          } else {
+            const bool need = mt > m_run + RESCALE_THRESHOLD;
+            if (__builtin_expect(__ballot(need) != 0, 0)) {  // rare: keep it a branch
+              const float m_new = need ? mt : m_run;
+              const float alpha = need ? __builtin_amdgcn_exp2f(m_run - m_new) : 1.0f;
+              lsum *= alpha;
 #pragma unroll
-      for (int ks = 0; ks < 4; ks++) {
+              for (int d = 0; d < 4; d++)
 #pragma unroll
-        for (int db = 0; db < 4; db++) {
-          const i16x4 lo = tr_read(Vcur + v_off(16 * ks + tr_row, 32 * db + tr_col));
-          const i16x4 hi = tr_read(Vcur + v_off(16 * ks + 8 + tr_row, 32 * db + tr_col));
-          const f16x4 flo = __builtin_bit_cast(f16x4, lo), fhi = __builtin_bit_cast(f16x4, hi);
-          const f16x8 a = {flo[0], flo[1], flo[2], flo[3], fhi[0], fhi[1], fhi[2], fhi[3]};
-          O[db] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a, pf[ks], O[db], 0, 0, 0);
+                for (int i = 0; i < 16; i++) O[d][i] *= alpha;
+              m_run = m_new;
+            }
+          }
+          float pr[32];
+#pragma unroll
+          for (int kb = 0; kb < 2; kb++)
+#pragma unroll
+            for (int i = 0; i < 16; i++)
+              pr[16 * kb + i] = __builtin_amdgcn_exp2f(__builtin_fmaf(S[kb][i], c, -m_run));
+          lsum += tree_sum<32>(pr);
+#pragma unroll
+          for (int ks = 0; ks < 4; ks++) pf[ks] = pack_p(&pr[8 * ks]);
         }
-      }
-
-      if constexpr (MODE != LAST) {
-        if constexpr (MODE == MASK) {
-          if (rem < BK) mask_tail(Sn, rem, hh);
-        }
-        const float mt = tile_max(Sn) * c;
-        const bool need = mt > m_run + RESCALE_THRESHOLD;
-        if (__builtin_expect(__ballot(need) != 0, 0)) {  // rare: keep it a branch, not a select
-          const float m_new = need ? mt : m_run;
-          const float alpha = need ? __builtin_amdgcn_exp2f(m_run - m_new) : 1.0f;
-          lsum *= alpha;
-#pragma unroll
-          for (int d = 0; d < 4; d++)
-#pragma unroll
-            for (int i = 0; i < 16; i++) O[d][i] *= alpha;
-          m_run = m_new;
-        }
-        S[0] = Sn[0];
-        S[1] = Sn[1];
       }
     };
 
-    // j = 0 .. ntiles-3 in FULL mode (unrolled by two so the buffers are fixed), then MASK, LAST
-    int j = 0;
-    for (; j + 3 < ntiles; j += 2) {
-      iteration(Par<0>{}, Par<FULL>{}, j);
-      iteration(Par<1>{}, Par<FULL>{}, j + 1);
+    __builtin_amdgcn_s_waitcnt(0xF70);  // K(0) has landed (the slot-0 barrier publishes it)
+    if (grp == 1) {                     // slot 0 of the trailing waves: barrier and copies only
+      __syncthreads();
+      issue_copies(0, Par<0>{});
     }
-    if (j + 2 < ntiles) {
-      iteration(Par<0>{}, Par<FULL>{}, j);
-      j++;
+    const int tau_last = 2 * ntiles + 1 - grp;
+    int tau = 0;
+    for (; tau + 3 <= tau_last; tau += 4) {
+      phase(tau, Par<0>{});
+      phase(tau + 1, Par<1>{});
+      phase(tau + 2, Par<2>{});
+      phase(tau + 3, Par<3>{});
     }
-    // now j == ntiles - 2 (or ntiles == 1 and j == 0)
-    if (j + 2 == ntiles) {
-      if (j & 1) iteration(Par<1>{}, Par<MASK>{}, j);
-      else iteration(Par<0>{}, Par<MASK>{}, j);
-      j++;
-    }
-    if (j & 1) iteration(Par<1>{}, Par<LAST>{}, j);
-    else iteration(Par<0>{}, Par<LAST>{}, j);
+    if (tau <= tau_last) phase(tau, Par<0>{});
+    if (tau + 1 <= tau_last) phase(tau + 1, Par<1>{});
+    if (tau + 2 <= tau_last) phase(tau + 2, Par<2>{});
 
     // ---------------- epilogue: one division per row, one bf16 rounding per element
-    float l_lo, l_hi;
-    swap_halves(lsum, l_lo, l_hi);
-    const float l = l_lo + l_hi;
+    float la, lb;
+    swap_halves(lsum, la, lb);
+    const float l = la + lb;
     const float inv = __fdiv_rn(1.0f, l);
     if (qvalid) {
       uint16_t* op = p.out + ((int64_t)(s0 + qrow) * H + head) * HD;
@@ -423,7 +488,7 @@ hipError_t launch_attend(const void* q, const void* wq, int64_t T, int32_t H, fl
   int64_t grid = grid_cap < max_work ? grid_cap : max_work;
   grid = (grid + 7) & ~(int64_t)7;
   p.xcd_slots = (int32_t)(grid / 8);
-  hipLaunchKernelGGL(k_attn_fwd, dim3((unsigned)grid), dim3(256), 0, stream, p);
+  hipLaunchKernelGGL(k_attn_fwd, dim3((unsigned)grid), dim3(64 * NWAVES), 0, stream, p);
   return hipGetLastError();
 }
 

@@ -39,8 +39,9 @@ def test_parity_batch2_full():
 
 
 def test_parity_ragged_tiles():
-    """Segment lengths around the 64-key and 128-query tile edges, plus single-token segments."""
-    lens = [1, 2, 63, 64, 65, 127, 128, 129, 300, 3, 1, 257]
+    """Segment lengths around the 32-key and 256-query tile edges (and the 64/128 edges of other
+    tilings), plus single-token segments."""
+    lens = [1, 2, 31, 32, 33, 63, 64, 65, 127, 128, 129, 255, 256, 257, 300, 3, 1, 513]
     _check_full("ragged", workloads.random_inputs(lens, 3, seed=21))
 
 
@@ -57,7 +58,7 @@ def test_parity_other_scale_and_eps():
 
 def _sample_rows(L, n, seed):
     rng = np.random.default_rng(seed)
-    fixed = [0, 1, 63, 64, 127, 128, L // 2, L - 129, L - 65, L - 2, L - 1]
+    fixed = [0, 1, 31, 32, 63, 64, 127, 128, 255, 256, L // 2, L - 257, L - 129, L - 65, L - 33, L - 2, L - 1]
     return np.unique(np.concatenate([fixed, rng.integers(0, L, n)]))
 
 
