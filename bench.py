@@ -26,6 +26,25 @@ def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
 
+def traffic_bytes(workload):
+    """HBM bytes per launch of the attention kernel, from the counter summary committed under
+    profiles/ (FETCH_SIZE + WRITE_SIZE of one dispatch, each scaled by the same counter's reading for
+    the calibration kernel), or None when there is none for this workload or the kernel source has
+    changed since the counters were taken."""
+    import hashlib
+    path = os.path.join(ROOT, "profiles", f"k_attn_fwd_{workload}.traffic.json")
+    src = os.path.join(ROOT, "deterministic_invariant_attention_amd", "csrc", "k_attn_fwd.hip")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        rec = json.load(f)
+    with open(src, "rb") as f:
+        sha = hashlib.sha256(f.read()).hexdigest()
+    if rec.get("kernel_source_sha256") != sha:
+        return None
+    return int(rec["traffic_bytes"])
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -62,13 +81,17 @@ def main():
     log(f"workload {wl.name}: {wl.description}; nominal {flops:.4e} FLOP/step")
 
     if args.copy_calibration:
-        src = torch.empty(256 << 20, dtype=torch.uint8, device=dev).fill_(1)
+        # A plain elementwise kernel of known traffic (256 MiB read, 256 MiB written), the reference
+        # that scales the FETCH_SIZE / WRITE_SIZE counters of a --pmc run into bytes.  Its grid
+        # (64 Mi elements) tells it apart from every other dispatch of the run.
+        src = torch.full((64 << 20,), 1.0, dtype=torch.float32, device=dev)
         dst = torch.empty_like(src)
+        scrub = torch.full((128 << 20,), 0.0, dtype=torch.float32, device=dev)  # 512 MiB: evicts the 256 MB MALL
         torch.cuda.synchronize()
-        dst.copy_(src)
+        torch.mul(src, 2.0, out=dst)
         torch.cuda.synchronize()
-        log("copy calibration: 268435456 bytes read + 268435456 bytes written")
-        del src, dst
+        log("copy calibration: torch.mul over 67108864 fp32 (268435456 bytes read + 268435456 bytes written)")
+        del src, dst, scrub
 
     def step():
         h3.h3attn_fwd(g["q"], g["k"], g["v"], g["seg"], g["wq"], g["wk"], eps=wl.eps, scale=wl.scale, out=out,
@@ -158,8 +181,8 @@ def main():
                    "pct_bf16_mfma_peak": round(100 * value / PEAK_MFMA_TFLOPS, 2),
                    "repeat_bitwise": repeat_bitwise, "device_status": status},
         "roofline": {"bound": "mfma", "achieved": round(attn_tflops, 2), "peak": PEAK_MFMA_TFLOPS,
-                     "unit": "TFLOP/s", "frac": round(attn_tflops / PEAK_MFMA_TFLOPS, 4), "traffic": None,
-                     "kernel": "k_attn_fwd", "kernel_ms": round(attn_ms, 4)},
+                     "unit": "TFLOP/s", "frac": round(attn_tflops / PEAK_MFMA_TFLOPS, 4),
+                     "traffic": traffic_bytes(wl.name), "kernel": "k_attn_fwd", "kernel_ms": round(attn_ms, 4)},
         "cpu_baseline": cpu,
     }
     print(json.dumps(line), flush=True)
