@@ -22,7 +22,8 @@
 //
 // K and V tiles (64 keys, 16 KB each) are copied from the workspace straight into LDS with
 // buffer_load_dwordx4 ... lds (no register staging), double-buffered; the copies of K(m+1) and
-// V(m) are issued at the start of phase slot 2m and have two slots to land.
+// V(m) are issued at the start of phase slot 2m and have two slots to land: the phase barriers
+// carry no memory fence, and each wave waits for its own copies only before slot 2m+2.
 //
 // LDS layouts are XOR-swizzled by 16-byte chunk (the copy picks, per lane, which global chunk
 // lands in its LDS slot), so that both read patterns are free of bank conflicts:
@@ -191,6 +192,17 @@ __device__ __forceinline__ void load_q(const AttnParams& p, int s0, int qrow, bo
 #pragma unroll
     for (int m = 0; m < 8; m++) qf[m] = __builtin_bit_cast(bf16x8, u32x4{0, 0, 0, 0});
   }
+}
+
+// Workgroup barrier between phases, without the memory fence of __syncthreads: that fence makes
+// every wave wait for all of its outstanding global-to-LDS copies at every phase, while a copy only
+// has to land two phases after it is issued (the explicit vmcnt wait in the phase loop).  Every LDS
+// read before the barrier has been consumed, so waited for, by then; the empty asm statements keep
+// the compiler from moving memory operations across the barrier.
+__device__ __forceinline__ void phase_barrier() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
 }
 
 template <int N>
@@ -379,8 +391,9 @@ __global__ __launch_bounds__(64 * NWAVES, 1) void k_attn_fwd(AttnParams p) {
     auto phase = [&](int tau, auto tm) {
       constexpr int TM = decltype(tm)::value;
       const int t = tau + grp;
-      if (t & 1) __builtin_amdgcn_s_waitcnt(0xF70);  // vmcnt(0): slot t-1's copies land before slot t+1
-      __syncthreads();
+      // copies issued at slot t-2 are read from slot t on: wait for them (vmcnt(0)) before the barrier
+      if (!(t & 1) && t >= 2) __builtin_amdgcn_s_waitcnt(0xF70);
+      phase_barrier();
       // slot t = tau + grp is even (a copy slot) for tau % 2 == grp; m = t / 2 has the parity below
       if constexpr ((TM & 1) == 0) {
         if (grp == 0) issue_copies(t, Par<(TM >> 1)>{});  // t = tau = 4n + TM: m = 2n + TM/2
@@ -428,7 +441,7 @@ __global__ __launch_bounds__(64 * NWAVES, 1) void k_attn_fwd(AttnParams p) {
 
     __builtin_amdgcn_s_waitcnt(0xF70);  // K(0) has landed (the slot-0 barrier publishes it)
     if (grp == 1) {                     // slot 0 of the trailing waves: barrier and copies only
-      __syncthreads();
+      phase_barrier();
       issue_copies(0, Par<0>{});
     }
     const int tau_last = 2 * ntiles + 1 - grp;
