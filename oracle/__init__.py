@@ -13,6 +13,9 @@ Functions follow the RL-Kernel MiniMax-H3 pull-request pages:
   * ``fwd`` / ``fwd_rows``: attention(causal=False) over packed sequences (same page, Bindings and
     Summary), evaluated exactly in FP64 ("33B forward/backward", Scope: FP32 accumulation, one
     final rounding -- the oracle is the value such a kernel approximates).
+  * ``bwd``: the gradients of that composite (norm, bf16 rounding taken as the identity, attention)
+    with respect to q, k, v and both norm weights, in FP64 -- the node inside the training step's
+    backward ("33B forward/backward" page).
 """
 from __future__ import annotations
 
@@ -69,7 +72,10 @@ def _load():
     lib.oracle_qknorm.argtypes = [P, P, P, I64, I32, D]
     lib.oracle_fwd.argtypes = [P, P, P, P, P, P, I64, I32, D, D, P, P]
     lib.oracle_fwd_rows.argtypes = [P, P, P, P, P, P, I64, I32, D, D, P, I64, P, P]
-    for f in (lib.oracle_segments, lib.oracle_rmsnorm_f64, lib.oracle_qknorm, lib.oracle_fwd, lib.oracle_fwd_rows):
+    lib.oracle_bwd.argtypes = [P, P, P, P, P, P, P, I64, I32, D, D, ctypes.c_int, P, P, P, P, P]
+    lib.oracle_fwd_opt.argtypes = [P, P, P, P, P, P, I64, I32, D, D, ctypes.c_int, P]
+    for f in (lib.oracle_segments, lib.oracle_rmsnorm_f64, lib.oracle_qknorm, lib.oracle_fwd, lib.oracle_fwd_rows,
+              lib.oracle_bwd, lib.oracle_fwd_opt):
         f.restype = ctypes.c_int
     _lib = lib
     return lib
@@ -183,3 +189,41 @@ def fwd_rows(q, k, v, seg_ids, rows, wq=None, wk=None, eps: float = 1e-6, scale:
     _check(_load().oracle_fwd_rows(_ptr(q), _ptr(k), _ptr(v), _ptr(s), _ptr(wq), _ptr(wk), T, H, float(eps), scale,
                                    _ptr(r), r.shape[0], _ptr(out), _ptr(lse)))
     return out, lse
+
+
+def bwd(q, k, v, seg_ids, dout, wq=None, wk=None, eps: float = 1e-6, scale: float | None = None,
+        round_operands: bool = True):
+    """FP64 gradients of the node for upstream gradient dout [T,H,128] (bf16 bits).
+
+    Returns (dq, dk, dv) FP64 [T,H,128] and (dwq, dwk) FP64 [128] (None without weights).  With
+    round_operands=False the normed operands are not rounded to bf16 (exact gradient of a smooth
+    function, for finite-difference checks)."""
+    q, k, v, dout = _bits(q), _bits(k), _bits(v), _bits(dout)
+    T, H, D = q.shape
+    assert D == HEAD_DIM and k.shape == q.shape and v.shape == q.shape and dout.shape == q.shape
+    wq, wk = _bits(wq, (HEAD_DIM,)), _bits(wk, (HEAD_DIM,))
+    s = np.ascontiguousarray(seg_ids, dtype=np.int32)
+    assert s.shape == (T,)
+    scale = float(HEAD_DIM ** -0.5 if scale is None else scale)
+    dq = np.empty((T, H, D), np.float64)
+    dk = np.empty((T, H, D), np.float64)
+    dv = np.empty((T, H, D), np.float64)
+    dwq = np.zeros(HEAD_DIM, np.float64) if wq is not None else None
+    dwk = np.zeros(HEAD_DIM, np.float64) if wq is not None else None
+    _check(_load().oracle_bwd(_ptr(q), _ptr(k), _ptr(v), _ptr(s), _ptr(wq), _ptr(wk), _ptr(dout), T, H, float(eps),
+                              scale, int(bool(round_operands)), _ptr(dq), _ptr(dk), _ptr(dv), _ptr(dwq), _ptr(dwk)))
+    return dq, dk, dv, dwq, dwk
+
+
+def fwd_opt(q, k, v, seg_ids, wq=None, wk=None, eps: float = 1e-6, scale: float | None = None,
+            round_operands: bool = True) -> np.ndarray:
+    """FP64 forward output with the operand rounding optional (see ``bwd``)."""
+    q, k, v = _bits(q), _bits(k), _bits(v)
+    T, H, D = q.shape
+    wq, wk = _bits(wq, (HEAD_DIM,)), _bits(wk, (HEAD_DIM,))
+    s = np.ascontiguousarray(seg_ids, dtype=np.int32)
+    scale = float(HEAD_DIM ** -0.5 if scale is None else scale)
+    out = np.empty((T, H, D), np.float64)
+    _check(_load().oracle_fwd_opt(_ptr(q), _ptr(k), _ptr(v), _ptr(s), _ptr(wq), _ptr(wk), T, H, float(eps), scale,
+                                  int(bool(round_operands)), _ptr(out)))
+    return out

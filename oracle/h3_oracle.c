@@ -270,3 +270,227 @@ int oracle_fwd_rows(const uint16_t* q, const uint16_t* k, const uint16_t* v, con
   if (n_rows == 0) return ORACLE_OK;
   return fwd_impl(q, k, v, seg, wq, wk, T, H, eps, scale, rows, n_rows, out, lse);
 }
+
+/* ---------------------------------------------------------------- backward */
+
+/* Gradients of the node's composite -- q_norm / k_norm, their bf16 rounding, attention(causal=False)
+ * over packed segments -- for an upstream gradient dO ("33B forward/backward" page: the node runs in
+ * the training step's backward as well; "ws1_one_h3_block" page, Bindings: the norm and attention
+ * nodes).  Everything in FP64.
+ *
+ * The bf16 rounding of the normed operands is treated as the identity (straight-through): P and the
+ * products use the rounded q̂ and k̂, exactly the operands of the forward, and the gradient with
+ * respect to q̂ flows unchanged to the unrounded norm output.  round_operands == 0 drops that
+ * rounding (q̂, k̂ exact FP64 norm outputs), which makes the result the exact gradient of a smooth
+ * function; the tests use that form against finite differences.
+ *
+ * For one segment and head, with s_ij = scale * q̂_i . k̂_j and P_ij = softmax_j(s_ij):
+ *   dV_j = sum_i P_ij dO_i
+ *   dP_ij = dO_i . v_j,  D_i = sum_j P_ij dP_ij,  dS_ij = P_ij (dP_ij - D_i)
+ *   dq̂_i = scale sum_j dS_ij k̂_j,   dk̂_j = scale sum_i dS_ij q̂_i
+ * then, per (token, head) row x with r = (mean(x^2) + eps)^(-1/2) and g = w * dŷ (dŷ = dq̂ or dk̂):
+ *   dx = r g - (r^3 / 128) x (g . x),    dw += dŷ * x * r   (summed over every token and head).
+ * Without weights (wq = wk = NULL) dq = dq̂ and dk = dk̂, and dwq / dwk are not produced. */
+
+/* q̂ / k̂ operands like normed_operand, optionally without the bf16 rounding. */
+static double* bwd_operand(const uint16_t* x, const uint16_t* w, int64_t T, int32_t H, double eps, int round) {
+  int64_t n = T * (int64_t)H * HD;
+  double* out = (double*)malloc((size_t)(n > 0 ? n : 1) * sizeof(double));
+  if (!out) return NULL;
+  int64_t rows = T * (int64_t)H;
+#pragma omp parallel for schedule(static)
+  for (int64_t r = 0; r < rows; r++) {
+    const int64_t t = r / H, h = r % H;
+    double* o = out + (h * T + t) * HD;
+    if (w) {
+      double yr[HD];
+      norm_row_f64(x + r * HD, w, eps, yr);
+      for (int d = 0; d < HD; d++) o[d] = round ? oracle_bf16_to_f64(oracle_f64_to_bf16(yr[d])) : yr[d];
+    } else {
+      for (int d = 0; d < HD; d++) o[d] = oracle_bf16_to_f64(x[r * HD + d]);
+    }
+  }
+  return out;
+}
+
+static double dot128(const double* a, const double* b) {
+  double part[4] = {0.0, 0.0, 0.0, 0.0};
+  for (int d = 0; d < HD; d += 4)
+    for (int r = 0; r < 4; r++) part[r] += a[d + r] * b[d + r];
+  return (part[0] + part[1]) + (part[2] + part[3]);
+}
+
+/* One segment of one head: accumulates dq̂ [L][128], dk̂ [L][128], dV [L][128] (zeroed by the caller)
+ * for the segment's rows; qh/kh/vd/go are head-major [H][T][128], the segment starts at token s0. */
+static void bwd_segment(const double* qh, const double* kh, const double* vd, const double* go, int64_t T, int h,
+                        int64_t s0, int64_t L, double scale, double* dqh, double* dkh, double* dvh, double* P,
+                        double* dP) {
+  for (int64_t i = 0; i < L; i++) {
+    const double* qi = qh + (h * T + s0 + i) * HD;
+    const double* gi = go + (h * T + s0 + i) * HD;
+    double m = -INFINITY;
+    for (int64_t j = 0; j < L; j++) {
+      P[j] = scale * dot128(qi, kh + (h * T + s0 + j) * HD);
+      if (P[j] > m) m = P[j];
+    }
+    double l = 0.0;
+    for (int64_t j = 0; j < L; j++) {
+      P[j] = exp(P[j] - m);
+      l += P[j];
+    }
+    double Di = 0.0;
+    for (int64_t j = 0; j < L; j++) {
+      P[j] /= l;
+      dP[j] = dot128(gi, vd + (h * T + s0 + j) * HD);
+      Di += P[j] * dP[j];
+    }
+    double* dqi = dqh + i * HD;
+    for (int64_t j = 0; j < L; j++) {
+      const double dS = P[j] * (dP[j] - Di);
+      const double* kj = kh + (h * T + s0 + j) * HD;
+      double* dkj = dkh + j * HD;
+      double* dvj = dvh + j * HD;
+      for (int d = 0; d < HD; d++) {
+        dvj[d] += P[j] * gi[d];
+        dqi[d] += scale * dS * kj[d];
+        dkj[d] += scale * dS * qi[d];
+      }
+    }
+  }
+}
+
+/* Norm backward of one row; adds this row's dw contribution to dw_row (caller-owned [128]). */
+static void norm_bwd_row(const uint16_t* x_bits, const uint16_t* w_bits, double eps, const double* dy, double* dx,
+                         double* dw_row) {
+  double x[HD], g[HD];
+  double ss = 0.0;
+  for (int d = 0; d < HD; d++) {
+    x[d] = oracle_bf16_to_f64(x_bits[d]);
+    ss += x[d] * x[d];
+  }
+  const double r = 1.0 / sqrt(ss / HD + eps);
+  double gx = 0.0;
+  for (int d = 0; d < HD; d++) {
+    g[d] = oracle_bf16_to_f64(w_bits[d]) * dy[d];
+    gx += g[d] * x[d];
+  }
+  for (int d = 0; d < HD; d++) {
+    dx[d] = r * g[d] - (r * r * r / HD) * x[d] * gx;
+    dw_row[d] = dy[d] * x[d] * r;
+  }
+}
+
+/* Backward of the whole node.  dout, q, k, v: bf16 bits [T,H,128]; outputs dq, dk, dv FP64 [T,H,128];
+ * dwq, dwk FP64 [128] (required when weights are given, ignored otherwise). */
+int oracle_bwd(const uint16_t* q, const uint16_t* k, const uint16_t* v, const int32_t* seg, const uint16_t* wq,
+               const uint16_t* wk, const uint16_t* dout, int64_t T, int32_t H, double eps, double scale,
+               int round_operands, double* dq, double* dk, double* dv, double* dwq, double* dwk) {
+  if (T < 0 || H < 1) return ORACLE_ERR_ARGS;
+  if ((wq == NULL) != (wk == NULL)) return ORACLE_ERR_ARGS;
+  if (wq && (!dwq || !dwk)) return ORACLE_ERR_ARGS;
+  if (wq)
+    for (int d = 0; d < HD; d++) dwq[d] = dwk[d] = 0.0;
+  if (T == 0) return ORACLE_OK;
+  if (!q || !k || !v || !seg || !dout || !dq || !dk || !dv) return ORACLE_ERR_ARGS;
+  int64_t* starts = (int64_t*)malloc((size_t)T * sizeof(int64_t));
+  int64_t* lens = (int64_t*)malloc((size_t)T * sizeof(int64_t));
+  if (!starts || !lens) { free(starts); free(lens); return ORACLE_ERR_NOMEM; }
+  int64_t nseg = 0;
+  int rc = oracle_segments(seg, T, starts, lens, &nseg);
+  if (rc != ORACLE_OK) { free(starts); free(lens); return rc; }
+  int64_t maxlen = 0;
+  for (int64_t s = 0; s < nseg; s++) if (lens[s] > maxlen) maxlen = lens[s];
+
+  const int64_t n = T * (int64_t)H * HD;
+  double* qh = bwd_operand(q, wq, T, H, eps, round_operands);
+  double* kh = bwd_operand(k, wk, T, H, eps, round_operands);
+  double* vd = bwd_operand(v, NULL, T, H, eps, 1);
+  double* go = bwd_operand(dout, NULL, T, H, eps, 1);
+  double* dqh = (double*)calloc((size_t)n, sizeof(double)); /* head-major [H][T][128] */
+  double* dkh = (double*)calloc((size_t)n, sizeof(double));
+  double* dvh = (double*)calloc((size_t)n, sizeof(double));
+  if (!qh || !kh || !vd || !go || !dqh || !dkh || !dvh) {
+    rc = ORACLE_ERR_NOMEM;
+  } else {
+    const int64_t units = nseg * (int64_t)H;
+#pragma omp parallel
+    {
+      double* P = (double*)malloc((size_t)(maxlen > 0 ? maxlen : 1) * sizeof(double));
+      double* dP = (double*)malloc((size_t)(maxlen > 0 ? maxlen : 1) * sizeof(double));
+#pragma omp for schedule(dynamic, 1)
+      for (int64_t u = 0; u < units; u++) { /* (segment, head) units write disjoint rows */
+        const int h = (int)(u % H);
+        const int64_t s = u / H;
+        const int64_t off = (h * T + starts[s]) * HD;
+        bwd_segment(qh, kh, vd, go, T, h, starts[s], lens[s], scale, dqh + off, dkh + off, dvh + off, P, dP);
+      }
+      free(P);
+      free(dP);
+    }
+    /* back to token-major, with the norm backward; dw summed over rows in (token, head) order */
+    double* dwq_rows = wq ? (double*)malloc((size_t)T * H * HD * sizeof(double)) : NULL;
+    double* dwk_rows = wq ? (double*)malloc((size_t)T * H * HD * sizeof(double)) : NULL;
+    if (wq && (!dwq_rows || !dwk_rows)) {
+      rc = ORACLE_ERR_NOMEM;
+    } else {
+      const int64_t rows = T * (int64_t)H;
+#pragma omp parallel for schedule(static)
+      for (int64_t r = 0; r < rows; r++) {
+        const int64_t t = r / H, h = r % H;
+        const int64_t src = (h * T + t) * HD;
+        for (int d = 0; d < HD; d++) dv[r * HD + d] = dvh[src + d];
+        if (wq) {
+          norm_bwd_row(q + r * HD, wq, eps, dqh + src, dq + r * HD, dwq_rows + r * HD);
+          norm_bwd_row(k + r * HD, wk, eps, dkh + src, dk + r * HD, dwk_rows + r * HD);
+        } else {
+          for (int d = 0; d < HD; d++) {
+            dq[r * HD + d] = dqh[src + d];
+            dk[r * HD + d] = dkh[src + d];
+          }
+        }
+      }
+      if (wq)
+        for (int64_t r = 0; r < rows; r++)
+          for (int d = 0; d < HD; d++) {
+            dwq[d] += dwq_rows[r * HD + d];
+            dwk[d] += dwk_rows[r * HD + d];
+          }
+    }
+    free(dwq_rows);
+    free(dwk_rows);
+  }
+  free(qh); free(kh); free(vd); free(go); free(dqh); free(dkh); free(dvh);
+  free(starts); free(lens);
+  return rc;
+}
+
+/* Forward with the operand rounding optional (round_operands == 0: exact FP64 norm outputs), for the
+ * finite-difference checks of the backward. */
+int oracle_fwd_opt(const uint16_t* q, const uint16_t* k, const uint16_t* v, const int32_t* seg, const uint16_t* wq,
+                   const uint16_t* wk, int64_t T, int32_t H, double eps, double scale, int round_operands,
+                   double* out) {
+  if (round_operands) return fwd_impl(q, k, v, seg, wq, wk, T, H, eps, scale, NULL, 0, out, NULL);
+  if (T < 0 || H < 1 || (wq == NULL) != (wk == NULL)) return ORACLE_ERR_ARGS;
+  if (T == 0) return ORACLE_OK;
+  int64_t* starts = (int64_t*)malloc((size_t)T * sizeof(int64_t));
+  int64_t* lens = (int64_t*)malloc((size_t)T * sizeof(int64_t));
+  if (!starts || !lens) { free(starts); free(lens); return ORACLE_ERR_NOMEM; }
+  int64_t nseg = 0;
+  int rc = oracle_segments(seg, T, starts, lens, &nseg);
+  double* qh = bwd_operand(q, wq, T, H, eps, 0);
+  double* kh = bwd_operand(k, wk, T, H, eps, 0);
+  double* vd = bwd_operand(v, NULL, T, H, eps, 1);
+  int64_t maxlen = 0;
+  for (int64_t s = 0; s < nseg; s++) if (lens[s] > maxlen) maxlen = lens[s];
+  double* scores = (double*)malloc((size_t)(maxlen > 0 ? maxlen : 1) * sizeof(double));
+  if (rc == ORACLE_OK && (!qh || !kh || !vd || !scores)) rc = ORACLE_ERR_NOMEM;
+  if (rc == ORACLE_OK)
+    for (int64_t s = 0; s < nseg; s++)
+      for (int h = 0; h < H; h++)
+        for (int64_t i = starts[s]; i < starts[s] + lens[s]; i++) {
+          double lse_val;
+          attend_one(qh, kh, vd, T, h, i, starts[s], lens[s], scale, scores, out + (i * H + h) * HD, &lse_val);
+        }
+  free(scores); free(qh); free(kh); free(vd); free(starts); free(lens);
+  return rc;
+}

@@ -105,10 +105,10 @@ def make_inputs(w: Workload, with_grad: bool = False) -> dict:
     return out
 
 
-def random_inputs(seg_lens, heads, seed=0, qk_scale=1.0, normed=True, w_scale=1.0) -> dict:
+def random_inputs(seg_lens, heads, seed=0, qk_scale=1.0, normed=True, w_scale=1.0, with_grad=False) -> dict:
     """Same recipe as make_inputs for an ad-hoc list of segment lengths."""
     wl = Workload("adhoc", (tuple(seg_lens),), heads, qk_scale=qk_scale, w_scale=w_scale, normed=normed, seed=seed)
-    return make_inputs(wl)
+    return make_inputs(wl, with_grad=with_grad)
 
 
 def row_slices(w: Workload):
