@@ -29,7 +29,8 @@ H3ATTN_ERR_RANGE = 9
 
 # every symbol the header declares
 EXPORTS = ("h3attn_version", "h3attn_strerror", "h3attn_workspace_bytes", "h3attn_qknorm", "h3attn_fwd",
-           "h3attn_plan", "h3attn_prep_kv", "h3attn_attend", "h3attn_status_read")
+           "h3attn_plan", "h3attn_prep_kv", "h3attn_attend", "h3attn_status_read", "h3attn_bwd_workspace_bytes",
+           "h3attn_bwd")
 
 
 class H3AttnError(RuntimeError):
@@ -61,8 +62,11 @@ def load():
     lib.h3attn_prep_kv.argtypes = [P, P, P, I64, I32, I32, F, P, SZ, P]
     lib.h3attn_attend.argtypes = [P, P, I64, I32, I32, F, F, P, P, P, SZ, P]
     lib.h3attn_status_read.argtypes = [P, ctypes.POINTER(ctypes.c_int32), P]
+    lib.h3attn_bwd_workspace_bytes.argtypes = [I64, I32]
+    lib.h3attn_bwd_workspace_bytes.restype = SZ
+    lib.h3attn_bwd.argtypes = [P, P, P, P, P, P, P, P, I64, I32, I32, F, F, P, P, P, P, P, P, SZ, P]
     for name in ("h3attn_qknorm", "h3attn_fwd", "h3attn_plan", "h3attn_prep_kv", "h3attn_attend",
-                 "h3attn_status_read"):
+                 "h3attn_status_read", "h3attn_bwd"):
         getattr(lib, name).restype = ctypes.c_int
     _lib = lib
     return lib
@@ -170,3 +174,39 @@ def h3attn_status_read(workspace_buf, stream=None) -> int:
     rc = load().h3attn_status_read(_ptr(workspace_buf), ctypes.byref(st), _stream(stream, workspace_buf.device))
     _check(rc, "h3attn_status_read")
     return st.value
+
+
+def h3attn_bwd_workspace_bytes(tokens: int, heads: int) -> int:
+    return load().h3attn_bwd_workspace_bytes(int(tokens), int(heads))
+
+
+def bwd_workspace(tokens: int, heads: int, device) -> torch.Tensor:
+    """A device buffer of h3attn_bwd_workspace_bytes(tokens, heads) bytes."""
+    n = h3attn_bwd_workspace_bytes(tokens, heads)
+    return torch.empty(max(n, 256), dtype=torch.uint8, device=device)
+
+
+def h3attn_bwd(dout, q, k, v, lse, seg_ids, wq=None, wk=None, eps: float = 1e-6, scale: float | None = None,
+               dq=None, dk=None, dv=None, dwq=None, dwk=None, workspace_buf=None, stream=None):
+    """Backward of the node: returns (dq, dk, dv, dwq, dwk) (dwq/dwk None without norm weights).
+    lse is the forward's fp32 [T, H] log-sum-exp (h3attn_fwd(..., want_lse=True))."""
+    for t, n in ((dout, "dout"), (q, "q"), (k, "k"), (v, "v"), (wq, "wq"), (wk, "wk")):
+        _bf16(t, n)
+    if seg_ids.dtype != torch.int32 or not seg_ids.is_contiguous():
+        raise TypeError("seg_ids must be a contiguous int32 tensor")
+    if lse.dtype != torch.float32 or not lse.is_contiguous():
+        raise TypeError("lse must be a contiguous float32 tensor")
+    T, H, D = _shape(q)
+    scale = D ** -0.5 if scale is None else scale
+    dq = torch.empty_like(q) if dq is None else _bf16(dq, "dq")
+    dk = torch.empty_like(q) if dk is None else _bf16(dk, "dk")
+    dv = torch.empty_like(q) if dv is None else _bf16(dv, "dv")
+    if wq is not None:
+        dwq = torch.empty(D, dtype=torch.float32, device=q.device) if dwq is None else dwq
+        dwk = torch.empty(D, dtype=torch.float32, device=q.device) if dwk is None else dwk
+    ws = bwd_workspace(T, H, q.device) if workspace_buf is None else workspace_buf
+    rc = load().h3attn_bwd(_ptr(dout), _ptr(q), _ptr(k), _ptr(v), _ptr(lse), _ptr(seg_ids), _ptr(wq), _ptr(wk), T, H,
+                           D, float(eps), float(scale), _ptr(dq), _ptr(dk), _ptr(dv), _ptr(dwq), _ptr(dwk), _ptr(ws),
+                           ws.numel(), _stream(stream, q.device))
+    _check(rc, "h3attn_bwd")
+    return dq, dk, dv, dwq, dwk

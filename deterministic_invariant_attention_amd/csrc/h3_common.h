@@ -47,6 +47,44 @@ __host__ __device__ inline WsLayout ws_layout(int64_t T, int32_t H) {
   return w;
 }
 
+// ---------------------------------------------------------------- backward workspace
+// [0, 256)   header: status bits, segment and work-item counts
+// segtab     int32 [2*T]
+// items      int32 [2*(T + ceil(T/BT))]: (segment, tile) work items, BT = 128 queries or keys
+// qhat, khat bf16 [H][T][128]: normed q, k (head-major)      qhat16, khat16: the same in fp16
+// vh, doh    bf16 [H][T][128]: v and dO (head-major)          do16: dO in fp16
+// lse2       fp32 [H][T]: the forward's log-sum-exp in log2 units
+// delta      fp32 [H][T]: D_i = sum_j P_ij dP_ij
+// dwq, dwk   fp32 [max_items][H][128]: per-item partial sums of the norm-weight gradients
+constexpr int BT = 128;  // queries (dq kernel) or keys (dk/dv kernel) per backward work item
+
+struct BwdLayout {
+  size_t segtab, items, qhat, qhat16, khat, khat16, vh, doh, do16, lse2, delta, dwq, dwk, total;
+  int64_t max_items;
+};
+
+__host__ __device__ inline BwdLayout bwd_layout(int64_t T, int32_t H) {
+  BwdLayout w;
+  const size_t tens = align256((size_t)T * H * HD * 2);
+  const size_t rowf = align256((size_t)T * H * 4);
+  w.max_items = T + (T + BT - 1) / BT;
+  w.segtab = 256;
+  w.items = w.segtab + align256((size_t)T * 8);
+  w.qhat = w.items + align256((size_t)w.max_items * 8);
+  w.qhat16 = w.qhat + tens;
+  w.khat = w.qhat16 + tens;
+  w.khat16 = w.khat + tens;
+  w.vh = w.khat16 + tens;
+  w.doh = w.vh + tens;
+  w.do16 = w.doh + tens;
+  w.lse2 = w.do16 + tens;
+  w.delta = w.lse2 + rowf;
+  w.dwq = w.delta + rowf;
+  w.dwk = w.dwq + align256((size_t)w.max_items * H * HD * 4);
+  w.total = w.dwk + align256((size_t)w.max_items * H * HD * 4);
+  return w;
+}
+
 // ---------------------------------------------------------------- vector types
 typedef __bf16 bf16x8 __attribute__((__vector_size__(8 * sizeof(__bf16))));
 typedef _Float16 f16x8 __attribute__((__vector_size__(8 * sizeof(_Float16))));

@@ -22,4 +22,19 @@ hipError_t launch_prep_kv(const void* k, const void* v, const void* wk, int64_t 
 hipError_t launch_attend(const void* q, const void* wq, int64_t T, int32_t H, float eps, float scale, void* out,
                          float* lse, void* ws, int grid_cap, hipStream_t stream);
 
+// Backward: segment decode with 128-token tiles into the backward workspace.
+hipError_t launch_plan_bwd(const int32_t* seg, int64_t T, void* ws, int32_t H, hipStream_t stream);
+
+// Backward operand staging (normed q/k in bf16 and fp16, v, dO in bf16 and fp16, LSE in log2 units).
+hipError_t launch_bwd_prep(const void* q, const void* k, const void* v, const void* dout, const float* lse,
+                           const void* wq, const void* wk, int64_t T, int32_t H, float eps, void* ws,
+                           hipStream_t stream);
+
+// Backward attention on the staged operands: dq with D, then dk/dv (each with its norm backward and
+// per-item weight-gradient partials), then the fixed-order reduction of the partials into dwq/dwk
+// when the weights are given.  q and k are the raw inputs (the norm backward reads them).
+hipError_t launch_bwd(const void* q, const void* k, const void* wq, const void* wk, int64_t T, int32_t H, float eps,
+                      float scale, void* dq, void* dk, void* dv, float* dwq, float* dwk, void* ws, int grid_cap,
+                      hipStream_t stream);
+
 }  // namespace h3

@@ -93,7 +93,7 @@ const char* h3attn_strerror(int status) {
     case H3ATTN_ERR_DEVICE: return "no current device or it is not gfx950 (MI355X)";
     case H3ATTN_ERR_LAUNCH: return "the HIP runtime rejected a launch or copy";
     case H3ATTN_ERR_SEGMENTS: return "segment ids decrease (device status)";
-    case H3ATTN_ERR_RANGE: return "a finite |v| > 65504 cannot enter the fp16 P.V product (device status)";
+    case H3ATTN_ERR_RANGE: return "a finite value beyond 65504 cannot enter an fp16 product (device status)";
     default: return "unknown status";
   }
 }
@@ -221,6 +221,52 @@ int h3attn_fwd(const void* q, const void* k, const void* v, const int32_t* seg_i
   if ((rc = launch_status(launch_plan(seg_ids, tokens, workspace, heads, st)))) return rc;
   if ((rc = launch_status(launch_prep_kv(k, v, wk, tokens, heads, eps, workspace, st)))) return rc;
   return launch_status(launch_attend(q, wq, tokens, heads, eps, scale, out, lse, workspace, di.cus, st));
+}
+
+size_t h3attn_bwd_workspace_bytes(int64_t tokens, int32_t heads) {
+  if (check_shape(tokens, heads, HD) != H3ATTN_OK) return 0;
+  if (tokens + (tokens + BT - 1) / BT > (int64_t)INT32_MAX / heads) return 0;
+  return bwd_layout(tokens, heads).total;
+}
+
+int h3attn_bwd(const void* dout, const void* q, const void* k, const void* v, const float* lse,
+               const int32_t* seg_ids, const void* wq, const void* wk, int64_t tokens, int32_t heads,
+               int32_t head_dim, float eps, float scale, void* dq, void* dk, void* dv, float* dwq, float* dwk,
+               void* workspace, size_t workspace_bytes, void* stream) {
+  int rc = check_shape(tokens, heads, head_dim);
+  if (rc) return rc;
+  if (tokens + (tokens + BT - 1) / BT > (int64_t)INT32_MAX / heads) return H3ATTN_ERR_SHAPE;
+  if ((wq == nullptr) != (wk == nullptr)) return H3ATTN_ERR_NULL;
+  if (wq && (!(eps > 0.0f) || !std::isfinite(eps))) return H3ATTN_ERR_SHAPE;
+  if (!(scale > 0.0f) || !std::isfinite(scale)) return H3ATTN_ERR_SHAPE;
+  if (tokens == 0) return H3ATTN_OK;
+  if (!dout || !q || !k || !v || !lse || !seg_ids || !dq || !dk || !dv || !workspace) return H3ATTN_ERR_NULL;
+  if (wq && (!dwq || !dwk)) return H3ATTN_ERR_NULL;
+  if (!aligned(dout, 16) || !aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(lse, 4) ||
+      !aligned(seg_ids, 4) || (wq && (!aligned(wq, 16) || !aligned(wk, 16) || !aligned(dwq, 4) || !aligned(dwk, 4))) ||
+      !aligned(dq, 16) || !aligned(dk, 16) || !aligned(dv, 16) || !aligned(workspace, 256))
+    return H3ATTN_ERR_ALIGN;
+  if (workspace_bytes < bwd_layout(tokens, heads).total) return H3ATTN_ERR_WORKSPACE;
+  const size_t n = tensor_bytes(tokens, heads);
+  const size_t nl = (size_t)tokens * heads * 4;
+  const size_t ns = (size_t)tokens * 4;
+  // every output against every input, the workspace and the other outputs
+  const void* ins[] = {dout, q, k, v, lse, seg_ids, wq, wk, workspace};
+  const size_t in_n[] = {n, n, n, n, nl, ns, (size_t)HD * 2, (size_t)HD * 2, workspace_bytes};
+  void* outs[] = {dq, dk, dv, dwq, dwk};
+  const size_t out_n[] = {n, n, n, wq ? (size_t)HD * 4 : 0, wq ? (size_t)HD * 4 : 0};
+  for (int o = 0; o < 5; o++) {
+    for (int i = 0; i < 9; i++)
+      if (overlap(outs[o], out_n[o], ins[i], in_n[i])) return H3ATTN_ERR_ALIAS;
+    for (int o2 = o + 1; o2 < 5; o2++)
+      if (overlap(outs[o], out_n[o], outs[o2], out_n[o2])) return H3ATTN_ERR_ALIAS;
+  }
+  DeviceInfo di;
+  if ((rc = device_info(&di))) return rc;
+  hipStream_t st = (hipStream_t)stream;
+  if ((rc = launch_status(launch_plan_bwd(seg_ids, tokens, workspace, heads, st)))) return rc;
+  if ((rc = launch_status(launch_bwd_prep(q, k, v, dout, lse, wq, wk, tokens, heads, eps, workspace, st)))) return rc;
+  return launch_status(launch_bwd(q, k, wq, wk, tokens, heads, eps, scale, dq, dk, dv, dwq, dwk, workspace, di.cus, st));
 }
 
 int h3attn_status_read(const void* workspace, int32_t* device_status, void* stream) {

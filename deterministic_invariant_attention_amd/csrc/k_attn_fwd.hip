@@ -41,14 +41,14 @@
 // O/l rescale is skipped on most tiles.  Lanes whose m does not move take alpha = 1 exactly.
 #include "h3_common.h"
 #include "h3_launch.h"
+#include "h3_tiles.h"
 
 namespace h3 {
 
 constexpr float LN2 = 0.69314718055994530942f;
 constexpr float RESCALE_THRESHOLD = 8.0f;  // log2 units
-constexpr int TILE_ELEMS = BK * HD;        // 16-bit elements in one K or V tile (16 KB)
 constexpr int NWAVES = 8;                 // waves per workgroup (two per SIMD)
-static_assert(BK == 64, "two 32-key blocks per tile");
+static_assert(BK == TILE_ROWS, "one LDS tile per KV tile of two 32-key blocks");
 static_assert(BQ == 32 * NWAVES, "one 32-query block per wave");
 
 struct AttnParams {
@@ -68,72 +68,6 @@ struct AttnParams {
   int32_t xcd_slots;  // workgroups per XCD (grid / 8), for the XCD-aware item order
 };
 
-typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
-typedef __attribute__((address_space(3))) void lds_void;
-typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
-typedef float f32x2 __attribute__((ext_vector_type(2)));
-
-// Element offsets of a 16-bit value (row r, column d) inside a swizzled tile.
-__device__ __forceinline__ int k_off(int r, int d) { return r * HD + ((((d >> 3) ^ (r & 15))) << 3) + (d & 7); }
-__device__ __forceinline__ int v_off(int r, int d) { return r * HD + ((((d >> 3) ^ ((r & 3) << 2))) << 3) + (d & 7); }
-
-// Copy one 64-row tile of a head-major [rows][128] 16-bit array into a swizzled LDS tile with
-// buffer_load_dwordx4 ... lds.  The buffer resource covers only the tile's rows inside the segment
-// (`valid` rows), so the rows past the segment end read as zeros: nothing outside the segment can
-// reach the products.  8 waves, 2 x 1 KB each; each lane's 16 bytes land at LDS base + lane * 16,
-// so the lane fetches the global chunk that belongs in that slot.  The slot pattern repeats every
-// 16 rows, so one lane offset serves both blocks.
-__device__ __forceinline__ int tile_lane_offset(bool is_v, int wv, int lane) {
-  const int r = 4 * wv + (lane >> 4);  // tile row of the lane's slot in block wv (rows 4wv..4wv+3)
-  const int slot = lane & 15;
-  const int c = is_v ? (slot ^ ((r & 3) << 2)) : (slot ^ (r & 15));
-  return r * 256 + c * 16;  // bytes
-}
-
-__device__ __forceinline__ void tile_to_lds(const uint16_t* gtile, int valid, uint16_t* lds_tile, int wv,
-                                            int lane_off) {
-  const __amdgpu_buffer_rsrc_t rs =
-      __builtin_amdgcn_make_buffer_rsrc((void*)gtile, (short)0, (valid < BK ? valid : BK) * 256, 0x00020000);
-#pragma unroll
-  for (int i = 0; i < BK / (4 * NWAVES); i++)  // block NWAVES*i + wv = rows 4*NWAVES*i + 4wv .. +3
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void*)(lds_tile + (NWAVES * i + wv) * 4 * HD), 16,
-                                             lane_off + i * NWAVES * 1024, 0, 0, 0);
-}
-
-// Transposed LDS read (ds_read_b64_tr_b16, gfx950): within each 16-lane group, lane s supplies the
-// address of 4 consecutive 16-bit elements C_s; lane s receives {C_{s/4}[s%4], C_{4+s/4}[s%4],
-// C_{8+s/4}[s%4], C_{12+s/4}[s%4]}.  With C_s = V[key0 + s/4][dim0 + 4(s%4) .. +3] lane s gets
-// V[key0 + i][dim0 + s], i = 0..3: four consecutive keys of one dim, the A-operand layout of a P.V
-// MFMA.  (Issued as inline assembly below: tr_read_asm.)
-
-// Every lane receives (x of lane l % 32, x of lane l % 32 + 32) in some fixed order; callers only
-// combine the pair with commutative operations (max, +), which give the same bits either way.
-__device__ __forceinline__ void swap_halves(float x, float& a, float& b) {
-  const auto r = __builtin_amdgcn_permlane32_swap(__builtin_bit_cast(uint32_t, x), __builtin_bit_cast(uint32_t, x),
-                                                  false, false);
-  a = __builtin_bit_cast(float, (uint32_t)r[0]);
-  b = __builtin_bit_cast(float, (uint32_t)r[1]);
-}
-
-template <int N>
-__device__ __forceinline__ float tree_sum(const float* x) {
-  if constexpr (N == 1) {
-    return x[0];
-  } else {
-    return tree_sum<N / 2>(x) + tree_sum<N / 2>(x + N / 2);
-  }
-}
-
-// Keys at or past `rem` (the valid keys of the segment's last tile) get -inf.  S[kb] holds keys
-// 32kb + 8(i/4) + 4hh + (i%4) of the lane's query.
-__device__ __forceinline__ void mask_tail(f32x16* S, int rem, int hh) {
-#pragma unroll
-  for (int kb = 0; kb < 2; kb++)
-#pragma unroll
-    for (int i = 0; i < 16; i++)
-      if (32 * kb + 8 * (i >> 2) + 4 * hh + (i & 3) >= rem) S[kb][i] = -__builtin_inff();
-}
-
 // Maximum over the query's 64 keys of one tile (exact: any evaluation order gives these bits).
 __device__ __forceinline__ float tile_max(const f32x16* S) {
   float a = -__builtin_inff();
@@ -144,17 +78,6 @@ __device__ __forceinline__ float tile_max(const f32x16* S) {
   float x, y;
   swap_halves(a, x, y);
   return __builtin_fmaxf(x, y);
-}
-
-// p -> packed fp16 B operand (8 keys), round to nearest even.
-__device__ __forceinline__ f16x8 pack_p(const float* p) {
-  u32x4 w4;
-#pragma unroll
-  for (int i = 0; i < 4; i++) {
-    const f32x2 two = {p[2 * i], p[2 * i + 1]};
-    w4[i] = __builtin_bit_cast(uint32_t, __builtin_convertvector(two, f16x2));
-  }
-  return __builtin_bit_cast(f16x8, w4);
 }
 
 // Q prologue for one 32-query block: load, RMSNorm (2 lanes per row), round to bf16 B-operands.
@@ -194,99 +117,10 @@ __device__ __forceinline__ void load_q(const AttnParams& p, int s0, int qrow, bo
   }
 }
 
-// Workgroup barrier between phases, without the memory fence of __syncthreads: that fence makes
-// every wave wait for all of its outstanding global-to-LDS copies at every phase, while a copy only
-// has to land two phases after it is issued (the explicit vmcnt wait in the phase loop).  Every LDS
-// read before the barrier has been consumed, so waited for, by then; the empty asm statements keep
-// the compiler from moving memory operations across the barrier.
-__device__ __forceinline__ void phase_barrier() {
-  asm volatile("" ::: "memory");
-  __builtin_amdgcn_s_barrier();
-  asm volatile("" ::: "memory");
-}
-
 template <int N>
 struct Par {
   static constexpr int value = N;
 };
-
-// Scores of one 64-key tile: S[kb] holds keys 32kb + 8(i/4) + 4hh + (i%4) of the lane's query.
-// Each accumulator sums its k-slices m = 0..7 in order.
-template <int NPRE>
-__device__ __forceinline__ void gemm_scores(const uint16_t* Kb, const bf16x8* qf, int l32, int hh, f32x16* S) {
-  bf16x8 ka[16];
-  auto kread = [&](int s) { ka[s] = *(const bf16x8*)(Kb + k_off(32 * (s & 1) + l32, 16 * (s >> 1) + 8 * hh)); };
-#pragma unroll
-  for (int kb = 0; kb < 2; kb++)
-#pragma unroll
-    for (int i = 0; i < 16; i++) S[kb][i] = 0.0f;
-#pragma unroll
-  for (int s = 0; s < NPRE; s++) kread(s);
-#pragma unroll
-  for (int s = 0; s < 16; s++) {  // step s = 2m + kb
-    if (s + NPRE < 16) kread(s + NPRE);
-    S[s & 1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka[s], qf[s >> 1], S[s & 1], 0, 0, 0);
-    __builtin_amdgcn_sched_barrier(0);
-  }
-}
-
-// ds_read_b64_tr_b16 as inline assembly.  The builtin carries no memory operand, so the compiler's
-// wait insertion assumes it may read what an outstanding global-to-LDS copy writes and waits for
-// every copy before it, which serialises the copies with the matrix phase.  The assembly form is
-// invisible to that analysis, so the caller waits for the results itself (LGKM_WAIT_TIED).  base is
-// an LDS byte address, OFF a constant byte offset (the instruction's 16-bit offset field).
-template <int OFF>
-__device__ __forceinline__ u32x2 tr_read_asm(uint32_t base) {
-  static_assert(OFF >= 0 && OFF < 65536, "ds offset field");
-  u32x2 r;
-  asm volatile("ds_read_b64_tr_b16 %0, %1 offset:%2" : "=v"(r) : "v"(base), "i"(OFF));
-  return r;
-}
-
-// Wait until at most N LDS operations are outstanding; x and y are tied to the wait, so nothing
-// that reads them can be scheduled before it.
-#define LGKM_WAIT_TIED(N, x, y) asm volatile("s_waitcnt lgkmcnt(" #N ")" : "+v"(x), "+v"(y))
-
-// V operand of P.V step T = 4ks + db from V buffer VBUF: rows 16ks + {0..7} and 16ks + 8 + {0..7}
-// of the tile.  vb[db] is the lane's LDS byte address of (row tr_row, column 32db + tr_col) in
-// buffer 0; the swizzle of a row depends on row & 3 only, so the other rows are constant offsets.
-template <int VBUF, int T>
-__device__ __forceinline__ void pv_read(const uint32_t* vb, u32x2 (&va)[16][2]) {
-  constexpr int ks = T >> 2, db = T & 3;
-  constexpr int off = (2 + VBUF) * TILE_ELEMS * 2 + 16 * ks * HD * 2;
-  va[T][0] = tr_read_asm<off>(vb[db]);
-  va[T][1] = tr_read_asm<off + 8 * HD * 2>(vb[db]);
-}
-
-// O^T += V^T P^T for one 64-key tile, step T = 4ks + db, so every O[db] sums its key slices in
-// order.  V operands are read 4 steps ahead; before step T's MFMA the reads of the steps after it
-// (two each, at most 4 steps) may still be in flight, and no other LDS operation is (the score
-// MFMAs before this have consumed their K reads).
-template <int VBUF, int T>
-__device__ __forceinline__ void pv_step(const uint32_t* vb, const f16x8* pf, f32x16* O, u32x2 (&va)[16][2]) {
-  if constexpr (T + 4 < 16) pv_read<VBUF, T + 4>(vb, va);
-  constexpr int ahead = (T + 4 < 16 ? T + 4 : 15) - T;  // later steps already issued
-  if constexpr (ahead == 4) LGKM_WAIT_TIED(8, va[T][0], va[T][1]);
-  else if constexpr (ahead == 3) LGKM_WAIT_TIED(6, va[T][0], va[T][1]);
-  else if constexpr (ahead == 2) LGKM_WAIT_TIED(4, va[T][0], va[T][1]);
-  else if constexpr (ahead == 1) LGKM_WAIT_TIED(2, va[T][0], va[T][1]);
-  else LGKM_WAIT_TIED(0, va[T][0], va[T][1]);
-  const f16x4 lo = __builtin_bit_cast(f16x4, va[T][0]), hi = __builtin_bit_cast(f16x4, va[T][1]);
-  const f16x8 a = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
-  O[T & 3] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a, pf[T >> 2], O[T & 3], 0, 0, 0);
-  __builtin_amdgcn_sched_barrier(0);
-  if constexpr (T + 1 < 16) pv_step<VBUF, T + 1>(vb, pf, O, va);
-}
-
-template <int VBUF>
-__device__ __forceinline__ void gemm_pv(const uint32_t* vb, const f16x8* pf, f32x16* O) {
-  u32x2 va[16][2];
-  pv_read<VBUF, 0>(vb, va);
-  pv_read<VBUF, 1>(vb, va);
-  pv_read<VBUF, 2>(vb, va);
-  pv_read<VBUF, 3>(vb, va);
-  pv_step<VBUF, 0>(vb, pf, O, va);
-}
 
 __global__ __launch_bounds__(64 * NWAVES, 1) void k_attn_fwd(AttnParams p) {
   // K tiles in buffers 0, 1 and V tiles in buffers 2, 3 (16 KB each)
@@ -354,7 +188,7 @@ __global__ __launch_bounds__(64 * NWAVES, 1) void k_attn_fwd(AttnParams p) {
 
     // Every wave has finished reading LDS for the previous item before it is overwritten.
     __syncthreads();
-    tile_to_lds(kbase, L, lds, wv, k_lane_off);  // K(0)
+    tile_to_lds<NWAVES>(kbase, L, lds, wv, k_lane_off);  // K(0)
 
     const int qrow = qt * BQ + wv * 32 + l32;
     const bool qvalid = qrow < L;
@@ -379,10 +213,10 @@ __global__ __launch_bounds__(64 * NWAVES, 1) void k_attn_fwd(AttnParams p) {
       constexpr int MP = decltype(mp)::value;
       const int m = t >> 1;
       if (m + 1 < ntiles)
-        tile_to_lds(kbase + (int64_t)(m + 1) * BK * HD, L - (m + 1) * BK, lds + (1 - MP) * TILE_ELEMS, wv,
+        tile_to_lds<NWAVES>(kbase + (int64_t)(m + 1) * BK * HD, L - (m + 1) * BK, lds + (1 - MP) * TILE_ELEMS, wv,
                     k_lane_off);
       if (m < ntiles)
-        tile_to_lds(vbase + (int64_t)m * BK * HD, L - m * BK, lds + (2 + MP) * TILE_ELEMS, wv, v_lane_off);
+        tile_to_lds<NWAVES>(vbase + (int64_t)m * BK * HD, L - m * BK, lds + (2 + MP) * TILE_ELEMS, wv, v_lane_off);
     };
 
     // Phase tau of this wave runs in slot t = tau + grp.  Even tau: G(k), k = tau/2 - 1 (scores of
@@ -405,7 +239,7 @@ __global__ __launch_bounds__(64 * NWAVES, 1) void k_attn_fwd(AttnParams p) {
         constexpr int KBUF = TM == 0 ? 0 : 1;  // K(k+1): k = 2n-1 -> K(2n); k = 2n -> K(2n+1)
         constexpr int VBUF = TM == 0 ? 1 : 0;  // V(k)
         if (k + 1 < ntiles) gemm_scores<4>(lds + KBUF * TILE_ELEMS, qf, l32, hh, S);
-        if (k >= 0) gemm_pv<VBUF>(vb, pf, O);
+        if (k >= 0) tr_gemm<2 + VBUF>(vb, pf, O);
       } else {
         const int k = (tau - 1) / 2 - 1;
         if (k + 1 < ntiles) {

@@ -1,6 +1,7 @@
 // The q_norm / k_norm node (RMSNorm over each 128-wide head, one 128-element weight shared by all
-// heads: "ws1_one_h3_block" page, Bindings table and Results) as a standalone kernel, and the K/V
-// staging kernel of the attention: K normed with the same arithmetic, V converted to fp16.
+// heads: "ws1_one_h3_block" page, Bindings table and Results) as a standalone kernel, the K/V
+// staging kernel of the attention (K normed with the same arithmetic, V converted to fp16) and the
+// operand staging kernel of the backward.
 //
 // Mapping: 16 lanes per (token, head) row, lane c holds channels 8c..8c+7 (one 16-byte chunk), so
 // each wave moves 4 rows with fully coalesced 16-byte accesses.  The sum of squares follows the
@@ -76,7 +77,114 @@ __global__ __launch_bounds__(256) void k_prep_kv(const uint16_t* __restrict__ k,
   if (any_over && (threadIdx.x & 63) == __builtin_ctzll(any_over)) atomicOr(&hdr->status, STATUS_RANGE_BIT);
 }
 
+// Operand staging of the backward: per (token, head) row, the normed q and k (the forward's exact
+// bits) in bf16 and fp16, v and dO in bf16, dO in fp16, all head-major; the forward's LSE in log2
+// units.  A finite value beyond the fp16 range in a converted operand sets STATUS_RANGE_BIT.
+struct BwdPrepParams {
+  const uint16_t* q;
+  const uint16_t* k;
+  const uint16_t* v;
+  const uint16_t* dout;
+  const float* lse;
+  const uint16_t* wq;
+  const uint16_t* wk;
+  uint16_t* qhat;
+  uint16_t* qhat16;
+  uint16_t* khat;
+  uint16_t* khat16;
+  uint16_t* vh;
+  uint16_t* doh;
+  uint16_t* do16;
+  float* lse2;
+  WsHeader* hdr;
+  int64_t T;
+  int32_t H;
+  float eps;
+};
+
+// bf16 chunk -> fp16 chunk (exact for magnitudes in fp16's normal range); over |= a finite value
+// beyond 65504.
+__device__ __forceinline__ u32x4 bf16_chunk_to_f16(const u32x4& x, bool& over) {
+  u32x4 o;
+#pragma unroll
+  for (int i = 0; i < 4; i++) {
+    const float a = bf16_lo(x[i]), b = bf16_hi(x[i]);
+    over |= (__builtin_fabsf(a) > 65504.0f && __builtin_fabsf(a) != __builtin_inff());
+    over |= (__builtin_fabsf(b) > 65504.0f && __builtin_fabsf(b) != __builtin_inff());
+    o[i] = pack_f16(a, b);
+  }
+  return o;
+}
+
+__global__ __launch_bounds__(256) void k_bwd_prep(BwdPrepParams p) {
+  const int64_t g = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  const int64_t row = g >> 4;
+  const int c = threadIdx.x & 15;
+  const int64_t rows = p.T * p.H;
+  const bool valid = row < rows;
+  const int64_t t = valid ? row / p.H : 0;
+  const int64_t h = valid ? row - t * p.H : 0;
+  const int64_t dst = (h * p.T + t) * HD + c * 8;
+
+  u32x4 qv = {0, 0, 0, 0}, kv = {0, 0, 0, 0}, vv = {0, 0, 0, 0}, gv = {0, 0, 0, 0};
+  if (valid) {
+    qv = ld16(p.q + row * HD + c * 8);
+    kv = ld16(p.k + row * HD + c * 8);
+    vv = ld16(p.v + row * HD + c * 8);
+    gv = ld16(p.dout + row * HD + c * 8);
+  }
+  const u32x4 qo = p.wq ? norm_16lane(qv, p.wq, c, p.eps) : qv;
+  const u32x4 ko = p.wk ? norm_16lane(kv, p.wk, c, p.eps) : kv;
+  bool over = false;
+  const u32x4 q16 = bf16_chunk_to_f16(qo, over);
+  const u32x4 k16 = bf16_chunk_to_f16(ko, over);
+  const u32x4 g16 = bf16_chunk_to_f16(gv, over);
+  if (valid) {
+    st16(p.qhat + dst, qo);
+    st16(p.qhat16 + dst, q16);
+    st16(p.khat + dst, ko);
+    st16(p.khat16 + dst, k16);
+    st16(p.vh + dst, vv);
+    st16(p.doh + dst, gv);
+    st16(p.do16 + dst, g16);
+    if (c == 0) p.lse2[h * p.T + t] = p.lse[t * p.H + h] * 1.44269504088896340736f;
+  }
+  const uint64_t any_over = __ballot(valid && over);
+  if (any_over && (threadIdx.x & 63) == __builtin_ctzll(any_over)) atomicOr(&p.hdr->status, STATUS_RANGE_BIT);
+}
+
 static inline unsigned grid_for_rows(int64_t rows) { return (unsigned)((rows * 16 + 255) / 256); }
+
+hipError_t launch_bwd_prep(const void* q, const void* k, const void* v, const void* dout, const float* lse,
+                           const void* wq, const void* wk, int64_t T, int32_t H, float eps, void* ws,
+                           hipStream_t stream) {
+  const int64_t rows = T * H;
+  if (rows == 0) return hipSuccess;
+  const BwdLayout L = bwd_layout(T, H);
+  char* base = (char*)ws;
+  BwdPrepParams p;
+  p.q = (const uint16_t*)q;
+  p.k = (const uint16_t*)k;
+  p.v = (const uint16_t*)v;
+  p.dout = (const uint16_t*)dout;
+  p.lse = lse;
+  p.wq = (const uint16_t*)wq;
+  p.wk = (const uint16_t*)wk;
+  p.qhat = (uint16_t*)(base + L.qhat);
+  p.qhat16 = (uint16_t*)(base + L.qhat16);
+  p.khat = (uint16_t*)(base + L.khat);
+  p.khat16 = (uint16_t*)(base + L.khat16);
+  p.vh = (uint16_t*)(base + L.vh);
+  p.doh = (uint16_t*)(base + L.doh);
+  p.do16 = (uint16_t*)(base + L.do16);
+  p.lse2 = (float*)(base + L.lse2);
+  p.hdr = (WsHeader*)base;
+  p.T = T;
+  p.H = H;
+  p.eps = eps;
+  hipLaunchKernelGGL(k_bwd_prep, dim3(grid_for_rows(rows)), dim3(256), 0, stream, p);
+  return hipGetLastError();
+}
 
 hipError_t launch_qknorm(const void* x, const void* w, void* y, int64_t T, int32_t H, float eps, hipStream_t stream) {
   const int64_t rows = T * H;

@@ -35,7 +35,7 @@ __device__ __forceinline__ int block_excl_scan(int v, int* lds_wave, int& total)
 }
 
 __global__ __launch_bounds__(1024) void k_plan(const int32_t* __restrict__ seg, int64_t T, WsHeader* hdr,
-                                              int32_t* __restrict__ segtab, int32_t* __restrict__ items) {
+                                              int32_t* __restrict__ segtab, int32_t* __restrict__ items, int tile) {
   __shared__ int lds_wave[16];
   __shared__ int s_bad;
   const int tid = threadIdx.x;
@@ -73,11 +73,11 @@ __global__ __launch_bounds__(1024) void k_plan(const int32_t* __restrict__ seg, 
   }
   __syncthreads();
 
-  // pass 3: work items, ceil(L / BQ) q-tiles per segment, in segment order
+  // pass 3: work items, ceil(L / tile) tiles per segment, in segment order
   int nitems = 0;
   for (int base = 0; base < nseg; base += 1024) {
     const int s = base + tid;
-    const int nt = (s < nseg) ? (segtab[2 * s + 1] + BQ - 1) / BQ : 0;
+    const int nt = (s < nseg) ? (segtab[2 * s + 1] + tile - 1) / tile : 0;
     int total;
     const int off = block_excl_scan(nt, lds_wave, total);
     for (int j = 0; j < nt; j++) {
@@ -99,7 +99,15 @@ hipError_t launch_plan(const int32_t* seg, int64_t T, void* ws, int32_t H, hipSt
   const WsLayout L = ws_layout(T, H);
   char* base = (char*)ws;
   hipLaunchKernelGGL(k_plan, dim3(1), dim3(1024), 0, stream, seg, T, (WsHeader*)base, (int32_t*)(base + L.segtab),
-                     (int32_t*)(base + L.items));
+                     (int32_t*)(base + L.items), BQ);
+  return hipGetLastError();
+}
+
+hipError_t launch_plan_bwd(const int32_t* seg, int64_t T, void* ws, int32_t H, hipStream_t stream) {
+  const BwdLayout L = bwd_layout(T, H);
+  char* base = (char*)ws;
+  hipLaunchKernelGGL(k_plan, dim3(1), dim3(1024), 0, stream, seg, T, (WsHeader*)base, (int32_t*)(base + L.segtab),
+                     (int32_t*)(base + L.items), BT);
   return hipGetLastError();
 }
 

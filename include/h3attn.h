@@ -65,7 +65,7 @@ enum {
   H3ATTN_ERR_DEVICE = 6,    /* no current device, or it is not gfx950 */
   H3ATTN_ERR_LAUNCH = 7,    /* the HIP runtime rejected a launch */
   H3ATTN_ERR_SEGMENTS = 8,  /* device status: segment ids decrease somewhere */
-  H3ATTN_ERR_RANGE = 9      /* device status: a finite |v| > 65504 cannot enter the fp16 P.V product */
+  H3ATTN_ERR_RANGE = 9      /* device status: a finite value > 65504 cannot enter an fp16 product */
 };
 
 /* H3ATTN_VERSION of the loaded library. */
@@ -107,6 +107,31 @@ int h3attn_prep_kv(const void* k, const void* v, const void* wk, int64_t tokens,
                    float eps, void* workspace, size_t workspace_bytes, void* stream);
 int h3attn_attend(const void* q, const void* wq, int64_t tokens, int32_t heads, int32_t head_dim, float eps,
                   float scale, void* out, float* lse, void* workspace, size_t workspace_bytes, void* stream);
+
+/* Bytes of device workspace that h3attn_bwd needs for `tokens` x `heads`: the header, the segment
+ * table and work list (128-token tiles), seven head-major staged operands (normed q and k in bf16
+ * and fp16, v, dO in bf16 and fp16: 7 * tokens * heads * 256 bytes), the log-sum-exp and D rows
+ * (2 * tokens * heads * 4 bytes) and the per-item norm-weight gradient partials.  0 if invalid. */
+size_t h3attn_bwd_workspace_bytes(int64_t tokens, int32_t heads);
+
+/* Backward of the node: gradients of sum(dout * out) with respect to q, k, v and the two norm
+ * weights ("33B forward/backward" page: the node inside the training step's backward).  The bf16
+ * rounding of the normed q and k is the identity for gradients (straight-through); P is recomputed
+ * from the forward's log-sum-exp `lse` (fp32 [T, H], natural log, as h3attn_fwd writes it), and
+ * D_i = sum_j P_ij dP_ij is recomputed in FP32 (not taken from the rounded forward output).
+ *   dout, q, k, v: bf16 [T, H, 128] (q, k, v as given to h3attn_fwd); seg_ids as for h3attn_fwd.
+ *   dq, dk, dv: bf16 [T, H, 128] outputs, each rounded once.
+ *   dwq, dwk: fp32 [128] outputs, required when wq/wk are given (ignored otherwise): sums over every
+ *     token and head of dy * x * r, added in a fixed order (bitwise repeatable).
+ * Determinism: no atomics on data; every gradient row of q, k and v is a function of its own
+ * segment's bytes only (the same bits alone or batched); dwq/dwk are sums over the whole batch.
+ * P and dS enter their products in fp16 (as P does in the forward); a finite normed q/k or dO value
+ * beyond 65504 sets H3ATTN_ERR_RANGE in the status word and NaN-fills the outputs.
+ * Outputs must not overlap any input, the workspace or each other. */
+int h3attn_bwd(const void* dout, const void* q, const void* k, const void* v, const float* lse,
+               const int32_t* seg_ids, const void* wq, const void* wk, int64_t tokens, int32_t heads,
+               int32_t head_dim, float eps, float scale, void* dq, void* dk, void* dv, float* dwq, float* dwk,
+               void* workspace, size_t workspace_bytes, void* stream);
 
 /* Wait for `stream`, then copy the workspace's device status word to *device_status (host memory):
  * H3ATTN_OK, H3ATTN_ERR_SEGMENTS or H3ATTN_ERR_RANGE (segments first if both).  Returns the HIP

@@ -22,7 +22,7 @@ def declared_functions():
 def test_every_declared_symbol_is_exported():
     lib = h3.load()
     names = declared_functions()
-    assert len(names) == 9
+    assert len(names) == 11
     for n in names:
         assert hasattr(lib, n), f"{n} missing from libh3attn.so"
     assert sorted(h3.EXPORTS) == names
@@ -105,3 +105,40 @@ def test_staged_calls_check_arguments():
     st = ctypes.c_int32(0)
     assert lib.h3attn_status_read(None, ctypes.byref(st), None) == h3.H3ATTN_ERR_NULL
     assert lib.h3attn_status_read(A + 4, ctypes.byref(st), None) == h3.H3ATTN_ERR_ALIGN
+
+
+def bwd(lib, dout=A + 0x7000000, q=A, k=A + 0x1000000, v=A + 0x2000000, lse=A + 0x8000000, seg=A + 0x3000000,
+        wq=A + 0x4000000, wk=A + 0x4001000, T=16, H=2, D=128, eps=1e-6, scale=0.088, dq=A + 0x9000000,
+        dk=A + 0xA000000, dv=A + 0xB000000, dwq=A + 0xC000000, dwk=A + 0xC001000, ws=A + 0x10000000, wsb=None):
+    if wsb is None:
+        wsb = h3.h3attn_bwd_workspace_bytes(T, H) if T >= 0 and H >= 1 else 0
+    return lib.h3attn_bwd(dout, q, k, v, lse, seg, wq, wk, T, H, D, eps, scale, dq, dk, dv, dwq, dwk, ws, wsb, None)
+
+
+def test_bwd_workspace_bytes():
+    n = h3.h3attn_bwd_workspace_bytes(8506, 40)
+    assert n >= 7 * 8506 * 40 * 256 + 2 * 8506 * 40 * 4 and n % 256 == 0
+    assert h3.h3attn_bwd_workspace_bytes(-1, 4) == 0 and h3.h3attn_bwd_workspace_bytes(10, 0) == 0
+
+
+def test_bwd_argument_errors():
+    lib = h3.load()
+    assert bwd(lib, T=0) == h3.H3ATTN_OK
+    assert bwd(lib, T=-1) == h3.H3ATTN_ERR_SHAPE
+    assert bwd(lib, D=64) == h3.H3ATTN_ERR_SHAPE
+    assert bwd(lib, scale=0.0) == h3.H3ATTN_ERR_SHAPE
+    assert bwd(lib, eps=float("inf")) == h3.H3ATTN_ERR_SHAPE
+    assert bwd(lib, lse=None) == h3.H3ATTN_ERR_NULL
+    assert bwd(lib, dout=None) == h3.H3ATTN_ERR_NULL
+    assert bwd(lib, dwq=None) == h3.H3ATTN_ERR_NULL              # weights given, gradient missing
+    assert bwd(lib, wk=None) == h3.H3ATTN_ERR_NULL               # exactly one weight missing
+    assert bwd(lib, dq=A + 0x9000008) == h3.H3ATTN_ERR_ALIGN
+    assert bwd(lib, lse=A + 0x8000002) == h3.H3ATTN_ERR_ALIGN
+    assert bwd(lib, dk=A) == h3.H3ATTN_ERR_ALIAS                  # dk == q
+    assert bwd(lib, dv=A + 0x9000000) == h3.H3ATTN_ERR_ALIAS      # dv == dq
+    assert bwd(lib, dwq=A + 0x10000000 + 512) == h3.H3ATTN_ERR_ALIAS  # inside the workspace
+    assert bwd(lib, wsb=4096) == h3.H3ATTN_ERR_WORKSPACE
+    import torch
+    if not torch.cuda.is_available():
+        assert bwd(lib) == h3.H3ATTN_ERR_DEVICE
+        assert bwd(lib, wq=None, wk=None, dwq=None, dwk=None) == h3.H3ATTN_ERR_DEVICE
