@@ -1,12 +1,17 @@
-"""Throughput of the H3 attention forward on one MI355X.
+"""Throughput of the H3 attention node on one MI355X.
 
-One step = one h3attn_fwd call (segment plan, K norm + fp16 V staging, attention with the fused Q
-norm) over the full workload, inputs resident in HBM.  Prints ONE JSON line:
+Forward (default): one step = one h3attn_fwd call (segment plan, K norm + fp16 V staging, attention
+with the fused Q norm) over the full workload, inputs resident in HBM.  Prints ONE JSON line:
   value     whole-step attention TFLOP/s (nominal 4 * sum(L^2) * H * 128 FLOPs per step)
   roofline  the attention kernel alone (h3attn_attend), timed per launch with HIP events on the
             launch stream, against the bf16/fp16 dense MFMA peak (2516.6 TFLOP/s)
   cpu_baseline  the FP64 CPU oracle on a bounded sample of query rows of the same workload
-Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload long] [--no-cpu-baseline]
+Backward (--pass bwd, default workload batch2): one step = one h3attn_bwd call (plan, operand
+staging, dq with D, dk/dv, weight-gradient reduction) given dO and the forward's LSE; TFLOP/s on
+the nominal 2.5 x forward FLOPs; the CPU baseline is the FP64 oracle's gradients on a subset of
+heads.
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload long] [--pass fwd|bwd]
+                       [--no-cpu-baseline]
 """
 import argparse
 import json
@@ -18,6 +23,7 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 METRIC = "attention fwd TFLOP/s + % bf16 MFMA peak @8349 tok; bitwise batch-invariant"
+METRIC_BWD = "attention bwd TFLOP/s (nominal 2.5x fwd FLOPs) + % bf16 MFMA peak @2x4253 tok; bitwise batch-invariant"
 PEAK_MFMA_TFLOPS = 2516.6  # MI355X dense bf16/fp16 MFMA: 256 CU x 2.4 GHz x 4096 FLOP/clk
 PEAK_HBM_GBS = 8000.0
 
@@ -31,18 +37,27 @@ def traffic_bytes(workload):
     profiles/ (FETCH_SIZE + WRITE_SIZE of one dispatch, each scaled by the same counter's reading for
     the calibration kernel), or None when there is none for this workload or the kernel source has
     changed since the counters were taken."""
-    import hashlib
     path = os.path.join(ROOT, "profiles", f"k_attn_fwd_{workload}.traffic.json")
-    src = os.path.join(ROOT, "deterministic_invariant_attention_amd", "csrc", "k_attn_fwd.hip")
     if not os.path.exists(path):
         return None
     with open(path) as f:
         rec = json.load(f)
-    with open(src, "rb") as f:
-        sha = hashlib.sha256(f.read()).hexdigest()
-    if rec.get("kernel_source_sha256") != sha:
+    if rec.get("kernel_source_sha256") != kernel_source_sha256():
         return None
     return int(rec["traffic_bytes"])
+
+
+FWD_KERNEL_SOURCES = ("k_attn_fwd.hip", "h3_tiles.h", "h3_common.h")
+
+
+def kernel_source_sha256():
+    """sha256 over the attention kernel's source and the headers it includes, in that order."""
+    import hashlib
+    h = hashlib.sha256()
+    for name in FWD_KERNEL_SOURCES:
+        with open(os.path.join(ROOT, "deterministic_invariant_attention_amd", "csrc", name), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()
 
 
 def main():
@@ -50,7 +65,8 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--workload", default="long")
+    ap.add_argument("--workload", default=None, help="default: long (fwd), batch2 (bwd)")
+    ap.add_argument("--pass", dest="which", choices=("fwd", "bwd"), default="fwd")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="target oracle time of the CPU sample")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -69,7 +85,9 @@ def main():
     import deterministic_invariant_attention_amd as h3
     import workloads
 
-    wl = workloads.WORKLOADS[args.workload]
+    if args.which == "bwd":
+        return bench_bwd(args, workloads.WORKLOADS[args.workload or "batch2"])
+    wl = workloads.WORKLOADS[args.workload or "long"]
     dev = torch.device("cuda:0")
     x = workloads.make_inputs(wl)
     g = {n: (t.to(dev) if t is not None else None) for n, t in x.items()}
@@ -151,9 +169,13 @@ def main():
             oracle.fwd_rows(x["q"], x["k"], x["v"], seg_np, rows, x["wq"], x["wk"], wl.eps, wl.scale)
             return rows, time.perf_counter() - t1
 
-        rows, dt = run_rows(min(32, T))
-        n = int(min(T, max(32, len(rows) * args.cpu_seconds / max(dt, 1e-3))))
-        rows, dt = run_rows(n)
+        # grow the sample until it takes at least half the target time (or is the whole workload)
+        n = min(32, T)
+        while True:
+            rows, dt = run_rows(n)
+            if dt >= 0.5 * args.cpu_seconds or n == T:
+                break
+            n = int(min(T, max(2 * n, n * args.cpu_seconds / max(dt, 1e-3))))
         starts, lens = oracle.segments(seg_np)
         seg_len = np.repeat(lens, lens)
         sample_flops = float(4.0 * np.sum(seg_len[rows]) * H * 128)
@@ -183,6 +205,103 @@ def main():
         "roofline": {"bound": "mfma", "achieved": round(attn_tflops, 2), "peak": PEAK_MFMA_TFLOPS,
                      "unit": "TFLOP/s", "frac": round(attn_tflops / PEAK_MFMA_TFLOPS, 4),
                      "traffic": traffic_bytes(wl.name), "kernel": "k_attn_fwd", "kernel_ms": round(attn_ms, 4)},
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(line), flush=True)
+
+
+def bench_bwd(args, wl):
+    import numpy as np
+    import torch
+
+    import deterministic_invariant_attention_amd as h3
+    import workloads
+
+    dev = torch.device("cuda:0")
+    x = workloads.make_inputs(wl, with_grad=True)
+    g = {n: (t.to(dev) if t is not None else None) for n, t in x.items()}
+    T, H = wl.tokens, wl.heads
+    flops = 2.5 * wl.flops()
+    stream = torch.cuda.current_stream(dev)
+    log(f"workload {wl.name} backward: {wl.description}; nominal {flops:.4e} FLOP/step (2.5 x forward)")
+    _, lse = h3.h3attn_fwd(g["q"], g["k"], g["v"], g["seg"], g["wq"], g["wk"], eps=wl.eps, scale=wl.scale,
+                           want_lse=True, stream=stream)
+    ws = h3.bwd_workspace(T, H, dev)
+    outs = [torch.empty_like(g["q"]) for _ in range(3)]
+    dw = [torch.empty(128, dtype=torch.float32, device=dev) for _ in range(2)]
+
+    def step():
+        h3.h3attn_bwd(g["dout"], g["q"], g["k"], g["v"], lse, g["seg"], g["wq"], g["wk"], eps=wl.eps,
+                      scale=wl.scale, dq=outs[0], dk=outs[1], dv=outs[2], dwq=dw[0], dwk=dw[1], workspace_buf=ws,
+                      stream=stream)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    ref = [t.clone() for t in outs + dw]
+
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for a, b in evs:
+        a.record(stream)
+        step()
+        b.record(stream)
+    torch.cuda.synchronize()
+    wall_ms = (time.perf_counter() - t0) * 1e3 / args.steps
+    ms = [a.elapsed_time(b) for a, b in evs]
+    ms_per_step = float(np.mean(ms))
+    repeat_bitwise = all(torch.equal(a.view(torch.int16) if a.dtype == torch.bfloat16 else a.view(torch.int32),
+                                     b.view(torch.int16) if b.dtype == torch.bfloat16 else b.view(torch.int32))
+                         for a, b in zip(outs + dw, ref))
+    status = h3.h3attn_status_read(ws, stream)
+    value = flops / (ms_per_step * 1e-3) / 1e12
+    log(f"bwd step: mean {ms_per_step:.4f} ms, median {np.median(ms):.4f} ms (wall {wall_ms:.4f} ms) -> "
+        f"{value:.1f} TFLOP/s ({100 * value / PEAK_MFMA_TFLOPS:.1f}% of peak); repeat bitwise {repeat_bitwise}; "
+        f"status {status}")
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        import oracle
+        seg_np = x["seg"].numpy()
+
+        def run_heads(nh):
+            sub = {n: x[n][:, :nh].contiguous() for n in ("q", "k", "v", "dout")}
+            t1 = time.perf_counter()
+            oracle.bwd(sub["q"], sub["k"], sub["v"], seg_np, sub["dout"], x["wq"], x["wk"], wl.eps, wl.scale)
+            return time.perf_counter() - t1
+
+        nh = 1
+        while True:
+            dt = run_heads(nh)
+            if dt >= 0.5 * args.cpu_seconds or nh == H:
+                break
+            nh = int(min(H, max(2 * nh, nh * args.cpu_seconds / max(dt, 1e-3))))
+        cpu = {"value": round(flops * nh / H / dt / 1e12, 6), "unit": "TFLOP/s", "cores": oracle.num_threads(),
+               "kind": "oracle",
+               "sample": f"gradients of {nh} of {H} heads, all {T} tokens of the {wl.name} workload; {dt:.1f} s FP64"}
+        log(f"cpu baseline: {cpu}")
+
+    line = {
+        "metric": METRIC_BWD,
+        "value": round(value, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": wl.name + "-bwd", "tokens": T, "heads": H, "head_dim": 128,
+                   "segments": list(wl.seg_lens), "products": "fp16 P, dS, dO, q/k hat; fp32 accumulate",
+                   "pct_bf16_mfma_peak": round(100 * value / PEAK_MFMA_TFLOPS, 2),
+                   "repeat_bitwise": repeat_bitwise, "device_status": status},
+        "roofline": {"bound": "mfma", "achieved": round(value, 2), "peak": PEAK_MFMA_TFLOPS, "unit": "TFLOP/s",
+                     "frac": round(value / PEAK_MFMA_TFLOPS, 4), "traffic": None,
+                     "kernel": "h3attn_bwd (all launches of one call)", "kernel_ms": round(ms_per_step, 4)},
         "cpu_baseline": cpu,
     }
     print(json.dumps(line), flush=True)

@@ -56,11 +56,12 @@ __host__ __device__ inline WsLayout ws_layout(int64_t T, int32_t H) {
 // lse2       fp32 [H][T]: the forward's log-sum-exp in log2 units
 // delta      fp32 [H][T]: D_i = sum_j P_ij dP_ij
 // dwq, dwk   fp32 [max_items][H][128]: per-item partial sums of the norm-weight gradients
-constexpr int BT = 128;  // queries (dq kernel) or keys (dk/dv kernel) per backward work item
+constexpr int BT = 128;        // queries (dq kernel) or keys (dk/dv kernel) per backward work item
+constexpr int DW_CHUNK = 64;  // work items per chunk of the weight-gradient reduction
 
 struct BwdLayout {
-  size_t segtab, items, qhat, qhat16, khat, khat16, vh, doh, do16, lse2, delta, dwq, dwk, total;
-  int64_t max_items;
+  size_t segtab, items, qhat, qhat16, khat, khat16, vh, doh, do16, lse2, delta, dwq, dwk, dw_item, dw_chunk, total;
+  int64_t max_items, max_chunks;
 };
 
 __host__ __device__ inline BwdLayout bwd_layout(int64_t T, int32_t H) {
@@ -81,7 +82,10 @@ __host__ __device__ inline BwdLayout bwd_layout(int64_t T, int32_t H) {
   w.delta = w.lse2 + rowf;
   w.dwq = w.delta + rowf;
   w.dwk = w.dwq + align256((size_t)w.max_items * H * HD * 4);
-  w.total = w.dwk + align256((size_t)w.max_items * H * HD * 4);
+  w.dw_item = w.dwk + align256((size_t)w.max_items * H * HD * 4);
+  w.max_chunks = (w.max_items + DW_CHUNK - 1) / DW_CHUNK;
+  w.dw_chunk = w.dw_item + align256((size_t)w.max_items * 2 * HD * 4);
+  w.total = w.dw_chunk + align256((size_t)w.max_chunks * 2 * HD * 4);
   return w;
 }
 

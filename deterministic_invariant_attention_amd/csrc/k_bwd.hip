@@ -17,7 +17,7 @@
 //   k_bwd_dkdv  work item = (segment, 128-key tile, head).  One pass over the query tiles:
 //               S = Q^ K^T and dP = dO V^T with the wave's 32 keys in registers, P and dS in fp16,
 //               dV^T += dO16^T P and dK^T += Q^16^T dS.  Epilogue: norm backward of k, dwk partial.
-// Then k_bwd_dw sums the per-item weight partials in item order.
+// Then three small kernels sum the per-item weight partials in a fixed tree (heads, items, chunks).
 //
 // D is recomputed rather than taken as rowsum(dO o O) from the forward's bf16 output: with a sharp
 // softmax the rounding of O moves D enough to cost dq and dk about twice the accuracy bound.
@@ -104,12 +104,17 @@ __device__ __forceinline__ void rowvec_to_lds(const float* g, int valid, lds_cha
   __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void*)lds, 4, lane * 4, 0, 0, 0);
 }
 
+// Rows of the dw terms in LDS are padded to 132 floats: with 128 the 32 rows a wave writes at once
+// would all start in the same bank.
+constexpr int RED_STRIDE = HD + 4;
+static_assert(BT * RED_STRIDE * 4 <= 6 * TILE_ELEMS * 2, "dw rows fit in the tiles they replace");
+
 // RMSNorm backward of one row held as a lane pair in the accumulator layout (dims 32db + 8g + 4hh +
 // e in dy[db][4g + e]), dy = the gradient with respect to the normed output; x: the raw row (bf16,
 // token-major), w: the weight.  Writes dx = r g - (r^3 / 128) x (g . x), g = w o dy, rounded once
-// to bf16 (if store), and the row's dw terms dy o x r into red[row][dim] (LDS).  r is the forward's
-// FP64 value (same fixed tree); the rest is evaluated in FP64, g . x over the lane's dims in a fixed
-// order and then across the pair.
+// to bf16 (if store), and the row's dw terms dy o x r into red[row][dim] (LDS, row stride
+// RED_STRIDE).  r is the forward's FP64 value (same fixed tree); the rest is evaluated in FP64,
+// g . x over the lane's dims in a fixed order and then across the pair.
 __device__ __forceinline__ void norm_bwd_pair(const f32x16* dy, const uint16_t* x, const uint16_t* w, float eps,
                                               int hh, bool store, uint16_t* dx, float* red, int row) {
   double part[8];
@@ -148,12 +153,14 @@ __device__ __forceinline__ void norm_bwd_pair(const f32x16* dy, const uint16_t* 
       float xf[4], wf[4];
       chunk(db, g, xf, wf);
       uint32_t o[4];
+      f32x4 t4;
 #pragma unroll
       for (int e = 0; e < 4; e++) {
         const double dyv = (double)dy[db][4 * g + e];
         o[e] = f64_to_bf16_rne(r * ((double)wf[e] * dyv) - k3 * (double)xf[e]);
-        red[row * HD + d0 + e] = store ? (float)(dyv * (double)xf[e] * r) : 0.0f;
+        t4[e] = store ? (float)(dyv * (double)xf[e] * r) : 0.0f;
       }
+      *(f32x4*)&red[row * RED_STRIDE + d0] = t4;
       if (store) {
         u32x2 o2;
         o2[0] = o[0] | (o[1] << 16);
@@ -169,7 +176,7 @@ __device__ __forceinline__ void dw_reduce(const float* red, int tid, float* out)
   __syncthreads();
   if (tid < HD) {
     float s = 0.0f;
-    for (int r = 0; r < BT; r++) s += red[r * HD + tid];
+    for (int r = 0; r < BT; r++) s += red[r * RED_STRIDE + tid];
     out[tid] = s;
   }
 }
@@ -489,23 +496,64 @@ __global__ __launch_bounds__(64 * BW, 1) void k_bwd_dkdv(BwdParams p) {
 
 // ============================================================================== dw
 
-// dw[d] = sum over work items and heads of the partials, in (item, head) order: one thread per
-// channel, sequential, so the result is repeatable bit for bit.  With a recorded data error the
-// weights' gradients are NaN like the other outputs.
-__global__ __launch_bounds__(256) void k_bwd_dw(const WsHeader* hdr, const float* qpart, const float* kpart,
-                                                int64_t max_items, int32_t H, float* dwq, float* dwk) {
-  const int t = threadIdx.x;
-  const int d = t & (HD - 1);
-  const float* part = t < HD ? qpart : kpart;
-  float* out = t < HD ? dwq : dwk;
+// dw[d] = the sum of the per-(item, head) partials in a fixed tree whose shape depends only on the
+// number of work items: (1) per item, over heads ascending; (2) per chunk of DW_CHUNK consecutive
+// items, ascending; (3) over the chunks, ascending.  Every level keeps several independent loads
+// in flight per thread (the sums themselves stay sequential), so the chains are short.  Thread t of
+// a 256-thread block: t < 128 works on dwq, else on dwk, channel t % 128.
+
+__device__ __forceinline__ float sum_strided(const float* base, int64_t n, int64_t stride) {
+  float s = 0.0f;
+  int64_t i = 0;
+  for (; i + 8 <= n; i += 8) {
+    float v[8];
+#pragma unroll
+    for (int u = 0; u < 8; u++) v[u] = base[(i + u) * stride];
+#pragma unroll
+    for (int u = 0; u < 8; u++) s += v[u];
+  }
+  for (; i < n; i++) s += base[i * stride];
+  return s;
+}
+
+__device__ __forceinline__ int64_t dw_items(const WsHeader* hdr, int64_t max_items) {
+  return min((int64_t)max(hdr->nitems, 0), max_items);
+}
+
+// (1) item_part[item][q/k][d] = sum over heads of part[item][head][d]
+__global__ __launch_bounds__(256) void k_bwd_dw_items(const WsHeader* hdr, const float* qpart, const float* kpart,
+                                                      int64_t max_items, int32_t H, float* item_part) {
+  const int t = threadIdx.x, d = t & (HD - 1), which = t >> 7;
+  const float* part = which ? kpart : qpart;
+  const int64_t n = dw_items(hdr, max_items);
+  for (int64_t it = blockIdx.x; it < n; it += gridDim.x)
+    item_part[(it * 2 + which) * HD + d] = sum_strided(part + it * H * HD + d, H, HD);
+}
+
+// (2) chunk_part[c][q/k][d] = sum over items c*DW_CHUNK .. of item_part
+__global__ __launch_bounds__(256) void k_bwd_dw_chunks(const WsHeader* hdr, const float* item_part, int64_t max_items,
+                                                       float* chunk_part) {
+  const int t = threadIdx.x, d = t & (HD - 1), which = t >> 7;
+  const int64_t n = dw_items(hdr, max_items);
+  const int64_t nc = (n + DW_CHUNK - 1) / DW_CHUNK;
+  for (int64_t c = blockIdx.x; c < nc; c += gridDim.x) {
+    const int64_t i0 = c * DW_CHUNK, cnt = min((int64_t)DW_CHUNK, n - i0);
+    chunk_part[(c * 2 + which) * HD + d] = sum_strided(item_part + (i0 * 2 + which) * HD + d, cnt, 2 * HD);
+  }
+}
+
+// (3) dw = sum over chunks.  With a recorded data error the weights' gradients are NaN like the other
+// outputs.
+__global__ __launch_bounds__(256) void k_bwd_dw_final(const WsHeader* hdr, const float* chunk_part, int64_t max_items,
+                                                      float* dwq, float* dwk) {
+  const int t = threadIdx.x, d = t & (HD - 1), which = t >> 7;
+  float* out = which ? dwk : dwq;
   if (hdr->status != 0) {
     out[d] = __builtin_nanf("");
     return;
   }
-  const int64_t n = min((int64_t)max(hdr->nitems, 0), max_items) * H;
-  float s = 0.0f;
-  for (int64_t i = 0; i < n; i++) s += part[i * HD + d];
-  out[d] = s;
+  const int64_t nc = (dw_items(hdr, max_items) + DW_CHUNK - 1) / DW_CHUNK;
+  out[d] = sum_strided(chunk_part + which * HD + d, nc, 2 * HD);
 }
 
 hipError_t launch_bwd(const void* q, const void* k, const void* wq, const void* wk, int64_t T, int32_t H, float eps,
@@ -551,8 +599,15 @@ hipError_t launch_bwd(const void* q, const void* k, const void* wq, const void* 
   e = hipGetLastError();
   if (e != hipSuccess) return e;
   if (wq) {
-    hipLaunchKernelGGL(k_bwd_dw, dim3(1), dim3(256), 0, stream, (const WsHeader*)base, p.dwq_part, p.dwk_part,
-                       Lw.max_items, H, dwq, dwk);
+    const WsHeader* hdr = (const WsHeader*)base;
+    float* item_part = (float*)(base + Lw.dw_item);
+    float* chunk_part = (float*)(base + Lw.dw_chunk);
+    const unsigned g1 = (unsigned)(Lw.max_items < 1024 ? Lw.max_items : 1024);
+    const unsigned g2 = (unsigned)(Lw.max_chunks < 256 ? Lw.max_chunks : 256);
+    hipLaunchKernelGGL(k_bwd_dw_items, dim3(g1), dim3(256), 0, stream, hdr, p.dwq_part, p.dwk_part, Lw.max_items, H,
+                       item_part);
+    hipLaunchKernelGGL(k_bwd_dw_chunks, dim3(g2), dim3(256), 0, stream, hdr, item_part, Lw.max_items, chunk_part);
+    hipLaunchKernelGGL(k_bwd_dw_final, dim3(1), dim3(256), 0, stream, hdr, chunk_part, Lw.max_items, dwq, dwk);
     e = hipGetLastError();
   }
   return e;
