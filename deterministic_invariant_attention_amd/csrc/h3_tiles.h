@@ -38,9 +38,13 @@ __device__ __forceinline__ void tile_to_lds(const uint16_t* gtile, int valid, ui
   static_assert(TILE_ROWS % (4 * NW) == 0, "whole 1 KB blocks per wave");
   const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
       (void*)gtile, (short)0, (valid < TILE_ROWS ? valid : TILE_ROWS) * 256, 0x00020000);
+  // The wave's block offset is opaque here, so each copy forms its LDS address (M0) next to its
+  // use instead of keeping one hoisted SGPR per buffer and block alive across the whole loop.
+  int wofs = wv * 4 * HD;
+  asm volatile("" : "+s"(wofs));
 #pragma unroll
   for (int i = 0; i < TILE_ROWS / (4 * NW); i++)  // block NW*i + wv = rows 4*NW*i + 4wv .. +3
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void*)(lds_tile + (NW * i + wv) * 4 * HD), 16,
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void*)(lds_tile + NW * i * 4 * HD + wofs), 16,
                                              lane_off + i * NW * 1024, 0, 0, 0);
 }
 
@@ -180,6 +184,14 @@ __device__ __forceinline__ void mask_tail(f32x16* S, int rem, int hh) {
 #pragma unroll
     for (int i = 0; i < 16; i++)
       if (32 * kb + 8 * (i >> 2) + 4 * hh + (i & 3) >= rem) S[kb][i] = -__builtin_inff();
+}
+// The same with the lane's limit given as rel = rem - 4hh.
+__device__ __forceinline__ void mask_tail_rel(f32x16* S, int rel) {
+#pragma unroll
+  for (int kb = 0; kb < 2; kb++)
+#pragma unroll
+    for (int i = 0; i < 16; i++)
+      if (32 * kb + 8 * (i >> 2) + (i & 3) >= rel) S[kb][i] = -__builtin_inff();
 }
 
 // Products whose A operand is a 64-row LDS tile read by rows (16-byte reads, K swizzle) and whose B

@@ -243,7 +243,14 @@ __global__ __launch_bounds__(64 * NWAVES, 1) void k_attn_fwd(AttnParams p) {
       } else {
         const int k = (tau - 1) / 2 - 1;
         if (k + 1 < ntiles) {
-          if (k + 1 == ntiles - 1 && rem < BK) mask_tail(S, rem, hh);
+          if (k + 1 == ntiles - 1 && rem < BK) {
+            // The key limit enters as an opaque per-lane value, so the 32 compares stay in this
+            // last-tile branch: hoisted out of the loop they were 32 SGPR masks, and the SGPR
+            // spills they caused were reloaded on every phase.
+            int r = rem - 4 * hh;
+            asm volatile("" : "+v"(r));
+            mask_tail_rel(S, r);
+          }
           const float mt = tile_max(S) * c;
           if (k + 1 == 0) {
             m_run = mt;  // first tile: m is the tile maximum (log2 units)
