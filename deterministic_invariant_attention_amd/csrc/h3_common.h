@@ -57,18 +57,22 @@ __host__ __device__ inline WsLayout ws_layout(int64_t T, int32_t H) {
 // delta      fp32 [H][T]: D_i = sum_j P_ij dP_ij
 // dwq, dwk   fp32 [max_items][H][128]: per-item partial sums of the norm-weight gradients
 constexpr int BT = 128;        // queries (dq kernel) or keys (dk/dv kernel) per backward work item
-constexpr int DW_CHUNK = 64;  // work items per chunk of the weight-gradient reduction
+constexpr int NR = 16;         // rows (token, head) per workgroup of the norm backward
+constexpr int DW_CHUNK = 64;   // partials per chunk of the weight-gradient reduction
 
 struct BwdLayout {
-  size_t segtab, items, qhat, qhat16, khat, khat16, vh, doh, do16, lse2, delta, dwq, dwk, dw_item, dw_chunk, total;
-  int64_t max_items, max_chunks;
+  size_t segtab, items, qhat, qhat16, khat, khat16, vh, doh, do16, lse2, delta, dqh, dkh, dw_part, dw_chunk, total;
+  int64_t max_items, nparts, nchunks;
 };
 
 __host__ __device__ inline BwdLayout bwd_layout(int64_t T, int32_t H) {
   BwdLayout w;
   const size_t tens = align256((size_t)T * H * HD * 2);
+  const size_t tens32 = align256((size_t)T * H * HD * 4);
   const size_t rowf = align256((size_t)T * H * 4);
   w.max_items = T + (T + BT - 1) / BT;
+  w.nparts = (T * H + NR - 1) / NR;
+  w.nchunks = (w.nparts + DW_CHUNK - 1) / DW_CHUNK;
   w.segtab = 256;
   w.items = w.segtab + align256((size_t)T * 8);
   w.qhat = w.items + align256((size_t)w.max_items * 8);
@@ -80,12 +84,11 @@ __host__ __device__ inline BwdLayout bwd_layout(int64_t T, int32_t H) {
   w.do16 = w.doh + tens;
   w.lse2 = w.do16 + tens;
   w.delta = w.lse2 + rowf;
-  w.dwq = w.delta + rowf;
-  w.dwk = w.dwq + align256((size_t)w.max_items * H * HD * 4);
-  w.dw_item = w.dwk + align256((size_t)w.max_items * H * HD * 4);
-  w.max_chunks = (w.max_items + DW_CHUNK - 1) / DW_CHUNK;
-  w.dw_chunk = w.dw_item + align256((size_t)w.max_items * 2 * HD * 4);
-  w.total = w.dw_chunk + align256((size_t)w.max_chunks * 2 * HD * 4);
+  w.dqh = w.delta + rowf;
+  w.dkh = w.dqh + tens32;
+  w.dw_part = w.dkh + tens32;
+  w.dw_chunk = w.dw_part + align256((size_t)2 * w.nparts * HD * 4);
+  w.total = w.dw_chunk + align256((size_t)2 * w.nchunks * HD * 4);
   return w;
 }
 

@@ -12,12 +12,14 @@
 // segment-anchored 64-row tiles, so every gradient row is a fixed function of its own segment:
 //   k_bwd_dq    work item = (segment, 128-query tile, head).  Pass 1 over the key tiles computes
 //               D_i exactly (in fp32, a fixed tree per tile); pass 2 recomputes S and dP, forms dS
-//               and accumulates dQ^T += K^16^T dS^T.  Epilogue: norm backward of q, per-item
-//               partial of dwq.
+//               and accumulates dQ^T += K^16^T dS^T.
 //   k_bwd_dkdv  work item = (segment, 128-key tile, head).  One pass over the query tiles:
 //               S = Q^ K^T and dP = dO V^T with the wave's 32 keys in registers, P and dS in fp16,
-//               dV^T += dO16^T P and dK^T += Q^16^T dS.  Epilogue: norm backward of k, dwk partial.
-// Then three small kernels sum the per-item weight partials in a fixed tree (heads, items, chunks).
+//               dV^T += dO16^T P and dK^T += Q^16^T dS; the scores of query tile j+1 are computed
+//               before the products of tile j, whose transposed reads run as one pipeline.
+// With norm weights both write dq^ / dk^ in fp32 and k_bwd_norm applies the RMSNorm backward per
+// row (FP64, one bf16 rounding) and writes fixed-order weight-gradient partials, which two small
+// kernels sum in a fixed tree; without weights the kernels write dq, dk directly.
 //
 // D is recomputed rather than taken as rowsum(dO o O) from the forward's bf16 output: with a sharp
 // softmax the rounding of O moves D enough to cost dq and dk about twice the accuracy bound.
@@ -49,8 +51,8 @@ struct BwdParams {
   uint16_t* dq;  // outputs, token-major
   uint16_t* dk;
   uint16_t* dv;
-  float* dwq_part;  // [max_items][H][128]
-  float* dwk_part;
+  float* dqh;  // with norm weights: gradients with respect to the normed q / k, fp32 token-major
+  float* dkh;
   const WsHeader* hdr;
   const int32_t* segtab;
   const int32_t* items;
@@ -104,83 +106,6 @@ __device__ __forceinline__ void rowvec_to_lds(const float* g, int valid, lds_cha
   __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void*)lds, 4, lane * 4, 0, 0, 0);
 }
 
-// Rows of the dw terms in LDS are padded to 132 floats: with 128 the 32 rows a wave writes at once
-// would all start in the same bank.
-constexpr int RED_STRIDE = HD + 4;
-static_assert(BT * RED_STRIDE * 4 <= 6 * TILE_ELEMS * 2, "dw rows fit in the tiles they replace");
-
-// RMSNorm backward of one row held as a lane pair in the accumulator layout (dims 32db + 8g + 4hh +
-// e in dy[db][4g + e]), dy = the gradient with respect to the normed output; x: the raw row (bf16,
-// token-major), w: the weight.  Writes dx = r g - (r^3 / 128) x (g . x), g = w o dy, rounded once
-// to bf16 (if store), and the row's dw terms dy o x r into red[row][dim] (LDS, row stride
-// RED_STRIDE).  r is the forward's FP64 value (same fixed tree); the rest is evaluated in FP64,
-// g . x over the lane's dims in a fixed order and then across the pair.
-__device__ __forceinline__ void norm_bwd_pair(const f32x16* dy, const uint16_t* x, const uint16_t* w, float eps,
-                                              int hh, bool store, uint16_t* dx, float* red, int row) {
-  double part[8];
-  {
-    float xs[8][8];
-#pragma unroll
-    for (int m = 0; m < 8; m++) unpack8_bf16(*(const u32x4*)(x + 16 * m + 8 * hh), xs[m]);
-#pragma unroll
-    for (int m = 0; m < 8; m++) part[m] = chunk_sumsq(xs[m]);
-  }
-  const double r = norm_rscale(row_total_2lanes(part), eps);
-  auto chunk = [&](int db, int g, float* xf, float* wf) {
-    const int d0 = 32 * db + 8 * g + 4 * hh;
-    const u32x2 xw = *(const u32x2*)(x + d0);
-    const u32x2 ww = *(const u32x2*)(w + d0);
-    xf[0] = bf16_lo(xw[0]), xf[1] = bf16_hi(xw[0]), xf[2] = bf16_lo(xw[1]), xf[3] = bf16_hi(xw[1]);
-    wf[0] = bf16_lo(ww[0]), wf[1] = bf16_hi(ww[0]), wf[2] = bf16_lo(ww[1]), wf[3] = bf16_hi(ww[1]);
-  };
-  double gx = 0.0;
-#pragma unroll
-  for (int db = 0; db < 4; db++)
-#pragma unroll
-    for (int g = 0; g < 4; g++) {
-      float xf[4], wf[4];
-      chunk(db, g, xf, wf);
-#pragma unroll
-      for (int e = 0; e < 4; e++) gx = __builtin_fma((double)wf[e] * (double)dy[db][4 * g + e], (double)xf[e], gx);
-    }
-  gx = gx + __shfl_xor(gx, 32, 64);  // both halves of the row (commutative: same bits in both lanes)
-  const double k3 = r * r * r * 0.0078125 * gx;
-#pragma unroll
-  for (int db = 0; db < 4; db++)
-#pragma unroll
-    for (int g = 0; g < 4; g++) {
-      const int d0 = 32 * db + 8 * g + 4 * hh;
-      float xf[4], wf[4];
-      chunk(db, g, xf, wf);
-      uint32_t o[4];
-      f32x4 t4;
-#pragma unroll
-      for (int e = 0; e < 4; e++) {
-        const double dyv = (double)dy[db][4 * g + e];
-        o[e] = f64_to_bf16_rne(r * ((double)wf[e] * dyv) - k3 * (double)xf[e]);
-        t4[e] = store ? (float)(dyv * (double)xf[e] * r) : 0.0f;
-      }
-      *(f32x4*)&red[row * RED_STRIDE + d0] = t4;
-      if (store) {
-        u32x2 o2;
-        o2[0] = o[0] | (o[1] << 16);
-        o2[1] = o[2] | (o[3] << 16);
-        *(u32x2*)(dx + d0) = o2;
-      }
-    }
-}
-
-// Sum the workgroup's 128 rows of dw terms (red[row][dim], LDS) into one partial [128] in a fixed
-// order (rows ascending).  The caller has written every row (zeros for rows past the segment end).
-__device__ __forceinline__ void dw_reduce(const float* red, int tid, float* out) {
-  __syncthreads();
-  if (tid < HD) {
-    float s = 0.0f;
-    for (int r = 0; r < BT; r++) s += red[r * RED_STRIDE + tid];
-    out[tid] = s;
-  }
-}
-
 // Store a row held as a lane pair in the accumulator layout, times s, rounded once to bf16.
 __device__ __forceinline__ void store_row(const f32x16* acc, float s, int hh, uint16_t* out) {
 #pragma unroll
@@ -192,6 +117,18 @@ __device__ __forceinline__ void store_row(const f32x16* acc, float s, int hh, ui
       o2[0] = pack_bf16(acc[db][4 * g] * s, acc[db][4 * g + 1] * s);
       o2[1] = pack_bf16(acc[db][4 * g + 2] * s, acc[db][4 * g + 3] * s);
       *(u32x2*)(out + d0) = o2;
+    }
+}
+
+// Store a row held as a lane pair in the accumulator layout, times s, in fp32.
+__device__ __forceinline__ void store_row_f32(const f32x16* acc, float s, int hh, float* out) {
+#pragma unroll
+  for (int db = 0; db < 4; db++)
+#pragma unroll
+    for (int g = 0; g < 4; g++) {
+      const int d0 = 32 * db + 8 * g + 4 * hh;
+      const f32x4 v = {acc[db][4 * g] * s, acc[db][4 * g + 1] * s, acc[db][4 * g + 2] * s, acc[db][4 * g + 3] * s};
+      *(f32x4*)(out + d0) = v;
     }
 }
 
@@ -345,21 +282,13 @@ __global__ __launch_bounds__(64 * BW, 1) void k_bwd_dq(BwdParams p) {
       if (j < ntk) pass2(Par2<0>{}, j);
     }
 
-    // ---- epilogue: dq^ = scale dQ, norm backward, dwq partial
-    const int qr = qvalid ? qrow : 0;
-    uint16_t* dqrow = p.dq + ((int64_t)(w.s0 + qr) * H + w.head) * HD;
-    if (p.wq) {
-      f32x16 dy[4];
-#pragma unroll
-      for (int d = 0; d < 4; d++)
-#pragma unroll
-        for (int i = 0; i < 16; i++) dy[d][i] = acc[d][i] * p.scale;
-      __syncthreads();  // every wave is done with the LDS tiles: they become the dw rows
-      norm_bwd_pair(dy, p.q + ((int64_t)(w.s0 + qr) * H + w.head) * HD, p.wq, p.eps, hh, qvalid, dqrow,
-                    (float*)lds, wv * 32 + l32);
-      dw_reduce((const float*)lds, tid, p.dwq_part + ((int64_t)w.item * H + w.head) * HD);
-    } else if (qvalid) {
-      store_row(acc, p.scale, hh, dqrow);
+    // ---- epilogue: dq^ = scale dQ (fp32 for the norm backward, else the output itself)
+    if (qvalid) {
+      const int64_t orow = ((int64_t)(w.s0 + qrow) * H + w.head) * HD;
+      if (p.wq)
+        store_row_f32(acc, p.scale, hh, p.dqh + orow);
+      else
+        store_row(acc, p.scale, hh, p.dq + orow);
     }
   }
 }
@@ -367,8 +296,9 @@ __global__ __launch_bounds__(64 * BW, 1) void k_bwd_dq(BwdParams p) {
 // ============================================================================== dk, dv
 
 __global__ __launch_bounds__(64 * BW, 1) void k_bwd_dkdv(BwdParams p) {
-  // tiles 0, 1: Q^16, 2, 3: dO16 (transposed reads) of stage 0 / 1; 4, 5: Q^, 6, 7: dO (row reads);
-  // then the fp32 rows [stage][lse2, D][64 queries]
+  // tiles 0, 1: Q^16 and 2, 3: dO16 (transposed reads) of transposed-read stage 0 / 1; 4, 5: Q^ and
+  // 6, 7: dO (row reads) of row stage 0 / 1; then the fp32 rows [row stage][lse2, D][64 queries].
+  // The row tiles (and their lse/D rows) run one query tile ahead of the transposed tiles.
   __shared__ __attribute__((aligned(1024))) uint16_t lds[8 * TILE_ELEMS + 2 * 2 * TILE_ROWS * 2];
   const float* lrow = (const float*)(lds + 8 * TILE_ELEMS);  // lrow[(2 * stage + which) * 64 + query]
   lds_char* const lrow3 = (lds_char*)lds + 8 * TILE_ELEMS * 2;  // the same rows as an LDS address
@@ -388,6 +318,7 @@ __global__ __launch_bounds__(64 * BW, 1) void k_bwd_dkdv(BwdParams p) {
   const int tr_off = tile_lane_offset(true, wv, lane);
   uint32_t vb[4];
   tr_bases(lds, lane, vb);
+  const RowBases rb = row_bases(lds, l32, hh);
   const float c = p.c;
 
   for (int round = 0;; round++) {
@@ -408,22 +339,40 @@ __global__ __launch_bounds__(64 * BW, 1) void k_bwd_dkdv(BwdParams p) {
     const int krow = row0 + l32;
     const bool kvalid = krow < w.L;
 
-    // stage ST of the tiles of query tile j (ST a compile-time constant at every call, so the
-    // compiler sees that a copy never writes the stage being read and adds no wait for it)
-    auto copies = [&](int j, auto stage) {
+    // Copies into a compile-time stage (so the compiler sees that a copy never writes the stage
+    // being read and adds no wait for it).
+    auto copy_rows = [&](int j, auto stage) {  // Q^, dO rows and the lse/D rows of query tile j
       constexpr int st = decltype(stage)::value;
       const int64_t o = (int64_t)j * TILE_ELEMS;
       const int v = w.L - j * TILE_ROWS;
-      tile_to_lds<BW>(q16b + o, v, lds + (0 + st) * TILE_ELEMS, wv, tr_off);
-      tile_to_lds<BW>(g16b + o, v, lds + (2 + st) * TILE_ELEMS, wv, tr_off);
       tile_to_lds<BW>(qb + o, v, lds + (4 + st) * TILE_ELEMS, wv, row_off);
       tile_to_lds<BW>(gb + o, v, lds + (6 + st) * TILE_ELEMS, wv, row_off);
       if (wv == 0) rowvec_to_lds(lb + j * TILE_ROWS, v, lrow3 + (2 * st + 0) * TILE_ROWS * 4, lane);
       if (wv == 1) rowvec_to_lds(db + j * TILE_ROWS, v, lrow3 + (2 * st + 1) * TILE_ROWS * 4, lane);
     };
+    auto copy_tr = [&](int j, auto stage) {  // Q^16, dO16 of query tile j
+      constexpr int st = decltype(stage)::value;
+      const int64_t o = (int64_t)j * TILE_ELEMS;
+      const int v = w.L - j * TILE_ROWS;
+      tile_to_lds<BW>(q16b + o, v, lds + (0 + st) * TILE_ELEMS, wv, tr_off);
+      tile_to_lds<BW>(g16b + o, v, lds + (2 + st) * TILE_ELEMS, wv, tr_off);
+    };
+    // lse2 / D of the queries a lane's score elements belong to (query 32qb + 8g + 4hh + e of the
+    // tile), from row stage ST
+    auto load_ld = [&](auto stage, f32x4 (&l4)[2][4], f32x4 (&d4)[2][4]) {
+      constexpr int ST = decltype(stage)::value;
+#pragma unroll
+      for (int q2 = 0; q2 < 2; q2++)
+#pragma unroll
+        for (int g = 0; g < 4; g++) {
+          l4[q2][g] = *(const f32x4*)&lrow[(2 * ST + 0) * TILE_ROWS + 32 * q2 + 8 * g + 4 * hh];
+          d4[q2][g] = *(const f32x4*)&lrow[(2 * ST + 1) * TILE_ROWS + 32 * q2 + 8 * g + 4 * hh];
+        }
+    };
 
     __syncthreads();  // the previous item's LDS reads are done
-    copies(0, Par2<0>{});
+    copy_rows(0, Par2<0>{});
+    copy_tr(0, Par2<0>{});
     bf16x8 kf[8], vf[8];
     load_b_rows(p.khat + (hT + w.s0 + row0) * HD, w.L - row0, l32, hh, kf);
     load_b_rows(p.vh + (hT + w.s0 + row0) * HD, w.L - row0, l32, hh, vf);
@@ -434,73 +383,206 @@ __global__ __launch_bounds__(64 * BW, 1) void k_bwd_dkdv(BwdParams p) {
 #pragma unroll
       for (int i = 0; i < 16; i++) dv[d][i] = dk[d][i] = 0.0f;
 
-    auto step = [&](auto st, int j) {
-      constexpr int ST = decltype(st)::value;
-      copies_barrier();  // tile j has landed, every wave is done with stage 1 - ST
-      if (j + 1 < ntq) copies(j + 1, Par2<1 - ST>{});
-      // S[qb][i] / dP[qb][i]: query 32qb + 8(i/4) + 4hh + (i%4) of the tile, key = the lane's key
+    // Query tile 0: S = Q^ K^T and dP = dO V^T (query 32qb + 8(i/4) + 4hh + (i%4), the lane's key),
+    // then P = exp2(S c - lse2) and dS = P (dP - D), packed to fp16 for the products.
+    f16x8 pf[4], dsf[4];
+    copies_barrier();  // tile 0 has landed everywhere
+    if (1 < ntq) copy_rows(1, Par2<1>{});
+    {
       f32x16 S[2], dP[2];
-      gemm_scores<4>(lds + (4 + ST) * TILE_ELEMS, kf, l32, hh, S);
-      gemm_scores<4>(lds + (6 + ST) * TILE_ELEMS, vf, l32, hh, dP);
+      f32x4 l4[2][4], d4[2][4];
+      load_ld(Par2<0>{}, l4, d4);
+      gemm_rows<4>(rb, kf, S, [](auto) {});
+#pragma unroll
+      for (int q2 = 0; q2 < 2; q2++)
+#pragma unroll
+        for (int g = 0; g < 4; g++) asm volatile("" : "+v"(l4[q2][g]), "+v"(d4[q2][g]));
       float pr[2][16], ds[2][16];
+      gemm_rows<6>(rb, vf, dP, [&](auto step) {
+        constexpr int st = decltype(step)::value;
 #pragma unroll
-      for (int qb = 0; qb < 2; qb++)
-#pragma unroll
-        for (int g = 0; g < 4; g++) {
-          const f32x4 l4 = *(const f32x4*)&lrow[(2 * ST + 0) * TILE_ROWS + 32 * qb + 8 * g + 4 * hh];
-          const f32x4 d4 = *(const f32x4*)&lrow[(2 * ST + 1) * TILE_ROWS + 32 * qb + 8 * g + 4 * hh];
-#pragma unroll
-          for (int e = 0; e < 4; e++) {
-            const float pv = __builtin_amdgcn_exp2f(__builtin_fmaf(S[qb][4 * g + e], c, -l4[e]));
-            pr[qb][4 * g + e] = pv;
-            ds[qb][4 * g + e] = pv * (dP[qb][4 * g + e] - d4[e]);
-          }
+        for (int u = 0; u < 2; u++) {
+          constexpr int q2 = st >> 3;
+          const int i = 2 * (st & 7) + u;
+          pr[q2][i] = __builtin_amdgcn_exp2f(__builtin_fmaf(S[q2][i], c, -l4[q2][i >> 2][i & 3]));
         }
-      f16x8 pf[4], dsf[4];
+        if constexpr ((st & 3) == 3) {
+          constexpr int ks = st >> 2;
+          pf[ks] = pack_p(&pr[ks >> 1][8 * (ks & 1)]);
+        }
+      });
 #pragma unroll
       for (int ks = 0; ks < 4; ks++) {
-        pf[ks] = pack_p(&pr[ks >> 1][8 * (ks & 1)]);
+#pragma unroll
+        for (int u = 0; u < 8; u++) {
+          const int q2 = ks >> 1, i = 8 * (ks & 1) + u;
+          ds[q2][i] = pr[q2][i] * (dP[q2][i] - d4[q2][i >> 2][i & 3]);
+        }
         dsf[ks] = pack_p(&ds[ks >> 1][8 * (ks & 1)]);
       }
-      __builtin_amdgcn_sched_barrier(0);
-      tr_gemm<2 + ST>(vb, pf, dv);   // dV^T += dO16^T P
-      tr_gemm<0 + ST>(vb, dsf, dk);  // dK^T += Q^16^T dS
+    }
+
+    // Iteration j: dV^T += dO16^T P and dK^T += Q^16^T dS over query tile j (one pipeline of 32
+    // transposed-read MFMAs), with the scores of tile j+1 computed first and its P / dS evaluated
+    // between those MFMAs.
+    auto iter = [&](auto par, int j) {
+      constexpr int P = decltype(par)::value;  // j & 1: tile j's transposed stage, tile j+1's row stage is 1 - P
+      copies_barrier();  // rows of tile j+1 and the transposed tiles of tile j have landed
+      if (j + 2 < ntq) copy_rows(j + 2, Par2<P>{});
+      if (j + 1 < ntq) copy_tr(j + 1, Par2<1 - P>{});
+      const f16x8* bop[2] = {pf, dsf};
+      f32x16* acc[2] = {dv, dk};
+      if (j + 1 < ntq) {
+        f32x16 S[2], dP[2];
+        f32x4 l4[2][4], d4[2][4];
+        load_ld(Par2<1 - P>{}, l4, d4);
+        gemm_rows<4 + 1 - P>(rb, kf, S, [](auto) {});
+        // the lse/D reads complete here, before the next pipelines count their own reads
+#pragma unroll
+        for (int q2 = 0; q2 < 2; q2++)
+#pragma unroll
+          for (int g = 0; g < 4; g++) asm volatile("" : "+v"(l4[q2][g]), "+v"(d4[q2][g]));
+        // dP = dO V^T, with P = exp2(S c - lse2) formed (and packed) between its MFMAs
+        float pr[2][16];
+        f16x8 pf2[4], dsf2[4];
+        gemm_rows<6 + 1 - P>(rb, vf, dP, [&](auto step) {
+          constexpr int st = decltype(step)::value;
+#pragma unroll
+          for (int u = 0; u < 2; u++) {
+            constexpr int q2 = st >> 3;
+            const int i = 2 * (st & 7) + u;
+            pr[q2][i] = __builtin_amdgcn_exp2f(__builtin_fmaf(S[q2][i], c, -l4[q2][i >> 2][i & 3]));
+          }
+          if constexpr ((st & 3) == 3) {
+            constexpr int ks = st >> 2;
+            pf2[ks] = pack_p(&pr[ks >> 1][8 * (ks & 1)]);
+          }
+        });
+        // dV^T += dO16^T P and dK^T += Q^16^T dS over tile j, with dS = P (dP - D) of tile j+1
+        // formed (and packed) between those MFMAs
+        float ds[2][16];
+        tr_gemm_hooked<TilePair<2 + P, 0 + P>, 2>(vb, bop, acc, [&](auto step) {
+          constexpr int t = decltype(step)::value;
+          constexpr int q2 = t >> 4, i = t & 15;
+          ds[q2][i] = pr[q2][i] * (dP[q2][i] - d4[q2][i >> 2][i & 3]);
+          if constexpr ((i & 7) == 7) {
+            constexpr int ks = 2 * q2 + (i >> 3);
+            dsf2[ks] = pack_p(&ds[q2][8 * (i >> 3)]);
+          }
+        });
+#pragma unroll
+        for (int ks = 0; ks < 4; ks++) {
+          pf[ks] = pf2[ks];
+          dsf[ks] = dsf2[ks];
+        }
+      } else {
+        tr_gemm_hooked<TilePair<2 + P, 0 + P>, 2>(vb, bop, acc, [](auto) {});
+      }
     };
     {
       int j = 0;
       for (; j + 1 < ntq; j += 2) {
-        step(Par2<0>{}, j);
-        step(Par2<1>{}, j + 1);
+        iter(Par2<0>{}, j);
+        iter(Par2<1>{}, j + 1);
       }
-      if (j < ntq) step(Par2<0>{}, j);
+      if (j < ntq) iter(Par2<0>{}, j);
     }
 
-    // ---- epilogue: dv, dk^ = scale dK, norm backward, dwk partial
-    const int kr = kvalid ? krow : 0;
-    const int64_t orow = ((int64_t)(w.s0 + kr) * H + w.head) * HD;
-    if (kvalid) store_row(dv, 1.0f, hh, p.dv + orow);
-    if (p.wk) {
-      f32x16 dy[4];
-#pragma unroll
-      for (int d = 0; d < 4; d++)
-#pragma unroll
-        for (int i = 0; i < 16; i++) dy[d][i] = dk[d][i] * p.scale;
-      __syncthreads();  // every wave is done with the LDS tiles: they become the dw rows
-      norm_bwd_pair(dy, p.k + orow, p.wk, p.eps, hh, kvalid, p.dk + orow, (float*)lds, wv * 32 + l32);
-      dw_reduce((const float*)lds, tid, p.dwk_part + ((int64_t)w.item * H + w.head) * HD);
-    } else if (kvalid) {
-      store_row(dk, p.scale, hh, p.dk + orow);
+    // ---- epilogue: dv, dk^ = scale dK (fp32 for the norm backward, else the output itself)
+    if (kvalid) {
+      const int64_t orow = ((int64_t)(w.s0 + krow) * H + w.head) * HD;
+      store_row(dv, 1.0f, hh, p.dv + orow);
+      if (p.wk)
+        store_row_f32(dk, p.scale, hh, p.dkh + orow);
+      else
+        store_row(dk, p.scale, hh, p.dk + orow);
     }
   }
 }
 
-// ============================================================================== dw
+// ============================================================================== norm backward, dw
 
-// dw[d] = the sum of the per-(item, head) partials in a fixed tree whose shape depends only on the
-// number of work items: (1) per item, over heads ascending; (2) per chunk of DW_CHUNK consecutive
-// items, ascending; (3) over the chunks, ascending.  Every level keeps several independent loads
-// in flight per thread (the sums themselves stay sequential), so the chains are short.  Thread t of
-// a 256-thread block: t < 128 works on dwq, else on dwk, channel t % 128.
+// RMSNorm backward of every (token, head) row: with y = (x r) o w and the gradient dy with respect
+// to y (dq^ or dk^, fp32), dx = r g - (r^3 / 128) x (g . x) where g = w o dy, rounded once to bf16,
+// and the weight-gradient terms dy o x r.  16 lanes per row (8 channels each), 16 rows per
+// workgroup; r is the forward's FP64 value (the same fixed tree as the norm itself); g . x is
+// summed in FP64, per lane over its 8 channels in order and then across the lanes in a fixed
+// butterfly (partners add the same two values, so every lane holds the same bits).  The
+// workgroup's dw partial sums its 16 rows in row order.  blockIdx.y: 0 = q, 1 = k.
+struct NormBwdParams {
+  const uint16_t* x[2];  // raw q, k (token-major)
+  const uint16_t* w[2];
+  const float* dy[2];    // dq^, dk^
+  uint16_t* dx[2];       // dq, dk
+  float* part;           // [2][nparts][128]
+  const WsHeader* hdr;
+  int64_t rows;          // T * H
+  int64_t nparts;
+  float eps;
+};
+
+__global__ __launch_bounds__(256) void k_bwd_norm(NormBwdParams p) {
+  __shared__ float red[NR][HD];
+  const int which = blockIdx.y;
+  const int tid = threadIdx.x;
+  const int c = tid & 15;
+  const int64_t row = (int64_t)blockIdx.x * NR + (tid >> 4);
+  const bool valid = row < p.rows;
+  if (p.hdr->status != 0) return;  // the attention kernels have filled the outputs with NaN
+
+  float x[8], dy[8], wf[8];
+  {
+    u32x4 xv = {0, 0, 0, 0};
+    f32x4 d0 = {0.0f, 0.0f, 0.0f, 0.0f}, d1 = d0;
+    if (valid) {
+      xv = *(const u32x4*)(p.x[which] + row * HD + 8 * c);
+      d0 = *(const f32x4*)(p.dy[which] + row * HD + 8 * c);
+      d1 = *(const f32x4*)(p.dy[which] + row * HD + 8 * c + 4);
+    }
+    unpack8_bf16(xv, x);
+    unpack8_bf16(*(const u32x4*)(p.w[which] + 8 * c), wf);
+#pragma unroll
+    for (int i = 0; i < 4; i++) dy[i] = d0[i], dy[4 + i] = d1[i];
+  }
+  const double r = norm_rscale(row_total_16lanes(chunk_sumsq(x)), p.eps);
+  double gx = 0.0;
+#pragma unroll
+  for (int i = 0; i < 8; i++) gx = __builtin_fma((double)wf[i] * (double)dy[i], (double)x[i], gx);
+  gx = gx + __shfl_xor(gx, 1, 64);
+  gx = gx + __shfl_xor(gx, 2, 64);
+  gx = gx + __shfl_xor(gx, 4, 64);
+  gx = gx + __shfl_xor(gx, 8, 64);
+  const double k3 = r * r * r * 0.0078125 * gx;
+  u32x4 o;
+#pragma unroll
+  for (int i = 0; i < 4; i++) {
+    const uint32_t a = f64_to_bf16_rne(r * ((double)wf[2 * i] * (double)dy[2 * i]) - k3 * (double)x[2 * i]);
+    const uint32_t b =
+        f64_to_bf16_rne(r * ((double)wf[2 * i + 1] * (double)dy[2 * i + 1]) - k3 * (double)x[2 * i + 1]);
+    o[i] = a | (b << 16);
+  }
+  if (valid) *(u32x4*)(p.dx[which] + row * HD + 8 * c) = o;
+  f32x4 t0, t1;
+#pragma unroll
+  for (int i = 0; i < 4; i++) {
+    t0[i] = valid ? (float)((double)dy[i] * (double)x[i] * r) : 0.0f;
+    t1[i] = valid ? (float)((double)dy[4 + i] * (double)x[4 + i] * r) : 0.0f;
+  }
+  *(f32x4*)&red[tid >> 4][8 * c] = t0;
+  *(f32x4*)&red[tid >> 4][8 * c + 4] = t1;
+  __syncthreads();
+  if (tid < HD) {
+    float s = 0.0f;
+#pragma unroll
+    for (int rr = 0; rr < NR; rr++) s += red[rr][tid];
+    p.part[((int64_t)which * p.nparts + blockIdx.x) * HD + tid] = s;
+  }
+}
+
+// dw = the workgroup partials summed in a fixed tree whose shape depends only on their number:
+// chunks of DW_CHUNK consecutive partials in order, then the chunks in order.  Several independent
+// loads are kept in flight per thread (the sums themselves stay sequential).  blockIdx.y: 0 = q,
+// 1 = k; thread = channel.
 
 __device__ __forceinline__ float sum_strided(const float* base, int64_t n, int64_t stride) {
   float s = 0.0f;
@@ -516,44 +598,27 @@ __device__ __forceinline__ float sum_strided(const float* base, int64_t n, int64
   return s;
 }
 
-__device__ __forceinline__ int64_t dw_items(const WsHeader* hdr, int64_t max_items) {
-  return min((int64_t)max(hdr->nitems, 0), max_items);
-}
-
-// (1) item_part[item][q/k][d] = sum over heads of part[item][head][d]
-__global__ __launch_bounds__(256) void k_bwd_dw_items(const WsHeader* hdr, const float* qpart, const float* kpart,
-                                                      int64_t max_items, int32_t H, float* item_part) {
-  const int t = threadIdx.x, d = t & (HD - 1), which = t >> 7;
-  const float* part = which ? kpart : qpart;
-  const int64_t n = dw_items(hdr, max_items);
-  for (int64_t it = blockIdx.x; it < n; it += gridDim.x)
-    item_part[(it * 2 + which) * HD + d] = sum_strided(part + it * H * HD + d, H, HD);
-}
-
-// (2) chunk_part[c][q/k][d] = sum over items c*DW_CHUNK .. of item_part
-__global__ __launch_bounds__(256) void k_bwd_dw_chunks(const WsHeader* hdr, const float* item_part, int64_t max_items,
-                                                       float* chunk_part) {
-  const int t = threadIdx.x, d = t & (HD - 1), which = t >> 7;
-  const int64_t n = dw_items(hdr, max_items);
-  const int64_t nc = (n + DW_CHUNK - 1) / DW_CHUNK;
-  for (int64_t c = blockIdx.x; c < nc; c += gridDim.x) {
-    const int64_t i0 = c * DW_CHUNK, cnt = min((int64_t)DW_CHUNK, n - i0);
-    chunk_part[(c * 2 + which) * HD + d] = sum_strided(item_part + (i0 * 2 + which) * HD + d, cnt, 2 * HD);
+__global__ __launch_bounds__(HD) void k_bwd_dw_chunks(const WsHeader* hdr, const float* part, int64_t nparts,
+                                                      int64_t nchunks, float* chunk_part) {
+  const int d = threadIdx.x, which = blockIdx.y;
+  if (hdr->status != 0) return;
+  for (int64_t ch = blockIdx.x; ch < nchunks; ch += gridDim.x) {
+    const int64_t i0 = ch * DW_CHUNK, cnt = min((int64_t)DW_CHUNK, nparts - i0);
+    chunk_part[((int64_t)which * nchunks + ch) * HD + d] =
+        sum_strided(part + ((int64_t)which * nparts + i0) * HD + d, cnt, HD);
   }
 }
 
-// (3) dw = sum over chunks.  With a recorded data error the weights' gradients are NaN like the other
-// outputs.
-__global__ __launch_bounds__(256) void k_bwd_dw_final(const WsHeader* hdr, const float* chunk_part, int64_t max_items,
-                                                      float* dwq, float* dwk) {
+// With a recorded data error the weights' gradients are NaN like the other outputs.
+__global__ __launch_bounds__(2 * HD) void k_bwd_dw_final(const WsHeader* hdr, const float* chunk_part, int64_t nchunks,
+                                                         float* dwq, float* dwk) {
   const int t = threadIdx.x, d = t & (HD - 1), which = t >> 7;
   float* out = which ? dwk : dwq;
   if (hdr->status != 0) {
     out[d] = __builtin_nanf("");
     return;
   }
-  const int64_t nc = (dw_items(hdr, max_items) + DW_CHUNK - 1) / DW_CHUNK;
-  out[d] = sum_strided(chunk_part + which * HD + d, nc, 2 * HD);
+  out[d] = sum_strided(chunk_part + (int64_t)which * nchunks * HD + d, nchunks, HD);
 }
 
 hipError_t launch_bwd(const void* q, const void* k, const void* wq, const void* wk, int64_t T, int32_t H, float eps,
@@ -578,8 +643,8 @@ hipError_t launch_bwd(const void* q, const void* k, const void* wq, const void* 
   p.dq = (uint16_t*)dq;
   p.dk = (uint16_t*)dk;
   p.dv = (uint16_t*)dv;
-  p.dwq_part = (float*)(base + Lw.dwq);
-  p.dwk_part = (float*)(base + Lw.dwk);
+  p.dqh = (float*)(base + Lw.dqh);
+  p.dkh = (float*)(base + Lw.dkh);
   p.hdr = (const WsHeader*)base;
   p.segtab = (const int32_t*)(base + Lw.segtab);
   p.items = (const int32_t*)(base + Lw.items);
@@ -599,15 +664,27 @@ hipError_t launch_bwd(const void* q, const void* k, const void* wq, const void* 
   e = hipGetLastError();
   if (e != hipSuccess) return e;
   if (wq) {
-    const WsHeader* hdr = (const WsHeader*)base;
-    float* item_part = (float*)(base + Lw.dw_item);
+    NormBwdParams np;
+    np.x[0] = (const uint16_t*)q;
+    np.x[1] = (const uint16_t*)k;
+    np.w[0] = (const uint16_t*)wq;
+    np.w[1] = (const uint16_t*)wk;
+    np.dy[0] = p.dqh;
+    np.dy[1] = p.dkh;
+    np.dx[0] = (uint16_t*)dq;
+    np.dx[1] = (uint16_t*)dk;
+    np.part = (float*)(base + Lw.dw_part);
+    np.hdr = (const WsHeader*)base;
+    np.rows = T * H;
+    np.nparts = Lw.nparts;
+    np.eps = eps;
+    hipLaunchKernelGGL(k_bwd_norm, dim3((unsigned)Lw.nparts, 2), dim3(256), 0, stream, np);
     float* chunk_part = (float*)(base + Lw.dw_chunk);
-    const unsigned g1 = (unsigned)(Lw.max_items < 1024 ? Lw.max_items : 1024);
-    const unsigned g2 = (unsigned)(Lw.max_chunks < 256 ? Lw.max_chunks : 256);
-    hipLaunchKernelGGL(k_bwd_dw_items, dim3(g1), dim3(256), 0, stream, hdr, p.dwq_part, p.dwk_part, Lw.max_items, H,
-                       item_part);
-    hipLaunchKernelGGL(k_bwd_dw_chunks, dim3(g2), dim3(256), 0, stream, hdr, item_part, Lw.max_items, chunk_part);
-    hipLaunchKernelGGL(k_bwd_dw_final, dim3(1), dim3(256), 0, stream, hdr, chunk_part, Lw.max_items, dwq, dwk);
+    const unsigned g2 = (unsigned)(Lw.nchunks < 1024 ? Lw.nchunks : 1024);
+    hipLaunchKernelGGL(k_bwd_dw_chunks, dim3(g2, 2), dim3(HD), 0, stream, (const WsHeader*)base, np.part, Lw.nparts,
+                       Lw.nchunks, chunk_part);
+    hipLaunchKernelGGL(k_bwd_dw_final, dim3(1), dim3(2 * HD), 0, stream, (const WsHeader*)base, chunk_part,
+                       Lw.nchunks, dwq, dwk);
     e = hipGetLastError();
   }
   return e;
