@@ -61,7 +61,7 @@ constexpr int NR = 16;         // rows (token, head) per workgroup of the norm b
 constexpr int DW_CHUNK = 64;   // partials per chunk of the weight-gradient reduction
 
 struct BwdLayout {
-  size_t segtab, items, qhat, qhat16, khat, khat16, vh, doh, do16, lse2, delta, dqh, dkh, dw_part, dw_chunk, total;
+  size_t segtab, items, qhat16, khat16, v16, do16, lse2, delta, dqh, dkh, dw_part, dw_chunk, total;
   int64_t max_items, nparts, nchunks;
 };
 
@@ -75,13 +75,10 @@ __host__ __device__ inline BwdLayout bwd_layout(int64_t T, int32_t H) {
   w.nchunks = (w.nparts + DW_CHUNK - 1) / DW_CHUNK;
   w.segtab = 256;
   w.items = w.segtab + align256((size_t)T * 8);
-  w.qhat = w.items + align256((size_t)w.max_items * 8);
-  w.qhat16 = w.qhat + tens;
-  w.khat = w.qhat16 + tens;
-  w.khat16 = w.khat + tens;
-  w.vh = w.khat16 + tens;
-  w.doh = w.vh + tens;
-  w.do16 = w.doh + tens;
+  w.qhat16 = w.items + align256((size_t)w.max_items * 8);
+  w.khat16 = w.qhat16 + tens;
+  w.v16 = w.khat16 + tens;
+  w.do16 = w.v16 + tens;
   w.lse2 = w.do16 + tens;
   w.delta = w.lse2 + rowf;
   w.dqh = w.delta + rowf;

@@ -18,6 +18,13 @@ typedef float f32x2 __attribute__((ext_vector_type(2)));
 // Element offsets of a 16-bit value (row r, column d) inside a swizzled tile.
 __device__ __forceinline__ int k_off(int r, int d) { return r * HD + ((((d >> 3) ^ (r & 15))) << 3) + (d & 7); }
 __device__ __forceinline__ int v_off(int r, int d) { return r * HD + ((((d >> 3) ^ ((r & 3) << 2))) << 3) + (d & 7); }
+// One layout for tiles that are read both ways (by rows with 16-byte reads and transposed with
+// ds_read_b64_tr_b16): row r, chunk c at slot c ^ u_swz(r), u_swz(r) = 4 (r & 3) + ((r >> 2) & 3).
+// A half-wave of row reads (32 rows, one chunk) then touches 16 distinct slots per 16 rows, and a
+// transposed read (4 consecutive rows from a 4-aligned row, 4 consecutive chunks from a 4-aligned
+// chunk) touches 16 distinct slots: both are free of bank conflicts.
+__device__ __forceinline__ int u_swz(int r) { return ((r & 3) << 2) | ((r >> 2) & 3); }
+__device__ __forceinline__ int u_off(int r, int d) { return r * HD + (((d >> 3) ^ u_swz(r)) << 3) + (d & 7); }
 
 // Copy one 64-row tile of a head-major [rows][128] 16-bit array into a swizzled LDS tile with
 // buffer_load_dwordx4 ... lds.  The buffer resource covers only the tile's rows inside the segment
@@ -30,6 +37,12 @@ __device__ __forceinline__ int tile_lane_offset(bool is_v, int wv, int lane) {
   const int slot = lane & 15;
   const int c = is_v ? (slot ^ ((r & 3) << 2)) : (slot ^ (r & 15));
   return r * 256 + c * 16;  // bytes
+}
+
+// The same for the unified layout.
+__device__ __forceinline__ int tile_lane_offset_u(int wv, int lane) {
+  const int r = 4 * wv + (lane >> 4);
+  return r * 256 + ((lane & 15) ^ u_swz(r)) * 16;
 }
 
 template <int NW>
@@ -178,8 +191,8 @@ struct StepIdx {
   static constexpr int value = V;
 };
 
-// NP products of 16 steps each, product p over tile TILES[p] with B operands bop[p] into acc[p];
-// reads run 4 steps ahead across product boundaries.
+// NP products of 16 steps each, product p over tile TILES[p] (unified layout) with B operands bop[p]
+// into acc[p]; reads run 4 steps ahead across product boundaries.  vb: tr_bases_u.
 template <int T0, int T1>
 struct TilePair {
   static constexpr int tile(int p) { return p == 0 ? T0 : T1; }
@@ -190,7 +203,7 @@ __device__ __forceinline__ void trh_read(const uint32_t* vb, u32x2 (&va)[32][2])
   constexpr int ks = T >> 2, db = T & 3;
   constexpr int off = Tiles::tile(p) * TILE_ELEMS * 2 + 16 * ks * HD * 2;
   va[S][0] = tr_read_asm<off>(vb[db]);
-  va[S][1] = tr_read_asm<off + 8 * HD * 2>(vb[db]);
+  va[S][1] = tr_read_asm<off>(vb[4 + db]);
 }
 template <typename Tiles, int NP, int S, typename Hook>
 __device__ __forceinline__ void trh_step(const uint32_t* vb, const f16x8* const* bop, f32x16* const* acc,
@@ -220,7 +233,7 @@ __device__ __forceinline__ void tr_gemm_hooked(const uint32_t* vb, const f16x8* 
 }
 
 // Row-read products (the gemm_scores shape) with assembly reads: S[kb] = sum over m of tile rows
-// 32kb + l32's 16-dim slice m times the B operand b[m], reads NPRE steps ahead, explicit waits, and
+// 32kb + l32's 16-dim slice m times the B operand b[m] (bf16 or fp16, the tile holds the same type), reads NPRE steps ahead, explicit waits, and
 // hook(StepIdx<s>) after step s's MFMA (the hook must not issue LDS reads).  The lane's read address
 // for slice m is its slice-0 address XOR (m << 5) (K swizzle), so one base register serves every
 // slice; kbase[0] addresses tiles 0..3 and kbase[1] tiles 4..7 (the ds offset field is 16 bits).
@@ -244,25 +257,37 @@ __device__ __forceinline__ RowBases row_bases(const uint16_t* lds, int l32, int 
   b.hi = b.lo + 4 * TILE_ELEMS * 2;
   return b;
 }
+// The same for tiles in the unified layout (slice m's slot is again the slice-0 slot XOR 2m).
+__device__ __forceinline__ RowBases row_bases_u(const uint16_t* lds, int l32, int hh) {
+  RowBases b;
+  b.lo = (uint32_t)(size_t)(const __attribute__((address_space(3))) uint16_t*)(lds + u_off(l32, 8 * hh));
+  b.hi = b.lo + 4 * TILE_ELEMS * 2;
+  return b;
+}
 template <int TILE, int s>
 __device__ __forceinline__ u32x4 rows_read(const RowBases& rb) {
   constexpr int kb = s & 1, m = s >> 1;
   constexpr int off = (TILE & 3) * TILE_ELEMS * 2 + kb * 32 * HD * 2;
   return ds_read_b128_asm<off>((TILE >= 4 ? rb.hi : rb.lo) ^ (uint32_t)(m << 5));
 }
-template <int TILE, int NPRE, int s, typename Hook>
-__device__ __forceinline__ void rows_step(const RowBases& rb, const bf16x8* b, f32x16* S, u32x4 (&ka)[16],
-                                          Hook& hook) {
+__device__ __forceinline__ f32x16 mfma_rows(const u32x4& a, const bf16x8& b, const f32x16& c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a), b, c, 0, 0, 0);
+}
+__device__ __forceinline__ f32x16 mfma_rows(const u32x4& a, const f16x8& b, const f32x16& c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(f16x8, a), b, c, 0, 0, 0);
+}
+template <int TILE, int NPRE, int s, typename BT, typename Hook>
+__device__ __forceinline__ void rows_step(const RowBases& rb, const BT* b, f32x16* S, u32x4 (&ka)[16], Hook& hook) {
   if constexpr (s + NPRE < 16) ka[s + NPRE] = rows_read<TILE, s + NPRE>(rb);
   constexpr int ahead = (s + NPRE < 16 ? NPRE : 15 - s);
   lgkm_wait_tied4<ahead>(ka[s]);
-  S[s & 1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, ka[s]), b[s >> 1], S[s & 1], 0, 0, 0);
+  S[s & 1] = mfma_rows(ka[s], b[s >> 1], S[s & 1]);
   hook(StepIdx<s>{});
   __builtin_amdgcn_sched_barrier(0);
   if constexpr (s + 1 < 16) rows_step<TILE, NPRE, s + 1>(rb, b, S, ka, hook);
 }
-template <int TILE, int NPRE = 4, typename Hook>
-__device__ __forceinline__ void gemm_rows(const RowBases& rb, const bf16x8* b, f32x16* S, Hook hook) {
+template <int TILE, int NPRE = 4, typename BT, typename Hook>
+__device__ __forceinline__ void gemm_rows(const RowBases& rb, const BT* b, f32x16* S, Hook hook) {
   static_assert(TILE >= 0 && TILE <= 7 && NPRE >= 1 && NPRE <= 8, "tile and prefetch depth");
 #pragma unroll
   for (int kb = 0; kb < 2; kb++)
@@ -278,6 +303,21 @@ __device__ __forceinline__ void gemm_rows(const RowBases& rb, const bf16x8* b, f
   if constexpr (NPRE > 6) ka[6] = rows_read<TILE, 6>(rb);
   if constexpr (NPRE > 7) ka[7] = rows_read<TILE, 7>(rb);
   rows_step<TILE, NPRE, 0>(rb, b, S, ka, hook);
+}
+
+// The lane's eight transposed-read base addresses in tile 0 of the unified layout: vb[4u + db] for
+// the read of rows 8u + 4hh + ((lane & 15) >> 2) (+16ks: the swizzle repeats every 16 rows, so the
+// row slices are constant offsets), columns 32db + the lane's 4-column group.
+__device__ __forceinline__ void tr_bases_u(const uint16_t* lds, int lane, uint32_t* vb) {
+  const int hh = lane >> 5;
+  const int tr_row = 4 * hh + ((lane & 15) >> 2);
+  const int tr_col = 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
+#pragma unroll
+  for (int u = 0; u < 2; u++)
+#pragma unroll
+    for (int db = 0; db < 4; db++)
+      vb[4 * u + db] = (uint32_t)(size_t)(const __attribute__((address_space(3))) uint16_t*)(
+          lds + u_off(tr_row + 8 * u, 32 * db + tr_col));
 }
 
 // The lane's four tr_gemm base addresses (tile 0, row tr_row, column 32db + tr_col).

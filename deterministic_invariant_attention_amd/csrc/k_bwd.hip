@@ -39,12 +39,9 @@ struct BwdParams {
   const uint16_t* k;
   const uint16_t* wq;
   const uint16_t* wk;
-  const uint16_t* qhat;  // staged operands, head-major
-  const uint16_t* qhat16;
-  const uint16_t* khat;
+  const uint16_t* qhat16;  // staged operands, fp16, head-major
   const uint16_t* khat16;
-  const uint16_t* vh;
-  const uint16_t* doh;
+  const uint16_t* v16;
   const uint16_t* do16;
   const float* lse2;
   float* delta;
@@ -86,14 +83,14 @@ __device__ __forceinline__ bool next_item(const BwdParams& p, int round, int nit
 
 // The lane's 32-row block as a B operand of a 32x32x16 MFMA: row l32 of rows [row0, row0+32) of a
 // head-major [.][128] array, dims 16m + 8hh .. +8 in register m; rows at or past nvalid are zero.
-__device__ __forceinline__ void load_b_rows(const uint16_t* rows, int nvalid, int l32, int hh, bf16x8* out) {
+__device__ __forceinline__ void load_b_rows(const uint16_t* rows, int nvalid, int l32, int hh, f16x8* out) {
   const bool ok = l32 < nvalid;
   const uint16_t* r = rows + (int64_t)(ok ? l32 : 0) * HD;
 #pragma unroll
   for (int m = 0; m < 8; m++) {
     u32x4 w = {0, 0, 0, 0};
     if (ok) w = *(const u32x4*)(r + 16 * m + 8 * hh);
-    out[m] = __builtin_bit_cast(bf16x8, w);
+    out[m] = __builtin_bit_cast(f16x8, w);
   }
 }
 
@@ -152,8 +149,9 @@ struct Par2 {
 // ============================================================================== dq (and D)
 
 __global__ __launch_bounds__(64 * BW, 1) void k_bwd_dq(BwdParams p) {
-  // tiles 0, 1: K^16 (transposed reads) of stage 0 / 1; 2, 3: K^; 4, 5: V (row reads)
-  __shared__ __attribute__((aligned(1024))) uint16_t lds[6 * TILE_ELEMS];
+  // tiles 0, 1: K^16 of stage 0 / 1 (read by rows for S and transposed for dQ); 2, 3: V16 of
+  // stage 0 / 1; both in the unified layout
+  __shared__ __attribute__((aligned(1024))) uint16_t lds[4 * TILE_ELEMS];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -166,10 +164,10 @@ __global__ __launch_bounds__(64 * BW, 1) void k_bwd_dq(BwdParams p) {
   const int64_t max_items = T + (T + BT - 1) / BT;
   const int nseg = (int)min((int64_t)max(p.hdr->nseg, 0), T);
   const int nitems = (int)min((int64_t)max(p.hdr->nitems, 0), max_items);
-  const int krow_off = tile_lane_offset(false, wv, lane);
-  const int ktr_off = tile_lane_offset(true, wv, lane);
-  uint32_t vb[4];
-  tr_bases(lds, lane, vb);
+  const int uoff = tile_lane_offset_u(wv, lane);
+  uint32_t vb[8];
+  tr_bases_u(lds, lane, vb);
+  const RowBases rb = row_bases_u(lds, l32, hh);
   const float c = p.c;
 
   for (int round = 0;; round++) {
@@ -181,43 +179,46 @@ __global__ __launch_bounds__(64 * BW, 1) void k_bwd_dq(BwdParams p) {
     const int ntk = (w.L + TILE_ROWS - 1) / TILE_ROWS;
     const int rem = w.L - (ntk - 1) * TILE_ROWS;
     const int64_t hT = (int64_t)w.head * T;
-    const uint16_t* kb = p.khat + (hT + w.s0) * HD;
     const uint16_t* k16b = p.khat16 + (hT + w.s0) * HD;
-    const uint16_t* vbp = p.vh + (hT + w.s0) * HD;
+    const uint16_t* v16b = p.v16 + (hT + w.s0) * HD;
     const int row0 = w.tile * BT + wv * 32;  // the wave's first query (segment-relative)
     const int qrow = row0 + l32;
     const bool qvalid = qrow < w.L;
 
-    __syncthreads();  // the previous item's LDS reads are done
-    tile_to_lds<BW>(kb, w.L, lds + 2 * TILE_ELEMS, wv, krow_off);
-    tile_to_lds<BW>(vbp, w.L, lds + 4 * TILE_ELEMS, wv, krow_off);
+    // key tile j into stage ST (compile-time, so the compiler sees that a copy never writes the
+    // stage being read)
+    auto copies = [&](int j, auto stage) {
+      constexpr int ST = decltype(stage)::value;
+      const int64_t o = (int64_t)j * TILE_ELEMS;
+      const int v = w.L - j * TILE_ROWS;
+      tile_to_lds<BW>(k16b + o, v, lds + (0 + ST) * TILE_ELEMS, wv, uoff);
+      tile_to_lds<BW>(v16b + o, v, lds + (2 + ST) * TILE_ELEMS, wv, uoff);
+    };
 
-    bf16x8 qf[8], gf[8];
-    load_b_rows(p.qhat + (hT + w.s0 + row0) * HD, w.L - row0, l32, hh, qf);
-    load_b_rows(p.doh + (hT + w.s0 + row0) * HD, w.L - row0, l32, hh, gf);
+    __syncthreads();  // the previous item's LDS reads are done
+    copies(0, Par2<0>{});
+    f16x8 qf[8], gf[8];
+    load_b_rows(p.qhat16 + (hT + w.s0 + row0) * HD, w.L - row0, l32, hh, qf);
+    load_b_rows(p.do16 + (hT + w.s0 + row0) * HD, w.L - row0, l32, hh, gf);
     const float lq = qvalid ? p.lse2[hT + w.s0 + qrow] : 0.0f;
 
-    // scores and dP of tile j from stage ST; keys past the segment end get P = 0
-    auto scores = [&](auto st, int j, f32x16* S, f32x16* dP) {
-      constexpr int ST = decltype(st)::value;
-      gemm_scores<4>(lds + (2 + ST) * TILE_ELEMS, qf, l32, hh, S);
-      gemm_scores<4>(lds + (4 + ST) * TILE_ELEMS, gf, l32, hh, dP);
+    // S = K^ Q^T and dP = V dO^T of key tile j from stage ST (key 32kb + 8(i/4) + 4hh + (i%4), the
+    // lane's query); keys past the segment end get P = 0
+    auto scores = [&](auto stage, int j, f32x16* S, f32x16* dP) {
+      constexpr int ST = decltype(stage)::value;
+      gemm_rows<0 + ST>(rb, qf, S, [](auto) {});
+      gemm_rows<2 + ST>(rb, gf, dP, [](auto) {});
       if (j == ntk - 1 && rem < TILE_ROWS) mask_tail(S, rem, hh);
     };
 
     // ---- pass 1: D_i = sum_j P_ij dP_ij
     float dacc = 0.0f;
-    auto pass1 = [&](auto st, int j) {
-      constexpr int ST = decltype(st)::value;
+    auto pass1 = [&](auto stage, int j) {
+      constexpr int ST = decltype(stage)::value;
       copies_barrier();  // tile j has landed, every wave is done with stage 1 - ST
-      if (j + 1 < ntk) {
-        tile_to_lds<BW>(kb + (int64_t)(j + 1) * TILE_ELEMS, w.L - (j + 1) * TILE_ROWS, lds + (3 - ST) * TILE_ELEMS, wv,
-                        krow_off);
-        tile_to_lds<BW>(vbp + (int64_t)(j + 1) * TILE_ELEMS, w.L - (j + 1) * TILE_ROWS, lds + (5 - ST) * TILE_ELEMS,
-                        wv, krow_off);
-      }
+      if (j + 1 < ntk) copies(j + 1, Par2<1 - ST>{});
       f32x16 S[2], dP[2];
-      scores(st, j, S, dP);
+      scores(stage, j, S, dP);
       float pd[32];
 #pragma unroll
       for (int kbk = 0; kbk < 2; kbk++)
@@ -240,27 +241,19 @@ __global__ __launch_bounds__(64 * BW, 1) void k_bwd_dq(BwdParams p) {
     if (qvalid && hh == 0) p.delta[hT + w.s0 + qrow] = Dq;
 
     // ---- pass 2: dQ^T += K^16^T dS^T
-    __syncthreads();
-    tile_to_lds<BW>(k16b, w.L, lds, wv, ktr_off);
-    tile_to_lds<BW>(kb, w.L, lds + 2 * TILE_ELEMS, wv, krow_off);
-    tile_to_lds<BW>(vbp, w.L, lds + 4 * TILE_ELEMS, wv, krow_off);
+    __syncthreads();  // every wave is done with pass 1's tiles
+    copies(0, Par2<0>{});
     f32x16 acc[4];
 #pragma unroll
     for (int d = 0; d < 4; d++)
 #pragma unroll
       for (int i = 0; i < 16; i++) acc[d][i] = 0.0f;
-    auto pass2 = [&](auto st, int j) {
-      constexpr int ST = decltype(st)::value;
+    auto pass2 = [&](auto stage, int j) {
+      constexpr int ST = decltype(stage)::value;
       copies_barrier();  // tile j has landed, every wave is done with stage 1 - ST
-      if (j + 1 < ntk) {
-        const int64_t o = (int64_t)(j + 1) * TILE_ELEMS;
-        const int v = w.L - (j + 1) * TILE_ROWS;
-        tile_to_lds<BW>(k16b + o, v, lds + (1 - ST) * TILE_ELEMS, wv, ktr_off);
-        tile_to_lds<BW>(kb + o, v, lds + (3 - ST) * TILE_ELEMS, wv, krow_off);
-        tile_to_lds<BW>(vbp + o, v, lds + (5 - ST) * TILE_ELEMS, wv, krow_off);
-      }
+      if (j + 1 < ntk) copies(j + 1, Par2<1 - ST>{});
       f32x16 S[2], dP[2];
-      scores(st, j, S, dP);
+      scores(stage, j, S, dP);
       float ds[32];
 #pragma unroll
       for (int kbk = 0; kbk < 2; kbk++)
@@ -270,8 +263,9 @@ __global__ __launch_bounds__(64 * BW, 1) void k_bwd_dq(BwdParams p) {
       f16x8 dsf[4];
 #pragma unroll
       for (int ks = 0; ks < 4; ks++) dsf[ks] = pack_p(&ds[8 * ks]);
-      __builtin_amdgcn_sched_barrier(0);
-      tr_gemm<ST>(vb, dsf, acc);
+      const f16x8* bop[1] = {dsf};
+      f32x16* accp[1] = {acc};
+      tr_gemm_hooked<TilePair<ST, ST>, 1>(vb, bop, accp, [](auto) {});
     };
     {
       int j = 0;
@@ -296,12 +290,11 @@ __global__ __launch_bounds__(64 * BW, 1) void k_bwd_dq(BwdParams p) {
 // ============================================================================== dk, dv
 
 __global__ __launch_bounds__(64 * BW, 1) void k_bwd_dkdv(BwdParams p) {
-  // tiles 0, 1: Q^16 and 2, 3: dO16 (transposed reads) of transposed-read stage 0 / 1; 4, 5: Q^ and
-  // 6, 7: dO (row reads) of row stage 0 / 1; then the fp32 rows [row stage][lse2, D][64 queries].
-  // The row tiles (and their lse/D rows) run one query tile ahead of the transposed tiles.
-  __shared__ __attribute__((aligned(1024))) uint16_t lds[8 * TILE_ELEMS + 2 * 2 * TILE_ROWS * 2];
-  const float* lrow = (const float*)(lds + 8 * TILE_ELEMS);  // lrow[(2 * stage + which) * 64 + query]
-  lds_char* const lrow3 = (lds_char*)lds + 8 * TILE_ELEMS * 2;  // the same rows as an LDS address
+  // tiles 0, 1: Q^16 and 2, 3: dO16 of stage 0 / 1, in the unified layout (read by rows for S and
+  // dP, transposed for dK and dV); then the fp32 rows [stage][lse2, D][64 queries]
+  __shared__ __attribute__((aligned(1024))) uint16_t lds[4 * TILE_ELEMS + 2 * 2 * TILE_ROWS * 2];
+  const float* lrow = (const float*)(lds + 4 * TILE_ELEMS);  // lrow[(2 * stage + which) * 64 + query]
+  lds_char* const lrow3 = (lds_char*)lds + 4 * TILE_ELEMS * 2;  // the same rows as an LDS address
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -314,11 +307,10 @@ __global__ __launch_bounds__(64 * BW, 1) void k_bwd_dkdv(BwdParams p) {
   const int64_t max_items = T + (T + BT - 1) / BT;
   const int nseg = (int)min((int64_t)max(p.hdr->nseg, 0), T);
   const int nitems = (int)min((int64_t)max(p.hdr->nitems, 0), max_items);
-  const int row_off = tile_lane_offset(false, wv, lane);
-  const int tr_off = tile_lane_offset(true, wv, lane);
-  uint32_t vb[4];
-  tr_bases(lds, lane, vb);
-  const RowBases rb = row_bases(lds, l32, hh);
+  const int uoff = tile_lane_offset_u(wv, lane);
+  uint32_t vb[8];
+  tr_bases_u(lds, lane, vb);
+  const RowBases rb = row_bases_u(lds, l32, hh);
   const float c = p.c;
 
   for (int round = 0;; round++) {
@@ -329,9 +321,7 @@ __global__ __launch_bounds__(64 * BW, 1) void k_bwd_dkdv(BwdParams p) {
     if (!ok) continue;
     const int ntq = (w.L + TILE_ROWS - 1) / TILE_ROWS;
     const int64_t hT = (int64_t)w.head * T;
-    const uint16_t* qb = p.qhat + (hT + w.s0) * HD;
     const uint16_t* q16b = p.qhat16 + (hT + w.s0) * HD;
-    const uint16_t* gb = p.doh + (hT + w.s0) * HD;
     const uint16_t* g16b = p.do16 + (hT + w.s0) * HD;
     const float* lb = p.lse2 + hT + w.s0;
     const float* db = p.delta + hT + w.s0;
@@ -339,43 +329,23 @@ __global__ __launch_bounds__(64 * BW, 1) void k_bwd_dkdv(BwdParams p) {
     const int krow = row0 + l32;
     const bool kvalid = krow < w.L;
 
-    // Copies into a compile-time stage (so the compiler sees that a copy never writes the stage
-    // being read and adds no wait for it).
-    auto copy_rows = [&](int j, auto stage) {  // Q^, dO rows and the lse/D rows of query tile j
+    // query tile j into stage ST (compile-time: the compiler sees that a copy never writes the
+    // stage being read)
+    auto copies = [&](int j, auto stage) {
       constexpr int st = decltype(stage)::value;
       const int64_t o = (int64_t)j * TILE_ELEMS;
       const int v = w.L - j * TILE_ROWS;
-      tile_to_lds<BW>(qb + o, v, lds + (4 + st) * TILE_ELEMS, wv, row_off);
-      tile_to_lds<BW>(gb + o, v, lds + (6 + st) * TILE_ELEMS, wv, row_off);
+      tile_to_lds<BW>(q16b + o, v, lds + (0 + st) * TILE_ELEMS, wv, uoff);
+      tile_to_lds<BW>(g16b + o, v, lds + (2 + st) * TILE_ELEMS, wv, uoff);
       if (wv == 0) rowvec_to_lds(lb + j * TILE_ROWS, v, lrow3 + (2 * st + 0) * TILE_ROWS * 4, lane);
       if (wv == 1) rowvec_to_lds(db + j * TILE_ROWS, v, lrow3 + (2 * st + 1) * TILE_ROWS * 4, lane);
     };
-    auto copy_tr = [&](int j, auto stage) {  // Q^16, dO16 of query tile j
-      constexpr int st = decltype(stage)::value;
-      const int64_t o = (int64_t)j * TILE_ELEMS;
-      const int v = w.L - j * TILE_ROWS;
-      tile_to_lds<BW>(q16b + o, v, lds + (0 + st) * TILE_ELEMS, wv, tr_off);
-      tile_to_lds<BW>(g16b + o, v, lds + (2 + st) * TILE_ELEMS, wv, tr_off);
-    };
-    // lse2 / D of the queries a lane's score elements belong to (query 32qb + 8g + 4hh + e of the
-    // tile), from row stage ST
-    auto load_ld = [&](auto stage, f32x4 (&l4)[2][4], f32x4 (&d4)[2][4]) {
-      constexpr int ST = decltype(stage)::value;
-#pragma unroll
-      for (int q2 = 0; q2 < 2; q2++)
-#pragma unroll
-        for (int g = 0; g < 4; g++) {
-          l4[q2][g] = *(const f32x4*)&lrow[(2 * ST + 0) * TILE_ROWS + 32 * q2 + 8 * g + 4 * hh];
-          d4[q2][g] = *(const f32x4*)&lrow[(2 * ST + 1) * TILE_ROWS + 32 * q2 + 8 * g + 4 * hh];
-        }
-    };
 
     __syncthreads();  // the previous item's LDS reads are done
-    copy_rows(0, Par2<0>{});
-    copy_tr(0, Par2<0>{});
-    bf16x8 kf[8], vf[8];
-    load_b_rows(p.khat + (hT + w.s0 + row0) * HD, w.L - row0, l32, hh, kf);
-    load_b_rows(p.vh + (hT + w.s0 + row0) * HD, w.L - row0, l32, hh, vf);
+    copies(0, Par2<0>{});
+    f16x8 kf[8], vf[8];
+    load_b_rows(p.khat16 + (hT + w.s0 + row0) * HD, w.L - row0, l32, hh, kf);
+    load_b_rows(p.v16 + (hT + w.s0 + row0) * HD, w.L - row0, l32, hh, vf);
 
     f32x16 dv[4], dk[4];
 #pragma unroll
@@ -383,109 +353,55 @@ __global__ __launch_bounds__(64 * BW, 1) void k_bwd_dkdv(BwdParams p) {
 #pragma unroll
       for (int i = 0; i < 16; i++) dv[d][i] = dk[d][i] = 0.0f;
 
-    // Query tile 0: S = Q^ K^T and dP = dO V^T (query 32qb + 8(i/4) + 4hh + (i%4), the lane's key),
-    // then P = exp2(S c - lse2) and dS = P (dP - D), packed to fp16 for the products.
-    f16x8 pf[4], dsf[4];
-    copies_barrier();  // tile 0 has landed everywhere
-    if (1 < ntq) copy_rows(1, Par2<1>{});
-    {
+    // Query tile j from stage ST: S = Q^ K^T and dP = dO V^T (query 32qb + 8(i/4) + 4hh + (i%4),
+    // the lane's key), P = exp2(S c - lse2) and dS = P (dP - D) in fp16, then dV^T += dO16^T P and
+    // dK^T += Q^16^T dS (one pipeline of 32 transposed-read MFMAs).
+    auto step = [&](auto stage, int j) {
+      constexpr int ST = decltype(stage)::value;
+      copies_barrier();  // tile j has landed, every wave is done with stage 1 - ST
+      if (j + 1 < ntq) copies(j + 1, Par2<1 - ST>{});
       f32x16 S[2], dP[2];
       f32x4 l4[2][4], d4[2][4];
-      load_ld(Par2<0>{}, l4, d4);
-      gemm_rows<4>(rb, kf, S, [](auto) {});
+#pragma unroll
+      for (int q2 = 0; q2 < 2; q2++)
+#pragma unroll
+        for (int g = 0; g < 4; g++) {
+          l4[q2][g] = *(const f32x4*)&lrow[(2 * ST + 0) * TILE_ROWS + 32 * q2 + 8 * g + 4 * hh];
+          d4[q2][g] = *(const f32x4*)&lrow[(2 * ST + 1) * TILE_ROWS + 32 * q2 + 8 * g + 4 * hh];
+        }
+      gemm_rows<0 + ST>(rb, kf, S, [](auto) {});
+      // the lse/D reads complete here, before the next pipelines count their own reads
 #pragma unroll
       for (int q2 = 0; q2 < 2; q2++)
 #pragma unroll
         for (int g = 0; g < 4; g++) asm volatile("" : "+v"(l4[q2][g]), "+v"(d4[q2][g]));
+      gemm_rows<2 + ST>(rb, vf, dP, [](auto) {});
       float pr[2][16], ds[2][16];
-      gemm_rows<6>(rb, vf, dP, [&](auto step) {
-        constexpr int st = decltype(step)::value;
 #pragma unroll
-        for (int u = 0; u < 2; u++) {
-          constexpr int q2 = st >> 3;
-          const int i = 2 * (st & 7) + u;
-          pr[q2][i] = __builtin_amdgcn_exp2f(__builtin_fmaf(S[q2][i], c, -l4[q2][i >> 2][i & 3]));
+      for (int q2 = 0; q2 < 2; q2++)
+#pragma unroll
+        for (int i = 0; i < 16; i++) {
+          const float pv = __builtin_amdgcn_exp2f(__builtin_fmaf(S[q2][i], c, -l4[q2][i >> 2][i & 3]));
+          pr[q2][i] = pv;
+          ds[q2][i] = pv * (dP[q2][i] - d4[q2][i >> 2][i & 3]);
         }
-        if constexpr ((st & 3) == 3) {
-          constexpr int ks = st >> 2;
-          pf[ks] = pack_p(&pr[ks >> 1][8 * (ks & 1)]);
-        }
-      });
+      f16x8 pf[4], dsf[4];
 #pragma unroll
       for (int ks = 0; ks < 4; ks++) {
-#pragma unroll
-        for (int u = 0; u < 8; u++) {
-          const int q2 = ks >> 1, i = 8 * (ks & 1) + u;
-          ds[q2][i] = pr[q2][i] * (dP[q2][i] - d4[q2][i >> 2][i & 3]);
-        }
+        pf[ks] = pack_p(&pr[ks >> 1][8 * (ks & 1)]);
         dsf[ks] = pack_p(&ds[ks >> 1][8 * (ks & 1)]);
       }
-    }
-
-    // Iteration j: dV^T += dO16^T P and dK^T += Q^16^T dS over query tile j (one pipeline of 32
-    // transposed-read MFMAs), with the scores of tile j+1 computed first and its P / dS evaluated
-    // between those MFMAs.
-    auto iter = [&](auto par, int j) {
-      constexpr int P = decltype(par)::value;  // j & 1: tile j's transposed stage, tile j+1's row stage is 1 - P
-      copies_barrier();  // rows of tile j+1 and the transposed tiles of tile j have landed
-      if (j + 2 < ntq) copy_rows(j + 2, Par2<P>{});
-      if (j + 1 < ntq) copy_tr(j + 1, Par2<1 - P>{});
       const f16x8* bop[2] = {pf, dsf};
       f32x16* acc[2] = {dv, dk};
-      if (j + 1 < ntq) {
-        f32x16 S[2], dP[2];
-        f32x4 l4[2][4], d4[2][4];
-        load_ld(Par2<1 - P>{}, l4, d4);
-        gemm_rows<4 + 1 - P>(rb, kf, S, [](auto) {});
-        // the lse/D reads complete here, before the next pipelines count their own reads
-#pragma unroll
-        for (int q2 = 0; q2 < 2; q2++)
-#pragma unroll
-          for (int g = 0; g < 4; g++) asm volatile("" : "+v"(l4[q2][g]), "+v"(d4[q2][g]));
-        // dP = dO V^T, with P = exp2(S c - lse2) formed (and packed) between its MFMAs
-        float pr[2][16];
-        f16x8 pf2[4], dsf2[4];
-        gemm_rows<6 + 1 - P>(rb, vf, dP, [&](auto step) {
-          constexpr int st = decltype(step)::value;
-#pragma unroll
-          for (int u = 0; u < 2; u++) {
-            constexpr int q2 = st >> 3;
-            const int i = 2 * (st & 7) + u;
-            pr[q2][i] = __builtin_amdgcn_exp2f(__builtin_fmaf(S[q2][i], c, -l4[q2][i >> 2][i & 3]));
-          }
-          if constexpr ((st & 3) == 3) {
-            constexpr int ks = st >> 2;
-            pf2[ks] = pack_p(&pr[ks >> 1][8 * (ks & 1)]);
-          }
-        });
-        // dV^T += dO16^T P and dK^T += Q^16^T dS over tile j, with dS = P (dP - D) of tile j+1
-        // formed (and packed) between those MFMAs
-        float ds[2][16];
-        tr_gemm_hooked<TilePair<2 + P, 0 + P>, 2>(vb, bop, acc, [&](auto step) {
-          constexpr int t = decltype(step)::value;
-          constexpr int q2 = t >> 4, i = t & 15;
-          ds[q2][i] = pr[q2][i] * (dP[q2][i] - d4[q2][i >> 2][i & 3]);
-          if constexpr ((i & 7) == 7) {
-            constexpr int ks = 2 * q2 + (i >> 3);
-            dsf2[ks] = pack_p(&ds[q2][8 * (i >> 3)]);
-          }
-        });
-#pragma unroll
-        for (int ks = 0; ks < 4; ks++) {
-          pf[ks] = pf2[ks];
-          dsf[ks] = dsf2[ks];
-        }
-      } else {
-        tr_gemm_hooked<TilePair<2 + P, 0 + P>, 2>(vb, bop, acc, [](auto) {});
-      }
+      tr_gemm_hooked<TilePair<2 + ST, 0 + ST>, 2>(vb, bop, acc, [](auto) {});
     };
     {
       int j = 0;
       for (; j + 1 < ntq; j += 2) {
-        iter(Par2<0>{}, j);
-        iter(Par2<1>{}, j + 1);
+        step(Par2<0>{}, j);
+        step(Par2<1>{}, j + 1);
       }
-      if (j < ntq) iter(Par2<0>{}, j);
+      if (j < ntq) step(Par2<0>{}, j);
     }
 
     // ---- epilogue: dv, dk^ = scale dK (fp32 for the norm backward, else the output itself)
@@ -631,12 +547,9 @@ hipError_t launch_bwd(const void* q, const void* k, const void* wq, const void* 
   p.k = (const uint16_t*)k;
   p.wq = (const uint16_t*)wq;
   p.wk = (const uint16_t*)wk;
-  p.qhat = (const uint16_t*)(base + Lw.qhat);
   p.qhat16 = (const uint16_t*)(base + Lw.qhat16);
-  p.khat = (const uint16_t*)(base + Lw.khat);
   p.khat16 = (const uint16_t*)(base + Lw.khat16);
-  p.vh = (const uint16_t*)(base + Lw.vh);
-  p.doh = (const uint16_t*)(base + Lw.doh);
+  p.v16 = (const uint16_t*)(base + Lw.v16);
   p.do16 = (const uint16_t*)(base + Lw.do16);
   p.lse2 = (const float*)(base + Lw.lse2);
   p.delta = (float*)(base + Lw.delta);

@@ -88,12 +88,9 @@ struct BwdPrepParams {
   const float* lse;
   const uint16_t* wq;
   const uint16_t* wk;
-  uint16_t* qhat;
   uint16_t* qhat16;
-  uint16_t* khat;
   uint16_t* khat16;
-  uint16_t* vh;
-  uint16_t* doh;
+  uint16_t* v16;
   uint16_t* do16;
   float* lse2;
   WsHeader* hdr;
@@ -102,8 +99,9 @@ struct BwdPrepParams {
   float eps;
 };
 
-// bf16 chunk -> fp16 chunk (exact for magnitudes in fp16's normal range); over |= a finite value
-// beyond 65504.
+// bf16 chunk -> fp16 chunk: exact for every bf16 value from 2^-17 up to 65504 in magnitude (and
+// zero); below 2^-17 fp16 subnormals round it, by at most 2^-25.  over |= a finite value beyond
+// 65504.
 __device__ __forceinline__ u32x4 bf16_chunk_to_f16(const u32x4& x, bool& over) {
   u32x4 o;
 #pragma unroll
@@ -116,6 +114,9 @@ __device__ __forceinline__ u32x4 bf16_chunk_to_f16(const u32x4& x, bool& over) {
   return o;
 }
 
+// The backward's operands, head-major, in fp16 (every product of the backward runs on fp16 MFMA
+// with FP32 accumulation): the normed q and k (rounded to bf16 exactly as in the forward, then
+// converted), v and dO; and the LSE in log2 units.
 __global__ __launch_bounds__(256) void k_bwd_prep(BwdPrepParams p) {
   const int64_t g = (int64_t)blockIdx.x * 256 + threadIdx.x;
   const int64_t row = g >> 4;
@@ -138,14 +139,12 @@ __global__ __launch_bounds__(256) void k_bwd_prep(BwdPrepParams p) {
   bool over = false;
   const u32x4 q16 = bf16_chunk_to_f16(qo, over);
   const u32x4 k16 = bf16_chunk_to_f16(ko, over);
+  const u32x4 v16 = bf16_chunk_to_f16(vv, over);
   const u32x4 g16 = bf16_chunk_to_f16(gv, over);
   if (valid) {
-    st16(p.qhat + dst, qo);
     st16(p.qhat16 + dst, q16);
-    st16(p.khat + dst, ko);
     st16(p.khat16 + dst, k16);
-    st16(p.vh + dst, vv);
-    st16(p.doh + dst, gv);
+    st16(p.v16 + dst, v16);
     st16(p.do16 + dst, g16);
     if (c == 0) p.lse2[h * p.T + t] = p.lse[t * p.H + h] * 1.44269504088896340736f;
   }
@@ -170,12 +169,9 @@ hipError_t launch_bwd_prep(const void* q, const void* k, const void* v, const vo
   p.lse = lse;
   p.wq = (const uint16_t*)wq;
   p.wk = (const uint16_t*)wk;
-  p.qhat = (uint16_t*)(base + L.qhat);
   p.qhat16 = (uint16_t*)(base + L.qhat16);
-  p.khat = (uint16_t*)(base + L.khat);
   p.khat16 = (uint16_t*)(base + L.khat16);
-  p.vh = (uint16_t*)(base + L.vh);
-  p.doh = (uint16_t*)(base + L.doh);
+  p.v16 = (uint16_t*)(base + L.v16);
   p.do16 = (uint16_t*)(base + L.do16);
   p.lse2 = (float*)(base + L.lse2);
   p.hdr = (WsHeader*)base;

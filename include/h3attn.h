@@ -109,9 +109,10 @@ int h3attn_attend(const void* q, const void* wq, int64_t tokens, int32_t heads, 
                   float scale, void* out, float* lse, void* workspace, size_t workspace_bytes, void* stream);
 
 /* Bytes of device workspace that h3attn_bwd needs for `tokens` x `heads`: the header, the segment
- * table and work list (128-token tiles), seven head-major staged operands (normed q and k in bf16
- * and fp16, v, dO in bf16 and fp16: 7 * tokens * heads * 256 bytes), the log-sum-exp and D rows
- * (2 * tokens * heads * 4 bytes) and the per-item norm-weight gradient partials.  0 if invalid. */
+ * table and work list (128-token tiles), four head-major fp16 staged operands (normed q and k, v,
+ * dO: 4 * tokens * heads * 256 bytes), the log-sum-exp and D rows (2 * tokens * heads * 4 bytes),
+ * the fp32 gradients with respect to the normed q and k (2 * tokens * heads * 512 bytes) and the
+ * norm-weight gradient partials.  0 if invalid. */
 size_t h3attn_bwd_workspace_bytes(int64_t tokens, int32_t heads);
 
 /* Backward of the node: gradients of sum(dout * out) with respect to q, k, v and the two norm
@@ -125,8 +126,10 @@ size_t h3attn_bwd_workspace_bytes(int64_t tokens, int32_t heads);
  *     token and head of dy * x * r, added in a fixed order (bitwise repeatable).
  * Determinism: no atomics on data; every gradient row of q, k and v is a function of its own
  * segment's bytes only (the same bits alone or batched); dwq/dwk are sums over the whole batch.
- * P and dS enter their products in fp16 (as P does in the forward); a finite normed q/k or dO value
- * beyond 65504 sets H3ATTN_ERR_RANGE in the status word and NaN-fills the outputs.
+ * Every product runs on fp16 MFMA with FP32 accumulation: P and dS are rounded to fp16 (as P is in
+ * the forward), and the normed q, k and v, dO are converted to fp16, which is exact for magnitudes
+ * from 2^-17 to 65504 (below 2^-17 the error is at most 2^-25); a finite value beyond 65504 in any of
+ * them sets H3ATTN_ERR_RANGE in the status word and NaN-fills the outputs.
  * Outputs must not overlap any input, the workspace or each other. */
 int h3attn_bwd(const void* dout, const void* q, const void* k, const void* v, const float* lse,
                const int32_t* seg_ids, const void* wq, const void* wk, int64_t tokens, int32_t heads,
