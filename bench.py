@@ -99,17 +99,7 @@ def main():
     log(f"workload {wl.name}: {wl.description}; nominal {flops:.4e} FLOP/step")
 
     if args.copy_calibration:
-        # A plain elementwise kernel of known traffic (256 MiB read, 256 MiB written), the reference
-        # that scales the FETCH_SIZE / WRITE_SIZE counters of a --pmc run into bytes.  Its grid
-        # (64 Mi elements) tells it apart from every other dispatch of the run.
-        src = torch.full((64 << 20,), 1.0, dtype=torch.float32, device=dev)
-        dst = torch.empty_like(src)
-        scrub = torch.full((128 << 20,), 0.0, dtype=torch.float32, device=dev)  # 512 MiB: evicts the 256 MB MALL
-        torch.cuda.synchronize()
-        torch.mul(src, 2.0, out=dst)
-        torch.cuda.synchronize()
-        log("copy calibration: torch.mul over 67108864 fp32 (268435456 bytes read + 268435456 bytes written)")
-        del src, dst, scrub
+        copy_calibration(dev)
 
     def step():
         h3.h3attn_fwd(g["q"], g["k"], g["v"], g["seg"], g["wq"], g["wk"], eps=wl.eps, scale=wl.scale, out=out,
@@ -210,6 +200,21 @@ def main():
     print(json.dumps(line), flush=True)
 
 
+def copy_calibration(dev):
+    """A plain elementwise kernel of known traffic (256 MiB read, 256 MiB written), the reference
+    that scales the FETCH_SIZE / WRITE_SIZE counters of a --pmc run into bytes.  Its grid (64 Mi
+    elements) tells it apart from every other dispatch of the run."""
+    import torch
+    src = torch.full((64 << 20,), 1.0, dtype=torch.float32, device=dev)
+    dst = torch.empty_like(src)
+    scrub = torch.full((128 << 20,), 0.0, dtype=torch.float32, device=dev)  # 512 MiB: evicts the 256 MB MALL
+    torch.cuda.synchronize()
+    torch.mul(src, 2.0, out=dst)
+    torch.cuda.synchronize()
+    log("copy calibration: torch.mul over 67108864 fp32 (268435456 bytes read + 268435456 bytes written)")
+    del src, dst, scrub
+
+
 def bench_bwd(args, wl):
     import numpy as np
     import torch
@@ -224,6 +229,8 @@ def bench_bwd(args, wl):
     flops = 2.5 * wl.flops()
     stream = torch.cuda.current_stream(dev)
     log(f"workload {wl.name} backward: {wl.description}; nominal {flops:.4e} FLOP/step (2.5 x forward)")
+    if args.copy_calibration:
+        copy_calibration(dev)
     _, lse = h3.h3attn_fwd(g["q"], g["k"], g["v"], g["seg"], g["wq"], g["wk"], eps=wl.eps, scale=wl.scale,
                            want_lse=True, stream=stream)
     ws = h3.bwd_workspace(T, H, dev)
