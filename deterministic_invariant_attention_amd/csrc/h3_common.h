@@ -22,7 +22,9 @@ struct WsHeader {
   int32_t status;  // OR of STATUS_* bits; reset by the plan kernel
   int32_t nseg;
   int32_t nitems;
-  int32_t pad[61];
+  int32_t nbkt;     // backward plan: cost classes in the work order
+  int32_t next[2];  // backward: work counters of the dq and the dk/dv kernel, reset by the plan kernel
+  int32_t pad[58];
 };
 static_assert(sizeof(WsHeader) == 256, "header is 256 bytes");
 
@@ -60,8 +62,10 @@ constexpr int BT = 128;        // queries (dq kernel) or keys (dk/dv kernel) per
 constexpr int NR = 16;         // rows (token, head) per workgroup of the norm backward
 constexpr int DW_CHUNK = 64;   // partials per chunk of the weight-gradient reduction
 
+constexpr int NBKT = 32;  // cost classes of the backward work order (floor(log2(64-row tiles)))
+
 struct BwdLayout {
-  size_t segtab, items, qhat16, khat16, v16, do16, lse2, delta, dqh, dkh, dw_part, dw_chunk, total;
+  size_t segtab, items, bkt, qhat16, khat16, v16, do16, lse2, delta, dqh, dkh, dw_part, dw_chunk, total;
   int64_t max_items, nparts, nchunks;
 };
 
@@ -75,7 +79,8 @@ __host__ __device__ inline BwdLayout bwd_layout(int64_t T, int32_t H) {
   w.nchunks = (w.nparts + DW_CHUNK - 1) / DW_CHUNK;
   w.segtab = 256;
   w.items = w.segtab + align256((size_t)T * 8);
-  w.qhat16 = w.items + align256((size_t)w.max_items * 8);
+  w.bkt = w.items + align256((size_t)w.max_items * 8);
+  w.qhat16 = w.bkt + align256((size_t)NBKT * 2 * 4);
   w.khat16 = w.qhat16 + tens;
   w.v16 = w.khat16 + tens;
   w.do16 = w.v16 + tens;

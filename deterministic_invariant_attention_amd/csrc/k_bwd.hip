@@ -51,34 +51,62 @@ struct BwdParams {
   float* dqh;  // with norm weights: gradients with respect to the normed q / k, fp32 token-major
   float* dkh;
   const WsHeader* hdr;
+  int32_t* next;  // the kernel's work counter (in the header)
   const int32_t* segtab;
   const int32_t* items;
+  const int32_t* bkt;  // cost classes of the work order: (first item, item count), most expensive first
   int64_t T;
   int32_t H;
   float eps;
   float c;      // scale * log2(e)
   float scale;
-  int32_t xcd_slots;
 };
 
-// One work item of the persistent walk (XCD-aware head-major order, as in the forward).
+// One work item of the persistent walk.  Items are handed out by an atomic counter (the order only
+// decides which workgroup runs an item, never a result); the work index v runs over the cost
+// classes of the plan in order (most expensive first) and, inside a class, head-major, so
+// consecutive items share a head's operands and the cheap ones come last.
 struct WorkItem {
   int head, item, s0, L, tile;
 };
 
-__device__ __forceinline__ bool next_item(const BwdParams& p, int round, int nitems, int nseg, WorkItem& w, bool& done) {
-  const int xcd = blockIdx.x & 7, slot = blockIdx.x >> 3;
-  const int64_t v = ((int64_t)round * 8 + xcd) * p.xcd_slots + slot;
+__device__ __forceinline__ bool item_of(const BwdParams& p, int64_t v, int nitems, int nseg, int nbkt, WorkItem& w,
+                                        bool& done) {
   done = v >= (int64_t)nitems * p.H;
   if (done) return false;
-  w.head = (int)(v / nitems);
-  w.item = (int)(v - (int64_t)w.head * nitems);
+  int64_t base = 0;
+  int b = 0, start = 0, cnt = 0;
+  for (; b < nbkt; b++) {
+    start = p.bkt[2 * b];
+    cnt = p.bkt[2 * b + 1];
+    const int64_t span = (int64_t)cnt * p.H;
+    if (v < base + span) break;
+    base += span;
+  }
+  if (b == nbkt || cnt <= 0) return false;
+  const int64_t local = v - base;
+  w.head = (int)(local / cnt);
+  w.item = start + (int)(local - (int64_t)w.head * cnt);
+  if ((unsigned)w.item >= (unsigned)nitems || (unsigned)w.head >= (unsigned)p.H) return false;
   const int seg = p.items[2 * w.item];
   w.tile = p.items[2 * w.item + 1];
   if ((unsigned)seg >= (unsigned)nseg) return false;
   w.s0 = p.segtab[2 * seg];
   w.L = p.segtab[2 * seg + 1];
   return !(w.s0 < 0 || w.L <= 0 || (int64_t)w.s0 + w.L > p.T || w.tile < 0 || w.tile * BT >= w.L);
+}
+
+// The next work index for the workgroup: thread 0 hands out the index it fetched during the previous
+// item and fetches the following one, so the atomic's latency is hidden.  The first barrier also
+// ends the previous item's LDS reads.
+__device__ __forceinline__ int64_t take_work(const BwdParams& p, int tid, int32_t& prefetched, int32_t* s_next) {
+  __syncthreads();
+  if (tid == 0) {
+    *s_next = prefetched;
+    prefetched = atomicAdd(p.next, 1);
+  }
+  __syncthreads();
+  return *s_next;
 }
 
 // The lane's 32-row block as a B operand of a 32x32x16 MFMA: row l32 of rows [row0, row0+32) of a
@@ -170,10 +198,14 @@ __global__ __launch_bounds__(64 * BW, 1) void k_bwd_dq(BwdParams p) {
   const RowBases rb = row_bases_u(lds, l32, hh);
   const float c = p.c;
 
-  for (int round = 0;; round++) {
+  const int nbkt = min(max(p.hdr->nbkt, 0), NBKT);
+  __shared__ int32_t s_next;
+  int32_t prefetched = tid == 0 ? atomicAdd(p.next, 1) : 0;
+  for (;;) {
     WorkItem w;
     bool done;
-    const bool ok = next_item(p, round, nitems, nseg, w, done);
+    const int64_t v = take_work(p, tid, prefetched, &s_next);
+    const bool ok = item_of(p, v, nitems, nseg, nbkt, w, done);
     if (done) break;
     if (!ok) continue;
     const int ntk = (w.L + TILE_ROWS - 1) / TILE_ROWS;
@@ -195,7 +227,6 @@ __global__ __launch_bounds__(64 * BW, 1) void k_bwd_dq(BwdParams p) {
       tile_to_lds<BW>(v16b + o, v, lds + (2 + ST) * TILE_ELEMS, wv, uoff);
     };
 
-    __syncthreads();  // the previous item's LDS reads are done
     copies(0, Par2<0>{});
     f16x8 qf[8], gf[8];
     load_b_rows(p.qhat16 + (hT + w.s0 + row0) * HD, w.L - row0, l32, hh, qf);
@@ -313,10 +344,14 @@ __global__ __launch_bounds__(64 * BW, 1) void k_bwd_dkdv(BwdParams p) {
   const RowBases rb = row_bases_u(lds, l32, hh);
   const float c = p.c;
 
-  for (int round = 0;; round++) {
+  const int nbkt = min(max(p.hdr->nbkt, 0), NBKT);
+  __shared__ int32_t s_next;
+  int32_t prefetched = tid == 0 ? atomicAdd(p.next, 1) : 0;
+  for (;;) {
     WorkItem w;
     bool done;
-    const bool ok = next_item(p, round, nitems, nseg, w, done);
+    const int64_t v = take_work(p, tid, prefetched, &s_next);
+    const bool ok = item_of(p, v, nitems, nseg, nbkt, w, done);
     if (done) break;
     if (!ok) continue;
     const int ntq = (w.L + TILE_ROWS - 1) / TILE_ROWS;
@@ -341,7 +376,6 @@ __global__ __launch_bounds__(64 * BW, 1) void k_bwd_dkdv(BwdParams p) {
       if (wv == 1) rowvec_to_lds(db + j * TILE_ROWS, v, lrow3 + (2 * st + 1) * TILE_ROWS * 4, lane);
     };
 
-    __syncthreads();  // the previous item's LDS reads are done
     copies(0, Par2<0>{});
     f16x8 kf[8], vf[8];
     load_b_rows(p.khat16 + (hT + w.s0 + row0) * HD, w.L - row0, l32, hh, kf);
@@ -561,6 +595,7 @@ hipError_t launch_bwd(const void* q, const void* k, const void* wq, const void* 
   p.hdr = (const WsHeader*)base;
   p.segtab = (const int32_t*)(base + Lw.segtab);
   p.items = (const int32_t*)(base + Lw.items);
+  p.bkt = (const int32_t*)(base + Lw.bkt);
   p.T = T;
   p.H = H;
   p.eps = eps;
@@ -569,10 +604,11 @@ hipError_t launch_bwd(const void* q, const void* k, const void* wq, const void* 
   const int64_t max_work = Lw.max_items * H;
   int64_t grid = grid_cap < max_work ? grid_cap : max_work;
   grid = (grid + 7) & ~(int64_t)7;
-  p.xcd_slots = (int32_t)(grid / 8);
+  p.next = &((WsHeader*)base)->next[0];
   hipLaunchKernelGGL(k_bwd_dq, dim3((unsigned)grid), dim3(64 * BW), 0, stream, p);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
+  p.next = &((WsHeader*)base)->next[1];
   hipLaunchKernelGGL(k_bwd_dkdv, dim3((unsigned)grid), dim3(64 * BW), 0, stream, p);
   e = hipGetLastError();
   if (e != hipSuccess) return e;

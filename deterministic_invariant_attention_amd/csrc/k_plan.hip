@@ -11,6 +11,8 @@
 
 namespace h3 {
 
+constexpr int TILE_ROWS_PLAN = 64;  // inner-loop tile of the backward kernels (their cost unit)
+
 // Exclusive scan of one int per thread over a 1024-thread block; also returns the block total.
 __device__ __forceinline__ int block_excl_scan(int v, int* lds_wave, int& total) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
@@ -34,10 +36,17 @@ __device__ __forceinline__ int block_excl_scan(int v, int* lds_wave, int& total)
   return before + x - v;
 }
 
+// bkt == nullptr: items in segment order (the forward's static, head-major walk).  Otherwise the
+// backward's order: items grouped by the cost class of their segment, floor(log2(ceil(L / 64))),
+// most expensive class first (the order inside a class is free: it only decides which workgroup
+// runs an item, never a result), and bkt[2b], bkt[2b+1] = first item and item count of the b-th
+// non-empty class; the work counters are reset.
 __global__ __launch_bounds__(1024) void k_plan(const int32_t* __restrict__ seg, int64_t T, WsHeader* hdr,
-                                              int32_t* __restrict__ segtab, int32_t* __restrict__ items, int tile) {
+                                              int32_t* __restrict__ segtab, int32_t* __restrict__ items, int tile,
+                                              int32_t* __restrict__ bkt) {
   __shared__ int lds_wave[16];
   __shared__ int s_bad;
+  __shared__ int s_cnt[NBKT], s_run[NBKT];
   const int tid = threadIdx.x;
   if (tid == 0) s_bad = 0;
   __syncthreads();
@@ -73,24 +82,66 @@ __global__ __launch_bounds__(1024) void k_plan(const int32_t* __restrict__ seg, 
   }
   __syncthreads();
 
-  // pass 3: work items, ceil(L / tile) tiles per segment, in segment order
+  // pass 3: work items, ceil(L / tile) tiles per segment
   int nitems = 0;
-  for (int base = 0; base < nseg; base += 1024) {
-    const int s = base + tid;
-    const int nt = (s < nseg) ? (segtab[2 * s + 1] + tile - 1) / tile : 0;
-    int total;
-    const int off = block_excl_scan(nt, lds_wave, total);
-    for (int j = 0; j < nt; j++) {
-      items[2 * (nitems + off + j)] = s;
-      items[2 * (nitems + off + j) + 1] = j;
+  int nbkt = 0;
+  if (bkt == nullptr) {  // segment order
+    for (int base = 0; base < nseg; base += 1024) {
+      const int s = base + tid;
+      const int nt = (s < nseg) ? (segtab[2 * s + 1] + tile - 1) / tile : 0;
+      int total;
+      const int off = block_excl_scan(nt, lds_wave, total);
+      for (int j = 0; j < nt; j++) {
+        items[2 * (nitems + off + j)] = s;
+        items[2 * (nitems + off + j) + 1] = j;
+      }
+      nitems += total;
     }
-    nitems += total;
+  } else {  // by cost class, most expensive first
+    if (tid < NBKT) s_cnt[tid] = 0;
+    __syncthreads();
+    for (int s = tid; s < nseg; s += 1024) {
+      const int L = segtab[2 * s + 1];
+      const int b = 31 - __builtin_clz((unsigned)((L + TILE_ROWS_PLAN - 1) / TILE_ROWS_PLAN));
+      atomicAdd(&s_cnt[b], (L + tile - 1) / tile);
+    }
+    __syncthreads();
+    if (tid == 0) {
+      int start = 0;
+      for (int b = NBKT - 1; b >= 0; b--) {
+        s_run[b] = start;
+        if (s_cnt[b] > 0) {
+          bkt[2 * nbkt] = start;
+          bkt[2 * nbkt + 1] = s_cnt[b];
+          nbkt++;
+        }
+        start += s_cnt[b];
+      }
+      s_cnt[0] = nbkt;  // broadcast
+      lds_wave[0] = start;
+    }
+    __syncthreads();
+    nbkt = s_cnt[0];
+    nitems = lds_wave[0];
+    for (int s = tid; s < nseg; s += 1024) {
+      const int L = segtab[2 * s + 1];
+      const int b = 31 - __builtin_clz((unsigned)((L + TILE_ROWS_PLAN - 1) / TILE_ROWS_PLAN));
+      const int nt = (L + tile - 1) / tile;
+      const int off = atomicAdd(&s_run[b], nt);
+      for (int j = 0; j < nt; j++) {
+        items[2 * (off + j)] = s;
+        items[2 * (off + j) + 1] = j;
+      }
+    }
   }
 
   if (tid == 0) {
     const int b = s_bad;
     hdr->nseg = b ? 0 : nseg;
     hdr->nitems = b ? 0 : nitems;
+    hdr->nbkt = b ? 0 : nbkt;
+    hdr->next[0] = 0;
+    hdr->next[1] = 0;
     hdr->status = b ? STATUS_SEG_BIT : 0;
   }
 }
@@ -99,7 +150,7 @@ hipError_t launch_plan(const int32_t* seg, int64_t T, void* ws, int32_t H, hipSt
   const WsLayout L = ws_layout(T, H);
   char* base = (char*)ws;
   hipLaunchKernelGGL(k_plan, dim3(1), dim3(1024), 0, stream, seg, T, (WsHeader*)base, (int32_t*)(base + L.segtab),
-                     (int32_t*)(base + L.items), BQ);
+                     (int32_t*)(base + L.items), BQ, nullptr);
   return hipGetLastError();
 }
 
@@ -107,7 +158,7 @@ hipError_t launch_plan_bwd(const int32_t* seg, int64_t T, void* ws, int32_t H, h
   const BwdLayout L = bwd_layout(T, H);
   char* base = (char*)ws;
   hipLaunchKernelGGL(k_plan, dim3(1), dim3(1024), 0, stream, seg, T, (WsHeader*)base, (int32_t*)(base + L.segtab),
-                     (int32_t*)(base + L.items), BT);
+                     (int32_t*)(base + L.items), BT, (int32_t*)(base + L.bkt));
   return hipGetLastError();
 }
 
