@@ -78,6 +78,29 @@ def test_bwd_parity_sharp_softmax():
     _check("sharp-w3", workloads.random_inputs([500, 130], 2, seed=13, w_scale=3.0, with_grad=True))
 
 
+def test_bwd_parity_many_segments():
+    """300 segments of random lengths 1..100 (every cost class of the work order, many items per
+    class), 2 heads, against the oracle."""
+    rng = np.random.default_rng(41)
+    lens = [int(x) for x in rng.integers(1, 101, 300)]
+    _check("many-segments", workloads.random_inputs(lens, 2, seed=42, with_grad=True))
+
+
+def test_bwd_parity_other_scale_and_eps():
+    x = workloads.random_inputs([150, 90], 2, seed=9, with_grad=True)
+    _check("scale0.2-eps1e-3", x, eps=float(np.float32(1e-3)), scale=0.2)
+
+
+def test_bwd_empty_input_is_a_noop():
+    x = workloads.random_inputs([4], 2, seed=1, with_grad=True)
+    g = to_dev(x)
+    e = {n: (t[:0].contiguous() if n in ("q", "k", "v", "dout", "seg") else t) for n, t in g.items()}
+    lse = torch.empty(0, 2, dtype=torch.float32, device=g["q"].device)
+    dq, dk, dv, dwq, dwk = h3.h3attn_bwd(e["dout"], e["q"], e["k"], e["v"], lse, e["seg"], e["wq"], e["wk"], eps=EPS)
+    torch.cuda.synchronize()
+    assert dq.numel() == 0 and dk.numel() == 0 and dv.numel() == 0
+
+
 def test_bwd_parity_batch2_heads():
     """Config 5 (2 x 4253 tokens, 40 heads) at full size, heads 0, 17 and 39 against the oracle."""
     _check("batch2", workloads.make_inputs(workloads.WORKLOADS["batch2"], with_grad=True), heads=(0, 17, 39))

@@ -110,8 +110,10 @@ def test_closed_forms():
     x = workloads.random_inputs([1, 5, 1, 77, 1], 3, seed=37)
     g = to_dev(x)
     o, _ = run_fwd(g)
-    for t in (0, 6, 84):                       # single-token segments return their own v exactly
-        assert bitwise_equal(o[t], g["v"][t])
+    for t in (0, 6, 84):  # single-token segments return their own v (exactly where fp16 holds it)
+        got, v = f64(o[t]), f64(g["v"][t])
+        exact = (np.abs(v) >= 2.0 ** -17) | (v == 0)
+        assert np.array_equal(got[exact], v[exact]) and np.all(np.abs(got - v) <= 2.0 ** -25)
     # identical keys within a segment: uniform softmax, the mean of V (only fp32 summation error)
     k = g["k"].clone()
     k[7:84] = k[7]

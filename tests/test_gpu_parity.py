@@ -45,6 +45,21 @@ def test_parity_ragged_tiles():
     _check_full("ragged", workloads.random_inputs(lens, 3, seed=21))
 
 
+def test_parity_many_single_token_segments():
+    """4096 one-token segments around a few longer ones (a work item per token): the whole output
+    matches the oracle, and every one-token segment returns its own v (P = 1): bit for bit where v
+    passes the fp16 conversion of the P.V operand exactly (|v| >= 2^-17, or 0), within 2^-25 below."""
+    lens = [1] * 2000 + [300] + [1] * 2000 + [129, 64] + [1] * 96
+    x = workloads.random_inputs(lens, 2, seed=23)
+    out = _check_full("single-token", x)
+    starts = np.cumsum([0] + lens[:-1])
+    ones = torch.as_tensor(starts[np.asarray(lens) == 1])
+    got, v = f64(out.cpu()[ones]), f64(x["v"][ones])
+    exact = (np.abs(v) >= 2.0 ** -17) | (v == 0)
+    assert np.array_equal(got[exact], v[exact])
+    assert np.all(np.abs(got[~exact] - v[~exact]) <= 2.0 ** -25)
+
+
 def test_parity_without_weights():
     """wq = wk = NULL: q and k enter Q.K^T as given (already-normalised inputs)."""
     x = workloads.random_inputs([200, 77], 4, seed=5, normed=False)
