@@ -10,6 +10,7 @@
 #include <mutex>
 
 #include "h3_common.h"
+#include "h3_bwd.h"
 #include "h3_launch.h"
 #include "h3attn.h"
 

@@ -8,6 +8,7 @@
 // fixed tree of h3_common.h, so these kernels and the attention's fused Q prologue (2 lanes per
 // row) give identical bits.
 #include "h3_common.h"
+#include "h3_bwd.h"
 #include "h3_launch.h"
 
 namespace h3 {

@@ -7,6 +7,7 @@
 // exclusive scans over tokens, then segments.  Its cost is T/1024 scan steps, negligible next to
 // the attention for the workloads served here.
 #include "h3_common.h"
+#include "h3_bwd.h"
 #include "h3_launch.h"
 
 namespace h3 {
