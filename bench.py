@@ -10,8 +10,10 @@ Backward (--pass bwd, default workload batch2): one step = one h3attn_bwd call (
 staging, dq with D, dk/dv, weight-gradient reduction) given dO and the forward's LSE; TFLOP/s on
 the nominal 2.5 x forward FLOPs; the CPU baseline is the FP64 oracle's gradients on a subset of
 heads.
+--order position: the tokens of every segment are shuffled (seeded) and the step calls the
+position-ordered entry points (h3attn_fwd_pos / h3attn_bwd_pos) with their position ids.
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload long] [--pass fwd|bwd]
-                       [--no-cpu-baseline]
+                       [--order packed|position] [--no-cpu-baseline]
 """
 import argparse
 import json
@@ -67,6 +69,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default=None, help="default: long (fwd), batch2 (bwd)")
     ap.add_argument("--pass", dest="which", choices=("fwd", "bwd"), default="fwd")
+    ap.add_argument("--order", choices=("packed", "position"), default="packed",
+                    help="position: shuffle each segment's tokens and pass their position ids")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="target oracle time of the CPU sample")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -89,7 +93,7 @@ def main():
         return bench_bwd(args, workloads.WORKLOADS[args.workload or "batch2"])
     wl = workloads.WORKLOADS[args.workload or "long"]
     dev = torch.device("cuda:0")
-    x = workloads.make_inputs(wl)
+    x, pos = ordered_inputs(workloads.make_inputs(wl), wl, args.order, dev)
     g = {n: (t.to(dev) if t is not None else None) for n, t in x.items()}
     T, H = wl.tokens, wl.heads
     flops = wl.flops()
@@ -102,8 +106,12 @@ def main():
         copy_calibration(dev)
 
     def step():
-        h3.h3attn_fwd(g["q"], g["k"], g["v"], g["seg"], g["wq"], g["wk"], eps=wl.eps, scale=wl.scale, out=out,
-                      workspace_buf=ws, stream=stream)
+        if pos is None:
+            h3.h3attn_fwd(g["q"], g["k"], g["v"], g["seg"], g["wq"], g["wk"], eps=wl.eps, scale=wl.scale, out=out,
+                          workspace_buf=ws, stream=stream)
+        else:
+            h3.h3attn_fwd_pos(g["q"], g["k"], g["v"], g["seg"], pos, g["wq"], g["wk"], eps=wl.eps, scale=wl.scale,
+                              out=out, workspace_buf=ws, stream=stream)
 
     for _ in range(args.warmup):
         step()
@@ -190,6 +198,7 @@ def main():
         "data": "synthetic",
         "config": {"workload": wl.name, "tokens": T, "heads": H, "head_dim": 128, "segments": list(wl.seg_lens),
                    "qk_draw_scale": wl.qk_scale, "pv_operands": "fp16", "accumulate": "fp32",
+                   "key_order": args.order,
                    "pct_bf16_mfma_peak": round(100 * value / PEAK_MFMA_TFLOPS, 2),
                    "repeat_bitwise": repeat_bitwise, "device_status": status},
         "roofline": {"bound": "mfma", "achieved": round(attn_tflops, 2), "peak": PEAK_MFMA_TFLOPS,
@@ -215,6 +224,17 @@ def copy_calibration(dev):
     del src, dst, scrub
 
 
+def ordered_inputs(x, wl, order, dev):
+    """packed: the inputs as drawn, no position ids.  position: every segment's tokens shuffled
+    (seed 11) and the matching position ids on the device."""
+    if order == "packed":
+        return x, None
+    import workloads
+    p = workloads.shuffle_within_segments(wl.seg_lens, 11)
+    x = {n: (t[p].contiguous() if n in ("q", "k", "v", "dout") else t) for n, t in x.items()}
+    return x, workloads.position_ids(wl.seg_lens)[p].contiguous().to(dev)
+
+
 def bench_bwd(args, wl):
     import numpy as np
     import torch
@@ -223,7 +243,7 @@ def bench_bwd(args, wl):
     import workloads
 
     dev = torch.device("cuda:0")
-    x = workloads.make_inputs(wl, with_grad=True)
+    x, pos = ordered_inputs(workloads.make_inputs(wl, with_grad=True), wl, args.order, dev)
     g = {n: (t.to(dev) if t is not None else None) for n, t in x.items()}
     T, H = wl.tokens, wl.heads
     flops = 2.5 * wl.flops()
@@ -231,16 +251,25 @@ def bench_bwd(args, wl):
     log(f"workload {wl.name} backward: {wl.description}; nominal {flops:.4e} FLOP/step (2.5 x forward)")
     if args.copy_calibration:
         copy_calibration(dev)
-    _, lse = h3.h3attn_fwd(g["q"], g["k"], g["v"], g["seg"], g["wq"], g["wk"], eps=wl.eps, scale=wl.scale,
-                           want_lse=True, stream=stream)
+    if pos is None:
+        _, lse = h3.h3attn_fwd(g["q"], g["k"], g["v"], g["seg"], g["wq"], g["wk"], eps=wl.eps, scale=wl.scale,
+                               want_lse=True, stream=stream)
+    else:
+        _, lse = h3.h3attn_fwd_pos(g["q"], g["k"], g["v"], g["seg"], pos, g["wq"], g["wk"], eps=wl.eps,
+                                   scale=wl.scale, want_lse=True, stream=stream)
     ws = h3.bwd_workspace(T, H, dev)
     outs = [torch.empty_like(g["q"]) for _ in range(3)]
     dw = [torch.empty(128, dtype=torch.float32, device=dev) for _ in range(2)]
 
     def step():
-        h3.h3attn_bwd(g["dout"], g["q"], g["k"], g["v"], lse, g["seg"], g["wq"], g["wk"], eps=wl.eps,
-                      scale=wl.scale, dq=outs[0], dk=outs[1], dv=outs[2], dwq=dw[0], dwk=dw[1], workspace_buf=ws,
-                      stream=stream)
+        if pos is None:
+            h3.h3attn_bwd(g["dout"], g["q"], g["k"], g["v"], lse, g["seg"], g["wq"], g["wk"], eps=wl.eps,
+                          scale=wl.scale, dq=outs[0], dk=outs[1], dv=outs[2], dwq=dw[0], dwk=dw[1], workspace_buf=ws,
+                          stream=stream)
+        else:
+            h3.h3attn_bwd_pos(g["dout"], g["q"], g["k"], g["v"], lse, g["seg"], pos, g["wq"], g["wk"], eps=wl.eps,
+                              scale=wl.scale, dq=outs[0], dk=outs[1], dv=outs[2], dwq=dw[0], dwk=dw[1],
+                              workspace_buf=ws, stream=stream)
 
     for _ in range(args.warmup):
         step()
@@ -304,6 +333,7 @@ def bench_bwd(args, wl):
         "data": "synthetic",
         "config": {"workload": wl.name + "-bwd", "tokens": T, "heads": H, "head_dim": 128,
                    "segments": list(wl.seg_lens), "products": "fp16 P, dS, dO, q/k hat; fp32 accumulate",
+                   "key_order": args.order,
                    "pct_bf16_mfma_peak": round(100 * value / PEAK_MFMA_TFLOPS, 2),
                    "repeat_bitwise": repeat_bitwise, "device_status": status},
         "roofline": {"bound": "mfma", "achieved": round(value, 2), "peak": PEAK_MFMA_TFLOPS, "unit": "TFLOP/s",

@@ -26,11 +26,12 @@ H3ATTN_ERR_DEVICE = 6
 H3ATTN_ERR_LAUNCH = 7
 H3ATTN_ERR_SEGMENTS = 8
 H3ATTN_ERR_RANGE = 9
+H3ATTN_ERR_POSITIONS = 10
 
 # every symbol the header declares
 EXPORTS = ("h3attn_version", "h3attn_strerror", "h3attn_workspace_bytes", "h3attn_qknorm", "h3attn_fwd",
-           "h3attn_plan", "h3attn_prep_kv", "h3attn_attend", "h3attn_status_read", "h3attn_bwd_workspace_bytes",
-           "h3attn_bwd")
+           "h3attn_fwd_pos", "h3attn_plan", "h3attn_prep_kv", "h3attn_attend", "h3attn_status_read",
+           "h3attn_bwd_workspace_bytes", "h3attn_bwd", "h3attn_bwd_pos")
 
 
 class H3AttnError(RuntimeError):
@@ -58,6 +59,7 @@ def load():
     lib.h3attn_workspace_bytes.restype = SZ
     lib.h3attn_qknorm.argtypes = [P, P, P, I64, I32, I32, F, P]
     lib.h3attn_fwd.argtypes = [P, P, P, P, P, P, I64, I32, I32, F, F, P, P, P, SZ, P]
+    lib.h3attn_fwd_pos.argtypes = [P, P, P, P, P, P, P, I64, I32, I32, F, F, P, P, P, SZ, P]
     lib.h3attn_plan.argtypes = [P, I64, I32, P, SZ, P]
     lib.h3attn_prep_kv.argtypes = [P, P, P, I64, I32, I32, F, P, SZ, P]
     lib.h3attn_attend.argtypes = [P, P, I64, I32, I32, F, F, P, P, P, SZ, P]
@@ -65,8 +67,9 @@ def load():
     lib.h3attn_bwd_workspace_bytes.argtypes = [I64, I32]
     lib.h3attn_bwd_workspace_bytes.restype = SZ
     lib.h3attn_bwd.argtypes = [P, P, P, P, P, P, P, P, I64, I32, I32, F, F, P, P, P, P, P, P, SZ, P]
-    for name in ("h3attn_qknorm", "h3attn_fwd", "h3attn_plan", "h3attn_prep_kv", "h3attn_attend",
-                 "h3attn_status_read", "h3attn_bwd"):
+    lib.h3attn_bwd_pos.argtypes = [P, P, P, P, P, P, P, P, P, I64, I32, I32, F, F, P, P, P, P, P, P, SZ, P]
+    for name in ("h3attn_qknorm", "h3attn_fwd", "h3attn_fwd_pos", "h3attn_plan", "h3attn_prep_kv", "h3attn_attend",
+                 "h3attn_status_read", "h3attn_bwd", "h3attn_bwd_pos"):
         getattr(lib, name).restype = ctypes.c_int
     _lib = lib
     return lib
@@ -127,22 +130,45 @@ def h3attn_qknorm(x, w, eps: float = 1e-6, out=None, stream=None):
     return y
 
 
+def _int32(t, name):
+    if t.dtype != torch.int32 or not t.is_contiguous():
+        raise TypeError(f"{name} must be a contiguous int32 tensor")
+    return t
+
+
 def h3attn_fwd(q, k, v, seg_ids, wq=None, wk=None, eps: float = 1e-6, scale: float | None = None, out=None,
                lse=None, workspace_buf=None, stream=None, want_lse: bool = False):
     """Forward of the attention node with its fused q/k norm.  Returns (out, lse) (lse None unless asked)."""
+    return _fwd(q, k, v, seg_ids, None, wq, wk, eps, scale, out, lse, workspace_buf, stream, want_lse)
+
+
+def h3attn_fwd_pos(q, k, v, seg_ids, pos_ids, wq=None, wk=None, eps: float = 1e-6, scale: float | None = None,
+                   out=None, lse=None, workspace_buf=None, stream=None, want_lse: bool = False):
+    """h3attn_fwd with each segment's keys walked in the order of pos_ids (int32 [T], a permutation of
+    0..L-1 within each segment).  Returns (out, lse)."""
+    return _fwd(q, k, v, seg_ids, _int32(pos_ids, "pos_ids"), wq, wk, eps, scale, out, lse, workspace_buf, stream,
+                want_lse)
+
+
+def _fwd(q, k, v, seg_ids, pos_ids, wq, wk, eps, scale, out, lse, workspace_buf, stream, want_lse):
     for t, n in ((q, "q"), (k, "k"), (v, "v"), (wq, "wq"), (wk, "wk")):
         _bf16(t, n)
-    if seg_ids.dtype != torch.int32 or not seg_ids.is_contiguous():
-        raise TypeError("seg_ids must be a contiguous int32 tensor")
+    _int32(seg_ids, "seg_ids")
     T, H, D = _shape(q)
     scale = D ** -0.5 if scale is None else scale
     out = torch.empty_like(q) if out is None else _bf16(out, "out")
     if lse is None and want_lse:
         lse = torch.empty((T, H), dtype=torch.float32, device=q.device)
     ws = workspace(T, H, q.device) if workspace_buf is None else workspace_buf
-    rc = load().h3attn_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(seg_ids), _ptr(wq), _ptr(wk), T, H, D, float(eps),
-                           float(scale), _ptr(out), _ptr(lse), _ptr(ws), ws.numel(), _stream(stream, q.device))
-    _check(rc, "h3attn_fwd")
+    st = _stream(stream, q.device)
+    if pos_ids is None:
+        rc = load().h3attn_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(seg_ids), _ptr(wq), _ptr(wk), T, H, D, float(eps),
+                               float(scale), _ptr(out), _ptr(lse), _ptr(ws), ws.numel(), st)
+        _check(rc, "h3attn_fwd")
+    else:
+        rc = load().h3attn_fwd_pos(_ptr(q), _ptr(k), _ptr(v), _ptr(seg_ids), _ptr(pos_ids), _ptr(wq), _ptr(wk), T, H,
+                                   D, float(eps), float(scale), _ptr(out), _ptr(lse), _ptr(ws), ws.numel(), st)
+        _check(rc, "h3attn_fwd_pos")
     return out, lse
 
 
@@ -190,10 +216,21 @@ def h3attn_bwd(dout, q, k, v, lse, seg_ids, wq=None, wk=None, eps: float = 1e-6,
                dq=None, dk=None, dv=None, dwq=None, dwk=None, workspace_buf=None, stream=None):
     """Backward of the node: returns (dq, dk, dv, dwq, dwk) (dwq/dwk None without norm weights).
     lse is the forward's fp32 [T, H] log-sum-exp (h3attn_fwd(..., want_lse=True))."""
+    return _bwd(dout, q, k, v, lse, seg_ids, None, wq, wk, eps, scale, dq, dk, dv, dwq, dwk, workspace_buf, stream)
+
+
+def h3attn_bwd_pos(dout, q, k, v, lse, seg_ids, pos_ids, wq=None, wk=None, eps: float = 1e-6,
+                   scale: float | None = None, dq=None, dk=None, dv=None, dwq=None, dwk=None, workspace_buf=None,
+                   stream=None):
+    """h3attn_bwd with every sum taken in the order of pos_ids (as for h3attn_fwd_pos)."""
+    return _bwd(dout, q, k, v, lse, seg_ids, _int32(pos_ids, "pos_ids"), wq, wk, eps, scale, dq, dk, dv, dwq, dwk,
+                workspace_buf, stream)
+
+
+def _bwd(dout, q, k, v, lse, seg_ids, pos_ids, wq, wk, eps, scale, dq, dk, dv, dwq, dwk, workspace_buf, stream):
     for t, n in ((dout, "dout"), (q, "q"), (k, "k"), (v, "v"), (wq, "wq"), (wk, "wk")):
         _bf16(t, n)
-    if seg_ids.dtype != torch.int32 or not seg_ids.is_contiguous():
-        raise TypeError("seg_ids must be a contiguous int32 tensor")
+    _int32(seg_ids, "seg_ids")
     if lse.dtype != torch.float32 or not lse.is_contiguous():
         raise TypeError("lse must be a contiguous float32 tensor")
     T, H, D = _shape(q)
@@ -205,8 +242,15 @@ def h3attn_bwd(dout, q, k, v, lse, seg_ids, wq=None, wk=None, eps: float = 1e-6,
         dwq = torch.empty(D, dtype=torch.float32, device=q.device) if dwq is None else dwq
         dwk = torch.empty(D, dtype=torch.float32, device=q.device) if dwk is None else dwk
     ws = bwd_workspace(T, H, q.device) if workspace_buf is None else workspace_buf
-    rc = load().h3attn_bwd(_ptr(dout), _ptr(q), _ptr(k), _ptr(v), _ptr(lse), _ptr(seg_ids), _ptr(wq), _ptr(wk), T, H,
-                           D, float(eps), float(scale), _ptr(dq), _ptr(dk), _ptr(dv), _ptr(dwq), _ptr(dwk), _ptr(ws),
-                           ws.numel(), _stream(stream, q.device))
-    _check(rc, "h3attn_bwd")
+    st = _stream(stream, q.device)
+    if pos_ids is None:
+        rc = load().h3attn_bwd(_ptr(dout), _ptr(q), _ptr(k), _ptr(v), _ptr(lse), _ptr(seg_ids), _ptr(wq), _ptr(wk),
+                               T, H, D, float(eps), float(scale), _ptr(dq), _ptr(dk), _ptr(dv), _ptr(dwq), _ptr(dwk),
+                               _ptr(ws), ws.numel(), st)
+        _check(rc, "h3attn_bwd")
+    else:
+        rc = load().h3attn_bwd_pos(_ptr(dout), _ptr(q), _ptr(k), _ptr(v), _ptr(lse), _ptr(seg_ids), _ptr(pos_ids),
+                                   _ptr(wq), _ptr(wk), T, H, D, float(eps), float(scale), _ptr(dq), _ptr(dk),
+                                   _ptr(dv), _ptr(dwq), _ptr(dwk), _ptr(ws), ws.numel(), st)
+        _check(rc, "h3attn_bwd_pos")
     return dq, dk, dv, dwq, dwk

@@ -16,7 +16,7 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 OUT_DIR = os.path.join(PKG, "lib")
 LIB = os.path.join(OUT_DIR, "libh3attn.so")
-SOURCES = ["h3attn_api.hip", "k_plan.hip", "k_norm.hip", "k_attn_fwd.hip", "k_bwd.hip"]
+SOURCES = ["h3attn_api.hip", "k_plan.hip", "k_order.hip", "k_norm.hip", "k_attn_fwd.hip", "k_bwd.hip"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 FLAGS = [

@@ -12,6 +12,7 @@
 #include "h3_common.h"
 #include "h3_bwd.h"
 #include "h3_launch.h"
+#include "h3_order.h"
 #include "h3attn.h"
 
 namespace {
@@ -95,13 +96,15 @@ const char* h3attn_strerror(int status) {
     case H3ATTN_ERR_LAUNCH: return "the HIP runtime rejected a launch or copy";
     case H3ATTN_ERR_SEGMENTS: return "segment ids decrease (device status)";
     case H3ATTN_ERR_RANGE: return "a finite value beyond 65504 cannot enter an fp16 product (device status)";
+    case H3ATTN_ERR_POSITIONS: return "position ids are not a permutation of 0..L-1 in some segment (device status)";
     default: return "unknown status";
   }
 }
 
+// Large enough for both h3attn_fwd and h3attn_fwd_pos (the ordering area follows the plain layout).
 size_t h3attn_workspace_bytes(int64_t tokens, int32_t heads) {
   if (check_shape(tokens, heads, HD) != H3ATTN_OK) return 0;
-  return ws_layout(tokens, heads).total;
+  return order_layout(ws_layout(tokens, heads).total, tokens).total;
 }
 
 int h3attn_qknorm(const void* x, const void* w, void* y, int64_t tokens, int32_t heads, int32_t head_dim, float eps,
@@ -181,7 +184,7 @@ int h3attn_prep_kv(const void* k, const void* v, const void* wk, int64_t tokens,
   if ((rc = check_prep(k, v, wk, tokens, heads, eps, workspace, workspace_bytes))) return rc;
   DeviceInfo di;
   if ((rc = device_info(&di))) return rc;
-  return launch_status(launch_prep_kv(k, v, wk, tokens, heads, eps, workspace, (hipStream_t)stream));
+  return launch_status(launch_prep_kv(k, v, wk, tokens, heads, eps, workspace, nullptr, (hipStream_t)stream));
 }
 
 int h3attn_attend(const void* q, const void* wq, int64_t tokens, int32_t heads, int32_t head_dim, float eps,
@@ -196,16 +199,18 @@ int h3attn_attend(const void* q, const void* wq, int64_t tokens, int32_t heads, 
       launch_attend(q, wq, tokens, heads, eps, scale, out, lse, workspace, di.cus, (hipStream_t)stream));
 }
 
-int h3attn_fwd(const void* q, const void* k, const void* v, const int32_t* seg_ids, const void* wq, const void* wk,
-               int64_t tokens, int32_t heads, int32_t head_dim, float eps, float scale, void* out, float* lse,
-               void* workspace, size_t workspace_bytes, void* stream) {
+// The forward; pos_ids NULL walks keys in packed order, else in position order.
+static int fwd_impl(const void* q, const void* k, const void* v, const int32_t* seg_ids, const int32_t* pos_ids,
+                    bool ordered, const void* wq, const void* wk, int64_t tokens, int32_t heads, int32_t head_dim,
+                    float eps, float scale, void* out, float* lse, void* workspace, size_t workspace_bytes,
+                    void* stream) {
   int rc = check_shape(tokens, heads, head_dim);
   if (rc) return rc;
   if ((wq == nullptr) != (wk == nullptr)) return H3ATTN_ERR_NULL;
   if (wq && (!(eps > 0.0f) || !std::isfinite(eps))) return H3ATTN_ERR_SHAPE;
   if (!(scale > 0.0f) || !std::isfinite(scale)) return H3ATTN_ERR_SHAPE;
   if (tokens == 0) return H3ATTN_OK;
-  if (!q || !k || !v || !seg_ids || !out || !workspace) return H3ATTN_ERR_NULL;
+  if (!q || !k || !v || !seg_ids || !out || !workspace || (ordered && !pos_ids)) return H3ATTN_ERR_NULL;
   if ((rc = check_plan(seg_ids, tokens, heads, workspace, workspace_bytes))) return rc;
   if ((rc = check_prep(k, v, wk, tokens, heads, eps, workspace, workspace_bytes))) return rc;
   if ((rc = check_attend(q, wq, tokens, heads, eps, scale, out, lse, workspace, workspace_bytes))) return rc;
@@ -216,24 +221,54 @@ int h3attn_fwd(const void* q, const void* k, const void* v, const int32_t* seg_i
       overlap(out, n, wk, HD * 2) || overlap(lse, nl, k, n) || overlap(lse, nl, v, n) ||
       overlap(lse, nl, seg_ids, ns) || overlap(lse, nl, wk, HD * 2))
     return H3ATTN_ERR_ALIAS;
+  const OrderLayout ol = order_layout(ws_layout(tokens, heads).total, tokens);
+  if (ordered) {
+    if (!aligned(pos_ids, 4)) return H3ATTN_ERR_ALIGN;
+    if (overlap(out, n, pos_ids, ns) || overlap(lse, nl, pos_ids, ns) ||
+        overlap(pos_ids, ns, workspace, workspace_bytes))
+      return H3ATTN_ERR_ALIAS;
+    if (workspace_bytes < ol.total) return H3ATTN_ERR_WORKSPACE;
+  }
   DeviceInfo di;
   if ((rc = device_info(&di))) return rc;
   hipStream_t st = (hipStream_t)stream;
+  char* base = (char*)workspace;
+  int32_t* slot = ordered ? (int32_t*)(base + ol.slot) : nullptr;
   if ((rc = launch_status(launch_plan(seg_ids, tokens, workspace, heads, st)))) return rc;
-  if ((rc = launch_status(launch_prep_kv(k, v, wk, tokens, heads, eps, workspace, st)))) return rc;
+  if (ordered &&
+      (rc = launch_status(launch_order(pos_ids, tokens, workspace, (const int32_t*)(base + ws_layout(tokens, heads).segtab),
+                                       slot, (int32_t*)(base + ol.inv), st))))
+    return rc;
+  if ((rc = launch_status(launch_prep_kv(k, v, wk, tokens, heads, eps, workspace, slot, st)))) return rc;
   return launch_status(launch_attend(q, wq, tokens, heads, eps, scale, out, lse, workspace, di.cus, st));
 }
 
+int h3attn_fwd(const void* q, const void* k, const void* v, const int32_t* seg_ids, const void* wq, const void* wk,
+               int64_t tokens, int32_t heads, int32_t head_dim, float eps, float scale, void* out, float* lse,
+               void* workspace, size_t workspace_bytes, void* stream) {
+  return fwd_impl(q, k, v, seg_ids, nullptr, false, wq, wk, tokens, heads, head_dim, eps, scale, out, lse, workspace,
+                  workspace_bytes, stream);
+}
+
+int h3attn_fwd_pos(const void* q, const void* k, const void* v, const int32_t* seg_ids, const int32_t* pos_ids,
+                   const void* wq, const void* wk, int64_t tokens, int32_t heads, int32_t head_dim, float eps,
+                   float scale, void* out, float* lse, void* workspace, size_t workspace_bytes, void* stream) {
+  return fwd_impl(q, k, v, seg_ids, pos_ids, true, wq, wk, tokens, heads, head_dim, eps, scale, out, lse, workspace,
+                  workspace_bytes, stream);
+}
+
+// Large enough for both h3attn_bwd and h3attn_bwd_pos.
 size_t h3attn_bwd_workspace_bytes(int64_t tokens, int32_t heads) {
   if (check_shape(tokens, heads, HD) != H3ATTN_OK) return 0;
   if (tokens + (tokens + BT - 1) / BT > (int64_t)INT32_MAX / heads) return 0;
-  return bwd_layout(tokens, heads).total;
+  return order_layout(bwd_layout(tokens, heads).total, tokens).total;
 }
 
-int h3attn_bwd(const void* dout, const void* q, const void* k, const void* v, const float* lse,
-               const int32_t* seg_ids, const void* wq, const void* wk, int64_t tokens, int32_t heads,
-               int32_t head_dim, float eps, float scale, void* dq, void* dk, void* dv, float* dwq, float* dwk,
-               void* workspace, size_t workspace_bytes, void* stream) {
+// The backward; ordered: operands staged and every sum taken in position order.
+static int bwd_impl(const void* dout, const void* q, const void* k, const void* v, const float* lse,
+                    const int32_t* seg_ids, const int32_t* pos_ids, bool ordered, const void* wq, const void* wk,
+                    int64_t tokens, int32_t heads, int32_t head_dim, float eps, float scale, void* dq, void* dk,
+                    void* dv, float* dwq, float* dwk, void* workspace, size_t workspace_bytes, void* stream) {
   int rc = check_shape(tokens, heads, head_dim);
   if (rc) return rc;
   if (tokens + (tokens + BT - 1) / BT > (int64_t)INT32_MAX / heads) return H3ATTN_ERR_SHAPE;
@@ -241,23 +276,27 @@ int h3attn_bwd(const void* dout, const void* q, const void* k, const void* v, co
   if (wq && (!(eps > 0.0f) || !std::isfinite(eps))) return H3ATTN_ERR_SHAPE;
   if (!(scale > 0.0f) || !std::isfinite(scale)) return H3ATTN_ERR_SHAPE;
   if (tokens == 0) return H3ATTN_OK;
-  if (!dout || !q || !k || !v || !lse || !seg_ids || !dq || !dk || !dv || !workspace) return H3ATTN_ERR_NULL;
+  if (!dout || !q || !k || !v || !lse || !seg_ids || !dq || !dk || !dv || !workspace || (ordered && !pos_ids))
+    return H3ATTN_ERR_NULL;
   if (wq && (!dwq || !dwk)) return H3ATTN_ERR_NULL;
   if (!aligned(dout, 16) || !aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(lse, 4) ||
       !aligned(seg_ids, 4) || (wq && (!aligned(wq, 16) || !aligned(wk, 16) || !aligned(dwq, 4) || !aligned(dwk, 4))) ||
-      !aligned(dq, 16) || !aligned(dk, 16) || !aligned(dv, 16) || !aligned(workspace, 256))
+      !aligned(dq, 16) || !aligned(dk, 16) || !aligned(dv, 16) || !aligned(workspace, 256) ||
+      (ordered && !aligned(pos_ids, 4)))
     return H3ATTN_ERR_ALIGN;
-  if (workspace_bytes < bwd_layout(tokens, heads).total) return H3ATTN_ERR_WORKSPACE;
+  const OrderLayout ol = order_layout(bwd_layout(tokens, heads).total, tokens);
+  if (workspace_bytes < (ordered ? ol.total : bwd_layout(tokens, heads).total)) return H3ATTN_ERR_WORKSPACE;
   const size_t n = tensor_bytes(tokens, heads);
   const size_t nl = (size_t)tokens * heads * 4;
   const size_t ns = (size_t)tokens * 4;
   // every output against every input, the workspace and the other outputs
-  const void* ins[] = {dout, q, k, v, lse, seg_ids, wq, wk, workspace};
-  const size_t in_n[] = {n, n, n, n, nl, ns, (size_t)HD * 2, (size_t)HD * 2, workspace_bytes};
+  const void* ins[] = {dout, q, k, v, lse, seg_ids, wq, wk, workspace, pos_ids};
+  const size_t in_n[] = {n, n, n, n, nl, ns, (size_t)HD * 2, (size_t)HD * 2, workspace_bytes, ordered ? ns : 0};
   void* outs[] = {dq, dk, dv, dwq, dwk};
   const size_t out_n[] = {n, n, n, wq ? (size_t)HD * 4 : 0, wq ? (size_t)HD * 4 : 0};
+  if (ordered && overlap(pos_ids, ns, workspace, workspace_bytes)) return H3ATTN_ERR_ALIAS;
   for (int o = 0; o < 5; o++) {
-    for (int i = 0; i < 9; i++)
+    for (int i = 0; i < 10; i++)
       if (overlap(outs[o], out_n[o], ins[i], in_n[i])) return H3ATTN_ERR_ALIAS;
     for (int o2 = o + 1; o2 < 5; o2++)
       if (overlap(outs[o], out_n[o], outs[o2], out_n[o2])) return H3ATTN_ERR_ALIAS;
@@ -265,9 +304,34 @@ int h3attn_bwd(const void* dout, const void* q, const void* k, const void* v, co
   DeviceInfo di;
   if ((rc = device_info(&di))) return rc;
   hipStream_t st = (hipStream_t)stream;
+  char* base = (char*)workspace;
+  int32_t* slot = ordered ? (int32_t*)(base + ol.slot) : nullptr;
+  int32_t* inv = ordered ? (int32_t*)(base + ol.inv) : nullptr;
   if ((rc = launch_status(launch_plan_bwd(seg_ids, tokens, workspace, heads, st)))) return rc;
-  if ((rc = launch_status(launch_bwd_prep(q, k, v, dout, lse, wq, wk, tokens, heads, eps, workspace, st)))) return rc;
-  return launch_status(launch_bwd(q, k, wq, wk, tokens, heads, eps, scale, dq, dk, dv, dwq, dwk, workspace, di.cus, st));
+  if (ordered &&
+      (rc = launch_status(launch_order(pos_ids, tokens, workspace,
+                                       (const int32_t*)(base + bwd_layout(tokens, heads).segtab), slot, inv, st))))
+    return rc;
+  if ((rc = launch_status(launch_bwd_prep(q, k, v, dout, lse, wq, wk, tokens, heads, eps, workspace, slot, st))))
+    return rc;
+  return launch_status(
+      launch_bwd(q, k, wq, wk, tokens, heads, eps, scale, dq, dk, dv, dwq, dwk, workspace, inv, di.cus, st));
+}
+
+int h3attn_bwd(const void* dout, const void* q, const void* k, const void* v, const float* lse,
+               const int32_t* seg_ids, const void* wq, const void* wk, int64_t tokens, int32_t heads,
+               int32_t head_dim, float eps, float scale, void* dq, void* dk, void* dv, float* dwq, float* dwk,
+               void* workspace, size_t workspace_bytes, void* stream) {
+  return bwd_impl(dout, q, k, v, lse, seg_ids, nullptr, false, wq, wk, tokens, heads, head_dim, eps, scale, dq, dk, dv,
+                  dwq, dwk, workspace, workspace_bytes, stream);
+}
+
+int h3attn_bwd_pos(const void* dout, const void* q, const void* k, const void* v, const float* lse,
+                   const int32_t* seg_ids, const int32_t* pos_ids, const void* wq, const void* wk, int64_t tokens,
+                   int32_t heads, int32_t head_dim, float eps, float scale, void* dq, void* dk, void* dv, float* dwq,
+                   float* dwk, void* workspace, size_t workspace_bytes, void* stream) {
+  return bwd_impl(dout, q, k, v, lse, seg_ids, pos_ids, true, wq, wk, tokens, heads, head_dim, eps, scale, dq, dk, dv,
+                  dwq, dwk, workspace, workspace_bytes, stream);
 }
 
 int h3attn_status_read(const void* workspace, int32_t* device_status, void* stream) {
@@ -280,7 +344,10 @@ int h3attn_status_read(const void* workspace, int32_t* device_status, void* stre
     (void)hipGetLastError();
     return H3ATTN_ERR_LAUNCH;
   }
-  *device_status = (bits & STATUS_SEG_BIT) ? H3ATTN_ERR_SEGMENTS : (bits & STATUS_RANGE_BIT) ? H3ATTN_ERR_RANGE : H3ATTN_OK;
+  *device_status = (bits & STATUS_SEG_BIT)     ? H3ATTN_ERR_SEGMENTS
+                   : (bits & STATUS_POS_BIT)   ? H3ATTN_ERR_POSITIONS
+                   : (bits & STATUS_RANGE_BIT) ? H3ATTN_ERR_RANGE
+                                               : H3ATTN_OK;
   return H3ATTN_OK;
 }
 

@@ -49,8 +49,9 @@ struct BwdParams {
   uint16_t* dq;  // outputs, token-major
   uint16_t* dk;
   uint16_t* dv;
-  float* dqh;  // with norm weights: gradients with respect to the normed q / k, fp32 token-major
+  float* dqh;  // with norm weights: gradients with respect to the normed q / k, fp32, staged row-major
   float* dkh;
+  const int32_t* inv;  // token of each staged row (position order), or NULL (staged row = token)
   const WsHeader* hdr;
   int32_t* next;  // the kernel's work counter (in the header)
   const int32_t* segtab;
@@ -310,11 +311,13 @@ __global__ __launch_bounds__(64 * BW, 1) void k_bwd_dq(BwdParams p) {
 
     // ---- epilogue: dq^ = scale dQ (fp32 for the norm backward, else the output itself)
     if (qvalid) {
-      const int64_t orow = ((int64_t)(w.s0 + qrow) * H + w.head) * HD;
-      if (p.wq)
-        store_row_f32(acc, p.scale, hh, p.dqh + orow);
-      else
-        store_row(acc, p.scale, hh, p.dq + orow);
+      const int64_t srow = w.s0 + qrow;
+      if (p.wq) {
+        store_row_f32(acc, p.scale, hh, p.dqh + (srow * H + w.head) * HD);
+      } else {
+        const int64_t trow = p.inv ? (int64_t)p.inv[srow] : srow;
+        store_row(acc, p.scale, hh, p.dq + (trow * H + w.head) * HD);
+      }
     }
   }
 }
@@ -441,12 +444,13 @@ __global__ __launch_bounds__(64 * BW, 1) void k_bwd_dkdv(BwdParams p) {
 
     // ---- epilogue: dv, dk^ = scale dK (fp32 for the norm backward, else the output itself)
     if (kvalid) {
-      const int64_t orow = ((int64_t)(w.s0 + krow) * H + w.head) * HD;
-      store_row(dv, 1.0f, hh, p.dv + orow);
+      const int64_t srow = w.s0 + krow;
+      const int64_t trow = p.inv ? (int64_t)p.inv[srow] : srow;
+      store_row(dv, 1.0f, hh, p.dv + (trow * H + w.head) * HD);
       if (p.wk)
-        store_row_f32(dk, p.scale, hh, p.dkh + orow);
+        store_row_f32(dk, p.scale, hh, p.dkh + (srow * H + w.head) * HD);
       else
-        store_row(dk, p.scale, hh, p.dk + orow);
+        store_row(dk, p.scale, hh, p.dk + (trow * H + w.head) * HD);
     }
   }
 }
@@ -458,16 +462,19 @@ __global__ __launch_bounds__(64 * BW, 1) void k_bwd_dkdv(BwdParams p) {
 // and the weight-gradient terms dy o x r.  16 lanes per row (8 channels each), 16 rows per
 // workgroup; r is the forward's FP64 value (the same fixed tree as the norm itself); g . x is
 // summed in FP64, per lane over its 8 channels in order and then across the lanes in a fixed
-// butterfly (partners add the same two values, so every lane holds the same bits).  The
-// workgroup's dw partial sums its 16 rows in row order.  blockIdx.y: 0 = q, 1 = k.
+// butterfly (partners add the same two values, so every lane holds the same bits).  Rows are walked
+// in staged order (the order of dy), so the workgroup's dw partial sums its 16 rows in that order;
+// x and dx are the token's rows.  blockIdx.y: 0 = q, 1 = k.
 struct NormBwdParams {
   const uint16_t* x[2];  // raw q, k (token-major)
   const uint16_t* w[2];
   const float* dy[2];    // dq^, dk^
   uint16_t* dx[2];       // dq, dk
   float* part;           // [2][nparts][128]
+  const int32_t* inv;    // token of each staged row, or NULL
   const WsHeader* hdr;
   int64_t rows;          // T * H
+  int32_t H;
   int64_t nparts;
   float eps;
 };
@@ -477,16 +484,21 @@ __global__ __launch_bounds__(256) void k_bwd_norm(NormBwdParams p) {
   const int which = blockIdx.y;
   const int tid = threadIdx.x;
   const int c = tid & 15;
-  const int64_t row = (int64_t)blockIdx.x * NR + (tid >> 4);
+  const int64_t row = (int64_t)blockIdx.x * NR + (tid >> 4);  // staged row: slot * H + head
   const bool valid = row < p.rows;
   if (p.hdr->status != 0) return;  // the attention kernels have filled the outputs with NaN
+  int64_t xrow = row;  // the token's row
+  if (p.inv && valid) {
+    const int64_t sl = row / p.H;
+    xrow = (int64_t)p.inv[sl] * p.H + (row - sl * p.H);
+  }
 
   float x[8], dy[8], wf[8];
   {
     u32x4 xv = {0, 0, 0, 0};
     f32x4 d0 = {0.0f, 0.0f, 0.0f, 0.0f}, d1 = d0;
     if (valid) {
-      xv = *(const u32x4*)(p.x[which] + row * HD + 8 * c);
+      xv = *(const u32x4*)(p.x[which] + xrow * HD + 8 * c);
       d0 = *(const f32x4*)(p.dy[which] + row * HD + 8 * c);
       d1 = *(const f32x4*)(p.dy[which] + row * HD + 8 * c + 4);
     }
@@ -512,7 +524,7 @@ __global__ __launch_bounds__(256) void k_bwd_norm(NormBwdParams p) {
         f64_to_bf16_rne(r * ((double)wf[2 * i + 1] * (double)dy[2 * i + 1]) - k3 * (double)x[2 * i + 1]);
     o[i] = a | (b << 16);
   }
-  if (valid) *(u32x4*)(p.dx[which] + row * HD + 8 * c) = o;
+  if (valid) *(u32x4*)(p.dx[which] + xrow * HD + 8 * c) = o;
   f32x4 t0, t1;
 #pragma unroll
   for (int i = 0; i < 4; i++) {
@@ -573,8 +585,8 @@ __global__ __launch_bounds__(2 * HD) void k_bwd_dw_final(const WsHeader* hdr, co
 }
 
 hipError_t launch_bwd(const void* q, const void* k, const void* wq, const void* wk, int64_t T, int32_t H, float eps,
-                      float scale, void* dq, void* dk, void* dv, float* dwq, float* dwk, void* ws, int grid_cap,
-                      hipStream_t stream) {
+                      float scale, void* dq, void* dk, void* dv, float* dwq, float* dwk, void* ws,
+                      const int32_t* inv, int grid_cap, hipStream_t stream) {
   const BwdLayout Lw = bwd_layout(T, H);
   char* base = (char*)ws;
   BwdParams p;
@@ -593,6 +605,7 @@ hipError_t launch_bwd(const void* q, const void* k, const void* wq, const void* 
   p.dv = (uint16_t*)dv;
   p.dqh = (float*)(base + Lw.dqh);
   p.dkh = (float*)(base + Lw.dkh);
+  p.inv = inv;
   p.hdr = (const WsHeader*)base;
   p.segtab = (const int32_t*)(base + Lw.segtab);
   p.items = (const int32_t*)(base + Lw.items);
@@ -624,8 +637,10 @@ hipError_t launch_bwd(const void* q, const void* k, const void* wq, const void* 
     np.dx[0] = (uint16_t*)dq;
     np.dx[1] = (uint16_t*)dk;
     np.part = (float*)(base + Lw.dw_part);
+    np.inv = inv;
     np.hdr = (const WsHeader*)base;
     np.rows = T * H;
+    np.H = H;
     np.nparts = Lw.nparts;
     np.eps = eps;
     hipLaunchKernelGGL(k_bwd_norm, dim3((unsigned)Lw.nparts, 2), dim3(256), 0, stream, np);

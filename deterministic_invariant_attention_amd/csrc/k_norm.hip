@@ -39,11 +39,11 @@ __global__ __launch_bounds__(256) void k_qknorm(const uint16_t* x, const uint16_
 }
 
 // rows are visited token-major (r = t*H + h) so the reads are contiguous; each row is written to
-// its head-major slot (h*T + t).
+// its head-major staged row (h*T + t, or h*T + slot[t] in position order).
 __global__ __launch_bounds__(256) void k_prep_kv(const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
                                                 const uint16_t* __restrict__ wk, uint16_t* __restrict__ khat,
                                                 uint16_t* __restrict__ v16, int64_t T, int32_t H, float eps,
-                                                WsHeader* hdr) {
+                                                WsHeader* hdr, const int32_t* __restrict__ slot) {
   const int64_t g = (int64_t)blockIdx.x * 256 + threadIdx.x;
   const int64_t row = g >> 4;
   const int c = threadIdx.x & 15;
@@ -51,7 +51,8 @@ __global__ __launch_bounds__(256) void k_prep_kv(const uint16_t* __restrict__ k,
   const bool valid = row < rows;
   const int64_t t = valid ? row / H : 0;
   const int64_t h = valid ? row - t * H : 0;
-  const int64_t dst = (h * T + t) * HD + c * 8;
+  const int64_t ts = slot ? (int64_t)slot[t] : t;  // slot[t] is in [0, T) by construction
+  const int64_t dst = (h * T + ts) * HD + c * 8;
 
   u32x4 kv = {0, 0, 0, 0}, vv = {0, 0, 0, 0};
   if (valid) {
@@ -79,8 +80,8 @@ __global__ __launch_bounds__(256) void k_prep_kv(const uint16_t* __restrict__ k,
 }
 
 // Operand staging of the backward: per (token, head) row, the normed q and k (the forward's exact
-// bits) in bf16 and fp16, v and dO in bf16, dO in fp16, all head-major; the forward's LSE in log2
-// units.  A finite value beyond the fp16 range in a converted operand sets STATUS_RANGE_BIT.
+// bits), v and dO, all in fp16 and head-major; the forward's LSE in log2 units.  A finite value
+// beyond the fp16 range in a converted operand sets STATUS_RANGE_BIT.
 struct BwdPrepParams {
   const uint16_t* q;
   const uint16_t* k;
@@ -94,6 +95,7 @@ struct BwdPrepParams {
   uint16_t* v16;
   uint16_t* do16;
   float* lse2;
+  const int32_t* slot;  // staged row of each token (position order), or NULL for packed order
   WsHeader* hdr;
   int64_t T;
   int32_t H;
@@ -126,7 +128,8 @@ __global__ __launch_bounds__(256) void k_bwd_prep(BwdPrepParams p) {
   const bool valid = row < rows;
   const int64_t t = valid ? row / p.H : 0;
   const int64_t h = valid ? row - t * p.H : 0;
-  const int64_t dst = (h * p.T + t) * HD + c * 8;
+  const int64_t ts = p.slot ? (int64_t)p.slot[t] : t;
+  const int64_t dst = (h * p.T + ts) * HD + c * 8;
 
   u32x4 qv = {0, 0, 0, 0}, kv = {0, 0, 0, 0}, vv = {0, 0, 0, 0}, gv = {0, 0, 0, 0};
   if (valid) {
@@ -147,7 +150,7 @@ __global__ __launch_bounds__(256) void k_bwd_prep(BwdPrepParams p) {
     st16(p.khat16 + dst, k16);
     st16(p.v16 + dst, v16);
     st16(p.do16 + dst, g16);
-    if (c == 0) p.lse2[h * p.T + t] = p.lse[t * p.H + h] * 1.44269504088896340736f;
+    if (c == 0) p.lse2[h * p.T + ts] = p.lse[t * p.H + h] * 1.44269504088896340736f;
   }
   const uint64_t any_over = __ballot(valid && over);
   if (any_over && (threadIdx.x & 63) == __builtin_ctzll(any_over)) atomicOr(&p.hdr->status, STATUS_RANGE_BIT);
@@ -157,7 +160,7 @@ static inline unsigned grid_for_rows(int64_t rows) { return (unsigned)((rows * 1
 
 hipError_t launch_bwd_prep(const void* q, const void* k, const void* v, const void* dout, const float* lse,
                            const void* wq, const void* wk, int64_t T, int32_t H, float eps, void* ws,
-                           hipStream_t stream) {
+                           const int32_t* slot, hipStream_t stream) {
   const int64_t rows = T * H;
   if (rows == 0) return hipSuccess;
   const BwdLayout L = bwd_layout(T, H);
@@ -175,6 +178,7 @@ hipError_t launch_bwd_prep(const void* q, const void* k, const void* v, const vo
   p.v16 = (uint16_t*)(base + L.v16);
   p.do16 = (uint16_t*)(base + L.do16);
   p.lse2 = (float*)(base + L.lse2);
+  p.slot = slot;
   p.hdr = (WsHeader*)base;
   p.T = T;
   p.H = H;
@@ -192,14 +196,14 @@ hipError_t launch_qknorm(const void* x, const void* w, void* y, int64_t T, int32
 }
 
 hipError_t launch_prep_kv(const void* k, const void* v, const void* wk, int64_t T, int32_t H, float eps, void* ws,
-                          hipStream_t stream) {
+                          const int32_t* slot, hipStream_t stream) {
   const int64_t rows = T * H;
   if (rows == 0) return hipSuccess;
   const WsLayout L = ws_layout(T, H);
   char* base = (char*)ws;
   hipLaunchKernelGGL(k_prep_kv, dim3(grid_for_rows(rows)), dim3(256), 0, stream, (const uint16_t*)k,
                      (const uint16_t*)v, (const uint16_t*)wk, (uint16_t*)(base + L.khat), (uint16_t*)(base + L.v16),
-                     T, H, eps, (WsHeader*)base);
+                     T, H, eps, (WsHeader*)base, slot);
   return hipGetLastError();
 }
 

@@ -40,8 +40,9 @@
  *
  * Errors are fail-closed, never a fallback.  Argument errors are returned synchronously before any
  * work is enqueued.  Data errors that only the device can see (decreasing segment ids, a V value
- * outside fp16 range) are recorded in the workspace's status word; the attention output is then
- * filled with NaN so it cannot be mistaken for a valid result, and h3attn_status_read reports it.
+ * outside fp16 range, position ids that are not a permutation) are recorded in the workspace's
+ * status word; the attention output is then filled with NaN so it cannot be mistaken for a valid
+ * result, and h3attn_status_read reports it.
  */
 #ifndef H3ATTN_H
 #define H3ATTN_H
@@ -53,7 +54,7 @@
 extern "C" {
 #endif
 
-#define H3ATTN_VERSION 1
+#define H3ATTN_VERSION 2
 
 enum {
   H3ATTN_OK = 0,
@@ -65,7 +66,8 @@ enum {
   H3ATTN_ERR_DEVICE = 6,    /* no current device, or it is not gfx950 */
   H3ATTN_ERR_LAUNCH = 7,    /* the HIP runtime rejected a launch */
   H3ATTN_ERR_SEGMENTS = 8,  /* device status: segment ids decrease somewhere */
-  H3ATTN_ERR_RANGE = 9      /* device status: a finite value > 65504 cannot enter an fp16 product */
+  H3ATTN_ERR_RANGE = 9,     /* device status: a finite value > 65504 cannot enter an fp16 product */
+  H3ATTN_ERR_POSITIONS = 10 /* device status: position ids are not a permutation of 0..L-1 in a segment */
 };
 
 /* H3ATTN_VERSION of the loaded library. */
@@ -74,10 +76,10 @@ int h3attn_version(void);
 /* Static, NUL-terminated description of a status code (never NULL). */
 const char* h3attn_strerror(int status);
 
-/* Bytes of device workspace that h3attn_fwd (and the staged calls) need for `tokens` x `heads`:
- * a 256-byte header (status word, counts), the segment table and work list (O(tokens) int32), and
- * the normed K and fp16 V in head-major layout (2 * tokens * heads * 256 bytes).  Returns 0 for
- * invalid sizes. */
+/* Bytes of device workspace that h3attn_fwd, h3attn_fwd_pos and the staged calls need for
+ * `tokens` x `heads`: a 256-byte header (status word, counts), the segment table and work list
+ * (O(tokens) int32), the normed K and fp16 V in head-major layout (2 * tokens * heads * 256 bytes)
+ * and the two int32 [tokens] maps of the position order.  Returns 0 for invalid sizes. */
 size_t h3attn_workspace_bytes(int64_t tokens, int32_t heads);
 
 /* The q_norm / k_norm node on its own: y = RMSNorm(x) * w per (token, head) row, as defined above,
@@ -97,6 +99,21 @@ int h3attn_fwd(const void* q, const void* k, const void* v, const int32_t* seg_i
                const void* wk, int64_t tokens, int32_t heads, int32_t head_dim, float eps, float scale, void* out,
                float* lse, void* workspace, size_t workspace_bytes, void* stream);
 
+/* h3attn_fwd with the keys of each segment walked in position order instead of packed order.  The
+ * "ws1_one_h3_block + full-model qualification" page (Results, control H-C3) reports that permuting
+ * the packed rows together with their positions changes output bits, because attention adds keys
+ * in packed order, and leaves that to the attention.  Here the order of the
+ * sums follows the positions, so permuting the tokens of a segment together with their position
+ * ids permutes the output rows and changes no bit of them.
+ *   pos_ids: int32 [T] device memory, 4-byte aligned: the position of each token within its
+ *     segment; the ids of a segment of L tokens must be a permutation of 0..L-1.  Anything else
+ *     sets H3ATTN_ERR_POSITIONS in the status word and NaN-fills the outputs (checked on the device).
+ * With pos_ids[t] = t - (start of t's segment) the result is bitwise that of h3attn_fwd.  Other
+ * arguments as for h3attn_fwd; out and lse must not overlap pos_ids either. */
+int h3attn_fwd_pos(const void* q, const void* k, const void* v, const int32_t* seg_ids, const int32_t* pos_ids,
+                   const void* wq, const void* wk, int64_t tokens, int32_t heads, int32_t head_dim, float eps,
+                   float scale, void* out, float* lse, void* workspace, size_t workspace_bytes, void* stream);
+
 /* The three stages of h3attn_fwd, for callers that reuse one segment plan across layers (the 50
  * blocks of the model share the packed layout) or time the stages.  They must be enqueued in this
  * order on one stream with one workspace: h3attn_plan (resets the status word), h3attn_prep_kv,
@@ -108,11 +125,12 @@ int h3attn_prep_kv(const void* k, const void* v, const void* wk, int64_t tokens,
 int h3attn_attend(const void* q, const void* wq, int64_t tokens, int32_t heads, int32_t head_dim, float eps,
                   float scale, void* out, float* lse, void* workspace, size_t workspace_bytes, void* stream);
 
-/* Bytes of device workspace that h3attn_bwd needs for `tokens` x `heads`: the header, the segment
- * table and work list (128-token tiles), four head-major fp16 staged operands (normed q and k, v,
- * dO: 4 * tokens * heads * 256 bytes), the log-sum-exp and D rows (2 * tokens * heads * 4 bytes),
- * the fp32 gradients with respect to the normed q and k (2 * tokens * heads * 512 bytes) and the
- * norm-weight gradient partials.  0 if invalid. */
+/* Bytes of device workspace that h3attn_bwd and h3attn_bwd_pos need for `tokens` x `heads`: the
+ * header, the segment table and work list (128-token tiles), four head-major fp16 staged operands
+ * (normed q and k, v, dO: 4 * tokens * heads * 256 bytes), the log-sum-exp and D rows
+ * (2 * tokens * heads * 4 bytes), the fp32 gradients with respect to the normed q and k
+ * (2 * tokens * heads * 512 bytes), the norm-weight gradient partials and the two int32 [tokens]
+ * maps of the position order.  0 if invalid. */
 size_t h3attn_bwd_workspace_bytes(int64_t tokens, int32_t heads);
 
 /* Backward of the node: gradients of sum(dout * out) with respect to q, k, v and the two norm
@@ -136,9 +154,22 @@ int h3attn_bwd(const void* dout, const void* q, const void* k, const void* v, co
                int32_t head_dim, float eps, float scale, void* dq, void* dk, void* dv, float* dwq, float* dwk,
                void* workspace, size_t workspace_bytes, void* stream);
 
+/* h3attn_bwd in position order (see h3attn_fwd_pos): the operands are staged by position, so the
+ * sums over keys (dq), over queries (dk, dv) and over rows (dwq, dwk) run in position order.
+ * Permuting the tokens of a segment together with their position ids permutes the gradient rows
+ * of q, k and v and changes no bit of them or of dwq and dwk.  pos_ids as for h3attn_fwd_pos (an
+ * invalid set gives H3ATTN_ERR_POSITIONS and NaN outputs); lse is the forward's, in packed token
+ * order as either forward writes it.  With pos_ids[t] = t - (start of t's segment) the result is
+ * bitwise that of h3attn_bwd.  Outputs must not overlap pos_ids either. */
+int h3attn_bwd_pos(const void* dout, const void* q, const void* k, const void* v, const float* lse,
+                   const int32_t* seg_ids, const int32_t* pos_ids, const void* wq, const void* wk, int64_t tokens,
+                   int32_t heads, int32_t head_dim, float eps, float scale, void* dq, void* dk, void* dv, float* dwq,
+                   float* dwk, void* workspace, size_t workspace_bytes, void* stream);
+
 /* Wait for `stream`, then copy the workspace's device status word to *device_status (host memory):
- * H3ATTN_OK, H3ATTN_ERR_SEGMENTS or H3ATTN_ERR_RANGE (segments first if both).  Returns the HIP
- * copy's status (H3ATTN_OK or H3ATTN_ERR_LAUNCH). */
+ * H3ATTN_OK, H3ATTN_ERR_SEGMENTS, H3ATTN_ERR_POSITIONS or H3ATTN_ERR_RANGE (in this order of
+ * precedence when several are recorded).  Returns the HIP copy's status (H3ATTN_OK or
+ * H3ATTN_ERR_LAUNCH). */
 int h3attn_status_read(const void* workspace, int32_t* device_status, void* stream);
 
 #ifdef __cplusplus

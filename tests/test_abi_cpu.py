@@ -22,15 +22,15 @@ def declared_functions():
 def test_every_declared_symbol_is_exported():
     lib = h3.load()
     names = declared_functions()
-    assert len(names) == 11
+    assert len(names) == 13
     for n in names:
         assert hasattr(lib, n), f"{n} missing from libh3attn.so"
     assert sorted(h3.EXPORTS) == names
 
 
 def test_version_and_strerror():
-    assert h3.h3attn_version() == 1
-    for code in range(10):
+    assert h3.h3attn_version() == 2
+    for code in range(11):
         assert h3.h3attn_strerror(code)
     assert h3.h3attn_strerror(999) == "unknown status"
 
@@ -115,6 +115,34 @@ def bwd(lib, dout=A + 0x7000000, q=A, k=A + 0x1000000, v=A + 0x2000000, lse=A + 
     return lib.h3attn_bwd(dout, q, k, v, lse, seg, wq, wk, T, H, D, eps, scale, dq, dk, dv, dwq, dwk, ws, wsb, None)
 
 
+def fwd_pos(lib, pos=A + 0xD000000, q=A, k=A + 0x1000000, v=A + 0x2000000, seg=A + 0x3000000, wq=A + 0x4000000,
+            wk=A + 0x4001000, T=16, H=2, D=128, eps=1e-6, scale=0.088, out=A + 0x5000000, lse=None, ws=A + 0x6000000,
+            wsb=None):
+    if wsb is None:
+        wsb = h3.h3attn_workspace_bytes(T, H) if T >= 0 and H >= 1 else 0
+    return lib.h3attn_fwd_pos(q, k, v, seg, pos, wq, wk, T, H, D, eps, scale, out, lse, ws, wsb, None)
+
+
+def test_fwd_pos_argument_errors():
+    lib = h3.load()
+    assert fwd_pos(lib, T=0) == h3.H3ATTN_OK
+    assert fwd_pos(lib, pos=None) == h3.H3ATTN_ERR_NULL
+    assert fwd_pos(lib, pos=A + 0xD000002) == h3.H3ATTN_ERR_ALIGN
+    assert fwd_pos(lib, out=A + 0xD000000 - 64) == h3.H3ATTN_ERR_ALIAS     # out runs into pos_ids
+    assert fwd_pos(lib, lse=A + 0xD000000 + 16) == h3.H3ATTN_ERR_ALIAS     # lse overlaps pos_ids
+    assert fwd_pos(lib, pos=A + 0x6000000 + 256) == h3.H3ATTN_ERR_ALIAS    # pos_ids inside the workspace
+    assert fwd_pos(lib, D=64) == h3.H3ATTN_ERR_SHAPE
+    assert fwd_pos(lib, wq=None) == h3.H3ATTN_ERR_NULL
+    # the position order needs the two int32 [T] maps beyond the plain forward's workspace
+    full = h3.h3attn_workspace_bytes(16, 2)
+    assert fwd_pos(lib, wsb=full - 512) == h3.H3ATTN_ERR_WORKSPACE
+    import torch
+    if not torch.cuda.is_available():
+        assert fwd(lib, wsb=full - 512) == h3.H3ATTN_ERR_DEVICE   # enough for the plain forward
+        assert fwd_pos(lib) == h3.H3ATTN_ERR_DEVICE
+        assert fwd_pos(lib, wq=None, wk=None) == h3.H3ATTN_ERR_DEVICE
+
+
 def test_bwd_workspace_bytes():
     n = h3.h3attn_bwd_workspace_bytes(8506, 40)
     assert n >= 7 * 8506 * 40 * 256 + 2 * 8506 * 40 * 4 and n % 256 == 0
@@ -142,3 +170,31 @@ def test_bwd_argument_errors():
     if not torch.cuda.is_available():
         assert bwd(lib) == h3.H3ATTN_ERR_DEVICE
         assert bwd(lib, wq=None, wk=None, dwq=None, dwk=None) == h3.H3ATTN_ERR_DEVICE
+
+
+def bwd_pos(lib, pos=A + 0xD000000, T=16, H=2, wsb=None, **kw):
+    args = dict(dout=A + 0x7000000, q=A, k=A + 0x1000000, v=A + 0x2000000, lse=A + 0x8000000, seg=A + 0x3000000,
+                wq=A + 0x4000000, wk=A + 0x4001000, D=128, eps=1e-6, scale=0.088, dq=A + 0x9000000, dk=A + 0xA000000,
+                dv=A + 0xB000000, dwq=A + 0xC000000, dwk=A + 0xC001000, ws=A + 0x10000000)
+    args.update(kw)
+    if wsb is None:
+        wsb = h3.h3attn_bwd_workspace_bytes(T, H) if T >= 0 and H >= 1 else 0
+    a = args
+    return lib.h3attn_bwd_pos(a["dout"], a["q"], a["k"], a["v"], a["lse"], a["seg"], pos, a["wq"], a["wk"], T, H,
+                              a["D"], a["eps"], a["scale"], a["dq"], a["dk"], a["dv"], a["dwq"], a["dwk"], a["ws"], wsb,
+                              None)
+
+
+def test_bwd_pos_argument_errors():
+    lib = h3.load()
+    assert bwd_pos(lib, T=0) == h3.H3ATTN_OK
+    assert bwd_pos(lib, pos=None) == h3.H3ATTN_ERR_NULL
+    assert bwd_pos(lib, pos=A + 0xD000001) == h3.H3ATTN_ERR_ALIGN
+    assert bwd_pos(lib, dq=A + 0xD000000) == h3.H3ATTN_ERR_ALIAS           # an output on pos_ids
+    assert bwd_pos(lib, pos=A + 0x10000000 + 1024) == h3.H3ATTN_ERR_ALIAS  # pos_ids inside the workspace
+    full = h3.h3attn_bwd_workspace_bytes(16, 2)
+    assert bwd_pos(lib, wsb=full - 512) == h3.H3ATTN_ERR_WORKSPACE
+    import torch
+    if not torch.cuda.is_available():
+        assert bwd(lib, wsb=full - 512) == h3.H3ATTN_ERR_DEVICE   # enough for the plain backward
+        assert bwd_pos(lib) == h3.H3ATTN_ERR_DEVICE

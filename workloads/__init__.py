@@ -86,6 +86,23 @@ def segment_ids(seg_lens) -> torch.Tensor:
     return torch.cat(ids) if ids else torch.zeros(0, dtype=torch.int32)
 
 
+def position_ids(seg_lens) -> torch.Tensor:
+    """int32 [T]: each token's position within its segment, 0..L-1 in packing order."""
+    ids = [torch.arange(L, dtype=torch.int32) for L in seg_lens]
+    return torch.cat(ids) if ids else torch.zeros(0, dtype=torch.int32)
+
+
+def shuffle_within_segments(seg_lens, seed: int) -> torch.Tensor:
+    """int64 [T]: a seeded permutation p of the token axis that keeps every token in its segment;
+    row i of the shuffled batch is row p[i] of the original (take q[p], k[p], v[p], positions[p])."""
+    g = torch.Generator().manual_seed(seed)
+    parts, t0 = [], 0
+    for L in seg_lens:
+        parts.append(t0 + torch.randperm(L, generator=g))
+        t0 += L
+    return torch.cat(parts) if parts else torch.zeros(0, dtype=torch.int64)
+
+
 def make_inputs(w: Workload, with_grad: bool = False) -> dict:
     """CPU tensors: q, k, v bf16 [T, H, 128]; seg int32 [T]; wq, wk bf16 [128] or None; dout if asked."""
     g = torch.Generator().manual_seed(w.seed)
