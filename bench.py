@@ -1,7 +1,7 @@
 """Throughput of the H3 attention node on one MI355X.
 
-Forward (default): one step = one h3attn_fwd call (segment plan, K norm + fp16 V staging, attention
-with the fused Q norm) over the full workload, inputs resident in HBM.  Prints ONE JSON line:
+Forward (default): one step = one h3attn_fwd call (segment plan, Q and K norm + fp16 V staging,
+attention) over the full workload, inputs resident in HBM.  Prints ONE JSON line:
   value     whole-step attention TFLOP/s (nominal 4 * sum(L^2) * H * 128 FLOPs per step)
   roofline  the attention kernel alone (h3attn_attend), timed per launch with HIP events on the
             launch stream, against the bf16/fp16 dense MFMA peak (2516.6 TFLOP/s)
@@ -137,7 +137,7 @@ def main():
 
     # ---- the dominant kernel alone: attention launches, one event pair each, on the launch stream
     h3.h3attn_plan(g["seg"], H, ws, stream=stream)
-    h3.h3attn_prep_kv(g["k"], g["v"], g["wk"], ws, eps=wl.eps, stream=stream)
+    h3.h3attn_prep_qkv(g["q"], g["k"], g["v"], g["wq"], g["wk"], ws, eps=wl.eps, stream=stream)
     for _ in range(2):
         h3.h3attn_attend(g["q"], g["wq"], ws, out, eps=wl.eps, scale=wl.scale, stream=stream)
     torch.cuda.synchronize()

@@ -30,7 +30,7 @@ H3ATTN_ERR_POSITIONS = 10
 
 # every symbol the header declares
 EXPORTS = ("h3attn_version", "h3attn_strerror", "h3attn_workspace_bytes", "h3attn_qknorm", "h3attn_fwd",
-           "h3attn_fwd_pos", "h3attn_plan", "h3attn_prep_kv", "h3attn_attend", "h3attn_status_read",
+           "h3attn_fwd_pos", "h3attn_plan", "h3attn_prep_qkv", "h3attn_attend", "h3attn_status_read",
            "h3attn_bwd_workspace_bytes", "h3attn_bwd", "h3attn_bwd_pos")
 
 
@@ -61,14 +61,14 @@ def load():
     lib.h3attn_fwd.argtypes = [P, P, P, P, P, P, I64, I32, I32, F, F, P, P, P, SZ, P]
     lib.h3attn_fwd_pos.argtypes = [P, P, P, P, P, P, P, I64, I32, I32, F, F, P, P, P, SZ, P]
     lib.h3attn_plan.argtypes = [P, I64, I32, P, SZ, P]
-    lib.h3attn_prep_kv.argtypes = [P, P, P, I64, I32, I32, F, P, SZ, P]
+    lib.h3attn_prep_qkv.argtypes = [P, P, P, P, P, I64, I32, I32, F, P, SZ, P]
     lib.h3attn_attend.argtypes = [P, P, I64, I32, I32, F, F, P, P, P, SZ, P]
     lib.h3attn_status_read.argtypes = [P, ctypes.POINTER(ctypes.c_int32), P]
     lib.h3attn_bwd_workspace_bytes.argtypes = [I64, I32]
     lib.h3attn_bwd_workspace_bytes.restype = SZ
     lib.h3attn_bwd.argtypes = [P, P, P, P, P, P, P, P, I64, I32, I32, F, F, P, P, P, P, P, P, SZ, P]
     lib.h3attn_bwd_pos.argtypes = [P, P, P, P, P, P, P, P, P, I64, I32, I32, F, F, P, P, P, P, P, P, SZ, P]
-    for name in ("h3attn_qknorm", "h3attn_fwd", "h3attn_fwd_pos", "h3attn_plan", "h3attn_prep_kv", "h3attn_attend",
+    for name in ("h3attn_qknorm", "h3attn_fwd", "h3attn_fwd_pos", "h3attn_plan", "h3attn_prep_qkv", "h3attn_attend",
                  "h3attn_status_read", "h3attn_bwd", "h3attn_bwd_pos"):
         getattr(lib, name).restype = ctypes.c_int
     _lib = lib
@@ -179,11 +179,11 @@ def h3attn_plan(seg_ids, heads: int, workspace_buf, stream=None):
     _check(rc, "h3attn_plan")
 
 
-def h3attn_prep_kv(k, v, wk, workspace_buf, eps: float = 1e-6, stream=None):
+def h3attn_prep_qkv(q, k, v, wq, wk, workspace_buf, eps: float = 1e-6, stream=None):
     T, H, D = _shape(k)
-    rc = load().h3attn_prep_kv(_ptr(k), _ptr(v), _ptr(wk), T, H, D, float(eps), _ptr(workspace_buf),
-                               workspace_buf.numel(), _stream(stream, k.device))
-    _check(rc, "h3attn_prep_kv")
+    rc = load().h3attn_prep_qkv(_ptr(q), _ptr(k), _ptr(v), _ptr(wq), _ptr(wk), T, H, D, float(eps),
+                                _ptr(workspace_buf), workspace_buf.numel(), _stream(stream, k.device))
+    _check(rc, "h3attn_prep_qkv")
 
 
 def h3attn_attend(q, wq, workspace_buf, out, lse=None, eps: float = 1e-6, scale: float | None = None, stream=None):

@@ -18,6 +18,7 @@ constexpr int BK = 64;   // keys per KV tile; the KV walk is in these tiles, asc
 // items               int32 [2*(T + ceil(T/BQ))]: (segment, q-tile) work items
 // khat                bf16 [H][T][128]: normed K (head-major, so a KV tile is contiguous)
 // v16                 fp16 [H][T][128]: V converted to fp16 (head-major)
+// qhat                bf16 [H][T][128]: normed Q (head-major, packed token order), with norm weights
 struct WsHeader {
   int32_t status;  // OR of STATUS_* bits; reset by the plan kernel
   int32_t nseg;
@@ -32,7 +33,7 @@ constexpr int32_t STATUS_SEG_BIT = 1;    // segment ids decrease
 constexpr int32_t STATUS_RANGE_BIT = 2;  // a finite |v| exceeds the fp16 range
 
 struct WsLayout {
-  size_t segtab, items, khat, v16, total;
+  size_t segtab, items, khat, v16, qhat, total;
   int64_t max_items;
 };
 
@@ -45,7 +46,8 @@ __host__ __device__ inline WsLayout ws_layout(int64_t T, int32_t H) {
   w.items = w.segtab + align256((size_t)T * 8);
   w.khat = w.items + align256((size_t)w.max_items * 8);
   w.v16 = w.khat + align256((size_t)T * H * HD * 2);
-  w.total = w.v16 + align256((size_t)T * H * HD * 2);
+  w.qhat = w.v16 + align256((size_t)T * H * HD * 2);
+  w.total = w.qhat + align256((size_t)T * H * HD * 2);
   return w;
 }
 

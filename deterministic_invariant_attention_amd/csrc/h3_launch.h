@@ -13,20 +13,21 @@ hipError_t launch_plan(const int32_t* seg, int64_t T, void* ws, int32_t H, hipSt
 // Standalone q/k RMSNorm of [T, H, 128] bf16 rows (y may equal x).
 hipError_t launch_qknorm(const void* x, const void* w, void* y, int64_t T, int32_t H, float eps, hipStream_t stream);
 
-// K -> normed bf16 K (or a copy when wk is NULL) and V -> fp16, both head-major, into the workspace;
-// token t's rows go to staged row slot[t] (position order) or, with slot NULL, to row t.
-hipError_t launch_prep_kv(const void* k, const void* v, const void* wk, int64_t T, int32_t H, float eps, void* ws,
-                          const int32_t* slot, hipStream_t stream);
+// Q -> normed bf16 Q (only with wq; head-major, packed token order), K -> normed bf16 K (or a copy
+// when wk is NULL) and V -> fp16, both head-major at staged row slot[t] (position order) or, with
+// slot NULL, at row t; all into the workspace.
+hipError_t launch_prep_qkv(const void* q, const void* k, const void* v, const void* wq, const void* wk, int64_t T,
+                           int32_t H, float eps, void* ws, const int32_t* slot, hipStream_t stream);
 
 // Position ids -> slot / inv maps of the ordering area, with the permutation check (STATUS_POS_BIT).
 // Needs the plan's segment table.
 hipError_t launch_order(const int32_t* pos, int64_t T, void* ws, const int32_t* segtab, int32_t* slot, int32_t* inv,
                         hipStream_t stream);
 
-// Attention over the planned work items with the Q norm fused into the load prologue.
-// grid_cap: most workgroups to launch (persistent grid).
-hipError_t launch_attend(const void* q, const void* wq, int64_t T, int32_t H, float eps, float scale, void* out,
-                         float* lse, void* ws, int grid_cap, hipStream_t stream);
+// Attention over the planned work items.  Queries: the staged normed Q when normed is true, else
+// the caller's q (token-major).  grid_cap: most workgroups to launch (persistent grid).
+hipError_t launch_attend(const void* q, bool normed, int64_t T, int32_t H, float scale, void* out, float* lse,
+                         void* ws, int grid_cap, hipStream_t stream);
 
 // Backward: segment decode with 128-token tiles into the backward workspace.
 hipError_t launch_plan_bwd(const int32_t* seg, int64_t T, void* ws, int32_t H, hipStream_t stream);

@@ -133,14 +133,17 @@ static int check_plan(const int32_t* seg_ids, int64_t tokens, int32_t heads, voi
   return H3ATTN_OK;
 }
 
-static int check_prep(const void* k, const void* v, const void* wk, int64_t tokens, int32_t heads, float eps,
-                      void* workspace, size_t workspace_bytes) {
+static int check_prep(const void* q, const void* k, const void* v, const void* wq, const void* wk, int64_t tokens,
+                      int32_t heads, float eps, void* workspace, size_t workspace_bytes) {
+  if ((wq == nullptr) != (wk == nullptr)) return H3ATTN_ERR_NULL;
   if (wk && (!(eps > 0.0f) || !std::isfinite(eps))) return H3ATTN_ERR_SHAPE;
-  if (!k || !v || !workspace) return H3ATTN_ERR_NULL;
-  if (!aligned(k, 16) || !aligned(v, 16) || (wk && !aligned(wk, 16)) || !aligned(workspace, 256))
+  if (!q || !k || !v || !workspace) return H3ATTN_ERR_NULL;
+  if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || (wq && !aligned(wq, 16)) || (wk && !aligned(wk, 16)) ||
+      !aligned(workspace, 256))
     return H3ATTN_ERR_ALIGN;
   const size_t n = tensor_bytes(tokens, heads);
-  if (overlap(k, n, workspace, workspace_bytes) || overlap(v, n, workspace, workspace_bytes) ||
+  if (overlap(q, n, workspace, workspace_bytes) || overlap(k, n, workspace, workspace_bytes) ||
+      overlap(v, n, workspace, workspace_bytes) || overlap(wq, HD * 2, workspace, workspace_bytes) ||
       overlap(wk, HD * 2, workspace, workspace_bytes))
     return H3ATTN_ERR_ALIAS;
   if (workspace_bytes < ws_layout(tokens, heads).total) return H3ATTN_ERR_WORKSPACE;
@@ -176,15 +179,15 @@ int h3attn_plan(const int32_t* seg_ids, int64_t tokens, int32_t heads, void* wor
   return launch_status(launch_plan(seg_ids, tokens, workspace, heads, (hipStream_t)stream));
 }
 
-int h3attn_prep_kv(const void* k, const void* v, const void* wk, int64_t tokens, int32_t heads, int32_t head_dim,
-                   float eps, void* workspace, size_t workspace_bytes, void* stream) {
+int h3attn_prep_qkv(const void* q, const void* k, const void* v, const void* wq, const void* wk, int64_t tokens,
+                    int32_t heads, int32_t head_dim, float eps, void* workspace, size_t workspace_bytes, void* stream) {
   int rc = check_shape(tokens, heads, head_dim);
   if (rc) return rc;
   if (tokens == 0) return H3ATTN_OK;
-  if ((rc = check_prep(k, v, wk, tokens, heads, eps, workspace, workspace_bytes))) return rc;
+  if ((rc = check_prep(q, k, v, wq, wk, tokens, heads, eps, workspace, workspace_bytes))) return rc;
   DeviceInfo di;
   if ((rc = device_info(&di))) return rc;
-  return launch_status(launch_prep_kv(k, v, wk, tokens, heads, eps, workspace, nullptr, (hipStream_t)stream));
+  return launch_status(launch_prep_qkv(q, k, v, wq, wk, tokens, heads, eps, workspace, nullptr, (hipStream_t)stream));
 }
 
 int h3attn_attend(const void* q, const void* wq, int64_t tokens, int32_t heads, int32_t head_dim, float eps,
@@ -196,7 +199,7 @@ int h3attn_attend(const void* q, const void* wq, int64_t tokens, int32_t heads, 
   DeviceInfo di;
   if ((rc = device_info(&di))) return rc;
   return launch_status(
-      launch_attend(q, wq, tokens, heads, eps, scale, out, lse, workspace, di.cus, (hipStream_t)stream));
+      launch_attend(q, wq != nullptr, tokens, heads, scale, out, lse, workspace, di.cus, (hipStream_t)stream));
 }
 
 // The forward; pos_ids NULL walks keys in packed order, else in position order.
@@ -212,7 +215,7 @@ static int fwd_impl(const void* q, const void* k, const void* v, const int32_t* 
   if (tokens == 0) return H3ATTN_OK;
   if (!q || !k || !v || !seg_ids || !out || !workspace || (ordered && !pos_ids)) return H3ATTN_ERR_NULL;
   if ((rc = check_plan(seg_ids, tokens, heads, workspace, workspace_bytes))) return rc;
-  if ((rc = check_prep(k, v, wk, tokens, heads, eps, workspace, workspace_bytes))) return rc;
+  if ((rc = check_prep(q, k, v, wq, wk, tokens, heads, eps, workspace, workspace_bytes))) return rc;
   if ((rc = check_attend(q, wq, tokens, heads, eps, scale, out, lse, workspace, workspace_bytes))) return rc;
   const size_t n = tensor_bytes(tokens, heads);
   const size_t nl = (size_t)tokens * heads * 4;
@@ -239,8 +242,8 @@ static int fwd_impl(const void* q, const void* k, const void* v, const int32_t* 
       (rc = launch_status(launch_order(pos_ids, tokens, workspace, (const int32_t*)(base + ws_layout(tokens, heads).segtab),
                                        slot, (int32_t*)(base + ol.inv), st))))
     return rc;
-  if ((rc = launch_status(launch_prep_kv(k, v, wk, tokens, heads, eps, workspace, slot, st)))) return rc;
-  return launch_status(launch_attend(q, wq, tokens, heads, eps, scale, out, lse, workspace, di.cus, st));
+  if ((rc = launch_status(launch_prep_qkv(q, k, v, wq, wk, tokens, heads, eps, workspace, slot, st)))) return rc;
+  return launch_status(launch_attend(q, wq != nullptr, tokens, heads, scale, out, lse, workspace, di.cus, st));
 }
 
 int h3attn_fwd(const void* q, const void* k, const void* v, const int32_t* seg_ids, const void* wq, const void* wk,

@@ -1,6 +1,6 @@
 // Forward attention of the H3 node: non-causal softmax attention inside each packed segment
-// ("ws1_one_h3_block" page, Bindings table: attention with causal=False over packed layouts), with
-// the q RMSNorm fused into the Q load prologue, FP32 accumulation and one bf16 rounding of the
+// ("ws1_one_h3_block" page, Bindings table: attention with causal=False over packed layouts) on the
+// normed Q and K that the staging kernel wrote, FP32 accumulation and one bf16 rounding of the
 // output ("33B forward/backward" page, Scope: strict mode).
 //
 // Work item = (segment, 256-query tile, head); a persistent grid of one workgroup per CU walks the
@@ -52,8 +52,9 @@ static_assert(BK == TILE_ROWS, "one LDS tile per KV tile of two 32-key blocks");
 static_assert(BQ == 32 * NWAVES, "one 32-query block per wave");
 
 struct AttnParams {
-  const uint16_t* q;
-  const uint16_t* wq;
+  const uint16_t* q;  // normed Q (head-major) or the caller's q (token-major): element (t, h, d) at
+  int64_t q_rs;       // t * q_rs + h * q_hs + d
+  int64_t q_hs;
   const uint16_t* khat;
   const uint16_t* v16;
   uint16_t* out;
@@ -63,7 +64,6 @@ struct AttnParams {
   const int32_t* items;
   int64_t T;
   int32_t H;
-  float eps;
   float c;            // scale * log2(e)
   int32_t xcd_slots;  // workgroups per XCD (grid / 8), for the XCD-aware item order
 };
@@ -80,40 +80,16 @@ __device__ __forceinline__ float tile_max(const f32x16* S) {
   return __builtin_fmaxf(x, y);
 }
 
-// Q prologue for one 32-query block: load, RMSNorm (2 lanes per row), round to bf16 B-operands.
+// Q prologue for one 32-query block: the lane's 64 bf16 values of its query row (lane half hh
+// holds dims 16m + 8hh .. +7), which are the B operands as they are; zeros past the segment end.
 __device__ __forceinline__ void load_q(const AttnParams& p, int s0, int qrow, bool qvalid, int head, int hh,
                                        bf16x8* qf) {
-  float x[8][8];
-  const uint16_t* qp = p.q + ((int64_t)(s0 + (qvalid ? qrow : 0)) * p.H + head) * HD;
+  const uint16_t* qp = p.q + (int64_t)head * p.q_hs + (int64_t)(s0 + (qvalid ? qrow : 0)) * p.q_rs;
 #pragma unroll
   for (int m = 0; m < 8; m++) {
     u32x4 w4 = {0, 0, 0, 0};
     if (qvalid) w4 = *(const u32x4*)(qp + 16 * m + 8 * hh);
-    unpack8_bf16(w4, x[m]);
-  }
-  if (p.wq) {
-    double part[8];
-#pragma unroll
-    for (int m = 0; m < 8; m++) part[m] = chunk_sumsq(x[m]);
-    const double r = norm_rscale(row_total_2lanes(part), p.eps);
-#pragma unroll
-    for (int m = 0; m < 8; m++) {
-      float wf[8];
-      unpack8_bf16(*(const u32x4*)(p.wq + 16 * m + 8 * hh), wf);
-      qf[m] = __builtin_bit_cast(bf16x8, norm_chunk(x[m], wf, r));
-    }
-  } else {
-#pragma unroll
-    for (int m = 0; m < 8; m++) {
-      u32x4 o;
-#pragma unroll
-      for (int i = 0; i < 4; i++) o[i] = pack_bf16(x[m][2 * i], x[m][2 * i + 1]);
-      qf[m] = __builtin_bit_cast(bf16x8, o);
-    }
-  }
-  if (!qvalid) {
-#pragma unroll
-    for (int m = 0; m < 8; m++) qf[m] = __builtin_bit_cast(bf16x8, u32x4{0, 0, 0, 0});
+    qf[m] = __builtin_bit_cast(bf16x8, w4);
   }
 }
 
@@ -319,13 +295,14 @@ __global__ __launch_bounds__(64 * NWAVES, 1) void k_attn_fwd(AttnParams p) {
   }
 }
 
-hipError_t launch_attend(const void* q, const void* wq, int64_t T, int32_t H, float eps, float scale, void* out,
-                         float* lse, void* ws, int grid_cap, hipStream_t stream) {
+hipError_t launch_attend(const void* q, bool normed, int64_t T, int32_t H, float scale, void* out, float* lse,
+                         void* ws, int grid_cap, hipStream_t stream) {
   const WsLayout Lw = ws_layout(T, H);
   char* base = (char*)ws;
   AttnParams p;
-  p.q = (const uint16_t*)q;
-  p.wq = (const uint16_t*)wq;
+  p.q = normed ? (const uint16_t*)(base + Lw.qhat) : (const uint16_t*)q;
+  p.q_rs = normed ? HD : (int64_t)H * HD;
+  p.q_hs = normed ? T * HD : HD;
   p.khat = (const uint16_t*)(base + Lw.khat);
   p.v16 = (const uint16_t*)(base + Lw.v16);
   p.out = (uint16_t*)out;
@@ -335,7 +312,6 @@ hipError_t launch_attend(const void* q, const void* wq, int64_t T, int32_t H, fl
   p.items = (const int32_t*)(base + Lw.items);
   p.T = T;
   p.H = H;
-  p.eps = eps;
   p.c = (float)((double)scale * 1.4426950408889634074);
   // a multiple of 8 workgroups (one slot per XCD each), at most grid_cap and no more than the work
   const int64_t max_work = Lw.max_items * H;

@@ -1,12 +1,11 @@
 // The q_norm / k_norm node (RMSNorm over each 128-wide head, one 128-element weight shared by all
-// heads: "ws1_one_h3_block" page, Bindings table and Results) as a standalone kernel, the K/V
-// staging kernel of the attention (K normed with the same arithmetic, V converted to fp16) and the
-// operand staging kernel of the backward.
+// heads: "ws1_one_h3_block" page, Bindings table and Results) as a standalone kernel, the operand
+// staging kernel of the attention (Q and K normed with the same arithmetic, V converted to fp16)
+// and the operand staging kernel of the backward.
 //
 // Mapping: 16 lanes per (token, head) row, lane c holds channels 8c..8c+7 (one 16-byte chunk), so
 // each wave moves 4 rows with fully coalesced 16-byte accesses.  The sum of squares follows the
-// fixed tree of h3_common.h, so these kernels and the attention's fused Q prologue (2 lanes per
-// row) give identical bits.
+// fixed tree of h3_common.h, so every kernel here gives the bits of the standalone norm.
 #include "h3_common.h"
 #include "h3_bwd.h"
 #include "h3_launch.h"
@@ -38,28 +37,52 @@ __global__ __launch_bounds__(256) void k_qknorm(const uint16_t* x, const uint16_
   if (valid) st16(y + row * HD + c * 8, o);
 }
 
+// Operand staging of the attention.  With norm weights, Q is normed into qhat (head-major, packed
+// token order: the queries are walked in packed order); K is normed (or copied) and V converted to
+// fp16, both at the token's staged row (slot[t] in position order, else t), where the key walk
+// reads them.
+struct PrepParams {
+  const uint16_t* q;
+  const uint16_t* k;
+  const uint16_t* v;
+  const uint16_t* wq;  // NULL: Q is not staged (the attention reads the caller's q)
+  const uint16_t* wk;
+  uint16_t* qhat;
+  uint16_t* khat;
+  uint16_t* v16;
+  const int32_t* slot;  // staged row of each token (position order), or NULL for packed order
+  WsHeader* hdr;
+  int64_t T;
+  int32_t H;
+  float eps;
+};
+
 // rows are visited token-major (r = t*H + h) so the reads are contiguous; each row is written to
-// its head-major staged row (h*T + t, or h*T + slot[t] in position order).
-__global__ __launch_bounds__(256) void k_prep_kv(const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
-                                                const uint16_t* __restrict__ wk, uint16_t* __restrict__ khat,
-                                                uint16_t* __restrict__ v16, int64_t T, int32_t H, float eps,
-                                                WsHeader* hdr, const int32_t* __restrict__ slot) {
+// its head-major staged row.
+__global__ __launch_bounds__(256) void k_prep_qkv(PrepParams p) {
   const int64_t g = (int64_t)blockIdx.x * 256 + threadIdx.x;
   const int64_t row = g >> 4;
   const int c = threadIdx.x & 15;
-  const int64_t rows = T * H;
+  const int64_t T = p.T;
+  const int64_t rows = T * p.H;
   const bool valid = row < rows;
-  const int64_t t = valid ? row / H : 0;
-  const int64_t h = valid ? row - t * H : 0;
-  const int64_t ts = slot ? (int64_t)slot[t] : t;  // slot[t] is in [0, T) by construction
+  const int64_t t = valid ? row / p.H : 0;
+  const int64_t h = valid ? row - t * p.H : 0;
+  const int64_t ts = p.slot ? (int64_t)p.slot[t] : t;  // slot[t] is in [0, T) by construction
   const int64_t dst = (h * T + ts) * HD + c * 8;
 
+  if (p.wq) {
+    u32x4 qv = {0, 0, 0, 0};
+    if (valid) qv = ld16(p.q + row * HD + c * 8);
+    const u32x4 qo = norm_16lane(qv, p.wq, c, p.eps);
+    if (valid) st16(p.qhat + (h * T + t) * HD + c * 8, qo);
+  }
   u32x4 kv = {0, 0, 0, 0}, vv = {0, 0, 0, 0};
   if (valid) {
-    kv = ld16(k + row * HD + c * 8);
-    vv = ld16(v + row * HD + c * 8);
+    kv = ld16(p.k + row * HD + c * 8);
+    vv = ld16(p.v + row * HD + c * 8);
   }
-  const u32x4 ko = wk ? norm_16lane(kv, wk, c, eps) : kv;
+  const u32x4 ko = p.wk ? norm_16lane(kv, p.wk, c, p.eps) : kv;
 
   // V: bf16 -> fp16, exact for normal fp16 magnitudes; a finite |v| > 65504 would overflow.
   u32x4 vo;
@@ -72,11 +95,11 @@ __global__ __launch_bounds__(256) void k_prep_kv(const uint16_t* __restrict__ k,
     vo[i] = pack_f16(a, b);
   }
   if (valid) {
-    st16(khat + dst, ko);
-    st16(v16 + dst, vo);
+    st16(p.khat + dst, ko);
+    st16(p.v16 + dst, vo);
   }
   const uint64_t any_over = __ballot(valid && over);
-  if (any_over && (threadIdx.x & 63) == __builtin_ctzll(any_over)) atomicOr(&hdr->status, STATUS_RANGE_BIT);
+  if (any_over && (threadIdx.x & 63) == __builtin_ctzll(any_over)) atomicOr(&p.hdr->status, STATUS_RANGE_BIT);
 }
 
 // Operand staging of the backward: per (token, head) row, the normed q and k (the forward's exact
@@ -195,15 +218,27 @@ hipError_t launch_qknorm(const void* x, const void* w, void* y, int64_t T, int32
   return hipGetLastError();
 }
 
-hipError_t launch_prep_kv(const void* k, const void* v, const void* wk, int64_t T, int32_t H, float eps, void* ws,
-                          const int32_t* slot, hipStream_t stream) {
+hipError_t launch_prep_qkv(const void* q, const void* k, const void* v, const void* wq, const void* wk, int64_t T,
+                           int32_t H, float eps, void* ws, const int32_t* slot, hipStream_t stream) {
   const int64_t rows = T * H;
   if (rows == 0) return hipSuccess;
   const WsLayout L = ws_layout(T, H);
   char* base = (char*)ws;
-  hipLaunchKernelGGL(k_prep_kv, dim3(grid_for_rows(rows)), dim3(256), 0, stream, (const uint16_t*)k,
-                     (const uint16_t*)v, (const uint16_t*)wk, (uint16_t*)(base + L.khat), (uint16_t*)(base + L.v16),
-                     T, H, eps, (WsHeader*)base, slot);
+  PrepParams p;
+  p.q = (const uint16_t*)q;
+  p.k = (const uint16_t*)k;
+  p.v = (const uint16_t*)v;
+  p.wq = (const uint16_t*)wq;
+  p.wk = (const uint16_t*)wk;
+  p.qhat = (uint16_t*)(base + L.qhat);
+  p.khat = (uint16_t*)(base + L.khat);
+  p.v16 = (uint16_t*)(base + L.v16);
+  p.slot = slot;
+  p.hdr = (WsHeader*)base;
+  p.T = T;
+  p.H = H;
+  p.eps = eps;
+  hipLaunchKernelGGL(k_prep_qkv, dim3(grid_for_rows(rows)), dim3(256), 0, stream, p);
   return hipGetLastError();
 }
 

@@ -78,8 +78,9 @@ const char* h3attn_strerror(int status);
 
 /* Bytes of device workspace that h3attn_fwd, h3attn_fwd_pos and the staged calls need for
  * `tokens` x `heads`: a 256-byte header (status word, counts), the segment table and work list
- * (O(tokens) int32), the normed K and fp16 V in head-major layout (2 * tokens * heads * 256 bytes)
- * and the two int32 [tokens] maps of the position order.  Returns 0 for invalid sizes. */
+ * (O(tokens) int32), the normed Q and K and the fp16 V in head-major layout
+ * (3 * tokens * heads * 256 bytes) and the two int32 [tokens] maps of the position order.
+ * Returns 0 for invalid sizes. */
 size_t h3attn_workspace_bytes(int64_t tokens, int32_t heads);
 
 /* The q_norm / k_norm node on its own: y = RMSNorm(x) * w per (token, head) row, as defined above,
@@ -89,7 +90,7 @@ int h3attn_qknorm(const void* x, const void* w, void* y, int64_t tokens, int32_t
                   float eps, void* stream);
 
 /* Full forward of the attention node with its fused q/k norm:
- *   plan (segment decode) -> K norm + fp16 V staging -> attention with the Q norm in the load prologue.
+ *   plan (segment decode) -> Q and K norm + fp16 V staging -> attention.
  * wq and wk both NULL means q and k are already normalised (no norm is applied); exactly one NULL
  * is H3ATTN_ERR_NULL.  scale is the softmax scale (the H3 node uses 1/sqrt(128)); it must be finite
  * and > 0.  out must not overlap q, k, v, seg_ids, lse or the workspace.  workspace: device memory
@@ -116,12 +117,14 @@ int h3attn_fwd_pos(const void* q, const void* k, const void* v, const int32_t* s
 
 /* The three stages of h3attn_fwd, for callers that reuse one segment plan across layers (the 50
  * blocks of the model share the packed layout) or time the stages.  They must be enqueued in this
- * order on one stream with one workspace: h3attn_plan (resets the status word), h3attn_prep_kv,
- * h3attn_attend.  h3attn_fwd is exactly these three calls. */
+ * order on one stream with one workspace: h3attn_plan (resets the status word), h3attn_prep_qkv,
+ * h3attn_attend.  h3attn_fwd is exactly these three calls.  h3attn_prep_qkv norms q and k into the
+ * workspace (wq, wk both given) and converts v; h3attn_attend takes the same q and wq: with wq it
+ * reads the normed Q of the workspace (q and eps are then only checked), without it it reads q. */
 int h3attn_plan(const int32_t* seg_ids, int64_t tokens, int32_t heads, void* workspace, size_t workspace_bytes,
                 void* stream);
-int h3attn_prep_kv(const void* k, const void* v, const void* wk, int64_t tokens, int32_t heads, int32_t head_dim,
-                   float eps, void* workspace, size_t workspace_bytes, void* stream);
+int h3attn_prep_qkv(const void* q, const void* k, const void* v, const void* wq, const void* wk, int64_t tokens,
+                    int32_t heads, int32_t head_dim, float eps, void* workspace, size_t workspace_bytes, void* stream);
 int h3attn_attend(const void* q, const void* wq, int64_t tokens, int32_t heads, int32_t head_dim, float eps,
                   float scale, void* out, float* lse, void* workspace, size_t workspace_bytes, void* stream);
 

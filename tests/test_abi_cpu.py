@@ -99,7 +99,12 @@ def test_staged_calls_check_arguments():
     wsb = h3.h3attn_workspace_bytes(16, 2)
     assert lib.h3attn_plan(None, 16, 2, A, wsb, None) == h3.H3ATTN_ERR_NULL
     assert lib.h3attn_plan(A, 16, 2, A + 0x1000000, 8, None) == h3.H3ATTN_ERR_WORKSPACE
-    assert lib.h3attn_prep_kv(A, None, None, 16, 2, 128, 1e-6, A + 0x1000000, wsb, None) == h3.H3ATTN_ERR_NULL
+    assert lib.h3attn_prep_qkv(A, A, None, None, None, 16, 2, 128, 1e-6, A + 0x1000000, wsb, None) == h3.H3ATTN_ERR_NULL
+    assert lib.h3attn_prep_qkv(A, A, A, A + 0x100000, None, 16, 2, 128, 1e-6, A + 0x1000000, wsb,
+                               None) == h3.H3ATTN_ERR_NULL   # exactly one weight
+    assert lib.h3attn_prep_qkv(A, A, A, None, None, 16, 2, 128, 1e-6, A + 0x1000000, 64, None) == h3.H3ATTN_ERR_WORKSPACE
+    assert lib.h3attn_prep_qkv(A + 0x1000000 + 512, A, A, None, None, 16, 2, 128, 1e-6, A + 0x1000000, wsb,
+                               None) == h3.H3ATTN_ERR_ALIAS  # q inside the workspace
     assert lib.h3attn_attend(A, None, 16, 2, 128, 1e-6, -1.0, A + 0x100000, None, A + 0x1000000, wsb,
                              None) == h3.H3ATTN_ERR_SHAPE
     st = ctypes.c_int32(0)
