@@ -6,8 +6,9 @@ attention) over the full workload, inputs resident in HBM.  Prints ONE JSON line
   roofline  the attention kernel alone (h3attn_attend), timed per launch with HIP events on the
             launch stream, against the bf16/fp16 dense MFMA peak (2516.6 TFLOP/s)
   cpu_baseline  the FP64 CPU oracle on a bounded sample of query rows of the same workload
-Backward (--pass bwd, default workload batch2): one step = one h3attn_bwd call (plan, operand
-staging, dq with D, dk/dv, weight-gradient reduction) given dO and the forward's LSE; TFLOP/s on
+Backward (--pass bwd, default workload batch2): one step = one h3attn_bwd_ex call (plan, operand
+staging with D = dO . O, dq, dk/dv, weight-gradient reduction) given dO and the forward's LSE and
+fp32 output (--d-from recompute: D recomputed by the dq kernel instead, h3attn_bwd); TFLOP/s on
 the nominal 2.5 x forward FLOPs; the CPU baseline is the FP64 oracle's gradients on a subset of
 heads.
 --order position: the tokens of every segment are shuffled (seeded) and the step calls the
@@ -71,6 +72,9 @@ def main():
     ap.add_argument("--pass", dest="which", choices=("fwd", "bwd"), default="fwd")
     ap.add_argument("--order", choices=("packed", "position"), default="packed",
                     help="position: shuffle each segment's tokens and pass their position ids")
+    ap.add_argument("--d-from", dest="d_from", choices=("o32", "recompute"), default="o32",
+                    help="backward: D = dO . O from the forward's fp32 output (h3attn_bwd_ex), or recomputed "
+                         "from P and dP by the dq kernel (h3attn_bwd)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="target oracle time of the CPU sample")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -251,25 +255,17 @@ def bench_bwd(args, wl):
     log(f"workload {wl.name} backward: {wl.description}; nominal {flops:.4e} FLOP/step (2.5 x forward)")
     if args.copy_calibration:
         copy_calibration(dev)
-    if pos is None:
-        _, lse = h3.h3attn_fwd(g["q"], g["k"], g["v"], g["seg"], g["wq"], g["wk"], eps=wl.eps, scale=wl.scale,
-                               want_lse=True, stream=stream)
-    else:
-        _, lse = h3.h3attn_fwd_pos(g["q"], g["k"], g["v"], g["seg"], pos, g["wq"], g["wk"], eps=wl.eps,
-                                   scale=wl.scale, want_lse=True, stream=stream)
+    # the forward that precedes the backward (not timed): LSE, and the fp32 output when D comes from it
+    _, lse, o32 = h3.h3attn_fwd_ex(g["q"], g["k"], g["v"], g["seg"], pos, g["wq"], g["wk"], eps=wl.eps,
+                                   scale=wl.scale, want_lse=True, want_o32=args.d_from == "o32", stream=stream)
     ws = h3.bwd_workspace(T, H, dev)
     outs = [torch.empty_like(g["q"]) for _ in range(3)]
     dw = [torch.empty(128, dtype=torch.float32, device=dev) for _ in range(2)]
 
     def step():
-        if pos is None:
-            h3.h3attn_bwd(g["dout"], g["q"], g["k"], g["v"], lse, g["seg"], g["wq"], g["wk"], eps=wl.eps,
-                          scale=wl.scale, dq=outs[0], dk=outs[1], dv=outs[2], dwq=dw[0], dwk=dw[1], workspace_buf=ws,
-                          stream=stream)
-        else:
-            h3.h3attn_bwd_pos(g["dout"], g["q"], g["k"], g["v"], lse, g["seg"], pos, g["wq"], g["wk"], eps=wl.eps,
-                              scale=wl.scale, dq=outs[0], dk=outs[1], dv=outs[2], dwq=dw[0], dwk=dw[1],
-                              workspace_buf=ws, stream=stream)
+        h3.h3attn_bwd_ex(g["dout"], g["q"], g["k"], g["v"], lse, g["seg"], pos, o32, g["wq"], g["wk"], eps=wl.eps,
+                         scale=wl.scale, dq=outs[0], dk=outs[1], dv=outs[2], dwq=dw[0], dwk=dw[1], workspace_buf=ws,
+                         stream=stream)
 
     for _ in range(args.warmup):
         step()
@@ -333,7 +329,7 @@ def bench_bwd(args, wl):
         "data": "synthetic",
         "config": {"workload": wl.name + "-bwd", "tokens": T, "heads": H, "head_dim": 128,
                    "segments": list(wl.seg_lens), "products": "fp16 P, dS, dO, q/k hat; fp32 accumulate",
-                   "key_order": args.order,
+                   "key_order": args.order, "d_from": args.d_from,
                    "pct_bf16_mfma_peak": round(100 * value / PEAK_MFMA_TFLOPS, 2),
                    "repeat_bitwise": repeat_bitwise, "device_status": status},
         "roofline": {"bound": "mfma", "achieved": round(value, 2), "peak": PEAK_MFMA_TFLOPS, "unit": "TFLOP/s",

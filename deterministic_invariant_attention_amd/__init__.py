@@ -30,8 +30,8 @@ H3ATTN_ERR_POSITIONS = 10
 
 # every symbol the header declares
 EXPORTS = ("h3attn_version", "h3attn_strerror", "h3attn_workspace_bytes", "h3attn_qknorm", "h3attn_fwd",
-           "h3attn_fwd_pos", "h3attn_plan", "h3attn_prep_qkv", "h3attn_attend", "h3attn_status_read",
-           "h3attn_bwd_workspace_bytes", "h3attn_bwd", "h3attn_bwd_pos")
+           "h3attn_fwd_pos", "h3attn_fwd_ex", "h3attn_plan", "h3attn_prep_qkv", "h3attn_attend", "h3attn_status_read",
+           "h3attn_bwd_workspace_bytes", "h3attn_bwd", "h3attn_bwd_pos", "h3attn_bwd_ex")
 
 
 class H3AttnError(RuntimeError):
@@ -60,6 +60,7 @@ def load():
     lib.h3attn_qknorm.argtypes = [P, P, P, I64, I32, I32, F, P]
     lib.h3attn_fwd.argtypes = [P, P, P, P, P, P, I64, I32, I32, F, F, P, P, P, SZ, P]
     lib.h3attn_fwd_pos.argtypes = [P, P, P, P, P, P, P, I64, I32, I32, F, F, P, P, P, SZ, P]
+    lib.h3attn_fwd_ex.argtypes = [P, P, P, P, P, P, P, I64, I32, I32, F, F, P, P, P, P, SZ, P]
     lib.h3attn_plan.argtypes = [P, I64, I32, P, SZ, P]
     lib.h3attn_prep_qkv.argtypes = [P, P, P, P, P, I64, I32, I32, F, P, SZ, P]
     lib.h3attn_attend.argtypes = [P, P, I64, I32, I32, F, F, P, P, P, SZ, P]
@@ -68,8 +69,9 @@ def load():
     lib.h3attn_bwd_workspace_bytes.restype = SZ
     lib.h3attn_bwd.argtypes = [P, P, P, P, P, P, P, P, I64, I32, I32, F, F, P, P, P, P, P, P, SZ, P]
     lib.h3attn_bwd_pos.argtypes = [P, P, P, P, P, P, P, P, P, I64, I32, I32, F, F, P, P, P, P, P, P, SZ, P]
-    for name in ("h3attn_qknorm", "h3attn_fwd", "h3attn_fwd_pos", "h3attn_plan", "h3attn_prep_qkv", "h3attn_attend",
-                 "h3attn_status_read", "h3attn_bwd", "h3attn_bwd_pos"):
+    lib.h3attn_bwd_ex.argtypes = [P, P, P, P, P, P, P, P, P, P, I64, I32, I32, F, F, P, P, P, P, P, P, SZ, P]
+    for name in ("h3attn_qknorm", "h3attn_fwd", "h3attn_fwd_pos", "h3attn_fwd_ex", "h3attn_plan", "h3attn_prep_qkv",
+                 "h3attn_attend", "h3attn_status_read", "h3attn_bwd", "h3attn_bwd_pos", "h3attn_bwd_ex"):
         getattr(lib, name).restype = ctypes.c_int
     _lib = lib
     return lib
@@ -150,7 +152,23 @@ def h3attn_fwd_pos(q, k, v, seg_ids, pos_ids, wq=None, wk=None, eps: float = 1e-
                 want_lse)
 
 
-def _fwd(q, k, v, seg_ids, pos_ids, wq, wk, eps, scale, out, lse, workspace_buf, stream, want_lse):
+def h3attn_fwd_ex(q, k, v, seg_ids, pos_ids=None, wq=None, wk=None, eps: float = 1e-6, scale: float | None = None,
+                  out=None, lse=None, o32=None, workspace_buf=None, stream=None, want_lse: bool = False,
+                  want_o32: bool = False):
+    """The forward with every option: position order when pos_ids is given, and the fp32 output
+    before its bf16 rounding (o32, for h3attn_bwd_ex) when asked.  Returns (out, lse, o32)."""
+    T = q.shape[0]
+    if o32 is None and want_o32:
+        o32 = torch.empty(q.shape, dtype=torch.float32, device=q.device)
+    if o32 is not None and (o32.dtype != torch.float32 or not o32.is_contiguous()):
+        raise TypeError("o32 must be a contiguous float32 tensor")
+    out, lse = _fwd(q, k, v, seg_ids, None if pos_ids is None else _int32(pos_ids, "pos_ids"), wq, wk, eps, scale,
+                    out, lse, workspace_buf, stream, want_lse, o32=o32, ex=True)
+    return out, lse, o32
+
+
+def _fwd(q, k, v, seg_ids, pos_ids, wq, wk, eps, scale, out, lse, workspace_buf, stream, want_lse, o32=None,
+         ex=False):
     for t, n in ((q, "q"), (k, "k"), (v, "v"), (wq, "wq"), (wk, "wk")):
         _bf16(t, n)
     _int32(seg_ids, "seg_ids")
@@ -161,7 +179,12 @@ def _fwd(q, k, v, seg_ids, pos_ids, wq, wk, eps, scale, out, lse, workspace_buf,
         lse = torch.empty((T, H), dtype=torch.float32, device=q.device)
     ws = workspace(T, H, q.device) if workspace_buf is None else workspace_buf
     st = _stream(stream, q.device)
-    if pos_ids is None:
+    if ex:
+        rc = load().h3attn_fwd_ex(_ptr(q), _ptr(k), _ptr(v), _ptr(seg_ids), _ptr(pos_ids), _ptr(wq), _ptr(wk), T, H,
+                                  D, float(eps), float(scale), _ptr(out), _ptr(lse), _ptr(o32), _ptr(ws), ws.numel(),
+                                  st)
+        _check(rc, "h3attn_fwd_ex")
+    elif pos_ids is None:
         rc = load().h3attn_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(seg_ids), _ptr(wq), _ptr(wk), T, H, D, float(eps),
                                float(scale), _ptr(out), _ptr(lse), _ptr(ws), ws.numel(), st)
         _check(rc, "h3attn_fwd")
@@ -227,7 +250,19 @@ def h3attn_bwd_pos(dout, q, k, v, lse, seg_ids, pos_ids, wq=None, wk=None, eps: 
                 workspace_buf, stream)
 
 
-def _bwd(dout, q, k, v, lse, seg_ids, pos_ids, wq, wk, eps, scale, dq, dk, dv, dwq, dwk, workspace_buf, stream):
+def h3attn_bwd_ex(dout, q, k, v, lse, seg_ids, pos_ids=None, o32=None, wq=None, wk=None, eps: float = 1e-6,
+                  scale: float | None = None, dq=None, dk=None, dv=None, dwq=None, dwk=None, workspace_buf=None,
+                  stream=None):
+    """The backward with every option: position order when pos_ids is given; D = dO . O from the
+    forward's o32 (h3attn_fwd_ex) when given, else recomputed.  Returns (dq, dk, dv, dwq, dwk)."""
+    if o32 is not None and (o32.dtype != torch.float32 or not o32.is_contiguous()):
+        raise TypeError("o32 must be a contiguous float32 tensor")
+    return _bwd(dout, q, k, v, lse, seg_ids, None if pos_ids is None else _int32(pos_ids, "pos_ids"), wq, wk, eps,
+                scale, dq, dk, dv, dwq, dwk, workspace_buf, stream, o32=o32, ex=True)
+
+
+def _bwd(dout, q, k, v, lse, seg_ids, pos_ids, wq, wk, eps, scale, dq, dk, dv, dwq, dwk, workspace_buf, stream,
+         o32=None, ex=False):
     for t, n in ((dout, "dout"), (q, "q"), (k, "k"), (v, "v"), (wq, "wq"), (wk, "wk")):
         _bf16(t, n)
     _int32(seg_ids, "seg_ids")
@@ -243,7 +278,12 @@ def _bwd(dout, q, k, v, lse, seg_ids, pos_ids, wq, wk, eps, scale, dq, dk, dv, d
         dwk = torch.empty(D, dtype=torch.float32, device=q.device) if dwk is None else dwk
     ws = bwd_workspace(T, H, q.device) if workspace_buf is None else workspace_buf
     st = _stream(stream, q.device)
-    if pos_ids is None:
+    if ex:
+        rc = load().h3attn_bwd_ex(_ptr(dout), _ptr(q), _ptr(k), _ptr(v), _ptr(lse), _ptr(o32), _ptr(seg_ids),
+                                  _ptr(pos_ids), _ptr(wq), _ptr(wk), T, H, D, float(eps), float(scale), _ptr(dq),
+                                  _ptr(dk), _ptr(dv), _ptr(dwq), _ptr(dwk), _ptr(ws), ws.numel(), st)
+        _check(rc, "h3attn_bwd_ex")
+    elif pos_ids is None:
         rc = load().h3attn_bwd(_ptr(dout), _ptr(q), _ptr(k), _ptr(v), _ptr(lse), _ptr(seg_ids), _ptr(wq), _ptr(wk),
                                T, H, D, float(eps), float(scale), _ptr(dq), _ptr(dk), _ptr(dv), _ptr(dwq), _ptr(dwk),
                                _ptr(ws), ws.numel(), st)

@@ -25,17 +25,19 @@ hipError_t launch_order(const int32_t* pos, int64_t T, void* ws, const int32_t* 
                         hipStream_t stream);
 
 // Attention over the planned work items.  Queries: the staged normed Q when normed is true, else
-// the caller's q (token-major).  grid_cap: most workgroups to launch (persistent grid).
+// the caller's q (token-major).  lse and o32 (the output before its bf16 rounding, fp32) are
+// optional.  grid_cap: most workgroups to launch (persistent grid).
 hipError_t launch_attend(const void* q, bool normed, int64_t T, int32_t H, float scale, void* out, float* lse,
-                         void* ws, int grid_cap, hipStream_t stream);
+                         float* o32, void* ws, int grid_cap, hipStream_t stream);
 
 // Backward: segment decode with 128-token tiles into the backward workspace.
 hipError_t launch_plan_bwd(const int32_t* seg, int64_t T, void* ws, int32_t H, hipStream_t stream);
 
 // Backward operand staging (normed q/k, v and dO in fp16, LSE in log2 units), at staged rows slot[t]
-// or, with slot NULL, at the token's own row.
+// or, with slot NULL, at the token's own row.  With o32 (the forward's fp32 output) it also writes
+// D = dO . O per row, and the dq kernel then skips its first pass.
 hipError_t launch_bwd_prep(const void* q, const void* k, const void* v, const void* dout, const float* lse,
-                           const void* wq, const void* wk, int64_t T, int32_t H, float eps, void* ws,
+                           const float* o32, const void* wq, const void* wk, int64_t T, int32_t H, float eps, void* ws,
                            const int32_t* slot, hipStream_t stream);
 
 // Backward attention on the staged operands: dq with D, then dk/dv; with norm weights, the norm
@@ -44,6 +46,6 @@ hipError_t launch_bwd_prep(const void* q, const void* k, const void* v, const vo
 // staged row to its token (position order) or is NULL.
 hipError_t launch_bwd(const void* q, const void* k, const void* wq, const void* wk, int64_t T, int32_t H, float eps,
                       float scale, void* dq, void* dk, void* dv, float* dwq, float* dwk, void* ws, const int32_t* inv,
-                      int grid_cap, hipStream_t stream);
+                      bool delta_ready, int grid_cap, hipStream_t stream);
 
 }  // namespace h3

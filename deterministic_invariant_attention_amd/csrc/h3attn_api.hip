@@ -199,14 +199,15 @@ int h3attn_attend(const void* q, const void* wq, int64_t tokens, int32_t heads, 
   DeviceInfo di;
   if ((rc = device_info(&di))) return rc;
   return launch_status(
-      launch_attend(q, wq != nullptr, tokens, heads, scale, out, lse, workspace, di.cus, (hipStream_t)stream));
+      launch_attend(q, wq != nullptr, tokens, heads, scale, out, lse, nullptr, workspace, di.cus, (hipStream_t)stream));
 }
 
-// The forward; pos_ids NULL walks keys in packed order, else in position order.
+// The forward; pos_ids NULL walks keys in packed order, else in position order; o32 (optional)
+// receives the output before its bf16 rounding.
 static int fwd_impl(const void* q, const void* k, const void* v, const int32_t* seg_ids, const int32_t* pos_ids,
                     bool ordered, const void* wq, const void* wk, int64_t tokens, int32_t heads, int32_t head_dim,
-                    float eps, float scale, void* out, float* lse, void* workspace, size_t workspace_bytes,
-                    void* stream) {
+                    float eps, float scale, void* out, float* lse, float* o32, void* workspace,
+                    size_t workspace_bytes, void* stream) {
   int rc = check_shape(tokens, heads, head_dim);
   if (rc) return rc;
   if ((wq == nullptr) != (wk == nullptr)) return H3ATTN_ERR_NULL;
@@ -224,6 +225,14 @@ static int fwd_impl(const void* q, const void* k, const void* v, const int32_t* 
       overlap(out, n, wk, HD * 2) || overlap(lse, nl, k, n) || overlap(lse, nl, v, n) ||
       overlap(lse, nl, seg_ids, ns) || overlap(lse, nl, wk, HD * 2))
     return H3ATTN_ERR_ALIAS;
+  if (o32) {
+    const size_t n32 = 2 * n;
+    if (!aligned(o32, 16)) return H3ATTN_ERR_ALIGN;
+    const void* ins[] = {q, k, v, seg_ids, wq, wk, workspace, pos_ids, out, lse};
+    const size_t in_n[] = {n, n, n, ns, (size_t)HD * 2, (size_t)HD * 2, workspace_bytes, pos_ids ? ns : 0, n, nl};
+    for (int i = 0; i < 10; i++)
+      if (overlap(o32, n32, ins[i], in_n[i])) return H3ATTN_ERR_ALIAS;
+  }
   const OrderLayout ol = order_layout(ws_layout(tokens, heads).total, tokens);
   if (ordered) {
     if (!aligned(pos_ids, 4)) return H3ATTN_ERR_ALIGN;
@@ -243,21 +252,29 @@ static int fwd_impl(const void* q, const void* k, const void* v, const int32_t* 
                                        slot, (int32_t*)(base + ol.inv), st))))
     return rc;
   if ((rc = launch_status(launch_prep_qkv(q, k, v, wq, wk, tokens, heads, eps, workspace, slot, st)))) return rc;
-  return launch_status(launch_attend(q, wq != nullptr, tokens, heads, scale, out, lse, workspace, di.cus, st));
+  return launch_status(launch_attend(q, wq != nullptr, tokens, heads, scale, out, lse, o32, workspace, di.cus, st));
 }
 
 int h3attn_fwd(const void* q, const void* k, const void* v, const int32_t* seg_ids, const void* wq, const void* wk,
                int64_t tokens, int32_t heads, int32_t head_dim, float eps, float scale, void* out, float* lse,
                void* workspace, size_t workspace_bytes, void* stream) {
-  return fwd_impl(q, k, v, seg_ids, nullptr, false, wq, wk, tokens, heads, head_dim, eps, scale, out, lse, workspace,
-                  workspace_bytes, stream);
+  return fwd_impl(q, k, v, seg_ids, nullptr, false, wq, wk, tokens, heads, head_dim, eps, scale, out, lse, nullptr,
+                  workspace, workspace_bytes, stream);
 }
 
 int h3attn_fwd_pos(const void* q, const void* k, const void* v, const int32_t* seg_ids, const int32_t* pos_ids,
                    const void* wq, const void* wk, int64_t tokens, int32_t heads, int32_t head_dim, float eps,
                    float scale, void* out, float* lse, void* workspace, size_t workspace_bytes, void* stream) {
-  return fwd_impl(q, k, v, seg_ids, pos_ids, true, wq, wk, tokens, heads, head_dim, eps, scale, out, lse, workspace,
-                  workspace_bytes, stream);
+  return fwd_impl(q, k, v, seg_ids, pos_ids, true, wq, wk, tokens, heads, head_dim, eps, scale, out, lse, nullptr,
+                  workspace, workspace_bytes, stream);
+}
+
+int h3attn_fwd_ex(const void* q, const void* k, const void* v, const int32_t* seg_ids, const int32_t* pos_ids,
+                  const void* wq, const void* wk, int64_t tokens, int32_t heads, int32_t head_dim, float eps,
+                  float scale, void* out, float* lse, float* o32, void* workspace, size_t workspace_bytes,
+                  void* stream) {
+  return fwd_impl(q, k, v, seg_ids, pos_ids, pos_ids != nullptr, wq, wk, tokens, heads, head_dim, eps, scale, out, lse,
+                  o32, workspace, workspace_bytes, stream);
 }
 
 // Large enough for both h3attn_bwd and h3attn_bwd_pos.
@@ -267,8 +284,9 @@ size_t h3attn_bwd_workspace_bytes(int64_t tokens, int32_t heads) {
   return order_layout(bwd_layout(tokens, heads).total, tokens).total;
 }
 
-// The backward; ordered: operands staged and every sum taken in position order.
-static int bwd_impl(const void* dout, const void* q, const void* k, const void* v, const float* lse,
+// The backward; ordered: operands staged and every sum taken in position order; o32 (optional):
+// the forward's fp32 output, from which D = dO . O is computed instead of recomputed from P and dP.
+static int bwd_impl(const void* dout, const void* q, const void* k, const void* v, const float* lse, const float* o32,
                     const int32_t* seg_ids, const int32_t* pos_ids, bool ordered, const void* wq, const void* wk,
                     int64_t tokens, int32_t heads, int32_t head_dim, float eps, float scale, void* dq, void* dk,
                     void* dv, float* dwq, float* dwk, void* workspace, size_t workspace_bytes, void* stream) {
@@ -285,7 +303,7 @@ static int bwd_impl(const void* dout, const void* q, const void* k, const void* 
   if (!aligned(dout, 16) || !aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(lse, 4) ||
       !aligned(seg_ids, 4) || (wq && (!aligned(wq, 16) || !aligned(wk, 16) || !aligned(dwq, 4) || !aligned(dwk, 4))) ||
       !aligned(dq, 16) || !aligned(dk, 16) || !aligned(dv, 16) || !aligned(workspace, 256) ||
-      (ordered && !aligned(pos_ids, 4)))
+      (ordered && !aligned(pos_ids, 4)) || (o32 && !aligned(o32, 16)))
     return H3ATTN_ERR_ALIGN;
   const OrderLayout ol = order_layout(bwd_layout(tokens, heads).total, tokens);
   if (workspace_bytes < (ordered ? ol.total : bwd_layout(tokens, heads).total)) return H3ATTN_ERR_WORKSPACE;
@@ -293,13 +311,15 @@ static int bwd_impl(const void* dout, const void* q, const void* k, const void* 
   const size_t nl = (size_t)tokens * heads * 4;
   const size_t ns = (size_t)tokens * 4;
   // every output against every input, the workspace and the other outputs
-  const void* ins[] = {dout, q, k, v, lse, seg_ids, wq, wk, workspace, pos_ids};
-  const size_t in_n[] = {n, n, n, n, nl, ns, (size_t)HD * 2, (size_t)HD * 2, workspace_bytes, ordered ? ns : 0};
+  const void* ins[] = {dout, q, k, v, lse, seg_ids, wq, wk, workspace, pos_ids, o32};
+  const size_t in_n[] = {n, n, n, n, nl, ns, (size_t)HD * 2, (size_t)HD * 2, workspace_bytes, ordered ? ns : 0,
+                         o32 ? 2 * n : 0};
   void* outs[] = {dq, dk, dv, dwq, dwk};
   const size_t out_n[] = {n, n, n, wq ? (size_t)HD * 4 : 0, wq ? (size_t)HD * 4 : 0};
   if (ordered && overlap(pos_ids, ns, workspace, workspace_bytes)) return H3ATTN_ERR_ALIAS;
+  if (o32 && overlap(o32, 2 * n, workspace, workspace_bytes)) return H3ATTN_ERR_ALIAS;
   for (int o = 0; o < 5; o++) {
-    for (int i = 0; i < 10; i++)
+    for (int i = 0; i < 11; i++)
       if (overlap(outs[o], out_n[o], ins[i], in_n[i])) return H3ATTN_ERR_ALIAS;
     for (int o2 = o + 1; o2 < 5; o2++)
       if (overlap(outs[o], out_n[o], outs[o2], out_n[o2])) return H3ATTN_ERR_ALIAS;
@@ -315,26 +335,34 @@ static int bwd_impl(const void* dout, const void* q, const void* k, const void* 
       (rc = launch_status(launch_order(pos_ids, tokens, workspace,
                                        (const int32_t*)(base + bwd_layout(tokens, heads).segtab), slot, inv, st))))
     return rc;
-  if ((rc = launch_status(launch_bwd_prep(q, k, v, dout, lse, wq, wk, tokens, heads, eps, workspace, slot, st))))
+  if ((rc = launch_status(launch_bwd_prep(q, k, v, dout, lse, o32, wq, wk, tokens, heads, eps, workspace, slot, st))))
     return rc;
-  return launch_status(
-      launch_bwd(q, k, wq, wk, tokens, heads, eps, scale, dq, dk, dv, dwq, dwk, workspace, inv, di.cus, st));
+  return launch_status(launch_bwd(q, k, wq, wk, tokens, heads, eps, scale, dq, dk, dv, dwq, dwk, workspace, inv,
+                                  o32 != nullptr, di.cus, st));
 }
 
 int h3attn_bwd(const void* dout, const void* q, const void* k, const void* v, const float* lse,
                const int32_t* seg_ids, const void* wq, const void* wk, int64_t tokens, int32_t heads,
                int32_t head_dim, float eps, float scale, void* dq, void* dk, void* dv, float* dwq, float* dwk,
                void* workspace, size_t workspace_bytes, void* stream) {
-  return bwd_impl(dout, q, k, v, lse, seg_ids, nullptr, false, wq, wk, tokens, heads, head_dim, eps, scale, dq, dk, dv,
-                  dwq, dwk, workspace, workspace_bytes, stream);
+  return bwd_impl(dout, q, k, v, lse, nullptr, seg_ids, nullptr, false, wq, wk, tokens, heads, head_dim, eps, scale, dq,
+                  dk, dv, dwq, dwk, workspace, workspace_bytes, stream);
 }
 
 int h3attn_bwd_pos(const void* dout, const void* q, const void* k, const void* v, const float* lse,
                    const int32_t* seg_ids, const int32_t* pos_ids, const void* wq, const void* wk, int64_t tokens,
                    int32_t heads, int32_t head_dim, float eps, float scale, void* dq, void* dk, void* dv, float* dwq,
                    float* dwk, void* workspace, size_t workspace_bytes, void* stream) {
-  return bwd_impl(dout, q, k, v, lse, seg_ids, pos_ids, true, wq, wk, tokens, heads, head_dim, eps, scale, dq, dk, dv,
-                  dwq, dwk, workspace, workspace_bytes, stream);
+  return bwd_impl(dout, q, k, v, lse, nullptr, seg_ids, pos_ids, true, wq, wk, tokens, heads, head_dim, eps, scale, dq,
+                  dk, dv, dwq, dwk, workspace, workspace_bytes, stream);
+}
+
+int h3attn_bwd_ex(const void* dout, const void* q, const void* k, const void* v, const float* lse, const float* o32,
+                  const int32_t* seg_ids, const int32_t* pos_ids, const void* wq, const void* wk, int64_t tokens,
+                  int32_t heads, int32_t head_dim, float eps, float scale, void* dq, void* dk, void* dv, float* dwq,
+                  float* dwk, void* workspace, size_t workspace_bytes, void* stream) {
+  return bwd_impl(dout, q, k, v, lse, o32, seg_ids, pos_ids, pos_ids != nullptr, wq, wk, tokens, heads, head_dim, eps,
+                  scale, dq, dk, dv, dwq, dwk, workspace, workspace_bytes, stream);
 }
 
 int h3attn_status_read(const void* workspace, int32_t* device_status, void* stream) {

@@ -59,6 +59,7 @@ struct AttnParams {
   const uint16_t* v16;
   uint16_t* out;
   float* lse;
+  float* o32;  // optional: the output before its bf16 rounding, fp32 token-major
   const WsHeader* hdr;
   const int32_t* segtab;
   const int32_t* items;
@@ -119,6 +120,11 @@ __global__ __launch_bounds__(64 * NWAVES, 1) void k_attn_fwd(AttnParams p) {
     for (int64_t e = (int64_t)blockIdx.x * blockDim.x + tid; e < n16; e += stride) *(u32x4*)(p.out + e * 8) = nan4;
     if (p.lse)
       for (int64_t e = (int64_t)blockIdx.x * blockDim.x + tid; e < T * H; e += stride) p.lse[e] = __builtin_nanf("");
+    if (p.o32) {
+      const f32x4 nanf4 = {__builtin_nanf(""), __builtin_nanf(""), __builtin_nanf(""), __builtin_nanf("")};
+      for (int64_t e = (int64_t)blockIdx.x * blockDim.x + tid; e < T * H * HD / 4; e += stride)
+        *(f32x4*)(p.o32 + e * 4) = nanf4;
+    }
     return;
   }
 
@@ -290,13 +296,23 @@ __global__ __launch_bounds__(64 * NWAVES, 1) void k_attn_fwd(AttnParams p) {
           o2[1] = pack_bf16(O[db][4 * g + 2] * inv, O[db][4 * g + 3] * inv);
           *(u32x2*)(op + d0) = o2;
         }
+      if (p.o32) {
+        float* o32p = p.o32 + ((int64_t)(s0 + qrow) * H + head) * HD;
+#pragma unroll
+        for (int db = 0; db < 4; db++)
+#pragma unroll
+          for (int g = 0; g < 4; g++) {
+            const f32x4 f = {O[db][4 * g] * inv, O[db][4 * g + 1] * inv, O[db][4 * g + 2] * inv, O[db][4 * g + 3] * inv};
+            *(f32x4*)(o32p + 32 * db + 8 * g + 4 * hh) = f;
+          }
+      }
       if (p.lse && hh == 0) p.lse[(int64_t)(s0 + qrow) * H + head] = (m_run + __builtin_amdgcn_logf(l)) * LN2;
     }
   }
 }
 
 hipError_t launch_attend(const void* q, bool normed, int64_t T, int32_t H, float scale, void* out, float* lse,
-                         void* ws, int grid_cap, hipStream_t stream) {
+                         float* o32, void* ws, int grid_cap, hipStream_t stream) {
   const WsLayout Lw = ws_layout(T, H);
   char* base = (char*)ws;
   AttnParams p;
@@ -307,6 +323,7 @@ hipError_t launch_attend(const void* q, bool normed, int64_t T, int32_t H, float
   p.v16 = (const uint16_t*)(base + Lw.v16);
   p.out = (uint16_t*)out;
   p.lse = lse;
+  p.o32 = o32;
   p.hdr = (const WsHeader*)base;
   p.segtab = (const int32_t*)(base + Lw.segtab);
   p.items = (const int32_t*)(base + Lw.items);

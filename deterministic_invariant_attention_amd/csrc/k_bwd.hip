@@ -52,6 +52,7 @@ struct BwdParams {
   float* dqh;  // with norm weights: gradients with respect to the normed q / k, fp32, staged row-major
   float* dkh;
   const int32_t* inv;  // token of each staged row (position order), or NULL (staged row = token)
+  int32_t delta_ready;  // D was written by the staging kernel (from the forward's fp32 output)
   const WsHeader* hdr;
   int32_t* next;  // the kernel's work counter (in the header)
   const int32_t* segtab;
@@ -244,38 +245,43 @@ __global__ __launch_bounds__(64 * BW, 1) void k_bwd_dq(BwdParams p) {
       if (j == ntk - 1 && rem < TILE_ROWS) mask_tail(S, rem, hh);
     };
 
-    // ---- pass 1: D_i = sum_j P_ij dP_ij
-    float dacc = 0.0f;
-    auto pass1 = [&](auto stage, int j) {
-      constexpr int ST = decltype(stage)::value;
-      copies_barrier();  // tile j has landed, every wave is done with stage 1 - ST
-      if (j + 1 < ntk) copies(j + 1, Par2<1 - ST>{});
-      f32x16 S[2], dP[2];
-      scores(stage, j, S, dP);
-      float pd[32];
+    // ---- pass 1: D_i = sum_j P_ij dP_ij (unless the staging kernel computed D = dO . O)
+    float Dq;
+    if (p.delta_ready) {
+      Dq = qvalid ? p.delta[hT + w.s0 + qrow] : 0.0f;
+    } else {
+      float dacc = 0.0f;
+      auto pass1 = [&](auto stage, int j) {
+        constexpr int ST = decltype(stage)::value;
+        copies_barrier();  // tile j has landed, every wave is done with stage 1 - ST
+        if (j + 1 < ntk) copies(j + 1, Par2<1 - ST>{});
+        f32x16 S[2], dP[2];
+        scores(stage, j, S, dP);
+        float pd[32];
 #pragma unroll
-      for (int kbk = 0; kbk < 2; kbk++)
+        for (int kbk = 0; kbk < 2; kbk++)
 #pragma unroll
-        for (int i = 0; i < 16; i++)
-          pd[16 * kbk + i] = __builtin_amdgcn_exp2f(__builtin_fmaf(S[kbk][i], c, -lq)) * dP[kbk][i];
-      dacc += tree_sum<32>(pd);
-    };
-    {
-      int j = 0;
-      for (; j + 1 < ntk; j += 2) {
-        pass1(Par2<0>{}, j);
-        pass1(Par2<1>{}, j + 1);
+          for (int i = 0; i < 16; i++)
+            pd[16 * kbk + i] = __builtin_amdgcn_exp2f(__builtin_fmaf(S[kbk][i], c, -lq)) * dP[kbk][i];
+        dacc += tree_sum<32>(pd);
+      };
+      {
+        int j = 0;
+        for (; j + 1 < ntk; j += 2) {
+          pass1(Par2<0>{}, j);
+          pass1(Par2<1>{}, j + 1);
+        }
+        if (j < ntk) pass1(Par2<0>{}, j);
       }
-      if (j < ntk) pass1(Par2<0>{}, j);
+      float da, db_;
+      swap_halves(dacc, da, db_);
+      Dq = da + db_;
+      if (qvalid && hh == 0) p.delta[hT + w.s0 + qrow] = Dq;
+      __syncthreads();  // every wave is done with pass 1's tiles
+      copies(0, Par2<0>{});
     }
-    float da, db_;
-    swap_halves(dacc, da, db_);
-    const float Dq = da + db_;
-    if (qvalid && hh == 0) p.delta[hT + w.s0 + qrow] = Dq;
 
     // ---- pass 2: dQ^T += K^16^T dS^T
-    __syncthreads();  // every wave is done with pass 1's tiles
-    copies(0, Par2<0>{});
     f32x16 acc[4];
 #pragma unroll
     for (int d = 0; d < 4; d++)
@@ -586,7 +592,7 @@ __global__ __launch_bounds__(2 * HD) void k_bwd_dw_final(const WsHeader* hdr, co
 
 hipError_t launch_bwd(const void* q, const void* k, const void* wq, const void* wk, int64_t T, int32_t H, float eps,
                       float scale, void* dq, void* dk, void* dv, float* dwq, float* dwk, void* ws,
-                      const int32_t* inv, int grid_cap, hipStream_t stream) {
+                      const int32_t* inv, bool delta_ready, int grid_cap, hipStream_t stream) {
   const BwdLayout Lw = bwd_layout(T, H);
   char* base = (char*)ws;
   BwdParams p;
@@ -606,6 +612,7 @@ hipError_t launch_bwd(const void* q, const void* k, const void* wq, const void* 
   p.dqh = (float*)(base + Lw.dqh);
   p.dkh = (float*)(base + Lw.dkh);
   p.inv = inv;
+  p.delta_ready = delta_ready ? 1 : 0;
   p.hdr = (const WsHeader*)base;
   p.segtab = (const int32_t*)(base + Lw.segtab);
   p.items = (const int32_t*)(base + Lw.items);

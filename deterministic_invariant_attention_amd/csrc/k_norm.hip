@@ -111,6 +111,7 @@ struct BwdPrepParams {
   const uint16_t* v;
   const uint16_t* dout;
   const float* lse;
+  const float* o32;  // optional: the forward's output before its bf16 rounding
   const uint16_t* wq;
   const uint16_t* wk;
   uint16_t* qhat16;
@@ -118,6 +119,7 @@ struct BwdPrepParams {
   uint16_t* v16;
   uint16_t* do16;
   float* lse2;
+  float* delta;         // D = dO . O per row (with o32)
   const int32_t* slot;  // staged row of each token (position order), or NULL for packed order
   WsHeader* hdr;
   int64_t T;
@@ -175,6 +177,27 @@ __global__ __launch_bounds__(256) void k_bwd_prep(BwdPrepParams p) {
     st16(p.do16 + dst, g16);
     if (c == 0) p.lse2[h * p.T + ts] = p.lse[t * p.H + h] * 1.44269504088896340736f;
   }
+  if (p.o32) {
+    // D_i = sum_d dO_id O_id: products and sums in FP64 (each lane its 8 channels in order, then a
+    // fixed butterfly over the 16 lanes of the row), rounded once to fp32
+    f32x4 o0 = {0.0f, 0.0f, 0.0f, 0.0f}, o1 = o0;
+    if (valid) {
+      o0 = *(const f32x4*)(p.o32 + row * HD + c * 8);
+      o1 = *(const f32x4*)(p.o32 + row * HD + c * 8 + 4);
+    }
+    float g[8];
+    unpack8_bf16(gv, g);
+    double d = 0.0;
+#pragma unroll
+    for (int i = 0; i < 4; i++) d = __builtin_fma((double)g[i], (double)o0[i], d);
+#pragma unroll
+    for (int i = 0; i < 4; i++) d = __builtin_fma((double)g[4 + i], (double)o1[i], d);
+    d = d + __shfl_xor(d, 1, 64);
+    d = d + __shfl_xor(d, 2, 64);
+    d = d + __shfl_xor(d, 4, 64);
+    d = d + __shfl_xor(d, 8, 64);
+    if (valid && c == 0) p.delta[h * p.T + ts] = (float)d;
+  }
   const uint64_t any_over = __ballot(valid && over);
   if (any_over && (threadIdx.x & 63) == __builtin_ctzll(any_over)) atomicOr(&p.hdr->status, STATUS_RANGE_BIT);
 }
@@ -182,7 +205,7 @@ __global__ __launch_bounds__(256) void k_bwd_prep(BwdPrepParams p) {
 static inline unsigned grid_for_rows(int64_t rows) { return (unsigned)((rows * 16 + 255) / 256); }
 
 hipError_t launch_bwd_prep(const void* q, const void* k, const void* v, const void* dout, const float* lse,
-                           const void* wq, const void* wk, int64_t T, int32_t H, float eps, void* ws,
+                           const float* o32, const void* wq, const void* wk, int64_t T, int32_t H, float eps, void* ws,
                            const int32_t* slot, hipStream_t stream) {
   const int64_t rows = T * H;
   if (rows == 0) return hipSuccess;
@@ -194,6 +217,7 @@ hipError_t launch_bwd_prep(const void* q, const void* k, const void* v, const vo
   p.v = (const uint16_t*)v;
   p.dout = (const uint16_t*)dout;
   p.lse = lse;
+  p.o32 = o32;
   p.wq = (const uint16_t*)wq;
   p.wk = (const uint16_t*)wk;
   p.qhat16 = (uint16_t*)(base + L.qhat16);
@@ -201,6 +225,7 @@ hipError_t launch_bwd_prep(const void* q, const void* k, const void* v, const vo
   p.v16 = (uint16_t*)(base + L.v16);
   p.do16 = (uint16_t*)(base + L.do16);
   p.lse2 = (float*)(base + L.lse2);
+  p.delta = (float*)(base + L.delta);
   p.slot = slot;
   p.hdr = (WsHeader*)base;
   p.T = T;

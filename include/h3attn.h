@@ -115,6 +115,16 @@ int h3attn_fwd_pos(const void* q, const void* k, const void* v, const int32_t* s
                    const void* wq, const void* wk, int64_t tokens, int32_t heads, int32_t head_dim, float eps,
                    float scale, void* out, float* lse, void* workspace, size_t workspace_bytes, void* stream);
 
+/* The forward with every option: pos_ids NULL walks keys in packed order (h3attn_fwd), else in
+ * position order (h3attn_fwd_pos); o32 (optional, fp32 [T, H, 128] device memory, 16-byte aligned)
+ * receives each output element before its one bf16 rounding, for the backward's D = dO . O (see
+ * h3attn_bwd_ex).  o32 must not overlap any input, out, lse or the workspace.  Everything else as
+ * for h3attn_fwd; out, lse and o32 carry the same bits whatever the other options are. */
+int h3attn_fwd_ex(const void* q, const void* k, const void* v, const int32_t* seg_ids, const int32_t* pos_ids,
+                  const void* wq, const void* wk, int64_t tokens, int32_t heads, int32_t head_dim, float eps,
+                  float scale, void* out, float* lse, float* o32, void* workspace, size_t workspace_bytes,
+                  void* stream);
+
 /* The three stages of h3attn_fwd, for callers that reuse one segment plan across layers (the 50
  * blocks of the model share the packed layout) or time the stages.  They must be enqueued in this
  * order on one stream with one workspace: h3attn_plan (resets the status word), h3attn_prep_qkv,
@@ -168,6 +178,20 @@ int h3attn_bwd_pos(const void* dout, const void* q, const void* k, const void* v
                    const int32_t* seg_ids, const int32_t* pos_ids, const void* wq, const void* wk, int64_t tokens,
                    int32_t heads, int32_t head_dim, float eps, float scale, void* dq, void* dk, void* dv, float* dwq,
                    float* dwk, void* workspace, size_t workspace_bytes, void* stream);
+
+/* The backward with every option.  pos_ids as for h3attn_fwd_ex (NULL: packed order).  o32: NULL,
+ * or the o32 that h3attn_fwd_ex wrote for the same inputs (and the same pos_ids, which change no bit
+ * of it).  With o32, D_i = dO_i . O_i is formed from it once per row (FP64 products and sums,
+ * one fp32 rounding) instead of being recomputed from P and dP over every key, which saves two
+ * of the dq kernel's five products per (query, key) pair.  O_i in fp32 differs from the exact O_i
+ * only by the forward's fp16 rounding of P, unlike the bf16 output, whose rounding alone moves D
+ * beyond the gradients' accuracy bound.  Results meet the same bound either way; they are
+ * bitwise repeatable and batch-invariant for each choice, and the two choices differ in the last
+ * bits.  o32 must not overlap an output or the workspace. */
+int h3attn_bwd_ex(const void* dout, const void* q, const void* k, const void* v, const float* lse, const float* o32,
+                  const int32_t* seg_ids, const int32_t* pos_ids, const void* wq, const void* wk, int64_t tokens,
+                  int32_t heads, int32_t head_dim, float eps, float scale, void* dq, void* dk, void* dv, float* dwq,
+                  float* dwk, void* workspace, size_t workspace_bytes, void* stream);
 
 /* Wait for `stream`, then copy the workspace's device status word to *device_status (host memory):
  * H3ATTN_OK, H3ATTN_ERR_SEGMENTS, H3ATTN_ERR_POSITIONS or H3ATTN_ERR_RANGE (in this order of

@@ -22,7 +22,7 @@ def declared_functions():
 def test_every_declared_symbol_is_exported():
     lib = h3.load()
     names = declared_functions()
-    assert len(names) == 13
+    assert len(names) == 15
     for n in names:
         assert hasattr(lib, n), f"{n} missing from libh3attn.so"
     assert sorted(h3.EXPORTS) == names
@@ -203,3 +203,38 @@ def test_bwd_pos_argument_errors():
     if not torch.cuda.is_available():
         assert bwd(lib, wsb=full - 512) == h3.H3ATTN_ERR_DEVICE   # enough for the plain backward
         assert bwd_pos(lib) == h3.H3ATTN_ERR_DEVICE
+
+
+def test_ex_argument_errors():
+    """h3attn_fwd_ex / h3attn_bwd_ex: the optional fp32 output is checked like any other buffer."""
+    lib = h3.load()
+    wsb = h3.h3attn_workspace_bytes(16, 2)
+    O32 = A + 0xE000000
+    n = 16 * 2 * 128 * 2
+
+    def fx(pos=None, o32=O32, out=A + 0x5000000, lse=None, T=16):
+        return lib.h3attn_fwd_ex(A, A + 0x1000000, A + 0x2000000, A + 0x3000000, pos, A + 0x4000000, A + 0x4001000,
+                                 T, 2, 128, 1e-6, 0.088, out, lse, o32, A + 0x6000000, wsb, None)
+
+    assert fx(T=0) == h3.H3ATTN_OK
+    assert fx(o32=O32 + 4) == h3.H3ATTN_ERR_ALIGN
+    assert fx(o32=A + 0x5000000 - 64) == h3.H3ATTN_ERR_ALIAS          # runs into out
+    assert fx(o32=A + 0x1000000 + n - 16) == h3.H3ATTN_ERR_ALIAS      # overlaps k
+    assert fx(o32=A + 0x6000000 + 256) == h3.H3ATTN_ERR_ALIAS         # inside the workspace
+    assert fx(lse=O32 + 1024) == h3.H3ATTN_ERR_ALIAS                  # lse inside o32
+    assert fx(pos=A + 0xD000002) == h3.H3ATTN_ERR_ALIGN
+    bwsb = h3.h3attn_bwd_workspace_bytes(16, 2)
+
+    def bx(o32=O32, pos=None, dq=A + 0x9000000):
+        return lib.h3attn_bwd_ex(A + 0x7000000, A, A + 0x1000000, A + 0x2000000, A + 0x8000000, o32, A + 0x3000000,
+                                 pos, A + 0x4000000, A + 0x4001000, 16, 2, 128, 1e-6, 0.088, dq, A + 0xA000000,
+                                 A + 0xB000000, A + 0xC000000, A + 0xC001000, A + 0x10000000, bwsb, None)
+
+    assert bx(o32=O32 + 8) == h3.H3ATTN_ERR_ALIGN
+    assert bx(dq=O32) == h3.H3ATTN_ERR_ALIAS                          # an output on o32
+    assert bx(o32=A + 0x10000000 + 512) == h3.H3ATTN_ERR_ALIAS        # o32 inside the workspace
+    import torch
+    if not torch.cuda.is_available():
+        assert fx() == h3.H3ATTN_ERR_DEVICE and fx(o32=None) == h3.H3ATTN_ERR_DEVICE
+        assert fx(pos=A + 0xD000000) == h3.H3ATTN_ERR_DEVICE
+        assert bx() == h3.H3ATTN_ERR_DEVICE and bx(o32=None) == h3.H3ATTN_ERR_DEVICE

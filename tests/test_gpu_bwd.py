@@ -20,21 +20,30 @@ from gpu_util import EPS, MAX_ABS_BOUND, REL_L2_BOUND, bitwise_equal, digest, f6
 
 pytestmark = pytest.mark.gpu
 SCALE = 128 ** -0.5
+# How D_i = sum_j P_ij dP_ij is formed: recomputed by the dq kernel (h3attn_bwd), or dO . O from the
+# forward's fp32 output (h3attn_fwd_ex / h3attn_bwd_ex with o32).  Every property holds for both.
+DMODES = ["recompute", "o32"]
 
 
-def run_bwd(g, weights=True, eps=EPS, scale=SCALE):
+def run_bwd(g, weights=True, eps=EPS, scale=SCALE, dmode="recompute"):
     wq, wk = (g["wq"], g["wk"]) if weights else (None, None)
-    _, lse = h3.h3attn_fwd(g["q"], g["k"], g["v"], g["seg"], wq, wk, eps=eps, scale=scale, want_lse=True)
-    res = h3.h3attn_bwd(g["dout"], g["q"], g["k"], g["v"], lse, g["seg"], wq, wk, eps=eps, scale=scale)
+    if dmode == "o32":
+        _, lse, o32 = h3.h3attn_fwd_ex(g["q"], g["k"], g["v"], g["seg"], None, wq, wk, eps=eps, scale=scale,
+                                       want_lse=True, want_o32=True)
+        res = h3.h3attn_bwd_ex(g["dout"], g["q"], g["k"], g["v"], lse, g["seg"], None, o32, wq, wk, eps=eps,
+                               scale=scale)
+    else:
+        _, lse = h3.h3attn_fwd(g["q"], g["k"], g["v"], g["seg"], wq, wk, eps=eps, scale=scale, want_lse=True)
+        res = h3.h3attn_bwd(g["dout"], g["q"], g["k"], g["v"], lse, g["seg"], wq, wk, eps=eps, scale=scale)
     torch.cuda.synchronize()
     return res
 
 
-def _check(name, x, heads=None, weights=True, eps=EPS, scale=SCALE):
+def _check(name, x, heads=None, weights=True, eps=EPS, scale=SCALE, dmode="recompute"):
     g = to_dev(x)
     T, H = x["q"].shape[0], x["q"].shape[1]
-    say(f"[bwd parity] {name}: T={T} H={H} heads={'all' if heads is None else heads}")
-    dq, dk, dv, dwq, dwk = run_bwd(g, weights=weights, eps=eps, scale=scale)
+    say(f"[bwd parity] {name} ({dmode}): T={T} H={H} heads={'all' if heads is None else heads}")
+    dq, dk, dv, dwq, dwk = run_bwd(g, weights=weights, eps=eps, scale=scale, dmode=dmode)
     hs = slice(None) if heads is None else list(heads)
     sub = {n: (x[n][:, hs].contiguous() if n in ("q", "k", "v", "dout") else x[n]) for n in x}
     wq, wk = (x["wq"], x["wk"]) if weights else (None, None)
@@ -55,40 +64,48 @@ def _check(name, x, heads=None, weights=True, eps=EPS, scale=SCALE):
     return dq, dk, dv
 
 
-def test_bwd_parity_tiny():
-    _check("tiny", workloads.make_inputs(workloads.WORKLOADS["tiny"], with_grad=True))
+@pytest.mark.parametrize("dmode", DMODES)
+def test_bwd_parity_tiny(dmode):
+    _check("tiny", workloads.make_inputs(workloads.WORKLOADS["tiny"], with_grad=True), dmode=dmode)
 
 
-def test_bwd_parity_ragged():
+@pytest.mark.parametrize("dmode", DMODES)
+def test_bwd_parity_ragged(dmode):
     """Segment lengths around the 64-row tiles and the 128-row work items, single-token segments."""
     lens = [1, 2, 31, 63, 64, 65, 127, 128, 129, 200, 3, 1, 257]
-    _check("ragged", workloads.random_inputs(lens, 3, seed=31, with_grad=True))
+    _check("ragged", workloads.random_inputs(lens, 3, seed=31, with_grad=True), dmode=dmode)
 
 
-def test_bwd_parity_short3():
-    _check("short3", workloads.make_inputs(workloads.WORKLOADS["short3"], with_grad=True))
+@pytest.mark.parametrize("dmode", DMODES)
+def test_bwd_parity_short3(dmode):
+    _check("short3", workloads.make_inputs(workloads.WORKLOADS["short3"], with_grad=True), dmode=dmode)
 
 
-def test_bwd_parity_without_weights():
-    _check("no-norm", workloads.random_inputs([150, 77], 2, seed=12, normed=False, with_grad=True), weights=False)
+@pytest.mark.parametrize("dmode", DMODES)
+def test_bwd_parity_without_weights(dmode):
+    _check("no-norm", workloads.random_inputs([150, 77], 2, seed=12, normed=False, with_grad=True), weights=False,
+           dmode=dmode)
 
 
-def test_bwd_parity_sharp_softmax():
+@pytest.mark.parametrize("dmode", DMODES)
+def test_bwd_parity_sharp_softmax(dmode):
     """Norm weights x3 (max logit ~50): the case where D from the rounded forward output would fail."""
-    _check("sharp-w3", workloads.random_inputs([500, 130], 2, seed=13, w_scale=3.0, with_grad=True))
+    _check("sharp-w3", workloads.random_inputs([500, 130], 2, seed=13, w_scale=3.0, with_grad=True), dmode=dmode)
 
 
-def test_bwd_parity_many_segments():
+@pytest.mark.parametrize("dmode", DMODES)
+def test_bwd_parity_many_segments(dmode):
     """300 segments of random lengths 1..100 (every cost class of the work order, many items per
     class), 2 heads, against the oracle."""
     rng = np.random.default_rng(41)
     lens = [int(x) for x in rng.integers(1, 101, 300)]
-    _check("many-segments", workloads.random_inputs(lens, 2, seed=42, with_grad=True))
+    _check("many-segments", workloads.random_inputs(lens, 2, seed=42, with_grad=True), dmode=dmode)
 
 
-def test_bwd_parity_other_scale_and_eps():
+@pytest.mark.parametrize("dmode", DMODES)
+def test_bwd_parity_other_scale_and_eps(dmode):
     x = workloads.random_inputs([150, 90], 2, seed=9, with_grad=True)
-    _check("scale0.2-eps1e-3", x, eps=float(np.float32(1e-3)), scale=0.2)
+    _check("scale0.2-eps1e-3", x, eps=float(np.float32(1e-3)), scale=0.2, dmode=dmode)
 
 
 def test_bwd_empty_input_is_a_noop():
@@ -101,64 +118,71 @@ def test_bwd_empty_input_is_a_noop():
     assert dq.numel() == 0 and dk.numel() == 0 and dv.numel() == 0
 
 
-def test_bwd_parity_batch2_heads():
+@pytest.mark.parametrize("dmode", DMODES)
+def test_bwd_parity_batch2_heads(dmode):
     """Config 5 (2 x 4253 tokens, 40 heads) at full size, heads 0, 17 and 39 against the oracle."""
-    _check("batch2", workloads.make_inputs(workloads.WORKLOADS["batch2"], with_grad=True), heads=(0, 17, 39))
+    _check("batch2", workloads.make_inputs(workloads.WORKLOADS["batch2"], with_grad=True), heads=(0, 17, 39),
+           dmode=dmode)
 
 
-def test_bwd_repeat_bitwise():
+@pytest.mark.parametrize("dmode", DMODES)
+def test_bwd_repeat_bitwise(dmode):
     g = to_dev(workloads.make_inputs(workloads.WORKLOADS["short3"], with_grad=True))
-    say("[bwd bitwise] short3 repeat x5")
-    ref = [digest(t) for t in run_bwd(g)]
+    say(f"[bwd bitwise] short3 repeat x5 ({dmode})")
+    ref = [digest(t) for t in run_bwd(g, dmode=dmode)]
     for _ in range(4):
-        assert [digest(t) for t in run_bwd(g)] == ref
+        assert [digest(t) for t in run_bwd(g, dmode=dmode)] == ref
 
 
-def test_bwd_repeat_bitwise_batch2():
+@pytest.mark.parametrize("dmode", DMODES)
+def test_bwd_repeat_bitwise_batch2(dmode):
     """Full config-5 size, all five outputs: many tiles per item, so a wave that read a 64-row tile
     before another wave's copy of it had landed would show up as differing bits."""
     g = to_dev(workloads.make_inputs(workloads.WORKLOADS["batch2"], with_grad=True))
-    say("[bwd bitwise] batch2 repeat x3")
-    ref = [digest(t) for t in run_bwd(g)]
+    say(f"[bwd bitwise] batch2 repeat x3 ({dmode})")
+    ref = [digest(t) for t in run_bwd(g, dmode=dmode)]
     for _ in range(2):
-        assert [digest(t) for t in run_bwd(g)] == ref
+        assert [digest(t) for t in run_bwd(g, dmode=dmode)] == ref
 
 
-def test_bwd_batch2_alone_equals_batched():
+@pytest.mark.parametrize("dmode", DMODES)
+def test_bwd_batch2_alone_equals_batched(dmode):
     """Each packed row's dq, dk, dv are the same bits alone as inside the batch (rollout vs train)."""
     wl = workloads.WORKLOADS["batch2"]
     g = to_dev(workloads.make_inputs(wl, with_grad=True))
-    say("[bwd bitwise] batch2 alone vs batched")
-    bq, bk, bv, _, _ = run_bwd(g)
+    say(f"[bwd bitwise] batch2 alone vs batched ({dmode})")
+    bq, bk, bv, _, _ = run_bwd(g, dmode=dmode)
     for (t0, t1) in workloads.row_slices(wl):
         alone = {n: (g[n][t0:t1].contiguous() if n in ("q", "k", "v", "seg", "dout") else g[n]) for n in g}
-        q, k, v, _, _ = run_bwd(alone)
+        q, k, v, _, _ = run_bwd(alone, dmode=dmode)
         assert bitwise_equal(q, bq[t0:t1]) and bitwise_equal(k, bk[t0:t1]) and bitwise_equal(v, bv[t0:t1])
 
 
+@pytest.mark.parametrize("dmode", DMODES)
 @pytest.mark.parametrize("pad", [1, 64, 127])
-def test_bwd_leading_segment_offset_invariance(pad):
+def test_bwd_leading_segment_offset_invariance(pad, dmode):
     x = workloads.random_inputs([300, 129, 64], 3, seed=17, with_grad=True)
     g = to_dev(x)
     say(f"[bwd bitwise] offset shift by a {pad}-token leading segment")
-    base = run_bwd(g)[:3]
+    base = run_bwd(g, dmode=dmode)[:3]
     d = workloads.random_inputs([pad], 3, seed=99, with_grad=True)
     sh = {n: torch.cat([d[n].to(g[n].device), g[n]]) for n in ("q", "k", "v", "dout")}
     sh["seg"] = torch.cat([torch.full((pad,), -1, dtype=torch.int32), x["seg"]]).to(g["seg"].device)
     sh["wq"], sh["wk"] = g["wq"], g["wk"]
-    shifted = run_bwd(sh)[:3]
+    shifted = run_bwd(sh, dmode=dmode)[:3]
     for a, b in zip(shifted, base):
         assert bitwise_equal(a[pad:], b)
 
 
-def test_bwd_nan_neighbour_does_not_leak():
+@pytest.mark.parametrize("dmode", DMODES)
+def test_bwd_nan_neighbour_does_not_leak(dmode):
     x = workloads.random_inputs([40, 70, 33], 2, seed=5, with_grad=True)
     g = to_dev(x)
-    base = run_bwd(g)[:3]
+    base = run_bwd(g, dmode=dmode)[:3]
     y = {n: g[n].clone() for n in g}
     for n in ("q", "k", "v", "dout"):
         y[n][40:110] = float("nan")
-    got = run_bwd(y)[:3]
+    got = run_bwd(y, dmode=dmode)[:3]
     for a, b in zip(got, base):
         assert bitwise_equal(a[:40], b[:40]) and bitwise_equal(a[110:], b[110:])
 
@@ -176,3 +200,38 @@ def test_bwd_dout_out_of_fp16_range_sets_status():
     assert h3.h3attn_status_read(ws) == h3.H3ATTN_ERR_RANGE
     for t in (dq, dk, dv, dwq, dwk):
         assert torch.isnan(t.float()).all()
+
+
+def test_fwd_ex_o32_is_the_output_before_its_rounding():
+    """o32 rounds (RNE) to exactly the bf16 output, in packed and in position order, and changes no
+    bit of out or lse."""
+    lens = [300, 129, 64, 1]
+    x = workloads.random_inputs(lens, 3, seed=61)
+    g = to_dev(x)
+    say("[fwd_ex] o32 vs out")
+    out, lse = h3.h3attn_fwd(g["q"], g["k"], g["v"], g["seg"], g["wq"], g["wk"], eps=EPS, want_lse=True)
+    out2, lse2, o32 = h3.h3attn_fwd_ex(g["q"], g["k"], g["v"], g["seg"], None, g["wq"], g["wk"], eps=EPS,
+                                       want_lse=True, want_o32=True)
+    pos = workloads.position_ids(lens).cuda()
+    out3, lse3, o32b = h3.h3attn_fwd_ex(g["q"], g["k"], g["v"], g["seg"], pos, g["wq"], g["wk"], eps=EPS,
+                                        want_lse=True, want_o32=True)
+    torch.cuda.synchronize()
+    assert bitwise_equal(out, out2) and bitwise_equal(lse, lse2) and bitwise_equal(out, out3)
+    assert bitwise_equal(o32.to(torch.bfloat16), out)
+    assert torch.equal(o32, o32b)
+    ref, _ = oracle.fwd(x["q"], x["k"], x["v"], x["seg"].numpy(), x["wq"], x["wk"], EPS, SCALE)
+    rel, mx = metrics(o32, ref)
+    say(f"[fwd_ex] o32 vs oracle: rel_l2={rel:.3e} max_abs={mx:.3e}")
+    assert rel <= REL_L2_BOUND and mx <= MAX_ABS_BOUND
+
+
+def test_fwd_ex_o32_nan_filled_on_data_error():
+    x = workloads.random_inputs([40, 40], 2, seed=53)
+    x["v"][10, 1, 5] = 1.0e5
+    g = to_dev(x)
+    ws = h3.workspace(80, 2, "cuda:0")
+    out, lse, o32 = h3.h3attn_fwd_ex(g["q"], g["k"], g["v"], g["seg"], None, g["wq"], g["wk"], eps=EPS,
+                                     want_lse=True, want_o32=True, workspace_buf=ws)
+    torch.cuda.synchronize()
+    assert h3.h3attn_status_read(ws) == h3.H3ATTN_ERR_RANGE
+    assert torch.isnan(o32).all() and torch.isnan(out.float()).all()

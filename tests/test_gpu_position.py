@@ -242,3 +242,27 @@ def test_empty_input_is_a_noop():
     res = h3.h3attn_bwd_pos(e, e, e, e, torch.empty((0, 2), device="cuda:0"), seg, seg, w, w)
     torch.cuda.synchronize()
     assert out.numel() == 0 and lse.numel() == 0 and res[0].numel() == 0
+
+
+def test_bwd_shuffle_with_o32_is_bitwise_invariant():
+    """The same with D = dO . O from the forward's fp32 output (h3attn_fwd_ex / h3attn_bwd_ex)."""
+    x = workloads.random_inputs(RAGGED, 3, seed=87, with_grad=True)
+    g = to_dev(x)
+    pos = workloads.position_ids(RAGGED).cuda()
+
+    def run(gg, pp):
+        _, lse, o32 = h3.h3attn_fwd_ex(gg["q"], gg["k"], gg["v"], gg["seg"], pp, gg["wq"], gg["wk"], eps=EPS,
+                                       scale=SCALE, want_lse=True, want_o32=True)
+        res = h3.h3attn_bwd_ex(gg["dout"], gg["q"], gg["k"], gg["v"], lse, gg["seg"], pp, o32, gg["wq"], gg["wk"],
+                               eps=EPS, scale=SCALE)
+        torch.cuda.synchronize()
+        return res
+
+    base = run(g, pos)
+    y, pos_y, p = shuffled(x, RAGGED, 3)
+    say("[position] bwd_ex with o32, shuffled")
+    got = run(to_dev(y), pos_y.cuda())
+    pd = p.cuda()
+    for a, b in zip(got[:3], base[:3]):
+        assert bitwise_equal(a, b[pd])
+    assert torch.equal(got[3], base[3]) and torch.equal(got[4], base[4])
