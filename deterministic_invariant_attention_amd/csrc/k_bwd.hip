@@ -25,6 +25,7 @@
 // softmax the rounding of O moves D enough to cost dq and dk about twice the accuracy bound.
 // P and dS enter their products as fp16 (bf16 would miss the bound, as for the forward's P).
 #include "h3_common.h"
+#include "h3_norm.h"
 #include "h3_bwd.h"
 #include "h3_launch.h"
 #include "h3_tiles_bwd.h"

@@ -7,6 +7,7 @@
 // each wave moves 4 rows with fully coalesced 16-byte accesses.  The sum of squares follows the
 // fixed tree of h3_common.h, so every kernel here gives the bits of the standalone norm.
 #include "h3_common.h"
+#include "h3_norm.h"
 #include "h3_bwd.h"
 #include "h3_launch.h"
 
