@@ -204,6 +204,7 @@ def main():
                    "qk_draw_scale": wl.qk_scale, "pv_operands": "fp16", "accumulate": "fp32",
                    "key_order": args.order,
                    "pct_bf16_mfma_peak": round(100 * value / PEAK_MFMA_TFLOPS, 2),
+                   "algorithmic_GBps": round(wl.algorithmic_bytes() / (ms_per_step * 1e-3) / 1e9, 1),
                    "repeat_bitwise": repeat_bitwise, "device_status": status},
         "roofline": {"bound": "mfma", "achieved": round(attn_tflops, 2), "peak": PEAK_MFMA_TFLOPS,
                      "unit": "TFLOP/s", "frac": round(attn_tflops / PEAK_MFMA_TFLOPS, 4),
