@@ -11,18 +11,22 @@
 // Two attention kernels, neither with atomics, both walking their inner dimension in ascending,
 // segment-anchored 64-row tiles, so every gradient row is a fixed function of its own segment:
 //   k_bwd_dq    work item = (segment, 128-query tile, head).  Pass 1 over the key tiles computes
-//               D_i exactly (in fp32, a fixed tree per tile); pass 2 recomputes S and dP, forms dS
-//               and accumulates dQ^T += K^16^T dS^T.
+//               D_i exactly (in fp32, a fixed tree per tile) unless the staging kernel formed it
+//               from the forward's fp32 output; pass 2 recomputes S and dP, forms dS and
+//               accumulates dQ^T += K^16^T dS^T.
 //   k_bwd_dkdv  work item = (segment, 128-key tile, head).  One pass over the query tiles:
 //               S = Q^ K^T and dP = dO V^T with the wave's 32 keys in registers, P and dS in fp16,
-//               dV^T += dO16^T P and dK^T += Q^16^T dS; the scores of query tile j+1 are computed
-//               before the products of tile j, whose transposed reads run as one pipeline.
+//               dV^T += dO16^T P and dK^T += Q^16^T dS, whose transposed reads run as one pipeline.
+// A wave's vector work overlaps its own MFMAs when a few independent instructions sit between
+// them, so P is formed between the dP MFMAs and dS between the MFMAs that only need P (dV's in
+// dk/dv, the first dQ steps in dq), each packed slice finished before its first use.
 // With norm weights both write dq^ / dk^ in fp32 and k_bwd_norm applies the RMSNorm backward per
 // row (FP64, one bf16 rounding) and writes fixed-order weight-gradient partials, which two small
 // kernels sum in a fixed tree; without weights the kernels write dq, dk directly.
 //
-// D is recomputed rather than taken as rowsum(dO o O) from the forward's bf16 output: with a sharp
-// softmax the rounding of O moves D enough to cost dq and dk about twice the accuracy bound.
+// D is recomputed (or formed from the forward's fp32 output) rather than taken as rowsum(dO o O)
+// from the bf16 output: with a sharp softmax that rounding moves D enough to cost dq and dk about
+// twice the accuracy bound.
 // P and dS enter their products as fp16 (bf16 would miss the bound, as for the forward's P).
 #include "h3_common.h"
 #include "h3_norm.h"
@@ -292,20 +296,38 @@ __global__ __launch_bounds__(64 * BW, 1) void k_bwd_dq(BwdParams p) {
       constexpr int ST = decltype(stage)::value;
       copies_barrier();  // tile j has landed, every wave is done with stage 1 - ST
       if (j + 1 < ntk) copies(j + 1, Par2<1 - ST>{});
+      // P between the dP MFMAs (two elements per step); dS slice 0 before the dQ products and
+      // slice k between the MFMAs of steps 4(k-1) .. 4k-1, four steps before its first use.
       f32x16 S[2], dP[2];
-      scores(stage, j, S, dP);
-      float ds[32];
+      gemm_rows<0 + ST>(rb, qf, S, [](auto) {});
+      if (j == ntk - 1 && rem < TILE_ROWS) mask_tail(S, rem, hh);
+      float pr[32], ds[32];
+      gemm_rows<2 + ST>(rb, gf, dP, [&](auto st) {
+        constexpr int s = decltype(st)::value;
 #pragma unroll
-      for (int kbk = 0; kbk < 2; kbk++)
-#pragma unroll
-        for (int i = 0; i < 16; i++)
-          ds[16 * kbk + i] = __builtin_amdgcn_exp2f(__builtin_fmaf(S[kbk][i], c, -lq)) * (dP[kbk][i] - Dq);
+        for (int u = 0; u < 2; u++) {
+          const int e = 2 * s + u;
+          pr[e] = __builtin_amdgcn_exp2f(__builtin_fmaf(S[e >> 4][e & 15], c, -lq));
+        }
+      });
       f16x8 dsf[4];
 #pragma unroll
-      for (int ks = 0; ks < 4; ks++) dsf[ks] = pack_p(&ds[8 * ks]);
+      for (int e = 0; e < 8; e++) ds[e] = pr[e] * (dP[0][e] - Dq);
+      dsf[0] = pack_p(&ds[0]);
       const f16x8* bop[1] = {dsf};
       f32x16* accp[1] = {acc};
-      tr_gemm_hooked<TilePair<ST, ST>, 1>(vb, bop, accp, [](auto) {});
+      tr_gemm_hooked<TilePair<ST, ST>, 1>(vb, bop, accp, [&](auto st) {
+        constexpr int s = decltype(st)::value;
+        if constexpr (s < 12) {
+          constexpr int sl = (s >> 2) + 1;
+#pragma unroll
+          for (int u = 0; u < 2; u++) {
+            const int e = 8 * sl + 2 * (s & 3) + u;
+            ds[e] = pr[e] * (dP[e >> 4][e & 15] - Dq);
+          }
+          if constexpr ((s & 3) == 3) dsf[sl] = pack_p(&ds[8 * sl]);
+        }
+      });
     };
     {
       int j = 0;
@@ -420,25 +442,32 @@ __global__ __launch_bounds__(64 * BW, 1) void k_bwd_dkdv(BwdParams p) {
       for (int q2 = 0; q2 < 2; q2++)
 #pragma unroll
         for (int g = 0; g < 4; g++) asm volatile("" : "+v"(l4[q2][g]), "+v"(d4[q2][g]));
-      gemm_rows<2 + ST>(rb, vf, dP, [](auto) {});
+      // P (two elements per step, a packed 8-query slice every fourth step) between the dP MFMAs,
+      // and dS between the dV MFMAs (which only need P); dK's MFMAs start after the last dS slice.
       float pr[2][16], ds[2][16];
-#pragma unroll
-      for (int q2 = 0; q2 < 2; q2++)
-#pragma unroll
-        for (int i = 0; i < 16; i++) {
-          const float pv = __builtin_amdgcn_exp2f(__builtin_fmaf(S[q2][i], c, -l4[q2][i >> 2][i & 3]));
-          pr[q2][i] = pv;
-          ds[q2][i] = pv * (dP[q2][i] - d4[q2][i >> 2][i & 3]);
-        }
       f16x8 pf[4], dsf[4];
+      gemm_rows<2 + ST>(rb, vf, dP, [&](auto st) {
+        constexpr int s = decltype(st)::value;
 #pragma unroll
-      for (int ks = 0; ks < 4; ks++) {
-        pf[ks] = pack_p(&pr[ks >> 1][8 * (ks & 1)]);
-        dsf[ks] = pack_p(&ds[ks >> 1][8 * (ks & 1)]);
-      }
+        for (int u = 0; u < 2; u++) {
+          const int e = 2 * s + u, q2 = e >> 4, i = e & 15;
+          pr[q2][i] = __builtin_amdgcn_exp2f(__builtin_fmaf(S[q2][i], c, -l4[q2][i >> 2][i & 3]));
+        }
+        if constexpr ((s & 3) == 3) pf[s >> 2] = pack_p(&pr[s >> 3][8 * ((s >> 2) & 1)]);
+      });
       const f16x8* bop[2] = {pf, dsf};
       f32x16* acc[2] = {dv, dk};
-      tr_gemm_hooked<TilePair<2 + ST, 0 + ST>, 2>(vb, bop, acc, [](auto) {});
+      tr_gemm_hooked<TilePair<2 + ST, 0 + ST>, 2>(vb, bop, acc, [&](auto st) {
+        constexpr int s = decltype(st)::value;
+        if constexpr (s < 16) {
+#pragma unroll
+          for (int u = 0; u < 2; u++) {
+            const int e = 2 * s + u, q2 = e >> 4, i = e & 15;
+            ds[q2][i] = pr[q2][i] * (dP[q2][i] - d4[q2][i >> 2][i & 3]);
+          }
+          if constexpr ((s & 3) == 3) dsf[s >> 2] = pack_p(&ds[s >> 3][8 * ((s >> 2) & 1)]);
+        }
+      });
     };
     {
       int j = 0;
