@@ -182,6 +182,14 @@ struct Par2 {
   static constexpr int value = N;
 };
 
+template <int I, int N, class F>
+__device__ __forceinline__ void static_for2(F&& f) {
+  if constexpr (I < N) {
+    f(StepIdx<I>{});
+    static_for2<I + 1, N>(f);
+  }
+}
+
 // ============================================================================== dq (and D)
 
 __global__ __launch_bounds__(64 * BW, 1) void k_bwd_dq(BwdParams p) {
@@ -357,7 +365,6 @@ __global__ __launch_bounds__(64 * BW, 1) void k_bwd_dkdv(BwdParams p) {
   // tiles 0, 1: Q^16 and 2, 3: dO16 of stage 0 / 1, in the unified layout (read by rows for S and
   // dP, transposed for dK and dV); then the fp32 rows [stage][lse2, D][64 queries]
   __shared__ __attribute__((aligned(1024))) uint16_t lds[4 * TILE_ELEMS + 2 * 2 * TILE_ROWS * 2];
-  const float* lrow = (const float*)(lds + 4 * TILE_ELEMS);  // lrow[(2 * stage + which) * 64 + query]
   lds_char* const lrow3 = (lds_char*)lds + 4 * TILE_ELEMS * 2;  // the same rows as an LDS address
 
   const int tid = threadIdx.x;
@@ -375,6 +382,7 @@ __global__ __launch_bounds__(64 * BW, 1) void k_bwd_dkdv(BwdParams p) {
   uint32_t vb[8];
   tr_bases_u(lds, lane, vb);
   const RowBases rb = row_bases_u(lds, l32, hh);
+  const uint32_t lrow_lane = (uint32_t)(size_t)lrow3 + 16 * hh;  // lrow[4hh] as an LDS byte address
   const float c = p.c;
 
   const int nbkt = min(max(p.hdr->nbkt, 0), NBKT);
@@ -429,15 +437,17 @@ __global__ __launch_bounds__(64 * BW, 1) void k_bwd_dkdv(BwdParams p) {
       if (j + 1 < ntq) copies(j + 1, Par2<1 - ST>{});
       f32x16 S[2], dP[2];
       f32x4 l4[2][4], d4[2][4];
-#pragma unroll
-      for (int q2 = 0; q2 < 2; q2++)
-#pragma unroll
-        for (int g = 0; g < 4; g++) {
-          l4[q2][g] = *(const f32x4*)&lrow[(2 * ST + 0) * TILE_ROWS + 32 * q2 + 8 * g + 4 * hh];
-          d4[q2][g] = *(const f32x4*)&lrow[(2 * ST + 1) * TILE_ROWS + 32 * q2 + 8 * g + 4 * hh];
-        }
+      // lse and D of the tile's queries, read as assembly: a plain LDS load here would make the
+      // compiler wait for every outstanding copy first (it cannot tell the copies' targets from
+      // these rows), which would expose the latency of the copies just issued
+      static_for2<0, 8>([&](auto gi) {
+        constexpr int q2 = decltype(gi)::value >> 2, g = decltype(gi)::value & 3;
+        l4[q2][g] = __builtin_bit_cast(f32x4, ds_read_b128_asm<((2 * ST + 0) * TILE_ROWS + 32 * q2 + 8 * g) * 4>(lrow_lane));
+        d4[q2][g] = __builtin_bit_cast(f32x4, ds_read_b128_asm<((2 * ST + 1) * TILE_ROWS + 32 * q2 + 8 * g) * 4>(lrow_lane));
+      });
       gemm_rows<0 + ST>(rb, kf, S, [](auto) {});
       // the lse/D reads complete here, before the next pipelines count their own reads
+      asm volatile("s_waitcnt lgkmcnt(0)" : "+v"(l4[0][0]), "+v"(d4[0][0]));
 #pragma unroll
       for (int q2 = 0; q2 < 2; q2++)
 #pragma unroll
