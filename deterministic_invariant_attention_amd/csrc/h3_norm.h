@@ -45,27 +45,29 @@ __device__ __forceinline__ double row_total_16lanes(double p) {
   return p;
 }
 
-// FP64 -> bf16 bit pattern, round to nearest even, in one step (no intermediate fp32 rounding).
-// |y| is rounded onto the bf16 grid of its binade by one add and one subtract of
-// c = 1.5 * 2^(e + 45), e = the binade's exponent clamped to [-126, 128]: the sum lies in c's
-// binade, whose spacing 2^(e - 7) is the bf16 spacing at |y| (2^-133 below 2^-126, the bf16
-// subnormals), so the IEEE adder rounds |y| to nearest with ties to an even multiple, which is the
-// even bf16 mantissa, and the subtraction is exact.  The result converts to fp32 exactly (or to
-// infinity past the bf16 range) and its top half is the bf16 pattern; NaN becomes the quiet NaN.
-// No branches: every element of a lane takes the same instructions.
-__device__ __forceinline__ uint32_t f64_to_bf16_rne(double y) {
-  const uint64_t b = __builtin_bit_cast(uint64_t, y);
-  const uint32_t hi = (uint32_t)(b >> 32);
-  const uint32_t sign = (hi >> 16) & 0x8000u;
-  const int ed = (int)((hi >> 20) & 0x7FFu);  // biased FP64 exponent
-  int e = ed - 1023;
-  e = e < -126 ? -126 : (e > 128 ? 128 : e);
-  const double c = __builtin_bit_cast(double, ((uint64_t)(e + 1068) << 52) | (1ull << 51));
-  const double a = __builtin_bit_cast(double, b & 0x7FFFFFFFFFFFFFFFull);
-  const double r = (a + c) - c;
-  uint32_t out = __builtin_bit_cast(uint32_t, (float)r) >> 16;
-  if (ed == 0x7FF && (b << 12) != 0) out = 0x7FC0u;
-  return sign | out;
+// FP64 -> bf16, round to nearest even, correctly rounded (as if rounded once from the FP64 value).
+// Two steps: y is first rounded to fp32 "to odd" (toward zero, with the last bit set when the
+// conversion is inexact), then that fp32 is rounded to bf16, nearest even, by the hardware
+// conversion.  Rounding to odd into a format with at least two more significand bits keeps the
+// information a later nearest-even rounding needs (fp32 has 24 bits against bf16's 8, and 16 more
+// bits in the subnormal range), so the two roundings give the one correct rounding of y.
+// The fp32 step: t = fp32(y) to nearest; r = y - t is exact in FP64 (at most 29 significant bits);
+// when r != 0 the conversion was inexact, and when r and y differ in sign t lies farther from zero
+// than y, so the value toward zero is the fp32 one step below t in magnitude (t's bit pattern - 1;
+// for t = infinity that is the largest finite fp32, which then rounds to bf16 infinity).  Exact
+// values (r == 0), infinities and NaN (r unordered) keep t.  No branches.
+__device__ __forceinline__ float f64_to_f32_odd(double y) {
+  const float t = (float)y;
+  const double r = y - (double)t;
+  const uint32_t inexact = (r < 0.0 || r > 0.0) ? 1u : 0u;
+  const uint32_t away =
+      (uint32_t)((__builtin_bit_cast(uint64_t, r) ^ __builtin_bit_cast(uint64_t, y)) >> 63) & inexact;
+  return __builtin_bit_cast(float, (__builtin_bit_cast(uint32_t, t) - away) | inexact);
+}
+
+// Two FP64 values -> packed bf16x2 (first value in the low half), each correctly rounded.
+__device__ __forceinline__ uint32_t f64x2_to_bf16x2_rne(double y0, double y1) {
+  return pack_bf16(f64_to_f32_odd(y0), f64_to_f32_odd(y1));
 }
 
 // Normalise one 8-channel chunk with the row's scale r and the chunk's weights; pack to bf16.
@@ -75,7 +77,7 @@ __device__ __forceinline__ u32x4 norm_chunk(const float* x, const float* w, doub
   for (int i = 0; i < 4; i++) {
     const double y0 = ((double)x[2 * i] * r) * (double)w[2 * i];
     const double y1 = ((double)x[2 * i + 1] * r) * (double)w[2 * i + 1];
-    o[i] = f64_to_bf16_rne(y0) | (f64_to_bf16_rne(y1) << 16);
+    o[i] = f64x2_to_bf16x2_rne(y0, y1);
   }
   return o;
 }

@@ -565,10 +565,8 @@ __global__ __launch_bounds__(256) void k_bwd_norm(NormBwdParams p) {
   u32x4 o;
 #pragma unroll
   for (int i = 0; i < 4; i++) {
-    const uint32_t a = f64_to_bf16_rne(r * ((double)wf[2 * i] * (double)dy[2 * i]) - k3 * (double)x[2 * i]);
-    const uint32_t b =
-        f64_to_bf16_rne(r * ((double)wf[2 * i + 1] * (double)dy[2 * i + 1]) - k3 * (double)x[2 * i + 1]);
-    o[i] = a | (b << 16);
+    o[i] = f64x2_to_bf16x2_rne(r * ((double)wf[2 * i] * (double)dy[2 * i]) - k3 * (double)x[2 * i],
+                               r * ((double)wf[2 * i + 1] * (double)dy[2 * i + 1]) - k3 * (double)x[2 * i + 1]);
   }
   if (valid) *(u32x4*)(p.dx[which] + xrow * HD + 8 * c) = o;
   f32x4 t0, t1;

@@ -5,7 +5,7 @@
 //
 // Mapping: 16 lanes per (token, head) row, lane c holds channels 8c..8c+7 (one 16-byte chunk), so
 // each wave moves 4 rows with fully coalesced 16-byte accesses.  The sum of squares follows the
-// fixed tree of h3_common.h, so every kernel here gives the bits of the standalone norm.
+// fixed tree of h3_norm.h, so every kernel here gives the bits of the standalone norm.
 #include "h3_common.h"
 #include "h3_norm.h"
 #include "h3_bwd.h"
@@ -16,13 +16,14 @@ namespace h3 {
 __device__ __forceinline__ u32x4 ld16(const uint16_t* p) { return *(const u32x4*)p; }
 __device__ __forceinline__ void st16(uint16_t* p, const u32x4& v) { *(u32x4*)p = v; }
 
-// Norm one row chunk held by this lane (16-lane mapping); every lane of the group must call it.
-__device__ __forceinline__ u32x4 norm_16lane(const u32x4& xv, const uint16_t* w, int c, float eps) {
+// Norm one row chunk held by this lane (16-lane mapping) with the lane's chunk of the weights;
+// every lane of the group must call it.
+__device__ __forceinline__ u32x4 norm_16lane(const u32x4& xv, const u32x4& wv, float eps) {
   float x[8], wf[8];
   unpack8_bf16(xv, x);
   const double total = row_total_16lanes(chunk_sumsq(x));
   const double r = norm_rscale(total, eps);
-  unpack8_bf16(ld16(w + c * 8), wf);
+  unpack8_bf16(wv, wf);
   return norm_chunk(x, wf, r);
 }
 
@@ -34,7 +35,7 @@ __global__ __launch_bounds__(256) void k_qknorm(const uint16_t* x, const uint16_
   const bool valid = row < rows;  // uniform over each 16-lane group
   u32x4 xv = {0, 0, 0, 0};
   if (valid) xv = ld16(x + row * HD + c * 8);
-  const u32x4 o = norm_16lane(xv, w, c, eps);
+  const u32x4 o = norm_16lane(xv, ld16(w + c * 8), eps);
   if (valid) st16(y + row * HD + c * 8, o);
 }
 
@@ -58,49 +59,53 @@ struct PrepParams {
   float eps;
 };
 
-// rows are visited token-major (r = t*H + h) so the reads are contiguous; each row is written to
-// its head-major staged row.
+// Rows are visited token-major (r = t*H + h) so the reads are contiguous; each row is written to
+// its head-major staged row.  Every load of the row precedes every store (the outputs live in
+// another buffer, but the compiler cannot know that), so each lane's three reads are in flight
+// together.
 __global__ __launch_bounds__(256) void k_prep_qkv(PrepParams p) {
-  const int64_t g = (int64_t)blockIdx.x * 256 + threadIdx.x;
-  const int64_t row = g >> 4;
   const int c = threadIdx.x & 15;
   const int64_t T = p.T;
-  const int64_t rows = T * p.H;
-  const bool valid = row < rows;
-  const int64_t t = valid ? row / p.H : 0;
+  const int64_t row = ((int64_t)blockIdx.x * 256 + threadIdx.x) >> 4;
+  const bool valid = row < T * p.H;
+  // T * H < 2^31 (the shape check of every entry point), so 32-bit division places the row
+  const int64_t t = valid ? (int64_t)((uint32_t)row / (uint32_t)p.H) : 0;
   const int64_t h = valid ? row - t * p.H : 0;
-  const int64_t ts = p.slot ? (int64_t)p.slot[t] : t;  // slot[t] is in [0, T) by construction
-  const int64_t dst = (h * T + ts) * HD + c * 8;
+  const int64_t ts = (valid && p.slot) ? (int64_t)p.slot[t] : t;  // slot[t] is in [0, T) by construction
+  const u32x4 zero4 = {0, 0, 0, 0};
+  const u32x4 wqv = p.wq ? ld16(p.wq + c * 8) : zero4, wkv = p.wk ? ld16(p.wk + c * 8) : zero4;
+  {
+    const int64_t src = row * HD + c * 8;
+    u32x4 qv = {0, 0, 0, 0}, kv = {0, 0, 0, 0}, vv = {0, 0, 0, 0};
+    if (valid) {
+      if (p.wq) qv = ld16(p.q + src);
+      kv = ld16(p.k + src);
+      vv = ld16(p.v + src);
+    }
+    if (p.wq) {
+      const u32x4 qo = norm_16lane(qv, wqv, p.eps);
+      if (valid) st16(p.qhat + (h * T + t) * HD + c * 8, qo);
+    }
+    const u32x4 ko = p.wk ? norm_16lane(kv, wkv, p.eps) : kv;
 
-  if (p.wq) {
-    u32x4 qv = {0, 0, 0, 0};
-    if (valid) qv = ld16(p.q + row * HD + c * 8);
-    const u32x4 qo = norm_16lane(qv, p.wq, c, p.eps);
-    if (valid) st16(p.qhat + (h * T + t) * HD + c * 8, qo);
-  }
-  u32x4 kv = {0, 0, 0, 0}, vv = {0, 0, 0, 0};
-  if (valid) {
-    kv = ld16(p.k + row * HD + c * 8);
-    vv = ld16(p.v + row * HD + c * 8);
-  }
-  const u32x4 ko = p.wk ? norm_16lane(kv, p.wk, c, p.eps) : kv;
-
-  // V: bf16 -> fp16, exact for normal fp16 magnitudes; a finite |v| > 65504 would overflow.
-  u32x4 vo;
-  bool over = false;
+    // V: bf16 -> fp16, exact for normal fp16 magnitudes; a finite |v| > 65504 would overflow.
+    u32x4 vo;
+    bool over = false;
 #pragma unroll
-  for (int i = 0; i < 4; i++) {
-    const float a = bf16_lo(vv[i]), b = bf16_hi(vv[i]);
-    over |= (__builtin_fabsf(a) > 65504.0f && __builtin_fabsf(a) != __builtin_inff());
-    over |= (__builtin_fabsf(b) > 65504.0f && __builtin_fabsf(b) != __builtin_inff());
-    vo[i] = pack_f16(a, b);
+    for (int i = 0; i < 4; i++) {
+      const float a = bf16_lo(vv[i]), b = bf16_hi(vv[i]);
+      over |= (__builtin_fabsf(a) > 65504.0f && __builtin_fabsf(a) != __builtin_inff());
+      over |= (__builtin_fabsf(b) > 65504.0f && __builtin_fabsf(b) != __builtin_inff());
+      vo[i] = pack_f16(a, b);
+    }
+    const int64_t dst = (h * T + ts) * HD + c * 8;
+    if (valid) {
+      st16(p.khat + dst, ko);
+      st16(p.v16 + dst, vo);
+    }
+    const uint64_t any_over = __ballot(valid && over);
+    if (any_over && (threadIdx.x & 63) == __builtin_ctzll(any_over)) atomicOr(&p.hdr->status, STATUS_RANGE_BIT);
   }
-  if (valid) {
-    st16(p.khat + dst, ko);
-    st16(p.v16 + dst, vo);
-  }
-  const uint64_t any_over = __ballot(valid && over);
-  if (any_over && (threadIdx.x & 63) == __builtin_ctzll(any_over)) atomicOr(&p.hdr->status, STATUS_RANGE_BIT);
 }
 
 // Operand staging of the backward: per (token, head) row, the normed q and k (the forward's exact
@@ -146,64 +151,71 @@ __device__ __forceinline__ u32x4 bf16_chunk_to_f16(const u32x4& x, bool& over) {
 // The backward's operands, head-major, in fp16 (every product of the backward runs on fp16 MFMA
 // with FP32 accumulation): the normed q and k (rounded to bf16 exactly as in the forward, then
 // converted), v and dO; and the LSE in log2 units.
+// Same mapping as k_prep_qkv.
 __global__ __launch_bounds__(256) void k_bwd_prep(BwdPrepParams p) {
-  const int64_t g = (int64_t)blockIdx.x * 256 + threadIdx.x;
-  const int64_t row = g >> 4;
   const int c = threadIdx.x & 15;
-  const int64_t rows = p.T * p.H;
-  const bool valid = row < rows;
-  const int64_t t = valid ? row / p.H : 0;
+  const int64_t row = ((int64_t)blockIdx.x * 256 + threadIdx.x) >> 4;
+  const bool valid = row < p.T * p.H;
+  const int64_t t = valid ? (int64_t)((uint32_t)row / (uint32_t)p.H) : 0;
   const int64_t h = valid ? row - t * p.H : 0;
-  const int64_t ts = p.slot ? (int64_t)p.slot[t] : t;
-  const int64_t dst = (h * p.T + ts) * HD + c * 8;
+  const int64_t ts = (valid && p.slot) ? (int64_t)p.slot[t] : t;
+  const u32x4 zero4 = {0, 0, 0, 0};
+  const u32x4 wqv = p.wq ? ld16(p.wq + c * 8) : zero4, wkv = p.wk ? ld16(p.wk + c * 8) : zero4;
+  {
+    const int64_t dst = (h * p.T + ts) * HD + c * 8;
 
-  u32x4 qv = {0, 0, 0, 0}, kv = {0, 0, 0, 0}, vv = {0, 0, 0, 0}, gv = {0, 0, 0, 0};
-  if (valid) {
-    qv = ld16(p.q + row * HD + c * 8);
-    kv = ld16(p.k + row * HD + c * 8);
-    vv = ld16(p.v + row * HD + c * 8);
-    gv = ld16(p.dout + row * HD + c * 8);
-  }
-  const u32x4 qo = p.wq ? norm_16lane(qv, p.wq, c, p.eps) : qv;
-  const u32x4 ko = p.wk ? norm_16lane(kv, p.wk, c, p.eps) : kv;
-  bool over = false;
-  const u32x4 q16 = bf16_chunk_to_f16(qo, over);
-  const u32x4 k16 = bf16_chunk_to_f16(ko, over);
-  const u32x4 v16 = bf16_chunk_to_f16(vv, over);
-  const u32x4 g16 = bf16_chunk_to_f16(gv, over);
-  if (valid) {
-    st16(p.qhat16 + dst, q16);
-    st16(p.khat16 + dst, k16);
-    st16(p.v16 + dst, v16);
-    st16(p.do16 + dst, g16);
-    if (c == 0) p.lse2[h * p.T + ts] = p.lse[t * p.H + h] * 1.44269504088896340736f;
-  }
-  if (p.o32) {
-    // D_i = sum_d dO_id O_id: products and sums in FP64 (each lane its 8 channels in order, then a
-    // fixed butterfly over the 16 lanes of the row), rounded once to fp32
+    // every load before any store (see k_prep_qkv)
+    u32x4 qv = {0, 0, 0, 0}, kv = {0, 0, 0, 0}, vv = {0, 0, 0, 0}, gv = {0, 0, 0, 0};
     f32x4 o0 = {0.0f, 0.0f, 0.0f, 0.0f}, o1 = o0;
+    float lse = 0.0f;
     if (valid) {
-      o0 = *(const f32x4*)(p.o32 + row * HD + c * 8);
-      o1 = *(const f32x4*)(p.o32 + row * HD + c * 8 + 4);
+      qv = ld16(p.q + row * HD + c * 8);
+      kv = ld16(p.k + row * HD + c * 8);
+      vv = ld16(p.v + row * HD + c * 8);
+      gv = ld16(p.dout + row * HD + c * 8);
+      if (p.o32) {
+        o0 = *(const f32x4*)(p.o32 + row * HD + c * 8);
+        o1 = *(const f32x4*)(p.o32 + row * HD + c * 8 + 4);
+      }
+      if (c == 0) lse = p.lse[row];
     }
-    float g[8];
-    unpack8_bf16(gv, g);
-    double d = 0.0;
+    const u32x4 qo = p.wq ? norm_16lane(qv, wqv, p.eps) : qv;
+    const u32x4 ko = p.wk ? norm_16lane(kv, wkv, p.eps) : kv;
+    bool over = false;
+    const u32x4 q16 = bf16_chunk_to_f16(qo, over);
+    const u32x4 k16 = bf16_chunk_to_f16(ko, over);
+    const u32x4 v16 = bf16_chunk_to_f16(vv, over);
+    const u32x4 g16 = bf16_chunk_to_f16(gv, over);
+    if (valid) {
+      st16(p.qhat16 + dst, q16);
+      st16(p.khat16 + dst, k16);
+      st16(p.v16 + dst, v16);
+      st16(p.do16 + dst, g16);
+      if (c == 0) p.lse2[h * p.T + ts] = lse * 1.44269504088896340736f;
+    }
+    if (p.o32) {
+      // D_i = sum_d dO_id O_id: products and sums in FP64 (each lane its 8 channels in order, then a
+      // fixed butterfly over the 16 lanes of the row), rounded once to fp32
+      float g[8];
+      unpack8_bf16(gv, g);
+      double d = 0.0;
 #pragma unroll
-    for (int i = 0; i < 4; i++) d = __builtin_fma((double)g[i], (double)o0[i], d);
+      for (int i = 0; i < 4; i++) d = __builtin_fma((double)g[i], (double)o0[i], d);
 #pragma unroll
-    for (int i = 0; i < 4; i++) d = __builtin_fma((double)g[4 + i], (double)o1[i], d);
-    d = d + __shfl_xor(d, 1, 64);
-    d = d + __shfl_xor(d, 2, 64);
-    d = d + __shfl_xor(d, 4, 64);
-    d = d + __shfl_xor(d, 8, 64);
-    if (valid && c == 0) p.delta[h * p.T + ts] = (float)d;
+      for (int i = 0; i < 4; i++) d = __builtin_fma((double)g[4 + i], (double)o1[i], d);
+      d = d + __shfl_xor(d, 1, 64);
+      d = d + __shfl_xor(d, 2, 64);
+      d = d + __shfl_xor(d, 4, 64);
+      d = d + __shfl_xor(d, 8, 64);
+      if (valid && c == 0) p.delta[h * p.T + ts] = (float)d;
+    }
+    const uint64_t any_over = __ballot(valid && over);
+    if (any_over && (threadIdx.x & 63) == __builtin_ctzll(any_over)) atomicOr(&p.hdr->status, STATUS_RANGE_BIT);
   }
-  const uint64_t any_over = __ballot(valid && over);
-  if (any_over && (threadIdx.x & 63) == __builtin_ctzll(any_over)) atomicOr(&p.hdr->status, STATUS_RANGE_BIT);
 }
 
 static inline unsigned grid_for_rows(int64_t rows) { return (unsigned)((rows * 16 + 255) / 256); }
+
 
 hipError_t launch_bwd_prep(const void* q, const void* k, const void* v, const void* dout, const float* lse,
                            const float* o32, const void* wq, const void* wk, int64_t T, int32_t H, float eps, void* ws,

@@ -40,6 +40,32 @@ def test_qknorm_matches_oracle_bitwise(name):
         assert dist.max() == 0
 
 
+def test_qknorm_extreme_ranges_match_oracle_bitwise():
+    """Weights spread over the whole bf16 range, so the normed values reach the bf16 subnormals and
+    overflow past the largest bf16 to infinity; plus a zero row and a row holding an infinity (its
+    norm is NaN).  Every code equals the oracle's (NaN where the oracle has NaN: the payload and
+    sign of a NaN are not part of the contract)."""
+    g = torch.Generator().manual_seed(59)
+    T, H = 48, 3
+    x = torch.randn(T, H, 128, generator=g).to(torch.bfloat16)
+    x[5, 1] = 0.0
+    x[9, 2, 17] = float("inf")
+    e = torch.randint(-133, 128, (128,), generator=g).to(torch.float64)
+    sgn = torch.where(torch.rand(128, generator=g) < 0.5, -1.0, 1.0).to(torch.float64)
+    w = (sgn * (1.0 + torch.rand(128, generator=g, dtype=torch.float64)) * torch.exp2(e)).to(torch.bfloat16)
+    w[0] = 0.0
+    say("[qknorm] extreme ranges")
+    y = h3.h3attn_qknorm(x.cuda(), w.cuda())
+    torch.cuda.synchronize()
+    got = y.cpu().view(torch.int16).numpy().view(np.uint16)
+    ref = oracle.qknorm(x, w, 1e-6)
+    ref_nan = ((ref & 0x7F80) == 0x7F80) & ((ref & 0x7F) != 0)
+    got_nan = ((got & 0x7F80) == 0x7F80) & ((got & 0x7F) != 0)
+    assert np.array_equal(ref_nan, got_nan)
+    assert ref_nan.any() and ((ref & 0x7FFF) == 0x7F80).any() and (((ref & 0x7F80) == 0) & ((ref & 0x7F) != 0)).any()
+    assert np.array_equal(got[~ref_nan], ref[~ref_nan])
+
+
 def test_qknorm_in_place_equals_out_of_place():
     x = workloads.random_inputs([333], 7, seed=41)
     a = x["q"].cuda()
