@@ -4,8 +4,8 @@
 // Packed layouts ("ws1_one_h3_block" page, Summary: several sequences share one token axis) are
 // described to the library by one id per token; a segment is a maximal run of equal ids, and ids
 // must not decrease.  The decode runs in one 1024-thread workgroup: three passes of block-wide
-// exclusive scans over tokens, then segments.  Its cost is T/1024 scan steps, negligible next to
-// the attention for the workloads served here.
+// exclusive scans over tokens, then segments.  Its cost is T/1024 scan steps (with the ids of up to
+// 16384 tokens loaded up front), negligible next to the attention for the workloads served here.
 #include "h3_common.h"
 #include "h3_bwd.h"
 #include "h3_launch.h"
@@ -52,17 +52,16 @@ __global__ __launch_bounds__(1024) void k_plan(const int32_t* __restrict__ seg, 
   if (tid == 0) s_bad = 0;
   __syncthreads();
 
-  // pass 1: segment starts at every token whose id differs from its predecessor's
+  // pass 1: segment starts at every token whose id differs from its predecessor's.  Up to
+  // PRE * 1024 tokens, every id is loaded before the first scan, so the scans do not wait on memory
+  // one chunk at a time.
   int nseg = 0, bad = 0;
-  for (int64_t base = 0; base < T; base += 1024) {
-    const int64_t t = base + tid;
+  auto chunk = [&](int64_t t, int32_t cur, int32_t prev) {
     int flag = 0;
     if (t < T) {
-      const int32_t cur = seg[t];
       if (t == 0) {
         flag = 1;
       } else {
-        const int32_t prev = seg[t - 1];
         flag = cur != prev;
         bad |= cur < prev;
       }
@@ -71,6 +70,24 @@ __global__ __launch_bounds__(1024) void k_plan(const int32_t* __restrict__ seg, 
     const int pos = block_excl_scan(flag, lds_wave, total);
     if (flag) segtab[2 * (nseg + pos)] = (int32_t)t;
     nseg += total;
+  };
+  constexpr int PRE = 16;
+  if (T <= (int64_t)PRE * 1024) {
+    int32_t cur[PRE], prev[PRE];
+#pragma unroll
+    for (int k = 0; k < PRE; k++) {
+      const int64_t t = (int64_t)k * 1024 + tid;
+      cur[k] = t < T ? seg[t] : 0;
+      prev[k] = (t < T && t > 0) ? seg[t - 1] : 0;
+    }
+#pragma unroll
+    for (int k = 0; k < PRE; k++)
+      if ((int64_t)k * 1024 < T) chunk((int64_t)k * 1024 + tid, cur[k], prev[k]);
+  } else {
+    for (int64_t base = 0; base < T; base += 1024) {
+      const int64_t t = base + tid;
+      chunk(t, t < T ? seg[t] : 0, (t < T && t > 0) ? seg[t - 1] : 0);
+    }
   }
   if (bad) atomicOr(&s_bad, 1);
   __syncthreads();
