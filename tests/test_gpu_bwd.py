@@ -235,3 +235,19 @@ def test_fwd_ex_o32_nan_filled_on_data_error():
     torch.cuda.synchronize()
     assert h3.h3attn_status_read(ws) == h3.H3ATTN_ERR_RANGE
     assert torch.isnan(o32).all() and torch.isnan(out.float()).all()
+
+
+def test_bwd_long_batch_past_the_decode_prefetch_alone_equals_batched():
+    """The backward's segment decode on 20100 tokens (its chunked path) against each segment alone
+    (the prefetched path): dq, dk, dv are the same bits."""
+    lens = [9000, 7000, 4100]
+    g = to_dev(workloads.random_inputs(lens, 2, seed=73, with_grad=True))
+    say(f"[bwd bitwise] {sum(lens)}-token batch vs its segments alone")
+    bq, bk, bv, _, _ = run_bwd(g, dmode="o32")
+    t0 = 0
+    for n in lens:
+        alone = {k: (g[k][t0:t0 + n].contiguous() if k in ("q", "k", "v", "seg", "dout") else g[k]) for k in g}
+        q, k, v, _, _ = run_bwd(alone, dmode="o32")
+        assert bitwise_equal(q, bq[t0:t0 + n]) and bitwise_equal(k, bk[t0:t0 + n]) and bitwise_equal(v, bv[t0:t0 + n])
+        t0 += n
+

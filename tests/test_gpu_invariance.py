@@ -131,3 +131,19 @@ def test_empty_input_is_a_noop():
     w = torch.ones(128, dtype=torch.bfloat16, device="cuda:0")
     out, _ = run_fwd(dict(q=e, k=e, v=e, seg=torch.zeros(0, dtype=torch.int32, device="cuda:0"), wq=w, wk=w))
     assert out.shape == (0, 2, 128)
+
+
+def test_long_batch_past_the_decode_prefetch_alone_equals_batched():
+    """A batch of 20100 tokens: the segment decode takes its chunked path (more than 16384 ids),
+    each segment alone the prefetched one; forward outputs and LSE are the same bits either way."""
+    lens = [9000, 7000, 4100]
+    x = workloads.random_inputs(lens, 2, seed=71)
+    g = to_dev(x)
+    say(f"[bitwise] {sum(lens)}-token batch vs its segments alone")
+    batched, blse = run_fwd(g, want_lse=True)
+    t0 = 0
+    for n in lens:
+        alone = {k: (g[k][t0:t0 + n].contiguous() if k in ("q", "k", "v", "seg") else g[k]) for k in g}
+        o, l = run_fwd(alone, want_lse=True)
+        assert bitwise_equal(o, batched[t0:t0 + n]) and bitwise_equal(l, blse[t0:t0 + n]), f"segment at {t0}"
+        t0 += n
