@@ -10,13 +10,13 @@
 //                                      in registers; v_mfma_f32_32x32x16_bf16)
 //   O^T[dim][query] += V^T . P^T      (A = 32 dims x 16 keys, read from the row-major V tile with
 //                                      ds_read_b64_tr_b16; B = P in fp16; v_mfma_f32_32x32x16_f16)
-// The softmax row max and row sum are lane-local over 32 scores plus one exchange with lane ^ 32
-// (the other half of the query's keys), done with v_permlane32_swap.
+// The softmax row sums (and, when needed, row maxima) are lane-local over 32 scores; the two halves
+// of a query's keys (lanes l and l ^ 32) meet through v_permlane32_swap.
 //
 // Ping-pong.  The KV walk of a wave alternates two kinds of phase: a matrix phase G(k) (the 16
 // score MFMAs of tile k+1 and the 16 P.V MFMAs of tile k, operands read from LDS a few MFMAs
-// ahead) and a vector phase V(k) (the softmax of tile k+1: maximum, lazy rescale, exp, sum, fp16
-// packing).  Waves 4..7 run one phase behind waves 0..3, and every phase ends at a workgroup
+// ahead) and a vector phase V(k) (the softmax of tile k+1: exp, sum, fp16 packing, and the rare
+// rescale).  Waves 4..7 run one phase behind waves 0..3, and every phase ends at a workgroup
 // barrier, so on each SIMD one wave issues MFMAs back to back while its partner does the vector
 // work: the matrix cores stay busy and the softmax is hidden behind them.
 //
@@ -36,9 +36,14 @@
 // is a function of its own segment's bytes, never of the batch, the offset, neighbours or the grid.
 // (Maxima are exact, so their evaluation order cannot change a bit.)
 //
-// Online softmax with a lazy maximum: the running maximum m (log2 units) moves only when a tile's
-// maximum exceeds it by more than 8, so p = exp2(s*c - m) <= 2^8 stays well inside fp16, and the
-// O/l rescale is skipped on most tiles.  Lanes whose m does not move take alpha = 1 exactly.
+// Online softmax with a lazy maximum, checked after the fact: p = exp2(s*c - m) is formed with the
+// running maximum m (log2 units) as it stands, and m moves only when the row's p over one tile no
+// longer fit: when a lane's 32 values sum past 4096 (or to infinity or NaN, as on the first tile,
+// where m starts at -inf).  Then the tile's maximum is taken, O and l are rescaled, and the tile's
+// p are formed again; until then every p is at most 4096, well inside fp16, and the common path
+// needs no maximum at all.  The decision is the row's own (both halves of the query's keys), and
+// rows whose m does not move take alpha = 1 exactly and re-form the same p, so a row's bits never
+// depend on its neighbours in the wave.
 #include "h3_common.h"
 #include "h3_launch.h"
 #include "h3_tiles.h"
@@ -46,7 +51,7 @@
 namespace h3 {
 
 constexpr float LN2 = 0.69314718055994530942f;
-constexpr float RESCALE_THRESHOLD = 8.0f;  // log2 units
+constexpr float P_SUM_LIMIT = 4096.0f;     // a lane's 32 p values of one tile sum to at most this
 constexpr int NWAVES = 8;                 // waves per workgroup (two per SIMD)
 static_assert(BK == TILE_ROWS, "one LDS tile per KV tile of two 32-key blocks");
 static_assert(BQ == 32 * NWAVES, "one 32-query block per wave");
@@ -92,6 +97,19 @@ __device__ __forceinline__ void load_q(const AttnParams& p, int s0, int qrow, bo
     if (qvalid) w4 = *(const u32x4*)(qp + 16 * m + 8 * hh);
     qf[m] = __builtin_bit_cast(bf16x8, w4);
   }
+}
+
+// p = exp2(s*c - m) for the lane's 32 keys, packed to fp16 B operands; returns the sum of the
+// FP32 values in a fixed binary tree.
+__device__ __forceinline__ float exp_pack_sum(const f32x16* S, float c, float m, f16x8* pf) {
+  float pr[32];
+#pragma unroll
+  for (int kb = 0; kb < 2; kb++)
+#pragma unroll
+    for (int i = 0; i < 16; i++) pr[16 * kb + i] = __builtin_amdgcn_exp2f(__builtin_fmaf(S[kb][i], c, -m));
+#pragma unroll
+  for (int ks = 0; ks < 4; ks++) pf[ks] = pack_p(&pr[8 * ks]);
+  return tree_sum<32>(pr);
 }
 
 template <int N>
@@ -185,7 +203,7 @@ __global__ __launch_bounds__(64 * NWAVES, 1) void k_attn_fwd(AttnParams p) {
 #pragma unroll
       for (int i = 0; i < 16; i++) O[d][i] = 0.0f;
     float lsum = 0.0f;
-    float m_run = 0.0f;
+    float m_run = -__builtin_inff();
 
     // Copies issued at phase slot 2m: K(m+1) and V(m), into the buffers of K(m-1) and V(m-2),
     // which were last read in slot 2m-1.
@@ -233,31 +251,24 @@ __global__ __launch_bounds__(64 * NWAVES, 1) void k_attn_fwd(AttnParams p) {
             asm volatile("" : "+v"(r));
             mask_tail_rel(S, r);
           }
-          const float mt = tile_max(S) * c;
-          if (k + 1 == 0) {
-            m_run = mt;  // first tile: m is the tile maximum (log2 units)
-          } else {
-            const bool need = mt > m_run + RESCALE_THRESHOLD;
-            if (__builtin_expect(__ballot(need) != 0, 0)) {  // rare: keep it a branch
-              const float m_new = need ? mt : m_run;
-              const float alpha = need ? __builtin_amdgcn_exp2f(m_run - m_new) : 1.0f;
-              lsum *= alpha;
+          float ts = exp_pack_sum(S, c, m_run, pf);
+          // rare (the first tile, where m is -inf, or a tile whose p would pass the limit): move m
+          if (__builtin_expect(__ballot(!(ts <= P_SUM_LIMIT)) != 0, 0)) {
+            float ta, tb;
+            swap_halves(ts, ta, tb);
+            const bool need = !(ta <= P_SUM_LIMIT) || !(tb <= P_SUM_LIMIT);
+            const float mt = tile_max(S) * c;
+            const float m_new = need ? __builtin_fmaxf(mt, m_run) : m_run;
+            const float alpha = need ? __builtin_amdgcn_exp2f(m_run - m_new) : 1.0f;
+            lsum *= alpha;
 #pragma unroll
-              for (int d = 0; d < 4; d++)
+            for (int d = 0; d < 4; d++)
 #pragma unroll
-                for (int i = 0; i < 16; i++) O[d][i] *= alpha;
-              m_run = m_new;
-            }
+              for (int i = 0; i < 16; i++) O[d][i] *= alpha;
+            m_run = m_new;
+            ts = exp_pack_sum(S, c, m_run, pf);
           }
-          float pr[32];
-#pragma unroll
-          for (int kb = 0; kb < 2; kb++)
-#pragma unroll
-            for (int i = 0; i < 16; i++)
-              pr[16 * kb + i] = __builtin_amdgcn_exp2f(__builtin_fmaf(S[kb][i], c, -m_run));
-          lsum += tree_sum<32>(pr);
-#pragma unroll
-          for (int ks = 0; ks < 4; ks++) pf[ks] = pack_p(&pr[8 * ks]);
+          lsum += ts;
         }
       }
     };
