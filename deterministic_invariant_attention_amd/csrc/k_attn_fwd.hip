@@ -22,8 +22,9 @@
 //
 // K and V tiles (64 keys, 16 KB each) are copied from the workspace straight into LDS with
 // buffer_load_dwordx4 ... lds (no register staging), double-buffered; the copies of K(m+1) and
-// V(m) are issued at the start of phase slot 2m and have two slots to land: the phase barriers
-// carry no memory fence, and each wave waits for its own copies only before slot 2m+2.
+// V(m) are issued at the start of phase slot 2m by the trailing waves (then in their vector phase)
+// and have two slots to land: the phase barriers carry no memory fence, and each wave waits for
+// its own copies only before slot 2m+2.
 //
 // LDS layouts are XOR-swizzled by 16-byte chunk (the copy picks, per lane, which global chunk
 // lands in its LDS slot), so that both read patterns are free of bank conflicts:
@@ -160,7 +161,9 @@ __global__ __launch_bounds__(64 * NWAVES, 1) void k_attn_fwd(AttnParams p) {
   const int nslots = p.xcd_slots;
 
   const int k_lane_off = tile_lane_offset(false, wv, lane);
-  const int v_lane_off = tile_lane_offset(true, wv, lane);
+  // the trailing waves issue the loop's copies, each a quarter of a tile
+  const int k_lane_off4 = tile_lane_offset(false, wv & 3, lane);
+  const int v_lane_off4 = tile_lane_offset(true, wv & 3, lane);
   const int tr_row = 4 * hh + ((lane & 15) >> 2);
   const int tr_col = 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
   const float c = p.c;
@@ -213,10 +216,10 @@ __global__ __launch_bounds__(64 * NWAVES, 1) void k_attn_fwd(AttnParams p) {
       constexpr int MP = decltype(mp)::value;
       const int m = t >> 1;
       if (m + 1 < ntiles)
-        tile_to_lds<NWAVES>(kbase + (int64_t)(m + 1) * BK * HD, L - (m + 1) * BK, lds + (1 - MP) * TILE_ELEMS, wv,
-                    k_lane_off);
+        tile_to_lds<4>(kbase + (int64_t)(m + 1) * BK * HD, L - (m + 1) * BK, lds + (1 - MP) * TILE_ELEMS, wv & 3,
+                       k_lane_off4);
       if (m < ntiles)
-        tile_to_lds<NWAVES>(vbase + (int64_t)m * BK * HD, L - m * BK, lds + (2 + MP) * TILE_ELEMS, wv, v_lane_off);
+        tile_to_lds<4>(vbase + (int64_t)m * BK * HD, L - m * BK, lds + (2 + MP) * TILE_ELEMS, wv & 3, v_lane_off4);
     };
 
     // Phase tau of this wave runs in slot t = tau + grp.  Even tau: G(k), k = tau/2 - 1 (scores of
@@ -230,7 +233,8 @@ __global__ __launch_bounds__(64 * NWAVES, 1) void k_attn_fwd(AttnParams p) {
       phase_barrier();
       // slot t = tau + grp is even (a copy slot) for tau % 2 == grp; m = t / 2 has the parity below
       if constexpr ((TM & 1) == 0) {
-        if (grp == 0) issue_copies(t, Par<(TM >> 1)>{});  // t = tau = 4n + TM: m = 2n + TM/2
+        // (the leading waves issue no copies: in a copy slot they are in their matrix phase, which
+        // is the longer one)
       } else {
         if (grp == 1) issue_copies(t, Par<(TM == 1 ? 1 : 0)>{});  // t = 4n + TM + 1: m = 2n + 1 or 2n + 2
       }
