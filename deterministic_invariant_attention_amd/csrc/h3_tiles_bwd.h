@@ -126,23 +126,30 @@ __device__ __forceinline__ f32x16 mfma_rows(const u32x4& a, const bf16x8& b, con
 __device__ __forceinline__ f32x16 mfma_rows(const u32x4& a, const f16x8& b, const f32x16& c) {
   return __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(f16x8, a), b, c, 0, 0, 0);
 }
+// init == nullptr: the accumulators start at zero; else S[kb] starts at init[kb] (the first MFMA of
+// each accumulator takes it as its addend).
 template <int TILE, int NPRE, int s, typename BT, typename Hook>
-__device__ __forceinline__ void rows_step(const RowBases& rb, const BT* b, f32x16* S, u32x4 (&ka)[16], Hook& hook) {
+__device__ __forceinline__ void rows_step(const RowBases& rb, const BT* b, f32x16* S, u32x4 (&ka)[16], Hook& hook,
+                                          const f32x16* init) {
   if constexpr (s + NPRE < 16) ka[s + NPRE] = rows_read<TILE, s + NPRE>(rb);
   constexpr int ahead = (s + NPRE < 16 ? NPRE : 15 - s);
   lgkm_wait_tied4<ahead>(ka[s]);
-  S[s & 1] = mfma_rows(ka[s], b[s >> 1], S[s & 1]);
+  if constexpr (s < 2) S[s & 1] = mfma_rows(ka[s], b[s >> 1], init ? init[s & 1] : S[s & 1]);
+  else S[s & 1] = mfma_rows(ka[s], b[s >> 1], S[s & 1]);
   hook(StepIdx<s>{});
   __builtin_amdgcn_sched_barrier(0);
-  if constexpr (s + 1 < 16) rows_step<TILE, NPRE, s + 1>(rb, b, S, ka, hook);
+  if constexpr (s + 1 < 16) rows_step<TILE, NPRE, s + 1>(rb, b, S, ka, hook, init);
 }
 template <int TILE, int NPRE = 4, typename BT, typename Hook>
-__device__ __forceinline__ void gemm_rows(const RowBases& rb, const BT* b, f32x16* S, Hook hook) {
+__device__ __forceinline__ void gemm_rows(const RowBases& rb, const BT* b, f32x16* S, Hook hook,
+                                          const f32x16* init = nullptr) {
   static_assert(TILE >= 0 && TILE <= 7 && NPRE >= 1 && NPRE <= 8, "tile and prefetch depth");
+  if (!init) {
 #pragma unroll
-  for (int kb = 0; kb < 2; kb++)
+    for (int kb = 0; kb < 2; kb++)
 #pragma unroll
-    for (int i = 0; i < 16; i++) S[kb][i] = 0.0f;
+      for (int i = 0; i < 16; i++) S[kb][i] = 0.0f;
+  }
   u32x4 ka[16];
   ka[0] = rows_read<TILE, 0>(rb);
   if constexpr (NPRE > 1) ka[1] = rows_read<TILE, 1>(rb);
@@ -152,7 +159,7 @@ __device__ __forceinline__ void gemm_rows(const RowBases& rb, const BT* b, f32x1
   if constexpr (NPRE > 5) ka[5] = rows_read<TILE, 5>(rb);
   if constexpr (NPRE > 6) ka[6] = rows_read<TILE, 6>(rb);
   if constexpr (NPRE > 7) ka[7] = rows_read<TILE, 7>(rb);
-  rows_step<TILE, NPRE, 0>(rb, b, S, ka, hook);
+  rows_step<TILE, NPRE, 0>(rb, b, S, ka, hook, init);
 }
 
 // The lane's eight transposed-read base addresses in tile 0 of the unified layout: vb[4u + db] for

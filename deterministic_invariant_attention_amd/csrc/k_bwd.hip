@@ -13,7 +13,9 @@
 //   k_bwd_dq    work item = (segment, 128-query tile, head).  Pass 1 over the key tiles computes
 //               D_i exactly (in fp32, a fixed tree per tile) unless the staging kernel formed it
 //               from the forward's fp32 output; pass 2 recomputes S and dP, forms dS and
-//               accumulates dQ^T += K^16^T dS^T.
+//               accumulates dQ^T += K^16^T dS^T.  Its dP products start from -D (D is one value
+//               per lane there), so they give dP - D and dS costs one multiply per element.
+// The workspace keeps -D per staged row.
 //   k_bwd_dkdv  work item = (segment, 128-key tile, head).  One pass over the query tiles:
 //               S = Q^ K^T and dP = dO V^T with the wave's 32 keys in registers, P and dS in fp16,
 //               dV^T += dO16^T P and dK^T += Q^16^T dS, whose transposed reads run as one pipeline.
@@ -50,7 +52,7 @@ struct BwdParams {
   const uint16_t* v16;
   const uint16_t* do16;
   const float* lse2;
-  float* delta;
+  float* delta;          // -D per staged row: the dP products start from it
   uint16_t* dq;  // outputs, token-major
   uint16_t* dk;
   uint16_t* dv;
@@ -261,7 +263,7 @@ __global__ __launch_bounds__(64 * BW, 1) void k_bwd_dq(BwdParams p) {
     // ---- pass 1: D_i = sum_j P_ij dP_ij (unless the staging kernel computed D = dO . O)
     float Dq;
     if (p.delta_ready) {
-      Dq = qvalid ? p.delta[hT + w.s0 + qrow] : 0.0f;
+      Dq = qvalid ? -p.delta[hT + w.s0 + qrow] : 0.0f;
     } else {
       float dacc = 0.0f;
       auto pass1 = [&](auto stage, int j) {
@@ -289,12 +291,17 @@ __global__ __launch_bounds__(64 * BW, 1) void k_bwd_dq(BwdParams p) {
       float da, db_;
       swap_halves(dacc, da, db_);
       Dq = da + db_;
-      if (qvalid && hh == 0) p.delta[hT + w.s0 + qrow] = Dq;
+      if (qvalid && hh == 0) p.delta[hT + w.s0 + qrow] = -Dq;
       __syncthreads();  // every wave is done with pass 1's tiles
       copies(0, Par2<0>{});
     }
 
-    // ---- pass 2: dQ^T += K^16^T dS^T
+    // ---- pass 2: dQ^T += K^16^T dS^T; the dP products start from -D, so they give dP - D
+    f32x16 negD[2];
+#pragma unroll
+    for (int kb = 0; kb < 2; kb++)
+#pragma unroll
+      for (int i = 0; i < 16; i++) negD[kb][i] = -Dq;
     f32x16 acc[4];
 #pragma unroll
     for (int d = 0; d < 4; d++)
@@ -317,10 +324,10 @@ __global__ __launch_bounds__(64 * BW, 1) void k_bwd_dq(BwdParams p) {
           const int e = 2 * s + u;
           pr[e] = __builtin_amdgcn_exp2f(__builtin_fmaf(S[e >> 4][e & 15], c, -lq));
         }
-      });
+      }, negD);
       f16x8 dsf[4];
 #pragma unroll
-      for (int e = 0; e < 8; e++) ds[e] = pr[e] * (dP[0][e] - Dq);
+      for (int e = 0; e < 8; e++) ds[e] = pr[e] * dP[0][e];
       dsf[0] = pack_p(&ds[0]);
       const f16x8* bop[1] = {dsf};
       f32x16* accp[1] = {acc};
@@ -331,7 +338,7 @@ __global__ __launch_bounds__(64 * BW, 1) void k_bwd_dq(BwdParams p) {
 #pragma unroll
           for (int u = 0; u < 2; u++) {
             const int e = 8 * sl + 2 * (s & 3) + u;
-            ds[e] = pr[e] * (dP[e >> 4][e & 15] - Dq);
+            ds[e] = pr[e] * dP[e >> 4][e & 15];
           }
           if constexpr ((s & 3) == 3) dsf[sl] = pack_p(&ds[8 * sl]);
         }
@@ -473,7 +480,7 @@ __global__ __launch_bounds__(64 * BW, 1) void k_bwd_dkdv(BwdParams p) {
 #pragma unroll
           for (int u = 0; u < 2; u++) {
             const int e = 2 * s + u, q2 = e >> 4, i = e & 15;
-            ds[q2][i] = pr[q2][i] * (dP[q2][i] - d4[q2][i >> 2][i & 3]);
+            ds[q2][i] = pr[q2][i] * (dP[q2][i] + d4[q2][i >> 2][i & 3]);  // d4 holds -D
           }
           if constexpr ((s & 3) == 3) dsf[s >> 2] = pack_p(&ds[s >> 3][8 * ((s >> 2) & 1)]);
         }

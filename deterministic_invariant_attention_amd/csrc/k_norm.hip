@@ -125,7 +125,7 @@ struct BwdPrepParams {
   uint16_t* v16;
   uint16_t* do16;
   float* lse2;
-  float* delta;         // D = dO . O per row (with o32)
+  float* delta;         // -D, D = dO . O per row (with o32)
   const int32_t* slot;  // staged row of each token (position order), or NULL for packed order
   WsHeader* hdr;
   int64_t T;
@@ -207,7 +207,7 @@ __global__ __launch_bounds__(256) void k_bwd_prep(BwdPrepParams p) {
       d = d + __shfl_xor(d, 2, 64);
       d = d + __shfl_xor(d, 4, 64);
       d = d + __shfl_xor(d, 8, 64);
-      if (valid && c == 0) p.delta[h * p.T + ts] = (float)d;
+      if (valid && c == 0) p.delta[h * p.T + ts] = -(float)d;
     }
     const uint64_t any_over = __ballot(valid && over);
     if (any_over && (threadIdx.x & 63) == __builtin_ctzll(any_over)) atomicOr(&p.hdr->status, STATUS_RANGE_BIT);
