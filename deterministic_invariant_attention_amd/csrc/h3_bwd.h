@@ -11,6 +11,17 @@ constexpr int DW_CHUNK = 64;   // partials per chunk of the weight-gradient redu
 
 constexpr int NBKT = 32;  // cost classes of the backward work order (floor(log2(64-row tiles)))
 
+// Backward workspace (h3attn_bwd_workspace_bytes):
+// [0, 256)          header: status bits, segment and work-item counts, work counters
+// segtab            int32 [2*T]
+// items             int32 [2*(T + ceil(T/BT))]: (segment, tile) work items
+// bkt               int32 [2*NBKT]: first item and count of each cost class in the work order
+// qhat16, khat16    fp16 [H][T][128]: normed q, k (head-major, staged row order)
+// v16, do16         fp16 [H][T][128]: v and dO
+// lse2              fp32 [H][T]: the forward's log-sum-exp in log2 units
+// delta             fp32 [H][T]: -D_i, D_i = sum_j P_ij dP_ij (the dq kernel's dP products start from it)
+// dqh, dkh          fp32 [T][H][128]: dq^, dk^ (gradients of the normed operands)
+// dw_part, dw_chunk fp32: 16-row weight-gradient partials and their first-level chunk sums
 struct BwdLayout {
   size_t segtab, items, bkt, qhat16, khat16, v16, do16, lse2, delta, dqh, dkh, dw_part, dw_chunk, total;
   int64_t max_items, nparts, nchunks;

@@ -51,15 +51,6 @@ __host__ __device__ inline WsLayout ws_layout(int64_t T, int32_t H) {
   return w;
 }
 
-// ---------------------------------------------------------------- backward workspace
-// [0, 256)   header: status bits, segment and work-item counts
-// segtab     int32 [2*T]
-// items      int32 [2*(T + ceil(T/BT))]: (segment, tile) work items, BT = 128 queries or keys
-// qhat, khat bf16 [H][T][128]: normed q, k (head-major)      qhat16, khat16: the same in fp16
-// vh, doh    bf16 [H][T][128]: v and dO (head-major)          do16: dO in fp16
-// lse2       fp32 [H][T]: the forward's log-sum-exp in log2 units
-// delta      fp32 [H][T]: -D_i, D_i = sum_j P_ij dP_ij (the dP products start from it)
-// dwq, dwk   fp32 [max_items][H][128]: per-item partial sums of the norm-weight gradients
 // ---------------------------------------------------------------- vector types
 typedef __bf16 bf16x8 __attribute__((__vector_size__(8 * sizeof(__bf16))));
 typedef _Float16 f16x8 __attribute__((__vector_size__(8 * sizeof(_Float16))));
