@@ -96,6 +96,23 @@ def test_parity_long_sampled(name):
     assert rel <= REL_L2_BOUND and mx <= MAX_ABS_BOUND and lse_err <= LSE_REL_BOUND
 
 
+def test_parity_segment_of_131072_tokens():
+    """One 131072-token segment (2048 KV tiles per work item, 512 query tiles) on one head,
+    sampled rows: large index products, the segment decode's chunked path, long key walks."""
+    T = 131072
+    x = workloads.random_inputs([T], 1, seed=17, qk_scale=2.0)
+    g = to_dev(x)
+    say(f"[parity] {T}-token segment, H=1")
+    out, lse = run_fwd(g, want_lse=True)
+    rows = _sample_rows(T, 24, seed=5)
+    ref, ref_lse = oracle.fwd_rows(x["q"], x["k"], x["v"], x["seg"].numpy(), rows, x["wq"], x["wk"], EPS)
+    rel, mx = metrics(f64(out)[rows], ref)
+    lse_err = lse_error(f64(lse)[rows], ref_lse)
+    say(f"[parity] {T}-token: rel_l2={rel:.3e} max_abs={mx:.3e} lse_rel_err={lse_err:.2e}")
+    assert np.all(np.isfinite(f64(out)))
+    assert rel <= REL_L2_BOUND and mx <= MAX_ABS_BOUND and lse_err <= LSE_REL_BOUND
+
+
 def test_parity_long_segment_many_tiles():
     """A 20000-token segment (313 KV tiles) on 2 heads, sampled rows."""
     x = workloads.random_inputs([20000], 2, seed=13, qk_scale=2.0)
