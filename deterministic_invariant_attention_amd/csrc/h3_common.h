@@ -10,7 +10,7 @@ namespace h3 {
 
 constexpr int HD = 128;  // head dim (fixed by the H3 node: 128-wide heads)
 constexpr int BQ = 256;  // queries per attention work item (8 waves x 32 rows)
-constexpr int BK = 64;   // keys per KV tile; the KV walk is in these tiles, ascending from the segment start
+constexpr int BK = 96;   // keys per KV tile; the KV walk is in these tiles, ascending from the segment start
 
 // ---------------------------------------------------------------- workspace
 // [0, 256)            header: status bits, segment and work-item counts

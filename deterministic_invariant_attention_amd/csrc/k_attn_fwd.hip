@@ -10,17 +10,18 @@
 //                                      in registers; v_mfma_f32_32x32x16_bf16)
 //   O^T[dim][query] += V^T . P^T      (A = 32 dims x 16 keys, read from the row-major V tile with
 //                                      ds_read_b64_tr_b16; B = P in fp16; v_mfma_f32_32x32x16_f16)
-// The softmax row sums (and, when needed, row maxima) are lane-local over 32 scores; the two halves
-// of a query's keys (lanes l and l ^ 32) meet through v_permlane32_swap.
+// A KV tile is 96 keys: three 32-key blocks.  The softmax row sums (and, when needed, row maxima)
+// are lane-local over the lane's 48 scores of a tile (16 of each block); the two halves of a
+// query's keys (lanes l and l ^ 32) meet through v_permlane32_swap.
 //
-// Ping-pong.  The KV walk of a wave alternates two kinds of phase: a matrix phase G(k) (the 16
-// score MFMAs of tile k+1 and the 16 P.V MFMAs of tile k, operands read from LDS a few MFMAs
+// Ping-pong.  The KV walk of a wave alternates two kinds of phase: a matrix phase G(k) (the 24
+// score MFMAs of tile k+1 and the 24 P.V MFMAs of tile k, operands read from LDS a few MFMAs
 // ahead) and a vector phase V(k) (the softmax of tile k+1: exp, sum, fp16 packing, and the rare
 // rescale).  Waves 4..7 run one phase behind waves 0..3, and every phase ends at a workgroup
 // barrier, so on each SIMD one wave issues MFMAs back to back while its partner does the vector
 // work: the matrix cores stay busy and the softmax is hidden behind them.
 //
-// K and V tiles (64 keys, 16 KB each) are copied from the workspace straight into LDS with
+// K and V tiles (96 keys, 24 KB each) are copied from the workspace straight into LDS with
 // buffer_load_dwordx4 ... lds (no register staging), double-buffered; the copies of K(m+1) and
 // V(m) are issued at the start of phase slot 2m by the trailing waves (then in their vector phase)
 // and have two slots to land: the phase barriers carry no memory fence, and each wave waits for
@@ -39,7 +40,7 @@
 //
 // Online softmax with a lazy maximum, checked after the fact: p = exp2(s*c - m) is formed with the
 // running maximum m (log2 units) as it stands, and m moves only when the row's p over one tile no
-// longer fit: when a lane's 32 values sum past 4096 (or to infinity or NaN, as on the first tile,
+// longer fit: when a lane's 48 values sum past 4096 (or to infinity or NaN, as on the first tile,
 // where m starts at -inf).  Then the tile's maximum is taken, O and l are rescaled, and the tile's
 // p are formed again; until then every p is at most 4096, well inside fp16, and the common path
 // needs no maximum at all.  The decision is the row's own (both halves of the query's keys), and
@@ -52,9 +53,91 @@
 namespace h3 {
 
 constexpr float LN2 = 0.69314718055994530942f;
-constexpr float P_SUM_LIMIT = 4096.0f;     // a lane's 32 p values of one tile sum to at most this
+constexpr float P_SUM_LIMIT = 4096.0f;     // a lane's 48 p values of one tile sum to at most this
 constexpr int NWAVES = 8;                 // waves per workgroup (two per SIMD)
-static_assert(BK == TILE_ROWS, "one LDS tile per KV tile of two 32-key blocks");
+constexpr int FROWS = BK;          // keys per KV tile
+static_assert(FROWS % 32 == 0, "whole 32-key blocks");
+constexpr int NKB = FROWS / 32;    // 32-key blocks per tile
+constexpr int NKS = FROWS / 16;    // 16-key slices per tile
+constexpr int FTILE = FROWS * HD;  // 16-bit elements per LDS tile
+
+template <int NW>
+__device__ __forceinline__ void ftile_to_lds(const uint16_t* gtile, int valid, uint16_t* lds_tile, int wv,
+                                             int lane_off) {
+  static_assert(FROWS % (4 * NW) == 0, "whole 1 KB blocks per wave");
+  const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
+      (void*)gtile, (short)0, (valid < FROWS ? valid : FROWS) * 256, 0x00020000);
+  int wofs = wv * 4 * HD;
+  asm volatile("" : "+s"(wofs));
+#pragma unroll
+  for (int i = 0; i < FROWS / (4 * NW); i++)
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void*)(lds_tile + NW * i * 4 * HD + wofs), 16,
+                                             lane_off + i * NW * 1024, 0, 0, 0);
+}
+
+template <int NPRE>
+__device__ __forceinline__ void fscores(const uint16_t* Kb, const bf16x8* qf, int l32, int hh, f32x16* S) {
+  constexpr int NS = 8 * NKB;
+  bf16x8 ka[NS];
+  auto kread = [&](int s) {
+    const int kb = s % NKB, m = s / NKB;
+    ka[s] = *(const bf16x8*)(Kb + k_off(32 * kb + l32, 16 * m + 8 * hh));
+  };
+#pragma unroll
+  for (int kb = 0; kb < NKB; kb++)
+#pragma unroll
+    for (int i = 0; i < 16; i++) S[kb][i] = 0.0f;
+#pragma unroll
+  for (int s = 0; s < NPRE; s++) kread(s);
+#pragma unroll
+  for (int s = 0; s < NS; s++) {  // step s = NKB m + kb
+    if (s + NPRE < NS) kread(s + NPRE);
+    S[s % NKB] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka[s], qf[s / NKB], S[s % NKB], 0, 0, 0);
+    __builtin_amdgcn_sched_barrier(0);
+  }
+}
+
+// P.V over the tile's NKS 16-key slices, V buffer VB (vb: the lane's addresses in V buffer 0)
+template <int VB, int T>
+__device__ __forceinline__ void ftr_read_step(const uint32_t* vb, u32x2 (&va)[4 * NKS][2]) {
+  constexpr int ks = T >> 2, db = T & 3;
+  constexpr int off = VB * FTILE * 2 + 16 * ks * HD * 2;
+  va[T][0] = tr_read_asm<off>(vb[db]);
+  va[T][1] = tr_read_asm<off + 8 * HD * 2>(vb[db]);
+}
+template <int VB, int T>
+__device__ __forceinline__ void ftr_gemm_step(const uint32_t* vb, const f16x8* pf, f32x16* O, u32x2 (&va)[4 * NKS][2]) {
+  constexpr int NT = 4 * NKS;
+  if constexpr (T + 4 < NT) ftr_read_step<VB, T + 4>(vb, va);
+  constexpr int ahead = (T + 4 < NT ? T + 4 : NT - 1) - T;
+  if constexpr (ahead == 4) LGKM_WAIT_TIED(8, va[T][0], va[T][1]);
+  else if constexpr (ahead == 3) LGKM_WAIT_TIED(6, va[T][0], va[T][1]);
+  else if constexpr (ahead == 2) LGKM_WAIT_TIED(4, va[T][0], va[T][1]);
+  else if constexpr (ahead == 1) LGKM_WAIT_TIED(2, va[T][0], va[T][1]);
+  else LGKM_WAIT_TIED(0, va[T][0], va[T][1]);
+  const f16x4 lo = __builtin_bit_cast(f16x4, va[T][0]), hi = __builtin_bit_cast(f16x4, va[T][1]);
+  const f16x8 a = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+  O[T & 3] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a, pf[T >> 2], O[T & 3], 0, 0, 0);
+  __builtin_amdgcn_sched_barrier(0);
+  if constexpr (T + 1 < NT) ftr_gemm_step<VB, T + 1>(vb, pf, O, va);
+}
+template <int VB>
+__device__ __forceinline__ void ftr_gemm(const uint32_t* vb, const f16x8* pf, f32x16* O) {
+  u32x2 va[4 * NKS][2];
+  ftr_read_step<VB, 0>(vb, va);
+  ftr_read_step<VB, 1>(vb, va);
+  ftr_read_step<VB, 2>(vb, va);
+  ftr_read_step<VB, 3>(vb, va);
+  ftr_gemm_step<VB, 0>(vb, pf, O, va);
+}
+
+__device__ __forceinline__ void fmask_tail_rel(f32x16* S, int rel) {
+#pragma unroll
+  for (int kb = 0; kb < NKB; kb++)
+#pragma unroll
+    for (int i = 0; i < 16; i++)
+      if (32 * kb + 8 * (i >> 2) + (i & 3) >= rel) S[kb][i] = -__builtin_inff();
+}
 static_assert(BQ == 32 * NWAVES, "one 32-query block per wave");
 
 struct AttnParams {
@@ -75,11 +158,11 @@ struct AttnParams {
   int32_t xcd_slots;  // workgroups per XCD (grid / 8), for the XCD-aware item order
 };
 
-// Maximum over the query's 64 keys of one tile (exact: any evaluation order gives these bits).
+// Maximum over the query's 96 keys of one tile (exact: any evaluation order gives these bits).
 __device__ __forceinline__ float tile_max(const f32x16* S) {
   float a = -__builtin_inff();
 #pragma unroll
-  for (int kb = 0; kb < 2; kb++)
+  for (int kb = 0; kb < NKB; kb++)
 #pragma unroll
     for (int i = 0; i < 16; i += 2) a = __builtin_fmaxf(__builtin_fmaxf(a, S[kb][i]), S[kb][i + 1]);
   float x, y;
@@ -100,17 +183,22 @@ __device__ __forceinline__ void load_q(const AttnParams& p, int s0, int qrow, bo
   }
 }
 
-// p = exp2(s*c - m) for the lane's 32 keys, packed to fp16 B operands; returns the sum of the
-// FP32 values in a fixed binary tree.
+// p = exp2(s*c - m) for the lane's 48 keys, packed to fp16 B operands; returns the sum of the
+// FP32 values in a fixed order (a binary tree within each 32-key block, then the blocks in order).
 __device__ __forceinline__ float exp_pack_sum(const f32x16* S, float c, float m, f16x8* pf) {
-  float pr[32];
+  // one 32-key block at a time, so at most 16 values of p are live
+  float t = 0.0f;
 #pragma unroll
-  for (int kb = 0; kb < 2; kb++)
+  for (int kb = 0; kb < NKB; kb++) {
+    float pr[16];
 #pragma unroll
-    for (int i = 0; i < 16; i++) pr[16 * kb + i] = __builtin_amdgcn_exp2f(__builtin_fmaf(S[kb][i], c, -m));
-#pragma unroll
-  for (int ks = 0; ks < 4; ks++) pf[ks] = pack_p(&pr[8 * ks]);
-  return tree_sum<32>(pr);
+    for (int i = 0; i < 16; i++) pr[i] = __builtin_amdgcn_exp2f(__builtin_fmaf(S[kb][i], c, -m));
+    pf[2 * kb] = pack_p(&pr[0]);
+    pf[2 * kb + 1] = pack_p(&pr[8]);
+    const float tb = tree_sum<16>(pr);
+    t = kb == 0 ? tb : t + tb;
+  }
+  return t;
 }
 
 template <int N>
@@ -119,8 +207,8 @@ struct Par {
 };
 
 __global__ __launch_bounds__(64 * NWAVES, 1) void k_attn_fwd(AttnParams p) {
-  // K tiles in buffers 0, 1 and V tiles in buffers 2, 3 (16 KB each)
-  __shared__ __attribute__((aligned(1024))) uint16_t lds[4 * TILE_ELEMS];
+  // K tiles in buffers 0, 1 and V tiles in buffers 2, 3 (24 KB each)
+  __shared__ __attribute__((aligned(1024))) uint16_t lds[4 * FTILE];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -170,7 +258,8 @@ __global__ __launch_bounds__(64 * NWAVES, 1) void k_attn_fwd(AttnParams p) {
   uint32_t vb[4];  // LDS byte addresses of the lane's V operand rows (buffer 0, rows tr_row), by db
 #pragma unroll
   for (int db = 0; db < 4; db++)
-    vb[db] = (uint32_t)(size_t)(const __attribute__((address_space(3))) uint16_t*)(lds + v_off(tr_row, 32 * db + tr_col));
+    vb[db] = (uint32_t)(size_t)(const __attribute__((address_space(3))) uint16_t*)(lds + 2 * FTILE +
+                                                                                   v_off(tr_row, 32 * db + tr_col));
 
   for (int round = 0;; round++) {
     const int64_t v = ((int64_t)round * 8 + xcd) * nslots + slot;
@@ -184,22 +273,22 @@ __global__ __launch_bounds__(64 * NWAVES, 1) void k_attn_fwd(AttnParams p) {
     const int L = p.segtab[2 * seg + 1];
     if (s0 < 0 || L <= 0 || (int64_t)s0 + L > T || qt < 0 || qt * BQ >= L) continue;
 
-    const int ntiles = (L + BK - 1) / BK;
-    const int rem = L - (ntiles - 1) * BK;  // valid keys of the last tile, 1..64
+    const int ntiles = (L + FROWS - 1) / FROWS;
+    const int rem = L - (ntiles - 1) * FROWS;  // valid keys of the last tile, 1..FROWS
     const uint16_t* kbase = p.khat + ((int64_t)head * T + s0) * HD;
     const uint16_t* vbase = p.v16 + ((int64_t)head * T + s0) * HD;
 
     // Every wave has finished reading LDS for the previous item before it is overwritten.
     __syncthreads();
-    tile_to_lds<NWAVES>(kbase, L, lds, wv, k_lane_off);  // K(0)
+    ftile_to_lds<NWAVES>(kbase, L, lds, wv, k_lane_off);  // K(0)
 
     const int qrow = qt * BQ + wv * 32 + l32;
     const bool qvalid = qrow < L;
     bf16x8 qf[8];
     load_q(p, s0, qrow, qvalid, head, hh, qf);
 
-    f32x16 S[2];   // scores of the tile whose softmax is next
-    f16x8 pf[4];   // P of the tile whose P.V is next
+    f32x16 S[NKB];  // scores of the tile whose softmax is next
+    f16x8 pf[NKS];  // P of the tile whose P.V is next
     f32x16 O[4];
 #pragma unroll
     for (int d = 0; d < 4; d++)
@@ -216,10 +305,10 @@ __global__ __launch_bounds__(64 * NWAVES, 1) void k_attn_fwd(AttnParams p) {
       constexpr int MP = decltype(mp)::value;
       const int m = t >> 1;
       if (m + 1 < ntiles)
-        tile_to_lds<4>(kbase + (int64_t)(m + 1) * BK * HD, L - (m + 1) * BK, lds + (1 - MP) * TILE_ELEMS, wv & 3,
-                       k_lane_off4);
+        ftile_to_lds<4>(kbase + (int64_t)(m + 1) * FROWS * HD, L - (m + 1) * FROWS, lds + (1 - MP) * FTILE, wv & 3,
+                        k_lane_off4);
       if (m < ntiles)
-        tile_to_lds<4>(vbase + (int64_t)m * BK * HD, L - m * BK, lds + (2 + MP) * TILE_ELEMS, wv & 3, v_lane_off4);
+        ftile_to_lds<4>(vbase + (int64_t)m * FROWS * HD, L - m * FROWS, lds + (2 + MP) * FTILE, wv & 3, v_lane_off4);
     };
 
     // Phase tau of this wave runs in slot t = tau + grp.  Even tau: G(k), k = tau/2 - 1 (scores of
@@ -242,18 +331,18 @@ __global__ __launch_bounds__(64 * NWAVES, 1) void k_attn_fwd(AttnParams p) {
         const int k = tau / 2 - 1;
         constexpr int KBUF = TM == 0 ? 0 : 1;  // K(k+1): k = 2n-1 -> K(2n); k = 2n -> K(2n+1)
         constexpr int VBUF = TM == 0 ? 1 : 0;  // V(k)
-        if (k + 1 < ntiles) gemm_scores<4>(lds + KBUF * TILE_ELEMS, qf, l32, hh, S);
-        if (k >= 0) tr_gemm<2 + VBUF>(vb, pf, O);
+        if (k + 1 < ntiles) fscores<4>(lds + KBUF * FTILE, qf, l32, hh, S);
+        if (k >= 0) ftr_gemm<VBUF>(vb, pf, O);
       } else {
         const int k = (tau - 1) / 2 - 1;
         if (k + 1 < ntiles) {
-          if (k + 1 == ntiles - 1 && rem < BK) {
-            // The key limit enters as an opaque per-lane value, so the 32 compares stay in this
-            // last-tile branch: hoisted out of the loop they were 32 SGPR masks, and the SGPR
+          if (k + 1 == ntiles - 1 && rem < FROWS) {
+            // The key limit enters as an opaque per-lane value, so the 48 compares stay in this
+            // last-tile branch: hoisted out of the loop they were 48 SGPR masks, and the SGPR
             // spills they caused were reloaded on every phase.
             int r = rem - 4 * hh;
             asm volatile("" : "+v"(r));
-            mask_tail_rel(S, r);
+            fmask_tail_rel(S, r);
           }
           float ts = exp_pack_sum(S, c, m_run, pf);
           // rare (the first tile, where m is -inf, or a tile whose p would pass the limit): move m
