@@ -22,10 +22,11 @@
 // work: the matrix cores stay busy and the softmax is hidden behind them.
 //
 // K and V tiles (96 keys, 24 KB each) are copied from the workspace straight into LDS with
-// buffer_load_dwordx4 ... lds (no register staging), double-buffered; the copies of K(m+1) and
-// V(m) are issued at the start of phase slot 2m by the trailing waves (then in their vector phase)
-// and have two slots to land: the phase barriers carry no memory fence, and each wave waits for
-// its own copies only before slot 2m+2.
+// buffer_load_dwordx4 ... lds (no register staging), double-buffered.  Copies are issued only in
+// vector phases, a quarter of a tile per wave: K(m+1) at the start of phase slot 2m by the
+// trailing waves (two slots to land) and V(m) at the start of slot 2m+1 by the leading waves (one
+// slot to land).  The phase barriers carry no memory fence; each wave waits for its own copies
+// only before slot 2m+2, where both are first read.
 //
 // LDS layouts are XOR-swizzled by 16-byte chunk (the copy picks, per lane, which global chunk
 // lands in its LDS slot), so that both read patterns are free of bank conflicts:
@@ -249,7 +250,7 @@ __global__ __launch_bounds__(64 * NWAVES, 1) void k_attn_fwd(AttnParams p) {
   const int nslots = p.xcd_slots;
 
   const int k_lane_off = tile_lane_offset(false, wv, lane);
-  // the trailing waves issue the loop's copies, each a quarter of a tile
+  // the loop's copies: each wave of a group issues a quarter of a tile
   const int k_lane_off4 = tile_lane_offset(false, wv & 3, lane);
   const int v_lane_off4 = tile_lane_offset(true, wv & 3, lane);
   const int tr_row = 4 * hh + ((lane & 15) >> 2);
@@ -297,16 +298,21 @@ __global__ __launch_bounds__(64 * NWAVES, 1) void k_attn_fwd(AttnParams p) {
     float lsum = 0.0f;
     float m_run = -__builtin_inff();
 
-    // Copies issued at phase slot 2m: K(m+1) and V(m), into the buffers of K(m-1) and V(m-2),
-    // which were last read in slot 2m-1.
+    // K(m+1) and V(m) go into the buffers of K(m-1) and V(m-2), which were last read in slot 2m-1.
     // The buffer parity MP = m & 1 is a compile-time constant at every call, so the compiler can
     // see that a copy never writes the buffers being read and needs no wait for it.
-    auto issue_copies = [&](int t, auto mp) {
+    // trailing waves, even slot t = 2m: K(m+1) (two slots to land)
+    auto issue_k = [&](int t, auto mp) {
       constexpr int MP = decltype(mp)::value;
       const int m = t >> 1;
       if (m + 1 < ntiles)
         ftile_to_lds<4>(kbase + (int64_t)(m + 1) * FROWS * HD, L - (m + 1) * FROWS, lds + (1 - MP) * FTILE, wv & 3,
                         k_lane_off4);
+    };
+    // leading waves, odd slot t = 2m+1: V(m) (one slot to land)
+    auto issue_v = [&](int t, auto mp) {
+      constexpr int MP = decltype(mp)::value;
+      const int m = t >> 1;
       if (m < ntiles)
         ftile_to_lds<4>(vbase + (int64_t)m * FROWS * HD, L - m * FROWS, lds + (2 + MP) * FTILE, wv & 3, v_lane_off4);
     };
@@ -317,15 +323,13 @@ __global__ __launch_bounds__(64 * NWAVES, 1) void k_attn_fwd(AttnParams p) {
     auto phase = [&](int tau, auto tm) {
       constexpr int TM = decltype(tm)::value;
       const int t = tau + grp;
-      // copies issued at slot t-2 are read from slot t on: wait for them (vmcnt(0)) before the barrier
+      // copies issued at slot t-2 or t-1 are read from slot t on: wait for them (vmcnt(0)) before the barrier
       if (!(t & 1) && t >= 2) __builtin_amdgcn_s_waitcnt(0xF70);
       phase_barrier();
-      // slot t = tau + grp is even (a copy slot) for tau % 2 == grp; m = t / 2 has the parity below
-      if constexpr ((TM & 1) == 0) {
-        // (the leading waves issue no copies: in a copy slot they are in their matrix phase, which
-        // is the longer one)
-      } else {
-        if (grp == 1) issue_copies(t, Par<(TM == 1 ? 1 : 0)>{});  // t = 4n + TM + 1: m = 2n + 1 or 2n + 2
+      // copies only in vector phases (odd tau); m = t / 2 has the parity below
+      if constexpr ((TM & 1) == 1) {
+        if (grp == 1) issue_k(t, Par<(TM == 1 ? 1 : 0)>{});  // t = 4n + TM + 1: m = 2n + 1 or 2n + 2
+        else issue_v(t, Par<(TM == 1 ? 0 : 1)>{});           // t = 4n + TM: m = 2n or 2n + 1
       }
       if constexpr ((TM & 1) == 0) {
         const int k = tau / 2 - 1;
@@ -369,7 +373,7 @@ __global__ __launch_bounds__(64 * NWAVES, 1) void k_attn_fwd(AttnParams p) {
     __builtin_amdgcn_s_waitcnt(0xF70);  // K(0) has landed (the slot-0 barrier publishes it)
     if (grp == 1) {                     // slot 0 of the trailing waves: barrier and copies only
       phase_barrier();
-      issue_copies(0, Par<0>{});
+      issue_k(0, Par<0>{});
     }
     const int tau_last = 2 * ntiles + 1 - grp;
     int tau = 0;
