@@ -147,3 +147,19 @@ def test_long_batch_past_the_decode_prefetch_alone_equals_batched():
         o, l = run_fwd(alone, want_lse=True)
         assert bitwise_equal(o, batched[t0:t0 + n]) and bitwise_equal(l, blse[t0:t0 + n]), f"segment at {t0}"
         t0 += n
+
+
+def test_key_tile_edges_alone_equal_batched():
+    """Segments one key short of, at, and one key past two, three and four KV tiles of 96 keys:
+    each alone gives the bits it gives in the batch."""
+    lens = [191, 192, 193, 287, 288, 289, 383, 384, 385]
+    x = workloads.random_inputs(lens, 2, seed=73)
+    g = to_dev(x)
+    say(f"[bitwise] {sum(lens)}-token batch of key-tile edge lengths vs its segments alone")
+    batched, blse = run_fwd(g, want_lse=True)
+    t0 = 0
+    for n in lens:
+        alone = {k: (g[k][t0:t0 + n].contiguous() if k in ("q", "k", "v", "seg") else g[k]) for k in g}
+        o, l = run_fwd(alone, want_lse=True)
+        assert bitwise_equal(o, batched[t0:t0 + n]) and bitwise_equal(l, blse[t0:t0 + n]), f"segment at {t0}"
+        t0 += n

@@ -45,6 +45,14 @@ def test_parity_ragged_tiles():
     _check_full("ragged", workloads.random_inputs(lens, 3, seed=21))
 
 
+def test_parity_key_tile_edges():
+    """Segment lengths around multiples of 96 keys (one to five KV tiles, the last tile one key
+    short, full or one key long), so both parities of the tile count and every remainder class of
+    the last tile run against the oracle."""
+    lens = [95, 96, 97, 191, 192, 193, 287, 288, 289, 383, 384, 385, 479, 480, 481]
+    _check_full("key_tiles", workloads.random_inputs(lens, 3, seed=29))
+
+
 def test_parity_many_single_token_segments():
     """4096 one-token segments around a few longer ones (a work item per token): the whole output
     matches the oracle, and every one-token segment returns its own v (P = 1): bit for bit where v
