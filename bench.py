@@ -83,7 +83,7 @@ def main():
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
         print(f"bench.py measures one GPU only (asked for --gpus {args.gpus}, WORLD_SIZE {world}); "
-              "the attention node shards by head or packed row with no exchange, see the design notes",
+              "the attention node shards by head or packed row with no exchange",
               file=sys.stderr)
         sys.exit(2)
 

@@ -24,9 +24,9 @@
  *     r = 1 / sqrt(ms + eps) (correctly rounded sqrt and division), y_d = (x_d * r) * w_d, then ONE
  *     round-to-nearest-even from FP64 to bf16.  The normed q and k enter Q.K^T as bf16.
  *   Attention: S = scale * Qn.Kn^T in FP32 (bf16 MFMA, FP32 accumulate); an online softmax over the
- *     segment's keys in fixed 64-key tiles, walked in ascending order from the segment's first key;
+ *     segment's keys in fixed 96-key tiles, walked in ascending order from the segment's first key;
  *     O = (sum_j p_ij v_j) / l_i, rounded once to bf16.  P.V runs on fp16 MFMA with V converted
- *     exactly to fp16 (bf16 P would miss the accuracy bound; see the design notes).
+ *     exactly to fp16 (bf16 P would miss the accuracy bound).
  *   lse (optional, may be NULL): fp32 [T, H], natural-log log-sum-exp of each row's scaled scores.
  *   Determinism: every output row is a function of its own segment's bytes, the weights, eps and
  *     scale only -- not of the batch, the segment's offset in the batch, neighbouring segments,

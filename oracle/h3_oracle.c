@@ -17,7 +17,7 @@
  *  - "33B forward/backward and rollout-vs-train control", Scope: FP32 accumulation with one final
  *    rounding.  The oracle is the exact (FP64) value that such a kernel approximates.
  *
- * Readings where the pages are silent (each is listed with its reason in the design notes):
+ * Readings where the pages are silent:
  *  - segments: int32 ids per token, non-decreasing; a segment is a maximal run of equal ids;
  *  - norm: y = x * (mean(x^2) + eps)^(-1/2) * w over the 128 channels of one (token, head), computed
  *    in FP64 and rounded ONCE, round-to-nearest-even, directly from FP64 to bf16 (the q_norm node's
