@@ -10,7 +10,8 @@ import torch
 
 import oracle
 import workloads
-from gpu_util import EPS, LSE_REL_BOUND, MAX_ABS_BOUND, REL_L2_BOUND, f64, lse_error, metrics, run_fwd, say, to_dev
+from gpu_util import (EPS, LSE_REL_BOUND, MAX_ABS_BOUND, REL_L2_BOUND, bitwise_equal, f64, lse_error, metrics, run_fwd,
+                      say, to_dev)
 
 pytestmark = pytest.mark.gpu
 
@@ -51,6 +52,42 @@ def test_parity_key_tile_edges():
     the last tile run against the oracle."""
     lens = [95, 96, 97, 191, 192, 193, 287, 288, 289, 383, 384, 385, 479, 480, 481]
     _check_full("key_tiles", workloads.random_inputs(lens, 3, seed=29))
+
+
+def test_parity_running_max_moves_on_every_tile():
+    """Keys turn from opposite to the queries' direction to along it over each segment, their cosine
+    to the queries rising linearly (norm weights of 6, so scaled scores span about -400..400): every
+    96-key tile passes the running maximum by far more than the p-sum limit allows, so the rescale branch runs on every tile of every row,
+    which the other workloads reach only on the first tile.  Oracle parity, and each segment alone
+    gives the bits it gives in the batch.  (A row here rests on a handful of keys, so the fp16
+    rounding of their p does not average out: rel L2 measured 1.7e-3 against the 2e-3 bound.)"""
+    lens = [1000, 700]
+    H = 2
+    x = workloads.random_inputs(lens, H, seed=31)
+    gen = torch.Generator().manual_seed(31)
+    T = sum(lens)
+    q = torch.empty(T, H, 128)
+    k = torch.empty(T, H, 128)
+    t0 = 0
+    for L in lens:
+        a = torch.linspace(-1.0, 1.0, L, dtype=torch.float64)[:, None]  # cosine to the queries, linear in the key
+        for h in range(H):
+            d, e = torch.linalg.qr(torch.randn(128, 2, generator=gen, dtype=torch.float64))[0].T
+            q[t0:t0 + L, h] = (d + 0.01 * torch.randn(L, 128, generator=gen, dtype=torch.float64)).float()
+            k[t0:t0 + L, h] = (a * d + torch.sqrt(1.0 - a * a) * e).float()
+        t0 += L
+    x["q"] = q.to(torch.bfloat16)
+    x["k"] = k.to(torch.bfloat16)
+    x["wq"] = torch.full((128,), 6.0, dtype=torch.bfloat16)
+    x["wk"] = torch.full((128,), 6.0, dtype=torch.bfloat16)
+    out = _check_full("running_max", x)
+    g = to_dev(x)
+    t0 = 0
+    for L in lens:
+        alone = {n: (g[n][t0:t0 + L].contiguous() if n in ("q", "k", "v", "seg") else g[n]) for n in g}
+        o, _ = run_fwd(alone, eps=EPS, scale=128 ** -0.5, want_lse=True)
+        assert bitwise_equal(o, out[t0:t0 + L]), f"segment at {t0}"
+        t0 += L
 
 
 def test_parity_many_single_token_segments():
