@@ -16,6 +16,9 @@ Functions follow the RL-Kernel MiniMax-H3 pull-request pages:
   * ``bwd``: the gradients of that composite (norm, bf16 rounding taken as the identity, attention)
     with respect to q, k, v and both norm weights, in FP64 -- the node inside the training step's
     backward ("33B forward/backward" page).
+  * ``rope_f64`` and the ``cos``/``sin`` arguments of ``fwd_ex`` / ``bwd``: the MM-RoPE node between
+    the norm and the attention ("ws1_one_h3_block", Bindings: rope_q/rope_k; Tests: 96 of 128
+    channels rotated), driven by per-token tables of the 48 pairs' cosines and sines.
 """
 from __future__ import annotations
 
@@ -74,8 +77,11 @@ def _load():
     lib.oracle_fwd_rows.argtypes = [P, P, P, P, P, P, I64, I32, D, D, P, I64, P, P]
     lib.oracle_bwd.argtypes = [P, P, P, P, P, P, P, I64, I32, D, D, ctypes.c_int, P, P, P, P, P]
     lib.oracle_fwd_opt.argtypes = [P, P, P, P, P, P, I64, I32, D, D, ctypes.c_int, P]
+    lib.oracle_fwd_ex.argtypes = [P, P, P, P, P, P, P, P, ctypes.c_int, I64, I32, D, D, P, I64, P, P]
+    lib.oracle_bwd_ex.argtypes = [P, P, P, P, P, P, P, P, P, I64, I32, D, D, ctypes.c_int, P, P, P, P, P]
+    lib.oracle_rope_f64.argtypes = [P, P, P, P, I64, I32]
     for f in (lib.oracle_segments, lib.oracle_rmsnorm_f64, lib.oracle_qknorm, lib.oracle_fwd, lib.oracle_fwd_rows,
-              lib.oracle_bwd, lib.oracle_fwd_opt):
+              lib.oracle_bwd, lib.oracle_fwd_opt, lib.oracle_fwd_ex, lib.oracle_bwd_ex, lib.oracle_rope_f64):
         f.restype = ctypes.c_int
     _lib = lib
     return lib
@@ -191,13 +197,62 @@ def fwd_rows(q, k, v, seg_ids, rows, wq=None, wk=None, eps: float = 1e-6, scale:
     return out, lse
 
 
+ROPE_PAIRS = 48
+
+
+def _table(t, T):
+    """A rope table: float32 [T, 48] (the cosines or sines of every token's 48 rotated pairs)."""
+    if t is None:
+        return None
+    if hasattr(t, "detach"):
+        t = t.detach().cpu().numpy()
+    t = np.ascontiguousarray(t, dtype=np.float32)
+    if t.shape != (T, ROPE_PAIRS):
+        raise ValueError(f"rope table must be [{T}, {ROPE_PAIRS}], got {t.shape}")
+    return t
+
+
+def rope_f64(x, cos, sin) -> np.ndarray:
+    """Unrounded FP64 rotation of every 128-wide row of x [T, H, 128] (bf16) by its token's table:
+    pairs (2i, 2i+1), i < 48, rotated by (cos[t, i], sin[t, i]); channels 96..127 unchanged."""
+    x = _bits(x)
+    T, H, D = x.shape
+    c, sn = _table(cos, T), _table(sin, T)
+    y = np.empty((T, H, D), np.float64)
+    _check(_load().oracle_rope_f64(_ptr(x), _ptr(c), _ptr(sn), _ptr(y), T, H))
+    return y
+
+
+def fwd_ex(q, k, v, seg_ids, wq=None, wk=None, eps: float = 1e-6, scale: float | None = None, cos=None, sin=None,
+           round_operands: bool = True, rows=None):
+    """The forward with every option: rope tables (cos, sin float32 [T, 48], with weights only), the
+    operands' bf16 roundings (round_operands=False: exact FP64 norm and rope outputs) and selected
+    query rows.  Returns (out FP64, lse FP64) for every token or for the listed rows."""
+    q, k, v = _bits(q), _bits(k), _bits(v)
+    T, H, D = q.shape
+    assert D == HEAD_DIM and k.shape == q.shape and v.shape == q.shape
+    wq, wk = _bits(wq, (HEAD_DIM,)), _bits(wk, (HEAD_DIM,))
+    c, sn = _table(cos, T), _table(sin, T)
+    s = np.ascontiguousarray(seg_ids, dtype=np.int32)
+    assert s.shape == (T,)
+    scale = float(HEAD_DIM ** -0.5 if scale is None else scale)
+    r = None if rows is None else np.ascontiguousarray(rows, dtype=np.int64)
+    n = T if r is None else r.shape[0]
+    out = np.empty((n, H, D), np.float64)
+    lse = np.empty((n, H), np.float64)
+    _check(_load().oracle_fwd_ex(_ptr(q), _ptr(k), _ptr(v), _ptr(s), _ptr(wq), _ptr(wk), _ptr(c), _ptr(sn),
+                                 int(bool(round_operands)), T, H, float(eps), scale, _ptr(r), 0 if r is None else n,
+                                 _ptr(out), _ptr(lse)))
+    return out, lse
+
+
 def bwd(q, k, v, seg_ids, dout, wq=None, wk=None, eps: float = 1e-6, scale: float | None = None,
-        round_operands: bool = True):
+        round_operands: bool = True, cos=None, sin=None):
     """FP64 gradients of the node for upstream gradient dout [T,H,128] (bf16 bits).
 
     Returns (dq, dk, dv) FP64 [T,H,128] and (dwq, dwk) FP64 [128] (None without weights).  With
     round_operands=False the normed operands are not rounded to bf16 (exact gradient of a smooth
-    function, for finite-difference checks)."""
+    function, for finite-difference checks).  cos, sin: rope tables as for fwd_ex."""
     q, k, v, dout = _bits(q), _bits(k), _bits(v), _bits(dout)
     T, H, D = q.shape
     assert D == HEAD_DIM and k.shape == q.shape and v.shape == q.shape and dout.shape == q.shape
@@ -210,8 +265,10 @@ def bwd(q, k, v, seg_ids, dout, wq=None, wk=None, eps: float = 1e-6, scale: floa
     dv = np.empty((T, H, D), np.float64)
     dwq = np.zeros(HEAD_DIM, np.float64) if wq is not None else None
     dwk = np.zeros(HEAD_DIM, np.float64) if wq is not None else None
-    _check(_load().oracle_bwd(_ptr(q), _ptr(k), _ptr(v), _ptr(s), _ptr(wq), _ptr(wk), _ptr(dout), T, H, float(eps),
-                              scale, int(bool(round_operands)), _ptr(dq), _ptr(dk), _ptr(dv), _ptr(dwq), _ptr(dwk)))
+    c, sn = _table(cos, T), _table(sin, T)
+    _check(_load().oracle_bwd_ex(_ptr(q), _ptr(k), _ptr(v), _ptr(s), _ptr(wq), _ptr(wk), _ptr(c), _ptr(sn), _ptr(dout),
+                                 T, H, float(eps), scale, int(bool(round_operands)), _ptr(dq), _ptr(dk), _ptr(dv),
+                                 _ptr(dwq), _ptr(dwk)))
     return dq, dk, dv, dwq, dwk
 
 

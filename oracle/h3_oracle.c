@@ -149,10 +149,64 @@ int oracle_qknorm(const uint16_t* x, const uint16_t* w, uint16_t* y, int64_t T, 
 
 /* ---------------------------------------------------------------- attention */
 
-/* The bf16 operands entering Q.K^T: the norm node's output, or the inputs themselves when no
- * weights are given.  Returned as FP64 in head-major order [H][T][128] (bf16 values are exact in
- * FP64), so one head's rows are contiguous. */
-static double* normed_operand(const uint16_t* x, const uint16_t* w, int64_t T, int32_t H, double eps) {
+/* ---------------------------------------------------------------- MM-RoPE (partial) */
+
+/* The rope node between q_norm/k_norm and attention ("ws1_one_h3_block" page, Bindings table:
+ * rope_q, rope_k; Tests: MM-RoPE rotates 96 of 128 channels).  The pages give neither the axis
+ * split nor the frequencies, so the rotation is table-driven: the caller supplies, per token, the
+ * cosine and sine of each of the 48 rotated pairs (cos_t, sin_t: [T][48], float32), having composed
+ * the three axes itself.  Pairing (a reading): channels (2i, 2i+1) for i < 48 form pair i and are
+ * rotated by that pair's angle; channels 96..127 pass through unchanged:
+ *   y_2i = x_2i cos - x_2i+1 sin,   y_2i+1 = x_2i sin + x_2i+1 cos.
+ * Evaluated in FP64 (the products of bf16 and float32 values are exact), unrounded here. */
+#define ROPE_PAIRS 48
+
+static void rope_row_f64(const double* x, const float* c, const float* sn, double* y) {
+  for (int i = 0; i < ROPE_PAIRS; i++) {
+    const double a = x[2 * i], b = x[2 * i + 1];
+    const double ci = (double)c[i], si = (double)sn[i];
+    y[2 * i] = a * ci - b * si;
+    y[2 * i + 1] = a * si + b * ci;
+  }
+  for (int d = 2 * ROPE_PAIRS; d < HD; d++) y[d] = x[d];
+}
+
+/* The transpose of the rotation (its gradient): dx_2i = dy_2i cos + dy_2i+1 sin,
+ * dx_2i+1 = -dy_2i sin + dy_2i+1 cos; channels 96..127 unchanged. */
+static void rope_row_transpose_f64(const double* dy, const float* c, const float* sn, double* dx) {
+  for (int i = 0; i < ROPE_PAIRS; i++) {
+    const double a = dy[2 * i], b = dy[2 * i + 1];
+    const double ci = (double)c[i], si = (double)sn[i];
+    dx[2 * i] = a * ci + b * si;
+    dx[2 * i + 1] = b * ci - a * si;
+  }
+  for (int d = 2 * ROPE_PAIRS; d < HD; d++) dx[d] = dy[d];
+}
+
+/* Unrounded FP64 rotation of every 128-wide row of x [T, H, 128] (bf16 bits) by its token's table. */
+int oracle_rope_f64(const uint16_t* x, const float* cos_t, const float* sin_t, double* y, int64_t T, int32_t H) {
+  if (T < 0 || H < 1 || (T > 0 && (!x || !cos_t || !sin_t || !y))) return ORACLE_ERR_ARGS;
+  int64_t rows = T * (int64_t)H;
+#pragma omp parallel for schedule(static)
+  for (int64_t r = 0; r < rows; r++) {
+    const int64_t t = r / H;
+    double xr[HD];
+    for (int d = 0; d < HD; d++) xr[d] = oracle_bf16_to_f64(x[r * HD + d]);
+    rope_row_f64(xr, cos_t + t * ROPE_PAIRS, sin_t + t * ROPE_PAIRS, y + r * HD);
+  }
+  return ORACLE_OK;
+}
+
+/* ---------------------------------------------------------------- attention */
+
+/* The operands entering Q.K^T, as FP64 in head-major order [H][T][128] (one head's rows contiguous).
+ * With weights: the norm node's output, rounded once to bf16 (the node's output dtype) when `round`;
+ * then, with rope tables, the rope node on that output, rounded once more to bf16 when `round` (the
+ * block's q_norm -> rope -> attention sequence, each node emitting bf16).  Without weights: the
+ * inputs themselves (already normalised by the caller; no rope).  round == 0 keeps every step exact
+ * (a smooth function, for the finite-difference and "pure" checks). */
+static double* operand(const uint16_t* x, const uint16_t* w, const float* cos_t, const float* sin_t, int64_t T,
+                       int32_t H, double eps, int round) {
   int64_t n = T * (int64_t)H * HD;
   double* out = (double*)malloc((size_t)(n > 0 ? n : 1) * sizeof(double));
   if (!out) return NULL;
@@ -164,7 +218,11 @@ static double* normed_operand(const uint16_t* x, const uint16_t* w, int64_t T, i
     if (w) {
       double yr[HD];
       norm_row_f64(x + r * HD, w, eps, yr);
-      for (int d = 0; d < HD; d++) o[d] = oracle_bf16_to_f64(oracle_f64_to_bf16(yr[d]));
+      for (int d = 0; d < HD; d++) o[d] = round ? oracle_bf16_to_f64(oracle_f64_to_bf16(yr[d])) : yr[d];
+      if (cos_t) {
+        rope_row_f64(o, cos_t + t * ROPE_PAIRS, sin_t + t * ROPE_PAIRS, yr);
+        for (int d = 0; d < HD; d++) o[d] = round ? oracle_bf16_to_f64(oracle_f64_to_bf16(yr[d])) : yr[d];
+      }
     } else {
       for (int d = 0; d < HD; d++) o[d] = oracle_bf16_to_f64(x[r * HD + d]);
     }
@@ -204,10 +262,11 @@ static void attend_one(const double* qh, const double* kh, const double* vd, int
 /* Shared driver.  rows == NULL: every token; else only the listed query tokens (n_rows of them),
  * with out/lse laid out [n_rows, H, 128] / [n_rows, H]. */
 static int fwd_impl(const uint16_t* q, const uint16_t* k, const uint16_t* v, const int32_t* seg, const uint16_t* wq,
-                    const uint16_t* wk, int64_t T, int32_t H, double eps, double scale, const int64_t* rows,
-                    int64_t n_rows, double* out, double* lse) {
+                    const uint16_t* wk, const float* cos_t, const float* sin_t, int round, int64_t T, int32_t H,
+                    double eps, double scale, const int64_t* rows, int64_t n_rows, double* out, double* lse) {
   if (T < 0 || H < 1) return ORACLE_ERR_ARGS;
   if ((wq == NULL) != (wk == NULL)) return ORACLE_ERR_ARGS;
+  if ((cos_t == NULL) != (sin_t == NULL) || (cos_t && !wq)) return ORACLE_ERR_ARGS; /* rope needs the norm */
   if (T == 0) return ORACLE_OK;
   if (!q || !k || !v || !seg || !out) return ORACLE_ERR_ARGS;
   int64_t* starts = (int64_t*)malloc((size_t)T * sizeof(int64_t));
@@ -222,9 +281,9 @@ static int fwd_impl(const uint16_t* q, const uint16_t* k, const uint16_t* v, con
   int64_t maxlen = 0;
   for (int64_t s = 0; s < nseg; s++) if (lens[s] > maxlen) maxlen = lens[s];
 
-  double* qh = normed_operand(q, wq, T, H, eps);
-  double* kh = normed_operand(k, wk, T, H, eps);
-  double* vd = normed_operand(v, NULL, T, H, eps); /* no weights: the exact values of v */
+  double* qh = operand(q, wq, cos_t, sin_t, T, H, eps, round);
+  double* kh = operand(k, wk, cos_t, sin_t, T, H, eps, round);
+  double* vd = operand(v, NULL, NULL, NULL, T, H, eps, 1); /* no weights: the exact values of v */
   if (!qh || !kh || !vd) {
     free(qh); free(kh); free(vd); free(starts); free(lens); free(seg_of);
     return ORACLE_ERR_NOMEM;
@@ -259,7 +318,7 @@ static int fwd_impl(const uint16_t* q, const uint16_t* k, const uint16_t* v, con
  * wq and wk both NULL means q and k are already normalised; exactly one NULL is an error. */
 int oracle_fwd(const uint16_t* q, const uint16_t* k, const uint16_t* v, const int32_t* seg, const uint16_t* wq,
                const uint16_t* wk, int64_t T, int32_t H, double eps, double scale, double* out, double* lse) {
-  return fwd_impl(q, k, v, seg, wq, wk, T, H, eps, scale, NULL, 0, out, lse);
+  return fwd_impl(q, k, v, seg, wq, wk, NULL, NULL, 1, T, H, eps, scale, NULL, 0, out, lse);
 }
 
 /* Forward for selected query tokens only (for sampling full-size workloads). */
@@ -268,7 +327,19 @@ int oracle_fwd_rows(const uint16_t* q, const uint16_t* k, const uint16_t* v, con
                     int64_t n_rows, double* out, double* lse) {
   if (n_rows < 0 || (n_rows > 0 && !rows)) return ORACLE_ERR_ARGS;
   if (n_rows == 0) return ORACLE_OK;
-  return fwd_impl(q, k, v, seg, wq, wk, T, H, eps, scale, rows, n_rows, out, lse);
+  return fwd_impl(q, k, v, seg, wq, wk, NULL, NULL, 1, T, H, eps, scale, rows, n_rows, out, lse);
+}
+
+/* The forward with every option: rope tables (cos_t, sin_t: [T][48] float32, both or neither; only
+ * with weights), the operand rounding (round_operands == 0: the exact FP64 norm and rope outputs),
+ * and optionally selected query rows (rows == NULL: every token). */
+int oracle_fwd_ex(const uint16_t* q, const uint16_t* k, const uint16_t* v, const int32_t* seg, const uint16_t* wq,
+                  const uint16_t* wk, const float* cos_t, const float* sin_t, int round_operands, int64_t T, int32_t H,
+                  double eps, double scale, const int64_t* rows, int64_t n_rows, double* out, double* lse) {
+  if (rows && n_rows == 0) return ORACLE_OK;
+  if (n_rows < 0) return ORACLE_ERR_ARGS;
+  return fwd_impl(q, k, v, seg, wq, wk, cos_t, sin_t, round_operands ? 1 : 0, T, H, eps, scale, rows, n_rows, out,
+                  lse);
 }
 
 /* ---------------------------------------------------------------- backward */
@@ -291,27 +362,6 @@ int oracle_fwd_rows(const uint16_t* q, const uint16_t* k, const uint16_t* v, con
  * then, per (token, head) row x with r = (mean(x^2) + eps)^(-1/2) and g = w * dŷ (dŷ = dq̂ or dk̂):
  *   dx = r g - (r^3 / 128) x (g . x),    dw += dŷ * x * r   (summed over every token and head).
  * Without weights (wq = wk = NULL) dq = dq̂ and dk = dk̂, and dwq / dwk are not produced. */
-
-/* q̂ / k̂ operands like normed_operand, optionally without the bf16 rounding. */
-static double* bwd_operand(const uint16_t* x, const uint16_t* w, int64_t T, int32_t H, double eps, int round) {
-  int64_t n = T * (int64_t)H * HD;
-  double* out = (double*)malloc((size_t)(n > 0 ? n : 1) * sizeof(double));
-  if (!out) return NULL;
-  int64_t rows = T * (int64_t)H;
-#pragma omp parallel for schedule(static)
-  for (int64_t r = 0; r < rows; r++) {
-    const int64_t t = r / H, h = r % H;
-    double* o = out + (h * T + t) * HD;
-    if (w) {
-      double yr[HD];
-      norm_row_f64(x + r * HD, w, eps, yr);
-      for (int d = 0; d < HD; d++) o[d] = round ? oracle_bf16_to_f64(oracle_f64_to_bf16(yr[d])) : yr[d];
-    } else {
-      for (int d = 0; d < HD; d++) o[d] = oracle_bf16_to_f64(x[r * HD + d]);
-    }
-  }
-  return out;
-}
 
 static double dot128(const double* a, const double* b) {
   double part[4] = {0.0, 0.0, 0.0, 0.0};
@@ -381,12 +431,16 @@ static void norm_bwd_row(const uint16_t* x_bits, const uint16_t* w_bits, double 
 }
 
 /* Backward of the whole node.  dout, q, k, v: bf16 bits [T,H,128]; outputs dq, dk, dv FP64 [T,H,128];
- * dwq, dwk FP64 [128] (required when weights are given, ignored otherwise). */
-int oracle_bwd(const uint16_t* q, const uint16_t* k, const uint16_t* v, const int32_t* seg, const uint16_t* wq,
-               const uint16_t* wk, const uint16_t* dout, int64_t T, int32_t H, double eps, double scale,
-               int round_operands, double* dq, double* dk, double* dv, double* dwq, double* dwk) {
+ * dwq, dwk FP64 [128] (required when weights are given, ignored otherwise).  With rope tables the
+ * gradient with respect to the rotated operand goes back through the transposed rotation before
+ * the norm backward (the rope node's rounding, like the norm's, is the identity for gradients). */
+int oracle_bwd_ex(const uint16_t* q, const uint16_t* k, const uint16_t* v, const int32_t* seg, const uint16_t* wq,
+                  const uint16_t* wk, const float* cos_t, const float* sin_t, const uint16_t* dout, int64_t T,
+                  int32_t H, double eps, double scale, int round_operands, double* dq, double* dk, double* dv,
+                  double* dwq, double* dwk) {
   if (T < 0 || H < 1) return ORACLE_ERR_ARGS;
   if ((wq == NULL) != (wk == NULL)) return ORACLE_ERR_ARGS;
+  if ((cos_t == NULL) != (sin_t == NULL) || (cos_t && !wq)) return ORACLE_ERR_ARGS;
   if (wq && (!dwq || !dwk)) return ORACLE_ERR_ARGS;
   if (wq)
     for (int d = 0; d < HD; d++) dwq[d] = dwk[d] = 0.0;
@@ -402,10 +456,10 @@ int oracle_bwd(const uint16_t* q, const uint16_t* k, const uint16_t* v, const in
   for (int64_t s = 0; s < nseg; s++) if (lens[s] > maxlen) maxlen = lens[s];
 
   const int64_t n = T * (int64_t)H * HD;
-  double* qh = bwd_operand(q, wq, T, H, eps, round_operands);
-  double* kh = bwd_operand(k, wk, T, H, eps, round_operands);
-  double* vd = bwd_operand(v, NULL, T, H, eps, 1);
-  double* go = bwd_operand(dout, NULL, T, H, eps, 1);
+  double* qh = operand(q, wq, cos_t, sin_t, T, H, eps, round_operands);
+  double* kh = operand(k, wk, cos_t, sin_t, T, H, eps, round_operands);
+  double* vd = operand(v, NULL, NULL, NULL, T, H, eps, 1);
+  double* go = operand(dout, NULL, NULL, NULL, T, H, eps, 1);
   double* dqh = (double*)calloc((size_t)n, sizeof(double)); /* head-major [H][T][128] */
   double* dkh = (double*)calloc((size_t)n, sizeof(double));
   double* dvh = (double*)calloc((size_t)n, sizeof(double));
@@ -440,8 +494,16 @@ int oracle_bwd(const uint16_t* q, const uint16_t* k, const uint16_t* v, const in
         const int64_t src = (h * T + t) * HD;
         for (int d = 0; d < HD; d++) dv[r * HD + d] = dvh[src + d];
         if (wq) {
-          norm_bwd_row(q + r * HD, wq, eps, dqh + src, dq + r * HD, dwq_rows + r * HD);
-          norm_bwd_row(k + r * HD, wk, eps, dkh + src, dk + r * HD, dwk_rows + r * HD);
+          double gq[HD], gk[HD];
+          if (cos_t) {
+            rope_row_transpose_f64(dqh + src, cos_t + t * ROPE_PAIRS, sin_t + t * ROPE_PAIRS, gq);
+            rope_row_transpose_f64(dkh + src, cos_t + t * ROPE_PAIRS, sin_t + t * ROPE_PAIRS, gk);
+          } else {
+            memcpy(gq, dqh + src, sizeof(gq));
+            memcpy(gk, dkh + src, sizeof(gk));
+          }
+          norm_bwd_row(q + r * HD, wq, eps, gq, dq + r * HD, dwq_rows + r * HD);
+          norm_bwd_row(k + r * HD, wk, eps, gk, dk + r * HD, dwk_rows + r * HD);
         } else {
           for (int d = 0; d < HD; d++) {
             dq[r * HD + d] = dqh[src + d];
@@ -464,33 +526,17 @@ int oracle_bwd(const uint16_t* q, const uint16_t* k, const uint16_t* v, const in
   return rc;
 }
 
+int oracle_bwd(const uint16_t* q, const uint16_t* k, const uint16_t* v, const int32_t* seg, const uint16_t* wq,
+               const uint16_t* wk, const uint16_t* dout, int64_t T, int32_t H, double eps, double scale,
+               int round_operands, double* dq, double* dk, double* dv, double* dwq, double* dwk) {
+  return oracle_bwd_ex(q, k, v, seg, wq, wk, NULL, NULL, dout, T, H, eps, scale, round_operands, dq, dk, dv, dwq,
+                       dwk);
+}
+
 /* Forward with the operand rounding optional (round_operands == 0: exact FP64 norm outputs), for the
- * finite-difference checks of the backward. */
+ * finite-difference checks of the backward and the "pure" reference of the parity report. */
 int oracle_fwd_opt(const uint16_t* q, const uint16_t* k, const uint16_t* v, const int32_t* seg, const uint16_t* wq,
                    const uint16_t* wk, int64_t T, int32_t H, double eps, double scale, int round_operands,
                    double* out) {
-  if (round_operands) return fwd_impl(q, k, v, seg, wq, wk, T, H, eps, scale, NULL, 0, out, NULL);
-  if (T < 0 || H < 1 || (wq == NULL) != (wk == NULL)) return ORACLE_ERR_ARGS;
-  if (T == 0) return ORACLE_OK;
-  int64_t* starts = (int64_t*)malloc((size_t)T * sizeof(int64_t));
-  int64_t* lens = (int64_t*)malloc((size_t)T * sizeof(int64_t));
-  if (!starts || !lens) { free(starts); free(lens); return ORACLE_ERR_NOMEM; }
-  int64_t nseg = 0;
-  int rc = oracle_segments(seg, T, starts, lens, &nseg);
-  double* qh = bwd_operand(q, wq, T, H, eps, 0);
-  double* kh = bwd_operand(k, wk, T, H, eps, 0);
-  double* vd = bwd_operand(v, NULL, T, H, eps, 1);
-  int64_t maxlen = 0;
-  for (int64_t s = 0; s < nseg; s++) if (lens[s] > maxlen) maxlen = lens[s];
-  double* scores = (double*)malloc((size_t)(maxlen > 0 ? maxlen : 1) * sizeof(double));
-  if (rc == ORACLE_OK && (!qh || !kh || !vd || !scores)) rc = ORACLE_ERR_NOMEM;
-  if (rc == ORACLE_OK)
-    for (int64_t s = 0; s < nseg; s++)
-      for (int h = 0; h < H; h++)
-        for (int64_t i = starts[s]; i < starts[s] + lens[s]; i++) {
-          double lse_val;
-          attend_one(qh, kh, vd, T, h, i, starts[s], lens[s], scale, scores, out + (i * H + h) * HD, &lse_val);
-        }
-  free(scores); free(qh); free(kh); free(vd); free(starts); free(lens);
-  return rc;
+  return fwd_impl(q, k, v, seg, wq, wk, NULL, NULL, round_operands ? 1 : 0, T, H, eps, scale, NULL, 0, out, NULL);
 }

@@ -344,3 +344,29 @@ def test_tiny_golden_regression():
     out, lse = oracle.fwd(x["q"], x["k"], x["v"], x["seg"].numpy(), x["wq"], x["wk"], wl.eps, wl.scale)
     assert np.max(np.abs(lse - np.array(doc["lse"]))) < 1e-15
     assert np.max(np.abs(out[:, :, :8] - np.array(doc["out_first8"]))) < 1e-15
+
+
+@pytest.mark.parametrize("normed", [True, False])
+def test_fwd_opt_unrounded_matches_sdpa_on_fp64_rms_norm(normed):
+    """The "pure" forward (normed operands kept in FP64, not rounded to bf16) against torch's FP64
+    rms_norm followed by its FP64 scaled_dot_product_attention with a block-diagonal mask (both
+    library routines), on ragged segments; with round_operands it is the node-faithful forward."""
+    lens = [1, 2, 63, 97, 130, 5, 64]
+    x = workloads.random_inputs(lens, 3, seed=41, normed=normed, w_scale=2.0)
+    seg = x["seg"].numpy()
+    scale = D ** -0.5
+    got = oracle.fwd_opt(x["q"], x["k"], x["v"], seg, x["wq"], x["wk"], 1e-6, scale, round_operands=False)
+    if normed:
+        qh = torch.nn.functional.rms_norm(x["q"].double(), (D,), x["wq"].double(), eps=1e-6).numpy()
+        kh = torch.nn.functional.rms_norm(x["k"].double(), (D,), x["wk"].double(), eps=1e-6).numpy()
+    else:
+        qh, kh = x["q"].double().numpy(), x["k"].double().numpy()
+    ref = _sdpa_fp64(qh, kh, x["v"].double().numpy(), seg, scale)
+    assert np.max(np.abs(got - ref)) < 1e-12
+    rounded = oracle.fwd_opt(x["q"], x["k"], x["v"], seg, x["wq"], x["wk"], 1e-6, scale, round_operands=True)
+    full, _ = oracle.fwd(x["q"], x["k"], x["v"], seg, x["wq"], x["wk"], 1e-6, scale)
+    assert np.array_equal(rounded, full)
+    if normed:  # the two differ by the operands' rounding: the unrounded form is not a copy of fwd
+        assert np.max(np.abs(got - full)) > 1e-6
+    else:
+        assert np.array_equal(got, full)
