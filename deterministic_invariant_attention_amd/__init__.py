@@ -81,9 +81,20 @@ def _ptr(t):
     return None if t is None else t.data_ptr()
 
 
-def _stream(stream, device):
+def _as_stream(stream, device):
+    """The torch stream object for a stream argument: None = torch's current stream on the device; a
+    torch.cuda.Stream as given; a raw hipStream_t handle (int) wrapped as an external stream."""
     if stream is None:
-        stream = torch.cuda.current_stream(device)
+        return torch.cuda.current_stream(device)
+    if isinstance(stream, torch.cuda.Stream):
+        return stream
+    return torch.cuda.ExternalStream(int(stream), device=device)
+
+
+def _stream(stream, device):
+    """The hipStream_t handle for a stream argument (see _as_stream)."""
+    if stream is None:
+        return torch.cuda.current_stream(device).cuda_stream
     return stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream)
 
 
@@ -93,7 +104,7 @@ def _check(rc: int, where: str):
 
 
 def _shape(q):
-    if q.dim() != 3:
+    if not isinstance(q, torch.Tensor) or q.dim() != 3:
         raise H3AttnError(H3ATTN_ERR_SHAPE, "expected [tokens, heads, head_dim]")
     return q.shape[0], q.shape[1], q.shape[2]
 
@@ -102,6 +113,66 @@ def _bf16(t, name):
     if t is not None and (t.dtype != torch.bfloat16 or not t.is_contiguous()):
         raise TypeError(f"{name} must be a contiguous bfloat16 tensor")
     return t
+
+
+class _Args:
+    """Checks every tensor argument of one call against the shapes the C ABI assumes, before the
+    library sees a pointer: a tensor of the wrong shape or on another device would hand the kernels
+    an undersized buffer or a host address.  Strict mode ("33B forward/backward" page, Scope):
+    wrong shapes, dtypes and devices raise; nothing falls back."""
+
+    def __init__(self, where, q):
+        self.where = where
+        T, H, D = _shape(q)
+        self.T, self.H, self.D = T, H, D
+        self.tensors = []
+        self.want(q, "q", torch.bfloat16, (T, H, D))
+
+    def want(self, t, name, dtype, shape):
+        if t is None:
+            return None
+        if not isinstance(t, torch.Tensor):
+            raise TypeError(f"{self.where}: {name} must be a torch tensor")
+        if t.dtype != dtype or not t.is_contiguous():
+            raise TypeError(f"{self.where}: {name} must be a contiguous {dtype} tensor")
+        if tuple(t.shape) != tuple(shape):
+            raise H3AttnError(H3ATTN_ERR_SHAPE, f"{self.where}: {name} has shape {tuple(t.shape)}, expected "
+                                                f"{tuple(shape)}")
+        self.tensors.append((name, t))
+        return t
+
+    def device(self):
+        """Every tensor on q's device, and that device a GPU (else ERR_DEVICE); returns it."""
+        dev = self.tensors[0][1].device
+        if dev.type != "cuda":
+            raise H3AttnError(H3ATTN_ERR_DEVICE, f"{self.where}: q is on {dev}, not a GPU")
+        for name, t in self.tensors:
+            if t.device != dev:
+                raise H3AttnError(H3ATTN_ERR_DEVICE, f"{self.where}: {name} is on {t.device}, q on {dev}")
+        return dev
+
+
+def _tok(a, t, name):
+    """An int32 [T] per-token tensor (segment or position ids)."""
+    return a.want(t, name, torch.int32, (a.T,))
+
+
+def _ws(a, t, need, name="workspace_buf"):
+    if t is None:
+        return None
+    if not isinstance(t, torch.Tensor) or t.dim() != 1 or not t.is_contiguous() or t.element_size() != 1:
+        raise TypeError(f"{a.where}: {name} must be a contiguous 1-D byte tensor")
+    if t.numel() < need:
+        raise H3AttnError(H3ATTN_ERR_WORKSPACE, f"{a.where}: {name} holds {t.numel()} bytes, needs {need}")
+    a.tensors.append((name, t))
+    return t
+
+
+def _status_or_raise(ws, stream, where):
+    """Read the device status word (synchronises the stream) and raise on a recorded data error."""
+    st = h3attn_status_read(ws, stream)
+    if st != H3ATTN_OK:
+        raise H3AttnError(st, where + " (device status)")
 
 
 def h3attn_version() -> int:
@@ -124,103 +195,150 @@ def workspace(tokens: int, heads: int, device) -> torch.Tensor:
 
 def h3attn_qknorm(x, w, eps: float = 1e-6, out=None, stream=None):
     """RMSNorm of every 128-wide (token, head) row of x [T, H, 128] with weight w [128]; returns y."""
-    _bf16(x, "x"), _bf16(w, "w")
-    T, H, D = _shape(x)
-    y = torch.empty_like(x) if out is None else _bf16(out, "out")
-    rc = load().h3attn_qknorm(_ptr(x), _ptr(w), _ptr(y), T, H, D, float(eps), _stream(stream, x.device))
+    a = _Args("h3attn_qknorm", x)
+    a.want(w, "w", torch.bfloat16, (a.D,))
+    a.want(out, "out", torch.bfloat16, (a.T, a.H, a.D))
+    dev = a.device()
+    st = _as_stream(stream, dev)
+    with torch.cuda.device(dev), torch.cuda.stream(st):
+        y = torch.empty_like(x) if out is None else out
+        rc = load().h3attn_qknorm(_ptr(x), _ptr(w), _ptr(y), a.T, a.H, a.D, float(eps), st.cuda_stream)
     _check(rc, "h3attn_qknorm")
     return y
 
 
 def _int32(t, name):
-    if t.dtype != torch.int32 or not t.is_contiguous():
+    if not isinstance(t, torch.Tensor) or t.dtype != torch.int32 or not t.is_contiguous():
         raise TypeError(f"{name} must be a contiguous int32 tensor")
     return t
 
 
 def h3attn_fwd(q, k, v, seg_ids, wq=None, wk=None, eps: float = 1e-6, scale: float | None = None, out=None,
-               lse=None, workspace_buf=None, stream=None, want_lse: bool = False):
-    """Forward of the attention node with its fused q/k norm.  Returns (out, lse) (lse None unless asked)."""
-    return _fwd(q, k, v, seg_ids, None, wq, wk, eps, scale, out, lse, workspace_buf, stream, want_lse)
+               lse=None, workspace_buf=None, stream=None, want_lse: bool = False, check_status: bool = False):
+    """Forward of the attention node with its fused q/k norm.  Returns (out, lse) (lse None unless asked).
+    check_status: read the device status word after the call (synchronises the stream) and raise on
+    a recorded data error (decreasing segment ids, a value beyond the fp16 range)."""
+    return _fwd(q, k, v, seg_ids, None, wq, wk, eps, scale, out, lse, workspace_buf, stream, want_lse,
+                check_status=check_status)
 
 
 def h3attn_fwd_pos(q, k, v, seg_ids, pos_ids, wq=None, wk=None, eps: float = 1e-6, scale: float | None = None,
-                   out=None, lse=None, workspace_buf=None, stream=None, want_lse: bool = False):
+                   out=None, lse=None, workspace_buf=None, stream=None, want_lse: bool = False,
+                   check_status: bool = False):
     """h3attn_fwd with each segment's keys walked in the order of pos_ids (int32 [T], a permutation of
     0..L-1 within each segment).  Returns (out, lse)."""
     return _fwd(q, k, v, seg_ids, _int32(pos_ids, "pos_ids"), wq, wk, eps, scale, out, lse, workspace_buf, stream,
-                want_lse)
+                want_lse, check_status=check_status)
 
 
 def h3attn_fwd_ex(q, k, v, seg_ids, pos_ids=None, wq=None, wk=None, eps: float = 1e-6, scale: float | None = None,
                   out=None, lse=None, o32=None, workspace_buf=None, stream=None, want_lse: bool = False,
-                  want_o32: bool = False):
+                  want_o32: bool = False, check_status: bool = False):
     """The forward with every option: position order when pos_ids is given, and the fp32 output
     before its bf16 rounding (o32, for h3attn_bwd_ex) when asked.  Returns (out, lse, o32)."""
-    T = q.shape[0]
-    if o32 is None and want_o32:
-        o32 = torch.empty(q.shape, dtype=torch.float32, device=q.device)
-    if o32 is not None and (o32.dtype != torch.float32 or not o32.is_contiguous()):
-        raise TypeError("o32 must be a contiguous float32 tensor")
-    out, lse = _fwd(q, k, v, seg_ids, None if pos_ids is None else _int32(pos_ids, "pos_ids"), wq, wk, eps, scale,
-                    out, lse, workspace_buf, stream, want_lse, o32=o32, ex=True)
-    return out, lse, o32
+    return _fwd(q, k, v, seg_ids, None if pos_ids is None else _int32(pos_ids, "pos_ids"), wq, wk, eps, scale,
+                out, lse, workspace_buf, stream, want_lse, o32=o32, want_o32=want_o32, ex=True,
+                check_status=check_status)
 
 
 def _fwd(q, k, v, seg_ids, pos_ids, wq, wk, eps, scale, out, lse, workspace_buf, stream, want_lse, o32=None,
-         ex=False):
-    for t, n in ((q, "q"), (k, "k"), (v, "v"), (wq, "wq"), (wk, "wk")):
-        _bf16(t, n)
-    _int32(seg_ids, "seg_ids")
-    T, H, D = _shape(q)
+         want_o32=False, ex=False, check_status=False):
+    a = _Args("h3attn_fwd", q)
+    T, H, D = a.T, a.H, a.D
+    for t, n in ((k, "k"), (v, "v")):
+        if t is None:
+            raise H3AttnError(H3ATTN_ERR_NULL, f"h3attn_fwd: {n} is required")
+        a.want(t, n, torch.bfloat16, (T, H, D))
+    _tok(a, _int32(seg_ids, "seg_ids"), "seg_ids")
+    _tok(a, pos_ids, "pos_ids")
+    a.want(wq, "wq", torch.bfloat16, (D,))
+    a.want(wk, "wk", torch.bfloat16, (D,))
+    a.want(out, "out", torch.bfloat16, (T, H, D))
+    a.want(lse, "lse", torch.float32, (T, H))
+    a.want(o32, "o32", torch.float32, (T, H, D))
+    _ws(a, workspace_buf, h3attn_workspace_bytes(T, H))
+    dev = a.device()
     scale = D ** -0.5 if scale is None else scale
-    out = torch.empty_like(q) if out is None else _bf16(out, "out")
-    if lse is None and want_lse:
-        lse = torch.empty((T, H), dtype=torch.float32, device=q.device)
-    ws = workspace(T, H, q.device) if workspace_buf is None else workspace_buf
-    st = _stream(stream, q.device)
-    if ex:
-        rc = load().h3attn_fwd_ex(_ptr(q), _ptr(k), _ptr(v), _ptr(seg_ids), _ptr(pos_ids), _ptr(wq), _ptr(wk), T, H,
-                                  D, float(eps), float(scale), _ptr(out), _ptr(lse), _ptr(o32), _ptr(ws), ws.numel(),
-                                  st)
-        _check(rc, "h3attn_fwd_ex")
-    elif pos_ids is None:
-        rc = load().h3attn_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(seg_ids), _ptr(wq), _ptr(wk), T, H, D, float(eps),
-                               float(scale), _ptr(out), _ptr(lse), _ptr(ws), ws.numel(), st)
-        _check(rc, "h3attn_fwd")
-    else:
-        rc = load().h3attn_fwd_pos(_ptr(q), _ptr(k), _ptr(v), _ptr(seg_ids), _ptr(pos_ids), _ptr(wq), _ptr(wk), T, H,
-                                   D, float(eps), float(scale), _ptr(out), _ptr(lse), _ptr(ws), ws.numel(), st)
-        _check(rc, "h3attn_fwd_pos")
-    return out, lse
+    st = _as_stream(stream, dev)
+    # outputs and the workspace are allocated on the launch stream, so the caching allocator never
+    # hands their memory to other work while the kernels still use it
+    with torch.cuda.device(dev), torch.cuda.stream(st):
+        out = torch.empty_like(q) if out is None else out
+        if lse is None and want_lse:
+            lse = torch.empty((T, H), dtype=torch.float32, device=dev)
+        if o32 is None and want_o32:
+            o32 = torch.empty((T, H, D), dtype=torch.float32, device=dev)
+        ws = workspace(T, H, dev) if workspace_buf is None else workspace_buf
+        h = st.cuda_stream
+        if ex:
+            rc = load().h3attn_fwd_ex(_ptr(q), _ptr(k), _ptr(v), _ptr(seg_ids), _ptr(pos_ids), _ptr(wq), _ptr(wk), T,
+                                      H, D, float(eps), float(scale), _ptr(out), _ptr(lse), _ptr(o32), _ptr(ws),
+                                      ws.numel(), h)
+            _check(rc, "h3attn_fwd_ex")
+        elif pos_ids is None:
+            rc = load().h3attn_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(seg_ids), _ptr(wq), _ptr(wk), T, H, D, float(eps),
+                                   float(scale), _ptr(out), _ptr(lse), _ptr(ws), ws.numel(), h)
+            _check(rc, "h3attn_fwd")
+        else:
+            rc = load().h3attn_fwd_pos(_ptr(q), _ptr(k), _ptr(v), _ptr(seg_ids), _ptr(pos_ids), _ptr(wq), _ptr(wk),
+                                       T, H, D, float(eps), float(scale), _ptr(out), _ptr(lse), _ptr(ws), ws.numel(),
+                                       h)
+            _check(rc, "h3attn_fwd_pos")
+        if check_status and T > 0:
+            _status_or_raise(ws, st, "h3attn_fwd")
+    return (out, lse, o32) if ex else (out, lse)
 
 
 def h3attn_plan(seg_ids, heads: int, workspace_buf, stream=None):
-    T = seg_ids.shape[0]
-    rc = load().h3attn_plan(_ptr(seg_ids), T, int(heads), _ptr(workspace_buf), workspace_buf.numel(),
-                            _stream(stream, seg_ids.device))
+    _int32(seg_ids, "seg_ids")
+    if seg_ids.dim() != 1:
+        raise H3AttnError(H3ATTN_ERR_SHAPE, "h3attn_plan: seg_ids must be int32 [T]")
+    T, H = seg_ids.shape[0], int(heads)
+    if not isinstance(workspace_buf, torch.Tensor) or workspace_buf.numel() < h3attn_workspace_bytes(T, H):
+        raise H3AttnError(H3ATTN_ERR_WORKSPACE, "h3attn_plan: workspace_buf is too small")
+    dev = seg_ids.device
+    if dev.type != "cuda" or workspace_buf.device != dev:
+        raise H3AttnError(H3ATTN_ERR_DEVICE, "h3attn_plan: seg_ids and the workspace must be on one GPU")
+    with torch.cuda.device(dev):
+        rc = load().h3attn_plan(_ptr(seg_ids), T, H, _ptr(workspace_buf), workspace_buf.numel(), _stream(stream, dev))
     _check(rc, "h3attn_plan")
 
 
 def h3attn_prep_qkv(q, k, v, wq, wk, workspace_buf, eps: float = 1e-6, stream=None):
-    T, H, D = _shape(k)
-    rc = load().h3attn_prep_qkv(_ptr(q), _ptr(k), _ptr(v), _ptr(wq), _ptr(wk), T, H, D, float(eps),
-                                _ptr(workspace_buf), workspace_buf.numel(), _stream(stream, k.device))
+    a = _Args("h3attn_prep_qkv", q)
+    a.want(k, "k", torch.bfloat16, (a.T, a.H, a.D))
+    a.want(v, "v", torch.bfloat16, (a.T, a.H, a.D))
+    a.want(wq, "wq", torch.bfloat16, (a.D,))
+    a.want(wk, "wk", torch.bfloat16, (a.D,))
+    _ws(a, workspace_buf, h3attn_workspace_bytes(a.T, a.H))
+    dev = a.device()
+    with torch.cuda.device(dev):
+        rc = load().h3attn_prep_qkv(_ptr(q), _ptr(k), _ptr(v), _ptr(wq), _ptr(wk), a.T, a.H, a.D, float(eps),
+                                    _ptr(workspace_buf), workspace_buf.numel(), _stream(stream, dev))
     _check(rc, "h3attn_prep_qkv")
 
 
 def h3attn_attend(q, wq, workspace_buf, out, lse=None, eps: float = 1e-6, scale: float | None = None, stream=None):
-    T, H, D = _shape(q)
-    scale = D ** -0.5 if scale is None else scale
-    rc = load().h3attn_attend(_ptr(q), _ptr(wq), T, H, D, float(eps), float(scale), _ptr(out), _ptr(lse),
-                              _ptr(workspace_buf), workspace_buf.numel(), _stream(stream, q.device))
+    a = _Args("h3attn_attend", q)
+    a.want(wq, "wq", torch.bfloat16, (a.D,))
+    a.want(out, "out", torch.bfloat16, (a.T, a.H, a.D))
+    a.want(lse, "lse", torch.float32, (a.T, a.H))
+    _ws(a, workspace_buf, h3attn_workspace_bytes(a.T, a.H))
+    dev = a.device()
+    scale = a.D ** -0.5 if scale is None else scale
+    with torch.cuda.device(dev):
+        rc = load().h3attn_attend(_ptr(q), _ptr(wq), a.T, a.H, a.D, float(eps), float(scale), _ptr(out), _ptr(lse),
+                                  _ptr(workspace_buf), workspace_buf.numel(), _stream(stream, dev))
     _check(rc, "h3attn_attend")
     return out
 
 
 def h3attn_status_read(workspace_buf, stream=None) -> int:
+    if not isinstance(workspace_buf, torch.Tensor) or workspace_buf.device.type != "cuda":
+        raise H3AttnError(H3ATTN_ERR_DEVICE, "h3attn_status_read: the workspace is not on a GPU")
     st = ctypes.c_int32(-1)
-    rc = load().h3attn_status_read(_ptr(workspace_buf), ctypes.byref(st), _stream(stream, workspace_buf.device))
+    with torch.cuda.device(workspace_buf.device):
+        rc = load().h3attn_status_read(_ptr(workspace_buf), ctypes.byref(st), _stream(stream, workspace_buf.device))
     _check(rc, "h3attn_status_read")
     return st.value
 
@@ -236,61 +354,79 @@ def bwd_workspace(tokens: int, heads: int, device) -> torch.Tensor:
 
 
 def h3attn_bwd(dout, q, k, v, lse, seg_ids, wq=None, wk=None, eps: float = 1e-6, scale: float | None = None,
-               dq=None, dk=None, dv=None, dwq=None, dwk=None, workspace_buf=None, stream=None):
+               dq=None, dk=None, dv=None, dwq=None, dwk=None, workspace_buf=None, stream=None,
+               check_status: bool = False):
     """Backward of the node: returns (dq, dk, dv, dwq, dwk) (dwq/dwk None without norm weights).
     lse is the forward's fp32 [T, H] log-sum-exp (h3attn_fwd(..., want_lse=True))."""
-    return _bwd(dout, q, k, v, lse, seg_ids, None, wq, wk, eps, scale, dq, dk, dv, dwq, dwk, workspace_buf, stream)
+    return _bwd(dout, q, k, v, lse, seg_ids, None, wq, wk, eps, scale, dq, dk, dv, dwq, dwk, workspace_buf, stream,
+                check_status=check_status)
 
 
 def h3attn_bwd_pos(dout, q, k, v, lse, seg_ids, pos_ids, wq=None, wk=None, eps: float = 1e-6,
                    scale: float | None = None, dq=None, dk=None, dv=None, dwq=None, dwk=None, workspace_buf=None,
-                   stream=None):
+                   stream=None, check_status: bool = False):
     """h3attn_bwd with every sum taken in the order of pos_ids (as for h3attn_fwd_pos)."""
     return _bwd(dout, q, k, v, lse, seg_ids, _int32(pos_ids, "pos_ids"), wq, wk, eps, scale, dq, dk, dv, dwq, dwk,
-                workspace_buf, stream)
+                workspace_buf, stream, check_status=check_status)
 
 
 def h3attn_bwd_ex(dout, q, k, v, lse, seg_ids, pos_ids=None, o32=None, wq=None, wk=None, eps: float = 1e-6,
                   scale: float | None = None, dq=None, dk=None, dv=None, dwq=None, dwk=None, workspace_buf=None,
-                  stream=None):
+                  stream=None, check_status: bool = False):
     """The backward with every option: position order when pos_ids is given; D = dO . O from the
     forward's o32 (h3attn_fwd_ex) when given, else recomputed.  Returns (dq, dk, dv, dwq, dwk)."""
-    if o32 is not None and (o32.dtype != torch.float32 or not o32.is_contiguous()):
-        raise TypeError("o32 must be a contiguous float32 tensor")
     return _bwd(dout, q, k, v, lse, seg_ids, None if pos_ids is None else _int32(pos_ids, "pos_ids"), wq, wk, eps,
-                scale, dq, dk, dv, dwq, dwk, workspace_buf, stream, o32=o32, ex=True)
+                scale, dq, dk, dv, dwq, dwk, workspace_buf, stream, o32=o32, ex=True, check_status=check_status)
 
 
 def _bwd(dout, q, k, v, lse, seg_ids, pos_ids, wq, wk, eps, scale, dq, dk, dv, dwq, dwk, workspace_buf, stream,
-         o32=None, ex=False):
-    for t, n in ((dout, "dout"), (q, "q"), (k, "k"), (v, "v"), (wq, "wq"), (wk, "wk")):
-        _bf16(t, n)
-    _int32(seg_ids, "seg_ids")
-    if lse.dtype != torch.float32 or not lse.is_contiguous():
-        raise TypeError("lse must be a contiguous float32 tensor")
-    T, H, D = _shape(q)
+         o32=None, ex=False, check_status=False):
+    a = _Args("h3attn_bwd", q)
+    T, H, D = a.T, a.H, a.D
+    for t, n in ((dout, "dout"), (k, "k"), (v, "v")):
+        if t is None:
+            raise H3AttnError(H3ATTN_ERR_NULL, f"h3attn_bwd: {n} is required")
+        a.want(t, n, torch.bfloat16, (T, H, D))
+    if lse is None:
+        raise H3AttnError(H3ATTN_ERR_NULL, "h3attn_bwd: lse is required")
+    a.want(lse, "lse", torch.float32, (T, H))
+    _tok(a, _int32(seg_ids, "seg_ids"), "seg_ids")
+    _tok(a, pos_ids, "pos_ids")
+    a.want(o32, "o32", torch.float32, (T, H, D))
+    a.want(wq, "wq", torch.bfloat16, (D,))
+    a.want(wk, "wk", torch.bfloat16, (D,))
+    for t, n in ((dq, "dq"), (dk, "dk"), (dv, "dv")):
+        a.want(t, n, torch.bfloat16, (T, H, D))
+    a.want(dwq, "dwq", torch.float32, (D,))
+    a.want(dwk, "dwk", torch.float32, (D,))
+    _ws(a, workspace_buf, h3attn_bwd_workspace_bytes(T, H))
+    dev = a.device()
     scale = D ** -0.5 if scale is None else scale
-    dq = torch.empty_like(q) if dq is None else _bf16(dq, "dq")
-    dk = torch.empty_like(q) if dk is None else _bf16(dk, "dk")
-    dv = torch.empty_like(q) if dv is None else _bf16(dv, "dv")
-    if wq is not None:
-        dwq = torch.empty(D, dtype=torch.float32, device=q.device) if dwq is None else dwq
-        dwk = torch.empty(D, dtype=torch.float32, device=q.device) if dwk is None else dwk
-    ws = bwd_workspace(T, H, q.device) if workspace_buf is None else workspace_buf
-    st = _stream(stream, q.device)
-    if ex:
-        rc = load().h3attn_bwd_ex(_ptr(dout), _ptr(q), _ptr(k), _ptr(v), _ptr(lse), _ptr(o32), _ptr(seg_ids),
-                                  _ptr(pos_ids), _ptr(wq), _ptr(wk), T, H, D, float(eps), float(scale), _ptr(dq),
-                                  _ptr(dk), _ptr(dv), _ptr(dwq), _ptr(dwk), _ptr(ws), ws.numel(), st)
-        _check(rc, "h3attn_bwd_ex")
-    elif pos_ids is None:
-        rc = load().h3attn_bwd(_ptr(dout), _ptr(q), _ptr(k), _ptr(v), _ptr(lse), _ptr(seg_ids), _ptr(wq), _ptr(wk),
-                               T, H, D, float(eps), float(scale), _ptr(dq), _ptr(dk), _ptr(dv), _ptr(dwq), _ptr(dwk),
-                               _ptr(ws), ws.numel(), st)
-        _check(rc, "h3attn_bwd")
-    else:
-        rc = load().h3attn_bwd_pos(_ptr(dout), _ptr(q), _ptr(k), _ptr(v), _ptr(lse), _ptr(seg_ids), _ptr(pos_ids),
-                                   _ptr(wq), _ptr(wk), T, H, D, float(eps), float(scale), _ptr(dq), _ptr(dk),
-                                   _ptr(dv), _ptr(dwq), _ptr(dwk), _ptr(ws), ws.numel(), st)
-        _check(rc, "h3attn_bwd_pos")
+    st = _as_stream(stream, dev)
+    with torch.cuda.device(dev), torch.cuda.stream(st):
+        dq = torch.empty_like(q) if dq is None else dq
+        dk = torch.empty_like(q) if dk is None else dk
+        dv = torch.empty_like(q) if dv is None else dv
+        if wq is not None:
+            dwq = torch.empty(D, dtype=torch.float32, device=dev) if dwq is None else dwq
+            dwk = torch.empty(D, dtype=torch.float32, device=dev) if dwk is None else dwk
+        ws = bwd_workspace(T, H, dev) if workspace_buf is None else workspace_buf
+        h = st.cuda_stream
+        if ex:
+            rc = load().h3attn_bwd_ex(_ptr(dout), _ptr(q), _ptr(k), _ptr(v), _ptr(lse), _ptr(o32), _ptr(seg_ids),
+                                      _ptr(pos_ids), _ptr(wq), _ptr(wk), T, H, D, float(eps), float(scale), _ptr(dq),
+                                      _ptr(dk), _ptr(dv), _ptr(dwq), _ptr(dwk), _ptr(ws), ws.numel(), h)
+            _check(rc, "h3attn_bwd_ex")
+        elif pos_ids is None:
+            rc = load().h3attn_bwd(_ptr(dout), _ptr(q), _ptr(k), _ptr(v), _ptr(lse), _ptr(seg_ids), _ptr(wq),
+                                   _ptr(wk), T, H, D, float(eps), float(scale), _ptr(dq), _ptr(dk), _ptr(dv),
+                                   _ptr(dwq), _ptr(dwk), _ptr(ws), ws.numel(), h)
+            _check(rc, "h3attn_bwd")
+        else:
+            rc = load().h3attn_bwd_pos(_ptr(dout), _ptr(q), _ptr(k), _ptr(v), _ptr(lse), _ptr(seg_ids),
+                                       _ptr(pos_ids), _ptr(wq), _ptr(wk), T, H, D, float(eps), float(scale),
+                                       _ptr(dq), _ptr(dk), _ptr(dv), _ptr(dwq), _ptr(dwk), _ptr(ws), ws.numel(), h)
+            _check(rc, "h3attn_bwd_pos")
+        if check_status and T > 0:
+            _status_or_raise(ws, st, "h3attn_bwd")
     return dq, dk, dv, dwq, dwk
