@@ -22,8 +22,13 @@ constexpr int NBKT = 32;  // cost classes of the backward work order (floor(log2
 // delta             fp32 [H][T]: -D_i, D_i = sum_j P_ij dP_ij (the dq kernel's dP products start from it)
 // dqh, dkh          fp32 [T][H][128]: dq^, dk^ (gradients of the normed operands)
 // dw_part, dw_chunk fp32: 16-row weight-gradient partials and their first-level chunk sums
+// tok2seg           int32 [T]: the segment (index into segtab) of every token
+// segflag           int32 [T]: per segment, nonzero when it cannot be computed (see the forward's)
+// dmax              uint32 [T][H]: per (segment, head), the largest |dO| as bf16 magnitude bits
+//                   (slots [0, nseg*H) are used; reset by the plan kernel)
 struct BwdLayout {
-  size_t segtab, items, bkt, qhat16, khat16, v16, do16, lse2, delta, dqh, dkh, dw_part, dw_chunk, total;
+  size_t segtab, items, bkt, qhat16, khat16, v16, do16, lse2, delta, dqh, dkh, dw_part, dw_chunk, tok2seg, segflag,
+      dmax, total;
   int64_t max_items, nparts, nchunks;
 };
 
@@ -48,8 +53,31 @@ __host__ __device__ inline BwdLayout bwd_layout(int64_t T, int32_t H) {
   w.dkh = w.dqh + tens32;
   w.dw_part = w.dkh + tens32;
   w.dw_chunk = w.dw_part + align256((size_t)2 * w.nparts * HD * 4);
-  w.total = w.dw_chunk + align256((size_t)2 * w.nchunks * HD * 4);
+  w.tok2seg = w.dw_chunk + align256((size_t)2 * w.nchunks * HD * 4);
+  w.segflag = w.tok2seg + align256((size_t)T * 4);
+  w.dmax = w.segflag + align256((size_t)T * 4);
+  w.total = w.dmax + align256((size_t)T * H * 4);
   return w;
+}
+
+// The power of two that scales dO before it enters the fp16 products of the backward.  fp16 keeps
+// bf16's 8 significant bits only from 2^-14 (2^-17 with its subnormals) up to 65504, while dO may
+// lie anywhere in bf16's range; so every (segment, head) is scaled by 2^s chosen from its own
+// largest |dO| (m, bf16 magnitude bits) to bring that maximum into [4, 8) -- the range of N(0, 1)
+// draws, which gets s = 0.  Every gradient is linear in dO, so the epilogues remove the factor
+// exactly (ldexp by -s).  m = 0, infinity or NaN: s = 0 (infinities and NaN propagate unscaled).
+__host__ __device__ inline int dout_scale_exp(uint32_t m) {
+  if (m == 0 || m >= 0x7F80u) return 0;
+  const int e = (int)(m >> 7);
+  int fl;  // floor(log2(m's value))
+  if (e > 0) {
+    fl = e - 127;
+  } else {  // subnormal: value = mantissa * 2^-133
+    int top = 6;
+    while (!((m >> top) & 1u)) top--;
+    fl = top - 133;
+  }
+  return 2 - fl;
 }
 
 }  // namespace h3

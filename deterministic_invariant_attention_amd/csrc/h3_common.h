@@ -19,6 +19,10 @@ constexpr int BK = 96;   // keys per KV tile; the KV walk is in these tiles, asc
 // khat                bf16 [H][T][128]: normed K (head-major, so a KV tile is contiguous)
 // v16                 fp16 [H][T][128]: V converted to fp16 (head-major)
 // qhat                bf16 [H][T][128]: normed Q (head-major, packed token order), with norm weights
+// tok2seg             int32 [T]: the segment (index into segtab) of every token
+// segflag             int32 [T]: per segment, nonzero when one of its values cannot enter the
+//                     products (a finite |v| beyond fp16) or its position ids are not a permutation;
+//                     that segment's outputs are NaN, the others are computed as usual
 struct WsHeader {
   int32_t status;  // OR of STATUS_* bits; reset by the plan kernel
   int32_t nseg;
@@ -29,11 +33,11 @@ struct WsHeader {
 };
 static_assert(sizeof(WsHeader) == 256, "header is 256 bytes");
 
-constexpr int32_t STATUS_SEG_BIT = 1;    // segment ids decrease
-constexpr int32_t STATUS_RANGE_BIT = 2;  // a finite |v| exceeds the fp16 range
+constexpr int32_t STATUS_SEG_BIT = 1;    // segment ids decrease (no segmentation exists: every output is NaN)
+constexpr int32_t STATUS_RANGE_BIT = 2;  // a finite |v| exceeds the fp16 range (in the flagged segments)
 
 struct WsLayout {
-  size_t segtab, items, khat, v16, qhat, total;
+  size_t segtab, items, khat, v16, qhat, tok2seg, segflag, total;
   int64_t max_items;
 };
 
@@ -47,8 +51,15 @@ __host__ __device__ inline WsLayout ws_layout(int64_t T, int32_t H) {
   w.khat = w.items + align256((size_t)w.max_items * 8);
   w.v16 = w.khat + align256((size_t)T * H * HD * 2);
   w.qhat = w.v16 + align256((size_t)T * H * HD * 2);
-  w.total = w.qhat + align256((size_t)T * H * HD * 2);
+  w.tok2seg = w.qhat + align256((size_t)T * H * HD * 2);
+  w.segflag = w.tok2seg + align256((size_t)T * 4);
+  w.total = w.segflag + align256((size_t)T * 4);
   return w;
+}
+
+// Mark segment sg as unusable (per-segment fail-closed; the caller also sets the status bit).
+__device__ __forceinline__ void flag_segment(int32_t* segflag, int32_t sg, int32_t nseg) {
+  if (sg >= 0 && sg < nseg) atomicOr(&segflag[sg], 1);
 }
 
 // ---------------------------------------------------------------- vector types

@@ -19,10 +19,10 @@ hipError_t launch_qknorm(const void* x, const void* w, void* y, int64_t T, int32
 hipError_t launch_prep_qkv(const void* q, const void* k, const void* v, const void* wq, const void* wk, int64_t T,
                            int32_t H, float eps, void* ws, const int32_t* slot, hipStream_t stream);
 
-// Position ids -> slot / inv maps of the ordering area, with the permutation check (STATUS_POS_BIT).
-// Needs the plan's segment table.
-hipError_t launch_order(const int32_t* pos, int64_t T, void* ws, const int32_t* segtab, int32_t* slot, int32_t* inv,
-                        hipStream_t stream);
+// Position ids -> slot / inv maps of the ordering area, with the permutation check (STATUS_POS_BIT,
+// and the failing segments flagged in segflag).  Needs the plan's segment table and token map.
+hipError_t launch_order(const int32_t* pos, int64_t T, void* ws, const int32_t* segtab, const int32_t* tok2seg,
+                        int32_t* segflag, int32_t* slot, int32_t* inv, hipStream_t stream);
 
 // Attention over the planned work items.  Queries: the staged normed Q when normed is true, else
 // the caller's q (token-major).  lse and o32 (the output before its bf16 rounding, fp32) are

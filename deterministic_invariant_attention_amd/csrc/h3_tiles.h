@@ -1,4 +1,4 @@
-// LDS tile machinery shared by the attention kernels: 64-row tiles of 128 16-bit columns copied
+// LDS tile machinery shared by the attention kernels: tiles of 128 16-bit columns copied
 // from head-major global arrays into XOR-swizzled LDS with buffer_load ... lds, the two read
 // patterns (16-byte row reads, transposed 8-byte reads), half-wave exchanges and fixed sum trees.
 #pragma once
@@ -111,51 +111,6 @@ __device__ __forceinline__ u32x2 tr_read_asm(uint32_t base) {
 // that reads them can be scheduled before it.
 #define LGKM_WAIT_TIED(N, x, y) asm volatile("s_waitcnt lgkmcnt(" #N ")" : "+v"(x), "+v"(y))
 
-// Products whose A operand is read transposed from a row-major LDS tile (rows = the contracted
-// index: keys for P.V, queries in the backward): ACC^T[dim][n] += X^T[dim][row] B[row][n] over the
-// tile's 64 rows, with B held as packed fp16 (bop[ks] = rows 16ks + {4hh..4hh+3, 8+4hh..8+4hh+3}).
-
-// A operand of step T = 4ks + db from LDS tile TILE (0..3): rows 16ks + {0..7} and 16ks + 8 + {0..7}.
-// vb[db] is the lane's LDS byte address of (row tr_row, column 32db + tr_col) in tile 0; the
-// swizzle of a row depends on row & 3 only, so the other rows and tiles are constant offsets.
-template <int TILE, int T>
-__device__ __forceinline__ void tr_read_step(const uint32_t* vb, u32x2 (&va)[16][2]) {
-  constexpr int ks = T >> 2, db = T & 3;
-  constexpr int off = TILE * TILE_ELEMS * 2 + 16 * ks * HD * 2;
-  va[T][0] = tr_read_asm<off>(vb[db]);
-  va[T][1] = tr_read_asm<off + 8 * HD * 2>(vb[db]);
-}
-
-// Step T = 4ks + db, so every ACC[db] sums its row slices in order.  Operands are read 4 steps
-// ahead; before step T's MFMA the reads of the steps after it (two each, at most 4 steps) may still
-// be in flight, and no other LDS operation is (the caller has consumed every earlier LDS read).
-template <int TILE, int T>
-__device__ __forceinline__ void tr_gemm_step(const uint32_t* vb, const f16x8* pf, f32x16* O, u32x2 (&va)[16][2]) {
-  if constexpr (T + 4 < 16) tr_read_step<TILE, T + 4>(vb, va);
-  constexpr int ahead = (T + 4 < 16 ? T + 4 : 15) - T;  // later steps already issued
-  if constexpr (ahead == 4) LGKM_WAIT_TIED(8, va[T][0], va[T][1]);
-  else if constexpr (ahead == 3) LGKM_WAIT_TIED(6, va[T][0], va[T][1]);
-  else if constexpr (ahead == 2) LGKM_WAIT_TIED(4, va[T][0], va[T][1]);
-  else if constexpr (ahead == 1) LGKM_WAIT_TIED(2, va[T][0], va[T][1]);
-  else LGKM_WAIT_TIED(0, va[T][0], va[T][1]);
-  const f16x4 lo = __builtin_bit_cast(f16x4, va[T][0]), hi = __builtin_bit_cast(f16x4, va[T][1]);
-  const f16x8 a = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
-  O[T & 3] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a, pf[T >> 2], O[T & 3], 0, 0, 0);
-  __builtin_amdgcn_sched_barrier(0);
-  if constexpr (T + 1 < 16) tr_gemm_step<TILE, T + 1>(vb, pf, O, va);
-}
-
-template <int TILE>
-__device__ __forceinline__ void tr_gemm(const uint32_t* vb, const f16x8* pf, f32x16* O) {
-  static_assert(TILE >= 0 && TILE <= 3, "the ds offset field reaches the first four tiles");
-  u32x2 va[16][2];
-  tr_read_step<TILE, 0>(vb, va);
-  tr_read_step<TILE, 1>(vb, va);
-  tr_read_step<TILE, 2>(vb, va);
-  tr_read_step<TILE, 3>(vb, va);
-  tr_gemm_step<TILE, 0>(vb, pf, O, va);
-}
-
 // Keys at or past `rem` (the valid keys of the segment's last tile) get -inf.  S[kb] holds keys
 // 32kb + 8(i/4) + 4hh + (i%4) of the lane's query.
 __device__ __forceinline__ void mask_tail(f32x16* S, int rem, int hh) {
@@ -164,36 +119,6 @@ __device__ __forceinline__ void mask_tail(f32x16* S, int rem, int hh) {
 #pragma unroll
     for (int i = 0; i < 16; i++)
       if (32 * kb + 8 * (i >> 2) + 4 * hh + (i & 3) >= rem) S[kb][i] = -__builtin_inff();
-}
-// The same with the lane's limit given as rel = rem - 4hh.
-__device__ __forceinline__ void mask_tail_rel(f32x16* S, int rel) {
-#pragma unroll
-  for (int kb = 0; kb < 2; kb++)
-#pragma unroll
-    for (int i = 0; i < 16; i++)
-      if (32 * kb + 8 * (i >> 2) + (i & 3) >= rel) S[kb][i] = -__builtin_inff();
-}
-
-// Products whose A operand is a 64-row LDS tile read by rows (16-byte reads, K swizzle) and whose B
-// operand is 32 rows held in registers: S[kb][i] = tile row 32kb + 8(i/4) + 4hh + (i%4) dotted with
-// the lane's register row (in the forward: the scores of one 64-key tile for the lane's query).
-// Each accumulator sums its k-slices m = 0..7 in order.
-template <int NPRE>
-__device__ __forceinline__ void gemm_scores(const uint16_t* Kb, const bf16x8* qf, int l32, int hh, f32x16* S) {
-  bf16x8 ka[16];
-  auto kread = [&](int s) { ka[s] = *(const bf16x8*)(Kb + k_off(32 * (s & 1) + l32, 16 * (s >> 1) + 8 * hh)); };
-#pragma unroll
-  for (int kb = 0; kb < 2; kb++)
-#pragma unroll
-    for (int i = 0; i < 16; i++) S[kb][i] = 0.0f;
-#pragma unroll
-  for (int s = 0; s < NPRE; s++) kread(s);
-#pragma unroll
-  for (int s = 0; s < 16; s++) {  // step s = 2m + kb
-    if (s + NPRE < 16) kread(s + NPRE);
-    S[s & 1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka[s], qf[s >> 1], S[s & 1], 0, 0, 0);
-    __builtin_amdgcn_sched_barrier(0);
-  }
 }
 
 }  // namespace h3

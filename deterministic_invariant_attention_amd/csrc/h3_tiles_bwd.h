@@ -87,7 +87,7 @@ __device__ __forceinline__ void tr_gemm_hooked(const uint32_t* vb, const f16x8* 
   trh_step<Tiles, NP, 0>(vb, bop, acc, va, hook);
 }
 
-// Row-read products (the gemm_scores shape) with assembly reads: S[kb] = sum over m of tile rows
+// Row-read products with assembly reads: S[kb] = sum over m of tile rows
 // 32kb + l32's 16-dim slice m times the B operand b[m] (bf16 or fp16, the tile holds the same
 // type), reads NPRE steps ahead, explicit waits, and hook(StepIdx<s>) after step s's MFMA (the hook
 // must not issue LDS reads).  The lane's read address for slice m is its slice-0 address XOR

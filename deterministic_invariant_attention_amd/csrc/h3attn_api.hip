@@ -247,9 +247,10 @@ static int fwd_impl(const void* q, const void* k, const void* v, const int32_t* 
   char* base = (char*)workspace;
   int32_t* slot = ordered ? (int32_t*)(base + ol.slot) : nullptr;
   if ((rc = launch_status(launch_plan(seg_ids, tokens, workspace, heads, st)))) return rc;
-  if (ordered &&
-      (rc = launch_status(launch_order(pos_ids, tokens, workspace, (const int32_t*)(base + ws_layout(tokens, heads).segtab),
-                                       slot, (int32_t*)(base + ol.inv), st))))
+  const WsLayout wl = ws_layout(tokens, heads);
+  if (ordered && (rc = launch_status(launch_order(pos_ids, tokens, workspace, (const int32_t*)(base + wl.segtab),
+                                                  (const int32_t*)(base + wl.tok2seg), (int32_t*)(base + wl.segflag),
+                                                  slot, (int32_t*)(base + ol.inv), st))))
     return rc;
   if ((rc = launch_status(launch_prep_qkv(q, k, v, wq, wk, tokens, heads, eps, workspace, slot, st)))) return rc;
   return launch_status(launch_attend(q, wq != nullptr, tokens, heads, scale, out, lse, o32, workspace, di.cus, st));
@@ -331,9 +332,10 @@ static int bwd_impl(const void* dout, const void* q, const void* k, const void* 
   int32_t* slot = ordered ? (int32_t*)(base + ol.slot) : nullptr;
   int32_t* inv = ordered ? (int32_t*)(base + ol.inv) : nullptr;
   if ((rc = launch_status(launch_plan_bwd(seg_ids, tokens, workspace, heads, st)))) return rc;
-  if (ordered &&
-      (rc = launch_status(launch_order(pos_ids, tokens, workspace,
-                                       (const int32_t*)(base + bwd_layout(tokens, heads).segtab), slot, inv, st))))
+  const BwdLayout bl = bwd_layout(tokens, heads);
+  if (ordered && (rc = launch_status(launch_order(pos_ids, tokens, workspace, (const int32_t*)(base + bl.segtab),
+                                                  (const int32_t*)(base + bl.tok2seg), (int32_t*)(base + bl.segflag),
+                                                  slot, inv, st))))
     return rc;
   if ((rc = launch_status(launch_bwd_prep(q, k, v, dout, lse, o32, wq, wk, tokens, heads, eps, workspace, slot, st))))
     return rc;

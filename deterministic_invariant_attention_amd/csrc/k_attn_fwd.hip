@@ -153,6 +153,7 @@ struct AttnParams {
   const WsHeader* hdr;
   const int32_t* segtab;
   const int32_t* items;
+  const int32_t* segflag;  // per segment: nonzero = a value cannot enter the products (NaN outputs)
   int64_t T;
   int32_t H;
   float c;            // scale * log2(e)
@@ -220,8 +221,8 @@ __global__ __launch_bounds__(64 * NWAVES, 1) void k_attn_fwd(AttnParams p) {
   const int64_t T = p.T;
   const int H = p.H;
 
-  if (p.hdr->status != 0) {
-    // A data error was recorded: make the result unmistakably invalid.
+  if (p.hdr->status & STATUS_SEG_BIT) {
+    // The segment ids decrease, so no segmentation exists: make the whole result unmistakably invalid.
     const int64_t n16 = T * H * HD / 8;
     const int64_t stride = (int64_t)gridDim.x * blockDim.x;
     const u32x4 nan4 = {0x7FC07FC0u, 0x7FC07FC0u, 0x7FC07FC0u, 0x7FC07FC0u};
@@ -273,6 +274,25 @@ __global__ __launch_bounds__(64 * NWAVES, 1) void k_attn_fwd(AttnParams p) {
     const int s0 = p.segtab[2 * seg];
     const int L = p.segtab[2 * seg + 1];
     if (s0 < 0 || L <= 0 || (int64_t)s0 + L > T || qt < 0 || qt * BQ >= L) continue;
+
+    if (p.segflag[seg] != 0) {
+      // This segment holds a value that cannot enter the products (or invalid position ids): its
+      // rows are NaN; every other segment is computed as usual.
+      const int qr = qt * BQ + wv * 32 + l32;
+      if (qr < L) {
+        const int64_t r = (int64_t)(s0 + qr) * H + head;
+        const u32x2 nan2 = {0x7FC07FC0u, 0x7FC07FC0u};
+#pragma unroll
+        for (int d = 0; d < HD / 2; d += 4) *(u32x2*)(p.out + r * HD + 2 * d + 4 * hh) = nan2;
+        if (p.lse && hh == 0) p.lse[r] = __builtin_nanf("");
+        if (p.o32) {
+          const f32x4 nanf4 = {__builtin_nanf(""), __builtin_nanf(""), __builtin_nanf(""), __builtin_nanf("")};
+#pragma unroll
+          for (int d = 0; d < HD / 2; d += 4) *(f32x4*)(p.o32 + r * HD + 2 * d + 4 * hh) = nanf4;
+        }
+      }
+      continue;
+    }
 
     const int ntiles = (L + FROWS - 1) / FROWS;
     const int rem = L - (ntiles - 1) * FROWS;  // valid keys of the last tile, 1..FROWS
@@ -435,6 +455,7 @@ hipError_t launch_attend(const void* q, bool normed, int64_t T, int32_t H, float
   p.hdr = (const WsHeader*)base;
   p.segtab = (const int32_t*)(base + Lw.segtab);
   p.items = (const int32_t*)(base + Lw.items);
+  p.segflag = (const int32_t*)(base + Lw.segflag);
   p.T = T;
   p.H = H;
   p.c = (float)((double)scale * 1.4426950408889634074);

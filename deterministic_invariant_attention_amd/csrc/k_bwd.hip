@@ -59,6 +59,8 @@ struct BwdParams {
   float* dqh;  // with norm weights: gradients with respect to the normed q / k, fp32, staged row-major
   float* dkh;
   const int32_t* inv;  // token of each staged row (position order), or NULL (staged row = token)
+  const uint32_t* dmax;  // per (segment, head): largest |dO|, which fixes the staged dO's power of two
+  const int32_t* segflag;  // per segment: nonzero = a value cannot enter the products (NaN outputs)
   int32_t delta_ready;  // D was written by the staging kernel (from the forward's fp32 output)
   const WsHeader* hdr;
   int32_t* next;  // the kernel's work counter (in the header)
@@ -77,7 +79,7 @@ struct BwdParams {
 // classes of the plan in order (most expensive first) and, inside a class, head-major, so
 // consecutive items share a head's operands and the cheap ones come last.
 struct WorkItem {
-  int head, item, s0, L, tile;
+  int head, item, seg, s0, L, tile;
 };
 
 __device__ __forceinline__ bool item_of(const BwdParams& p, int64_t v, int nitems, int nseg, int nbkt, WorkItem& w,
@@ -101,6 +103,7 @@ __device__ __forceinline__ bool item_of(const BwdParams& p, int64_t v, int nitem
   const int seg = p.items[2 * w.item];
   w.tile = p.items[2 * w.item + 1];
   if ((unsigned)seg >= (unsigned)nseg) return false;
+  w.seg = seg;
   w.s0 = p.segtab[2 * seg];
   w.L = p.segtab[2 * seg + 1];
   return !(w.s0 < 0 || w.L <= 0 || (int64_t)w.s0 + w.L > p.T || w.tile < 0 || w.tile * BT >= w.L);
@@ -141,34 +144,38 @@ __device__ __forceinline__ void rowvec_to_lds(const float* g, int valid, lds_cha
   __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void*)lds, 4, lane * 4, 0, 0, 0);
 }
 
-// Store a row held as a lane pair in the accumulator layout, times s, rounded once to bf16.
-__device__ __forceinline__ void store_row(const f32x16* acc, float s, int hh, uint16_t* out) {
+// Store a row held as a lane pair in the accumulator layout, times s and then 2^ex (which removes
+// the staged dO's power of two exactly), rounded once to bf16.
+__device__ __forceinline__ void store_row(const f32x16* acc, float s, int ex, int hh, uint16_t* out) {
+  auto f = [&](float a) { return __builtin_ldexpf(a * s, ex); };
 #pragma unroll
   for (int db = 0; db < 4; db++)
 #pragma unroll
     for (int g = 0; g < 4; g++) {
       const int d0 = 32 * db + 8 * g + 4 * hh;
       u32x2 o2;
-      o2[0] = pack_bf16(acc[db][4 * g] * s, acc[db][4 * g + 1] * s);
-      o2[1] = pack_bf16(acc[db][4 * g + 2] * s, acc[db][4 * g + 3] * s);
+      o2[0] = pack_bf16(f(acc[db][4 * g]), f(acc[db][4 * g + 1]));
+      o2[1] = pack_bf16(f(acc[db][4 * g + 2]), f(acc[db][4 * g + 3]));
       *(u32x2*)(out + d0) = o2;
     }
 }
 
-// Store a row held as a lane pair in the accumulator layout, times s, in fp32.
-__device__ __forceinline__ void store_row_f32(const f32x16* acc, float s, int hh, float* out) {
+// Store a row held as a lane pair in the accumulator layout, times s and then 2^ex, in fp32.
+__device__ __forceinline__ void store_row_f32(const f32x16* acc, float s, int ex, int hh, float* out) {
+  auto f = [&](float a) { return __builtin_ldexpf(a * s, ex); };
 #pragma unroll
   for (int db = 0; db < 4; db++)
 #pragma unroll
     for (int g = 0; g < 4; g++) {
       const int d0 = 32 * db + 8 * g + 4 * hh;
-      const f32x4 v = {acc[db][4 * g] * s, acc[db][4 * g + 1] * s, acc[db][4 * g + 2] * s, acc[db][4 * g + 3] * s};
+      const f32x4 v = {f(acc[db][4 * g]), f(acc[db][4 * g + 1]), f(acc[db][4 * g + 2]), f(acc[db][4 * g + 3])};
       *(f32x4*)(out + d0) = v;
     }
 }
 
+// Decreasing segment ids: no segmentation exists, every output is NaN.
 __device__ __forceinline__ bool fill_nan_if_bad(const BwdParams& p, uint16_t* a, uint16_t* b) {
-  if (p.hdr->status == 0) return false;
+  if (!(p.hdr->status & STATUS_SEG_BIT)) return false;
   const int64_t n16 = p.T * p.H * HD / 8;
   const int64_t stride = (int64_t)gridDim.x * blockDim.x;
   const u32x4 nan4 = {0x7FC07FC0u, 0x7FC07FC0u, 0x7FC07FC0u, 0x7FC07FC0u};
@@ -177,6 +184,13 @@ __device__ __forceinline__ bool fill_nan_if_bad(const BwdParams& p, uint16_t* a,
     if (b) *(u32x4*)(b + e * 8) = nan4;
   }
   return true;
+}
+
+__device__ __forceinline__ f32x16 nan_acc() {
+  f32x16 a;
+#pragma unroll
+  for (int i = 0; i < 16; i++) a[i] = __builtin_nanf("");
+  return a;
 }
 
 template <int N>
@@ -226,6 +240,17 @@ __global__ __launch_bounds__(64 * BW, 1) void k_bwd_dq(BwdParams p) {
     const bool ok = item_of(p, v, nitems, nseg, nbkt, w, done);
     if (done) break;
     if (!ok) continue;
+    if (p.segflag[w.seg] != 0) {  // a flagged segment: NaN rows (the order maps are not trusted there)
+      const int qr = w.tile * BT + wv * 32 + l32;
+      if (qr < w.L) {
+        const int64_t srow = w.s0 + qr;
+        const f32x16 nan16 = nan_acc();
+        const f32x16 nan4[4] = {nan16, nan16, nan16, nan16};
+        if (p.wq) store_row_f32(nan4, 1.0f, 0, hh, p.dqh + (srow * H + w.head) * HD);
+        else store_row(nan4, 1.0f, 0, hh, p.dq + (srow * H + w.head) * HD);
+      }
+      continue;
+    }
     const int ntk = (w.L + TILE_ROWS - 1) / TILE_ROWS;
     const int rem = w.L - (ntk - 1) * TILE_ROWS;
     const int64_t hT = (int64_t)w.head * T;
@@ -353,14 +378,15 @@ __global__ __launch_bounds__(64 * BW, 1) void k_bwd_dq(BwdParams p) {
       if (j < ntk) pass2(Par2<0>{}, j);
     }
 
-    // ---- epilogue: dq^ = scale dQ (fp32 for the norm backward, else the output itself)
+    // ---- epilogue: dq^ = scale dQ 2^-s (fp32 for the norm backward, else the output itself)
     if (qvalid) {
       const int64_t srow = w.s0 + qrow;
+      const int ex = -dout_scale_exp(p.dmax[(int64_t)w.seg * H + w.head]);
       if (p.wq) {
-        store_row_f32(acc, p.scale, hh, p.dqh + (srow * H + w.head) * HD);
+        store_row_f32(acc, p.scale, ex, hh, p.dqh + (srow * H + w.head) * HD);
       } else {
         const int64_t trow = p.inv ? (int64_t)p.inv[srow] : srow;
-        store_row(acc, p.scale, hh, p.dq + (trow * H + w.head) * HD);
+        store_row(acc, p.scale, ex, hh, p.dq + (trow * H + w.head) * HD);
       }
     }
   }
@@ -402,6 +428,18 @@ __global__ __launch_bounds__(64 * BW, 1) void k_bwd_dkdv(BwdParams p) {
     const bool ok = item_of(p, v, nitems, nseg, nbkt, w, done);
     if (done) break;
     if (!ok) continue;
+    if (p.segflag[w.seg] != 0) {  // a flagged segment: NaN rows (the order maps are not trusted there)
+      const int kr = w.tile * BT + wv * 32 + l32;
+      if (kr < w.L) {
+        const int64_t srow = w.s0 + kr;
+        const f32x16 nan16 = nan_acc();
+        const f32x16 nan4[4] = {nan16, nan16, nan16, nan16};
+        store_row(nan4, 1.0f, 0, hh, p.dv + (srow * H + w.head) * HD);
+        if (p.wk) store_row_f32(nan4, 1.0f, 0, hh, p.dkh + (srow * H + w.head) * HD);
+        else store_row(nan4, 1.0f, 0, hh, p.dk + (srow * H + w.head) * HD);
+      }
+      continue;
+    }
     const int ntq = (w.L + TILE_ROWS - 1) / TILE_ROWS;
     const int64_t hT = (int64_t)w.head * T;
     const uint16_t* q16b = p.qhat16 + (hT + w.s0) * HD;
@@ -495,15 +533,16 @@ __global__ __launch_bounds__(64 * BW, 1) void k_bwd_dkdv(BwdParams p) {
       if (j < ntq) step(Par2<0>{}, j);
     }
 
-    // ---- epilogue: dv, dk^ = scale dK (fp32 for the norm backward, else the output itself)
+    // ---- epilogue: dv 2^-s, dk^ = scale dK 2^-s (fp32 for the norm backward, else the output itself)
     if (kvalid) {
       const int64_t srow = w.s0 + krow;
       const int64_t trow = p.inv ? (int64_t)p.inv[srow] : srow;
-      store_row(dv, 1.0f, hh, p.dv + (trow * H + w.head) * HD);
+      const int ex = -dout_scale_exp(p.dmax[(int64_t)w.seg * H + w.head]);
+      store_row(dv, 1.0f, ex, hh, p.dv + (trow * H + w.head) * HD);
       if (p.wk)
-        store_row_f32(dk, p.scale, hh, p.dkh + (srow * H + w.head) * HD);
+        store_row_f32(dk, p.scale, ex, hh, p.dkh + (srow * H + w.head) * HD);
       else
-        store_row(dk, p.scale, hh, p.dk + (trow * H + w.head) * HD);
+        store_row(dk, p.scale, ex, hh, p.dk + (trow * H + w.head) * HD);
     }
   }
 }
@@ -525,6 +564,8 @@ struct NormBwdParams {
   uint16_t* dx[2];       // dq, dk
   float* part;           // [2][nparts][128]
   const int32_t* inv;    // token of each staged row, or NULL
+  const int32_t* tok2seg;
+  const int32_t* segflag;  // rows of a flagged segment are NaN, written at their own token row
   const WsHeader* hdr;
   int64_t rows;          // T * H
   int32_t H;
@@ -539,11 +580,18 @@ __global__ __launch_bounds__(256) void k_bwd_norm(NormBwdParams p) {
   const int c = tid & 15;
   const int64_t row = (int64_t)blockIdx.x * NR + (tid >> 4);  // staged row: slot * H + head
   const bool valid = row < p.rows;
-  if (p.hdr->status != 0) return;  // the attention kernels have filled the outputs with NaN
+  if (p.hdr->status & STATUS_SEG_BIT) return;  // the attention kernels have filled the outputs with NaN
+  // A staged row lies in the rows of the same segment as the token of that index, so tok2seg names
+  // its segment.  In a flagged segment the order maps may be invalid: the row is NaN and stays at
+  // its own index.
+  bool bad = false;
   int64_t xrow = row;  // the token's row
-  if (p.inv && valid) {
+  if (valid) {
     const int64_t sl = row / p.H;
-    xrow = (int64_t)p.inv[sl] * p.H + (row - sl * p.H);
+    const int sg = p.tok2seg[sl];
+    const int nseg = p.hdr->nseg;
+    bad = sg >= 0 && sg < nseg && p.segflag[sg] != 0;
+    if (p.inv && !bad) xrow = (int64_t)p.inv[sl] * p.H + (row - sl * p.H);
   }
 
   float x[8], dy[8], wf[8];
@@ -575,6 +623,7 @@ __global__ __launch_bounds__(256) void k_bwd_norm(NormBwdParams p) {
     o[i] = f64x2_to_bf16x2_rne(r * ((double)wf[2 * i] * (double)dy[2 * i]) - k3 * (double)x[2 * i],
                                r * ((double)wf[2 * i + 1] * (double)dy[2 * i + 1]) - k3 * (double)x[2 * i + 1]);
   }
+  if (bad) o = u32x4{0x7FC07FC0u, 0x7FC07FC0u, 0x7FC07FC0u, 0x7FC07FC0u};
   if (valid) *(u32x4*)(p.dx[which] + xrow * HD + 8 * c) = o;
   f32x4 t0, t1;
 #pragma unroll
@@ -657,6 +706,8 @@ hipError_t launch_bwd(const void* q, const void* k, const void* wq, const void* 
   p.dqh = (float*)(base + Lw.dqh);
   p.dkh = (float*)(base + Lw.dkh);
   p.inv = inv;
+  p.dmax = (const uint32_t*)(base + Lw.dmax);
+  p.segflag = (const int32_t*)(base + Lw.segflag);
   p.delta_ready = delta_ready ? 1 : 0;
   p.hdr = (const WsHeader*)base;
   p.segtab = (const int32_t*)(base + Lw.segtab);
@@ -690,6 +741,8 @@ hipError_t launch_bwd(const void* q, const void* k, const void* wq, const void* 
     np.dx[1] = (uint16_t*)dk;
     np.part = (float*)(base + Lw.dw_part);
     np.inv = inv;
+    np.tok2seg = (const int32_t*)(base + Lw.tok2seg);
+    np.segflag = (const int32_t*)(base + Lw.segflag);
     np.hdr = (const WsHeader*)base;
     np.rows = T * H;
     np.H = H;

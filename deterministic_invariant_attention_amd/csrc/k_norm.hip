@@ -53,6 +53,8 @@ struct PrepParams {
   uint16_t* khat;
   uint16_t* v16;
   const int32_t* slot;  // staged row of each token (position order), or NULL for packed order
+  const int32_t* tok2seg;
+  int32_t* segflag;  // a segment with a value beyond fp16 is flagged (its outputs become NaN)
   WsHeader* hdr;
   int64_t T;
   int32_t H;
@@ -105,6 +107,7 @@ __global__ __launch_bounds__(256) void k_prep_qkv(PrepParams p) {
       st16(p.khat + dst, ko);
       st16(p.v16 + dst, vo);
     }
+    if (valid && over) flag_segment(p.segflag, p.tok2seg[t], p.hdr->nseg);
     const uint64_t any_over = __ballot(valid && over);
     if (any_over && (threadIdx.x & 63) == __builtin_ctzll(any_over)) atomicOr(&p.hdr->status, STATUS_RANGE_BIT);
   }
@@ -129,11 +132,69 @@ struct BwdPrepParams {
   float* lse2;
   float* delta;         // -D, D = dO . O per row (with o32)
   const int32_t* slot;  // staged row of each token (position order), or NULL for packed order
+  const int32_t* tok2seg;  // segment of each token
+  int32_t* segflag;        // a segment with a q^, k^ or v value beyond fp16 is flagged (NaN outputs)
+  const uint32_t* dmax;    // per (segment, head): largest |dO| (bf16 magnitude bits)
   WsHeader* hdr;
   int64_t T;
   int32_t H;
   float eps;
 };
+
+// The largest |dO| of every (segment, head): one workgroup per 64 tokens of one head (workgroup b:
+// head b % H, tokens 64 (b / H) ..), 16 lanes per (token, head) row.  Each row's maximum (bf16 magnitude bits, exact integers) goes to
+// LDS; thread 0 then walks the block's 64 tokens and, at the end of each run of one segment, folds
+// the run's maximum into the segment's slot with an integer atomicMax, so the result is the same
+// whatever the order of the workgroups.
+constexpr int DMAX_TOK = 64;  // tokens per workgroup
+
+__global__ __launch_bounds__(256) void k_bwd_dmax(const uint16_t* __restrict__ dout, const int32_t* __restrict__ tok2seg,
+                                                  uint32_t* __restrict__ dmax, const WsHeader* hdr, int64_t T,
+                                                  int32_t H) {
+  __shared__ uint32_t s_max[DMAX_TOK];
+  __shared__ int32_t s_seg[DMAX_TOK];
+  const int c = threadIdx.x & 15;
+  const int h = (int)(blockIdx.x % (unsigned)H);
+  const int64_t t0 = (int64_t)(blockIdx.x / (unsigned)H) * DMAX_TOK;
+#pragma unroll
+  for (int it = 0; it < DMAX_TOK / 16; it++) {
+    const int i = it * 16 + (threadIdx.x >> 4);  // token within the block
+    const int64_t t = t0 + i;
+    uint32_t m = 0;
+    if (t < T) {
+      const u32x4 w = *(const u32x4*)(dout + (t * H + h) * HD + c * 8);
+#pragma unroll
+      for (int j = 0; j < 4; j++) {
+        const uint32_t a = w[j] & 0x7FFFu, b = (w[j] >> 16) & 0x7FFFu;
+        m = a > m ? a : m;
+        m = b > m ? b : m;
+      }
+    }
+#pragma unroll
+    for (int o = 1; o < 16; o <<= 1) {
+      const uint32_t y = (uint32_t)__shfl_xor((int)m, o, 64);
+      m = y > m ? y : m;
+    }
+    if (c == 0) {
+      s_max[i] = m;
+      s_seg[i] = t < T ? tok2seg[t] : -1;
+    }
+  }
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    const int nseg = hdr->nseg;  // 0 after a segment-id error: nothing is folded
+    uint32_t run = 0;
+    for (int i = 0; i < DMAX_TOK; i++) {
+      const int sg = s_seg[i];
+      run = s_max[i] > run ? s_max[i] : run;
+      const bool last = i + 1 == DMAX_TOK || s_seg[i + 1] != sg;
+      if (last) {
+        if (sg >= 0 && sg < nseg) atomicMax(&dmax[(int64_t)sg * H + h], run);
+        run = 0;
+      }
+    }
+  }
+}
 
 // bf16 chunk -> fp16 chunk: exact for every bf16 value from 2^-17 up to 65504 in magnitude (and
 // zero); below 2^-17 fp16 subnormals round it, by at most 2^-25.  over |= a finite value beyond
@@ -187,7 +248,17 @@ __global__ __launch_bounds__(256) void k_bwd_prep(BwdPrepParams p) {
     const u32x4 q16 = bf16_chunk_to_f16(qo, over);
     const u32x4 k16 = bf16_chunk_to_f16(ko, over);
     const u32x4 v16 = bf16_chunk_to_f16(vv, over);
-    const u32x4 g16 = bf16_chunk_to_f16(gv, over);
+    // dO times 2^s of its (segment, head) (exact: a power of two; the largest |dO| lands in [4, 8),
+    // so the fp16 conversion neither overflows nor loses the small values of a small gradient)
+    int sx = 0;
+    const int nseg = p.hdr->nseg;
+    const int sg = valid ? p.tok2seg[t] : -1;
+    if (sg >= 0 && sg < nseg) sx = dout_scale_exp(p.dmax[(int64_t)sg * p.H + h]);
+    if (valid && over) flag_segment(p.segflag, sg, nseg);
+    u32x4 g16;
+#pragma unroll
+    for (int i = 0; i < 4; i++)
+      g16[i] = pack_f16(__builtin_ldexpf(bf16_lo(gv[i]), sx), __builtin_ldexpf(bf16_hi(gv[i]), sx));
     if (valid) {
       st16(p.qhat16 + dst, q16);
       st16(p.khat16 + dst, k16);
@@ -209,7 +280,8 @@ __global__ __launch_bounds__(256) void k_bwd_prep(BwdPrepParams p) {
       d = d + __shfl_xor(d, 2, 64);
       d = d + __shfl_xor(d, 4, 64);
       d = d + __shfl_xor(d, 8, 64);
-      if (valid && c == 0) p.delta[h * p.T + ts] = -(float)d;
+      // D of the scaled dO: the same power of two, applied in FP64 before the one fp32 rounding
+      if (valid && c == 0) p.delta[h * p.T + ts] = -(float)__builtin_ldexp(d, sx);
     }
     const uint64_t any_over = __ballot(valid && over);
     if (any_over && (threadIdx.x & 63) == __builtin_ctzll(any_over)) atomicOr(&p.hdr->status, STATUS_RANGE_BIT);
@@ -242,10 +314,17 @@ hipError_t launch_bwd_prep(const void* q, const void* k, const void* v, const vo
   p.lse2 = (float*)(base + L.lse2);
   p.delta = (float*)(base + L.delta);
   p.slot = slot;
+  p.tok2seg = (const int32_t*)(base + L.tok2seg);
+  p.segflag = (int32_t*)(base + L.segflag);
+  p.dmax = (const uint32_t*)(base + L.dmax);
   p.hdr = (WsHeader*)base;
   p.T = T;
   p.H = H;
   p.eps = eps;
+  hipLaunchKernelGGL(k_bwd_dmax, dim3((unsigned)((T + DMAX_TOK - 1) / DMAX_TOK * H)), dim3(256), 0, stream,
+                     (const uint16_t*)dout, p.tok2seg, (uint32_t*)(base + L.dmax), (const WsHeader*)base, T, H);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
   hipLaunchKernelGGL(k_bwd_prep, dim3(grid_for_rows(rows)), dim3(256), 0, stream, p);
   return hipGetLastError();
 }
@@ -274,6 +353,8 @@ hipError_t launch_prep_qkv(const void* q, const void* k, const void* v, const vo
   p.khat = (uint16_t*)(base + L.khat);
   p.v16 = (uint16_t*)(base + L.v16);
   p.slot = slot;
+  p.tok2seg = (const int32_t*)(base + L.tok2seg);
+  p.segflag = (int32_t*)(base + L.segflag);
   p.hdr = (WsHeader*)base;
   p.T = T;
   p.H = H;

@@ -42,9 +42,14 @@ __device__ __forceinline__ int block_excl_scan(int v, int* lds_wave, int& total)
 // most expensive class first (the order inside a class is free: it only decides which workgroup
 // runs an item, never a result), and bkt[2b], bkt[2b+1] = first item and item count of the b-th
 // non-empty class; the work counters are reset.
+// tok2seg: the segment index of every token; segflag: the per-segment error flags, cleared for the
+// call's nseg segments; dmax (backward only, else NULL): the per-(segment, head) maxima of |dO|,
+// zeroed for the nseg * H slots the call uses.
 __global__ __launch_bounds__(1024) void k_plan(const int32_t* __restrict__ seg, int64_t T, WsHeader* hdr,
                                               int32_t* __restrict__ segtab, int32_t* __restrict__ items, int tile,
-                                              int32_t* __restrict__ bkt) {
+                                              int32_t* __restrict__ bkt, int32_t* __restrict__ tok2seg,
+                                              int32_t* __restrict__ segflag, uint32_t* __restrict__ dmax,
+                                              int32_t H) {
   __shared__ int lds_wave[16];
   __shared__ int s_bad;
   __shared__ int s_cnt[NBKT], s_run[NBKT];
@@ -69,6 +74,7 @@ __global__ __launch_bounds__(1024) void k_plan(const int32_t* __restrict__ seg, 
     int total;
     const int pos = block_excl_scan(flag, lds_wave, total);
     if (flag) segtab[2 * (nseg + pos)] = (int32_t)t;
+    if (t < T) tok2seg[t] = nseg + pos + flag - 1;
     nseg += total;
   };
   constexpr int PRE = 16;
@@ -90,6 +96,9 @@ __global__ __launch_bounds__(1024) void k_plan(const int32_t* __restrict__ seg, 
     }
   }
   if (bad) atomicOr(&s_bad, 1);
+  for (int i = tid; i < nseg; i += 1024) segflag[i] = 0;
+  if (dmax)
+    for (int64_t i = tid; i < (int64_t)nseg * H; i += 1024) dmax[i] = 0u;
   __syncthreads();
 
   // pass 2: lengths
@@ -168,7 +177,8 @@ hipError_t launch_plan(const int32_t* seg, int64_t T, void* ws, int32_t H, hipSt
   const WsLayout L = ws_layout(T, H);
   char* base = (char*)ws;
   hipLaunchKernelGGL(k_plan, dim3(1), dim3(1024), 0, stream, seg, T, (WsHeader*)base, (int32_t*)(base + L.segtab),
-                     (int32_t*)(base + L.items), BQ, nullptr);
+                     (int32_t*)(base + L.items), BQ, nullptr, (int32_t*)(base + L.tok2seg), (int32_t*)(base + L.segflag),
+                     nullptr, H);
   return hipGetLastError();
 }
 
@@ -176,7 +186,8 @@ hipError_t launch_plan_bwd(const int32_t* seg, int64_t T, void* ws, int32_t H, h
   const BwdLayout L = bwd_layout(T, H);
   char* base = (char*)ws;
   hipLaunchKernelGGL(k_plan, dim3(1), dim3(1024), 0, stream, seg, T, (WsHeader*)base, (int32_t*)(base + L.segtab),
-                     (int32_t*)(base + L.items), BT, (int32_t*)(base + L.bkt));
+                     (int32_t*)(base + L.items), BT, (int32_t*)(base + L.bkt), (int32_t*)(base + L.tok2seg),
+                     (int32_t*)(base + L.segflag), (uint32_t*)(base + L.dmax), H);
   return hipGetLastError();
 }
 

@@ -6,9 +6,10 @@ max(1, max |oracle|) for dq, dk, dv; relative L2 <= 2e-3 for dwq, dwk (fp32).  T
 the forward's (whose outputs are O(1)) scaled by the gradient's largest magnitude: gradients of a
 sharp softmax reach ~40, where one bf16 rounding alone moves a value by up to 0.125.  The oracle
 evaluates the gradients at the rounded normed operands with the rounding as the identity
-(straight-through), the definition the kernels implement.  The full config-5 shape (2 x 4253 tokens, 40 heads) is checked on a subset of
-heads, which are independent; its weight gradients (sums over all heads) are compared on the
-smaller workloads."""
+(straight-through), the definition the kernels implement.  The full config-5 shape (2 x 4253 tokens,
+40 heads) is compared on every head and on both weight gradients, in both ways of forming D."""
+import functools
+
 import numpy as np
 import pytest
 import torch
@@ -39,7 +40,16 @@ def run_bwd(g, weights=True, eps=EPS, scale=SCALE, dmode="recompute"):
     return res
 
 
-def _check(name, x, heads=None, weights=True, eps=EPS, scale=SCALE, dmode="recompute"):
+@functools.lru_cache(maxsize=1)
+def _oracle_workload_bwd(name):
+    """The oracle's gradients of a configured workload (cached: both D modes compare against them)."""
+    wl = workloads.WORKLOADS[name]
+    x = workloads.make_inputs(wl, with_grad=True)
+    say(f"[bwd parity] oracle gradients of {name} (T={wl.tokens} H={wl.heads}, all heads)")
+    return oracle.bwd(x["q"], x["k"], x["v"], x["seg"].numpy(), x["dout"], x["wq"], x["wk"], wl.eps, wl.scale)
+
+
+def _check(name, x, heads=None, weights=True, eps=EPS, scale=SCALE, dmode="recompute", ref=None, abs_rel=False):
     g = to_dev(x)
     T, H = x["q"].shape[0], x["q"].shape[1]
     say(f"[bwd parity] {name} ({dmode}): T={T} H={H} heads={'all' if heads is None else heads}")
@@ -47,13 +57,14 @@ def _check(name, x, heads=None, weights=True, eps=EPS, scale=SCALE, dmode="recom
     hs = slice(None) if heads is None else list(heads)
     sub = {n: (x[n][:, hs].contiguous() if n in ("q", "k", "v", "dout") else x[n]) for n in x}
     wq, wk = (x["wq"], x["wk"]) if weights else (None, None)
-    ref = oracle.bwd(sub["q"], sub["k"], sub["v"], x["seg"].numpy(), sub["dout"], wq, wk, eps, scale)
+    if ref is None:
+        ref = oracle.bwd(sub["q"], sub["k"], sub["v"], x["seg"].numpy(), sub["dout"], wq, wk, eps, scale)
     res, mag = {}, {}
     for nm, a, r in (("dq", dq, ref[0]), ("dk", dk, ref[1]), ("dv", dv, ref[2])):
         a = a[:, hs]
         assert np.all(np.isfinite(f64(a))), nm
         res[nm] = metrics(a, r)
-        mag[nm] = max(1.0, float(np.abs(r).max())) if r.size else 1.0
+        mag[nm] = (float(np.abs(r).max()) if abs_rel else max(1.0, float(np.abs(r).max()))) if r.size else 1.0
     if weights and heads is None:
         for nm, a, r in (("dwq", dwq, ref[3]), ("dwk", dwk, ref[4])):
             res[nm] = (float(np.linalg.norm(a.cpu().double().numpy() - r) / np.linalg.norm(r)), 0.0)
@@ -119,10 +130,11 @@ def test_bwd_empty_input_is_a_noop():
 
 
 @pytest.mark.parametrize("dmode", DMODES)
-def test_bwd_parity_batch2_heads(dmode):
-    """Config 5 (2 x 4253 tokens, 40 heads) at full size, heads 0, 17 and 39 against the oracle."""
-    _check("batch2", workloads.make_inputs(workloads.WORKLOADS["batch2"], with_grad=True), heads=(0, 17, 39),
-           dmode=dmode)
+def test_bwd_parity_batch2_full(dmode):
+    """Config 5 (2 x 4253 tokens, 40 heads) at full size: dq, dk, dv on every head and both norm-weight
+    gradients (sums over every token and head) against the oracle."""
+    _check("batch2", workloads.make_inputs(workloads.WORKLOADS["batch2"], with_grad=True), dmode=dmode,
+           ref=_oracle_workload_bwd("batch2"))
 
 
 @pytest.mark.parametrize("dmode", DMODES)
@@ -187,13 +199,52 @@ def test_bwd_nan_neighbour_does_not_leak(dmode):
         assert bitwise_equal(a[:40], b[:40]) and bitwise_equal(a[110:], b[110:])
 
 
-def test_bwd_dout_out_of_fp16_range_sets_status():
-    x = workloads.random_inputs([20], 2, seed=6, with_grad=True)
+@pytest.mark.parametrize("dmode", DMODES)
+@pytest.mark.parametrize("dscale", [1e-6, 1e-8, 1e-30, 1e6])
+def test_bwd_parity_small_and_large_dout(dscale, dmode):
+    """dO far from N(0, 1): bf16 draws times 1e-6, 1e-8, 1e-30 (below fp16's whole range) and 1e6
+    (beyond it).  The staging scales each (segment, head) of dO by a power of two before the fp16
+    products and the epilogues remove it, so the gradients keep the accuracy of the N(0, 1) case.
+    The max-abs bound is relative to the gradient's own largest magnitude here."""
+    x = workloads.random_inputs([300, 129, 1, 64], 3, seed=71, with_grad=True)
+    x["dout"] = (x["dout"].float() * dscale).to(torch.bfloat16)
+    _check(f"dout x{dscale:g}", x, dmode=dmode, abs_rel=True)
+
+
+@pytest.mark.parametrize("dmode", DMODES)
+def test_bwd_dout_power_of_two_scales_every_gradient_exactly(dmode):
+    """Every gradient is linear in dO, and the staging's power of two cancels exactly: dO 2^k gives
+    dq, dk, dv, dwq, dwk times 2^k bit for bit (while the results stay normal numbers)."""
+    x = workloads.random_inputs([200, 77, 5], 2, seed=72, with_grad=True)
     g = to_dev(x)
-    g["dout"][3, 1, 7] = 1e6
+    say(f"[bwd bitwise] dO times powers of two ({dmode})")
+    base = run_bwd(g, dmode=dmode)
+    for k in (-100, -24, 20):
+        gk = dict(g, dout=(g["dout"].float() * 2.0 ** k).to(torch.bfloat16))
+        got = run_bwd(gk, dmode=dmode)
+        for nm, a, b in zip(("dq", "dk", "dv", "dwq", "dwk"), got, base):
+            expect = (b.float() * 2.0 ** k).to(b.dtype)
+            assert bitwise_equal(a, expect), f"{nm} at 2^{k}"
+
+
+def test_bwd_large_dout_is_scaled_and_v_out_of_range_sets_status():
+    """A dO of 1e6 (beyond fp16) is scaled into range and gives correct gradients with status OK; a v
+    beyond the fp16 range still cannot enter the products and sets ERR_RANGE (NaN outputs)."""
+    x = workloads.random_inputs([20], 2, seed=6, with_grad=True)
+    x["dout"][3, 1, 7] = 1e6
+    g = to_dev(x)
     _, lse = h3.h3attn_fwd(g["q"], g["k"], g["v"], g["seg"], g["wq"], g["wk"], eps=EPS, want_lse=True)
     T, H = x["q"].shape[:2]
     ws = h3.bwd_workspace(T, H, g["q"].device)
+    dq, dk, dv, dwq, dwk = h3.h3attn_bwd(g["dout"], g["q"], g["k"], g["v"], lse, g["seg"], g["wq"], g["wk"], eps=EPS,
+                                         workspace_buf=ws)
+    torch.cuda.synchronize()
+    assert h3.h3attn_status_read(ws) == h3.H3ATTN_OK
+    ref = oracle.bwd(x["q"], x["k"], x["v"], x["seg"].numpy(), x["dout"], x["wq"], x["wk"], EPS, SCALE)
+    for nm, a, r in zip(("dq", "dk", "dv"), (dq, dk, dv), ref):
+        rel, mx = metrics(a, r)
+        assert rel <= REL_L2_BOUND and mx <= MAX_ABS_BOUND * float(np.abs(r).max()), nm
+    g["v"][5, 0, 2] = 7.0e4
     dq, dk, dv, dwq, dwk = h3.h3attn_bwd(g["dout"], g["q"], g["k"], g["v"], lse, g["seg"], g["wq"], g["wk"], eps=EPS,
                                          workspace_buf=ws)
     torch.cuda.synchronize()
@@ -226,6 +277,7 @@ def test_fwd_ex_o32_is_the_output_before_its_rounding():
 
 
 def test_fwd_ex_o32_nan_filled_on_data_error():
+    """A value beyond fp16 in segment 0: its rows of o32 and out are NaN, segment 1's are computed."""
     x = workloads.random_inputs([40, 40], 2, seed=53)
     x["v"][10, 1, 5] = 1.0e5
     g = to_dev(x)
@@ -234,7 +286,31 @@ def test_fwd_ex_o32_nan_filled_on_data_error():
                                      want_lse=True, want_o32=True, workspace_buf=ws)
     torch.cuda.synchronize()
     assert h3.h3attn_status_read(ws) == h3.H3ATTN_ERR_RANGE
-    assert torch.isnan(o32).all() and torch.isnan(out.float()).all()
+    assert torch.isnan(o32[:40]).all() and torch.isnan(out[:40].float()).all()
+    assert torch.isfinite(o32[40:]).all() and bitwise_equal(o32[40:].to(torch.bfloat16), out[40:])
+
+
+def test_bwd_out_of_range_fails_its_own_segment_only():
+    """A v beyond fp16 in the middle segment: the backward's rows of that segment are NaN, the other
+    segments' dq, dk, dv keep the bits of a clean run (and of each segment alone); dwq / dwk, sums
+    over the whole batch, are NaN."""
+    x = workloads.random_inputs([50, 60, 70], 2, seed=79, with_grad=True)
+    g = to_dev(x)
+    clean = {dm: run_bwd(g, dmode=dm) for dm in DMODES}
+    g["v"][70, 1, 3] = 9.0e4
+    say("[bwd status] |v| > 65504 in segment 1")
+    for dmode in DMODES:
+        got = run_bwd(g, dmode=dmode)
+        for t in got[:3]:
+            assert torch.isnan(t[50:110].float()).all()
+        for t in got[3:]:
+            assert torch.isnan(t).all()
+        for t0, t1 in ((0, 50), (110, 180)):
+            alone = {n: (g[n][t0:t1].contiguous() if n in ("q", "k", "v", "seg", "dout") else g[n]) for n in g}
+            a = run_bwd(alone, dmode=dmode)
+            for t, c, cl in zip(got[:3], a[:3], clean[dmode][:3]):
+                assert bitwise_equal(t[t0:t1], cl[t0:t1])
+                assert bitwise_equal(t[t0:t1], c)
 
 
 def test_bwd_long_batch_past_the_decode_prefetch_alone_equals_batched():

@@ -104,15 +104,24 @@ def test_decreasing_segment_ids_set_status_and_nan_fill():
     assert torch.isfinite(out2.float()).all()
 
 
-def test_v_out_of_fp16_range_sets_status():
+def test_v_out_of_fp16_range_fails_its_own_segment_only():
+    """A finite |v| beyond fp16 cannot enter the P.V product: the status word reports ERR_RANGE and
+    the rows of that value's segment are NaN (fail closed), while every other segment keeps the
+    bits it has alone, so alone == batched holds for such inputs too."""
     x = workloads.random_inputs([40, 40], 2, seed=53)
+    g0 = to_dev(x)
+    clean, clse = run_fwd(g0, want_lse=True)
     x["v"][10, 1, 5] = 1.0e5
     g = to_dev(x)
-    say("[status] |v| > 65504")
+    say("[status] |v| > 65504 in segment 0")
     ws = h3.workspace(80, 2, "cuda:0")
-    out, _ = run_fwd(g, ws=ws)
+    out, lse = run_fwd(g, want_lse=True, ws=ws)
     assert h3.h3attn_status_read(ws) == h3.H3ATTN_ERR_RANGE
-    assert torch.isnan(out.float()).all()
+    assert torch.isnan(out[:40].float()).all() and torch.isnan(lse[:40]).all()
+    assert bitwise_equal(out[40:], clean[40:]) and bitwise_equal(lse[40:], clse[40:])
+    alone = {n: (g[n][40:].contiguous() if n in ("q", "k", "v", "seg") else g[n]) for n in g}
+    oa, la = run_fwd(alone, want_lse=True)
+    assert bitwise_equal(oa, out[40:]) and bitwise_equal(la, lse[40:])
     # infinities are not a range error: they propagate as IEEE values (only in their own segment)
     x["v"][10, 1, 5] = float("inf")
     g = to_dev(x)

@@ -9,6 +9,7 @@ keys in packed order.  With position ids the library adds them in position order
   * natural positions (0..L-1 in packing order) give bitwise the plain entry points' results;
   * the result still meets the oracle's bound (the oracle's FP64 sums do not depend on the order);
   * ids that are not a permutation of 0..L-1 in some segment set H3ATTN_ERR_POSITIONS and NaN-fill
+    that segment's rows (the other segments keep their bits)
     every output; the next valid call on the workspace computes normally.
 """
 import numpy as np
@@ -198,28 +199,37 @@ def bad_positions(kind, seg_lens):
 
 
 @pytest.mark.parametrize("kind", ["duplicate", "too_large", "negative", "huge", "shifted"])
-def test_invalid_positions_set_status_and_nan_fill(kind):
+def test_invalid_positions_fail_their_own_segment_only(kind):
+    """Ids that are not a permutation of 0..L-1 in one segment: ERR_POSITIONS, that segment's rows
+    NaN (forward and backward), the other segment's rows the bits of valid ids; the weight
+    gradients, sums over the whole batch, are NaN."""
     seg_lens = [40, 40]
     x = workloads.random_inputs(seg_lens, 2, seed=97, with_grad=True)
     g = to_dev(x)
     pos = bad_positions(kind, seg_lens).cuda()
+    bad = slice(0, 40) if kind == "negative" else slice(40, 80)
+    good_rows = slice(40, 80) if kind == "negative" else slice(0, 40)
     say(f"[position] invalid ids: {kind}")
+    good = workloads.position_ids(seg_lens).cuda()
     ws = h3.workspace(80, 2, "cuda:0")
+    ref, rlse = fwd_pos(g, good, ws=ws)
+    assert h3.h3attn_status_read(ws) == h3.H3ATTN_OK
     out, lse = fwd_pos(g, pos, ws=ws)
     assert h3.h3attn_status_read(ws) == h3.H3ATTN_ERR_POSITIONS
-    assert torch.isnan(out.float()).all() and torch.isnan(lse).all()
-    good = workloads.position_ids(seg_lens).cuda()
-    _, glse = fwd_pos(g, good, ws=ws)
-    assert h3.h3attn_status_read(ws) == h3.H3ATTN_OK
+    assert torch.isnan(out[bad].float()).all() and torch.isnan(lse[bad]).all()
+    assert bitwise_equal(out[good_rows], ref[good_rows]) and bitwise_equal(lse[good_rows], rlse[good_rows])
     bws = h3.bwd_workspace(80, 2, "cuda:0")
-    res = bwd_pos(g, pos, glse, ws=bws)
-    assert h3.h3attn_status_read(bws) == h3.H3ATTN_ERR_POSITIONS
-    for t in res:
-        assert torch.isnan(t.float()).all()
-    res = bwd_pos(g, good, glse, ws=bws)
+    gref = bwd_pos(g, good, rlse, ws=bws)
     assert h3.h3attn_status_read(bws) == h3.H3ATTN_OK
-    for t in res:
+    for t in gref:
         assert torch.isfinite(t.float()).all()
+    res = bwd_pos(g, pos, rlse, ws=bws)
+    assert h3.h3attn_status_read(bws) == h3.H3ATTN_ERR_POSITIONS
+    for t, r in zip(res[:3], gref[:3]):
+        assert torch.isnan(t[bad].float()).all()
+        assert bitwise_equal(t[good_rows], r[good_rows])
+    for t in res[3:]:
+        assert torch.isnan(t).all()
 
 
 def test_decreasing_segments_take_precedence_over_positions():
