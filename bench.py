@@ -5,7 +5,10 @@ attention) over the full workload, inputs resident in HBM.  Prints ONE JSON line
   value     whole-step attention TFLOP/s (nominal 4 * sum(L^2) * H * 128 FLOPs per step)
   roofline  the attention kernel alone (h3attn_attend), timed per launch with HIP events on the
             launch stream, against the bf16/fp16 dense MFMA peak (2516.6 TFLOP/s)
-  cpu_baseline  the FP64 CPU oracle on a bounded sample of query rows of the same workload
+  cpu_baseline  the FP64 CPU oracle on a bounded sample of query rows of the same workload (with
+            the host's CPU model and the time of each growing probe)
+  parity    the benched output on those same rows against the oracle (relative L2 and max abs,
+            with the bounds 2e-3 / 2e-2): the accuracy of the timed output itself
 Backward (--pass bwd, default workload batch2): one step = one h3attn_bwd_ex call (plan, operand
 staging with D = dO . O, dq, dk/dv, weight-gradient reduction) given dO and the forward's LSE and
 fp32 output (--d-from recompute: D recomputed by the dq kernel instead, h3attn_bwd); TFLOP/s on
@@ -157,8 +160,9 @@ def main():
     log(f"attention kernel: mean {attn_ms:.4f} ms, median {np.median(kms):.4f} ms -> {attn_tflops:.1f} TFLOP/s "
         f"({100 * attn_tflops / PEAK_MFMA_TFLOPS:.1f}% of bf16 MFMA peak)")
 
-    # ---- CPU baseline: the FP64 oracle on a bounded sample of query rows (rank 0, N = 1)
-    cpu = None
+    # ---- CPU baseline: the FP64 oracle on a bounded sample of query rows (rank 0, N = 1); the same
+    # rows of the benched output are then checked against it (the accuracy of the timed output)
+    cpu, parity = None, None
     if not args.no_cpu_baseline:
         import oracle
         seg_np = x["seg"].numpy()
@@ -166,15 +170,16 @@ def main():
         L = max(wl.seg_lens)
 
         def run_rows(n):
-            rows = np.sort(rng.choice(T, size=n, replace=False))
+            rows = np.arange(T) if n == T else np.sort(rng.choice(T, size=n, replace=False))
             t1 = time.perf_counter()
-            oracle.fwd_rows(x["q"], x["k"], x["v"], seg_np, rows, x["wq"], x["wk"], wl.eps, wl.scale)
-            return rows, time.perf_counter() - t1
+            ref = oracle.fwd_rows(x["q"], x["k"], x["v"], seg_np, rows, x["wq"], x["wk"], wl.eps, wl.scale)[0]
+            return rows, ref, time.perf_counter() - t1
 
         # grow the sample until it takes at least half the target time (or is the whole workload)
-        n = min(32, T)
+        n, probes = min(32, T), []
         while True:
-            rows, dt = run_rows(n)
+            rows, ref, dt = run_rows(n)
+            probes.append([int(n), round(dt, 3)])
             if dt >= 0.5 * args.cpu_seconds or n == T:
                 break
             n = int(min(T, max(2 * n, n * args.cpu_seconds / max(dt, 1e-3))))
@@ -184,8 +189,17 @@ def main():
         cpu = {"value": round(sample_flops / dt / 1e12, 6), "unit": "TFLOP/s", "cores": oracle.num_threads(),
                "kind": "oracle",
                "sample": f"{len(rows)} of {T} query rows x {H} heads of the {wl.name} workload "
-                         f"(segment length {L}); {dt:.1f} s FP64"}
+                         f"(segment length {L}); {dt:.1f} s FP64",
+               "cpu_model": cpu_model(), "probes_rows_seconds": probes}
         log(f"cpu baseline: {cpu}")
+        # (with --order position both the benched output and the oracle's rows are in the shuffled
+        # packing order of x)
+        got = out.float().cpu().double().numpy()[rows]
+        diff = got - ref
+        parity = {"rows": int(len(rows)), "of_rows": T, "rel_l2": float(np.linalg.norm(diff) / np.linalg.norm(ref)),
+                  "max_abs": float(np.max(np.abs(diff))), "bound_rel_l2": 2e-3, "bound_max_abs": 2e-2}
+        parity["ok"] = bool(parity["rel_l2"] <= 2e-3 and parity["max_abs"] <= 2e-2)
+        log(f"benched output vs oracle: {parity}")
 
     line = {
         "metric": METRIC,
@@ -210,8 +224,21 @@ def main():
                      "unit": "TFLOP/s", "frac": round(attn_tflops / PEAK_MFMA_TFLOPS, 4),
                      "traffic": traffic_bytes(wl.name), "kernel": "k_attn_fwd", "kernel_ms": round(attn_ms, 4)},
         "cpu_baseline": cpu,
+        "parity": parity,
     }
     print(json.dumps(line), flush=True)
+
+
+def cpu_model():
+    """The host CPU's model name (from /proc/cpuinfo), for the CPU-baseline record."""
+    try:
+        with open("/proc/cpuinfo") as f:
+            for ln in f:
+                if ln.startswith("model name"):
+                    return ln.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return None
 
 
 def copy_calibration(dev):
