@@ -39,10 +39,15 @@
  * the default stream) of the current device.  Entry points are thread-safe.
  *
  * Errors are fail-closed, never a fallback.  Argument errors are returned synchronously before any
- * work is enqueued.  Data errors that only the device can see (decreasing segment ids, a V value
- * outside fp16 range, position ids that are not a permutation) are recorded in the workspace's
- * status word; the attention output is then filled with NaN so it cannot be mistaken for a valid
- * result, and h3attn_status_read reports it.
+ * work is enqueued.  Data errors that only the device can see are recorded in the workspace's
+ * status word, which h3attn_status_read reports, and the affected outputs are filled with NaN so
+ * they cannot be mistaken for valid results:
+ *   - decreasing segment ids: no segmentation exists, every output of the call is NaN;
+ *   - a value that cannot enter an fp16 product (a finite |v| > 65504; in the backward also a normed
+ *     q or k), or position ids that are not a permutation of 0..L-1: only the rows of that value's
+ *     segment are NaN.  Every other segment is computed as usual and keeps the bits it has alone,
+ *     so a row's output never depends on another segment's bytes.  (The backward's dwq / dwk are
+ *     sums over the whole batch and are NaN after any data error.)
  */
 #ifndef H3ATTN_H
 #define H3ATTN_H
@@ -66,8 +71,8 @@ enum {
   H3ATTN_ERR_DEVICE = 6,    /* no current device, or it is not gfx950 */
   H3ATTN_ERR_LAUNCH = 7,    /* the HIP runtime rejected a launch */
   H3ATTN_ERR_SEGMENTS = 8,  /* device status: segment ids decrease somewhere */
-  H3ATTN_ERR_RANGE = 9,     /* device status: a finite value > 65504 cannot enter an fp16 product */
-  H3ATTN_ERR_POSITIONS = 10 /* device status: position ids are not a permutation of 0..L-1 in a segment */
+  H3ATTN_ERR_RANGE = 9,     /* device status: a finite value > 65504 cannot enter an fp16 product (its segment is NaN) */
+  H3ATTN_ERR_POSITIONS = 10 /* device status: position ids are not a permutation of 0..L-1 in a segment (NaN there) */
 };
 
 /* H3ATTN_VERSION of the loaded library. */
@@ -108,7 +113,8 @@ int h3attn_fwd(const void* q, const void* k, const void* v, const int32_t* seg_i
  * ids permutes the output rows and changes no bit of them.
  *   pos_ids: int32 [T] device memory, 4-byte aligned: the position of each token within its
  *     segment; the ids of a segment of L tokens must be a permutation of 0..L-1.  Anything else
- *     sets H3ATTN_ERR_POSITIONS in the status word and NaN-fills the outputs (checked on the device).
+ *     sets H3ATTN_ERR_POSITIONS in the status word and NaN-fills that segment's outputs (checked on
+ *     the device).
  * With pos_ids[t] = t - (start of t's segment) the result is bitwise that of h3attn_fwd.  Other
  * arguments as for h3attn_fwd; out and lse must not overlap pos_ids either. */
 int h3attn_fwd_pos(const void* q, const void* k, const void* v, const int32_t* seg_ids, const int32_t* pos_ids,
@@ -158,9 +164,14 @@ size_t h3attn_bwd_workspace_bytes(int64_t tokens, int32_t heads);
  * Determinism: no atomics on data; every gradient row of q, k and v is a function of its own
  * segment's bytes only (the same bits alone or batched); dwq/dwk are sums over the whole batch.
  * Every product runs on fp16 MFMA with FP32 accumulation: P and dS are rounded to fp16 (as P is in
- * the forward), and the normed q, k and v, dO are converted to fp16, which is exact for magnitudes
+ * the forward), and the normed q, k and v are converted to fp16, which is exact for magnitudes
  * from 2^-17 to 65504 (below 2^-17 the error is at most 2^-25); a finite value beyond 65504 in any of
- * them sets H3ATTN_ERR_RANGE in the status word and NaN-fills the outputs.
+ * them sets H3ATTN_ERR_RANGE in the status word and NaN-fills its segment's outputs.  dO may take any
+ * bf16 value: each (segment, head) of dO is multiplied by the power of two 2^s that brings its
+ * largest |dO| into [4, 8) before the fp16 conversion (N(0,1) gradients get s = 0), and the
+ * gradients are multiplied by 2^-s on output, both exactly; within one (segment, head), elements
+ * more than 2^17 times smaller than the largest lose precision to fp16's subnormals, elements more
+ * than 2^27 times smaller are dropped -- a relative error far below the accuracy bound.
  * Outputs must not overlap any input, the workspace or each other. */
 int h3attn_bwd(const void* dout, const void* q, const void* k, const void* v, const float* lse,
                const int32_t* seg_ids, const void* wq, const void* wk, int64_t tokens, int32_t heads,
