@@ -47,7 +47,12 @@ def metrics(gpu_out, ref):
 
 
 def bits(t):
-    return t.detach().contiguous().view(torch.int16) if t.dtype in (torch.bfloat16, torch.float16) else t
+    """The tensor's bit patterns (so that NaN == NaN and -0 != +0 in a bitwise comparison)."""
+    if t.dtype in (torch.bfloat16, torch.float16):
+        return t.detach().contiguous().view(torch.int16)
+    if t.dtype == torch.float32:
+        return t.detach().contiguous().view(torch.int32)
+    return t
 
 
 def digest(t):
