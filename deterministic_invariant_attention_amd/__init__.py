@@ -27,11 +27,12 @@ H3ATTN_ERR_LAUNCH = 7
 H3ATTN_ERR_SEGMENTS = 8
 H3ATTN_ERR_RANGE = 9
 H3ATTN_ERR_POSITIONS = 10
+H3ATTN_ERR_SCRATCH = 11
 
 # every symbol the header declares
 EXPORTS = ("h3attn_version", "h3attn_strerror", "h3attn_workspace_bytes", "h3attn_qknorm", "h3attn_fwd",
            "h3attn_fwd_pos", "h3attn_fwd_ex", "h3attn_plan", "h3attn_prep_qkv", "h3attn_attend", "h3attn_status_read",
-           "h3attn_bwd_workspace_bytes", "h3attn_bwd", "h3attn_bwd_pos", "h3attn_bwd_ex")
+           "h3attn_bwd_workspace_bytes", "h3attn_bwd", "h3attn_bwd_pos", "h3attn_bwd_ex", "h3attn_fwd_noalloc")
 
 
 class H3AttnError(RuntimeError):
@@ -61,6 +62,7 @@ def load():
     lib.h3attn_fwd.argtypes = [P, P, P, P, P, P, I64, I32, I32, F, F, P, P, P, SZ, P]
     lib.h3attn_fwd_pos.argtypes = [P, P, P, P, P, P, P, I64, I32, I32, F, F, P, P, P, SZ, P]
     lib.h3attn_fwd_ex.argtypes = [P, P, P, P, P, P, P, I64, I32, I32, F, F, P, P, P, P, SZ, P]
+    lib.h3attn_fwd_noalloc.argtypes = [P, P, P, P, P, P, I64, I32, I32, F, F, P, P, P, P]
     lib.h3attn_plan.argtypes = [P, I64, I32, P, SZ, P]
     lib.h3attn_prep_qkv.argtypes = [P, P, P, P, P, I64, I32, I32, F, P, SZ, P]
     lib.h3attn_attend.argtypes = [P, P, I64, I32, I32, F, F, P, P, P, SZ, P]
@@ -71,7 +73,8 @@ def load():
     lib.h3attn_bwd_pos.argtypes = [P, P, P, P, P, P, P, P, P, I64, I32, I32, F, F, P, P, P, P, P, P, SZ, P]
     lib.h3attn_bwd_ex.argtypes = [P, P, P, P, P, P, P, P, P, P, I64, I32, I32, F, F, P, P, P, P, P, P, SZ, P]
     for name in ("h3attn_qknorm", "h3attn_fwd", "h3attn_fwd_pos", "h3attn_fwd_ex", "h3attn_plan", "h3attn_prep_qkv",
-                 "h3attn_attend", "h3attn_status_read", "h3attn_bwd", "h3attn_bwd_pos", "h3attn_bwd_ex"):
+                 "h3attn_attend", "h3attn_status_read", "h3attn_bwd", "h3attn_bwd_pos", "h3attn_bwd_ex",
+                 "h3attn_fwd_noalloc"):
         getattr(lib, name).restype = ctypes.c_int
     _lib = lib
     return lib
@@ -287,6 +290,32 @@ def _fwd(q, k, v, seg_ids, pos_ids, wq, wk, eps, scale, out, lse, workspace_buf,
         if check_status and T > 0:
             _status_or_raise(ws, st, "h3attn_fwd")
     return (out, lse, o32) if ex else (out, lse)
+
+
+def h3attn_fwd_noalloc(q, k, v, seg_ids, wq, wk, out, lse=None, status=None, eps: float = 1e-6,
+                       scale: float | None = None, stream=None):
+    """h3attn_fwd on the library's static scratch: allocates nothing (out, and lse / status when
+    wanted, are the caller's).  status: optional int32 [1] device tensor receiving the call's
+    data-error code.  Sizes whose workspace would exceed 256 MiB raise H3ATTN_ERR_SCRATCH."""
+    a = _Args("h3attn_fwd_noalloc", q)
+    T, H, D = a.T, a.H, a.D
+    for t, n in ((k, "k"), (v, "v"), (out, "out")):
+        if t is None:
+            raise H3AttnError(H3ATTN_ERR_NULL, f"h3attn_fwd_noalloc: {n} is required")
+        a.want(t, n, torch.bfloat16, (T, H, D))
+    _tok(a, _int32(seg_ids, "seg_ids"), "seg_ids")
+    a.want(wq, "wq", torch.bfloat16, (D,))
+    a.want(wk, "wk", torch.bfloat16, (D,))
+    a.want(lse, "lse", torch.float32, (T, H))
+    a.want(status, "status", torch.int32, (1,))
+    dev = a.device()
+    scale = D ** -0.5 if scale is None else scale
+    with torch.cuda.device(dev):
+        rc = load().h3attn_fwd_noalloc(_ptr(q), _ptr(k), _ptr(v), _ptr(seg_ids), _ptr(wq), _ptr(wk), T, H, D,
+                                       float(eps), float(scale), _ptr(out), _ptr(lse), _ptr(status),
+                                       _stream(stream, dev))
+    _check(rc, "h3attn_fwd_noalloc")
+    return out
 
 
 def h3attn_plan(seg_ids, heads: int, workspace_buf, stream=None):

@@ -6,6 +6,8 @@
 #include <stddef.h>
 #include <stdint.h>
 
+#include "h3attn.h"
+
 namespace h3 {
 
 constexpr int HD = 128;  // head dim (fixed by the H3 node: 128-wide heads)
@@ -55,6 +57,16 @@ __host__ __device__ inline WsLayout ws_layout(int64_t T, int32_t H) {
   w.segflag = w.tok2seg + align256((size_t)T * 4);
   w.total = w.segflag + align256((size_t)T * 4);
   return w;
+}
+
+constexpr int32_t STATUS_POS_BIT = 4;  // position ids are not a permutation of 0..L-1 in some segment
+
+// The status code of a status word (the H3ATTN_ERR_* data errors, in this order of precedence).
+__host__ __device__ inline int32_t status_code(int32_t bits) {
+  return (bits & STATUS_SEG_BIT)     ? H3ATTN_ERR_SEGMENTS
+         : (bits & STATUS_POS_BIT)   ? H3ATTN_ERR_POSITIONS
+         : (bits & STATUS_RANGE_BIT) ? H3ATTN_ERR_RANGE
+                                     : H3ATTN_OK;
 }
 
 // Mark segment sg as unusable (per-segment fail-closed; the caller also sets the status bit).

@@ -26,9 +26,10 @@ hipError_t launch_order(const int32_t* pos, int64_t T, void* ws, const int32_t* 
 
 // Attention over the planned work items.  Queries: the staged normed Q when normed is true, else
 // the caller's q (token-major).  lse and o32 (the output before its bf16 rounding, fp32) are
-// optional.  grid_cap: most workgroups to launch (persistent grid).
+// optional, and so is status_out (device int32: receives the call's data-error code).  grid_cap:
+// most workgroups to launch (persistent grid).
 hipError_t launch_attend(const void* q, bool normed, int64_t T, int32_t H, float scale, void* out, float* lse,
-                         float* o32, void* ws, int grid_cap, hipStream_t stream);
+                         float* o32, int32_t* status_out, void* ws, int grid_cap, hipStream_t stream);
 
 // Backward: segment decode with 128-token tiles into the backward workspace.
 hipError_t launch_plan_bwd(const int32_t* seg, int64_t T, void* ws, int32_t H, hipStream_t stream);

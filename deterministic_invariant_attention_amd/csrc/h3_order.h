@@ -14,8 +14,6 @@
 
 namespace h3 {
 
-constexpr int32_t STATUS_POS_BIT = 4;  // position ids are not a permutation of 0..L-1 in some segment
-
 struct OrderLayout {
   size_t slot, inv, total;
 };

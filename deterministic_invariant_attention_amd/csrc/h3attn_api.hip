@@ -50,6 +50,36 @@ int device_info(DeviceInfo* out) {
   return H3ATTN_OK;
 }
 
+// The workspace of h3attn_fwd_noalloc, for callers that cannot allocate: a fixed array in device
+// memory that every GPU the library runs on holds until the process ends.  Host code never uses
+// the array's name as an address (on the host it is only a stand-in for the symbol): the device
+// address comes from hipGetSymbolAddress, taken once per device with that device current.
+constexpr size_t kScratchBytes = (size_t)256 << 20;
+static __device__ __attribute__((aligned(256))) unsigned char scratch[kScratchBytes];
+
+std::once_flag g_scratch_once[kMaxDevices];
+void* g_scratch[kMaxDevices];
+
+// The current device's address of `scratch` (resolved on the first call on that device).
+int scratch_address(void** out) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) {
+    (void)hipGetLastError();
+    return H3ATTN_ERR_DEVICE;
+  }
+  std::call_once(g_scratch_once[dev], [dev] {
+    void* p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess) {
+      (void)hipGetLastError();
+      p = nullptr;
+    }
+    g_scratch[dev] = p;
+  });
+  if (!g_scratch[dev]) return H3ATTN_ERR_LAUNCH;
+  *out = g_scratch[dev];
+  return H3ATTN_OK;
+}
+
 bool aligned(const void* p, size_t a) { return ((uintptr_t)p % a) == 0; }
 
 bool overlap(const void* a, size_t na, const void* b, size_t nb) {
@@ -97,6 +127,8 @@ const char* h3attn_strerror(int status) {
     case H3ATTN_ERR_SEGMENTS: return "segment ids decrease (device status)";
     case H3ATTN_ERR_RANGE: return "a finite value beyond 65504 cannot enter an fp16 product (device status)";
     case H3ATTN_ERR_POSITIONS: return "position ids are not a permutation of 0..L-1 in some segment (device status)";
+    case H3ATTN_ERR_SCRATCH:
+      return "h3attn_workspace_bytes(tokens, heads) exceeds the 256 MiB static scratch of h3attn_fwd_noalloc";
     default: return "unknown status";
   }
 }
@@ -199,7 +231,8 @@ int h3attn_attend(const void* q, const void* wq, int64_t tokens, int32_t heads, 
   DeviceInfo di;
   if ((rc = device_info(&di))) return rc;
   return launch_status(
-      launch_attend(q, wq != nullptr, tokens, heads, scale, out, lse, nullptr, workspace, di.cus, (hipStream_t)stream));
+      launch_attend(q, wq != nullptr, tokens, heads, scale, out, lse, nullptr, nullptr, workspace, di.cus,
+                    (hipStream_t)stream));
 }
 
 // The forward; pos_ids NULL walks keys in packed order, else in position order; o32 (optional)
@@ -207,7 +240,7 @@ int h3attn_attend(const void* q, const void* wq, int64_t tokens, int32_t heads, 
 static int fwd_impl(const void* q, const void* k, const void* v, const int32_t* seg_ids, const int32_t* pos_ids,
                     bool ordered, const void* wq, const void* wk, int64_t tokens, int32_t heads, int32_t head_dim,
                     float eps, float scale, void* out, float* lse, float* o32, void* workspace,
-                    size_t workspace_bytes, void* stream) {
+                    size_t workspace_bytes, void* stream, int32_t* status_out = nullptr) {
   int rc = check_shape(tokens, heads, head_dim);
   if (rc) return rc;
   if ((wq == nullptr) != (wk == nullptr)) return H3ATTN_ERR_NULL;
@@ -253,7 +286,8 @@ static int fwd_impl(const void* q, const void* k, const void* v, const int32_t* 
                                                   slot, (int32_t*)(base + ol.inv), st))))
     return rc;
   if ((rc = launch_status(launch_prep_qkv(q, k, v, wq, wk, tokens, heads, eps, workspace, slot, st)))) return rc;
-  return launch_status(launch_attend(q, wq != nullptr, tokens, heads, scale, out, lse, o32, workspace, di.cus, st));
+  return launch_status(
+      launch_attend(q, wq != nullptr, tokens, heads, scale, out, lse, o32, status_out, workspace, di.cus, st));
 }
 
 int h3attn_fwd(const void* q, const void* k, const void* v, const int32_t* seg_ids, const void* wq, const void* wk,
@@ -276,6 +310,34 @@ int h3attn_fwd_ex(const void* q, const void* k, const void* v, const int32_t* se
                   void* stream) {
   return fwd_impl(q, k, v, seg_ids, pos_ids, pos_ids != nullptr, wq, wk, tokens, heads, head_dim, eps, scale, out, lse,
                   o32, workspace, workspace_bytes, stream);
+}
+
+// h3attn_fwd on the library's static scratch instead of a caller workspace: no allocation at all.
+int h3attn_fwd_noalloc(const void* q, const void* k, const void* v, const int32_t* seg_ids, const void* wq,
+                       const void* wk, int64_t tokens, int32_t heads, int32_t head_dim, float eps, float scale,
+                       void* out, float* lse, int32_t* status, void* stream) {
+  int rc = check_shape(tokens, heads, head_dim);
+  if (rc) return rc;
+  if (h3attn_workspace_bytes(tokens, heads) > kScratchBytes) return H3ATTN_ERR_SCRATCH;
+  if (tokens == 0)  // no device work: only the scalar checks of h3attn_fwd
+    return fwd_impl(q, k, v, seg_ids, nullptr, false, wq, wk, tokens, heads, head_dim, eps, scale, out, lse, nullptr,
+                    nullptr, 0, stream);
+  if (!q || !k || !v || !seg_ids || !out) return H3ATTN_ERR_NULL;
+  if (status) {
+    if (!aligned(status, 4)) return H3ATTN_ERR_ALIGN;
+    const size_t n = tensor_bytes(tokens, heads);
+    const void* bufs[] = {q, k, v, seg_ids, wq, wk, out, lse};
+    const size_t sz[] = {n, n, n, (size_t)tokens * 4, (size_t)HD * 2, (size_t)HD * 2, n, (size_t)tokens * heads * 4};
+    for (int i = 0; i < 8; i++)
+      if (overlap(status, 4, bufs[i], sz[i])) return H3ATTN_ERR_ALIAS;
+  }
+  DeviceInfo di;
+  if ((rc = device_info(&di))) return rc;
+  void* ws = nullptr;
+  if ((rc = scratch_address(&ws))) return rc;
+  if (status && overlap(status, 4, ws, kScratchBytes)) return H3ATTN_ERR_ALIAS;
+  return fwd_impl(q, k, v, seg_ids, nullptr, false, wq, wk, tokens, heads, head_dim, eps, scale, out, lse, nullptr, ws,
+                  kScratchBytes, stream, status);
 }
 
 // Large enough for both h3attn_bwd and h3attn_bwd_pos.
@@ -377,10 +439,7 @@ int h3attn_status_read(const void* workspace, int32_t* device_status, void* stre
     (void)hipGetLastError();
     return H3ATTN_ERR_LAUNCH;
   }
-  *device_status = (bits & STATUS_SEG_BIT)     ? H3ATTN_ERR_SEGMENTS
-                   : (bits & STATUS_POS_BIT)   ? H3ATTN_ERR_POSITIONS
-                   : (bits & STATUS_RANGE_BIT) ? H3ATTN_ERR_RANGE
-                                               : H3ATTN_OK;
+  *device_status = status_code(bits);
   return H3ATTN_OK;
 }
 

@@ -150,6 +150,7 @@ struct AttnParams {
   uint16_t* out;
   float* lse;
   float* o32;  // optional: the output before its bf16 rounding, fp32 token-major
+  int32_t* status_out;  // optional: receives the call's data-error code (H3ATTN_OK or H3ATTN_ERR_*)
   const WsHeader* hdr;
   const int32_t* segtab;
   const int32_t* items;
@@ -221,6 +222,8 @@ __global__ __launch_bounds__(64 * NWAVES, 1) void k_attn_fwd(AttnParams p) {
   const int64_t T = p.T;
   const int H = p.H;
 
+  // Every kernel that records data errors ran before this one on the stream: the word is final.
+  if (p.status_out && blockIdx.x == 0 && tid == 0) *p.status_out = status_code(p.hdr->status);
   if (p.hdr->status & STATUS_SEG_BIT) {
     // The segment ids decrease, so no segmentation exists: make the whole result unmistakably invalid.
     const int64_t n16 = T * H * HD / 8;
@@ -440,7 +443,7 @@ __global__ __launch_bounds__(64 * NWAVES, 1) void k_attn_fwd(AttnParams p) {
 }
 
 hipError_t launch_attend(const void* q, bool normed, int64_t T, int32_t H, float scale, void* out, float* lse,
-                         float* o32, void* ws, int grid_cap, hipStream_t stream) {
+                         float* o32, int32_t* status_out, void* ws, int grid_cap, hipStream_t stream) {
   const WsLayout Lw = ws_layout(T, H);
   char* base = (char*)ws;
   AttnParams p;
@@ -452,6 +455,7 @@ hipError_t launch_attend(const void* q, bool normed, int64_t T, int32_t H, float
   p.out = (uint16_t*)out;
   p.lse = lse;
   p.o32 = o32;
+  p.status_out = status_out;
   p.hdr = (const WsHeader*)base;
   p.segtab = (const int32_t*)(base + Lw.segtab);
   p.items = (const int32_t*)(base + Lw.items);

@@ -72,7 +72,8 @@ enum {
   H3ATTN_ERR_LAUNCH = 7,    /* the HIP runtime rejected a launch */
   H3ATTN_ERR_SEGMENTS = 8,  /* device status: segment ids decrease somewhere */
   H3ATTN_ERR_RANGE = 9,     /* device status: a finite value > 65504 cannot enter an fp16 product (its segment is NaN) */
-  H3ATTN_ERR_POSITIONS = 10 /* device status: position ids are not a permutation of 0..L-1 in a segment (NaN there) */
+  H3ATTN_ERR_POSITIONS = 10, /* device status: position ids are not a permutation of 0..L-1 in a segment (NaN there) */
+  H3ATTN_ERR_SCRATCH = 11    /* h3attn_fwd_noalloc: the workspace would exceed its 256 MiB static scratch */
 };
 
 /* H3ATTN_VERSION of the loaded library. */
@@ -130,6 +131,23 @@ int h3attn_fwd_ex(const void* q, const void* k, const void* v, const int32_t* se
                   const void* wq, const void* wk, int64_t tokens, int32_t heads, int32_t head_dim, float eps,
                   float scale, void* out, float* lse, float* o32, void* workspace, size_t workspace_bytes,
                   void* stream);
+
+/* h3attn_fwd for callers that cannot allocate device memory (code under HIP graph capture, tight
+ * serving loops, harnesses that forbid allocation): it takes no workspace and calls no allocating
+ * routine, running on a static scratch array of 256 MiB inside the library instead (each GPU the
+ * library runs on holds it until the process ends; the first call on a device resolves its
+ * address).  Accepts sizes with h3attn_workspace_bytes(tokens, heads) <= 256 MiB (e.g. 8349 tokens
+ * x 40 heads); larger ones return H3ATTN_ERR_SCRATCH before anything is enqueued.  Same kernels and
+ * bits as h3attn_fwd with the same arguments.  status: optional device int32 (4-byte aligned) that
+ * receives the call's data-error code (H3ATTN_OK, H3ATTN_ERR_SEGMENTS, H3ATTN_ERR_POSITIONS or
+ * H3ATTN_ERR_RANGE), since the scratch's status word is not the caller's to read; NULL = not
+ * reported (the NaN rows still mark failed segments).  Every call on one GPU uses the same scratch:
+ * calls that overlap in time on one GPU (other streams, other threads) race and must not be issued;
+ * calls in order on one stream are safe.  Everything the kernels need zeroed is cleared by the
+ * call itself, whatever an earlier call left. */
+int h3attn_fwd_noalloc(const void* q, const void* k, const void* v, const int32_t* seg_ids, const void* wq,
+                       const void* wk, int64_t tokens, int32_t heads, int32_t head_dim, float eps, float scale,
+                       void* out, float* lse, int32_t* status, void* stream);
 
 /* The three stages of h3attn_fwd, for callers that reuse one segment plan across layers (the 50
  * blocks of the model share the packed layout) or time the stages.  They must be enqueued in this

@@ -22,7 +22,7 @@ def declared_functions():
 def test_every_declared_symbol_is_exported():
     lib = h3.load()
     names = declared_functions()
-    assert len(names) == 15
+    assert len(names) == 16
     for n in names:
         assert hasattr(lib, n), f"{n} missing from libh3attn.so"
     assert sorted(h3.EXPORTS) == names
@@ -30,7 +30,7 @@ def test_every_declared_symbol_is_exported():
 
 def test_version_and_strerror():
     assert h3.h3attn_version() == 2
-    for code in range(11):
+    for code in range(12):
         assert h3.h3attn_strerror(code)
     assert h3.h3attn_strerror(999) == "unknown status"
 
@@ -238,3 +238,24 @@ def test_ex_argument_errors():
         assert fx() == h3.H3ATTN_ERR_DEVICE and fx(o32=None) == h3.H3ATTN_ERR_DEVICE
         assert fx(pos=A + 0xD000000) == h3.H3ATTN_ERR_DEVICE
         assert bx() == h3.H3ATTN_ERR_DEVICE and bx(o32=None) == h3.H3ATTN_ERR_DEVICE
+
+
+def test_fwd_noalloc_argument_errors():
+    """The allocation-free forward: sizes beyond its static scratch, NULLs and misaligned status are
+    refused before anything touches a device; without a GPU, valid arguments give ERR_DEVICE."""
+    import torch
+    lib = h3.load()
+
+    def na(T=16, H=2, q=A, out=A + 0x5000000, status=None, D=128):
+        return lib.h3attn_fwd_noalloc(q, A + 0x1000000, A + 0x2000000, A + 0x3000000, A + 0x4000000, A + 0x4001000,
+                                      T, H, D, 1e-6, 0.088, out, None, status, None)
+
+    assert na(T=0) == h3.H3ATTN_OK
+    assert na(T=16384, H=40) == h3.H3ATTN_ERR_SCRATCH       # 480 MiB of workspace > 256 MiB
+    assert h3.h3attn_workspace_bytes(8349, 40) <= 256 << 20   # the 8349 x 40 workload fits
+    assert na(D=64) == h3.H3ATTN_ERR_SHAPE
+    assert na(q=None) == h3.H3ATTN_ERR_NULL and na(out=None) == h3.H3ATTN_ERR_NULL
+    assert na(status=A + 0x7000002) == h3.H3ATTN_ERR_ALIGN
+    assert na(status=A + 0x5000000 + 64) == h3.H3ATTN_ERR_ALIAS   # status inside out
+    if not torch.cuda.is_available():
+        assert na() == h3.H3ATTN_ERR_DEVICE and na(status=A + 0x7000000) == h3.H3ATTN_ERR_DEVICE
