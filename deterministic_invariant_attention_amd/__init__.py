@@ -15,6 +15,7 @@ import torch
 _PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_PKG, "lib", "libh3attn.so")
 HEAD_DIM = 128
+ROPE_PAIRS = 48  # MM-RoPE: the rotated pairs of channels (96 of 128)
 
 H3ATTN_OK = 0
 H3ATTN_ERR_NULL = 1
@@ -61,7 +62,7 @@ def load():
     lib.h3attn_qknorm.argtypes = [P, P, P, I64, I32, I32, F, P]
     lib.h3attn_fwd.argtypes = [P, P, P, P, P, P, I64, I32, I32, F, F, P, P, P, SZ, P]
     lib.h3attn_fwd_pos.argtypes = [P, P, P, P, P, P, P, I64, I32, I32, F, F, P, P, P, SZ, P]
-    lib.h3attn_fwd_ex.argtypes = [P, P, P, P, P, P, P, I64, I32, I32, F, F, P, P, P, P, SZ, P]
+    lib.h3attn_fwd_ex.argtypes = [P, P, P, P, P, P, P, P, P, I64, I32, I32, F, F, P, P, P, P, SZ, P]
     lib.h3attn_fwd_noalloc.argtypes = [P, P, P, P, P, P, I64, I32, I32, F, F, P, P, P, P]
     lib.h3attn_plan.argtypes = [P, I64, I32, P, SZ, P]
     lib.h3attn_prep_qkv.argtypes = [P, P, P, P, P, I64, I32, I32, F, P, SZ, P]
@@ -71,7 +72,7 @@ def load():
     lib.h3attn_bwd_workspace_bytes.restype = SZ
     lib.h3attn_bwd.argtypes = [P, P, P, P, P, P, P, P, I64, I32, I32, F, F, P, P, P, P, P, P, SZ, P]
     lib.h3attn_bwd_pos.argtypes = [P, P, P, P, P, P, P, P, P, I64, I32, I32, F, F, P, P, P, P, P, P, SZ, P]
-    lib.h3attn_bwd_ex.argtypes = [P, P, P, P, P, P, P, P, P, P, I64, I32, I32, F, F, P, P, P, P, P, P, SZ, P]
+    lib.h3attn_bwd_ex.argtypes = [P, P, P, P, P, P, P, P, P, P, P, P, I64, I32, I32, F, F, P, P, P, P, P, P, SZ, P]
     for name in ("h3attn_qknorm", "h3attn_fwd", "h3attn_fwd_pos", "h3attn_fwd_ex", "h3attn_plan", "h3attn_prep_qkv",
                  "h3attn_attend", "h3attn_status_read", "h3attn_bwd", "h3attn_bwd_pos", "h3attn_bwd_ex",
                  "h3attn_fwd_noalloc"):
@@ -236,16 +237,28 @@ def h3attn_fwd_pos(q, k, v, seg_ids, pos_ids, wq=None, wk=None, eps: float = 1e-
 
 def h3attn_fwd_ex(q, k, v, seg_ids, pos_ids=None, wq=None, wk=None, eps: float = 1e-6, scale: float | None = None,
                   out=None, lse=None, o32=None, workspace_buf=None, stream=None, want_lse: bool = False,
-                  want_o32: bool = False, check_status: bool = False):
-    """The forward with every option: position order when pos_ids is given, and the fp32 output
-    before its bf16 rounding (o32, for h3attn_bwd_ex) when asked.  Returns (out, lse, o32)."""
+                  want_o32: bool = False, check_status: bool = False, rope_cos=None, rope_sin=None):
+    """The forward with every option: position order when pos_ids is given, the fp32 output before
+    its bf16 rounding (o32, for h3attn_bwd_ex) when asked, and the MM-RoPE node on the normed q and k
+    when rope tables are given (rope_cos, rope_sin: float32 [T, 48]; with wq/wk only).
+    Returns (out, lse, o32)."""
     return _fwd(q, k, v, seg_ids, None if pos_ids is None else _int32(pos_ids, "pos_ids"), wq, wk, eps, scale,
                 out, lse, workspace_buf, stream, want_lse, o32=o32, want_o32=want_o32, ex=True,
-                check_status=check_status)
+                check_status=check_status, rope=(rope_cos, rope_sin))
+
+
+def _rope(a, rope):
+    """The two rope tables (both or neither), float32 [T, 48]."""
+    rc, rs = rope
+    if (rc is None) != (rs is None):
+        raise H3AttnError(H3ATTN_ERR_NULL, f"{a.where}: give both rope tables or neither")
+    a.want(rc, "rope_cos", torch.float32, (a.T, ROPE_PAIRS))
+    a.want(rs, "rope_sin", torch.float32, (a.T, ROPE_PAIRS))
+    return rc, rs
 
 
 def _fwd(q, k, v, seg_ids, pos_ids, wq, wk, eps, scale, out, lse, workspace_buf, stream, want_lse, o32=None,
-         want_o32=False, ex=False, check_status=False):
+         want_o32=False, ex=False, check_status=False, rope=(None, None)):
     a = _Args("h3attn_fwd", q)
     T, H, D = a.T, a.H, a.D
     for t, n in ((k, "k"), (v, "v")):
@@ -259,6 +272,7 @@ def _fwd(q, k, v, seg_ids, pos_ids, wq, wk, eps, scale, out, lse, workspace_buf,
     a.want(out, "out", torch.bfloat16, (T, H, D))
     a.want(lse, "lse", torch.float32, (T, H))
     a.want(o32, "o32", torch.float32, (T, H, D))
+    rc_, rs_ = _rope(a, rope)
     _ws(a, workspace_buf, h3attn_workspace_bytes(T, H))
     dev = a.device()
     scale = D ** -0.5 if scale is None else scale
@@ -274,9 +288,9 @@ def _fwd(q, k, v, seg_ids, pos_ids, wq, wk, eps, scale, out, lse, workspace_buf,
         ws = workspace(T, H, dev) if workspace_buf is None else workspace_buf
         h = st.cuda_stream
         if ex:
-            rc = load().h3attn_fwd_ex(_ptr(q), _ptr(k), _ptr(v), _ptr(seg_ids), _ptr(pos_ids), _ptr(wq), _ptr(wk), T,
-                                      H, D, float(eps), float(scale), _ptr(out), _ptr(lse), _ptr(o32), _ptr(ws),
-                                      ws.numel(), h)
+            rc = load().h3attn_fwd_ex(_ptr(q), _ptr(k), _ptr(v), _ptr(seg_ids), _ptr(pos_ids), _ptr(wq), _ptr(wk),
+                                      _ptr(rc_), _ptr(rs_), T, H, D, float(eps), float(scale), _ptr(out), _ptr(lse),
+                                      _ptr(o32), _ptr(ws), ws.numel(), h)
             _check(rc, "h3attn_fwd_ex")
         elif pos_ids is None:
             rc = load().h3attn_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(seg_ids), _ptr(wq), _ptr(wk), T, H, D, float(eps),
@@ -401,15 +415,17 @@ def h3attn_bwd_pos(dout, q, k, v, lse, seg_ids, pos_ids, wq=None, wk=None, eps: 
 
 def h3attn_bwd_ex(dout, q, k, v, lse, seg_ids, pos_ids=None, o32=None, wq=None, wk=None, eps: float = 1e-6,
                   scale: float | None = None, dq=None, dk=None, dv=None, dwq=None, dwk=None, workspace_buf=None,
-                  stream=None, check_status: bool = False):
+                  stream=None, check_status: bool = False, rope_cos=None, rope_sin=None):
     """The backward with every option: position order when pos_ids is given; D = dO . O from the
-    forward's o32 (h3attn_fwd_ex) when given, else recomputed.  Returns (dq, dk, dv, dwq, dwk)."""
+    forward's o32 (h3attn_fwd_ex) when given, else recomputed; the rope tables given to the forward.
+    Returns (dq, dk, dv, dwq, dwk)."""
     return _bwd(dout, q, k, v, lse, seg_ids, None if pos_ids is None else _int32(pos_ids, "pos_ids"), wq, wk, eps,
-                scale, dq, dk, dv, dwq, dwk, workspace_buf, stream, o32=o32, ex=True, check_status=check_status)
+                scale, dq, dk, dv, dwq, dwk, workspace_buf, stream, o32=o32, ex=True, check_status=check_status,
+                rope=(rope_cos, rope_sin))
 
 
 def _bwd(dout, q, k, v, lse, seg_ids, pos_ids, wq, wk, eps, scale, dq, dk, dv, dwq, dwk, workspace_buf, stream,
-         o32=None, ex=False, check_status=False):
+         o32=None, ex=False, check_status=False, rope=(None, None)):
     a = _Args("h3attn_bwd", q)
     T, H, D = a.T, a.H, a.D
     for t, n in ((dout, "dout"), (k, "k"), (v, "v")):
@@ -428,6 +444,7 @@ def _bwd(dout, q, k, v, lse, seg_ids, pos_ids, wq, wk, eps, scale, dq, dk, dv, d
         a.want(t, n, torch.bfloat16, (T, H, D))
     a.want(dwq, "dwq", torch.float32, (D,))
     a.want(dwk, "dwk", torch.float32, (D,))
+    rc_, rs_ = _rope(a, rope)
     _ws(a, workspace_buf, h3attn_bwd_workspace_bytes(T, H))
     dev = a.device()
     scale = D ** -0.5 if scale is None else scale
@@ -443,8 +460,9 @@ def _bwd(dout, q, k, v, lse, seg_ids, pos_ids, wq, wk, eps, scale, dq, dk, dv, d
         h = st.cuda_stream
         if ex:
             rc = load().h3attn_bwd_ex(_ptr(dout), _ptr(q), _ptr(k), _ptr(v), _ptr(lse), _ptr(o32), _ptr(seg_ids),
-                                      _ptr(pos_ids), _ptr(wq), _ptr(wk), T, H, D, float(eps), float(scale), _ptr(dq),
-                                      _ptr(dk), _ptr(dv), _ptr(dwq), _ptr(dwk), _ptr(ws), ws.numel(), h)
+                                      _ptr(pos_ids), _ptr(wq), _ptr(wk), _ptr(rc_), _ptr(rs_), T, H, D, float(eps),
+                                      float(scale), _ptr(dq), _ptr(dk), _ptr(dv), _ptr(dwq), _ptr(dwk), _ptr(ws),
+                                      ws.numel(), h)
             _check(rc, "h3attn_bwd_ex")
         elif pos_ids is None:
             rc = load().h3attn_bwd(_ptr(dout), _ptr(q), _ptr(k), _ptr(v), _ptr(lse), _ptr(seg_ids), _ptr(wq),

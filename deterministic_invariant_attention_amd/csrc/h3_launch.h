@@ -15,9 +15,11 @@ hipError_t launch_qknorm(const void* x, const void* w, void* y, int64_t T, int32
 
 // Q -> normed bf16 Q (only with wq; head-major, packed token order), K -> normed bf16 K (or a copy
 // when wk is NULL) and V -> fp16, both head-major at staged row slot[t] (position order) or, with
-// slot NULL, at row t; all into the workspace.
+// slot NULL, at row t; all into the workspace.  With rope tables (float32 [T][48], only with the
+// weights) the normed Q and K are rotated (MM-RoPE on 96 channels) and rounded again to bf16.
 hipError_t launch_prep_qkv(const void* q, const void* k, const void* v, const void* wq, const void* wk, int64_t T,
-                           int32_t H, float eps, void* ws, const int32_t* slot, hipStream_t stream);
+                           int32_t H, float eps, void* ws, const int32_t* slot, const float* rope_cos,
+                           const float* rope_sin, hipStream_t stream);
 
 // Position ids -> slot / inv maps of the ordering area, with the permutation check (STATUS_POS_BIT,
 // and the failing segments flagged in segflag).  Needs the plan's segment table and token map.
@@ -36,10 +38,11 @@ hipError_t launch_plan_bwd(const int32_t* seg, int64_t T, void* ws, int32_t H, h
 
 // Backward operand staging (normed q/k, v and dO in fp16, LSE in log2 units), at staged rows slot[t]
 // or, with slot NULL, at the token's own row.  With o32 (the forward's fp32 output) it also writes
-// D = dO . O per row, and the dq kernel then skips its first pass.
+// D = dO . O per row, and the dq kernel then skips its first pass.  Rope tables as for
+// launch_prep_qkv.
 hipError_t launch_bwd_prep(const void* q, const void* k, const void* v, const void* dout, const float* lse,
                            const float* o32, const void* wq, const void* wk, int64_t T, int32_t H, float eps, void* ws,
-                           const int32_t* slot, hipStream_t stream);
+                           const int32_t* slot, const float* rope_cos, const float* rope_sin, hipStream_t stream);
 
 // Backward attention on the staged operands: dq with D, then dk/dv; with norm weights, the norm
 // backward (16-row weight-gradient partials in staged order) and the fixed-order reduction of the
@@ -47,6 +50,7 @@ hipError_t launch_bwd_prep(const void* q, const void* k, const void* v, const vo
 // staged row to its token (position order) or is NULL.
 hipError_t launch_bwd(const void* q, const void* k, const void* wq, const void* wk, int64_t T, int32_t H, float eps,
                       float scale, void* dq, void* dk, void* dv, float* dwq, float* dwk, void* ws, const int32_t* inv,
-                      bool delta_ready, int grid_cap, hipStream_t stream);
+                      bool delta_ready, const float* rope_cos, const float* rope_sin, int grid_cap,
+                      hipStream_t stream);
 
 }  // namespace h3

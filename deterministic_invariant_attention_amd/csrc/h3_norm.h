@@ -82,4 +82,39 @@ __device__ __forceinline__ u32x4 norm_chunk(const float* x, const float* w, doub
   return o;
 }
 
+// ---------------------------------------------------------------- MM-RoPE (partial)
+// The rope node between the norm and the attention rotates 96 of the 128 channels ("ws1_one_h3_block"
+// page, Bindings table: rope_q/rope_k; Tests: 96 of 128 channels).  Table-driven: per token, the
+// cosine and sine (float32) of each of the 48 rotated pairs; pair i is channels (2i, 2i+1):
+//   y_2i = x_2i cos_i - x_2i+1 sin_i,   y_2i+1 = x_2i sin_i + x_2i+1 cos_i,
+// channels 96..127 unchanged.  The products of a bf16 and a float32 value are exact in FP64, so each
+// output is one FP64 rounding of the exact expression, then one correct rounding to bf16 (the
+// node's output dtype): the same bits as any FP64 evaluation in this order.
+constexpr int ROPE_PAIRS = 48;
+constexpr int ROPE_CHUNKS = ROPE_PAIRS / 4;  // 8-channel chunks touched by the rotation (0..11)
+
+// Rotate one 8-channel chunk (4 pairs) of bf16 values x with the chunk's 4 cosines and sines.
+__device__ __forceinline__ u32x4 rope_chunk(const u32x4& x, const f32x4& cs, const f32x4& sn) {
+  u32x4 o;
+#pragma unroll
+  for (int j = 0; j < 4; j++) {
+    const double a = (double)bf16_lo(x[j]), b = (double)bf16_hi(x[j]);
+    const double c = (double)cs[j], s = (double)sn[j];
+    o[j] = f64x2_to_bf16x2_rne(a * c - b * s, a * s + b * c);
+  }
+  return o;
+}
+
+// The transposed rotation of one chunk of a gradient (FP64 in and out):
+//   dx_2i = dy_2i cos_i + dy_2i+1 sin_i,   dx_2i+1 = dy_2i+1 cos_i - dy_2i sin_i.
+__device__ __forceinline__ void rope_chunk_transpose(double* dy, const f32x4& cs, const f32x4& sn) {
+#pragma unroll
+  for (int j = 0; j < 4; j++) {
+    const double a = dy[2 * j], b = dy[2 * j + 1];
+    const double c = (double)cs[j], s = (double)sn[j];
+    dy[2 * j] = a * c + b * s;
+    dy[2 * j + 1] = b * c - a * s;
+  }
+}
+
 }  // namespace h3

@@ -219,7 +219,8 @@ int h3attn_prep_qkv(const void* q, const void* k, const void* v, const void* wq,
   if ((rc = check_prep(q, k, v, wq, wk, tokens, heads, eps, workspace, workspace_bytes))) return rc;
   DeviceInfo di;
   if ((rc = device_info(&di))) return rc;
-  return launch_status(launch_prep_qkv(q, k, v, wq, wk, tokens, heads, eps, workspace, nullptr, (hipStream_t)stream));
+  return launch_status(
+      launch_prep_qkv(q, k, v, wq, wk, tokens, heads, eps, workspace, nullptr, nullptr, nullptr, (hipStream_t)stream));
 }
 
 int h3attn_attend(const void* q, const void* wq, int64_t tokens, int32_t heads, int32_t head_dim, float eps,
@@ -237,13 +238,29 @@ int h3attn_attend(const void* q, const void* wq, int64_t tokens, int32_t heads, 
 
 // The forward; pos_ids NULL walks keys in packed order, else in position order; o32 (optional)
 // receives the output before its bf16 rounding.
+// MM-RoPE tables: both or neither, only with the norm weights (the fused q_norm -> rope chain), float32
+// [T][48], 16-byte aligned; no output and not the workspace may overlap them.
+static int check_rope(const float* rc, const float* rs, const void* wq, int64_t tokens, void* const* outs,
+                      const size_t* out_n, int nout) {
+  if ((rc == nullptr) != (rs == nullptr)) return H3ATTN_ERR_NULL;
+  if (!rc) return H3ATTN_OK;
+  if (!wq) return H3ATTN_ERR_NULL;
+  if (!aligned(rc, 16) || !aligned(rs, 16)) return H3ATTN_ERR_ALIGN;
+  const size_t nt = (size_t)tokens * 48 * 4;
+  for (int i = 0; i < nout; i++)
+    if (overlap(outs[i], out_n[i], rc, nt) || overlap(outs[i], out_n[i], rs, nt)) return H3ATTN_ERR_ALIAS;
+  return H3ATTN_OK;
+}
+
 static int fwd_impl(const void* q, const void* k, const void* v, const int32_t* seg_ids, const int32_t* pos_ids,
                     bool ordered, const void* wq, const void* wk, int64_t tokens, int32_t heads, int32_t head_dim,
                     float eps, float scale, void* out, float* lse, float* o32, void* workspace,
-                    size_t workspace_bytes, void* stream, int32_t* status_out = nullptr) {
+                    size_t workspace_bytes, void* stream, int32_t* status_out = nullptr,
+                    const float* rope_cos = nullptr, const float* rope_sin = nullptr) {
   int rc = check_shape(tokens, heads, head_dim);
   if (rc) return rc;
   if ((wq == nullptr) != (wk == nullptr)) return H3ATTN_ERR_NULL;
+  if ((rope_cos == nullptr) != (rope_sin == nullptr) || (rope_cos && !wq)) return H3ATTN_ERR_NULL;
   if (wq && (!(eps > 0.0f) || !std::isfinite(eps))) return H3ATTN_ERR_SHAPE;
   if (!(scale > 0.0f) || !std::isfinite(scale)) return H3ATTN_ERR_SHAPE;
   if (tokens == 0) return H3ATTN_OK;
@@ -274,6 +291,11 @@ static int fwd_impl(const void* q, const void* k, const void* v, const int32_t* 
       return H3ATTN_ERR_ALIAS;
     if (workspace_bytes < ol.total) return H3ATTN_ERR_WORKSPACE;
   }
+  {
+    void* outs[] = {out, lse, o32, workspace};
+    const size_t out_n[] = {n, nl, o32 ? 2 * n : 0, workspace_bytes};
+    if ((rc = check_rope(rope_cos, rope_sin, wq, tokens, outs, out_n, 4))) return rc;
+  }
   DeviceInfo di;
   if ((rc = device_info(&di))) return rc;
   hipStream_t st = (hipStream_t)stream;
@@ -285,7 +307,9 @@ static int fwd_impl(const void* q, const void* k, const void* v, const int32_t* 
                                                   (const int32_t*)(base + wl.tok2seg), (int32_t*)(base + wl.segflag),
                                                   slot, (int32_t*)(base + ol.inv), st))))
     return rc;
-  if ((rc = launch_status(launch_prep_qkv(q, k, v, wq, wk, tokens, heads, eps, workspace, slot, st)))) return rc;
+  if ((rc = launch_status(
+           launch_prep_qkv(q, k, v, wq, wk, tokens, heads, eps, workspace, slot, rope_cos, rope_sin, st))))
+    return rc;
   return launch_status(
       launch_attend(q, wq != nullptr, tokens, heads, scale, out, lse, o32, status_out, workspace, di.cus, st));
 }
@@ -305,11 +329,11 @@ int h3attn_fwd_pos(const void* q, const void* k, const void* v, const int32_t* s
 }
 
 int h3attn_fwd_ex(const void* q, const void* k, const void* v, const int32_t* seg_ids, const int32_t* pos_ids,
-                  const void* wq, const void* wk, int64_t tokens, int32_t heads, int32_t head_dim, float eps,
-                  float scale, void* out, float* lse, float* o32, void* workspace, size_t workspace_bytes,
-                  void* stream) {
+                  const void* wq, const void* wk, const float* rope_cos, const float* rope_sin, int64_t tokens,
+                  int32_t heads, int32_t head_dim, float eps, float scale, void* out, float* lse, float* o32,
+                  void* workspace, size_t workspace_bytes, void* stream) {
   return fwd_impl(q, k, v, seg_ids, pos_ids, pos_ids != nullptr, wq, wk, tokens, heads, head_dim, eps, scale, out, lse,
-                  o32, workspace, workspace_bytes, stream);
+                  o32, workspace, workspace_bytes, stream, nullptr, rope_cos, rope_sin);
 }
 
 // h3attn_fwd on the library's static scratch instead of a caller workspace: no allocation at all.
@@ -352,11 +376,13 @@ size_t h3attn_bwd_workspace_bytes(int64_t tokens, int32_t heads) {
 static int bwd_impl(const void* dout, const void* q, const void* k, const void* v, const float* lse, const float* o32,
                     const int32_t* seg_ids, const int32_t* pos_ids, bool ordered, const void* wq, const void* wk,
                     int64_t tokens, int32_t heads, int32_t head_dim, float eps, float scale, void* dq, void* dk,
-                    void* dv, float* dwq, float* dwk, void* workspace, size_t workspace_bytes, void* stream) {
+                    void* dv, float* dwq, float* dwk, void* workspace, size_t workspace_bytes, void* stream,
+                    const float* rope_cos = nullptr, const float* rope_sin = nullptr) {
   int rc = check_shape(tokens, heads, head_dim);
   if (rc) return rc;
   if (tokens + (tokens + BT - 1) / BT > (int64_t)INT32_MAX / heads) return H3ATTN_ERR_SHAPE;
   if ((wq == nullptr) != (wk == nullptr)) return H3ATTN_ERR_NULL;
+  if ((rope_cos == nullptr) != (rope_sin == nullptr) || (rope_cos && !wq)) return H3ATTN_ERR_NULL;
   if (wq && (!(eps > 0.0f) || !std::isfinite(eps))) return H3ATTN_ERR_SHAPE;
   if (!(scale > 0.0f) || !std::isfinite(scale)) return H3ATTN_ERR_SHAPE;
   if (tokens == 0) return H3ATTN_OK;
@@ -387,6 +413,11 @@ static int bwd_impl(const void* dout, const void* q, const void* k, const void* 
     for (int o2 = o + 1; o2 < 5; o2++)
       if (overlap(outs[o], out_n[o], outs[o2], out_n[o2])) return H3ATTN_ERR_ALIAS;
   }
+  {
+    void* outs6[] = {dq, dk, dv, dwq, dwk, workspace};
+    const size_t out_n6[] = {n, n, n, out_n[3], out_n[4], workspace_bytes};
+    if ((rc = check_rope(rope_cos, rope_sin, wq, tokens, outs6, out_n6, 6))) return rc;
+  }
   DeviceInfo di;
   if ((rc = device_info(&di))) return rc;
   hipStream_t st = (hipStream_t)stream;
@@ -399,10 +430,11 @@ static int bwd_impl(const void* dout, const void* q, const void* k, const void* 
                                                   (const int32_t*)(base + bl.tok2seg), (int32_t*)(base + bl.segflag),
                                                   slot, inv, st))))
     return rc;
-  if ((rc = launch_status(launch_bwd_prep(q, k, v, dout, lse, o32, wq, wk, tokens, heads, eps, workspace, slot, st))))
+  if ((rc = launch_status(launch_bwd_prep(q, k, v, dout, lse, o32, wq, wk, tokens, heads, eps, workspace, slot,
+                                          rope_cos, rope_sin, st))))
     return rc;
   return launch_status(launch_bwd(q, k, wq, wk, tokens, heads, eps, scale, dq, dk, dv, dwq, dwk, workspace, inv,
-                                  o32 != nullptr, di.cus, st));
+                                  o32 != nullptr, rope_cos, rope_sin, di.cus, st));
 }
 
 int h3attn_bwd(const void* dout, const void* q, const void* k, const void* v, const float* lse,
@@ -422,11 +454,12 @@ int h3attn_bwd_pos(const void* dout, const void* q, const void* k, const void* v
 }
 
 int h3attn_bwd_ex(const void* dout, const void* q, const void* k, const void* v, const float* lse, const float* o32,
-                  const int32_t* seg_ids, const int32_t* pos_ids, const void* wq, const void* wk, int64_t tokens,
-                  int32_t heads, int32_t head_dim, float eps, float scale, void* dq, void* dk, void* dv, float* dwq,
-                  float* dwk, void* workspace, size_t workspace_bytes, void* stream) {
+                  const int32_t* seg_ids, const int32_t* pos_ids, const void* wq, const void* wk,
+                  const float* rope_cos, const float* rope_sin, int64_t tokens, int32_t heads, int32_t head_dim,
+                  float eps, float scale, void* dq, void* dk, void* dv, float* dwq, float* dwk, void* workspace,
+                  size_t workspace_bytes, void* stream) {
   return bwd_impl(dout, q, k, v, lse, o32, seg_ids, pos_ids, pos_ids != nullptr, wq, wk, tokens, heads, head_dim, eps,
-                  scale, dq, dk, dv, dwq, dwk, workspace, workspace_bytes, stream);
+                  scale, dq, dk, dv, dwq, dwk, workspace, workspace_bytes, stream, rope_cos, rope_sin);
 }
 
 int h3attn_status_read(const void* workspace, int32_t* device_status, void* stream) {

@@ -566,6 +566,8 @@ struct NormBwdParams {
   const int32_t* inv;    // token of each staged row, or NULL
   const int32_t* tok2seg;
   const int32_t* segflag;  // rows of a flagged segment are NaN, written at their own token row
+  const float* rope_cos;   // optional MM-RoPE tables, float32 [T][48]: dy goes back through the
+  const float* rope_sin;   // transposed rotation before the norm backward
   const WsHeader* hdr;
   int64_t rows;          // T * H
   int32_t H;
@@ -594,7 +596,8 @@ __global__ __launch_bounds__(256) void k_bwd_norm(NormBwdParams p) {
     if (p.inv && !bad) xrow = (int64_t)p.inv[sl] * p.H + (row - sl * p.H);
   }
 
-  float x[8], dy[8], wf[8];
+  float x[8], wf[8];
+  double dy[8];  // the gradient with respect to the norm's output (through the rope when given)
   {
     u32x4 xv = {0, 0, 0, 0};
     f32x4 d0 = {0.0f, 0.0f, 0.0f, 0.0f}, d1 = d0;
@@ -606,12 +609,18 @@ __global__ __launch_bounds__(256) void k_bwd_norm(NormBwdParams p) {
     unpack8_bf16(xv, x);
     unpack8_bf16(*(const u32x4*)(p.w[which] + 8 * c), wf);
 #pragma unroll
-    for (int i = 0; i < 4; i++) dy[i] = d0[i], dy[4 + i] = d1[i];
+    for (int i = 0; i < 4; i++) dy[i] = (double)d0[i], dy[4 + i] = (double)d1[i];
+    if (p.rope_cos && valid && c < ROPE_CHUNKS) {
+      const int64_t tok = xrow / p.H;
+      const f32x4 cs = *(const f32x4*)(p.rope_cos + tok * ROPE_PAIRS + 4 * c);
+      const f32x4 sn = *(const f32x4*)(p.rope_sin + tok * ROPE_PAIRS + 4 * c);
+      rope_chunk_transpose(dy, cs, sn);
+    }
   }
   const double r = norm_rscale(row_total_16lanes(chunk_sumsq(x)), p.eps);
   double gx = 0.0;
 #pragma unroll
-  for (int i = 0; i < 8; i++) gx = __builtin_fma((double)wf[i] * (double)dy[i], (double)x[i], gx);
+  for (int i = 0; i < 8; i++) gx = __builtin_fma((double)wf[i] * dy[i], (double)x[i], gx);
   gx = gx + __shfl_xor(gx, 1, 64);
   gx = gx + __shfl_xor(gx, 2, 64);
   gx = gx + __shfl_xor(gx, 4, 64);
@@ -620,16 +629,16 @@ __global__ __launch_bounds__(256) void k_bwd_norm(NormBwdParams p) {
   u32x4 o;
 #pragma unroll
   for (int i = 0; i < 4; i++) {
-    o[i] = f64x2_to_bf16x2_rne(r * ((double)wf[2 * i] * (double)dy[2 * i]) - k3 * (double)x[2 * i],
-                               r * ((double)wf[2 * i + 1] * (double)dy[2 * i + 1]) - k3 * (double)x[2 * i + 1]);
+    o[i] = f64x2_to_bf16x2_rne(r * ((double)wf[2 * i] * dy[2 * i]) - k3 * (double)x[2 * i],
+                               r * ((double)wf[2 * i + 1] * dy[2 * i + 1]) - k3 * (double)x[2 * i + 1]);
   }
   if (bad) o = u32x4{0x7FC07FC0u, 0x7FC07FC0u, 0x7FC07FC0u, 0x7FC07FC0u};
   if (valid) *(u32x4*)(p.dx[which] + xrow * HD + 8 * c) = o;
   f32x4 t0, t1;
 #pragma unroll
   for (int i = 0; i < 4; i++) {
-    t0[i] = valid ? (float)((double)dy[i] * (double)x[i] * r) : 0.0f;
-    t1[i] = valid ? (float)((double)dy[4 + i] * (double)x[4 + i] * r) : 0.0f;
+    t0[i] = valid ? (float)(dy[i] * (double)x[i] * r) : 0.0f;
+    t1[i] = valid ? (float)(dy[4 + i] * (double)x[4 + i] * r) : 0.0f;
   }
   *(f32x4*)&red[tid >> 4][8 * c] = t0;
   *(f32x4*)&red[tid >> 4][8 * c + 4] = t1;
@@ -686,7 +695,8 @@ __global__ __launch_bounds__(2 * HD) void k_bwd_dw_final(const WsHeader* hdr, co
 
 hipError_t launch_bwd(const void* q, const void* k, const void* wq, const void* wk, int64_t T, int32_t H, float eps,
                       float scale, void* dq, void* dk, void* dv, float* dwq, float* dwk, void* ws,
-                      const int32_t* inv, bool delta_ready, int grid_cap, hipStream_t stream) {
+                      const int32_t* inv, bool delta_ready, const float* rope_cos, const float* rope_sin,
+                      int grid_cap, hipStream_t stream) {
   const BwdLayout Lw = bwd_layout(T, H);
   char* base = (char*)ws;
   BwdParams p;
@@ -743,6 +753,8 @@ hipError_t launch_bwd(const void* q, const void* k, const void* wq, const void* 
     np.inv = inv;
     np.tok2seg = (const int32_t*)(base + Lw.tok2seg);
     np.segflag = (const int32_t*)(base + Lw.segflag);
+    np.rope_cos = rope_cos;
+    np.rope_sin = rope_sin;
     np.hdr = (const WsHeader*)base;
     np.rows = T * H;
     np.H = H;

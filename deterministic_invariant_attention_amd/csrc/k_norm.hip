@@ -55,11 +55,24 @@ struct PrepParams {
   const int32_t* slot;  // staged row of each token (position order), or NULL for packed order
   const int32_t* tok2seg;
   int32_t* segflag;  // a segment with a value beyond fp16 is flagged (its outputs become NaN)
+  const float* rope_cos;  // optional MM-RoPE tables, float32 [T][48] (only with norm weights)
+  const float* rope_sin;
   WsHeader* hdr;
   int64_t T;
   int32_t H;
   float eps;
 };
+
+// The rope tables' entries for the lane's chunk (chunks 0..11 of token t); zeros elsewhere.
+__device__ __forceinline__ void rope_entries(const float* rc, const float* rs, int64_t t, int c, bool valid, f32x4& cs,
+                                             f32x4& sn) {
+  cs = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+  sn = cs;
+  if (rc && valid && c < ROPE_CHUNKS) {
+    cs = *(const f32x4*)(rc + t * ROPE_PAIRS + 4 * c);
+    sn = *(const f32x4*)(rs + t * ROPE_PAIRS + 4 * c);
+  }
+}
 
 // Rows are visited token-major (r = t*H + h) so the reads are contiguous; each row is written to
 // its head-major staged row.  Every load of the row precedes every store (the outputs live in
@@ -86,11 +99,16 @@ __global__ __launch_bounds__(256) void k_prep_qkv(PrepParams p) {
       kv = __builtin_nontemporal_load((const u32x4*)(p.k + src));
       vv = __builtin_nontemporal_load((const u32x4*)(p.v + src));
     }
+    f32x4 rcs, rsn;
+    rope_entries(p.rope_cos, p.rope_sin, t, c, valid, rcs, rsn);
+    const bool rot = p.rope_cos && c < ROPE_CHUNKS;  // this lane's chunk is rotated
     if (p.wq) {
-      const u32x4 qo = norm_16lane(qv, wqv, p.eps);
+      u32x4 qo = norm_16lane(qv, wqv, p.eps);
+      if (rot) qo = rope_chunk(qo, rcs, rsn);
       if (valid) st16(p.qhat + (h * T + t) * HD + c * 8, qo);
     }
-    const u32x4 ko = p.wk ? norm_16lane(kv, wkv, p.eps) : kv;
+    u32x4 ko = p.wk ? norm_16lane(kv, wkv, p.eps) : kv;
+    if (rot) ko = rope_chunk(ko, rcs, rsn);
 
     // V: bf16 -> fp16, exact for normal fp16 magnitudes; a finite |v| > 65504 would overflow.
     u32x4 vo;
@@ -134,6 +152,8 @@ struct BwdPrepParams {
   const int32_t* slot;  // staged row of each token (position order), or NULL for packed order
   const int32_t* tok2seg;  // segment of each token
   int32_t* segflag;        // a segment with a q^, k^ or v value beyond fp16 is flagged (NaN outputs)
+  const float* rope_cos;   // optional MM-RoPE tables, float32 [T][48]
+  const float* rope_sin;
   const uint32_t* dmax;    // per (segment, head): largest |dO| (bf16 magnitude bits)
   WsHeader* hdr;
   int64_t T;
@@ -242,8 +262,14 @@ __global__ __launch_bounds__(256) void k_bwd_prep(BwdPrepParams p) {
       }
       if (c == 0) lse = p.lse[row];
     }
-    const u32x4 qo = p.wq ? norm_16lane(qv, wqv, p.eps) : qv;
-    const u32x4 ko = p.wk ? norm_16lane(kv, wkv, p.eps) : kv;
+    u32x4 qo = p.wq ? norm_16lane(qv, wqv, p.eps) : qv;
+    u32x4 ko = p.wk ? norm_16lane(kv, wkv, p.eps) : kv;
+    if (p.rope_cos && c < ROPE_CHUNKS) {  // the rotated operands, bitwise those of the forward
+      f32x4 rcs, rsn;
+      rope_entries(p.rope_cos, p.rope_sin, t, c, valid, rcs, rsn);
+      qo = rope_chunk(qo, rcs, rsn);
+      ko = rope_chunk(ko, rcs, rsn);
+    }
     bool over = false;
     const u32x4 q16 = bf16_chunk_to_f16(qo, over);
     const u32x4 k16 = bf16_chunk_to_f16(ko, over);
@@ -293,7 +319,7 @@ static inline unsigned grid_for_rows(int64_t rows) { return (unsigned)((rows * 1
 
 hipError_t launch_bwd_prep(const void* q, const void* k, const void* v, const void* dout, const float* lse,
                            const float* o32, const void* wq, const void* wk, int64_t T, int32_t H, float eps, void* ws,
-                           const int32_t* slot, hipStream_t stream) {
+                           const int32_t* slot, const float* rope_cos, const float* rope_sin, hipStream_t stream) {
   const int64_t rows = T * H;
   if (rows == 0) return hipSuccess;
   const BwdLayout L = bwd_layout(T, H);
@@ -316,6 +342,8 @@ hipError_t launch_bwd_prep(const void* q, const void* k, const void* v, const vo
   p.slot = slot;
   p.tok2seg = (const int32_t*)(base + L.tok2seg);
   p.segflag = (int32_t*)(base + L.segflag);
+  p.rope_cos = rope_cos;
+  p.rope_sin = rope_sin;
   p.dmax = (const uint32_t*)(base + L.dmax);
   p.hdr = (WsHeader*)base;
   p.T = T;
@@ -338,7 +366,8 @@ hipError_t launch_qknorm(const void* x, const void* w, void* y, int64_t T, int32
 }
 
 hipError_t launch_prep_qkv(const void* q, const void* k, const void* v, const void* wq, const void* wk, int64_t T,
-                           int32_t H, float eps, void* ws, const int32_t* slot, hipStream_t stream) {
+                           int32_t H, float eps, void* ws, const int32_t* slot, const float* rope_cos,
+                           const float* rope_sin, hipStream_t stream) {
   const int64_t rows = T * H;
   if (rows == 0) return hipSuccess;
   const WsLayout L = ws_layout(T, H);
@@ -355,6 +384,8 @@ hipError_t launch_prep_qkv(const void* q, const void* k, const void* v, const vo
   p.slot = slot;
   p.tok2seg = (const int32_t*)(base + L.tok2seg);
   p.segflag = (int32_t*)(base + L.segflag);
+  p.rope_cos = rope_cos;
+  p.rope_sin = rope_sin;
   p.hdr = (WsHeader*)base;
   p.T = T;
   p.H = H;

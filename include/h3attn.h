@@ -59,7 +59,7 @@
 extern "C" {
 #endif
 
-#define H3ATTN_VERSION 2
+#define H3ATTN_VERSION 3
 
 enum {
   H3ATTN_OK = 0,
@@ -125,12 +125,22 @@ int h3attn_fwd_pos(const void* q, const void* k, const void* v, const int32_t* s
 /* The forward with every option: pos_ids NULL walks keys in packed order (h3attn_fwd), else in
  * position order (h3attn_fwd_pos); o32 (optional, fp32 [T, H, 128] device memory, 16-byte aligned)
  * receives each output element before its one bf16 rounding, for the backward's D = dO . O (see
- * h3attn_bwd_ex).  o32 must not overlap any input, out, lse or the workspace.  Everything else as
- * for h3attn_fwd; out, lse and o32 carry the same bits whatever the other options are. */
+ * h3attn_bwd_ex).  o32 must not overlap any input, out, lse or the workspace.
+ * rope_cos, rope_sin (optional, both or neither, only with wq/wk): the MM-RoPE node that the block
+ * runs between q_norm/k_norm and the attention ("ws1_one_h3_block + full-model qualification" page,
+ * Bindings table: rope_q, rope_k; Tests: MM-RoPE rotates 96 of 128 channels).  The pages give
+ * neither its axis split nor its frequencies, so the rotation is table-driven: float32 [T, 48]
+ * device arrays (16-byte aligned, token-major, packed token order) holding, for every token, the
+ * cosine and sine of the angle of each of the 48 rotated pairs -- the caller composes the three
+ * axes.  Pair i is channels (2i, 2i+1): y_2i = x_2i cos - x_2i+1 sin, y_2i+1 = x_2i sin +
+ * x_2i+1 cos; channels 96..127 pass through.  It acts on the normed bf16 q and k, in FP64 with one
+ * rounding back to bf16 (each node of the block emits bf16), before Q.K^T.  No output and not the
+ * workspace may overlap the tables.  Everything else as for h3attn_fwd; out, lse and o32 carry the
+ * same bits whatever pos_ids is; an identity table (cos 1, sin 0) gives the bits of no rope. */
 int h3attn_fwd_ex(const void* q, const void* k, const void* v, const int32_t* seg_ids, const int32_t* pos_ids,
-                  const void* wq, const void* wk, int64_t tokens, int32_t heads, int32_t head_dim, float eps,
-                  float scale, void* out, float* lse, float* o32, void* workspace, size_t workspace_bytes,
-                  void* stream);
+                  const void* wq, const void* wk, const float* rope_cos, const float* rope_sin, int64_t tokens,
+                  int32_t heads, int32_t head_dim, float eps, float scale, void* out, float* lse, float* o32,
+                  void* workspace, size_t workspace_bytes, void* stream);
 
 /* h3attn_fwd for callers that cannot allocate device memory (code under HIP graph capture, tight
  * serving loops, harnesses that forbid allocation): it takes no workspace and calls no allocating
@@ -216,11 +226,15 @@ int h3attn_bwd_pos(const void* dout, const void* q, const void* k, const void* v
  * only by the forward's fp16 rounding of P, unlike the bf16 output, whose rounding alone moves D
  * beyond the gradients' accuracy bound.  Results meet the same bound either way; they are
  * bitwise repeatable and batch-invariant for each choice, and the two choices differ in the last
- * bits.  o32 must not overlap an output or the workspace. */
+ * bits.  o32 must not overlap an output or the workspace.  rope_cos, rope_sin: the tables given
+ * to h3attn_fwd_ex (or NULL): the products use the rotated operands, and the gradient with respect
+ * to each rotated q or k goes back through the transposed rotation before the norm backward (the
+ * rope's rounding, like the norm's, is the identity for gradients). */
 int h3attn_bwd_ex(const void* dout, const void* q, const void* k, const void* v, const float* lse, const float* o32,
-                  const int32_t* seg_ids, const int32_t* pos_ids, const void* wq, const void* wk, int64_t tokens,
-                  int32_t heads, int32_t head_dim, float eps, float scale, void* dq, void* dk, void* dv, float* dwq,
-                  float* dwk, void* workspace, size_t workspace_bytes, void* stream);
+                  const int32_t* seg_ids, const int32_t* pos_ids, const void* wq, const void* wk,
+                  const float* rope_cos, const float* rope_sin, int64_t tokens, int32_t heads, int32_t head_dim,
+                  float eps, float scale, void* dq, void* dk, void* dv, float* dwq, float* dwk, void* workspace,
+                  size_t workspace_bytes, void* stream);
 
 /* Wait for `stream`, then copy the workspace's device status word to *device_status (host memory):
  * H3ATTN_OK, H3ATTN_ERR_SEGMENTS, H3ATTN_ERR_POSITIONS or H3ATTN_ERR_RANGE (in this order of

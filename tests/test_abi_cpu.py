@@ -29,7 +29,7 @@ def test_every_declared_symbol_is_exported():
 
 
 def test_version_and_strerror():
-    assert h3.h3attn_version() == 2
+    assert h3.h3attn_version() == 3
     for code in range(12):
         assert h3.h3attn_strerror(code)
     assert h3.h3attn_strerror(999) == "unknown status"
@@ -212,8 +212,8 @@ def test_ex_argument_errors():
     O32 = A + 0xE000000
     n = 16 * 2 * 128 * 2
 
-    def fx(pos=None, o32=O32, out=A + 0x5000000, lse=None, T=16):
-        return lib.h3attn_fwd_ex(A, A + 0x1000000, A + 0x2000000, A + 0x3000000, pos, A + 0x4000000, A + 0x4001000,
+    def fx(pos=None, o32=O32, out=A + 0x5000000, lse=None, T=16, rc=None, rs=None, wq=A + 0x4000000, wk=A + 0x4001000):
+        return lib.h3attn_fwd_ex(A, A + 0x1000000, A + 0x2000000, A + 0x3000000, pos, wq, wk, rc, rs,
                                  T, 2, 128, 1e-6, 0.088, out, lse, o32, A + 0x6000000, wsb, None)
 
     assert fx(T=0) == h3.H3ATTN_OK
@@ -225,18 +225,27 @@ def test_ex_argument_errors():
     assert fx(pos=A + 0xD000002) == h3.H3ATTN_ERR_ALIGN
     bwsb = h3.h3attn_bwd_workspace_bytes(16, 2)
 
-    def bx(o32=O32, pos=None, dq=A + 0x9000000):
+    def bx(o32=O32, pos=None, dq=A + 0x9000000, rc=None, rs=None):
         return lib.h3attn_bwd_ex(A + 0x7000000, A, A + 0x1000000, A + 0x2000000, A + 0x8000000, o32, A + 0x3000000,
-                                 pos, A + 0x4000000, A + 0x4001000, 16, 2, 128, 1e-6, 0.088, dq, A + 0xA000000,
+                                 pos, A + 0x4000000, A + 0x4001000, rc, rs, 16, 2, 128, 1e-6, 0.088, dq, A + 0xA000000,
                                  A + 0xB000000, A + 0xC000000, A + 0xC001000, A + 0x10000000, bwsb, None)
 
     assert bx(o32=O32 + 8) == h3.H3ATTN_ERR_ALIGN
     assert bx(dq=O32) == h3.H3ATTN_ERR_ALIAS                          # an output on o32
     assert bx(o32=A + 0x10000000 + 512) == h3.H3ATTN_ERR_ALIAS        # o32 inside the workspace
+    R = A + 0xF000000  # rope tables: float32 [16, 48] each
+    assert fx(rc=R) == h3.H3ATTN_ERR_NULL                             # one table only
+    assert fx(rc=R, rs=R + 4096, wq=None, wk=None) == h3.H3ATTN_ERR_NULL  # rope needs the norm weights
+    assert fx(rc=R + 4, rs=R + 4096) == h3.H3ATTN_ERR_ALIGN
+    assert fx(rc=R, rs=R + 4096, o32=R + 1024) == h3.H3ATTN_ERR_ALIAS  # an output on a table
+    assert bx(rc=R + 8, rs=R + 4096) == h3.H3ATTN_ERR_ALIGN
+    assert bx(rc=R, rs=R + 4096, dq=R + 2048) == h3.H3ATTN_ERR_ALIAS
     import torch
     if not torch.cuda.is_available():
         assert fx() == h3.H3ATTN_ERR_DEVICE and fx(o32=None) == h3.H3ATTN_ERR_DEVICE
         assert fx(pos=A + 0xD000000) == h3.H3ATTN_ERR_DEVICE
+        assert fx(rc=A + 0xF000000, rs=A + 0xF001000) == h3.H3ATTN_ERR_DEVICE
+        assert bx(rc=A + 0xF000000, rs=A + 0xF001000) == h3.H3ATTN_ERR_DEVICE
         assert bx() == h3.H3ATTN_ERR_DEVICE and bx(o32=None) == h3.H3ATTN_ERR_DEVICE
 
 

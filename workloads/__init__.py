@@ -128,6 +128,32 @@ def random_inputs(seg_lens, heads, seed=0, qk_scale=1.0, normed=True, w_scale=1.
     return make_inputs(wl, with_grad=with_grad)
 
 
+ROPE_PAIRS = 48  # MM-RoPE: 48 rotated pairs (96 of the 128 channels)
+
+
+def rope_tables(seg_lens, kind: str = "grid", seed: int = 0):
+    """float32 [T, 48] cosine and sine tables of the partial MM-RoPE, per token (packed order).
+
+    kind "grid": a synthetic 3-axis layout standing in for video tokens: each segment's tokens fill a
+    frames x 8 x 8 grid in order, pairs 0-15 take the frame index, 16-31 the row, 32-47 the column,
+    with angle = position * 10000^(-j/16) for the j-th pair of an axis.  kind "random": uniform
+    angles in [0, 2 pi).  kind "identity": cos 1, sin 0.  (The pages give neither the axis split nor
+    the frequencies; these are inputs, not part of the method.)"""
+    T = sum(seg_lens)
+    if kind == "identity":
+        return torch.ones(T, ROPE_PAIRS), torch.zeros(T, ROPE_PAIRS)
+    if kind == "random":
+        g = torch.Generator().manual_seed(seed)
+        ang = torch.rand(T, ROPE_PAIRS, generator=g, dtype=torch.float64) * (2 * torch.pi)
+    else:
+        pos = torch.cat([torch.arange(L, dtype=torch.float64) for L in seg_lens]) if T else torch.zeros(0)
+        f, rem = torch.div(pos, 64, rounding_mode="floor"), torch.remainder(pos, 64)
+        y, x = torch.div(rem, 8, rounding_mode="floor"), torch.remainder(rem, 8)
+        freq = 10000.0 ** (-torch.arange(16, dtype=torch.float64) / 16)
+        ang = torch.cat([f[:, None] * freq, y[:, None] * freq, x[:, None] * freq], 1)
+    return torch.cos(ang).float().contiguous(), torch.sin(ang).float().contiguous()
+
+
 def row_slices(w: Workload):
     """Token ranges [(t0, t1)] of each packed row of the workload."""
     out, t = [], 0
