@@ -63,6 +63,19 @@ constexpr int NKS = FROWS / 16;    // 16-key slices per tile
 constexpr int FTILE = FROWS * HD;  // 16-bit elements per LDS tile
 
 template <int NW>
+__device__ __forceinline__ void ftile_to_lds_o(const uint16_t* gtile, int valid, uint16_t* lds_tile, int wv,
+                                               const int* offs) {
+  static_assert(FROWS % (4 * NW) == 0, "whole 1 KB blocks per wave");
+  const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
+      (void*)gtile, (short)0, (valid < FROWS ? valid : FROWS) * 256, 0x00020000);
+  int wofs = wv * 4 * HD;
+  asm volatile("" : "+s"(wofs));
+#pragma unroll
+  for (int i = 0; i < FROWS / (4 * NW); i++)
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void*)(lds_tile + NW * i * 4 * HD + wofs), 16, offs[i], 0, 0, 0);
+}
+
+template <int NW>
 __device__ __forceinline__ void ftile_to_lds(const uint16_t* gtile, int valid, uint16_t* lds_tile, int wv,
                                              int lane_off) {
   static_assert(FROWS % (4 * NW) == 0, "whole 1 KB blocks per wave");
@@ -257,6 +270,14 @@ __global__ __launch_bounds__(64 * NWAVES, 1) void k_attn_fwd(AttnParams p) {
   // the loop's copies: each wave of a group issues a quarter of a tile
   const int k_lane_off4 = tile_lane_offset(false, wv & 3, lane);
   const int v_lane_off4 = tile_lane_offset(true, wv & 3, lane);
+  // the loop's copies: each wave copies one kind (K in the trailing group, V in the leading one);
+  // its six lane offsets are kept in registers of their own
+  int coffs[FROWS / 16];
+#pragma unroll
+  for (int i = 0; i < FROWS / 16; i++) {
+    coffs[i] = (grp ? k_lane_off4 : v_lane_off4) + i * 4096;
+    asm volatile("" : "+v"(coffs[i]));
+  }
   const int tr_row = 4 * hh + ((lane & 15) >> 2);
   const int tr_col = 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
   const float c = p.c;
@@ -329,15 +350,15 @@ __global__ __launch_bounds__(64 * NWAVES, 1) void k_attn_fwd(AttnParams p) {
       constexpr int MP = decltype(mp)::value;
       const int m = t >> 1;
       if (m + 1 < ntiles)
-        ftile_to_lds<4>(kbase + (int64_t)(m + 1) * FROWS * HD, L - (m + 1) * FROWS, lds + (1 - MP) * FTILE, wv & 3,
-                        k_lane_off4);
+        ftile_to_lds_o<4>(kbase + (int64_t)(m + 1) * FROWS * HD, L - (m + 1) * FROWS, lds + (1 - MP) * FTILE, wv & 3,
+                          coffs);
     };
     // leading waves, odd slot t = 2m+1: V(m) (one slot to land)
     auto issue_v = [&](int t, auto mp) {
       constexpr int MP = decltype(mp)::value;
       const int m = t >> 1;
       if (m < ntiles)
-        ftile_to_lds<4>(vbase + (int64_t)m * FROWS * HD, L - m * FROWS, lds + (2 + MP) * FTILE, wv & 3, v_lane_off4);
+        ftile_to_lds_o<4>(vbase + (int64_t)m * FROWS * HD, L - m * FROWS, lds + (2 + MP) * FTILE, wv & 3, coffs);
     };
 
     // Phase tau of this wave runs in slot t = tau + grp.  Even tau: G(k), k = tau/2 - 1 (scores of

@@ -3,9 +3,9 @@
 //
 // Packed layouts ("ws1_one_h3_block" page, Summary: several sequences share one token axis) are
 // described to the library by one id per token; a segment is a maximal run of equal ids, and ids
-// must not decrease.  The decode runs in one 1024-thread workgroup: three passes of block-wide
-// exclusive scans over tokens, then segments.  Its cost is T/1024 scan steps (with the ids of up to
-// 16384 tokens loaded up front), negligible next to the attention for the workloads served here.
+// must not decrease.  The decode runs in one 1024-thread workgroup: each thread walks a contiguous
+// run of tokens (then of segments), and one block-wide exclusive scan per pass places every run's
+// results, so the whole decode costs two scans and three barriers whatever T is.
 #include "h3_common.h"
 #include "h3_bwd.h"
 #include "h3_launch.h"
@@ -57,42 +57,32 @@ __global__ __launch_bounds__(1024) void k_plan(const int32_t* __restrict__ seg, 
   if (tid == 0) s_bad = 0;
   __syncthreads();
 
-  // pass 1: segment starts at every token whose id differs from its predecessor's.  Up to
-  // PRE * 1024 tokens, every id is loaded before the first scan, so the scans do not wait on memory
-  // one chunk at a time.
-  int nseg = 0, bad = 0;
-  auto chunk = [&](int64_t t, int32_t cur, int32_t prev) {
-    int flag = 0;
-    if (t < T) {
-      if (t == 0) {
-        flag = 1;
-      } else {
-        flag = cur != prev;
-        bad |= cur < prev;
-      }
+  // pass 1: segment starts at every token whose id differs from its predecessor's.  Each thread owns
+  // a contiguous run of ceil(T / 1024) tokens: it counts the starts in its run, one block-wide scan
+  // gives every run its first segment index, and a second walk over the run writes the starts and
+  // every token's segment.
+  const int64_t per = (T + 1023) / 1024;
+  const int64_t t0 = min(T, (int64_t)tid * per), t1 = min(T, t0 + per);
+  int cnt = 0, bad = 0;
+  {
+    int32_t prev = t0 > 0 ? seg[t0 - 1] : 0;
+    for (int64_t t = t0; t < t1; t++) {
+      const int32_t cur = seg[t];
+      cnt += (t == 0 || cur != prev) ? 1 : 0;
+      bad |= (t > 0 && cur < prev) ? 1 : 0;
+      prev = cur;
     }
-    int total;
-    const int pos = block_excl_scan(flag, lds_wave, total);
-    if (flag) segtab[2 * (nseg + pos)] = (int32_t)t;
-    if (t < T) tok2seg[t] = nseg + pos + flag - 1;
-    nseg += total;
-  };
-  constexpr int PRE = 16;
-  if (T <= (int64_t)PRE * 1024) {
-    int32_t cur[PRE], prev[PRE];
-#pragma unroll
-    for (int k = 0; k < PRE; k++) {
-      const int64_t t = (int64_t)k * 1024 + tid;
-      cur[k] = t < T ? seg[t] : 0;
-      prev[k] = (t < T && t > 0) ? seg[t - 1] : 0;
-    }
-#pragma unroll
-    for (int k = 0; k < PRE; k++)
-      if ((int64_t)k * 1024 < T) chunk((int64_t)k * 1024 + tid, cur[k], prev[k]);
-  } else {
-    for (int64_t base = 0; base < T; base += 1024) {
-      const int64_t t = base + tid;
-      chunk(t, t < T ? seg[t] : 0, (t < T && t > 0) ? seg[t - 1] : 0);
+  }
+  int nseg;
+  const int first = block_excl_scan(cnt, lds_wave, nseg);
+  {
+    int si = first - 1;  // the segment of token t0 - 1 (the run's tokens before its first start)
+    int32_t prev = t0 > 0 ? seg[t0 - 1] : 0;
+    for (int64_t t = t0; t < t1; t++) {
+      const int32_t cur = seg[t];
+      if (t == 0 || cur != prev) segtab[2 * (++si)] = (int32_t)t;
+      tok2seg[t] = si;
+      prev = cur;
     }
   }
   if (bad) atomicOr(&s_bad, 1);
@@ -112,17 +102,19 @@ __global__ __launch_bounds__(1024) void k_plan(const int32_t* __restrict__ seg, 
   // pass 3: work items, ceil(L / tile) tiles per segment
   int nitems = 0;
   int nbkt = 0;
-  if (bkt == nullptr) {  // segment order
-    for (int base = 0; base < nseg; base += 1024) {
-      const int s = base + tid;
-      const int nt = (s < nseg) ? (segtab[2 * s + 1] + tile - 1) / tile : 0;
-      int total;
-      const int off = block_excl_scan(nt, lds_wave, total);
-      for (int j = 0; j < nt; j++) {
-        items[2 * (nitems + off + j)] = s;
-        items[2 * (nitems + off + j) + 1] = j;
+  if (bkt == nullptr) {  // segment order: each thread owns a contiguous run of segments
+    const int sper = (nseg + 1023) / 1024;
+    const int s0 = min(nseg, tid * sper), s1 = min(nseg, s0 + sper);
+    int nt = 0;
+    for (int sg = s0; sg < s1; sg++) nt += (segtab[2 * sg + 1] + tile - 1) / tile;
+    const int off = block_excl_scan(nt, lds_wave, nitems);
+    int it = off;
+    for (int sg = s0; sg < s1; sg++) {
+      const int n = (segtab[2 * sg + 1] + tile - 1) / tile;
+      for (int j = 0; j < n; j++, it++) {
+        items[2 * it] = sg;
+        items[2 * it + 1] = j;
       }
-      nitems += total;
     }
   } else {  // by cost class, most expensive first
     if (tid < NBKT) s_cnt[tid] = 0;
