@@ -1,10 +1,15 @@
 """Throughput of the H3 attention node on one MI355X.
 
 Forward (default): one step = one h3attn_fwd call (segment plan, Q and K norm + fp16 V staging,
-attention) over the full workload, inputs resident in HBM.  Prints ONE JSON line:
+attention) over the full workload, inputs resident in HBM; by default the step is captured once in
+a HIP graph and replayed (--launch eager: one library call per step), and its output is checked bit
+for bit against an eager step.  Before the W warmup steps, untimed steps run for --prewarm-s seconds
+so the clocks reach steady state.  Prints ONE JSON line:
   value     whole-step attention TFLOP/s (nominal 4 * sum(L^2) * H * 128 FLOPs per step)
   roofline  the attention kernel alone (h3attn_attend), timed per launch with HIP events on the
             launch stream, against the bf16/fp16 dense MFMA peak (2516.6 TFLOP/s)
+  config.hbm  algorithmic bytes per step over the step time, warm (the previous step's data in the
+            256 MB MALL) and cold (a 512 MiB write before each step, untimed), against 8 TB/s
   cpu_baseline  the FP64 CPU oracle on a bounded sample of query rows of the same workload (with
             the host's CPU model and the time of each growing probe)
   parity    the benched output on those same rows against the oracle (relative L2 and max abs,
@@ -82,6 +87,11 @@ def main():
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="target oracle time of the CPU sample")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run one plain 256 MiB device copy (the reference kernel for HBM byte counters)")
+    ap.add_argument("--launch", choices=("graph", "eager"), default="graph",
+                    help="graph: the step is captured once in a HIP graph and replayed (its outputs are checked "
+                         "bit for bit against an eager step); eager: one library call per step")
+    ap.add_argument("--prewarm-s", type=float, default=0.25,
+                    help="seconds of untimed steps before the warmup steps, so the clocks reach steady state")
     args = ap.parse_args()
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
@@ -112,18 +122,36 @@ def main():
     if args.copy_calibration:
         copy_calibration(dev)
 
-    def step():
+    def eager_step(st):
         if pos is None:
             h3.h3attn_fwd(g["q"], g["k"], g["v"], g["seg"], g["wq"], g["wk"], eps=wl.eps, scale=wl.scale, out=out,
-                          workspace_buf=ws, stream=stream)
+                          workspace_buf=ws, stream=st)
         else:
             h3.h3attn_fwd_pos(g["q"], g["k"], g["v"], g["seg"], pos, g["wq"], g["wk"], eps=wl.eps, scale=wl.scale,
-                              out=out, workspace_buf=ws, stream=stream)
+                              out=out, workspace_buf=ws, stream=st)
 
+    # the reference bits: one eager step
+    eager_step(stream)
+    torch.cuda.synchronize()
+    ref_bits = out.view(torch.int16).clone()
+    step = lambda: eager_step(stream)  # noqa: E731
+    if args.launch == "graph":
+        # The library allocates nothing and clears its counters with its own kernels (no memset), so a
+        # step is capturable as it stands; each replay enqueues the same three kernels.
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph):
+            eager_step(torch.cuda.current_stream(dev))
+        step = graph.replay
+    # untimed steps until the clocks have settled (they ramp during the first ~0.1 s of load), then the
+    # warmup steps proper
+    t_end = time.perf_counter() + args.prewarm_s
+    while time.perf_counter() < t_end:
+        for _ in range(8):
+            step()
+        torch.cuda.synchronize()
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
-    ref_bits = out.view(torch.int16).clone()
 
     # ---- timed region: K whole steps
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
@@ -159,6 +187,27 @@ def main():
     attn_tflops = flops / (attn_ms * 1e-3) / 1e12
     log(f"attention kernel: mean {attn_ms:.4f} ms, median {np.median(kms):.4f} ms -> {attn_tflops:.1f} TFLOP/s "
         f"({100 * attn_tflops / PEAK_MFMA_TFLOPS:.1f}% of bf16 MFMA peak)")
+
+    # ---- algorithmic HBM rate of the whole step, warm (inputs left in the 256 MB MALL by the previous
+    # step) and cold (a 512 MiB write evicts them before each step; the scrub is not timed)
+    alg_bytes = wl.algorithmic_bytes()
+    scrub = torch.empty(128 << 20, dtype=torch.float32, device=dev)
+    cold = []
+    for _ in range(max(5, min(args.steps, 20))):
+        scrub.fill_(1.0)
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record(stream)
+        step()
+        b.record(stream)
+        torch.cuda.synchronize()
+        cold.append(a.elapsed_time(b))
+    del scrub
+    cold_ms = float(np.median(cold))
+    hbm = {"algorithmic_bytes": alg_bytes, "warm_GBps": round(alg_bytes / (ms_per_step * 1e-3) / 1e9, 1),
+           "cold_GBps": round(alg_bytes / (cold_ms * 1e-3) / 1e9, 1), "cold_ms_per_step": round(cold_ms, 4),
+           "peak_GBps": PEAK_HBM_GBS}
+    log(f"HBM (algorithmic bytes / step time): warm {hbm['warm_GBps']} GB/s, cold {hbm['cold_GBps']} GB/s "
+        f"({cold_ms:.4f} ms per cold step)")
 
     # ---- CPU baseline: the FP64 oracle on a bounded sample of query rows (rank 0, N = 1); the same
     # rows of the benched output are then checked against it (the accuracy of the timed output)
@@ -216,10 +265,10 @@ def main():
         "data": "synthetic",
         "config": {"workload": wl.name, "tokens": T, "heads": H, "head_dim": 128, "segments": list(wl.seg_lens),
                    "qk_draw_scale": wl.qk_scale, "pv_operands": "fp16", "accumulate": "fp32",
-                   "key_order": args.order,
+                   "key_order": args.order, "launch": args.launch,
                    "pct_bf16_mfma_peak": round(100 * value / PEAK_MFMA_TFLOPS, 2),
                    "algorithmic_GBps": round(wl.algorithmic_bytes() / (ms_per_step * 1e-3) / 1e9, 1),
-                   "repeat_bitwise": repeat_bitwise, "device_status": status},
+                   "hbm": hbm, "repeat_bitwise": repeat_bitwise, "device_status": status},
         "roofline": {"bound": "mfma", "achieved": round(attn_tflops, 2), "peak": PEAK_MFMA_TFLOPS,
                      "unit": "TFLOP/s", "frac": round(attn_tflops / PEAK_MFMA_TFLOPS, 4),
                      "traffic": traffic_bytes(wl.name), "kernel": "k_attn_fwd", "kernel_ms": round(attn_ms, 4)},
