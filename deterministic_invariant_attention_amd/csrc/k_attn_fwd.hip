@@ -4,7 +4,9 @@
 // output ("33B forward/backward" page, Scope: strict mode).
 //
 // Work item = (segment, 256-query tile, head); a persistent grid of one workgroup per CU walks the
-// items.  The workgroup has 8 waves of 32 queries; waves w and w + 4 share a SIMD.  The products
+// items, each XCD its own eighth of them (a sparse last round runs as 128-query halves, see the
+// work order in the kernel).  The workgroup has 8 waves of 32 queries; waves w and w + 4 share a
+// SIMD.  The products
 // are computed transposed so that one lane pair owns one query:
 //   S^T[key][query] = Khat . Qhat^T   (A = 32 keys x 16 dims from LDS, B = the wave's normed Q held
 //                                      in registers; v_mfma_f32_32x32x16_bf16)
@@ -260,11 +262,21 @@ __global__ __launch_bounds__(64 * NWAVES, 1) void k_attn_fwd(AttnParams p) {
   const int nitems = (int)min((int64_t)max(p.hdr->nitems, 0), max_items);
   const int nwork = nitems * H;
 
-  // XCD-aware order: workgroup b runs on XCD b % 8; the workgroups of one XCD take consecutive
-  // positions of the head-major work order, so they share the K/V tiles of one head in that XCD's L2.
+  // Work order: workgroup b runs on XCD b % 8, and XCD x owns the x-th eighth of the head-major
+  // order of (segment, 256-query tile, head) items, which its workgroups take in turn (slot s takes
+  // its units s, s + nslots, ...), so the workgroups of one XCD share the K/V tiles of one head in
+  // that XCD's L2.  When the XCD's last round of items would be at most half full, those items are
+  // split into 128-query halves: waves 0..3 compute a half with no partner on their SIMDs (each
+  // phase slot is then one wave's phase, not the longer of two), while waves 4..7 issue only their
+  // K copies and meet the barriers.  Whether an item runs whole or in halves, and which workgroup
+  // runs it, changes no bit of any output: every row runs the same instructions either way.
   const int xcd = blockIdx.x & 7;
   const int slot = blockIdx.x >> 3;
   const int nslots = p.xcd_slots;
+  const int64_t lo = (int64_t)nwork * xcd / 8, cnt = (int64_t)nwork * (xcd + 1) / 8 - lo;
+  const int64_t last = cnt % nslots;  // items of the XCD's last round
+  const int64_t nfull = (last != 0 && 2 * last <= nslots) ? cnt - last : cnt;
+  const int64_t nunits = nfull + 2 * (cnt - nfull);
 
   const int k_lane_off = tile_lane_offset(false, wv, lane);
   // the loop's copies: each wave of a group issues a quarter of a tile
@@ -287,9 +299,10 @@ __global__ __launch_bounds__(64 * NWAVES, 1) void k_attn_fwd(AttnParams p) {
     vb[db] = (uint32_t)(size_t)(const __attribute__((address_space(3))) uint16_t*)(lds + 2 * FTILE +
                                                                                    v_off(tr_row, 32 * db + tr_col));
 
-  for (int round = 0;; round++) {
-    const int64_t v = ((int64_t)round * 8 + xcd) * nslots + slot;
-    if (v >= nwork) break;
+  for (int64_t u = slot; u < nunits; u += nslots) {
+    // unit u: item v, whole (half = -1) or its first or second 128 queries (half = 0, 1)
+    const int64_t v = lo + (u < nfull ? u : nfull + ((u - nfull) >> 1));
+    const int half = u < nfull ? -1 : (int)((u - nfull) & 1);
     const int head = (int)(v / nitems);
     const int item = (int)(v - (int64_t)head * nitems);
     const int seg = p.items[2 * item];
@@ -299,11 +312,13 @@ __global__ __launch_bounds__(64 * NWAVES, 1) void k_attn_fwd(AttnParams p) {
     const int L = p.segtab[2 * seg + 1];
     if (s0 < 0 || L <= 0 || (int64_t)s0 + L > T || qt < 0 || qt * BQ >= L) continue;
 
+    // the wave's 32 query rows (segment-relative); in a half item waves w and w + 4 name the same rows
+    const int row0 = qt * BQ + (half < 0 ? 32 * wv : 128 * half + 32 * (wv & 3));
     if (p.segflag[seg] != 0) {
       // This segment holds a value that cannot enter the products (or invalid position ids): its
       // rows are NaN; every other segment is computed as usual.
-      const int qr = qt * BQ + wv * 32 + l32;
-      if (qr < L) {
+      const int qr = row0 + l32;
+      if (qr < L && (half < 0 || grp == 0)) {
         const int64_t r = (int64_t)(s0 + qr) * H + head;
         const u32x2 nan2 = {0x7FC07FC0u, 0x7FC07FC0u};
 #pragma unroll
@@ -327,21 +342,6 @@ __global__ __launch_bounds__(64 * NWAVES, 1) void k_attn_fwd(AttnParams p) {
     __syncthreads();
     ftile_to_lds<NWAVES>(kbase, L, lds, wv, k_lane_off);  // K(0)
 
-    const int qrow = qt * BQ + wv * 32 + l32;
-    const bool qvalid = qrow < L;
-    bf16x8 qf[8];
-    load_q(p, s0, qrow, qvalid, head, hh, qf);
-
-    f32x16 S[NKB];  // scores of the tile whose softmax is next
-    f16x8 pf[NKS];  // P of the tile whose P.V is next
-    f32x16 O[4];
-#pragma unroll
-    for (int d = 0; d < 4; d++)
-#pragma unroll
-      for (int i = 0; i < 16; i++) O[d][i] = 0.0f;
-    float lsum = 0.0f;
-    float m_run = -__builtin_inff();
-
     // K(m+1) and V(m) go into the buffers of K(m-1) and V(m-2), which were last read in slot 2m-1.
     // The buffer parity MP = m & 1 is a compile-time constant at every call, so the compiler can
     // see that a copy never writes the buffers being read and needs no wait for it.
@@ -360,6 +360,47 @@ __global__ __launch_bounds__(64 * NWAVES, 1) void k_attn_fwd(AttnParams p) {
       if (m < ntiles)
         ftile_to_lds_o<4>(vbase + (int64_t)m * FROWS * HD, L - m * FROWS, lds + (2 + MP) * FTILE, wv & 3, coffs);
     };
+
+    if (half >= 0 && grp == 1) {
+      // waves 4..7 of a half item: the trailing group's K copies and barriers, and no arithmetic
+      const int tau_idle = 2 * ntiles;
+      auto idle_phase = [&](int tau, auto tm) {
+        constexpr int TM = decltype(tm)::value;
+        const int t = tau + 1;
+        if (!(t & 1)) __builtin_amdgcn_s_waitcnt(0xF70);
+        phase_barrier();
+        if constexpr ((TM & 1) == 1) issue_k(t, Par<(TM == 1 ? 1 : 0)>{});
+      };
+      __builtin_amdgcn_s_waitcnt(0xF70);
+      phase_barrier();
+      issue_k(0, Par<0>{});
+      int tau = 0;
+      for (; tau + 3 <= tau_idle; tau += 4) {
+        idle_phase(tau, Par<0>{});
+        idle_phase(tau + 1, Par<1>{});
+        idle_phase(tau + 2, Par<2>{});
+        idle_phase(tau + 3, Par<3>{});
+      }
+      if (tau <= tau_idle) idle_phase(tau, Par<0>{});
+      if (tau + 1 <= tau_idle) idle_phase(tau + 1, Par<1>{});
+      if (tau + 2 <= tau_idle) idle_phase(tau + 2, Par<2>{});
+      continue;
+    }
+
+    const int qrow = row0 + l32;
+    const bool qvalid = qrow < L;
+    bf16x8 qf[8];
+    load_q(p, s0, qrow, qvalid, head, hh, qf);
+
+    f32x16 S[NKB];  // scores of the tile whose softmax is next
+    f16x8 pf[NKS];  // P of the tile whose P.V is next
+    f32x16 O[4];
+#pragma unroll
+    for (int d = 0; d < 4; d++)
+#pragma unroll
+      for (int i = 0; i < 16; i++) O[d][i] = 0.0f;
+    float lsum = 0.0f;
+    float m_run = -__builtin_inff();
 
     // Phase tau of this wave runs in slot t = tau + grp.  Even tau: G(k), k = tau/2 - 1 (scores of
     // tile k+1 from K buffer (k+1)&1, P.V of tile k from V buffer k&1).  Odd tau: V(k),

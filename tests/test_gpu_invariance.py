@@ -5,8 +5,9 @@ import numpy as np
 import pytest
 import torch
 
+import oracle
 import workloads
-from gpu_util import bitwise_equal, digest, f64, run_fwd, say, to_dev
+from gpu_util import EPS, MAX_ABS_BOUND, REL_L2_BOUND, bitwise_equal, digest, f64, metrics, run_fwd, say, to_dev
 
 pytestmark = pytest.mark.gpu
 
@@ -163,3 +164,24 @@ def test_key_tile_edges_alone_equal_batched():
         o, l = run_fwd(alone, want_lse=True)
         assert bitwise_equal(o, batched[t0:t0 + n]) and bitwise_equal(l, blse[t0:t0 + n]), f"segment at {t0}"
         t0 += n
+
+
+@pytest.mark.parametrize("la", [1000, 800])
+def test_half_items_alone_equal_whole_items_batched(la):
+    """A segment of 4 query tiles x 8 heads alone is too little work to fill a round, so its tiles
+    run as 128-query halves (4 waves computing); packed beside a 7168-token segment the 32 x 8
+    items fill whole rounds and run whole.  The rows must come out bitwise equal both ways, and
+    the alone run must match the oracle.  la = 800 leaves the second half of the last tile with
+    no valid row."""
+    x = workloads.random_inputs([la, 28 * 256], 8, seed=31)
+    g = to_dev(x)
+    say(f"[bitwise] {la}-token segment alone (half items) vs packed with 7168 tokens (whole items)")
+    batched, blse = run_fwd(g, want_lse=True)
+    alone = {n: (g[n][:la].contiguous() if n in ("q", "k", "v", "seg") else g[n]) for n in g}
+    o, l = run_fwd(alone, want_lse=True)
+    assert bitwise_equal(o, batched[:la]) and bitwise_equal(l, blse[:la])
+    xa = {n: (x[n][:la] if n in ("q", "k", "v", "seg") else x[n]) for n in x}
+    ref, _ = oracle.fwd(xa["q"], xa["k"], xa["v"], xa["seg"].numpy(), xa["wq"], xa["wk"], EPS, 128 ** -0.5)
+    rel, mx = metrics(o, ref)
+    say(f"[parity] {la} alone: rel_l2={rel:.3e} max_abs={mx:.3e}")
+    assert rel <= REL_L2_BOUND and mx <= MAX_ABS_BOUND
