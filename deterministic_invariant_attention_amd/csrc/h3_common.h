@@ -38,8 +38,15 @@ static_assert(sizeof(WsHeader) == 256, "header is 256 bytes");
 constexpr int32_t STATUS_SEG_BIT = 1;    // segment ids decrease (no segmentation exists: every output is NaN)
 constexpr int32_t STATUS_RANGE_BIT = 2;  // a finite |v| exceeds the fp16 range (in the flagged segments)
 
+// The forward attention kernel's work queues, at the end of the forward workspace: one counter per
+// XCD, each on its own 128-byte line (int index SCHED_STRIDE * x), and the count of workgroups that
+// have left the work loop (index SCHED_DONE).  All zero between launches.
+constexpr size_t SCHED_BYTES = 2048;
+constexpr int SCHED_STRIDE = 32;
+constexpr int SCHED_DONE = 8 * SCHED_STRIDE;
+
 struct WsLayout {
-  size_t segtab, items, khat, v16, qhat, tok2seg, segflag, total;
+  size_t segtab, items, khat, v16, qhat, tok2seg, segflag, sched, total;
   int64_t max_items;
 };
 
@@ -55,7 +62,8 @@ __host__ __device__ inline WsLayout ws_layout(int64_t T, int32_t H) {
   w.qhat = w.v16 + align256((size_t)T * H * HD * 2);
   w.tok2seg = w.qhat + align256((size_t)T * H * HD * 2);
   w.segflag = w.tok2seg + align256((size_t)T * 4);
-  w.total = w.segflag + align256((size_t)T * 4);
+  w.sched = w.segflag + align256((size_t)T * 4);
+  w.total = w.sched + SCHED_BYTES;
   return w;
 }
 

@@ -170,6 +170,7 @@ struct AttnParams {
   const int32_t* segtab;
   const int32_t* items;
   const int32_t* segflag;  // per segment: nonzero = a value cannot enter the products (NaN outputs)
+  int32_t* sched;          // the per-XCD work counters and the done count (zero between launches)
   int64_t T;
   int32_t H;
   float c;            // scale * log2(e)
@@ -263,13 +264,15 @@ __global__ __launch_bounds__(64 * NWAVES, 1) void k_attn_fwd(AttnParams p) {
   const int nwork = nitems * H;
 
   // Work order: workgroup b runs on XCD b % 8, and XCD x owns the x-th eighth of the head-major
-  // order of (segment, 256-query tile, head) items, which its workgroups take in turn (slot s takes
-  // its units s, s + nslots, ...), so the workgroups of one XCD share the K/V tiles of one head in
-  // that XCD's L2.  When the XCD's last round of items would be at most half full, those items are
-  // split into 128-query halves: waves 0..3 compute a half with no partner on their SIMDs (each
-  // phase slot is then one wave's phase, not the longer of two), while waves 4..7 issue only their
-  // K copies and meet the barriers.  Whether an item runs whole or in halves, and which workgroup
-  // runs it, changes no bit of any output: every row runs the same instructions either way.
+  // order of (segment, 256-query tile, head) items, so the workgroups of one XCD share the K/V tiles
+  // of one head in that XCD's L2.  A workgroup's first unit is its slot s; after that the XCD's
+  // workgroups take units from a counter of their own, so one that finishes early (items of short
+  // segments cost less) takes the next.  When the XCD's last round of items would be at most half
+  // full, those items are split into 128-query halves: waves 0..3 compute a half with no partner on
+  // their SIMDs (each phase slot is then one wave's phase, not the longer of two), while waves 4..7
+  // issue only their K copies and meet the barriers.  Whether an item runs whole or in halves, and
+  // which workgroup runs it, changes no bit of any output: every row runs the same instructions
+  // either way.
   const int xcd = blockIdx.x & 7;
   const int slot = blockIdx.x >> 3;
   const int nslots = p.xcd_slots;
@@ -277,6 +280,9 @@ __global__ __launch_bounds__(64 * NWAVES, 1) void k_attn_fwd(AttnParams p) {
   const int64_t last = cnt % nslots;  // items of the XCD's last round
   const int64_t nfull = (last != 0 && 2 * last <= nslots) ? cnt - last : cnt;
   const int64_t nunits = nfull + 2 * (cnt - nfull);
+  // No XCD has more units than workgroups (nunits <= nslots holds exactly when cnt <= nslots, and
+  // cnt <= ceil(nwork / 8)): every unit is some workgroup's first, and the counters stay untouched.
+  const bool one_round = (nwork + 7) / 8 <= nslots;
 
   const int k_lane_off = tile_lane_offset(false, wv, lane);
   // the loop's copies: each wave of a group issues a quarter of a tile
@@ -299,7 +305,12 @@ __global__ __launch_bounds__(64 * NWAVES, 1) void k_attn_fwd(AttnParams p) {
     vb[db] = (uint32_t)(size_t)(const __attribute__((address_space(3))) uint16_t*)(lds + 2 * FTILE +
                                                                                    v_off(tr_row, 32 * db + tr_col));
 
-  for (int64_t u = slot; u < nunits; u += nslots) {
+  __shared__ int32_t s_unit;
+  int32_t fetched = 0;  // thread 0: the counter value fetched during the current unit
+  for (int64_t u = slot; u < nunits;) {
+    do {  // one unit; its early exits (continue) end the do, not the walk over units
+    // the next unit's counter value, fetched now and used at the end of this unit
+    if (!one_round && tid == 0) fetched = atomicAdd(&p.sched[SCHED_STRIDE * xcd], 1);
     // unit u: item v, whole (half = -1) or its first or second 128 queries (half = 0, 1)
     const int64_t v = lo + (u < nfull ? u : nfull + ((u - nfull) >> 1));
     const int half = u < nfull ? -1 : (int)((u - nfull) & 1);
@@ -501,6 +512,20 @@ __global__ __launch_bounds__(64 * NWAVES, 1) void k_attn_fwd(AttnParams p) {
       }
       if (p.lse && hh == 0) p.lse[(int64_t)(s0 + qrow) * H + head] = (m_run + __builtin_amdgcn_logf(l)) * LN2;
     }
+    } while (0);
+    if (one_round) break;
+    // the counter hands out the units from nslots on (the first nslots are the slots themselves)
+    if (tid == 0) s_unit = nslots + fetched;
+    __syncthreads();
+    u = s_unit;
+  }
+
+  // The last workgroup to leave zeroes the counters, so that the next launch on this workspace (the
+  // staged entry points may attend several times per plan) starts from the first unit again.  Every
+  // workgroup has made its last fetch, and had its result, before it counts itself out.
+  if (!one_round && tid == 0 && atomicAdd(&p.sched[SCHED_DONE], 1) == (int)gridDim.x - 1) {
+    for (int x = 0; x < 8; x++) atomicExch(&p.sched[SCHED_STRIDE * x], 0);
+    atomicExch(&p.sched[SCHED_DONE], 0);
   }
 }
 
@@ -522,6 +547,7 @@ hipError_t launch_attend(const void* q, bool normed, int64_t T, int32_t H, float
   p.segtab = (const int32_t*)(base + Lw.segtab);
   p.items = (const int32_t*)(base + Lw.items);
   p.segflag = (const int32_t*)(base + Lw.segflag);
+  p.sched = (int32_t*)(base + Lw.sched);
   p.T = T;
   p.H = H;
   p.c = (float)((double)scale * 1.4426950408889634074);

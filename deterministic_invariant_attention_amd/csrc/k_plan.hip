@@ -44,12 +44,13 @@ __device__ __forceinline__ int block_excl_scan(int v, int* lds_wave, int& total)
 // non-empty class; the work counters are reset.
 // tok2seg: the segment index of every token; segflag: the per-segment error flags, cleared for the
 // call's nseg segments; dmax (backward only, else NULL): the per-(segment, head) maxima of |dO|,
-// zeroed for the nseg * H slots the call uses.
+// zeroed for the nseg * H slots the call uses; sched (forward only, else NULL): the attention
+// kernel's work counters, zeroed.
 __global__ __launch_bounds__(1024) void k_plan(const int32_t* __restrict__ seg, int64_t T, WsHeader* hdr,
                                               int32_t* __restrict__ segtab, int32_t* __restrict__ items, int tile,
                                               int32_t* __restrict__ bkt, int32_t* __restrict__ tok2seg,
                                               int32_t* __restrict__ segflag, uint32_t* __restrict__ dmax,
-                                              int32_t H) {
+                                              int32_t H, int32_t* __restrict__ sched) {
   __shared__ int lds_wave[16];
   __shared__ int s_bad;
   __shared__ int s_cnt[NBKT], s_run[NBKT];
@@ -89,6 +90,8 @@ __global__ __launch_bounds__(1024) void k_plan(const int32_t* __restrict__ seg, 
   for (int i = tid; i < nseg; i += 1024) segflag[i] = 0;
   if (dmax)
     for (int64_t i = tid; i < (int64_t)nseg * H; i += 1024) dmax[i] = 0u;
+  if (sched)
+    for (int i = tid; i < (int)(SCHED_BYTES / 4); i += 1024) sched[i] = 0;
   __syncthreads();
 
   // pass 2: lengths
@@ -170,7 +173,7 @@ hipError_t launch_plan(const int32_t* seg, int64_t T, void* ws, int32_t H, hipSt
   char* base = (char*)ws;
   hipLaunchKernelGGL(k_plan, dim3(1), dim3(1024), 0, stream, seg, T, (WsHeader*)base, (int32_t*)(base + L.segtab),
                      (int32_t*)(base + L.items), BQ, nullptr, (int32_t*)(base + L.tok2seg), (int32_t*)(base + L.segflag),
-                     nullptr, H);
+                     nullptr, H, (int32_t*)(base + L.sched));
   return hipGetLastError();
 }
 
@@ -179,7 +182,7 @@ hipError_t launch_plan_bwd(const int32_t* seg, int64_t T, void* ws, int32_t H, h
   char* base = (char*)ws;
   hipLaunchKernelGGL(k_plan, dim3(1), dim3(1024), 0, stream, seg, T, (WsHeader*)base, (int32_t*)(base + L.segtab),
                      (int32_t*)(base + L.items), BT, (int32_t*)(base + L.bkt), (int32_t*)(base + L.tok2seg),
-                     (int32_t*)(base + L.segflag), (uint32_t*)(base + L.dmax), H);
+                     (int32_t*)(base + L.segflag), (uint32_t*)(base + L.dmax), H, nullptr);
   return hipGetLastError();
 }
 

@@ -5,6 +5,7 @@ import numpy as np
 import pytest
 import torch
 
+import deterministic_invariant_attention_amd as h3
 import oracle
 import workloads
 from gpu_util import EPS, MAX_ABS_BOUND, REL_L2_BOUND, bitwise_equal, digest, f64, metrics, run_fwd, say, to_dev
@@ -185,3 +186,25 @@ def test_half_items_alone_equal_whole_items_batched(la):
     rel, mx = metrics(o, ref)
     say(f"[parity] {la} alone: rel_l2={rel:.3e} max_abs={mx:.3e}")
     assert rel <= REL_L2_BOUND and mx <= MAX_ABS_BOUND
+
+
+@pytest.mark.parametrize("name", ["batch2", "short3"])
+def test_staged_attend_repeated_after_one_plan(name):
+    """One plan and one staging, then three attention launches on the same workspace (a caller that
+    reuses a plan across blocks): each must equal the one-call forward bit for bit.  On batch2 the
+    workgroups take their later units from per-XCD counters that each launch returns to zero at its
+    end; short3 fits one round and uses none."""
+    wl = workloads.WORKLOADS[name]
+    g = to_dev(workloads.make_inputs(wl))
+    say(f"[bitwise] {name}: plan once, attend three times")
+    ref, rlse = run_fwd(g, want_lse=True)
+    T, H = g["q"].shape[0], g["q"].shape[1]
+    ws = h3.workspace(T, H, g["q"].device)
+    h3.h3attn_plan(g["seg"], H, ws)
+    h3.h3attn_prep_qkv(g["q"], g["k"], g["v"], g["wq"], g["wk"], ws, eps=EPS)
+    for i in range(3):
+        out = torch.full_like(g["q"], float("nan"))
+        lse = torch.full((T, H), float("nan"), dtype=torch.float32, device=g["q"].device)
+        h3.h3attn_attend(g["q"], g["wq"], ws, out, lse=lse, eps=EPS, scale=128 ** -0.5)
+        torch.cuda.synchronize()
+        assert bitwise_equal(out, ref) and bitwise_equal(lse, rlse), f"launch {i}"
