@@ -176,19 +176,24 @@ __global__ __launch_bounds__(256) void k_bwd_dmax(const uint16_t* __restrict__ d
   const int c = threadIdx.x & 15;
   const int h = (int)(blockIdx.x % (unsigned)H);
   const int64_t t0 = (int64_t)(blockIdx.x / (unsigned)H) * DMAX_TOK;
+  // every load of the block's rows is issued before the first is reduced
+  u32x4 w[DMAX_TOK / 16];
+#pragma unroll
+  for (int it = 0; it < DMAX_TOK / 16; it++) {
+    const int64_t t = t0 + it * 16 + (threadIdx.x >> 4);
+    const u32x4 zero = {0u, 0u, 0u, 0u};
+    w[it] = t < T ? *(const u32x4*)(dout + (t * H + h) * HD + c * 8) : zero;
+  }
 #pragma unroll
   for (int it = 0; it < DMAX_TOK / 16; it++) {
     const int i = it * 16 + (threadIdx.x >> 4);  // token within the block
     const int64_t t = t0 + i;
     uint32_t m = 0;
-    if (t < T) {
-      const u32x4 w = *(const u32x4*)(dout + (t * H + h) * HD + c * 8);
 #pragma unroll
-      for (int j = 0; j < 4; j++) {
-        const uint32_t a = w[j] & 0x7FFFu, b = (w[j] >> 16) & 0x7FFFu;
-        m = a > m ? a : m;
-        m = b > m ? b : m;
-      }
+    for (int j = 0; j < 4; j++) {
+      const uint32_t a = w[it][j] & 0x7FFFu, b = (w[it][j] >> 16) & 0x7FFFu;
+      m = a > m ? a : m;
+      m = b > m ? b : m;
     }
 #pragma unroll
     for (int o = 1; o < 16; o <<= 1) {
