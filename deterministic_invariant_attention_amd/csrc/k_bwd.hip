@@ -586,6 +586,15 @@ __global__ __launch_bounds__(256) void k_bwd_norm(NormBwdParams p) {
   // A staged row lies in the rows of the same segment as the token of that index, so tok2seg names
   // its segment.  In a flagged segment the order maps may be invalid: the row is NaN and stays at
   // its own index.
+  // dy, and x in packed order, do not depend on the segment's flag: their loads go out first
+  const bool pos = p.inv != nullptr;
+  u32x4 xv = {0, 0, 0, 0};
+  f32x4 d0 = {0.0f, 0.0f, 0.0f, 0.0f}, d1 = d0;
+  if (valid) {
+    d0 = *(const f32x4*)(p.dy[which] + row * HD + 8 * c);
+    d1 = *(const f32x4*)(p.dy[which] + row * HD + 8 * c + 4);
+    if (!pos) xv = *(const u32x4*)(p.x[which] + row * HD + 8 * c);
+  }
   bool bad = false;
   int64_t xrow = row;  // the token's row
   if (valid) {
@@ -593,19 +602,13 @@ __global__ __launch_bounds__(256) void k_bwd_norm(NormBwdParams p) {
     const int sg = p.tok2seg[sl];
     const int nseg = p.hdr->nseg;
     bad = sg >= 0 && sg < nseg && p.segflag[sg] != 0;
-    if (p.inv && !bad) xrow = (int64_t)p.inv[sl] * p.H + (row - sl * p.H);
+    if (pos && !bad) xrow = (int64_t)p.inv[sl] * p.H + (row - sl * p.H);
   }
+  if (valid && pos) xv = *(const u32x4*)(p.x[which] + xrow * HD + 8 * c);
 
   float x[8], wf[8];
   double dy[8];  // the gradient with respect to the norm's output (through the rope when given)
   {
-    u32x4 xv = {0, 0, 0, 0};
-    f32x4 d0 = {0.0f, 0.0f, 0.0f, 0.0f}, d1 = d0;
-    if (valid) {
-      xv = *(const u32x4*)(p.x[which] + xrow * HD + 8 * c);
-      d0 = *(const f32x4*)(p.dy[which] + row * HD + 8 * c);
-      d1 = *(const f32x4*)(p.dy[which] + row * HD + 8 * c + 4);
-    }
     unpack8_bf16(xv, x);
     unpack8_bf16(*(const u32x4*)(p.w[which] + 8 * c), wf);
 #pragma unroll
