@@ -23,12 +23,14 @@ def test_repeat_bitwise_short3_x10():
         assert digest(o) == d0 and digest(l) == l0
 
 
-def test_repeat_bitwise_long_x3():
+def test_repeat_bitwise_long_x10():
+    """The headline workload ten times: output and LSE bit for bit the same every time."""
     g = to_dev(workloads.make_inputs(workloads.WORKLOADS["long"]))
-    say("[bitwise] long repeat x3")
-    d0 = digest(run_fwd(g)[0])
-    for _ in range(2):
-        assert digest(run_fwd(g)[0]) == d0
+    say("[bitwise] long repeat x10")
+    ref, rlse = run_fwd(g, want_lse=True)
+    for i in range(9):
+        o, l = run_fwd(g, want_lse=True)
+        assert bitwise_equal(o, ref) and bitwise_equal(l, rlse), f"repeat {i + 1}"
 
 
 def test_batch2_alone_equals_batched():
