@@ -26,10 +26,15 @@ FLAGS = [
     "-Wall", "-Wno-unused-function",
     "-I", os.path.join(ROOT, "include"), "-I", CSRC,
 ]
+# The backward kernels hold S, P, dP and dS of a 64-row tile in registers.  By default the compiler
+# writes MFMA results to accumulation registers and copies every element back to ordinary VGPRs
+# before the softmax arithmetic reads it; asking for the VGPR form of the MFMA removes those copies
+# (the code computes the same values in the same order, so results are unchanged).
+SRC_FLAGS = {"k_bwd.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
 
 
 def _compile(src: str, obj: str) -> None:
-    cmd = [HIPCC, *FLAGS, "-c", os.path.join(CSRC, src), "-o", obj]
+    cmd = [HIPCC, *FLAGS, *SRC_FLAGS.get(src, []), "-c", os.path.join(CSRC, src), "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     # hipcc's host pass does not know the packed-fp32 feature and says so; that line is harmless
     err = "\n".join(l for l in r.stderr.splitlines() if "packed-fp32-ops" not in l)
