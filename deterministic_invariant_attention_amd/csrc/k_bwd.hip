@@ -13,15 +13,16 @@
 //   k_bwd_dq    work item = (segment, 128-query tile, head).  Pass 1 over the key tiles computes
 //               D_i exactly (in fp32, a fixed tree per tile) unless the staging kernel formed it
 //               from the forward's fp32 output; pass 2 recomputes S and dP, forms dS and
-//               accumulates dQ^T += K^16^T dS^T.  Its dP products start from -D (D is one value
-//               per lane there), so they give dP - D and dS costs one multiply per element.
+//               accumulates dQ^T += K^16^T dS^T.  Two workgroups share a CU (two waves per
+//               SIMD, at most 256 registers each), so one wave's vector work runs beside the
+//               other's MFMAs.
 // The workspace keeps -D per staged row.
 //   k_bwd_dkdv  work item = (segment, 128-key tile, head).  One pass over the query tiles:
 //               S = Q^ K^T and dP = dO V^T with the wave's 32 keys in registers, P and dS in fp16,
 //               dV^T += dO16^T P and dK^T += Q^16^T dS, whose transposed reads run as one pipeline.
-// A wave's vector work overlaps its own MFMAs when a few independent instructions sit between
-// them, so P is formed between the dP MFMAs and dS between the MFMAs that only need P (dV's in
-// dk/dv, the first dQ steps in dq), each packed slice finished before its first use.
+// In dk/dv (one wave per SIMD) a wave's vector work overlaps its own MFMAs when a few independent
+// instructions sit between them, so P is formed between the dP MFMAs and dS between the dV MFMAs
+// that only need P, each packed slice finished before its first use.
 // With norm weights both write dq^ / dk^ in fp32 and k_bwd_norm applies the RMSNorm backward per
 // row (FP64, one bf16 rounding) and writes fixed-order weight-gradient partials, which two small
 // kernels sum in a fixed tree; without weights the kernels write dq, dk directly.
@@ -208,7 +209,7 @@ __device__ __forceinline__ void static_for2(F&& f) {
 
 // ============================================================================== dq (and D)
 
-__global__ __launch_bounds__(64 * BW, 1) void k_bwd_dq(BwdParams p) {
+__global__ __launch_bounds__(64 * BW, 2) void k_bwd_dq(BwdParams p) {
   // tiles 0, 1: K^16 of stage 0 / 1 (read by rows for S and transposed for dQ); 2, 3: V16 of
   // stage 0 / 1; both in the unified layout
   __shared__ __attribute__((aligned(1024))) uint16_t lds[4 * TILE_ELEMS];
@@ -321,12 +322,7 @@ __global__ __launch_bounds__(64 * BW, 1) void k_bwd_dq(BwdParams p) {
       copies(0, Par2<0>{});
     }
 
-    // ---- pass 2: dQ^T += K^16^T dS^T; the dP products start from -D, so they give dP - D
-    f32x16 negD[2];
-#pragma unroll
-    for (int kb = 0; kb < 2; kb++)
-#pragma unroll
-      for (int i = 0; i < 16; i++) negD[kb][i] = -Dq;
+    // ---- pass 2: dQ^T += K^16^T dS^T
     f32x16 acc[4];
 #pragma unroll
     for (int d = 0; d < 4; d++)
@@ -336,8 +332,7 @@ __global__ __launch_bounds__(64 * BW, 1) void k_bwd_dq(BwdParams p) {
       constexpr int ST = decltype(stage)::value;
       copies_barrier();  // tile j has landed, every wave is done with stage 1 - ST
       if (j + 1 < ntk) copies(j + 1, Par2<1 - ST>{});
-      // P between the dP MFMAs (two elements per step); dS slice 0 before the dQ products and
-      // slice k between the MFMAs of steps 4(k-1) .. 4k-1, four steps before its first use.
+      // P between the dP MFMAs (two elements per step), then dS = P (dP - D) packed to fp16
       f32x16 S[2], dP[2];
       gemm_rows<0 + ST>(rb, qf, S, [](auto) {});
       if (j == ntk - 1 && rem < TILE_ROWS) mask_tail(S, rem, hh);
@@ -349,25 +344,15 @@ __global__ __launch_bounds__(64 * BW, 1) void k_bwd_dq(BwdParams p) {
           const int e = 2 * s + u;
           pr[e] = __builtin_amdgcn_exp2f(__builtin_fmaf(S[e >> 4][e & 15], c, -lq));
         }
-      }, negD);
+      });
       f16x8 dsf[4];
 #pragma unroll
-      for (int e = 0; e < 8; e++) ds[e] = pr[e] * dP[0][e];
-      dsf[0] = pack_p(&ds[0]);
+      for (int e = 0; e < 32; e++) ds[e] = pr[e] * (dP[e >> 4][e & 15] - Dq);
+#pragma unroll
+      for (int sl = 0; sl < 4; sl++) dsf[sl] = pack_p(&ds[8 * sl]);
       const f16x8* bop[1] = {dsf};
       f32x16* accp[1] = {acc};
-      tr_gemm_hooked<TilePair<ST, ST>, 1>(vb, bop, accp, [&](auto st) {
-        constexpr int s = decltype(st)::value;
-        if constexpr (s < 12) {
-          constexpr int sl = (s >> 2) + 1;
-#pragma unroll
-          for (int u = 0; u < 2; u++) {
-            const int e = 8 * sl + 2 * (s & 3) + u;
-            ds[e] = pr[e] * dP[e >> 4][e & 15];
-          }
-          if constexpr ((s & 3) == 3) dsf[sl] = pack_p(&ds[8 * sl]);
-        }
-      });
+      tr_gemm_hooked<TilePair<ST, ST>, 1>(vb, bop, accp, [](auto) {});
     };
     {
       int j = 0;
@@ -735,7 +720,8 @@ hipError_t launch_bwd(const void* q, const void* k, const void* wq, const void* 
   int64_t grid = grid_cap < max_work ? grid_cap : max_work;
   grid = (grid + 7) & ~(int64_t)7;
   p.next = &((WsHeader*)base)->next[0];
-  hipLaunchKernelGGL(k_bwd_dq, dim3((unsigned)grid), dim3(64 * BW), 0, stream, p);
+  // grid_cap is the CU count: dq runs two workgroups per CU, dk/dv one
+  hipLaunchKernelGGL(k_bwd_dq, dim3((unsigned)(2 * grid)), dim3(64 * BW), 0, stream, p);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   p.next = &((WsHeader*)base)->next[1];
