@@ -114,9 +114,16 @@ __device__ __forceinline__ RowBases row_bases_u(const uint16_t* lds, int l32, in
   b.hi = b.lo + 4 * TILE_ELEMS * 2;
   return b;
 }
-template <int TILE, int s>
+// Step s covers row block kb and dim slice m: interleaved (kb = s % 2, the two accumulators
+// alternate) or, with KM, block-major (kb = s / 8: block 0's eight steps first, so its result is
+// complete halfway through).
+template <int s, bool KM>
+struct RowStep {
+  static constexpr int kb = KM ? (s >> 3) : (s & 1), m = KM ? (s & 7) : (s >> 1);
+};
+template <int TILE, int s, bool KM = false>
 __device__ __forceinline__ u32x4 rows_read(const RowBases& rb) {
-  constexpr int kb = s & 1, m = s >> 1;
+  constexpr int kb = RowStep<s, KM>::kb, m = RowStep<s, KM>::m;
   constexpr int off = (TILE & 3) * TILE_ELEMS * 2 + kb * 32 * HD * 2;
   return ds_read_b128_asm<off>((TILE >= 4 ? rb.hi : rb.lo) ^ (uint32_t)(m << 5));
 }
@@ -128,19 +135,20 @@ __device__ __forceinline__ f32x16 mfma_rows(const u32x4& a, const f16x8& b, cons
 }
 // init == nullptr: the accumulators start at zero; else S[kb] starts at init[kb] (the first MFMA of
 // each accumulator takes it as its addend).
-template <int TILE, int NPRE, int s, typename BT, typename Hook>
+template <int TILE, int NPRE, int s, bool KM, typename BT, typename Hook>
 __device__ __forceinline__ void rows_step(const RowBases& rb, const BT* b, f32x16* S, u32x4 (&ka)[16], Hook& hook,
                                           const f32x16* init) {
-  if constexpr (s + NPRE < 16) ka[s + NPRE] = rows_read<TILE, s + NPRE>(rb);
+  constexpr int kb = RowStep<s, KM>::kb, m = RowStep<s, KM>::m;
+  if constexpr (s + NPRE < 16) ka[s + NPRE] = rows_read<TILE, s + NPRE, KM>(rb);
   constexpr int ahead = (s + NPRE < 16 ? NPRE : 15 - s);
   lgkm_wait_tied4<ahead>(ka[s]);
-  if constexpr (s < 2) S[s & 1] = mfma_rows(ka[s], b[s >> 1], init ? init[s & 1] : S[s & 1]);
-  else S[s & 1] = mfma_rows(ka[s], b[s >> 1], S[s & 1]);
+  if constexpr (m == 0) S[kb] = mfma_rows(ka[s], b[m], init ? init[kb] : S[kb]);
+  else S[kb] = mfma_rows(ka[s], b[m], S[kb]);
   hook(StepIdx<s>{});
   __builtin_amdgcn_sched_barrier(0);
-  if constexpr (s + 1 < 16) rows_step<TILE, NPRE, s + 1>(rb, b, S, ka, hook, init);
+  if constexpr (s + 1 < 16) rows_step<TILE, NPRE, s + 1, KM>(rb, b, S, ka, hook, init);
 }
-template <int TILE, int NPRE = 4, typename BT, typename Hook>
+template <int TILE, int NPRE = 4, bool KM = false, typename BT, typename Hook>
 __device__ __forceinline__ void gemm_rows(const RowBases& rb, const BT* b, f32x16* S, Hook hook,
                                           const f32x16* init = nullptr) {
   static_assert(TILE >= 0 && TILE <= 7 && NPRE >= 1 && NPRE <= 8, "tile and prefetch depth");
@@ -151,15 +159,15 @@ __device__ __forceinline__ void gemm_rows(const RowBases& rb, const BT* b, f32x1
       for (int i = 0; i < 16; i++) S[kb][i] = 0.0f;
   }
   u32x4 ka[16];
-  ka[0] = rows_read<TILE, 0>(rb);
-  if constexpr (NPRE > 1) ka[1] = rows_read<TILE, 1>(rb);
-  if constexpr (NPRE > 2) ka[2] = rows_read<TILE, 2>(rb);
-  if constexpr (NPRE > 3) ka[3] = rows_read<TILE, 3>(rb);
-  if constexpr (NPRE > 4) ka[4] = rows_read<TILE, 4>(rb);
-  if constexpr (NPRE > 5) ka[5] = rows_read<TILE, 5>(rb);
-  if constexpr (NPRE > 6) ka[6] = rows_read<TILE, 6>(rb);
-  if constexpr (NPRE > 7) ka[7] = rows_read<TILE, 7>(rb);
-  rows_step<TILE, NPRE, 0>(rb, b, S, ka, hook, init);
+  ka[0] = rows_read<TILE, 0, KM>(rb);
+  if constexpr (NPRE > 1) ka[1] = rows_read<TILE, 1, KM>(rb);
+  if constexpr (NPRE > 2) ka[2] = rows_read<TILE, 2, KM>(rb);
+  if constexpr (NPRE > 3) ka[3] = rows_read<TILE, 3, KM>(rb);
+  if constexpr (NPRE > 4) ka[4] = rows_read<TILE, 4, KM>(rb);
+  if constexpr (NPRE > 5) ka[5] = rows_read<TILE, 5, KM>(rb);
+  if constexpr (NPRE > 6) ka[6] = rows_read<TILE, 6, KM>(rb);
+  if constexpr (NPRE > 7) ka[7] = rows_read<TILE, 7, KM>(rb);
+  rows_step<TILE, NPRE, 0, KM>(rb, b, S, ka, hook, init);
 }
 
 // The lane's eight transposed-read base addresses in tile 0 of the unified layout: vb[4u + db] for

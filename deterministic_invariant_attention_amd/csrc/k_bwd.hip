@@ -379,15 +379,71 @@ __global__ __launch_bounds__(64 * BW, 2) void k_bwd_dq(BwdParams p) {
 
 // ============================================================================== dk, dv
 
-__global__ __launch_bounds__(64 * BW, 1) void k_bwd_dkdv(BwdParams p) {
+// The P exchange of the dk/dv kernel: wave kw of the P role writes the 32 fp32 P values of each of
+// its lanes (lane-major 16-byte pieces, so both sides are free of bank conflicts) and wave kw + 4
+// reads them back after a barrier; one asm block each, with the wait inside, so no register of the
+// exchange is touched while an LDS operation on it is in flight.
+__device__ __forceinline__ void xch_write(uint32_t a, const float (&pr)[2][16]) {
+  const f32x4 v0 = {pr[0][0], pr[0][1], pr[0][2], pr[0][3]}, v1 = {pr[0][4], pr[0][5], pr[0][6], pr[0][7]};
+  const f32x4 v2 = {pr[0][8], pr[0][9], pr[0][10], pr[0][11]}, v3 = {pr[0][12], pr[0][13], pr[0][14], pr[0][15]};
+  const f32x4 v4 = {pr[1][0], pr[1][1], pr[1][2], pr[1][3]}, v5 = {pr[1][4], pr[1][5], pr[1][6], pr[1][7]};
+  const f32x4 v6 = {pr[1][8], pr[1][9], pr[1][10], pr[1][11]}, v7 = {pr[1][12], pr[1][13], pr[1][14], pr[1][15]};
+  asm volatile(
+      "ds_write_b128 %0, %1\n\t"
+      "ds_write_b128 %0, %2 offset:1024\n\t"
+      "ds_write_b128 %0, %3 offset:2048\n\t"
+      "ds_write_b128 %0, %4 offset:3072\n\t"
+      "ds_write_b128 %0, %5 offset:4096\n\t"
+      "ds_write_b128 %0, %6 offset:5120\n\t"
+      "ds_write_b128 %0, %7 offset:6144\n\t"
+      "ds_write_b128 %0, %8 offset:7168\n\t"
+      "s_waitcnt lgkmcnt(0)"
+      :
+      : "v"(a), "v"(v0), "v"(v1), "v"(v2), "v"(v3), "v"(v4), "v"(v5), "v"(v6), "v"(v7)
+      : "memory");
+}
+__device__ __forceinline__ void xch_read(uint32_t a, float (&pr)[2][16]) {
+  f32x4 v0, v1, v2, v3, v4, v5, v6, v7;
+  asm volatile(
+      "ds_read_b128 %0, %8\n\t"
+      "ds_read_b128 %1, %8 offset:1024\n\t"
+      "ds_read_b128 %2, %8 offset:2048\n\t"
+      "ds_read_b128 %3, %8 offset:3072\n\t"
+      "ds_read_b128 %4, %8 offset:4096\n\t"
+      "ds_read_b128 %5, %8 offset:5120\n\t"
+      "ds_read_b128 %6, %8 offset:6144\n\t"
+      "ds_read_b128 %7, %8 offset:7168\n\t"
+      "s_waitcnt lgkmcnt(0)"
+      : "=&v"(v0), "=&v"(v1), "=&v"(v2), "=&v"(v3), "=&v"(v4), "=&v"(v5), "=&v"(v6), "=&v"(v7)
+      : "v"(a)
+      : "memory");
+  const f32x4 v[8] = {v0, v1, v2, v3, v4, v5, v6, v7};
+#pragma unroll
+  for (int g = 0; g < 8; g++)
+#pragma unroll
+    for (int i = 0; i < 4; i++) pr[g >> 2][4 * (g & 3) + i] = v[g][i];
+}
+
+// Eight waves, two per SIMD, in two roles over the same 128 keys: wave kw (< 4) recomputes
+// S = Q^ K^T and P for keys 32kw .. 32kw + 31, hands P to wave kw + 4 through LDS and accumulates
+// dV^T += dO16^T P; wave kw + 4 computes dP = dO V^T, dS = P (dP - D) and dK^T += Q^16^T dS.  Waves
+// kw and kw + 4 share a SIMD, so each one's vector work runs beside the other's MFMAs.  Every
+// accumulator sees the same products in the same order as in one wave doing all four, so the
+// split does not change a bit.
+constexpr int BWK = 2 * BW;
+
+__global__ __launch_bounds__(64 * BWK, 1) void k_bwd_dkdv(BwdParams p) {
   // tiles 0, 1: Q^16 and 2, 3: dO16 of stage 0 / 1, in the unified layout (read by rows for S and
-  // dP, transposed for dK and dV); then the fp32 rows [stage][lse2, D][64 queries]
-  __shared__ __attribute__((aligned(1024))) uint16_t lds[4 * TILE_ELEMS + 2 * 2 * TILE_ROWS * 2];
+  // dP, transposed for dK and dV); then the fp32 rows [stage][lse2, D][64 queries]; then the P
+  // exchange, 8 KB per key block
+  constexpr int XCH_OFF = 4 * TILE_ELEMS * 2 + 2 * 2 * TILE_ROWS * 4;
+  __shared__ __attribute__((aligned(1024))) uint16_t lds[XCH_OFF / 2 + BW * 64 * 32 * 2];
   lds_char* const lrow3 = (lds_char*)lds + 4 * TILE_ELEMS * 2;  // the same rows as an LDS address
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int role = wv >> 2, kw = wv & 3;  // role 0: P and dV; 1: dS and dK; kw: the key block
   const int hh = lane >> 5, l32 = lane & 31;
   if (fill_nan_if_bad(p, p.dk, p.dv)) return;
 
@@ -401,6 +457,7 @@ __global__ __launch_bounds__(64 * BW, 1) void k_bwd_dkdv(BwdParams p) {
   tr_bases_u(lds, lane, vb);
   const RowBases rb = row_bases_u(lds, l32, hh);
   const uint32_t lrow_lane = (uint32_t)(size_t)lrow3 + 16 * hh;  // lrow[4hh] as an LDS byte address
+  const uint32_t xch = (uint32_t)(size_t)((lds_char*)lds + XCH_OFF) + kw * 8192 + lane * 16;
   const float c = p.c;
 
   const int nbkt = min(max(p.hdr->nbkt, 0), NBKT);
@@ -413,14 +470,16 @@ __global__ __launch_bounds__(64 * BW, 1) void k_bwd_dkdv(BwdParams p) {
     const bool ok = item_of(p, v, nitems, nseg, nbkt, w, done);
     if (done) break;
     if (!ok) continue;
+    const int row0 = w.tile * BT + kw * 32;  // the wave's first key (segment-relative)
+    const int krow = row0 + l32;
+    const bool kvalid = krow < w.L;
     if (p.segflag[w.seg] != 0) {  // a flagged segment: NaN rows (the order maps are not trusted there)
-      const int kr = w.tile * BT + wv * 32 + l32;
-      if (kr < w.L) {
-        const int64_t srow = w.s0 + kr;
+      if (kvalid) {
+        const int64_t srow = w.s0 + krow;
         const f32x16 nan16 = nan_acc();
         const f32x16 nan4[4] = {nan16, nan16, nan16, nan16};
-        store_row(nan4, 1.0f, 0, hh, p.dv + (srow * H + w.head) * HD);
-        if (p.wk) store_row_f32(nan4, 1.0f, 0, hh, p.dkh + (srow * H + w.head) * HD);
+        if (role == 0) store_row(nan4, 1.0f, 0, hh, p.dv + (srow * H + w.head) * HD);
+        else if (p.wk) store_row_f32(nan4, 1.0f, 0, hh, p.dkh + (srow * H + w.head) * HD);
         else store_row(nan4, 1.0f, 0, hh, p.dk + (srow * H + w.head) * HD);
       }
       continue;
@@ -431,103 +490,144 @@ __global__ __launch_bounds__(64 * BW, 1) void k_bwd_dkdv(BwdParams p) {
     const uint16_t* g16b = p.do16 + (hT + w.s0) * HD;
     const float* lb = p.lse2 + hT + w.s0;
     const float* db = p.delta + hT + w.s0;
-    const int row0 = w.tile * BT + wv * 32;  // the wave's first key (segment-relative)
-    const int krow = row0 + l32;
-    const bool kvalid = krow < w.L;
+    const int64_t srow = w.s0 + krow;
+    const int ex = -dout_scale_exp(p.dmax[(int64_t)w.seg * H + w.head]);
 
     // query tile j into stage ST (compile-time: the compiler sees that a copy never writes the
-    // stage being read)
+    // stage being read); all eight waves share the copies
     auto copies = [&](int j, auto stage) {
       constexpr int st = decltype(stage)::value;
       const int64_t o = (int64_t)j * TILE_ELEMS;
       const int v = w.L - j * TILE_ROWS;
-      tile_to_lds<BW>(q16b + o, v, lds + (0 + st) * TILE_ELEMS, wv, uoff);
-      tile_to_lds<BW>(g16b + o, v, lds + (2 + st) * TILE_ELEMS, wv, uoff);
+      tile_to_lds<BWK>(q16b + o, v, lds + (0 + st) * TILE_ELEMS, wv, uoff);
+      tile_to_lds<BWK>(g16b + o, v, lds + (2 + st) * TILE_ELEMS, wv, uoff);
       if (wv == 0) rowvec_to_lds(lb + j * TILE_ROWS, v, lrow3 + (2 * st + 0) * TILE_ROWS * 4, lane);
       if (wv == 1) rowvec_to_lds(db + j * TILE_ROWS, v, lrow3 + (2 * st + 1) * TILE_ROWS * 4, lane);
     };
-
-    copies(0, Par2<0>{});
-    f16x8 kf[8], vf[8];
-    load_b_rows(p.khat16 + (hT + w.s0 + row0) * HD, w.L - row0, l32, hh, kf);
-    load_b_rows(p.v16 + (hT + w.s0 + row0) * HD, w.L - row0, l32, hh, vf);
-
-    f32x16 dv[4], dk[4];
-#pragma unroll
-    for (int d = 0; d < 4; d++)
-#pragma unroll
-      for (int i = 0; i < 16; i++) dv[d][i] = dk[d][i] = 0.0f;
-
-    // Query tile j from stage ST: S = Q^ K^T and dP = dO V^T (query 32qb + 8(i/4) + 4hh + (i%4),
-    // the lane's key), P = exp2(S c - lse2) and dS = P (dP - D) in fp16, then dV^T += dO16^T P and
-    // dK^T += Q^16^T dS (one pipeline of 32 transposed-read MFMAs).
-    auto step = [&](auto stage, int j) {
-      constexpr int ST = decltype(stage)::value;
-      copies_barrier();  // tile j has landed, every wave is done with stage 1 - ST
-      if (j + 1 < ntq) copies(j + 1, Par2<1 - ST>{});
-      f32x16 S[2], dP[2];
-      f32x4 l4[2][4], d4[2][4];
-      // lse and D of the tile's queries, read as assembly: a plain LDS load here would make the
-      // compiler wait for every outstanding copy first (it cannot tell the copies' targets from
-      // these rows), which would expose the latency of the copies just issued
+    // lse (R = 0) or -D (R = 1) of the tile's queries in the S layout (query 32q2 + 8g + 4hh + i),
+    // read as assembly: a plain LDS load here would make the compiler wait for every outstanding
+    // copy first (it cannot tell the copies' targets from these rows), which would expose the
+    // latency of the copies just issued
+    auto rowvals = [&](auto stage, auto which, f32x4 (&r4)[2][4]) {
+      constexpr int ST = decltype(stage)::value, R = decltype(which)::value;
       static_for2<0, 8>([&](auto gi) {
         constexpr int q2 = decltype(gi)::value >> 2, g = decltype(gi)::value & 3;
-        l4[q2][g] = __builtin_bit_cast(f32x4, ds_read_b128_asm<((2 * ST + 0) * TILE_ROWS + 32 * q2 + 8 * g) * 4>(lrow_lane));
-        d4[q2][g] = __builtin_bit_cast(f32x4, ds_read_b128_asm<((2 * ST + 1) * TILE_ROWS + 32 * q2 + 8 * g) * 4>(lrow_lane));
+        r4[q2][g] = __builtin_bit_cast(f32x4, ds_read_b128_asm<((2 * ST + R) * TILE_ROWS + 32 * q2 + 8 * g) * 4>(lrow_lane));
       });
-      gemm_rows<0 + ST>(rb, kf, S, [](auto) {});
-      // the lse/D reads complete here, before the next pipelines count their own reads
-      asm volatile("s_waitcnt lgkmcnt(0)" : "+v"(l4[0][0]), "+v"(d4[0][0]));
+    };
+    auto rowvals_wait = [&](f32x4 (&r4)[2][4]) {
+      asm volatile("s_waitcnt lgkmcnt(0)" : "+v"(r4[0][0]));
 #pragma unroll
       for (int q2 = 0; q2 < 2; q2++)
 #pragma unroll
-        for (int g = 0; g < 4; g++) asm volatile("" : "+v"(l4[q2][g]), "+v"(d4[q2][g]));
-      // P (two elements per step, a packed 8-query slice every fourth step) between the dP MFMAs,
-      // and dS between the dV MFMAs (which only need P); dK's MFMAs start after the last dS slice.
-      float pr[2][16], ds[2][16];
-      f16x8 pf[4], dsf[4];
-      gemm_rows<2 + ST>(rb, vf, dP, [&](auto st) {
-        constexpr int s = decltype(st)::value;
-#pragma unroll
-        for (int u = 0; u < 2; u++) {
-          const int e = 2 * s + u, q2 = e >> 4, i = e & 15;
-          pr[q2][i] = __builtin_amdgcn_exp2f(__builtin_fmaf(S[q2][i], c, -l4[q2][i >> 2][i & 3]));
-        }
-        if constexpr ((s & 3) == 3) pf[s >> 2] = pack_p(&pr[s >> 3][8 * ((s >> 2) & 1)]);
-      });
-      const f16x8* bop[2] = {pf, dsf};
-      f32x16* acc[2] = {dv, dk};
-      tr_gemm_hooked<TilePair<2 + ST, 0 + ST>, 2>(vb, bop, acc, [&](auto st) {
-        constexpr int s = decltype(st)::value;
-        if constexpr (s < 16) {
-#pragma unroll
-          for (int u = 0; u < 2; u++) {
-            const int e = 2 * s + u, q2 = e >> 4, i = e & 15;
-            ds[q2][i] = pr[q2][i] * (dP[q2][i] + d4[q2][i >> 2][i & 3]);  // d4 holds -D
-          }
-          if constexpr ((s & 3) == 3) dsf[s >> 2] = pack_p(&ds[s >> 3][8 * ((s >> 2) & 1)]);
-        }
-      });
+        for (int g = 0; g < 4; g++) asm volatile("" : "+v"(r4[q2][g]));
     };
-    {
+
+    copies(0, Par2<0>{});
+    if (role == 0) {
+      f16x8 kf[8];
+      load_b_rows(p.khat16 + (hT + w.s0 + row0) * HD, w.L - row0, l32, hh, kf);
+      f32x16 dv[4];
+#pragma unroll
+      for (int d = 0; d < 4; d++)
+#pragma unroll
+        for (int i = 0; i < 16; i++) dv[d][i] = 0.0f;
+      // query tile j from stage ST: S = Q^ K^T (query 32q2 + 8(i/4) + 4hh + (i%4), the lane's
+      // key), P = exp2(S c - lse2) to the exchange, then dV^T += dO16^T P16
+      auto step = [&](auto stage, int j) {
+        constexpr int ST = decltype(stage)::value;
+        copies_barrier();  // tile j has landed, every wave is done with stage 1 - ST
+        if (j + 1 < ntq) copies(j + 1, Par2<1 - ST>{});
+        f32x4 l4[2][4];
+        rowvals(stage, Par2<0>{}, l4);
+        f32x16 S[2];
+        float pr[2][16];
+        // block-major S: block 0 is complete after step 7, and its P is formed between the MFMAs of
+        // block 1 (two elements per step)
+        gemm_rows<0 + ST, 4, true>(rb, kf, S, [&](auto st) {
+          constexpr int s = decltype(st)::value;
+          if constexpr (s == 0) {  // step 0 waited for every read but the newest four: the lse rows are in
+            asm volatile("s_waitcnt lgkmcnt(4)" : "+v"(l4[0][0]), "+v"(l4[0][1]), "+v"(l4[0][2]), "+v"(l4[0][3]),
+                         "+v"(l4[1][0]), "+v"(l4[1][1]), "+v"(l4[1][2]), "+v"(l4[1][3]));
+          }
+          if constexpr (s >= 8) {
+#pragma unroll
+            for (int u = 0; u < 2; u++) {
+              const int i = 2 * (s - 8) + u;
+              pr[0][i] = __builtin_amdgcn_exp2f(__builtin_fmaf(S[0][i], c, -l4[0][i >> 2][i & 3]));
+            }
+          }
+        });
+#pragma unroll
+        for (int i = 0; i < 16; i++) pr[1][i] = __builtin_amdgcn_exp2f(__builtin_fmaf(S[1][i], c, -l4[1][i >> 2][i & 3]));
+        xch_write(xch, pr);
+        phase_barrier();  // P of tile j is visible to the dS waves
+        f16x8 pf[4];
+#pragma unroll
+        for (int sl = 0; sl < 4; sl++) pf[sl] = pack_p(&pr[sl >> 1][8 * (sl & 1)]);
+        const f16x8* bop[1] = {pf};
+        f32x16* acc[1] = {dv};
+        tr_gemm_hooked<TilePair<2 + ST, 2 + ST>, 1>(vb, bop, acc, [](auto) {});
+      };
       int j = 0;
       for (; j + 1 < ntq; j += 2) {
         step(Par2<0>{}, j);
         step(Par2<1>{}, j + 1);
       }
       if (j < ntq) step(Par2<0>{}, j);
-    }
-
-    // ---- epilogue: dv 2^-s, dk^ = scale dK 2^-s (fp32 for the norm backward, else the output itself)
-    if (kvalid) {
-      const int64_t srow = w.s0 + krow;
-      const int64_t trow = p.inv ? (int64_t)p.inv[srow] : srow;
-      const int ex = -dout_scale_exp(p.dmax[(int64_t)w.seg * H + w.head]);
-      store_row(dv, 1.0f, ex, hh, p.dv + (trow * H + w.head) * HD);
-      if (p.wk)
-        store_row_f32(dk, p.scale, ex, hh, p.dkh + (srow * H + w.head) * HD);
-      else
-        store_row(dk, p.scale, ex, hh, p.dk + (trow * H + w.head) * HD);
+      // ---- epilogue: dv 2^-s
+      if (kvalid) {
+        const int64_t trow = p.inv ? (int64_t)p.inv[srow] : srow;
+        store_row(dv, 1.0f, ex, hh, p.dv + (trow * H + w.head) * HD);
+      }
+    } else {
+      f16x8 vf[8];
+      load_b_rows(p.v16 + (hT + w.s0 + row0) * HD, w.L - row0, l32, hh, vf);
+      f32x16 dk[4];
+#pragma unroll
+      for (int d = 0; d < 4; d++)
+#pragma unroll
+        for (int i = 0; i < 16; i++) dk[d][i] = 0.0f;
+      // query tile j from stage ST: dP = dO V^T, then (once P is in the exchange) dS = P (dP - D)
+      // in fp16 and dK^T += Q^16^T dS
+      auto step = [&](auto stage, int j) {
+        constexpr int ST = decltype(stage)::value;
+        copies_barrier();  // tile j has landed, every wave is done with stage 1 - ST
+        if (j + 1 < ntq) copies(j + 1, Par2<1 - ST>{});
+        f32x4 d4[2][4];
+        rowvals(stage, Par2<1>{}, d4);
+        f32x16 dP[2];
+        gemm_rows<2 + ST>(rb, vf, dP, [](auto) {});
+        rowvals_wait(d4);
+        phase_barrier();  // P of tile j is in the exchange
+        float pr[2][16], ds[2][16];
+        xch_read(xch, pr);
+#pragma unroll
+        for (int q2 = 0; q2 < 2; q2++)
+#pragma unroll
+          for (int i = 0; i < 16; i++) ds[q2][i] = pr[q2][i] * (dP[q2][i] + d4[q2][i >> 2][i & 3]);  // d4 holds -D
+        f16x8 dsf[4];
+#pragma unroll
+        for (int sl = 0; sl < 4; sl++) dsf[sl] = pack_p(&ds[sl >> 1][8 * (sl & 1)]);
+        const f16x8* bop[1] = {dsf};
+        f32x16* acc[1] = {dk};
+        tr_gemm_hooked<TilePair<0 + ST, 0 + ST>, 1>(vb, bop, acc, [](auto) {});
+      };
+      int j = 0;
+      for (; j + 1 < ntq; j += 2) {
+        step(Par2<0>{}, j);
+        step(Par2<1>{}, j + 1);
+      }
+      if (j < ntq) step(Par2<0>{}, j);
+      // ---- epilogue: dk^ = scale dK 2^-s (fp32 for the norm backward, else the output itself)
+      if (kvalid) {
+        if (p.wk) {
+          store_row_f32(dk, p.scale, ex, hh, p.dkh + (srow * H + w.head) * HD);
+        } else {
+          const int64_t trow = p.inv ? (int64_t)p.inv[srow] : srow;
+          store_row(dk, p.scale, ex, hh, p.dk + (trow * H + w.head) * HD);
+        }
+      }
     }
   }
 }
@@ -725,7 +825,7 @@ hipError_t launch_bwd(const void* q, const void* k, const void* wq, const void* 
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   p.next = &((WsHeader*)base)->next[1];
-  hipLaunchKernelGGL(k_bwd_dkdv, dim3((unsigned)grid), dim3(64 * BW), 0, stream, p);
+  hipLaunchKernelGGL(k_bwd_dkdv, dim3((unsigned)grid), dim3(64 * BWK), 0, stream, p);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
   if (wq) {
