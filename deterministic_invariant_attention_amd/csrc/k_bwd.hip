@@ -740,9 +740,9 @@ __global__ __launch_bounds__(256) void k_bwd_norm(NormBwdParams p) {
 }
 
 // dw = the workgroup partials summed in a fixed tree whose shape depends only on their number:
-// chunks of DW_CHUNK consecutive partials in order, then the chunks in order.  Several independent
-// loads are kept in flight per thread (the sums themselves stay sequential).  blockIdx.y: 0 = q,
-// 1 = k; thread = channel.
+// each chunk of DW_CHUNK consecutive partials as its two halves, each summed in order, then added;
+// the chunks as eight consecutive runs, each summed in order, then added pairwise.  Several
+// independent loads are kept in flight per thread (the sums themselves stay sequential).
 
 __device__ __forceinline__ float sum_strided(const float* base, int64_t n, int64_t stride) {
   float s = 0.0f;
@@ -758,27 +758,43 @@ __device__ __forceinline__ float sum_strided(const float* base, int64_t n, int64
   return s;
 }
 
-__global__ __launch_bounds__(HD) void k_bwd_dw_chunks(const WsHeader* hdr, const float* part, int64_t nparts,
-                                                      int64_t nchunks, float* chunk_part) {
-  const int d = threadIdx.x, which = blockIdx.y;
+// blockIdx.y: 0 = q, 1 = k; thread = (half, channel).
+__global__ __launch_bounds__(2 * HD) void k_bwd_dw_chunks(const WsHeader* hdr, const float* part, int64_t nparts,
+                                                          int64_t nchunks, float* chunk_part) {
+  __shared__ float upper[HD];
+  const int d = threadIdx.x & (HD - 1), g = threadIdx.x >> 7, which = blockIdx.y;
   if (hdr->status != 0) return;
   for (int64_t ch = blockIdx.x; ch < nchunks; ch += gridDim.x) {
     const int64_t i0 = ch * DW_CHUNK, cnt = min((int64_t)DW_CHUNK, nparts - i0);
-    chunk_part[((int64_t)which * nchunks + ch) * HD + d] =
-        sum_strided(part + ((int64_t)which * nparts + i0) * HD + d, cnt, HD);
+    const int64_t lo = min(cnt, (int64_t)(DW_CHUNK / 2));
+    const float* b = part + ((int64_t)which * nparts + i0) * HD + d;
+    const float sh = g == 0 ? sum_strided(b, lo, HD) : sum_strided(b + lo * HD, cnt - lo, HD);
+    if (g == 1) upper[d] = sh;
+    __syncthreads();
+    if (g == 0) chunk_part[((int64_t)which * nchunks + ch) * HD + d] = sh + upper[d];
+    __syncthreads();
   }
 }
 
-// With a recorded data error the weights' gradients are NaN like the other outputs.
-__global__ __launch_bounds__(2 * HD) void k_bwd_dw_final(const WsHeader* hdr, const float* chunk_part, int64_t nchunks,
-                                                         float* dwq, float* dwk) {
-  const int t = threadIdx.x, d = t & (HD - 1), which = t >> 7;
+// With a recorded data error the weights' gradients are NaN like the other outputs.  blockIdx.x:
+// 0 = q, 1 = k; thread = (run, channel).
+constexpr int DW_RUNS = 8;
+__global__ __launch_bounds__(DW_RUNS * HD) void k_bwd_dw_final(const WsHeader* hdr, const float* chunk_part,
+                                                               int64_t nchunks, float* dwq, float* dwk) {
+  __shared__ float run[DW_RUNS][HD];
+  const int d = threadIdx.x & (HD - 1), g = threadIdx.x >> 7, which = blockIdx.x;
   float* out = which ? dwk : dwq;
   if (hdr->status != 0) {
-    out[d] = __builtin_nanf("");
+    if (g == 0) out[d] = __builtin_nanf("");
     return;
   }
-  out[d] = sum_strided(chunk_part + (int64_t)which * nchunks * HD + d, nchunks, HD);
+  const int64_t per = (nchunks + DW_RUNS - 1) / DW_RUNS;
+  const int64_t c0 = min(nchunks, g * per), c1 = min(nchunks, c0 + per);
+  run[g][d] = sum_strided(chunk_part + ((int64_t)which * nchunks + c0) * HD + d, c1 - c0, HD);
+  __syncthreads();
+  static_assert(DW_RUNS == 8, "the pairwise tree below");
+  if (g == 0)
+    out[d] = ((run[0][d] + run[1][d]) + (run[2][d] + run[3][d])) + ((run[4][d] + run[5][d]) + (run[6][d] + run[7][d]));
 }
 
 hipError_t launch_bwd(const void* q, const void* k, const void* wq, const void* wk, int64_t T, int32_t H, float eps,
@@ -852,9 +868,9 @@ hipError_t launch_bwd(const void* q, const void* k, const void* wq, const void* 
     hipLaunchKernelGGL(k_bwd_norm, dim3((unsigned)Lw.nparts, 2), dim3(256), 0, stream, np);
     float* chunk_part = (float*)(base + Lw.dw_chunk);
     const unsigned g2 = (unsigned)(Lw.nchunks < 1024 ? Lw.nchunks : 1024);
-    hipLaunchKernelGGL(k_bwd_dw_chunks, dim3(g2, 2), dim3(HD), 0, stream, (const WsHeader*)base, np.part, Lw.nparts,
-                       Lw.nchunks, chunk_part);
-    hipLaunchKernelGGL(k_bwd_dw_final, dim3(1), dim3(2 * HD), 0, stream, (const WsHeader*)base, chunk_part,
+    hipLaunchKernelGGL(k_bwd_dw_chunks, dim3(g2, 2), dim3(2 * HD), 0, stream, (const WsHeader*)base, np.part,
+                       Lw.nparts, Lw.nchunks, chunk_part);
+    hipLaunchKernelGGL(k_bwd_dw_final, dim3(2), dim3(DW_RUNS * HD), 0, stream, (const WsHeader*)base, chunk_part,
                        Lw.nchunks, dwq, dwk);
     e = hipGetLastError();
   }

@@ -162,10 +162,12 @@ struct BwdPrepParams {
 };
 
 // The largest |dO| of every (segment, head): one workgroup per 64 tokens of one head (workgroup b:
-// head b % H, tokens 64 (b / H) ..), 16 lanes per (token, head) row.  Each row's maximum (bf16 magnitude bits, exact integers) goes to
-// LDS; thread 0 then walks the block's 64 tokens and, at the end of each run of one segment, folds
-// the run's maximum into the segment's slot with an integer atomicMax, so the result is the same
-// whatever the order of the workgroups.
+// head b % H, tokens 64 (b / H) ..), 16 lanes per (token, head) row.  Each row's maximum (bf16
+// magnitude bits, exact integers) goes to LDS; the first wave, one lane per token, takes a
+// segmented running maximum over the block's tokens (segments are runs of tokens, so a lane o
+// places back belongs to the same run exactly when it has the same segment), and the last lane of
+// each run folds the run's maximum into the segment's slot with an integer atomicMax, so the result
+// is the same whatever the order of the workgroups.
 constexpr int DMAX_TOK = 64;  // tokens per workgroup
 
 __global__ __launch_bounds__(256) void k_bwd_dmax(const uint16_t* __restrict__ dout, const int32_t* __restrict__ tok2seg,
@@ -206,18 +208,21 @@ __global__ __launch_bounds__(256) void k_bwd_dmax(const uint16_t* __restrict__ d
     }
   }
   __syncthreads();
-  if (threadIdx.x == 0) {
+  static_assert(DMAX_TOK == 64, "one lane per token of the block");
+  if (threadIdx.x < DMAX_TOK) {
+    const int i = threadIdx.x;
     const int nseg = hdr->nseg;  // 0 after a segment-id error: nothing is folded
-    uint32_t run = 0;
-    for (int i = 0; i < DMAX_TOK; i++) {
-      const int sg = s_seg[i];
-      run = s_max[i] > run ? s_max[i] : run;
-      const bool last = i + 1 == DMAX_TOK || s_seg[i + 1] != sg;
-      if (last) {
-        if (sg >= 0 && sg < nseg) atomicMax(&dmax[(int64_t)sg * H + h], run);
-        run = 0;
-      }
+    const int sg = s_seg[i];
+    uint32_t m = s_max[i];
+#pragma unroll
+    for (int o = 1; o < DMAX_TOK; o <<= 1) {
+      const uint32_t y = (uint32_t)__shfl_up((int)m, o, 64);
+      const int ys = __shfl_up(sg, o, 64);
+      if (i >= o && ys == sg) m = y > m ? y : m;
     }
+    const int next = __shfl_down(sg, 1, 64);
+    const bool last = i + 1 == DMAX_TOK || next != sg;
+    if (last && sg >= 0 && sg < nseg) atomicMax(&dmax[(int64_t)sg * H + h], m);
   }
 }
 
