@@ -670,36 +670,38 @@ __global__ __launch_bounds__(256) void k_bwd_norm(NormBwdParams p) {
   if (p.hdr->status & STATUS_SEG_BIT) return;  // the attention kernels have filled the outputs with NaN
   // A staged row lies in the rows of the same segment as the token of that index, so tok2seg names
   // its segment.  In a flagged segment the order maps may be invalid: the row is NaN and stays at
-  // its own index.
-  // dy, and x in packed order, do not depend on the segment's flag: their loads go out first
+  // its own index (every flag also sets the status, so dw is NaN then and the row's terms in it do
+  // not matter).  Loads are unconditional, from clamped indices, so the independent ones go out
+  // together: dy, w, the segment and (position order) the token first, then the flag, x and the
+  // rotary table.
   const bool pos = p.inv != nullptr;
-  u32x4 xv = {0, 0, 0, 0};
-  f32x4 d0 = {0.0f, 0.0f, 0.0f, 0.0f}, d1 = d0;
-  if (valid) {
-    d0 = *(const f32x4*)(p.dy[which] + row * HD + 8 * c);
-    d1 = *(const f32x4*)(p.dy[which] + row * HD + 8 * c + 4);
-    if (!pos) xv = *(const u32x4*)(p.x[which] + row * HD + 8 * c);
+  const int64_t rc = valid ? row : p.rows - 1;
+  const int64_t T = p.rows / p.H;
+  const int64_t sl = rc / p.H;
+  const f32x4 d0 = *(const f32x4*)(p.dy[which] + rc * HD + 8 * c);
+  const f32x4 d1 = *(const f32x4*)(p.dy[which] + rc * HD + 8 * c + 4);
+  const u32x4 wv = *(const u32x4*)(p.w[which] + 8 * c);
+  const int sg = p.tok2seg[sl];
+  int64_t tok = sl;  // the token of the staged row
+  if (pos) {
+    const int64_t t = p.inv[sl];
+    tok = t >= 0 && t < T ? t : sl;
   }
-  bool bad = false;
-  int64_t xrow = row;  // the token's row
-  if (valid) {
-    const int64_t sl = row / p.H;
-    const int sg = p.tok2seg[sl];
-    const int nseg = p.hdr->nseg;
-    bad = sg >= 0 && sg < nseg && p.segflag[sg] != 0;
-    if (pos && !bad) xrow = (int64_t)p.inv[sl] * p.H + (row - sl * p.H);
-  }
-  if (valid && pos) xv = *(const u32x4*)(p.x[which] + xrow * HD + 8 * c);
+  const int nseg = p.hdr->nseg;
+  const bool sg_ok = sg >= 0 && sg < nseg;
+  const bool bad = valid && sg_ok && p.segflag[sg_ok ? sg : 0] != 0;
+  const int64_t xt = tok * p.H + (rc - sl * p.H);  // the token's row
+  const u32x4 xv = *(const u32x4*)(p.x[which] + xt * HD + 8 * c);
+  const int64_t xrow = bad ? row : xt;  // where dx goes
 
   float x[8], wf[8];
   double dy[8];  // the gradient with respect to the norm's output (through the rope when given)
   {
     unpack8_bf16(xv, x);
-    unpack8_bf16(*(const u32x4*)(p.w[which] + 8 * c), wf);
+    unpack8_bf16(wv, wf);
 #pragma unroll
     for (int i = 0; i < 4; i++) dy[i] = (double)d0[i], dy[4 + i] = (double)d1[i];
-    if (p.rope_cos && valid && c < ROPE_CHUNKS) {
-      const int64_t tok = xrow / p.H;
+    if (p.rope_cos && c < ROPE_CHUNKS) {
       const f32x4 cs = *(const f32x4*)(p.rope_cos + tok * ROPE_PAIRS + 4 * c);
       const f32x4 sn = *(const f32x4*)(p.rope_sin + tok * ROPE_PAIRS + 4 * c);
       rope_chunk_transpose(dy, cs, sn);

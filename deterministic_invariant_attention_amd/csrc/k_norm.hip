@@ -161,39 +161,46 @@ struct BwdPrepParams {
   float eps;
 };
 
-// The largest |dO| of every (segment, head): one workgroup per 64 tokens of one head (workgroup b:
-// head b % H, tokens 64 (b / H) ..), 16 lanes per (token, head) row.  Each row's maximum (bf16
-// magnitude bits, exact integers) goes to LDS; the first wave, one lane per token, takes a
-// segmented running maximum over the block's tokens (segments are runs of tokens, so a lane o
-// places back belongs to the same run exactly when it has the same segment), and the last lane of
-// each run folds the run's maximum into the segment's slot with an integer atomicMax, so the result
-// is the same whatever the order of the workgroups.
-constexpr int DMAX_TOK = 64;  // tokens per workgroup
+// The largest |dO| of every (segment, head): one workgroup per 16 tokens x 16 heads (workgroup
+// b: tokens 16 (b / n) .., heads 16 (b % n) .., n = ceil(H / 16)), so each pass of 16 rows reads one token's 16 heads, 4 KB
+// in a row; 16 lanes per (token, head) row.  Each row's maximum (bf16 magnitude bits, exact
+// integers) goes to LDS; then 16 lanes per head, one per token, take a segmented running maximum
+// over the block's tokens (segments are runs of tokens, so a lane o places back belongs to the
+// same run exactly when it has the same segment), and the last lane of each run folds the run's
+// maximum into the segment's slot with an integer atomicMax, so the result is the same whatever the
+// order of the workgroups.
+constexpr int DMAX_TOK = 16;  // tokens per workgroup
+constexpr int DMAX_HEADS = 16;  // heads per workgroup
 
 __global__ __launch_bounds__(256) void k_bwd_dmax(const uint16_t* __restrict__ dout, const int32_t* __restrict__ tok2seg,
                                                   uint32_t* __restrict__ dmax, const WsHeader* hdr, int64_t T,
                                                   int32_t H) {
-  __shared__ uint32_t s_max[DMAX_TOK];
+  __shared__ uint32_t s_max[DMAX_TOK][DMAX_HEADS];
   __shared__ int32_t s_seg[DMAX_TOK];
-  const int c = threadIdx.x & 15;
-  const int h = (int)(blockIdx.x % (unsigned)H);
-  const int64_t t0 = (int64_t)(blockIdx.x / (unsigned)H) * DMAX_TOK;
-  // every load of the block's rows is issued before the first is reduced
-  u32x4 w[DMAX_TOK / 16];
+  const int c = threadIdx.x & 15, rr = threadIdx.x >> 4;  // lane in the row, row in the pass (= head)
+  const int nhc = (H + DMAX_HEADS - 1) / DMAX_HEADS;
+  const int64_t t0 = (int64_t)(blockIdx.x / (unsigned)nhc) * DMAX_TOK;
+  const int h0 = (int)(blockIdx.x % (unsigned)nhc) * DMAX_HEADS;
+  const int h = h0 + rr;
+  // every load of the block's rows is issued before the first is reduced: rows past the end read
+  // the last row (no branch around the loads) and count as zero
+  u32x4 w[DMAX_TOK];
+  const int hc = h < H ? h : H - 1;
 #pragma unroll
-  for (int it = 0; it < DMAX_TOK / 16; it++) {
-    const int64_t t = t0 + it * 16 + (threadIdx.x >> 4);
-    const u32x4 zero = {0u, 0u, 0u, 0u};
-    w[it] = t < T ? *(const u32x4*)(dout + (t * H + h) * HD + c * 8) : zero;
+  for (int i = 0; i < DMAX_TOK; i++) {
+    const int64_t t = t0 + i < T ? t0 + i : T - 1;
+    w[i] = *(const u32x4*)(dout + (t * H + hc) * HD + c * 8);
   }
 #pragma unroll
-  for (int it = 0; it < DMAX_TOK / 16; it++) {
-    const int i = it * 16 + (threadIdx.x >> 4);  // token within the block
-    const int64_t t = t0 + i;
+  for (int i = 0; i < DMAX_TOK; i++)
+    if (t0 + i >= T || h >= H) w[i] = u32x4{0u, 0u, 0u, 0u};
+  if (threadIdx.x < DMAX_TOK) s_seg[threadIdx.x] = t0 + threadIdx.x < T ? tok2seg[t0 + threadIdx.x] : -1;
+#pragma unroll
+  for (int i = 0; i < DMAX_TOK; i++) {
     uint32_t m = 0;
 #pragma unroll
     for (int j = 0; j < 4; j++) {
-      const uint32_t a = w[it][j] & 0x7FFFu, b = (w[it][j] >> 16) & 0x7FFFu;
+      const uint32_t a = w[i][j] & 0x7FFFu, b = (w[i][j] >> 16) & 0x7FFFu;
       m = a > m ? a : m;
       m = b > m ? b : m;
     }
@@ -202,27 +209,24 @@ __global__ __launch_bounds__(256) void k_bwd_dmax(const uint16_t* __restrict__ d
       const uint32_t y = (uint32_t)__shfl_xor((int)m, o, 64);
       m = y > m ? y : m;
     }
-    if (c == 0) {
-      s_max[i] = m;
-      s_seg[i] = t < T ? tok2seg[t] : -1;
-    }
+    if (c == 0) s_max[i][rr] = m;
   }
   __syncthreads();
-  static_assert(DMAX_TOK == 64, "one lane per token of the block");
-  if (threadIdx.x < DMAX_TOK) {
-    const int i = threadIdx.x;
+  // fold: lane (head rr, token c)
+  {
+    const int i = c;
     const int nseg = hdr->nseg;  // 0 after a segment-id error: nothing is folded
     const int sg = s_seg[i];
-    uint32_t m = s_max[i];
+    uint32_t m = s_max[i][rr];
 #pragma unroll
     for (int o = 1; o < DMAX_TOK; o <<= 1) {
-      const uint32_t y = (uint32_t)__shfl_up((int)m, o, 64);
-      const int ys = __shfl_up(sg, o, 64);
+      const uint32_t y = (uint32_t)__shfl_up((int)m, o, 16);
+      const int ys = __shfl_up(sg, o, 16);
       if (i >= o && ys == sg) m = y > m ? y : m;
     }
-    const int next = __shfl_down(sg, 1, 64);
+    const int next = __shfl_down(sg, 1, 16);
     const bool last = i + 1 == DMAX_TOK || next != sg;
-    if (last && sg >= 0 && sg < nseg) atomicMax(&dmax[(int64_t)sg * H + h], m);
+    if (last && h < H && sg >= 0 && sg < nseg) atomicMax(&dmax[(int64_t)sg * H + h], m);
   }
 }
 
@@ -359,7 +363,8 @@ hipError_t launch_bwd_prep(const void* q, const void* k, const void* v, const vo
   p.T = T;
   p.H = H;
   p.eps = eps;
-  hipLaunchKernelGGL(k_bwd_dmax, dim3((unsigned)((T + DMAX_TOK - 1) / DMAX_TOK * H)), dim3(256), 0, stream,
+  hipLaunchKernelGGL(k_bwd_dmax, dim3((unsigned)((T + DMAX_TOK - 1) / DMAX_TOK * ((H + DMAX_HEADS - 1) / DMAX_HEADS))),
+                     dim3(256), 0, stream,
                      (const uint16_t*)dout, p.tok2seg, (uint32_t*)(base + L.dmax), (const WsHeader*)base, T, H);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
