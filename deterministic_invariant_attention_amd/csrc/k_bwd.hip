@@ -379,65 +379,48 @@ __global__ __launch_bounds__(64 * BW, 2) void k_bwd_dq(BwdParams p) {
 
 // ============================================================================== dk, dv
 
-// The P exchange of the dk/dv kernel: wave kw of the P role writes the 32 fp32 P values of each of
-// its lanes (lane-major 16-byte pieces, so both sides are free of bank conflicts) and wave kw + 4
-// reads them back after a barrier; one asm block each, with the wait inside, so no register of the
-// exchange is touched while an LDS operation on it is in flight.
-__device__ __forceinline__ void xch_write(uint32_t a, const float (&pr)[2][16]) {
-  const f32x4 v0 = {pr[0][0], pr[0][1], pr[0][2], pr[0][3]}, v1 = {pr[0][4], pr[0][5], pr[0][6], pr[0][7]};
-  const f32x4 v2 = {pr[0][8], pr[0][9], pr[0][10], pr[0][11]}, v3 = {pr[0][12], pr[0][13], pr[0][14], pr[0][15]};
-  const f32x4 v4 = {pr[1][0], pr[1][1], pr[1][2], pr[1][3]}, v5 = {pr[1][4], pr[1][5], pr[1][6], pr[1][7]};
-  const f32x4 v6 = {pr[1][8], pr[1][9], pr[1][10], pr[1][11]}, v7 = {pr[1][12], pr[1][13], pr[1][14], pr[1][15]};
+// The P exchange of the dk/dv kernel: wave kw of the P role writes its lanes' packed fp16 P (the
+// B operand of its dV products; lane-major 16-byte pieces, so both sides are free of bank
+// conflicts) and wave kw + 4 reads it back after a barrier; one asm block each, with the wait
+// inside, so no register of the exchange is touched while an LDS operation on it is in flight.
+__device__ __forceinline__ void xch_write(uint32_t a, const f16x8 (&pf)[4]) {
   asm volatile(
       "ds_write_b128 %0, %1\n\t"
       "ds_write_b128 %0, %2 offset:1024\n\t"
       "ds_write_b128 %0, %3 offset:2048\n\t"
       "ds_write_b128 %0, %4 offset:3072\n\t"
-      "ds_write_b128 %0, %5 offset:4096\n\t"
-      "ds_write_b128 %0, %6 offset:5120\n\t"
-      "ds_write_b128 %0, %7 offset:6144\n\t"
-      "ds_write_b128 %0, %8 offset:7168\n\t"
       "s_waitcnt lgkmcnt(0)"
       :
-      : "v"(a), "v"(v0), "v"(v1), "v"(v2), "v"(v3), "v"(v4), "v"(v5), "v"(v6), "v"(v7)
+      : "v"(a), "v"(pf[0]), "v"(pf[1]), "v"(pf[2]), "v"(pf[3])
       : "memory");
 }
-__device__ __forceinline__ void xch_read(uint32_t a, float (&pr)[2][16]) {
-  f32x4 v0, v1, v2, v3, v4, v5, v6, v7;
+__device__ __forceinline__ void xch_read(uint32_t a, f16x8 (&pf)[4]) {
+  f16x8 v0, v1, v2, v3;
   asm volatile(
-      "ds_read_b128 %0, %8\n\t"
-      "ds_read_b128 %1, %8 offset:1024\n\t"
-      "ds_read_b128 %2, %8 offset:2048\n\t"
-      "ds_read_b128 %3, %8 offset:3072\n\t"
-      "ds_read_b128 %4, %8 offset:4096\n\t"
-      "ds_read_b128 %5, %8 offset:5120\n\t"
-      "ds_read_b128 %6, %8 offset:6144\n\t"
-      "ds_read_b128 %7, %8 offset:7168\n\t"
+      "ds_read_b128 %0, %4\n\t"
+      "ds_read_b128 %1, %4 offset:1024\n\t"
+      "ds_read_b128 %2, %4 offset:2048\n\t"
+      "ds_read_b128 %3, %4 offset:3072\n\t"
       "s_waitcnt lgkmcnt(0)"
-      : "=&v"(v0), "=&v"(v1), "=&v"(v2), "=&v"(v3), "=&v"(v4), "=&v"(v5), "=&v"(v6), "=&v"(v7)
+      : "=&v"(v0), "=&v"(v1), "=&v"(v2), "=&v"(v3)
       : "v"(a)
       : "memory");
-  const f32x4 v[8] = {v0, v1, v2, v3, v4, v5, v6, v7};
-#pragma unroll
-  for (int g = 0; g < 8; g++)
-#pragma unroll
-    for (int i = 0; i < 4; i++) pr[g >> 2][4 * (g & 3) + i] = v[g][i];
+  pf[0] = v0; pf[1] = v1; pf[2] = v2; pf[3] = v3;
 }
 
 // Eight waves, two per SIMD, in two roles over the same 128 keys: wave kw (< 4) recomputes
-// S = Q^ K^T and P for keys 32kw .. 32kw + 31, hands P to wave kw + 4 through LDS and accumulates
-// dV^T += dO16^T P; wave kw + 4 computes dP = dO V^T, dS = P (dP - D) and dK^T += Q^16^T dS.  Waves
-// kw and kw + 4 share a SIMD, so each one's vector work runs beside the other's MFMAs.  Every
-// accumulator sees the same products in the same order as in one wave doing all four, so the
-// split does not change a bit.
+// S = Q^ K^T and P for keys 32kw .. 32kw + 31, hands P (fp16, as its dV products take it) to wave
+// kw + 4 through LDS and accumulates dV^T += dO16^T P; wave kw + 4 computes dP = dO V^T,
+// dS = P (dP - D) and dK^T += Q^16^T dS.  Waves kw and kw + 4 share a SIMD, so each one's vector
+// work runs beside the other's MFMAs.
 constexpr int BWK = 2 * BW;
 
 __global__ __launch_bounds__(64 * BWK, 1) void k_bwd_dkdv(BwdParams p) {
   // tiles 0, 1: Q^16 and 2, 3: dO16 of stage 0 / 1, in the unified layout (read by rows for S and
   // dP, transposed for dK and dV); then the fp32 rows [stage][lse2, D][64 queries]; then the P
-  // exchange, 8 KB per key block
+  // exchange, 4 KB per key block
   constexpr int XCH_OFF = 4 * TILE_ELEMS * 2 + 2 * 2 * TILE_ROWS * 4;
-  __shared__ __attribute__((aligned(1024))) uint16_t lds[XCH_OFF / 2 + BW * 64 * 32 * 2];
+  __shared__ __attribute__((aligned(1024))) uint16_t lds[XCH_OFF / 2 + BW * 64 * 32];
   lds_char* const lrow3 = (lds_char*)lds + 4 * TILE_ELEMS * 2;  // the same rows as an LDS address
 
   const int tid = threadIdx.x;
@@ -457,7 +440,7 @@ __global__ __launch_bounds__(64 * BWK, 1) void k_bwd_dkdv(BwdParams p) {
   tr_bases_u(lds, lane, vb);
   const RowBases rb = row_bases_u(lds, l32, hh);
   const uint32_t lrow_lane = (uint32_t)(size_t)lrow3 + 16 * hh;  // lrow[4hh] as an LDS byte address
-  const uint32_t xch = (uint32_t)(size_t)((lds_char*)lds + XCH_OFF) + kw * 8192 + lane * 16;
+  const uint32_t xch = (uint32_t)(size_t)((lds_char*)lds + XCH_OFF) + kw * 4096 + lane * 16;
   const float c = p.c;
 
   const int nbkt = min(max(p.hdr->nbkt, 0), NBKT);
@@ -560,11 +543,11 @@ __global__ __launch_bounds__(64 * BWK, 1) void k_bwd_dkdv(BwdParams p) {
         });
 #pragma unroll
         for (int i = 0; i < 16; i++) pr[1][i] = __builtin_amdgcn_exp2f(__builtin_fmaf(S[1][i], c, -l4[1][i >> 2][i & 3]));
-        xch_write(xch, pr);
-        phase_barrier();  // P of tile j is visible to the dS waves
         f16x8 pf[4];
 #pragma unroll
         for (int sl = 0; sl < 4; sl++) pf[sl] = pack_p(&pr[sl >> 1][8 * (sl & 1)]);
+        xch_write(xch, pf);
+        phase_barrier();  // P of tile j is visible to the dS waves
         const f16x8* bop[1] = {pf};
         f32x16* acc[1] = {dv};
         tr_gemm_hooked<TilePair<2 + ST, 2 + ST>, 1>(vb, bop, acc, [](auto) {});
@@ -601,7 +584,14 @@ __global__ __launch_bounds__(64 * BWK, 1) void k_bwd_dkdv(BwdParams p) {
         rowvals_wait(d4);
         phase_barrier();  // P of tile j is in the exchange
         float pr[2][16], ds[2][16];
-        xch_read(xch, pr);
+        {
+          f16x8 pf[4];
+          xch_read(xch, pf);
+#pragma unroll
+          for (int sl = 0; sl < 4; sl++)
+#pragma unroll
+            for (int e = 0; e < 8; e++) pr[sl >> 1][8 * (sl & 1) + e] = (float)pf[sl][e];
+        }
 #pragma unroll
         for (int q2 = 0; q2 < 2; q2++)
 #pragma unroll
