@@ -17,12 +17,12 @@
 //               SIMD, at most 256 registers each), so one wave's vector work runs beside the
 //               other's MFMAs.
 // The workspace keeps -D per staged row.
-//   k_bwd_dkdv  work item = (segment, 128-key tile, head).  One pass over the query tiles:
-//               S = Q^ K^T and dP = dO V^T with the wave's 32 keys in registers, P and dS in fp16,
-//               dV^T += dO16^T P and dK^T += Q^16^T dS, whose transposed reads run as one pipeline.
-// In dk/dv (one wave per SIMD) a wave's vector work overlaps its own MFMAs when a few independent
-// instructions sit between them, so P is formed between the dP MFMAs and dS between the dV MFMAs
-// that only need P, each packed slice finished before its first use.
+//   k_bwd_dkdv  work item = (segment, 128-key tile, head).  One pass over the query tiles, eight
+//               waves in two roles over the item's keys (32 per wave pair, in registers): waves
+//               0-3 form S = Q^ K^T, P (fp16) and dV^T += dO16^T P, and hand P through LDS to
+//               waves 4-7, which form dP = dO V^T, dS in fp16 and dK^T += Q^16^T dS.  The two
+//               waves of a SIMD hold different roles, so one's vector work runs beside the
+//               other's MFMAs.
 // With norm weights both write dq^ / dk^ in fp32 and k_bwd_norm applies the RMSNorm backward per
 // row (FP64, one bf16 rounding) and writes fixed-order weight-gradient partials, which two small
 // kernels sum in a fixed tree; without weights the kernels write dq, dk directly.
