@@ -332,24 +332,35 @@ __global__ __launch_bounds__(64 * BW, 2) void k_bwd_dq(BwdParams p) {
       constexpr int ST = decltype(stage)::value;
       copies_barrier();  // tile j has landed, every wave is done with stage 1 - ST
       if (j + 1 < ntk) copies(j + 1, Par2<1 - ST>{});
-      // P between the dP MFMAs (two elements per step), then dS = P (dP - D) packed to fp16
+      // P between the first dP MFMAs, then dS = P (dP - D) packed to fp16
       f32x16 S[2], dP[2];
       gemm_rows<0 + ST>(rb, qf, S, [](auto) {});
       if (j == ntk - 1 && rem < TILE_ROWS) mask_tail(S, rem, hh);
       float pr[32], ds[32];
-      gemm_rows<2 + ST>(rb, gf, dP, [&](auto st) {
+      f16x8 dsf[4];
+      // dP block-major: P (two elements per step) between the first eight MFMAs, block 0's dS
+      // between the last eight
+      gemm_rows<2 + ST, 4, true>(rb, gf, dP, [&](auto st) {
         constexpr int s = decltype(st)::value;
+        if constexpr (s < 8) {
 #pragma unroll
-        for (int u = 0; u < 2; u++) {
-          const int e = 2 * s + u;
-          pr[e] = __builtin_amdgcn_exp2f(__builtin_fmaf(S[e >> 4][e & 15], c, -lq));
+          for (int u = 0; u < 4; u++) {
+            const int e = 4 * s + u;
+            pr[e] = __builtin_amdgcn_exp2f(__builtin_fmaf(S[e >> 4][e & 15], c, -lq));
+          }
+        } else {
+#pragma unroll
+          for (int u = 0; u < 2; u++) {
+            const int e = 2 * (s - 8) + u;
+            ds[e] = pr[e] * (dP[0][e] - Dq);
+          }
+          if constexpr ((s & 3) == 3) dsf[(s - 8) >> 2] = pack_p(&ds[8 * ((s - 8) >> 2)]);
         }
       });
-      f16x8 dsf[4];
 #pragma unroll
-      for (int e = 0; e < 32; e++) ds[e] = pr[e] * (dP[e >> 4][e & 15] - Dq);
-#pragma unroll
-      for (int sl = 0; sl < 4; sl++) dsf[sl] = pack_p(&ds[8 * sl]);
+      for (int e = 16; e < 32; e++) ds[e] = pr[e] * (dP[1][e - 16] - Dq);
+      dsf[2] = pack_p(&ds[16]);
+      dsf[3] = pack_p(&ds[24]);
       const f16x8* bop[1] = {dsf};
       f32x16* accp[1] = {acc};
       tr_gemm_hooked<TilePair<ST, ST>, 1>(vb, bop, accp, [](auto) {});
