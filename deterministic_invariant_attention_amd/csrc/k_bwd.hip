@@ -332,14 +332,13 @@ __global__ __launch_bounds__(64 * BW, 2) void k_bwd_dq(BwdParams p) {
       constexpr int ST = decltype(stage)::value;
       copies_barrier();  // tile j has landed, every wave is done with stage 1 - ST
       if (j + 1 < ntk) copies(j + 1, Par2<1 - ST>{});
-      // P between the first dP MFMAs, then dS = P (dP - D) packed to fp16
       f32x16 S[2], dP[2];
       gemm_rows<0 + ST>(rb, qf, S, [](auto) {});
       if (j == ntk - 1 && rem < TILE_ROWS) mask_tail(S, rem, hh);
       float pr[32], ds[32];
       f16x8 dsf[4];
-      // dP block-major: P (two elements per step) between the first eight MFMAs, block 0's dS
-      // between the last eight
+      // dS = P (dP - D) in fp16, dP block-major: P (four elements per step) between the first
+      // eight MFMAs, block 0's dS (two per step) between the last eight, block 1's after them
       gemm_rows<2 + ST, 4, true>(rb, gf, dP, [&](auto st) {
         constexpr int s = decltype(st)::value;
         if constexpr (s < 8) {
