@@ -170,6 +170,7 @@ struct BwdPrepParams {
 // maximum into the segment's slot with an integer atomicMax, so the result is the same whatever the
 // order of the workgroups.
 constexpr int DMAX_TOK = 16;  // tokens per workgroup
+__device__ __forceinline__ uint32_t max_u32(uint32_t a, uint32_t b) { return a > b ? a : b; }
 constexpr int DMAX_HEADS = 16;  // heads per workgroup
 
 __global__ __launch_bounds__(256) void k_bwd_dmax(const uint16_t* __restrict__ dout, const int32_t* __restrict__ tok2seg,
@@ -204,11 +205,12 @@ __global__ __launch_bounds__(256) void k_bwd_dmax(const uint16_t* __restrict__ d
       m = a > m ? a : m;
       m = b > m ? b : m;
     }
-#pragma unroll
-    for (int o = 1; o < 16; o <<= 1) {
-      const uint32_t y = (uint32_t)__shfl_xor((int)m, o, 64);
-      m = y > m ? y : m;
-    }
+    // the row's 16 lanes: rotations by 8, 4, 2, 1 within the row (DPP, no LDS traffic); a
+    // maximum does not depend on the order
+    m = max_u32(m, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)m, 0x128, 0xF, 0xF, false));  // row_ror:8
+    m = max_u32(m, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)m, 0x124, 0xF, 0xF, false));  // row_ror:4
+    m = max_u32(m, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)m, 0x122, 0xF, 0xF, false));  // row_ror:2
+    m = max_u32(m, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)m, 0x121, 0xF, 0xF, false));  // row_ror:1
     if (c == 0) s_max[i][rr] = m;
   }
   __syncthreads();
