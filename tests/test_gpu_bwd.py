@@ -137,6 +137,23 @@ def test_bwd_parity_batch2_full(dmode):
            ref=_oracle_workload_bwd("batch2"))
 
 
+@functools.lru_cache(maxsize=1)
+def _long_segment_inputs():
+    x = workloads.random_inputs([8349], 2, seed=7100, qk_scale=3.0, with_grad=True)
+    say("[bwd parity] oracle gradients of one 8349-token segment (H=2)")
+    ref = oracle.bwd(x["q"], x["k"], x["v"], x["seg"].numpy(), x["dout"], x["wq"], x["wk"], EPS, SCALE)
+    return x, ref
+
+
+@pytest.mark.parametrize("dmode", DMODES)
+def test_bwd_parity_long_segment(dmode):
+    """One segment of the headline forward's length (8349 tokens, q/k drawn as there), 2 heads: every
+    work item of both attention kernels walks 131 tiles, and P ~ 1e-4 stays in fp16's normal range.
+    All outputs and both weight gradients against the oracle."""
+    x, ref = _long_segment_inputs()
+    _check("long-segment", x, dmode=dmode, ref=ref)
+
+
 @pytest.mark.parametrize("dmode", DMODES)
 def test_bwd_repeat_bitwise(dmode):
     g = to_dev(workloads.make_inputs(workloads.WORKLOADS["short3"], with_grad=True))
