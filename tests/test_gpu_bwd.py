@@ -145,6 +145,26 @@ def _long_segment_inputs():
     return x, ref
 
 
+def test_bwd_32768_token_segment_alone_equals_batched():
+    """A 32768-token segment (512 query and key tiles per item) alone and between two others, packed
+    at an offset: dq, dk, dv of its rows are the same bits, and a repeat of the batch gives the
+    same bits (no oracle at this length)."""
+    lens = [300, 32768, 200]
+    x = workloads.random_inputs(lens, 1, seed=7200, with_grad=True)
+    g = to_dev(x)
+    say("[bwd bitwise] 32768-token segment alone vs between two others, and a repeat")
+    b = run_bwd(g, dmode="o32")
+    b2 = run_bwd(g, dmode="o32")
+    for u, w in zip(b, b2):
+        assert bitwise_equal(u, w)
+    s0, s1 = lens[0], lens[0] + lens[1]
+    alone = {n: (g[n][s0:s1].contiguous() if n in ("q", "k", "v", "seg", "dout") else g[n]) for n in g}
+    a = run_bwd(alone, dmode="o32")
+    for nm, u, w in (("dq", a[0], b[0]), ("dk", a[1], b[1]), ("dv", a[2], b[2])):
+        assert np.all(np.isfinite(f64(u))), nm
+        assert bitwise_equal(u, w[s0:s1]), nm
+
+
 @pytest.mark.parametrize("dmode", DMODES)
 def test_bwd_parity_long_segment(dmode):
     """One segment of the headline forward's length (8349 tokens, q/k drawn as there), 2 heads: every
