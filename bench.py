@@ -21,8 +21,11 @@ the nominal 2.5 x forward FLOPs; the CPU baseline is the FP64 oracle's gradients
 heads.
 --order position: the tokens of every segment are shuffled (seeded) and the step calls the
 position-ordered entry points (h3attn_fwd_pos / h3attn_bwd_pos) with their position ids.
+--rope grid|random: the step calls h3attn_fwd_ex / h3attn_bwd_ex with MM-RoPE tables (the node
+between the q/k norm and the attention), and the CPU baseline and parity take the oracle with the
+same tables.
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload long] [--pass fwd|bwd]
-                       [--order packed|position] [--no-cpu-baseline]
+                       [--order packed|position] [--rope none|grid|random] [--no-cpu-baseline]
 """
 import argparse
 import json
@@ -80,6 +83,8 @@ def main():
     ap.add_argument("--pass", dest="which", choices=("fwd", "bwd"), default="fwd")
     ap.add_argument("--order", choices=("packed", "position"), default="packed",
                     help="position: shuffle each segment's tokens and pass their position ids")
+    ap.add_argument("--rope", choices=("none", "grid", "random"), default="none",
+                    help="MM-RoPE tables for the normed q and k (workloads.rope_tables of this kind)")
     ap.add_argument("--d-from", dest="d_from", choices=("o32", "recompute"), default="o32",
                     help="backward: D = dO . O from the forward's fp32 output (h3attn_bwd_ex), or recomputed "
                          "from P and dP by the dq kernel (h3attn_bwd)")
@@ -111,6 +116,7 @@ def main():
     wl = workloads.WORKLOADS[args.workload or "long"]
     dev = torch.device("cuda:0")
     x, pos = ordered_inputs(workloads.make_inputs(wl), wl, args.order, dev)
+    rope = rope_inputs(wl, args, dev)
     g = {n: (t.to(dev) if t is not None else None) for n, t in x.items()}
     T, H = wl.tokens, wl.heads
     flops = wl.flops()
@@ -123,7 +129,10 @@ def main():
         copy_calibration(dev)
 
     def eager_step(st):
-        if pos is None:
+        if rope is not None:
+            h3.h3attn_fwd_ex(g["q"], g["k"], g["v"], g["seg"], pos, g["wq"], g["wk"], eps=wl.eps, scale=wl.scale,
+                             out=out, workspace_buf=ws, stream=st, rope_cos=rope[0], rope_sin=rope[1])
+        elif pos is None:
             h3.h3attn_fwd(g["q"], g["k"], g["v"], g["seg"], g["wq"], g["wk"], eps=wl.eps, scale=wl.scale, out=out,
                           workspace_buf=ws, stream=st)
         else:
@@ -221,7 +230,11 @@ def main():
         def run_rows(n):
             rows = np.arange(T) if n == T else np.sort(rng.choice(T, size=n, replace=False))
             t1 = time.perf_counter()
-            ref = oracle.fwd_rows(x["q"], x["k"], x["v"], seg_np, rows, x["wq"], x["wk"], wl.eps, wl.scale)[0]
+            if rope is None:
+                ref = oracle.fwd_rows(x["q"], x["k"], x["v"], seg_np, rows, x["wq"], x["wk"], wl.eps, wl.scale)[0]
+            else:
+                ref = oracle.fwd_ex(x["q"], x["k"], x["v"], seg_np, x["wq"], x["wk"], wl.eps, wl.scale,
+                                    cos=rope[0].cpu(), sin=rope[1].cpu(), rows=rows)[0]
             return rows, ref, time.perf_counter() - t1
 
         # grow the sample until it takes at least half the target time (or is the whole workload)
@@ -265,7 +278,7 @@ def main():
         "data": "synthetic",
         "config": {"workload": wl.name, "tokens": T, "heads": H, "head_dim": 128, "segments": list(wl.seg_lens),
                    "qk_draw_scale": wl.qk_scale, "pv_operands": "fp16", "accumulate": "fp32",
-                   "key_order": args.order, "launch": args.launch,
+                   "key_order": args.order, "rope": args.rope, "launch": args.launch,
                    "pct_bf16_mfma_peak": round(100 * value / PEAK_MFMA_TFLOPS, 2),
                    "algorithmic_GBps": round(wl.algorithmic_bytes() / (ms_per_step * 1e-3) / 1e9, 1),
                    "hbm": hbm, "repeat_bitwise": repeat_bitwise, "device_status": status},
@@ -316,6 +329,19 @@ def ordered_inputs(x, wl, order, dev):
     return x, workloads.position_ids(wl.seg_lens)[p].contiguous().to(dev)
 
 
+def rope_inputs(wl, args, dev):
+    """--rope: float32 [T, 48] cosine and sine tables on the device (token order of the inputs: with
+    --order position they follow the same shuffle as the tokens), else None."""
+    if args.rope == "none":
+        return None
+    import workloads
+    c, s = workloads.rope_tables(wl.seg_lens, args.rope)
+    if args.order == "position":
+        p = workloads.shuffle_within_segments(wl.seg_lens, 11)
+        c, s = c[p].contiguous(), s[p].contiguous()
+    return c.to(dev), s.to(dev)
+
+
 def bench_bwd(args, wl):
     import numpy as np
     import torch
@@ -325,6 +351,8 @@ def bench_bwd(args, wl):
 
     dev = torch.device("cuda:0")
     x, pos = ordered_inputs(workloads.make_inputs(wl, with_grad=True), wl, args.order, dev)
+    rope = rope_inputs(wl, args, dev)
+    rc, rs = (None, None) if rope is None else rope
     g = {n: (t.to(dev) if t is not None else None) for n, t in x.items()}
     T, H = wl.tokens, wl.heads
     flops = 2.5 * wl.flops()
@@ -334,7 +362,8 @@ def bench_bwd(args, wl):
         copy_calibration(dev)
     # the forward that precedes the backward (not timed): LSE, and the fp32 output when D comes from it
     _, lse, o32 = h3.h3attn_fwd_ex(g["q"], g["k"], g["v"], g["seg"], pos, g["wq"], g["wk"], eps=wl.eps,
-                                   scale=wl.scale, want_lse=True, want_o32=args.d_from == "o32", stream=stream)
+                                   scale=wl.scale, want_lse=True, want_o32=args.d_from == "o32", stream=stream,
+                                   rope_cos=rc, rope_sin=rs)
     ws = h3.bwd_workspace(T, H, dev)
     outs = [torch.empty_like(g["q"]) for _ in range(3)]
     dw = [torch.empty(128, dtype=torch.float32, device=dev) for _ in range(2)]
@@ -342,7 +371,7 @@ def bench_bwd(args, wl):
     def step():
         h3.h3attn_bwd_ex(g["dout"], g["q"], g["k"], g["v"], lse, g["seg"], pos, o32, g["wq"], g["wk"], eps=wl.eps,
                          scale=wl.scale, dq=outs[0], dk=outs[1], dv=outs[2], dwq=dw[0], dwk=dw[1], workspace_buf=ws,
-                         stream=stream)
+                         stream=stream, rope_cos=rc, rope_sin=rs)
 
     for _ in range(args.warmup):
         step()
@@ -377,7 +406,8 @@ def bench_bwd(args, wl):
         def run_heads(nh):
             sub = {n: x[n][:, :nh].contiguous() for n in ("q", "k", "v", "dout")}
             t1 = time.perf_counter()
-            oracle.bwd(sub["q"], sub["k"], sub["v"], seg_np, sub["dout"], x["wq"], x["wk"], wl.eps, wl.scale)
+            oracle.bwd(sub["q"], sub["k"], sub["v"], seg_np, sub["dout"], x["wq"], x["wk"], wl.eps, wl.scale,
+                       cos=None if rope is None else rc.cpu(), sin=None if rope is None else rs.cpu())
             return time.perf_counter() - t1
 
         nh = 1
@@ -406,7 +436,7 @@ def bench_bwd(args, wl):
         "data": "synthetic",
         "config": {"workload": wl.name + "-bwd", "tokens": T, "heads": H, "head_dim": 128,
                    "segments": list(wl.seg_lens), "products": "fp16 P, dS, dO, q/k hat; fp32 accumulate",
-                   "key_order": args.order, "d_from": args.d_from,
+                   "key_order": args.order, "rope": args.rope, "d_from": args.d_from,
                    "pct_bf16_mfma_peak": round(100 * value / PEAK_MFMA_TFLOPS, 2),
                    "repeat_bitwise": repeat_bitwise, "device_status": status},
         "roofline": {"bound": "mfma", "achieved": round(value, 2), "peak": PEAK_MFMA_TFLOPS, "unit": "TFLOP/s",
