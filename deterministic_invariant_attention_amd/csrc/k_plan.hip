@@ -5,7 +5,11 @@
 // described to the library by one id per token; a segment is a maximal run of equal ids, and ids
 // must not decrease.  The decode runs in one 1024-thread workgroup: each thread walks a contiguous
 // run of tokens (then of segments), and one block-wide exclusive scan per pass places every run's
-// results, so the whole decode costs two scans and three barriers whatever T is.
+// results, so the whole decode costs two scans and three barriers whatever T is.  For runs of more
+// than two tokens (T in (2048, PLAN_STAGE]) the ids are first copied to LDS with coalesced loads
+// that are all in flight at once, so the walks read LDS instead of waiting on one global load per
+// token (8349 tokens: 12.5 -> 10.3 us per call; at T <= 2048 the extra barrier costs more than it
+// saves).
 #include "h3_common.h"
 #include "h3_bwd.h"
 #include "h3_launch.h"
@@ -13,6 +17,7 @@
 namespace h3 {
 
 constexpr int TILE_ROWS_PLAN = 64;  // inner-loop tile of the backward kernels (their cost unit)
+constexpr int PLAN_STAGE = 16384;   // tokens whose ids the decode stages in LDS (64 KB)
 
 // Exclusive scan of one int per thread over a 1024-thread block; also returns the block total.
 __device__ __forceinline__ int block_excl_scan(int v, int* lds_wave, int& total) {
@@ -65,25 +70,60 @@ __global__ __launch_bounds__(1024) void k_plan(const int32_t* __restrict__ seg, 
   const int64_t per = (T + 1023) / 1024;
   const int64_t t0 = min(T, (int64_t)tid * per), t1 = min(T, t0 + per);
   int cnt = 0, bad = 0;
-  {
-    int32_t prev = t0 > 0 ? seg[t0 - 1] : 0;
-    for (int64_t t = t0; t < t1; t++) {
-      const int32_t cur = seg[t];
-      cnt += (t == 0 || cur != prev) ? 1 : 0;
-      bad |= (t > 0 && cur < prev) ? 1 : 0;
-      prev = cur;
-    }
-  }
   int nseg;
-  const int first = block_excl_scan(cnt, lds_wave, nseg);
-  {
-    int si = first - 1;  // the segment of token t0 - 1 (the run's tokens before its first start)
-    int32_t prev = t0 > 0 ? seg[t0 - 1] : 0;
-    for (int64_t t = t0; t < t1; t++) {
-      const int32_t cur = seg[t];
-      if (t == 0 || cur != prev) segtab[2 * (++si)] = (int32_t)t;
-      tok2seg[t] = si;
-      prev = cur;
+  if (T > 2048 && T <= PLAN_STAGE) {
+    // ids staged in LDS; the second walk overwrites each id with its token's segment index, which
+    // is then stored coalesced
+    __shared__ int32_t s_ids[PLAN_STAGE];
+#pragma unroll
+    for (int k = 0; k < PLAN_STAGE / 1024; k++) {
+      const int t = k * 1024 + tid;
+      if (t < T) s_ids[t] = seg[t];
+    }
+    __syncthreads();
+    const int32_t prev0 = t0 > 0 ? s_ids[t0 - 1] : 0;  // read before any thread overwrites it
+    {
+      int32_t prev = prev0;
+      for (int t = (int)t0; t < (int)t1; t++) {
+        const int32_t cur = s_ids[t];
+        cnt += (t == 0 || cur != prev) ? 1 : 0;
+        bad |= (t > 0 && cur < prev) ? 1 : 0;
+        prev = cur;
+      }
+    }
+    const int first = block_excl_scan(cnt, lds_wave, nseg);  // its barriers order prev0 before the writes
+    {
+      int si = first - 1;
+      int32_t prev = prev0;
+      for (int t = (int)t0; t < (int)t1; t++) {
+        const int32_t cur = s_ids[t];
+        if (t == 0 || cur != prev) segtab[2 * (++si)] = t;
+        s_ids[t] = si;
+        prev = cur;
+      }
+    }
+    __syncthreads();
+    for (int t = tid; t < (int)T; t += 1024) tok2seg[t] = s_ids[t];
+  } else {
+    {
+      int32_t prev = t0 > 0 ? seg[t0 - 1] : 0;
+      for (int64_t t = t0; t < t1; t++) {
+        const int32_t cur = seg[t];
+        cnt += (t == 0 || cur != prev) ? 1 : 0;
+        bad |= (t > 0 && cur < prev) ? 1 : 0;
+        prev = cur;
+      }
+    }
+    const int first = block_excl_scan(cnt, lds_wave, nseg);
+    {
+      int si = first - 1;  // the segment of token t0 - 1 (the run's tokens before its first start)
+      int32_t prev = t0 > 0 ? seg[t0 - 1] : 0;
+      for (int64_t t = t0; t < t1; t++) {
+        const int32_t cur = seg[t];
+        if (t == 0 || cur != prev) segtab[2 * (++si)] = (int32_t)t;
+        tok2seg[t] = si;
+        prev = cur;
+      }
     }
   }
   if (bad) atomicOr(&s_bad, 1);
