@@ -30,7 +30,10 @@ FLAGS = [
 # writes MFMA results to accumulation registers and copies every element back to ordinary VGPRs
 # before the softmax arithmetic reads it; asking for the VGPR form of the MFMA removes those copies
 # (the code computes the same values in the same order, so results are unchanged).
-SRC_FLAGS = {"k_bwd.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
+# k_attn_fwd.hip: its one work-counter fetch per unit is issued by one lane; the atomic optimizer's
+# wave-wide rewrite of it needs the reply at once, which would expose the fetch at every unit start
+SRC_FLAGS = {"k_bwd.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"],
+             "k_attn_fwd.hip": ["-mllvm", "-amdgpu-atomic-optimizer-strategy=None"]}
 
 
 def _compile(src: str, obj: str) -> None:

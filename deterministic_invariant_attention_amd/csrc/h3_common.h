@@ -17,7 +17,7 @@ constexpr int BK = 96;   // keys per KV tile; the KV walk is in these tiles, asc
 // ---------------------------------------------------------------- workspace
 // [0, 256)            header: status bits, segment and work-item counts
 // segtab              int32 [2*T]: (start, length) of each segment, in packing order
-// items               int32 [2*(T + ceil(T/BQ))]: (segment, q-tile) work items
+// items               int32 [4*(T + ceil(T/BQ))]: (segment, q-tile, segment start, length) work items
 // khat                bf16 [H][T][128]: normed K (head-major, so a KV tile is contiguous)
 // v16                 fp16 [H][T][128]: V converted to fp16 (head-major)
 // qhat                bf16 [H][T][128]: normed Q (head-major, packed token order), with norm weights
@@ -57,7 +57,7 @@ __host__ __device__ inline WsLayout ws_layout(int64_t T, int32_t H) {
   w.max_items = T + (T + BQ - 1) / BQ;
   w.segtab = 256;
   w.items = w.segtab + align256((size_t)T * 8);
-  w.khat = w.items + align256((size_t)w.max_items * 8);
+  w.khat = w.items + align256((size_t)w.max_items * 16);
   w.v16 = w.khat + align256((size_t)T * H * HD * 2);
   w.qhat = w.v16 + align256((size_t)T * H * HD * 2);
   w.tok2seg = w.qhat + align256((size_t)T * H * HD * 2);

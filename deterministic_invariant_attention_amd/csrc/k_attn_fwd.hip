@@ -178,6 +178,14 @@ struct AttnParams {
 };
 
 // Maximum over the query's 96 keys of one tile (exact: any evaluation order gives these bits).
+// Workgroup barrier for LDS hazards only: this wave's LDS operations are complete (lgkmcnt(0)),
+// outstanding global stores are not waited for.
+__device__ __forceinline__ void lds_barrier() {
+  asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
 __device__ __forceinline__ float tile_max(const f32x16* S) {
   float a = -__builtin_inff();
 #pragma unroll
@@ -273,6 +281,11 @@ __global__ __launch_bounds__(64 * NWAVES, 1) void k_attn_fwd(AttnParams p) {
   // issue only their K copies and meet the barriers.  Whether an item runs whole or in halves, and
   // which workgroup runs it, changes no bit of any output: every row runs the same instructions
   // either way.
+  // A unit's start waits on memory once: the item entry (which carries the segment's start and
+  // length), then the segment's flag, the counter's reply, K(0) and Q all in flight together.  The
+  // barriers at a unit's start and end guard LDS only, so no unit waits for the previous one's
+  // output stores; the next unit's index goes through LDS slot it & 1, written as soon as the
+  // counter's reply is known to have arrived.
   const int xcd = blockIdx.x & 7;
   const int slot = blockIdx.x >> 3;
   const int nslots = p.xcd_slots;
@@ -305,9 +318,11 @@ __global__ __launch_bounds__(64 * NWAVES, 1) void k_attn_fwd(AttnParams p) {
     vb[db] = (uint32_t)(size_t)(const __attribute__((address_space(3))) uint16_t*)(lds + 2 * FTILE +
                                                                                    v_off(tr_row, 32 * db + tr_col));
 
-  __shared__ int32_t s_unit;
+  __shared__ int32_t s_unit[2];  // the next unit, written during unit i into slot i & 1
   int32_t fetched = 0;  // thread 0: the counter value fetched during the current unit
+  int it = 0;           // units this workgroup has started
   for (int64_t u = slot; u < nunits;) {
+    bool posted = false;  // thread 0: the next unit is in s_unit[it & 1]
     do {  // one unit; its early exits (continue) end the do, not the walk over units
     // the next unit's counter value, fetched now and used at the end of this unit
     if (!one_round && tid == 0) fetched = atomicAdd(&p.sched[SCHED_STRIDE * xcd], 1);
@@ -316,16 +331,38 @@ __global__ __launch_bounds__(64 * NWAVES, 1) void k_attn_fwd(AttnParams p) {
     const int half = u < nfull ? -1 : (int)((u - nfull) & 1);
     const int head = (int)(v / nitems);
     const int item = (int)(v - (int64_t)head * nitems);
-    const int seg = p.items[2 * item];
-    const int qt = p.items[2 * item + 1];
+    // the item: (segment, query tile, the segment's start, its length)
+    const u32x4 it4 = *(const u32x4*)(p.items + 4 * item);
+    const int seg = (int)it4[0], qt = (int)it4[1], s0 = (int)it4[2], L = (int)it4[3];
     if ((unsigned)seg >= (unsigned)nseg) continue;
-    const int s0 = p.segtab[2 * seg];
-    const int L = p.segtab[2 * seg + 1];
     if (s0 < 0 || L <= 0 || (int64_t)s0 + L > T || qt < 0 || qt * BQ >= L) continue;
 
     // the wave's 32 query rows (segment-relative); in a half item waves w and w + 4 name the same rows
     const int row0 = qt * BQ + (half < 0 ? 32 * wv : 128 * half + 32 * (wv & 3));
-    if (p.segflag[seg] != 0) {
+    // the segment's flag, read now and tested once K(0) and Q have landed (its latency overlaps theirs)
+    const int flag = p.segflag[seg];
+    const int ntiles = (L + FROWS - 1) / FROWS;
+    const int rem = L - (ntiles - 1) * FROWS;  // valid keys of the last tile, 1..FROWS
+    const uint16_t* kbase = p.khat + ((int64_t)head * T + s0) * HD;
+    const uint16_t* vbase = p.v16 + ((int64_t)head * T + s0) * HD;
+
+    // Every wave has finished reading LDS for the previous item before it is overwritten (LDS
+    // only: the previous item's output stores need not have landed).
+    lds_barrier();
+    ftile_to_lds<NWAVES>(kbase, L, lds, wv, k_lane_off);  // K(0)
+    const bool idle = half >= 0 && grp == 1;  // waves 4..7 of a half item: copies and barriers only
+    const int qrow = row0 + l32;
+    const bool qvalid = qrow < L;
+    bf16x8 qf[8];
+    if (!idle) load_q(p, s0, qrow, qvalid, head, hh, qf);
+    __builtin_amdgcn_s_waitcnt(0xF70);  // K(0), Q and the flag have landed
+    // the counter's reply arrived with them (vmcnt counts all): post the next unit now, so the
+    // unit's end waits for no memory operation
+    if (!one_round && tid == 0) {
+      s_unit[it & 1] = nslots + fetched;
+      posted = true;
+    }
+    if (flag != 0) {
       // This segment holds a value that cannot enter the products (or invalid position ids): its
       // rows are NaN; every other segment is computed as usual.
       const int qr = row0 + l32;
@@ -344,14 +381,6 @@ __global__ __launch_bounds__(64 * NWAVES, 1) void k_attn_fwd(AttnParams p) {
       continue;
     }
 
-    const int ntiles = (L + FROWS - 1) / FROWS;
-    const int rem = L - (ntiles - 1) * FROWS;  // valid keys of the last tile, 1..FROWS
-    const uint16_t* kbase = p.khat + ((int64_t)head * T + s0) * HD;
-    const uint16_t* vbase = p.v16 + ((int64_t)head * T + s0) * HD;
-
-    // Every wave has finished reading LDS for the previous item before it is overwritten.
-    __syncthreads();
-    ftile_to_lds<NWAVES>(kbase, L, lds, wv, k_lane_off);  // K(0)
 
     // K(m+1) and V(m) go into the buffers of K(m-1) and V(m-2), which were last read in slot 2m-1.
     // The buffer parity MP = m & 1 is a compile-time constant at every call, so the compiler can
@@ -372,7 +401,7 @@ __global__ __launch_bounds__(64 * NWAVES, 1) void k_attn_fwd(AttnParams p) {
         ftile_to_lds_o<4>(vbase + (int64_t)m * FROWS * HD, L - m * FROWS, lds + (2 + MP) * FTILE, wv & 3, coffs);
     };
 
-    if (half >= 0 && grp == 1) {
+    if (idle) {
       // waves 4..7 of a half item: the trailing group's K copies and barriers, and no arithmetic
       const int tau_idle = 2 * ntiles;
       auto idle_phase = [&](int tau, auto tm) {
@@ -398,10 +427,6 @@ __global__ __launch_bounds__(64 * NWAVES, 1) void k_attn_fwd(AttnParams p) {
       continue;
     }
 
-    const int qrow = row0 + l32;
-    const bool qvalid = qrow < L;
-    bf16x8 qf[8];
-    load_q(p, s0, qrow, qvalid, head, hh, qf);
 
     f32x16 S[NKB];  // scores of the tile whose softmax is next
     f16x8 pf[NKS];  // P of the tile whose P.V is next
@@ -466,7 +491,6 @@ __global__ __launch_bounds__(64 * NWAVES, 1) void k_attn_fwd(AttnParams p) {
       }
     };
 
-    __builtin_amdgcn_s_waitcnt(0xF70);  // K(0) has landed (the slot-0 barrier publishes it)
     if (grp == 1) {                     // slot 0 of the trailing waves: barrier and copies only
       phase_barrier();
       issue_k(0, Par<0>{});
@@ -515,9 +539,10 @@ __global__ __launch_bounds__(64 * NWAVES, 1) void k_attn_fwd(AttnParams p) {
     } while (0);
     if (one_round) break;
     // the counter hands out the units from nslots on (the first nslots are the slots themselves)
-    if (tid == 0) s_unit = nslots + fetched;
-    __syncthreads();
-    u = s_unit;
+    if (tid == 0 && !posted) s_unit[it & 1] = nslots + fetched;
+    lds_barrier();
+    u = s_unit[it & 1];
+    it++;
   }
 
   // The last workgroup to leave zeroes the counters, so that the next launch on this workspace (the

@@ -1,5 +1,7 @@
 // Segment decode: per-token int32 segment ids -> segment table (start, length) and the list of
-// (segment, q-tile) attention work items, plus the status word.
+// attention work items, plus the status word.  A forward item is (segment, query tile, the
+// segment's start, its length), so the attention kernel reads one 16-byte entry per unit; a backward
+// item is (segment, tile).
 //
 // Packed layouts ("ws1_one_h3_block" page, Summary: several sequences share one token axis) are
 // described to the library by one id per token; a segment is a maximal run of equal ids, and ids
@@ -42,11 +44,11 @@ __device__ __forceinline__ int block_excl_scan(int v, int* lds_wave, int& total)
   return before + x - v;
 }
 
-// bkt == nullptr: items in segment order (the forward's static, head-major walk).  Otherwise the
-// backward's order: items grouped by the cost class of their segment, floor(log2(ceil(L / 64))),
-// most expensive class first (the order inside a class is free: it only decides which workgroup
-// runs an item, never a result), and bkt[2b], bkt[2b+1] = first item and item count of the b-th
-// non-empty class; the work counters are reset.
+// bkt == nullptr: forward items (16 bytes each) in segment order (the forward's head-major walk).
+// Otherwise the backward's order: items grouped by the cost class of their segment,
+// floor(log2(ceil(L / 64))), most expensive class first (the order inside a class is free: it only
+// decides which workgroup runs an item, never a result), and bkt[2b], bkt[2b+1] = first item and
+// item count of the b-th non-empty class; the work counters are reset.
 // tok2seg: the segment index of every token; segflag: the per-segment error flags, cleared for the
 // call's nseg segments; dmax (backward only, else NULL): the per-(segment, head) maxima of |dO|,
 // zeroed for the nseg * H slots the call uses; sched (forward only, else NULL): the attention
@@ -154,9 +156,10 @@ __global__ __launch_bounds__(1024) void k_plan(const int32_t* __restrict__ seg, 
     int it = off;
     for (int sg = s0; sg < s1; sg++) {
       const int n = (segtab[2 * sg + 1] + tile - 1) / tile;
+      const int st = segtab[2 * sg], len = segtab[2 * sg + 1];
       for (int j = 0; j < n; j++, it++) {
-        items[2 * it] = sg;
-        items[2 * it + 1] = j;
+        const u32x4 e = {(uint32_t)sg, (uint32_t)j, (uint32_t)st, (uint32_t)len};
+        *(u32x4*)(items + 4 * it) = e;
       }
     }
   } else {  // by cost class, most expensive first

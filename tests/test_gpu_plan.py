@@ -1,8 +1,9 @@
 """The segment decode (h3attn_plan) read back from the workspace and compared with a decode written
 here in plain Python: the header's counts, the segment table (start, length), the work items
-(segment, 256-query tile) in segment order and every token's segment index.  Packed layouts
-("ws1_one_h3_block" page, Summary: several sequences share one token axis) reach the library as
-one id per token; a segment is a maximal run of equal ids and ids never decrease.  The sizes sit
+(segment, 256-query tile, segment start, length) in segment order and every token's segment
+index.  Packed layouts ("ws1_one_h3_block" page, Summary: several sequences share one token axis)
+reach the library as one id per token; a segment is a maximal run of equal ids and ids never
+decrease.  The sizes sit
 on both sides of the decode's two paths: the ids staged in LDS for 2048 < T <= 16384, read from
 global memory otherwise."""
 import numpy as np
@@ -27,18 +28,19 @@ def _offsets(T, H):
     max_items = T + (T + BQ - 1) // BQ
     segtab = 256
     items = segtab + _a256(T * 8)
-    khat = items + _a256(max_items * 8)
+    khat = items + _a256(max_items * 16)
     tok2seg = khat + 3 * _a256(T * H * HD * 2)
     return segtab, items, tok2seg
 
 
 def _decode(ids):
-    """Segments as (start, length) runs of equal ids, the (segment, tile) items and tok2seg."""
+    """Segments as (start, length) runs of equal ids, the (segment, tile, start, length) items and
+    tok2seg."""
     T = len(ids)
     starts = [t for t in range(T) if t == 0 or ids[t] != ids[t - 1]]
     bounds = starts + [T]
     segtab = [(bounds[i], bounds[i + 1] - bounds[i]) for i in range(len(starts))]
-    items = [(s, j) for s, (_, L) in enumerate(segtab) for j in range((L + BQ - 1) // BQ)]
+    items = [(s, j, st, L) for s, (st, L) in enumerate(segtab) for j in range((L + BQ - 1) // BQ)]
     tok2seg = np.repeat(np.arange(len(segtab)), [L for _, L in segtab])
     return segtab, items, tok2seg
 
@@ -68,8 +70,8 @@ def _check(ids, H=2):
     assert hdr[1] == len(segtab) and hdr[2] == len(items), (hdr[1], hdr[2], len(segtab), len(items))
     got_seg = w[so:so + 8 * len(segtab)].view(torch.int32).numpy().reshape(-1, 2)
     assert np.array_equal(got_seg, np.array(segtab, dtype=np.int32).reshape(-1, 2))
-    got_items = w[io:io + 8 * len(items)].view(torch.int32).numpy().reshape(-1, 2)
-    assert np.array_equal(got_items, np.array(items, dtype=np.int32).reshape(-1, 2))
+    got_items = w[io:io + 16 * len(items)].view(torch.int32).numpy().reshape(-1, 4)
+    assert np.array_equal(got_items, np.array(items, dtype=np.int32).reshape(-1, 4))
     got_t2s = w[to:to + 4 * T].view(torch.int32).numpy()
     assert np.array_equal(got_t2s, tok2seg.astype(np.int32))
 
