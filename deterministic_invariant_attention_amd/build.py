@@ -32,7 +32,7 @@ FLAGS = [
 # (the code computes the same values in the same order, so results are unchanged).
 # k_attn_fwd.hip: its one work-counter fetch per unit is issued by one lane; the atomic optimizer's
 # wave-wide rewrite of it needs the reply at once, which would expose the fetch at every unit start
-SRC_FLAGS = {"k_bwd.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"],
+SRC_FLAGS = {"k_bwd.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form", "-mllvm", "-amdgpu-atomic-optimizer-strategy=None"],
              "k_attn_fwd.hip": ["-mllvm", "-amdgpu-atomic-optimizer-strategy=None"]}
 
 

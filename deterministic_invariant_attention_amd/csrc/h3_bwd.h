@@ -14,7 +14,7 @@ constexpr int NBKT = 32;  // cost classes of the backward work order (floor(log2
 // Backward workspace (h3attn_bwd_workspace_bytes):
 // [0, 256)          header: status bits, segment and work-item counts, work counters
 // segtab            int32 [2*T]
-// items             int32 [2*(T + ceil(T/BT))]: (segment, tile) work items
+// items             int32 [4*(T + ceil(T/BT))]: (segment, tile, segment start, length) work items
 // bkt               int32 [2*NBKT]: first item and count of each cost class in the work order
 // qhat16, khat16    fp16 [H][T][128]: normed q, k (head-major, staged row order)
 // v16, do16         fp16 [H][T][128]: v and dO
@@ -42,7 +42,7 @@ __host__ __device__ inline BwdLayout bwd_layout(int64_t T, int32_t H) {
   w.nchunks = (w.nparts + DW_CHUNK - 1) / DW_CHUNK;
   w.segtab = 256;
   w.items = w.segtab + align256((size_t)T * 8);
-  w.bkt = w.items + align256((size_t)w.max_items * 8);
+  w.bkt = w.items + align256((size_t)w.max_items * 16);
   w.qhat16 = w.bkt + align256((size_t)NBKT * 2 * 4);
   w.khat16 = w.qhat16 + tens;
   w.v16 = w.khat16 + tens;

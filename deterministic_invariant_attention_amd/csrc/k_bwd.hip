@@ -83,15 +83,16 @@ struct WorkItem {
   int head, item, seg, s0, L, tile;
 };
 
-__device__ __forceinline__ bool item_of(const BwdParams& p, int64_t v, int nitems, int nseg, int nbkt, WorkItem& w,
-                                        bool& done) {
+// bkt: the plan's cost classes (first item, count), staged in LDS at the kernel's start.
+__device__ __forceinline__ bool item_of(const BwdParams& p, const int32_t* bkt, int64_t v, int nitems, int nseg,
+                                        int nbkt, WorkItem& w, bool& done) {
   done = v >= (int64_t)nitems * p.H;
   if (done) return false;
   int64_t base = 0;
   int b = 0, start = 0, cnt = 0;
   for (; b < nbkt; b++) {
-    start = p.bkt[2 * b];
-    cnt = p.bkt[2 * b + 1];
+    start = bkt[2 * b];
+    cnt = bkt[2 * b + 1];
     const int64_t span = (int64_t)cnt * p.H;
     if (v < base + span) break;
     base += span;
@@ -101,27 +102,36 @@ __device__ __forceinline__ bool item_of(const BwdParams& p, int64_t v, int nitem
   w.head = (int)(local / cnt);
   w.item = start + (int)(local - (int64_t)w.head * cnt);
   if ((unsigned)w.item >= (unsigned)nitems || (unsigned)w.head >= (unsigned)p.H) return false;
-  const int seg = p.items[2 * w.item];
-  w.tile = p.items[2 * w.item + 1];
+  // the item: (segment, tile, the segment's start, its length)
+  const u32x4 it4 = *(const u32x4*)(p.items + 4 * w.item);
+  const int seg = (int)it4[0];
+  w.tile = (int)it4[1];
   if ((unsigned)seg >= (unsigned)nseg) return false;
   w.seg = seg;
-  w.s0 = p.segtab[2 * seg];
-  w.L = p.segtab[2 * seg + 1];
+  w.s0 = (int)it4[2];
+  w.L = (int)it4[3];
   return !(w.s0 < 0 || w.L <= 0 || (int64_t)w.s0 + w.L > p.T || w.tile < 0 || w.tile * BT >= w.L);
 }
 
 // The next work index for the workgroup: thread 0 hands out the index it fetched during the previous
 // item and fetches the following one, so the atomic's latency is hidden.  The first barrier also
-// ends the previous item's LDS reads.
+// ends the previous item's LDS reads.  Both barriers guard LDS only: the previous item's output
+// stores need not have landed, and the new fetch's reply is awaited with the next item's first
+// copies (each kernel ties `prefetched` after that wait, and after an explicit one on the paths
+// that skip the copies, so the compiler needs no memory wait here).
 __device__ __forceinline__ int64_t take_work(const BwdParams& p, int tid, int32_t& prefetched, int32_t* s_next) {
-  __syncthreads();
+  lds_barrier();
   if (tid == 0) {
     *s_next = prefetched;
     prefetched = atomicAdd(p.next, 1);
   }
-  __syncthreads();
+  lds_barrier();
   return *s_next;
 }
+
+// After an explicit vmcnt(0): the counter's reply has arrived; from here on the compiler treats
+// the register as written by ordinary code, so no later use waits for memory.
+__device__ __forceinline__ void reply_landed(int32_t& prefetched) { asm volatile("" : "+v"(prefetched)); }
 
 // The lane's 32-row block as a B operand of a 32x32x16 MFMA: row l32 of rows [row0, row0+32) of a
 // head-major [.][128] array, dims 16m + 8hh .. +8 in register m; rows at or past nvalid are zero.
@@ -233,25 +243,25 @@ __global__ __launch_bounds__(64 * BW, 2) void k_bwd_dq(BwdParams p) {
 
   const int nbkt = min(max(p.hdr->nbkt, 0), NBKT);
   __shared__ int32_t s_next;
+  __shared__ int32_t s_bkt[2 * NBKT];
+  if (tid < 2 * NBKT) s_bkt[tid] = tid < 2 * nbkt ? p.bkt[tid] : 0;
   int32_t prefetched = tid == 0 ? atomicAdd(p.next, 1) : 0;
+  __builtin_amdgcn_s_waitcnt(0xF70);
+  reply_landed(prefetched);
   for (;;) {
     WorkItem w;
     bool done;
     const int64_t v = take_work(p, tid, prefetched, &s_next);
-    const bool ok = item_of(p, v, nitems, nseg, nbkt, w, done);
+    const bool ok = item_of(p, s_bkt, v, nitems, nseg, nbkt, w, done);
     if (done) break;
-    if (!ok) continue;
-    if (p.segflag[w.seg] != 0) {  // a flagged segment: NaN rows (the order maps are not trusted there)
-      const int qr = w.tile * BT + wv * 32 + l32;
-      if (qr < w.L) {
-        const int64_t srow = w.s0 + qr;
-        const f32x16 nan16 = nan_acc();
-        const f32x16 nan4[4] = {nan16, nan16, nan16, nan16};
-        if (p.wq) store_row_f32(nan4, 1.0f, 0, hh, p.dqh + (srow * H + w.head) * HD);
-        else store_row(nan4, 1.0f, 0, hh, p.dq + (srow * H + w.head) * HD);
-      }
+    if (!ok) {
+      __builtin_amdgcn_s_waitcnt(0xF70);
+      reply_landed(prefetched);
       continue;
     }
+    // the segment's flag and dO scale: loaded now, used once the first copies have landed
+    const int flag = p.segflag[w.seg];
+    const uint32_t dmx = p.dmax[(int64_t)w.seg * H + w.head];
     const int ntk = (w.L + TILE_ROWS - 1) / TILE_ROWS;
     const int rem = w.L - (ntk - 1) * TILE_ROWS;
     const int64_t hT = (int64_t)w.head * T;
@@ -276,6 +286,20 @@ __global__ __launch_bounds__(64 * BW, 2) void k_bwd_dq(BwdParams p) {
     load_b_rows(p.qhat16 + (hT + w.s0 + row0) * HD, w.L - row0, l32, hh, qf);
     load_b_rows(p.do16 + (hT + w.s0 + row0) * HD, w.L - row0, l32, hh, gf);
     const float lq = qvalid ? p.lse2[hT + w.s0 + qrow] : 0.0f;
+    const float d_staged = (p.delta_ready && qvalid) ? -p.delta[hT + w.s0 + qrow] : 0.0f;
+    __builtin_amdgcn_s_waitcnt(0xF70);  // tile 0, the rows, the flag and the counter's reply have landed
+    reply_landed(prefetched);
+    if (flag != 0) {  // a flagged segment: NaN rows (the order maps are not trusted there)
+      const int qr = w.tile * BT + wv * 32 + l32;
+      if (qr < w.L) {
+        const int64_t srow = w.s0 + qr;
+        const f32x16 nan16 = nan_acc();
+        const f32x16 nan4[4] = {nan16, nan16, nan16, nan16};
+        if (p.wq) store_row_f32(nan4, 1.0f, 0, hh, p.dqh + (srow * H + w.head) * HD);
+        else store_row(nan4, 1.0f, 0, hh, p.dq + (srow * H + w.head) * HD);
+      }
+      continue;
+    }
 
     // S = K^ Q^T and dP = V dO^T of key tile j from stage ST (key 32kb + 8(i/4) + 4hh + (i%4), the
     // lane's query); keys past the segment end get P = 0
@@ -289,7 +313,7 @@ __global__ __launch_bounds__(64 * BW, 2) void k_bwd_dq(BwdParams p) {
     // ---- pass 1: D_i = sum_j P_ij dP_ij (unless the staging kernel computed D = dO . O)
     float Dq;
     if (p.delta_ready) {
-      Dq = qvalid ? -p.delta[hT + w.s0 + qrow] : 0.0f;
+      Dq = d_staged;
     } else {
       float dacc = 0.0f;
       auto pass1 = [&](auto stage, int j) {
@@ -376,7 +400,7 @@ __global__ __launch_bounds__(64 * BW, 2) void k_bwd_dq(BwdParams p) {
     // ---- epilogue: dq^ = scale dQ 2^-s (fp32 for the norm backward, else the output itself)
     if (qvalid) {
       const int64_t srow = w.s0 + qrow;
-      const int ex = -dout_scale_exp(p.dmax[(int64_t)w.seg * H + w.head]);
+      const int ex = -dout_scale_exp(dmx);
       if (p.wq) {
         store_row_f32(acc, p.scale, ex, hh, p.dqh + (srow * H + w.head) * HD);
       } else {
@@ -455,28 +479,28 @@ __global__ __launch_bounds__(64 * BWK, 1) void k_bwd_dkdv(BwdParams p) {
 
   const int nbkt = min(max(p.hdr->nbkt, 0), NBKT);
   __shared__ int32_t s_next;
+  __shared__ int32_t s_bkt[2 * NBKT];
+  if (tid < 2 * NBKT) s_bkt[tid] = tid < 2 * nbkt ? p.bkt[tid] : 0;
   int32_t prefetched = tid == 0 ? atomicAdd(p.next, 1) : 0;
+  __builtin_amdgcn_s_waitcnt(0xF70);
+  reply_landed(prefetched);
   for (;;) {
     WorkItem w;
     bool done;
     const int64_t v = take_work(p, tid, prefetched, &s_next);
-    const bool ok = item_of(p, v, nitems, nseg, nbkt, w, done);
+    const bool ok = item_of(p, s_bkt, v, nitems, nseg, nbkt, w, done);
     if (done) break;
-    if (!ok) continue;
+    if (!ok) {
+      __builtin_amdgcn_s_waitcnt(0xF70);
+      reply_landed(prefetched);
+      continue;
+    }
     const int row0 = w.tile * BT + kw * 32;  // the wave's first key (segment-relative)
     const int krow = row0 + l32;
     const bool kvalid = krow < w.L;
-    if (p.segflag[w.seg] != 0) {  // a flagged segment: NaN rows (the order maps are not trusted there)
-      if (kvalid) {
-        const int64_t srow = w.s0 + krow;
-        const f32x16 nan16 = nan_acc();
-        const f32x16 nan4[4] = {nan16, nan16, nan16, nan16};
-        if (role == 0) store_row(nan4, 1.0f, 0, hh, p.dv + (srow * H + w.head) * HD);
-        else if (p.wk) store_row_f32(nan4, 1.0f, 0, hh, p.dkh + (srow * H + w.head) * HD);
-        else store_row(nan4, 1.0f, 0, hh, p.dk + (srow * H + w.head) * HD);
-      }
-      continue;
-    }
+    // the segment's flag and dO scale: loaded now, used once the first copies have landed
+    const int flag = p.segflag[w.seg];
+    const uint32_t dmx = p.dmax[(int64_t)w.seg * H + w.head];
     const int ntq = (w.L + TILE_ROWS - 1) / TILE_ROWS;
     const int64_t hT = (int64_t)w.head * T;
     const uint16_t* q16b = p.qhat16 + (hT + w.s0) * HD;
@@ -484,7 +508,6 @@ __global__ __launch_bounds__(64 * BWK, 1) void k_bwd_dkdv(BwdParams p) {
     const float* lb = p.lse2 + hT + w.s0;
     const float* db = p.delta + hT + w.s0;
     const int64_t srow = w.s0 + krow;
-    const int ex = -dout_scale_exp(p.dmax[(int64_t)w.seg * H + w.head]);
 
     // query tile j into stage ST (compile-time: the compiler sees that a copy never writes the
     // stage being read); all eight waves share the copies
@@ -497,6 +520,25 @@ __global__ __launch_bounds__(64 * BWK, 1) void k_bwd_dkdv(BwdParams p) {
       if (wv == 0) rowvec_to_lds(lb + j * TILE_ROWS, v, lrow3 + (2 * st + 0) * TILE_ROWS * 4, lane);
       if (wv == 1) rowvec_to_lds(db + j * TILE_ROWS, v, lrow3 + (2 * st + 1) * TILE_ROWS * 4, lane);
     };
+
+    copies(0, Par2<0>{});
+    // the wave's 32 rows of K^ (P role) or V (dS role): the B operand of its S or dP products
+    f16x8 bf[8];
+    load_b_rows((role == 0 ? p.khat16 : p.v16) + (hT + w.s0 + row0) * HD, w.L - row0, l32, hh, bf);
+    __builtin_amdgcn_s_waitcnt(0xF70);  // tile 0, the rows, the flag and the counter's reply have landed
+    reply_landed(prefetched);
+    if (flag != 0) {  // a flagged segment: NaN rows (the order maps are not trusted there)
+      if (kvalid) {
+        const int64_t srow = w.s0 + krow;
+        const f32x16 nan16 = nan_acc();
+        const f32x16 nan4[4] = {nan16, nan16, nan16, nan16};
+        if (role == 0) store_row(nan4, 1.0f, 0, hh, p.dv + (srow * H + w.head) * HD);
+        else if (p.wk) store_row_f32(nan4, 1.0f, 0, hh, p.dkh + (srow * H + w.head) * HD);
+        else store_row(nan4, 1.0f, 0, hh, p.dk + (srow * H + w.head) * HD);
+      }
+      continue;
+    }
+    const int ex = -dout_scale_exp(dmx);
     // lse (R = 0) or -D (R = 1) of the tile's queries in the S layout (query 32q2 + 8g + 4hh + i),
     // read as assembly: a plain LDS load here would make the compiler wait for every outstanding
     // copy first (it cannot tell the copies' targets from these rows), which would expose the
@@ -516,10 +558,8 @@ __global__ __launch_bounds__(64 * BWK, 1) void k_bwd_dkdv(BwdParams p) {
         for (int g = 0; g < 4; g++) asm volatile("" : "+v"(r4[q2][g]));
     };
 
-    copies(0, Par2<0>{});
     if (role == 0) {
-      f16x8 kf[8];
-      load_b_rows(p.khat16 + (hT + w.s0 + row0) * HD, w.L - row0, l32, hh, kf);
+      const f16x8* kf = bf;
       f32x16 dv[4];
 #pragma unroll
       for (int d = 0; d < 4; d++)
@@ -574,8 +614,7 @@ __global__ __launch_bounds__(64 * BWK, 1) void k_bwd_dkdv(BwdParams p) {
         store_row(dv, 1.0f, ex, hh, p.dv + (trow * H + w.head) * HD);
       }
     } else {
-      f16x8 vf[8];
-      load_b_rows(p.v16 + (hT + w.s0 + row0) * HD, w.L - row0, l32, hh, vf);
+      const f16x8* vf = bf;
       f32x16 dk[4];
 #pragma unroll
       for (int d = 0; d < 4; d++)

@@ -1,7 +1,6 @@
 // Segment decode: per-token int32 segment ids -> segment table (start, length) and the list of
-// attention work items, plus the status word.  A forward item is (segment, query tile, the
-// segment's start, its length), so the attention kernel reads one 16-byte entry per unit; a backward
-// item is (segment, tile).
+// attention work items, plus the status word.  An item is (segment, tile, the segment's start, its
+// length), so the attention kernels read one 16-byte entry per unit.
 //
 // Packed layouts ("ws1_one_h3_block" page, Summary: several sequences share one token axis) are
 // described to the library by one id per token; a segment is a maximal run of equal ids, and ids
@@ -44,7 +43,7 @@ __device__ __forceinline__ int block_excl_scan(int v, int* lds_wave, int& total)
   return before + x - v;
 }
 
-// bkt == nullptr: forward items (16 bytes each) in segment order (the forward's head-major walk).
+// bkt == nullptr: items in segment order (the forward's head-major walk).
 // Otherwise the backward's order: items grouped by the cost class of their segment,
 // floor(log2(ceil(L / 64))), most expensive class first (the order inside a class is free: it only
 // decides which workgroup runs an item, never a result), and bkt[2b], bkt[2b+1] = first item and
@@ -193,9 +192,10 @@ __global__ __launch_bounds__(1024) void k_plan(const int32_t* __restrict__ seg, 
       const int b = 31 - __builtin_clz((unsigned)((L + TILE_ROWS_PLAN - 1) / TILE_ROWS_PLAN));
       const int nt = (L + tile - 1) / tile;
       const int off = atomicAdd(&s_run[b], nt);
+      const int st = segtab[2 * s];
       for (int j = 0; j < nt; j++) {
-        items[2 * (off + j)] = s;
-        items[2 * (off + j) + 1] = j;
+        const u32x4 e = {(uint32_t)s, (uint32_t)j, (uint32_t)st, (uint32_t)L};
+        *(u32x4*)(items + 4 * (off + j)) = e;
       }
     }
   }
