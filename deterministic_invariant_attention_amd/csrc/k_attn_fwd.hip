@@ -324,7 +324,7 @@ __global__ __launch_bounds__(64 * NWAVES, 1) void k_attn_fwd(AttnParams p) {
   for (int64_t u = slot; u < nunits;) {
     bool posted = false;  // thread 0: the next unit is in s_unit[it & 1]
     do {  // one unit; its early exits (continue) end the do, not the walk over units
-    // the next unit's counter value, fetched now and used at the end of this unit
+    // the next unit's counter value, fetched now and posted once K(0) has landed (below)
     if (!one_round && tid == 0) fetched = atomicAdd(&p.sched[SCHED_STRIDE * xcd], 1);
     // unit u: item v, whole (half = -1) or its first or second 128 queries (half = 0, 1)
     const int64_t v = lo + (u < nfull ? u : nfull + ((u - nfull) >> 1));
@@ -381,7 +381,6 @@ __global__ __launch_bounds__(64 * NWAVES, 1) void k_attn_fwd(AttnParams p) {
       continue;
     }
 
-
     // K(m+1) and V(m) go into the buffers of K(m-1) and V(m-2), which were last read in slot 2m-1.
     // The buffer parity MP = m & 1 is a compile-time constant at every call, so the compiler can
     // see that a copy never writes the buffers being read and needs no wait for it.
@@ -426,7 +425,6 @@ __global__ __launch_bounds__(64 * NWAVES, 1) void k_attn_fwd(AttnParams p) {
       if (tau + 2 <= tau_idle) idle_phase(tau + 2, Par<2>{});
       continue;
     }
-
 
     f32x16 S[NKB];  // scores of the tile whose softmax is next
     f16x8 pf[NKS];  // P of the tile whose P.V is next
