@@ -350,6 +350,29 @@ def test_bwd_out_of_range_fails_its_own_segment_only():
                 assert bitwise_equal(t[t0:t1], c)
 
 
+def test_bwd_flagged_segments_in_a_multi_round_walk():
+    """48 segments x 8 heads: over a thousand backward items for the dq and dk/dv workgroups, taken
+    from their counters.  Four segments scattered over the work order hold a v beyond fp16: their
+    rows of dq, dk and dv are NaN, every other row keeps the bits of a clean run."""
+    rng = np.random.default_rng(93)
+    lens = [int(n) for n in rng.integers(150, 700, size=48)]
+    g = to_dev(workloads.random_inputs(lens, 8, seed=94, with_grad=True))
+    starts = np.concatenate([[0], np.cumsum(lens)[:-1]])
+    clean = run_bwd(g, dmode="o32")
+    bad = [3, 17, 30, 46]
+    for sgi in bad:
+        g["v"][int(starts[sgi]) + 5, 3, 7] = 9.0e4
+    say(f"[bwd status] {sum(lens)} tokens x 8 heads, |v| > 65504 in segments {bad}")
+    got = run_bwd(g, dmode="o32")
+    flagged = np.zeros(sum(lens), dtype=bool)
+    for sgi in bad:
+        flagged[starts[sgi]:starts[sgi] + lens[sgi]] = True
+    fl = torch.from_numpy(flagged).to(got[0].device)
+    for t, c in zip(got[:3], clean[:3]):
+        assert torch.isnan(t[fl].float()).all()
+        assert bitwise_equal(t[~fl], c[~fl])
+
+
 def test_bwd_long_batch_past_the_decode_prefetch_alone_equals_batched():
     """The backward's segment decode on 20100 tokens (its chunked path) against each segment alone
     (the prefetched path): dq, dk, dv are the same bits."""

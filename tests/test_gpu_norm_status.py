@@ -130,6 +130,32 @@ def test_v_out_of_fp16_range_fails_its_own_segment_only():
     assert torch.isfinite(out[40:].float()).all()
 
 
+def test_flagged_segments_in_a_multi_round_walk():
+    """48 segments x 8 heads: about 800 work units for 256 workgroups, so the workgroups take their
+    later units from the per-XCD counters.  Four segments scattered over the item list hold a v
+    beyond fp16: their rows are NaN, and every other row keeps the bits of a clean run."""
+    rng = np.random.default_rng(91)
+    lens = [int(n) for n in rng.integers(150, 700, size=48)]
+    x = workloads.random_inputs(lens, 8, seed=92)
+    starts = np.concatenate([[0], np.cumsum(lens)[:-1]])
+    g0 = to_dev(x)
+    clean, clse = run_fwd(g0, want_lse=True)
+    bad = [3, 17, 30, 46]
+    for sgi in bad:
+        x["v"][int(starts[sgi]) + 5, 3, 7] = 1.0e5
+    g = to_dev(x)
+    say(f"[status] {sum(lens)} tokens x 8 heads, |v| > 65504 in segments {bad}")
+    ws = h3.workspace(sum(lens), 8, "cuda:0")
+    out, lse = run_fwd(g, want_lse=True, ws=ws)
+    assert h3.h3attn_status_read(ws) == h3.H3ATTN_ERR_RANGE
+    flagged = np.zeros(sum(lens), dtype=bool)
+    for sgi in bad:
+        flagged[starts[sgi]:starts[sgi] + lens[sgi]] = True
+    fl = torch.from_numpy(flagged).to(out.device)
+    assert torch.isnan(out[fl].float()).all() and torch.isnan(lse[fl]).all()
+    assert bitwise_equal(out[~fl], clean[~fl]) and bitwise_equal(lse[~fl], clse[~fl])
+
+
 def test_wrong_arguments_raise():
     x = to_dev(workloads.random_inputs([8], 2, seed=1))
     with pytest.raises(h3.H3AttnError):
