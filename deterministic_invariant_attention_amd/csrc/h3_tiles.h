@@ -94,6 +94,15 @@ __device__ __forceinline__ void phase_barrier() {
   asm volatile("" ::: "memory");
 }
 
+// Workgroup barrier for LDS hazards only: this wave's LDS operations are complete (lgkmcnt(0));
+// outstanding global loads and stores are not waited for (unlike __syncthreads, whose fence waits
+// for them).
+__device__ __forceinline__ void lds_barrier() {
+  asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
 // ds_read_b64_tr_b16 as inline assembly.  The builtin carries no memory operand, so the compiler's
 // wait insertion assumes it may read what an outstanding global-to-LDS copy writes and waits for
 // every copy before it, which serialises the copies with the matrix phase.  The assembly form is

@@ -34,15 +34,6 @@ __device__ __forceinline__ void copies_barrier() {
 }
 
 
-// Workgroup barrier for LDS hazards only: this wave's LDS operations are complete (lgkmcnt(0));
-// outstanding global loads and stores are not waited for.
-__device__ __forceinline__ void lds_barrier() {
-  asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
-  __builtin_amdgcn_s_barrier();
-  asm volatile("" ::: "memory");
-}
-
-
 // The same products with a hook between the MFMAs: hook(Par<T>) runs right after step T's MFMA is
 // issued, so independent vector work (the next tile's softmax) executes while the matrix core is
 // busy.  Waits are explicit counts, so the hook must not issue LDS reads.

@@ -178,14 +178,6 @@ struct AttnParams {
 };
 
 // Maximum over the query's 96 keys of one tile (exact: any evaluation order gives these bits).
-// Workgroup barrier for LDS hazards only: this wave's LDS operations are complete (lgkmcnt(0)),
-// outstanding global stores are not waited for.
-__device__ __forceinline__ void lds_barrier() {
-  asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
-  __builtin_amdgcn_s_barrier();
-  asm volatile("" ::: "memory");
-}
-
 __device__ __forceinline__ float tile_max(const f32x16* S) {
   float a = -__builtin_inff();
 #pragma unroll
