@@ -9,8 +9,6 @@ constexpr int BT = 128;        // queries (dq kernel) or keys (dk/dv kernel) per
 constexpr int NR = 16;         // rows (token, head) per workgroup of the norm backward
 constexpr int DW_CHUNK = 64;   // partials per chunk of the weight-gradient reduction
 
-constexpr int NBKT = 32;  // cost classes of the backward work order (floor(log2(64-row tiles)))
-
 // Backward workspace (h3attn_bwd_workspace_bytes):
 // [0, 256)          header: status bits, segment and work-item counts, work counters
 // segtab            int32 [2*T]

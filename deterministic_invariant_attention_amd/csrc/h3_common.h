@@ -25,6 +25,8 @@ constexpr int BK = 96;   // keys per KV tile; the KV walk is in these tiles, asc
 // segflag             int32 [T]: per segment, nonzero when one of its values cannot enter the
 //                     products (a finite |v| beyond fp16) or its position ids are not a permutation;
 //                     that segment's outputs are NaN, the others are computed as usual
+// sched               the attention kernel's work counters (SCHED_BYTES, below)
+// bkt                 int32 [2*NBKT]: first item and count of each cost class of the work order
 struct WsHeader {
   int32_t status;  // OR of STATUS_* bits; reset by the plan kernel
   int32_t nseg;
@@ -45,8 +47,10 @@ constexpr size_t SCHED_BYTES = 2048;
 constexpr int SCHED_STRIDE = 32;
 constexpr int SCHED_DONE = 8 * SCHED_STRIDE;
 
+constexpr int NBKT = 32;  // cost classes of a work order: floor(log2(64-row tiles of the segment))
+
 struct WsLayout {
-  size_t segtab, items, khat, v16, qhat, tok2seg, segflag, sched, total;
+  size_t segtab, items, khat, v16, qhat, tok2seg, segflag, sched, bkt, total;
   int64_t max_items;
 };
 
@@ -63,7 +67,8 @@ __host__ __device__ inline WsLayout ws_layout(int64_t T, int32_t H) {
   w.tok2seg = w.qhat + align256((size_t)T * H * HD * 2);
   w.segflag = w.tok2seg + align256((size_t)T * 4);
   w.sched = w.segflag + align256((size_t)T * 4);
-  w.total = w.sched + SCHED_BYTES;
+  w.bkt = w.sched + SCHED_BYTES;
+  w.total = w.bkt + align256((size_t)NBKT * 2 * 4);
   return w;
 }
 

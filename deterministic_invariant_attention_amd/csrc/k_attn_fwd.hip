@@ -171,6 +171,7 @@ struct AttnParams {
   const int32_t* items;
   const int32_t* segflag;  // per segment: nonzero = a value cannot enter the products (NaN outputs)
   int32_t* sched;          // the per-XCD work counters and the done count (zero between launches)
+  const int32_t* bkt;      // cost classes of the item list: first item and count, most expensive first
   int64_t T;
   int32_t H;
   float c;            // scale * log2(e)
@@ -281,13 +282,33 @@ __global__ __launch_bounds__(64 * NWAVES, 1) void k_attn_fwd(AttnParams p) {
   const int xcd = blockIdx.x & 7;
   const int slot = blockIdx.x >> 3;
   const int nslots = p.xcd_slots;
-  const int64_t lo = (int64_t)nwork * xcd / 8, cnt = (int64_t)nwork * (xcd + 1) / 8 - lo;
+  // One round (no XCD has more of the list's units than workgroups): units in list order, each
+  // workgroup's slot its only unit.  Otherwise longest first: the plan groups the items by the cost
+  // class of their segment, most expensive first, and XCD x takes the x-th eighth of every class
+  // (head-major inside a class, so a head's items still share an L2), so the cheap units come last
+  // and even out the workgroups' ends.  Either order changes which workgroup runs an item, never a
+  // result.
+  const bool one_round = (nwork + 7) / 8 <= nslots;
+  const int nbkt = min(max(p.hdr->nbkt, 0), NBKT);
+  __shared__ int32_t s_bkt[2 * NBKT];
+  int64_t lo = 0, cnt = 0;
+  if (one_round) {
+    lo = (int64_t)nwork * xcd / 8;
+    cnt = (int64_t)nwork * (xcd + 1) / 8 - lo;
+  } else {
+    if (tid < 2 * NBKT) s_bkt[tid] = tid < 2 * nbkt ? p.bkt[tid] : 0;
+    lds_barrier();
+    for (int b = 0; b < nbkt; b++) {
+      const int64_t span = (int64_t)max(s_bkt[2 * b + 1], 0) * H;
+      cnt += span * (xcd + 1) / 8 - span * xcd / 8;
+    }
+  }
   const int64_t last = cnt % nslots;  // items of the XCD's last round
   const int64_t nfull = (last != 0 && 2 * last <= nslots) ? cnt - last : cnt;
   const int64_t nunits = nfull + 2 * (cnt - nfull);
-  // No XCD has more units than workgroups (nunits <= nslots holds exactly when cnt <= nslots, and
-  // cnt <= ceil(nwork / 8)): every unit is some workgroup's first, and the counters stay untouched.
-  const bool one_round = (nwork + 7) / 8 <= nslots;
+  // In one round no XCD has more units than workgroups (nunits <= nslots holds exactly when
+  // cnt <= nslots, and cnt <= ceil(nwork / 8)): every unit is some workgroup's first, and the
+  // counters stay untouched.
 
   const int k_lane_off = tile_lane_offset(false, wv, lane);
   // the loop's copies: each wave of a group issues a quarter of a tile
@@ -318,11 +339,29 @@ __global__ __launch_bounds__(64 * NWAVES, 1) void k_attn_fwd(AttnParams p) {
     do {  // one unit; its early exits (continue) end the do, not the walk over units
     // the next unit's counter value, fetched now and posted once K(0) has landed (below)
     if (!one_round && tid == 0) fetched = atomicAdd(&p.sched[SCHED_STRIDE * xcd], 1);
-    // unit u: item v, whole (half = -1) or its first or second 128 queries (half = 0, 1)
-    const int64_t v = lo + (u < nfull ? u : nfull + ((u - nfull) >> 1));
+    // unit u: the XCD's k-th item, whole (half = -1) or its first or second 128 queries (half = 0, 1)
+    const int64_t k = u < nfull ? u : nfull + ((u - nfull) >> 1);
     const int half = u < nfull ? -1 : (int)((u - nfull) & 1);
-    const int head = (int)(v / nitems);
-    const int item = (int)(v - (int64_t)head * nitems);
+    int head = -1, item = -1;
+    if (one_round) {
+      const int64_t v = lo + k;
+      head = (int)(v / nitems);
+      item = (int)(v - (int64_t)head * nitems);
+    } else {
+      int64_t kc = k;
+      for (int b = 0; b < nbkt; b++) {
+        const int cb = max(s_bkt[2 * b + 1], 0);
+        const int64_t span = (int64_t)cb * H, blo = span * xcd / 8, blen = span * (xcd + 1) / 8 - blo;
+        if (kc < blen) {
+          const int64_t g = blo + kc;
+          head = (int)(g / cb);
+          item = s_bkt[2 * b] + (int)(g - (int64_t)head * cb);
+          break;
+        }
+        kc -= blen;
+      }
+    }
+    if ((unsigned)item >= (unsigned)nitems || (unsigned)head >= (unsigned)H) continue;
     // the item: (segment, query tile, the segment's start, its length)
     const u32x4 it4 = *(const u32x4*)(p.items + 4 * item);
     const int seg = (int)it4[0], qt = (int)it4[1], s0 = (int)it4[2], L = (int)it4[3];
@@ -563,6 +602,7 @@ hipError_t launch_attend(const void* q, bool normed, int64_t T, int32_t H, float
   p.items = (const int32_t*)(base + Lw.items);
   p.segflag = (const int32_t*)(base + Lw.segflag);
   p.sched = (int32_t*)(base + Lw.sched);
+  p.bkt = (const int32_t*)(base + Lw.bkt);
   p.T = T;
   p.H = H;
   p.c = (float)((double)scale * 1.4426950408889634074);

@@ -14,6 +14,7 @@
 #include "h3_common.h"
 #include "h3_bwd.h"
 #include "h3_launch.h"
+#include "h3_tiles.h"
 
 namespace h3 {
 
@@ -43,11 +44,10 @@ __device__ __forceinline__ int block_excl_scan(int v, int* lds_wave, int& total)
   return before + x - v;
 }
 
-// bkt == nullptr: items in segment order (the forward's head-major walk).
-// Otherwise the backward's order: items grouped by the cost class of their segment,
-// floor(log2(ceil(L / 64))), most expensive class first (the order inside a class is free: it only
-// decides which workgroup runs an item, never a result), and bkt[2b], bkt[2b+1] = first item and
-// item count of the b-th non-empty class; the work counters are reset.
+// Items are grouped by the cost class of their segment, floor(log2(ceil(L / 64))), most expensive
+// class first (the order inside a class is free: it only decides which workgroup runs an item,
+// never a result; a segment's tiles stay together, in order), and bkt[2b], bkt[2b+1] = first item
+// and item count of the b-th non-empty class; the work counters are reset.
 // tok2seg: the segment index of every token; segflag: the per-segment error flags, cleared for the
 // call's nseg segments; dmax (backward only, else NULL): the per-(segment, head) maxima of |dO|,
 // zeroed for the nseg * H slots the call uses; sched (forward only, else NULL): the attention
@@ -60,6 +60,7 @@ __global__ __launch_bounds__(1024) void k_plan(const int32_t* __restrict__ seg, 
   __shared__ int lds_wave[16];
   __shared__ int s_bad;
   __shared__ int s_cnt[NBKT], s_run[NBKT];
+  __shared__ int s_nbkt;
   const int tid = threadIdx.x;
   if (tid == 0) s_bad = 0;
   __syncthreads();
@@ -146,46 +147,39 @@ __global__ __launch_bounds__(1024) void k_plan(const int32_t* __restrict__ seg, 
   // pass 3: work items, ceil(L / tile) tiles per segment
   int nitems = 0;
   int nbkt = 0;
-  if (bkt == nullptr) {  // segment order: each thread owns a contiguous run of segments
-    const int sper = (nseg + 1023) / 1024;
-    const int s0 = min(nseg, tid * sper), s1 = min(nseg, s0 + sper);
-    int nt = 0;
-    for (int sg = s0; sg < s1; sg++) nt += (segtab[2 * sg + 1] + tile - 1) / tile;
-    const int off = block_excl_scan(nt, lds_wave, nitems);
-    int it = off;
-    for (int sg = s0; sg < s1; sg++) {
-      const int n = (segtab[2 * sg + 1] + tile - 1) / tile;
-      const int st = segtab[2 * sg], len = segtab[2 * sg + 1];
-      for (int j = 0; j < n; j++, it++) {
-        const u32x4 e = {(uint32_t)sg, (uint32_t)j, (uint32_t)st, (uint32_t)len};
-        *(u32x4*)(items + 4 * it) = e;
-      }
-    }
-  } else {  // by cost class, most expensive first
+  {  // by cost class, most expensive first (the class counts and offsets live in LDS, so the
+     // barriers below guard LDS only and do not wait for the table's global stores)
     if (tid < NBKT) s_cnt[tid] = 0;
-    __syncthreads();
+    lds_barrier();
     for (int s = tid; s < nseg; s += 1024) {
       const int L = segtab[2 * s + 1];
       const int b = 31 - __builtin_clz((unsigned)((L + TILE_ROWS_PLAN - 1) / TILE_ROWS_PLAN));
       atomicAdd(&s_cnt[b], (L + tile - 1) / tile);
     }
-    __syncthreads();
-    if (tid == 0) {
-      int start = 0;
-      for (int b = NBKT - 1; b >= 0; b--) {
-        s_run[b] = start;
-        if (s_cnt[b] > 0) {
-          bkt[2 * nbkt] = start;
-          bkt[2 * nbkt + 1] = s_cnt[b];
-          nbkt++;
-        }
-        start += s_cnt[b];
+    lds_barrier();
+    if (tid < 64) {  // one wave: lane l takes class NBKT - 1 - l (most expensive first)
+      const int c = NBKT - 1 - tid;
+      const int n = tid < NBKT ? s_cnt[c] : 0;
+      int x = n;  // inclusive prefix sum of the counts over the lanes
+#pragma unroll
+      for (int o = 1; o < 64; o <<= 1) {
+        const int y = __shfl_up(x, o, 64);
+        if (tid >= o) x += y;
       }
-      s_cnt[0] = nbkt;  // broadcast
-      lds_wave[0] = start;
+      const uint64_t nonempty = __ballot(n > 0);
+      if (tid < NBKT) s_run[c] = x - n;
+      if (n > 0) {
+        const int idx = __builtin_popcountll(nonempty & ((1ull << tid) - 1));
+        bkt[2 * idx] = x - n;
+        bkt[2 * idx + 1] = n;
+      }
+      if (tid == 63) {
+        s_nbkt = __builtin_popcountll(nonempty);
+        lds_wave[0] = x;
+      }
     }
-    __syncthreads();
-    nbkt = s_cnt[0];
+    lds_barrier();
+    nbkt = s_nbkt;
     nitems = lds_wave[0];
     for (int s = tid; s < nseg; s += 1024) {
       const int L = segtab[2 * s + 1];
@@ -215,8 +209,8 @@ hipError_t launch_plan(const int32_t* seg, int64_t T, void* ws, int32_t H, hipSt
   const WsLayout L = ws_layout(T, H);
   char* base = (char*)ws;
   hipLaunchKernelGGL(k_plan, dim3(1), dim3(1024), 0, stream, seg, T, (WsHeader*)base, (int32_t*)(base + L.segtab),
-                     (int32_t*)(base + L.items), BQ, nullptr, (int32_t*)(base + L.tok2seg), (int32_t*)(base + L.segflag),
-                     nullptr, H, (int32_t*)(base + L.sched));
+                     (int32_t*)(base + L.items), BQ, (int32_t*)(base + L.bkt), (int32_t*)(base + L.tok2seg),
+                     (int32_t*)(base + L.segflag), nullptr, H, (int32_t*)(base + L.sched));
   return hipGetLastError();
 }
 

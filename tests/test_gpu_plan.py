@@ -1,7 +1,8 @@
 """The segment decode (h3attn_plan) read back from the workspace and compared with a decode written
 here in plain Python: the header's counts, the segment table (start, length), the work items
-(segment, 256-query tile, segment start, length) in segment order and every token's segment
-index.  Packed layouts ("ws1_one_h3_block" page, Summary: several sequences share one token axis)
+(segment, 256-query tile, segment start, length) grouped by the cost class of their segment, most
+expensive first (a segment's tiles together and in order; the segments of a class in any order),
+the class table, and every token's segment index.  Packed layouts ("ws1_one_h3_block" page, Summary: several sequences share one token axis)
 reach the library as one id per token; a segment is a maximal run of equal ids and ids never
 decrease.  The sizes sit
 on both sides of the decode's two paths: the ids staged in LDS for 2048 < T <= 16384, read from
@@ -17,6 +18,7 @@ pytestmark = pytest.mark.gpu
 
 BQ, HD = 256, 128
 STATUS_SEG_BIT = 1
+SCHED_BYTES = 2048
 
 
 def _a256(x):
@@ -30,7 +32,14 @@ def _offsets(T, H):
     items = segtab + _a256(T * 8)
     khat = items + _a256(max_items * 16)
     tok2seg = khat + 3 * _a256(T * H * HD * 2)
-    return segtab, items, tok2seg
+    sched = tok2seg + 2 * _a256(T * 4)
+    bkt = sched + SCHED_BYTES
+    return segtab, items, tok2seg, bkt
+
+
+def _cost_class(L):
+    """floor(log2(ceil(L / 64))): the segment's cost class."""
+    return int(np.floor(np.log2((L + 63) // 64)))
 
 
 def _decode(ids):
@@ -40,9 +49,8 @@ def _decode(ids):
     starts = [t for t in range(T) if t == 0 or ids[t] != ids[t - 1]]
     bounds = starts + [T]
     segtab = [(bounds[i], bounds[i + 1] - bounds[i]) for i in range(len(starts))]
-    items = [(s, j, st, L) for s, (st, L) in enumerate(segtab) for j in range((L + BQ - 1) // BQ)]
     tok2seg = np.repeat(np.arange(len(segtab)), [L for _, L in segtab])
-    return segtab, items, tok2seg
+    return segtab, tok2seg
 
 
 def _ids_from_lengths(lens, first=0, step=1):
@@ -58,22 +66,44 @@ def _run_plan(ids, H=2):
     torch.cuda.synchronize()
     w = ws.cpu()
     hdr = w[:256].view(torch.int32).numpy()
-    so, io, to = _offsets(T, H)
-    return hdr, w, so, io, to
+    return hdr, w, _offsets(T, H)
 
 
 def _check(ids, H=2):
     T = len(ids)
-    hdr, w, so, io, to = _run_plan(ids, H)
-    segtab, items, tok2seg = _decode(ids)
+    hdr, w, (so, io, to, bo) = _run_plan(ids, H)
+    segtab, tok2seg = _decode(ids)
+    ntiles = [(L + BQ - 1) // BQ for _, L in segtab]
     assert hdr[0] == 0, f"status {hdr[0]}"
-    assert hdr[1] == len(segtab) and hdr[2] == len(items), (hdr[1], hdr[2], len(segtab), len(items))
+    assert hdr[1] == len(segtab) and hdr[2] == sum(ntiles), (hdr[1], hdr[2], len(segtab), sum(ntiles))
     got_seg = w[so:so + 8 * len(segtab)].view(torch.int32).numpy().reshape(-1, 2)
     assert np.array_equal(got_seg, np.array(segtab, dtype=np.int32).reshape(-1, 2))
-    got_items = w[io:io + 16 * len(items)].view(torch.int32).numpy().reshape(-1, 4)
-    assert np.array_equal(got_items, np.array(items, dtype=np.int32).reshape(-1, 4))
     got_t2s = w[to:to + 4 * T].view(torch.int32).numpy()
     assert np.array_equal(got_t2s, tok2seg.astype(np.int32))
+    # the class table: non-empty classes, most expensive first
+    cls = [_cost_class(L) for _, L in segtab]
+    order = sorted(set(cls), reverse=True)
+    want_bkt, first = [], 0
+    for c in order:
+        n = sum(nt for nt, cc in zip(ntiles, cls) if cc == c)
+        want_bkt.append((first, n))
+        first += n
+    assert hdr[3] == len(order)
+    got_bkt = w[bo:bo + 8 * len(order)].view(torch.int32).numpy().reshape(-1, 2)
+    assert np.array_equal(got_bkt, np.array(want_bkt, dtype=np.int32).reshape(-1, 2))
+    # the items: within each class, every segment of that class once, its tiles together and in order
+    got = w[io:io + 16 * sum(ntiles)].view(torch.int32).numpy().reshape(-1, 4)
+    for c, (f, n) in zip(order, want_bkt):
+        rows, seen, r = got[f:f + n], set(), 0
+        while r < n:
+            sg = int(rows[r, 0])
+            assert 0 <= sg < len(segtab) and cls[sg] == c and sg not in seen, (c, r, sg)
+            seen.add(sg)
+            st, L = segtab[sg]
+            want = np.array([(sg, j, st, L) for j in range(ntiles[sg])], dtype=np.int32)
+            assert np.array_equal(rows[r:r + ntiles[sg]], want), (c, sg)
+            r += ntiles[sg]
+        assert seen == {s for s in range(len(segtab)) if cls[s] == c}
 
 
 def _random_lengths(rng, T, lo, hi):
